@@ -1,0 +1,122 @@
+"""Key and value compression, float64, step by step.
+
+Keys ("How 0xsero/turboquant works", "Compression Pipeline"; "turbo-attn
+0.24.0", "How it works"; "5x Faster LLM Inference? ...", "Example 4:
+Kernel-Level Operations": normalise -> rotate -> Lloyd-Max quantise -> pack,
+plus a 1-bit QJL residual sign):
+    n     = ||k||                                    stored as fp16
+    t     = sqrt(d) * R k / n        (t = 0 if n = 0)
+    idx_j = #{i : beta_i < t_j}                      b_k-bit codebook index
+    rho   = t - c[idx]
+    gamma = ||rho||                                  stored as fp16
+    y     = S rho,   z_j = [y_j >= 0]                1 sign bit per coordinate
+The code decisions use the unrounded n and gamma.
+
+Values ("How 0xsero/turboquant works", "Value Compression": group
+quantisation with per-group scale/zero; "tiny-turboquant 0.18.0",
+"Measured quality": groups of 32 channels, each with its own scale/zero):
+    v'     = R v                       (the same rotation as the head's keys)
+    per group of G consecutive coordinates:
+    scale  = fp16((max - min) / (2^b_v - 1)),   zero = fp16(min)
+    code_j = clamp(round_half_even((v'_j - zero) / scale), 0, 2^b_v - 1)
+             (code_j = 0 when scale == 0)
+The codes are computed from the stored (fp16) scale and zero so that the
+decoder's zero + scale * code is the nearest grid point.
+"""
+
+import math
+
+import numpy as np
+
+from . import bits, codebook, layout as lay
+
+
+def compress_keys(K, R, S, centroids, boundaries):
+    """K: [n, d] float64 (exact input values).  Returns a dict of per-vector arrays."""
+    K = np.asarray(K, dtype=np.float64)
+    d = K.shape[-1]
+    n = np.sqrt(np.sum(K * K, axis=-1))
+    rk = K @ R.T
+    safe = np.where(n > 0.0, n, 1.0)
+    t = np.where((n > 0.0)[:, None], (math.sqrt(d) / safe)[:, None] * rk, 0.0)
+    idx = codebook.quantize_index(t, boundaries)
+    chat = np.asarray(centroids)[idx]
+    rho = t - chat
+    gamma = np.sqrt(np.sum(rho * rho, axis=-1))
+    y = rho @ S.T
+    z = (y >= 0.0).astype(np.int64)
+    return {
+        "n": n, "t": t, "idx": idx, "rho": rho, "gamma": gamma, "y": y, "z": z,
+        "n16": n.astype(np.float16), "gamma16": gamma.astype(np.float16),
+    }
+
+
+def quantize_groups(vrot, v_bits, group):
+    """Group scale/zero quantisation of rotated values vrot: [n, d]."""
+    n, d = vrot.shape
+    g = vrot.reshape(n, d // group, group)
+    mn = g.min(axis=-1)
+    mx = g.max(axis=-1)
+    top = (1 << v_bits) - 1
+    scale16 = ((mx - mn) / top).astype(np.float16)
+    zero16 = mn.astype(np.float16)
+    s = scale16.astype(np.float64)[..., None]
+    z = zero16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint((g - z) / np.where(s > 0.0, s, 1.0))
+    codes = np.where(s > 0.0, np.clip(q, 0, top), 0).astype(np.int64)
+    return codes.reshape(n, d), scale16, zero16
+
+
+def compress_values(V, R, v_bits, group):
+    V = np.asarray(V, dtype=np.float64)
+    vrot = V @ R.T
+    codes, scale16, zero16 = quantize_groups(vrot, v_bits, group)
+    return {"vrot": vrot, "codes": codes, "scale16": scale16, "zero16": zero16}
+
+
+def _scatter(pool, starts, data):
+    data = np.asarray(data, dtype=np.uint8)
+    idx = np.asarray(starts, dtype=np.int64)[:, None] + np.arange(data.shape[-1])
+    pool[idx] = data
+
+
+def compress_into_pool(K, V, slots, pool, layout, state):
+    """Compress K, V [N, H_kv, d] (float64 values of the inputs) into `pool` at `slots` [N].
+
+    Tokens with a negative slot are skipped.  `state` is an oracle.state.LayerState.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = slots >= 0
+    K, V, slots = K[keep], V[keep], slots[keep]
+    n_tok, H, d = K.shape
+    blocks, offs = np.divmod(slots, lay.P)
+    out = {}
+    for h in range(H):
+        ck = compress_keys(K[:, h], state.R[h], state.S[h], state.centroids, state.boundaries)
+        cv = compress_values(V[:, h], state.R[h], layout.v_bits, layout.group)
+        base = (blocks * H + h) * layout.block_bytes
+        _scatter(pool, base + layout.off_kc + offs * layout.kc_bytes, bits.pack(ck["idx"], layout.k_bits))
+        _scatter(pool, base + layout.off_ks + offs * layout.ks_bytes, bits.pack(ck["z"], 1))
+        kn = np.stack([ck["n16"], ck["gamma16"]], axis=-1).view(np.uint8)
+        _scatter(pool, base + layout.off_kn + offs * layout.kn_bytes, kn)
+        _scatter(pool, base + layout.off_vc + offs * layout.vc_bytes, bits.pack(cv["codes"], layout.v_bits))
+        sz = np.stack([cv["scale16"], cv["zero16"]], axis=-1).reshape(n_tok, -1).view(np.uint8)
+        _scatter(pool, base + layout.off_vsz + offs * layout.vsz_bytes, sz)
+        out[h] = (ck, cv)
+    return out
+
+
+def store_bypass(K_bits16, V_bits16, slots, pool, layout, n_kv_heads):
+    """Uncompressed layers: copy bf16 K, V bit patterns [N, H, d] into the pool."""
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = slots >= 0
+    Kb = np.asarray(K_bits16, np.uint16)[keep]
+    Vb = np.asarray(V_bits16, np.uint16)[keep]
+    blocks, offs = np.divmod(slots[keep], lay.P)
+    for h in range(n_kv_heads):
+        base = (blocks * n_kv_heads + h) * layout.block_bytes
+        _scatter(pool, base + layout.off_kb + offs * layout.kb_bytes, Kb[:, h].view(np.uint8).reshape(len(offs), -1))
+        _scatter(pool, base + layout.off_vb + offs * layout.kb_bytes, Vb[:, h].view(np.uint8).reshape(len(offs), -1))

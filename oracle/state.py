@@ -1,0 +1,59 @@
+"""Per-(layer, KV head) rotation R and QJL projection S.
+
+R: a Haar-random orthogonal d x d matrix ("How 0xsero/turboquant works",
+"Compression Pipeline": random orthogonal rotation; "5x Faster LLM
+Inference? ...", "What is TurboQuant-GPU?": random orthogonal rotation makes the
+coordinates approximately Gaussian).  Drawn as in Mezzadri, "How to generate
+random matrices from the classical compact groups" (2007): QR-factorise a
+matrix of i.i.d. N(0,1) entries (filled row-major from the rotation stream)
+and multiply column j of Q by the sign of R_jj (sign(0) taken as +1), which
+makes the factor unique and Haar distributed.
+
+S: an m x d matrix of i.i.d. N(0,1) entries from the projection stream, m = d
+(the QJL residual-sign projection of the same sections).
+
+Both are stored, and used by every consumer, as float32-rounded values; the
+oracle then computes in float64 on exactly those numbers.
+"""
+
+import numpy as np
+
+from . import rng
+
+
+def gaussian_matrix(seed, layer, head, tag, rows, cols):
+    vals = rng.gaussians(seed, layer, head, tag, rows * cols)
+    return np.array(vals, dtype=np.float64).reshape(rows, cols)
+
+
+def haar_rotation_f64(seed, layer, head, d):
+    g = gaussian_matrix(seed, layer, head, rng.TAG_ROTATION, d, d)
+    q, r = np.linalg.qr(g)
+    signs = np.where(np.diag(r) < 0.0, -1.0, 1.0)
+    return q * signs[None, :]
+
+
+def haar_rotation(seed, layer, head, d):
+    """float32-rounded Haar rotation, returned as float64 values."""
+    return haar_rotation_f64(seed, layer, head, d).astype(np.float32).astype(np.float64)
+
+
+def qjl_projection(seed, layer, head, d, m=None):
+    m = d if m is None else m
+    s = gaussian_matrix(seed, layer, head, rng.TAG_PROJECTION, m, d)
+    return s.astype(np.float32).astype(np.float64)
+
+
+class LayerState:
+    """All state of one compressed layer: R and S per KV head plus the key codebook."""
+
+    def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian"):
+        from . import codebook
+
+        self.seed, self.layer, self.n_kv_heads, self.d = seed, layer, n_kv_heads, d
+        self.k_bits, self.v_bits, self.group, self.dist = k_bits, v_bits, group, dist
+        self.R = np.stack([haar_rotation(seed, layer, h, d) for h in range(n_kv_heads)])
+        self.S = np.stack([qjl_projection(seed, layer, h, d) for h in range(n_kv_heads)])
+        c64, b64, _ = codebook.lloyd_max(k_bits, dist, d)
+        self.centroids = c64.astype(np.float32).astype(np.float64)
+        self.boundaries = b64.astype(np.float32).astype(np.float64)

@@ -1,0 +1,121 @@
+"""Pins of the oracle's key/value compression."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codebook, compress, metrics, state
+
+D = 128
+
+
+def _cb(bits):
+    c, b, mse = codebook.lloyd_max(bits, "gaussian", D)
+    return c.astype(np.float32).astype(np.float64), b.astype(np.float32).astype(np.float64), mse
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("outliers", [False, True])
+def test_mse_reconstruction_cosine(bits, outliers):
+    """Mean cos(k, k_hat) -> sqrt(1 - D_b) for the codebook reconstruction (rotated
+    coordinates are ~N(0,1) at d = 128 whatever the channel scales)."""
+    rng = np.random.default_rng(bits)
+    K = rng.standard_normal((4096, D))
+    if outliers:
+        K[:, rng.choice(D, 4, replace=False)] *= 10.0
+    R = state.haar_rotation(11, 0, 0, D)
+    S = state.qjl_projection(11, 0, 0, D)
+    c, b, mse = _cb(bits)
+    ck = compress.compress_keys(K, R, S, c, b)
+    cos = metrics.cosine_rows(K, metrics.reconstruct_keys_mse(ck, R, c, D)).mean()
+    assert abs(cos - math.sqrt(1.0 - mse)) < 3e-3
+    if bits == 3:
+        assert cos >= 0.98          # the target quality at 3 bits
+
+
+def test_codes_are_nearest_centroid_of_rotated_standardised_key():
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((64, D)) * rng.uniform(0.1, 30.0, (64, 1))
+    R = state.haar_rotation(3, 1, 2, D)
+    S = state.qjl_projection(3, 1, 2, D)
+    c, b, _ = _cb(4)
+    ck = compress.compress_keys(K, R, S, c, b)
+    # brute force, written from the definitions: unit vector, rotation, nearest centroid
+    for i in range(64):
+        unit = K[i] / math.sqrt(sum(x * x for x in K[i]))
+        t = math.sqrt(D) * np.array([sum(R[r, j] * unit[j] for j in range(D)) for r in range(D)])
+        idx = [int(np.argmin(np.abs(tj - c))) for tj in t]
+        assert idx == list(ck["idx"][i])
+        rho = t - c[idx]
+        y = np.array([sum(S[r, j] * rho[j] for j in range(D)) for r in range(D)])
+        assert list((y >= 0).astype(int)) == list(ck["z"][i])
+    assert np.array_equal(ck["n16"], np.linalg.norm(K, axis=1).astype(np.float16))
+
+
+def test_qjl_estimator_unbiased():
+    """E_S[q'.c + sqrt(pi/2)/m gamma <S q', sign(S rho)>] = q'.t over random S,
+    with standard deviation at most sqrt(pi/(2m)) ||q'|| gamma."""
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal(D)
+    qp = rng.standard_normal(D)
+    R = np.eye(D)
+    c, b, _ = _cb(2)
+    n_seeds = 4000
+    est = np.empty(n_seeds)
+    from oracle import decode
+    for s in range(n_seeds):
+        S = np.random.default_rng(1000 + s).standard_normal((D, D))
+        ck = compress.compress_keys(k[None, :], R, S, c, b)
+        f = {"idx": ck["idx"], "z": ck["z"], "n16": np.array([math.sqrt(D)]),
+             "g16": ck["gamma"]}
+        est[s] = decode.token_scores(qp, S @ qp, f, c, D, D, 1.0)[0]
+    truth = qp @ ck["t"][0]
+    se = est.std() / math.sqrt(n_seeds)
+    assert abs(est.mean() - truth) < 4 * se
+    gamma = ck["gamma"][0]
+    assert est.std() <= math.sqrt(math.pi / (2 * D)) * np.linalg.norm(qp) * gamma * 1.05
+
+
+@pytest.mark.parametrize("v_bits", [2, 3, 4])
+def test_value_group_quantiser_bounds(v_bits):
+    rng = np.random.default_rng(v_bits)
+    V = rng.standard_normal((512, D)) * 3.0
+    R = state.haar_rotation(4, 0, 0, D)
+    cv = compress.compress_values(V, R, v_bits, 32)
+    top = (1 << v_bits) - 1
+    assert cv["codes"].min() >= 0 and cv["codes"].max() <= top
+    g = cv["vrot"].reshape(512, 4, 32)
+    assert np.array_equal(cv["zero16"], g.min(axis=-1).astype(np.float16))
+    assert np.array_equal(cv["scale16"], ((g.max(-1) - g.min(-1)) / top).astype(np.float16))
+    s = np.repeat(cv["scale16"].astype(np.float64), 32, axis=1)
+    z = np.repeat(cv["zero16"].astype(np.float64), 32, axis=1)
+    err = np.abs(cv["vrot"] - (z + s * cv["codes"]))
+    assert np.all(err <= 0.5 * s * (1 + 1e-9) + 1e-12)
+    # every group uses its extreme codes
+    codes = cv["codes"].reshape(512, 4, 32)
+    assert np.all(codes.min(-1) == 0) and np.all(codes.max(-1) == top)
+
+
+def test_value_grid_points_are_exact():
+    """Rotated values already on an fp16 scale/zero grid come back exactly."""
+    R = state.haar_rotation(4, 0, 1, D)
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 8, (16, D))
+    codes[:, ::32] = 0
+    codes[:, 1::32] = 7
+    scale = np.float16(0.375)
+    zero = np.float16(-1.25)
+    vrot = float(zero) + float(scale) * codes
+    V = vrot @ R            # v = R^T v'
+    cv = compress.compress_values(V, R, 3, 32)
+    assert np.array_equal(cv["codes"], codes)
+    assert np.all(cv["scale16"] == scale) and np.all(cv["zero16"] == zero)
+
+
+def test_zero_norm_key():
+    c, b, _ = _cb(3)
+    ck = compress.compress_keys(np.zeros((1, D)), np.eye(D), np.eye(D), c, b)
+    assert ck["n16"][0] == 0 and np.all(ck["t"] == 0)
+    assert np.all(ck["idx"] == np.sum(b < 0))
+    assert np.isfinite(ck["gamma"][0])
