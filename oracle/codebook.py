@@ -17,8 +17,9 @@ Lloyd's algorithm (Lloyd 1957 / Max 1960) with L = 2**bits levels:
   boundaries  beta_i = (c_i + c_{i+1}) / 2                         (nearest neighbour)
   centroids   c_i = E[x | beta_{i-1} < x <= beta_i]                (centroid condition)
 iterated from the quantile midpoints F^-1((i + 1/2) / L) until
-max |c_new - c_old| < tol.  Cell probabilities and moments are evaluated in
-closed form (Gaussian: erfc and the density; sphere: the regularised
+max |c_new - c_old| < tol.  Both densities are even, so each iterate is
+symmetrised (c_i = -c_{L-1-i}); the middle boundary is then exactly 0.
+Cell probabilities and moments are evaluated in closed form (Gaussian: erfc and the density; sphere: the regularised
 incomplete beta function and the closed-form first moment).
 """
 
@@ -113,6 +114,7 @@ def lloyd_max(bits, dist="gaussian", dim=128, tol=1e-14, max_iter=200000):
         for i in range(levels):
             p, m1, _ = _moments(edges[i], edges[i + 1], dist, dim)
             new[i] = m1 / p
+        new = 0.5 * (new - new[::-1])          # both densities are symmetric about 0
         delta = float(np.max(np.abs(new - c)))
         c = new
         if delta < tol:

@@ -81,16 +81,17 @@ def _scatter(pool, starts, data):
     pool[idx] = data
 
 
-def compress_into_pool(K, V, slots, pool, layout, state):
+def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     """Compress K, V [N, H_kv, d] (float64 values of the inputs) into `pool` at `slots` [N].
 
     Tokens with a negative slot are skipped.  `state` is an oracle.state.LayerState.
+    Returns the per-head intermediate results ({head: (keys, values)}) if `keep`.
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     slots = np.asarray(slots, dtype=np.int64)
-    keep = slots >= 0
-    K, V, slots = K[keep], V[keep], slots[keep]
+    valid = slots >= 0
+    K, V, slots = K[valid], V[valid], slots[valid]
     n_tok, H, d = K.shape
     blocks, offs = np.divmod(slots, lay.P)
     out = {}
@@ -105,7 +106,8 @@ def compress_into_pool(K, V, slots, pool, layout, state):
         _scatter(pool, base + layout.off_vc + offs * layout.vc_bytes, bits.pack(cv["codes"], layout.v_bits))
         sz = np.stack([cv["scale16"], cv["zero16"]], axis=-1).reshape(n_tok, -1).view(np.uint8)
         _scatter(pool, base + layout.off_vsz + offs * layout.vsz_bytes, sz)
-        out[h] = (ck, cv)
+        if keep:
+            out[h] = (ck, cv)
     return out
 
 
