@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-KV hot path on one MI355X.
+
+Headline workload: a Llama-3-8B-shaped decode layer -- batch 16, 32 query / 8
+KV heads, head_dim 128, context 4096, bf16 N(0,1) K/V with 4 outlier channels
+per head scaled x10, keys 4-bit codebook + 1-bit QJL, values 4-bit groups of
+32, 16-token pages.  One step = compress each sequence's newest token into the
+paged store, then split-K decode attention over the whole context (all kernels
+of the path).  The store is rotated over several copies so the timed reads come
+from HBM and not from the 256 MB last-level cache.
+
+Also reported: fused compress throughput on 1,048,576 tokens x 8 heads (keys
+2-bit + QJL, values 3-bit), and the float64 CPU oracle timed on a bounded
+sample of the headline workload on this host.
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--pools", type=int, default=6, help="store copies rotated to defeat the cache")
+    ap.add_argument("--compress-iters", type=int, default=5)
+    ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def decode_workload(torch, tq, synth, args):
+    W = synth.WORKLOADS[2]
+    sd = synth.seeds(2)
+    B, Hq, Hkv, T = W["B"], W["Hq"], W["Hkv"], W["ctx"]
+    kb, vb = W["k_bits"], W["v_bits"]
+    layer = tq.Layer(tq.config(Hkv, kb, vb, seed=sd["state"]))
+    maxb = T // 16
+    table = synth.block_table(sd["table"], B, maxb, W["table"])
+    k, v = synth.kv_device(sd["data"], B * T, Hkv, outliers=W["outliers"])
+    pos = torch.arange(T, device="cuda").repeat(B)
+    seq = torch.arange(B, device="cuda").repeat_interleave(T)
+    bt = torch.from_numpy(table).cuda()
+    slots = bt[seq, pos // 16].long() * 16 + pos % 16
+    pool0 = layer.new_pool(B * maxb)
+    tq.compress_kv(layer, k, v, slots, pool0)
+    pools = [pool0] + [pool0.clone() for _ in range(args.pools - 1)]
+    last = torch.arange(B, device="cuda") * T + (T - 1)
+    k_new, v_new, slot_new = k[last].contiguous(), v[last].contiguous(), slots[last].contiguous()
+    q = torch.from_numpy(synth.queries_host(sd["data"], B, Hq)).to("cuda", torch.bfloat16)
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = tq.new_workspace(layer, B, Hq, T)
+    torch.cuda.synchronize()
+
+    def step(i):
+        p = pools[i % len(pools)]
+        tq.compress_kv(layer, k_new, v_new, slot_new, p)
+        tq.decode_attn(layer, q, p, bt, sl, T, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tq.profile_reset()
+    tq.profile_enable(1 << tq.K_SPLITK)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    sk_ms, sk_n = tq.profile_read(tq.K_SPLITK)
+    tq.profile_enable(0)
+    rec = W["k_bits"] * 16 + 16 + 4 + W["v_bits"] * 16 + 16
+    kv_bytes = B * T * Hkv * rec
+    # algorithmic bytes of one split-K launch: the KV records, the block-table
+    # entries, the sequence lengths and the rotated query/projection (f32) once
+    splitk_bytes = kv_bytes + B * maxb * 4 + B * 4 + B * Hq * 2 * 128 * 4
+    # whole step: + new-token K/V in (bf16) + their records out + q in + out
+    step_bytes = splitk_bytes + B * Hkv * (512 + rec) + B * 8 + B * Hq * 128 * 2 * 2
+    sk_avg_s = sk_ms / max(sk_n, 1) / 1e3
+    achieved = splitk_bytes / sk_avg_s / 1e9
+    res = {
+        "ms_per_step": ms,
+        "value": B / (ms / 1e3),
+        "kv_tok_s": B * T / (ms / 1e3),
+        "step_hbm_gbs": step_bytes / (ms / 1e3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "splitk_kernel<4,4,4>", "avg_us": round(sk_avg_s * 1e6, 3),
+                     "launches": sk_n, "bytes_per_launch": splitk_bytes},
+        "config": {"workload": W["name"], "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
+                   "context": T, "k_bits": kb, "qjl_bits": 1, "v_bits": vb, "v_group": 32, "page": 16,
+                   "outlier_channels": W["outliers"], "store_copies_rotated": len(pools)},
+    }
+    ctx = {"k": k, "v": v, "q": q, "table": table, "layer": layer, "W": W, "sd": sd}
+    return res, ctx
+
+
+def compress_workload(torch, tq, synth, args):
+    W = synth.WORKLOADS[3]
+    sd = synth.seeds(3)
+    N, H = W["N"], W["Hkv"]
+    layer = tq.Layer(tq.config(H, W["k_bits"], W["v_bits"], seed=sd["state"]))
+    k, v = synth.kv_device(sd["data"], N, H)
+    pool = layer.new_pool(N // 16)
+    slots = torch.arange(N, dtype=torch.int64, device="cuda")
+    tq.compress_kv(layer, k, v, slots, pool)
+    torch.cuda.synchronize()
+    tq.profile_reset()
+    tq.profile_enable(1 << tq.K_COMPRESS)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.compress_iters):
+        tq.compress_kv(layer, k, v, slots, pool)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.compress_iters
+    c_ms, c_n = tq.profile_read(tq.K_COMPRESS)
+    tq.profile_enable(0)
+    rec = W["k_bits"] * 16 + 20 + W["v_bits"] * 16 + 16
+    nbytes = N * H * (512 + rec) + N * 8
+    avg_s = c_ms / max(c_n, 1) / 1e3
+    layer.close()
+    del k, v, pool
+    return {"workload": W["name"], "tokens": N, "kv_heads": H, "k_bits": W["k_bits"], "v_bits": W["v_bits"],
+            "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "compress_kernel<bf16,2,3>",
+                         "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
+
+
+def cpu_baseline(torch, synth, ctx, budget_s):
+    """The float64 oracle on the headline workload, one sequence at a time, until
+    the time budget is spent.  Setup (compressing each sampled sequence's context)
+    is not timed; the timed part is the step: compress the newest token, decode."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import compress as ocomp, decode as odec, layout as olay, state as ostate
+
+    W, sd = ctx["W"], ctx["sd"]
+    B, Hq, Hkv, T = W["B"], W["Hq"], W["Hkv"], W["ctx"]
+    st = ostate.LayerState(sd["state"], 0, Hkv, 128, W["k_bits"], W["v_bits"], 32)
+    lay = olay.StoreLayout(128, W["k_bits"], W["v_bits"], 32)
+    maxb = T // 16
+    q = ctx["q"].float().cpu().numpy().astype(np.float64)
+    table = ctx["table"]
+    done, spent = 0, 0.0
+    with threadpool_limits(1):
+        for b in range(B):
+            K = ctx["k"][b * T:(b + 1) * T].float().cpu().numpy()
+            V = ctx["v"][b * T:(b + 1) * T].float().cpu().numpy()
+            pos = np.arange(T)
+            slots = table[b][pos // 16].astype(np.int64) * 16 + pos % 16
+            pool = olay.new_pool(B * maxb, Hkv, lay)
+            ocomp.compress_into_pool(K[:-1], V[:-1], slots[:-1], pool, lay, st, keep=False)
+            t0 = time.perf_counter()
+            ocomp.compress_into_pool(K[-1:], V[-1:], slots[-1:], pool, lay, st, keep=False)
+            odec.decode(q[b:b + 1], pool, lay, Hkv, table[b:b + 1], np.array([T]), st)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+    return {"value": round(done / spent, 3), "unit": "decode tok/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d sequences of the headline workload (float64 NumPy, one thread); "
+                      "timed: compress the newest token of 8 KV heads + decode 32 query heads over "
+                      "4096 tokens, per sequence" % (done, B),
+            "seconds": round(spent, 2), "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the compressed-KV path runs on one device per process and "
+              "this build has no multi-GPU path (--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import compressed_decode_attention_tq_amd as tq
+    from compressed_decode_attention_tq_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    tq.lib()
+    log("decode workload")
+    dec, ctx = decode_workload(torch, tq, synth, args)
+    comp = None
+    if not args.no_compress:
+        log("compress workload")
+        comp = compress_workload(torch, tq, synth, args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        cpu = cpu_baseline(torch, synth, ctx, args.cpu_budget_s)
+    line = {
+        "metric": "compressed-KV decode attn tokens/s + HBM GB/s (% of peak); compress Mtok/s",
+        "value": round(dec["value"], 1),
+        "unit": "decode tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) bf16 K/V with outlier channels)",
+        "config": dec["config"],
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "kv_tok_s": round(dec["kv_tok_s"], 1),
+        "step_hbm_gbs": round(dec["step_hbm_gbs"], 1),
+        "step_hbm_frac": round(dec["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
+        "compress": comp,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+"""Python binding of libtq (TurboQuant-style compressed KV cache for MI355X).
+
+Argument marshalling only: every step of compression and decode attention runs
+in the library's HIP kernels.  PyTorch supplies device memory and the current
+HIP stream.  If libtq.so is missing the calls raise; there is no fallback.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_HIP, ERR_NOT_CONVERGED = range(6)
+F32, BF16, F16 = 0, 1, 2
+DIST_GAUSSIAN, DIST_SPHERE = 0, 1
+EXPORTED = [
+    "tq_last_error", "tq_abi_version", "tq_codebook_build", "tq_layer_state_host",
+    "tq_layer_create", "tq_layer_destroy", "tq_store_layout", "tq_compress_kv",
+    "tq_decode_workspace_size", "tq_decode_attn", "tq_profile_enable", "tq_profile_read",
+    "tq_profile_reset",
+]
+K_COMPRESS, K_PROLOGUE, K_SPLITK, K_COMBINE = range(4)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("libtq status %d: %s" % (status, msg))
+        self.status = status
+
+
+class LayerConfig(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int), ("n_kv_heads", ctypes.c_int), ("k_bits", ctypes.c_int),
+        ("v_bits", ctypes.c_int), ("v_group", ctypes.c_int), ("block_size", ctypes.c_int),
+        ("layer", ctypes.c_int), ("dist", ctypes.c_int), ("seed", ctypes.c_ulonglong),
+        ("bypass", ctypes.c_int),
+    ]
+
+
+def config(n_kv_heads, k_bits=4, v_bits=4, seed=0, layer=0, dist=DIST_GAUSSIAN, bypass=False,
+           head_dim=128, v_group=32, block_size=16):
+    return LayerConfig(head_dim, n_kv_heads, k_bits, v_bits, v_group, block_size, layer, dist, seed,
+                       int(bool(bypass)))
+
+
+_LIB = None
+
+
+def lib():
+    """Load libtq.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtq.so not built: run `python -m compressed_decode_attention_tq_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_ll, c_size, vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_size_t, ctypes.c_void_p
+    dp, fp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)
+    L.tq_last_error.restype = ctypes.c_char_p
+    L.tq_abi_version.restype = c_int
+    L.tq_codebook_build.argtypes = [c_int, c_int, c_int, dp, dp, dp]
+    L.tq_layer_state_host.argtypes = [ctypes.POINTER(LayerConfig), fp, fp, fp, fp]
+    L.tq_layer_create.argtypes = [ctypes.POINTER(LayerConfig), vp, ctypes.POINTER(vp)]
+    L.tq_layer_destroy.argtypes = [vp]
+    L.tq_store_layout.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(c_size), ctypes.POINTER(c_size)]
+    L.tq_compress_kv.argtypes = [vp, vp, vp, c_int, c_ll, c_ll, c_ll, vp, vp, c_ll, vp]
+    L.tq_decode_workspace_size.argtypes = [vp, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)]
+    L.tq_decode_attn.argtypes = [vp, vp, c_int, c_int, c_int, vp, c_ll, vp, c_int, vp, c_int,
+                                 ctypes.c_float, c_int, vp, c_int, vp, c_size, vp]
+    L.tq_profile_enable.argtypes = [ctypes.c_uint]
+    L.tq_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_ll)]
+    L.tq_profile_reset.argtypes = []
+    for name in ["tq_codebook_build", "tq_layer_state_host", "tq_layer_create", "tq_layer_destroy",
+                 "tq_store_layout", "tq_compress_kv", "tq_decode_workspace_size", "tq_decode_attn",
+                 "tq_profile_enable", "tq_profile_read", "tq_profile_reset"]:
+        getattr(L, name).restype = c_int
+    _LIB = L
+    return L
+
+
+def _check(status):
+    if status != OK:
+        raise TQError(status, lib().tq_last_error().decode())
+
+
+def _dptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _fptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+# ------------------------------------------------------------------- host only
+def codebook_build(bits, dist=DIST_GAUSSIAN, dim=128):
+    L = 1 << bits
+    c = np.zeros(L)
+    b = np.zeros(max(L - 1, 1))
+    mse = ctypes.c_double(0.0)
+    _check(lib().tq_codebook_build(bits, dist, dim, _dptr(c), _dptr(b), ctypes.byref(mse)))
+    return c, b[: L - 1], mse.value
+
+
+def layer_state_host(cfg):
+    H, d = cfg.n_kv_heads, cfg.head_dim
+    R = np.zeros((H, d, d), np.float32)
+    S = np.zeros((H, d, d), np.float32)
+    nl = 0 if cfg.bypass else (1 << cfg.k_bits)
+    c = np.zeros(max(nl, 1), np.float32)
+    b = np.zeros(max(nl - 1, 1), np.float32)
+    _check(lib().tq_layer_state_host(ctypes.byref(cfg), _fptr(R), _fptr(S), _fptr(c), _fptr(b)))
+    return R, S, c[:nl], b[: max(nl - 1, 0)]
+
+
+def store_layout(cfg):
+    bb = ctypes.c_size_t(0)
+    offs = (ctypes.c_size_t * 5)()
+    _check(lib().tq_store_layout(ctypes.byref(cfg), ctypes.byref(bb), offs))
+    return bb.value, list(offs)
+
+
+# ------------------------------------------------------------------ device side
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float16:
+        return F16
+    raise TQError(ERR_UNSUPPORTED, "unsupported tensor dtype %s" % t.dtype)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Layer:
+    """Device state of one layer (R, S, codebook).  Owns it until close()."""
+
+    def __init__(self, cfg, stream=None):
+        self.cfg = cfg
+        self.handle = ctypes.c_void_p()
+        _check(lib().tq_layer_create(ctypes.byref(cfg), _stream(stream), ctypes.byref(self.handle)))
+        self.block_bytes, self.field_offsets = store_layout(cfg)
+
+    def close(self):
+        if self.handle:
+            _check(lib().tq_layer_destroy(self.handle))
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def new_pool(self, num_blocks):
+        torch = _torch()
+        return torch.zeros(num_blocks * self.cfg.n_kv_heads * self.block_bytes, dtype=torch.uint8, device="cuda")
+
+
+def compress_kv(layer, k, v, slot_mapping, pool, stream=None):
+    """k, v: [N, H_kv, 128] (f32 or bf16, token stride = k.stride(0)); slot_mapping int64 [N]."""
+    torch = _torch()
+    assert slot_mapping.dtype == torch.int64 and pool.dtype == torch.uint8
+    n = k.shape[0]
+    num_blocks = pool.numel() // (layer.cfg.n_kv_heads * layer.block_bytes)
+    _check(lib().tq_compress_kv(layer.handle, _ptr(k), _ptr(v), _dtype_code(k), n, k.stride(0), v.stride(0),
+                                _ptr(slot_mapping), _ptr(pool), num_blocks, _stream(stream)))
+
+
+def decode_workspace_size(layer, batch, n_q_heads, max_seq_len, num_splits=0):
+    out = ctypes.c_size_t(0)
+    _check(lib().tq_decode_workspace_size(layer.handle, batch, n_q_heads, max_seq_len, num_splits,
+                                          ctypes.byref(out)))
+    return out.value
+
+
+def new_workspace(layer, batch, n_q_heads, max_seq_len, num_splits=0):
+    torch = _torch()
+    nbytes = decode_workspace_size(layer, batch, n_q_heads, max_seq_len, num_splits)
+    return torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+
+def decode_attn(layer, q, pool, block_table, seq_lens, max_seq_len, out=None, workspace=None,
+                softmax_scale=0.0, num_splits=0, out_dtype=None, stream=None):
+    """q: [B, H_q, 128]; block_table int32 [B, max_blocks]; seq_lens int32 [B]."""
+    torch = _torch()
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    B, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=out_dtype or torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(layer, B, Hq, max_seq_len, num_splits)
+    num_blocks = pool.numel() // (layer.cfg.n_kv_heads * layer.block_bytes)
+    _check(lib().tq_decode_attn(layer.handle, _ptr(q), _dtype_code(q), B, Hq, _ptr(pool), num_blocks,
+                                _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
+                                float(softmax_scale), num_splits, _ptr(out), _dtype_code(out),
+                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------- profiling
+def profile_enable(mask):
+    _check(lib().tq_profile_enable(mask))
+
+
+def profile_read(kernel):
+    """(total milliseconds, launches) of the timed launches of `kernel` since the last reset."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_longlong(0)
+    _check(lib().tq_profile_read(kernel, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def profile_reset():
+    _check(lib().tq_profile_reset())

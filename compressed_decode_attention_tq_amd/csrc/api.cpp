@@ -1,0 +1,360 @@
+// C ABI of libtq: argument validation, layer state, store layout and decode
+// planning.  Kernels live in compress.hip and decode.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "tq_internal.hpp"
+
+namespace tq {
+
+namespace {
+thread_local std::string g_error;
+}
+
+tq_status fail(tq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+void clear_error() { g_error.clear(); }
+
+tq_status validate_config(const tq_layer_config* cfg) {
+  if (!cfg) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer config");
+  if (cfg->head_dim != kDim)
+    return fail(TQ_ERR_UNSUPPORTED, "head_dim %d not supported (only %d)", cfg->head_dim, kDim);
+  if (cfg->n_kv_heads < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "n_kv_heads must be >= 1");
+  if (cfg->block_size != kPage)
+    return fail(TQ_ERR_UNSUPPORTED, "block_size %d not supported (only %d)", cfg->block_size, kPage);
+  if (cfg->layer < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "layer index must be >= 0");
+  if (cfg->bypass) return TQ_OK;
+  if (cfg->k_bits < 2 || cfg->k_bits > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "k_bits %d not supported (2..4)", cfg->k_bits);
+  if (cfg->v_bits < 2 || cfg->v_bits > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "v_bits %d not supported (2..4)", cfg->v_bits);
+  if (cfg->v_group != kGroup)
+    return fail(TQ_ERR_UNSUPPORTED, "v_group %d not supported (only %d)", cfg->v_group, kGroup);
+  if (cfg->dist != TQ_DIST_GAUSSIAN && cfg->dist != TQ_DIST_SPHERE)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "unknown codebook density %d", static_cast<int>(cfg->dist));
+  return TQ_OK;
+}
+
+tq_status make_layout(const tq_layer_config* cfg, Layout* out) {
+  tq_status st = validate_config(cfg);
+  if (st != TQ_OK) return st;
+  Layout l;
+  if (cfg->bypass) {
+    l.bypass = true;
+    l.off_kc = 0;                              // K [16][128] bf16
+    l.off_vc = static_cast<size_t>(kPage) * kDim * 2;   // V [16][128] bf16
+    l.block_bytes = 2 * l.off_vc;
+    *out = l;
+    return TQ_OK;
+  }
+  l.k_bits = cfg->k_bits;
+  l.v_bits = cfg->v_bits;
+  l.kc_bytes = kDim * cfg->k_bits / 8;
+  l.ks_bytes = kDim / 8;
+  l.kn_bytes = 4;
+  l.vc_bytes = kDim * cfg->v_bits / 8;
+  l.vsz_bytes = 4 * (kDim / kGroup);
+  size_t o = 0;
+  l.off_kc = o; o += static_cast<size_t>(kPage) * l.kc_bytes;
+  l.off_ks = o; o += static_cast<size_t>(kPage) * l.ks_bytes;
+  l.off_kn = o; o += static_cast<size_t>(kPage) * l.kn_bytes;
+  l.off_vc = o; o += static_cast<size_t>(kPage) * l.vc_bytes;
+  l.off_vsz = o; o += static_cast<size_t>(kPage) * l.vsz_bytes;
+  l.block_bytes = o;
+  *out = l;
+  return TQ_OK;
+}
+
+namespace {
+
+// Host state of one layer: R, S (float32, [H][d][d]) and the float32 codebook.
+tq_status build_state(const tq_layer_config* cfg, std::vector<float>* R, std::vector<float>* S,
+                      float* cent, float* bnd, int* levels) {
+  const int d = kDim, H = cfg->n_kv_heads;
+  if (R) R->resize(static_cast<size_t>(H) * d * d);
+  if (S) S->resize(static_cast<size_t>(H) * d * d);
+  std::vector<double> tmp(static_cast<size_t>(d) * d);
+  for (int h = 0; h < H; ++h) {
+    if (R) {
+      haar_rotation(cfg->seed, cfg->layer, h, d, tmp.data());
+      for (size_t i = 0; i < tmp.size(); ++i) (*R)[h * tmp.size() + i] = static_cast<float>(tmp[i]);
+    }
+    if (S) {
+      gaussians(cfg->seed, static_cast<uint64_t>(cfg->layer), static_cast<uint64_t>(h),
+                kTagProjection, tmp.size(), tmp.data());
+      for (size_t i = 0; i < tmp.size(); ++i) (*S)[h * tmp.size() + i] = static_cast<float>(tmp[i]);
+    }
+  }
+  *levels = 0;
+  if (!cfg->bypass) {
+    double c[256], b[255];
+    tq_status st = lloyd_max(cfg->k_bits, cfg->dist, d, c, b, nullptr);
+    if (st != TQ_OK) return st;
+    const int L = 1 << cfg->k_bits;
+    for (int i = 0; i < L; ++i) cent[i] = static_cast<float>(c[i]);
+    for (int i = 0; i + 1 < L; ++i) bnd[i] = static_cast<float>(b[i]);
+    *levels = L;
+  }
+  return TQ_OK;
+}
+
+tq_status hip_fail(hipError_t e, const char* what) {
+  return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int env_splits() {
+  const char* s = std::getenv("TQ_DECODE_SPLITS");
+  if (!s || !*s) return 0;
+  const int v = std::atoi(s);
+  return v > 0 ? v : 0;
+}
+
+}  // namespace
+
+tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_len, int num_splits,
+                      DecodePlan* plan) {
+  DecodePlan p;
+  p.batch = batch;
+  p.n_q_heads = n_q_heads;
+  p.rep = n_q_heads / L->cfg.n_kv_heads;
+  const int ctx = max_seq_len > 0 ? max_seq_len : 1;
+  const int ctx64 = (ctx + 63) / 64 * 64;
+  int splits = num_splits > 0 ? num_splits : env_splits();
+  int split_tokens;
+  if (splits > 0) {
+    split_tokens = ((ctx + splits - 1) / splits + 63) / 64 * 64;
+  } else {
+    // Automatic: aim for ~4 workgroups per CU over (batch x kv_heads x splits),
+    // each split 256..4096 tokens (whole 64-token chunks).
+    const long long pairs = static_cast<long long>(batch) * L->cfg.n_kv_heads;
+    const long long target = 4LL * (L->cu_count > 0 ? L->cu_count : 256);
+    const long long want = pairs > 0 ? (target + pairs - 1) / pairs : 1;
+    long long t = (ctx + want - 1) / want;
+    t = (t + 63) / 64 * 64;
+    if (t < 256) t = 256;
+    if (t > 4096) t = 4096;
+    if (t > ctx64) t = ctx64;
+    split_tokens = static_cast<int>(t);
+  }
+  p.split_tokens = split_tokens;
+  p.n_splits = (ctx + split_tokens - 1) / split_tokens;
+  const size_t bh = static_cast<size_t>(batch) * n_q_heads;
+  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.ws_qu = 0;
+  p.ws_part = align(bh * 2 * kDim * sizeof(float));
+  p.ws_bytes = p.ws_part + align(bh * static_cast<size_t>(p.n_splits) * (kDim + 4) * sizeof(float));
+  if (p.ws_bytes == 0) p.ws_bytes = 256;
+  *plan = p;
+  return TQ_OK;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_error.c_str(); }
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids, double* boundaries,
+                            double* mse) {
+  clear_error();
+  if (bits < 1 || bits > 8) return fail(TQ_ERR_INVALID_ARGUMENT, "codebook bits must be 1..8, got %d", bits);
+  if (!centroids || (bits > 0 && !boundaries)) return fail(TQ_ERR_INVALID_ARGUMENT, "null codebook output");
+  double c[256], b[255];
+  tq_status st = lloyd_max(bits, dist, dim, c, b, mse);
+  if (st != TQ_OK) return st;
+  const int L = 1 << bits;
+  std::memcpy(centroids, c, sizeof(double) * L);
+  std::memcpy(boundaries, b, sizeof(double) * (L - 1));
+  return TQ_OK;
+}
+
+tq_status tq_store_layout(const tq_layer_config* cfg, size_t* block_bytes, size_t* field_offsets) {
+  clear_error();
+  if (!block_bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "null block_bytes");
+  Layout l;
+  tq_status st = make_layout(cfg, &l);
+  if (st != TQ_OK) return st;
+  *block_bytes = l.block_bytes;
+  if (field_offsets) {
+    if (l.bypass) {
+      field_offsets[0] = l.off_kc; field_offsets[1] = l.off_vc;
+      field_offsets[2] = field_offsets[3] = field_offsets[4] = 0;
+    } else {
+      field_offsets[0] = l.off_kc; field_offsets[1] = l.off_ks; field_offsets[2] = l.off_kn;
+      field_offsets[3] = l.off_vc; field_offsets[4] = l.off_vsz;
+    }
+  }
+  return TQ_OK;
+}
+
+tq_status tq_layer_state_host(const tq_layer_config* cfg, float* R, float* S, float* centroids,
+                              float* boundaries) {
+  clear_error();
+  tq_status st = validate_config(cfg);
+  if (st != TQ_OK) return st;
+  std::vector<float> r, s;
+  float c[256], b[256];
+  int levels = 0;
+  st = build_state(cfg, R ? &r : nullptr, S ? &s : nullptr, c, b, &levels);
+  if (st != TQ_OK) return st;
+  if (R) std::memcpy(R, r.data(), r.size() * sizeof(float));
+  if (S) std::memcpy(S, s.data(), s.size() * sizeof(float));
+  if (centroids && levels) std::memcpy(centroids, c, levels * sizeof(float));
+  if (boundaries && levels) std::memcpy(boundaries, b, (levels - 1) * sizeof(float));
+  return TQ_OK;
+}
+
+tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer** out) {
+  clear_error();
+  if (!out) return fail(TQ_ERR_INVALID_ARGUMENT, "null output pointer");
+  *out = nullptr;
+  tq_layer* L = new tq_layer();
+  tq_status st = make_layout(cfg, &L->lay);
+  if (st != TQ_OK) { delete L; return st; }
+  L->cfg = *cfg;
+  std::vector<float> R, S;
+  st = build_state(cfg, &R, cfg->bypass ? nullptr : &S, L->centroids, L->boundaries, &L->levels);
+  if (st != TQ_OK) { delete L; return st; }
+  hipError_t e = hipGetDevice(&L->device);
+  if (e != hipSuccess) { delete L; return hip_fail(e, "hipGetDevice"); }
+  e = hipDeviceGetAttribute(&L->cu_count, hipDeviceAttributeMultiprocessorCount, L->device);
+  if (e != hipSuccess) { delete L; return hip_fail(e, "hipDeviceGetAttribute"); }
+  if (!cfg->bypass) {
+    const int d = kDim, H = cfg->n_kv_heads;
+    const size_t n = static_cast<size_t>(H) * d * d;
+    std::vector<float> RT(n), ST(n);
+    for (int h = 0; h < H; ++h)
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+          RT[(static_cast<size_t>(h) * d + j) * d + i] = R[(static_cast<size_t>(h) * d + i) * d + j];
+          ST[(static_cast<size_t>(h) * d + j) * d + i] = S[(static_cast<size_t>(h) * d + i) * d + j];
+        }
+    float** bufs[3] = {&L->dR, &L->dRT, &L->dST};
+    const std::vector<float>* src[3] = {&R, &RT, &ST};
+    for (int i = 0; i < 3; ++i) {
+      e = hipMalloc(reinterpret_cast<void**>(bufs[i]), n * sizeof(float));
+      if (e != hipSuccess) {
+        tq_layer_destroy(L);
+        return fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc of layer state failed: %s", hipGetErrorString(e));
+      }
+      e = hipMemcpyAsync(*bufs[i], src[i]->data(), n * sizeof(float), hipMemcpyHostToDevice,
+                         static_cast<hipStream_t>(hip_stream));
+      if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
+    }
+    e = hipStreamSynchronize(static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipStreamSynchronize"); }
+  }
+  *out = L;
+  return TQ_OK;
+}
+
+tq_status tq_layer_destroy(tq_layer* L) {
+  clear_error();
+  if (!L) return TQ_OK;
+  hipError_t e1 = L->dR ? hipFree(L->dR) : hipSuccess;
+  hipError_t e2 = L->dRT ? hipFree(L->dRT) : hipSuccess;
+  hipError_t e3 = L->dST ? hipFree(L->dST) : hipSuccess;
+  delete L;
+  if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
+  if (e3 != hipSuccess) return hip_fail(e3, "hipFree");
+  return TQ_OK;
+}
+
+tq_status tq_compress_kv(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype,
+                         long long n_tokens, long long k_token_stride, long long v_token_stride,
+                         const long long* slot_mapping, void* pool, long long num_blocks,
+                         void* hip_stream) {
+  clear_error();
+  if (!L) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer");
+  if (n_tokens < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0");
+  if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
+  const long long row = static_cast<long long>(L->cfg.n_kv_heads) * kDim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "token strides must be >= n_kv_heads*128 (got %lld, %lld)",
+                k_token_stride, v_token_stride);
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "compress input dtype %d not supported (F32, BF16)", static_cast<int>(in_dtype));
+  if (L->cfg.bypass && in_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "bypass layers store bf16: input dtype must be BF16");
+  if (n_tokens == 0) return TQ_OK;
+  if (!k || !v || !slot_mapping || !pool) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
+  return launch_compress(L, k, v, in_dtype, n_tokens, k_token_stride, v_token_stride, slot_mapping,
+                         pool, hip_stream);
+}
+
+tq_status tq_decode_workspace_size(const tq_layer* L, int batch, int n_q_heads, int max_seq_len,
+                                   int num_splits, size_t* bytes) {
+  clear_error();
+  if (!L || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "null argument");
+  if (batch < 0 || n_q_heads <= 0 || max_seq_len < 0 || num_splits < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "negative size");
+  DecodePlan p;
+  tq_status st = plan_decode(L, batch, n_q_heads, max_seq_len, num_splits, &p);
+  if (st != TQ_OK) return st;
+  *bytes = p.ws_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_decode_attn(const tq_layer* L, const void* q, tq_dtype q_dtype, int batch,
+                         int n_q_heads, const void* pool, long long num_blocks,
+                         const int* block_table, int max_blocks_per_seq, const int* seq_lens,
+                         int max_seq_len, float softmax_scale, int num_splits, void* out,
+                         tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+  clear_error();
+  if (!L) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer");
+  if (batch < 0 || n_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_blocks_per_seq < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "negative size");
+  if (n_q_heads % L->cfg.n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
+                L->cfg.n_kv_heads);
+  const int rep = n_q_heads / L->cfg.n_kv_heads;
+  if (rep != 1 && rep != 2 && rep != 4 && rep != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head = %d not supported (1, 2, 4, 8)", rep);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "query dtype %d not supported (F32, BF16)", static_cast<int>(q_dtype));
+  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
+  if (static_cast<long long>(max_blocks_per_seq) * kPage < max_seq_len)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "max_blocks_per_seq*16 = %lld < max_seq_len %d",
+                static_cast<long long>(max_blocks_per_seq) * kPage, max_seq_len);
+  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (batch == 0) return TQ_OK;
+  if (!q || !pool || !block_table || !seq_lens || !out || !workspace)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  DecodePlan p;
+  tq_status st = plan_decode(L, batch, n_q_heads, max_seq_len, num_splits, &p);
+  if (st != TQ_OK) return st;
+  if (workspace_bytes < p.ws_bytes)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", workspace_bytes, p.ws_bytes);
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kDim));
+  return launch_decode(L, p, q, q_dtype, pool, block_table, max_blocks_per_seq, seq_lens, scale, out,
+                       out_dtype, workspace, hip_stream);
+}
+
+}  // extern "C"

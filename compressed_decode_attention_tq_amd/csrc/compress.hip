@@ -1,0 +1,262 @@
+// Fused K+V compression into the paged store (gfx950).
+//
+// Keys ("How 0xsero/turboquant works", "Compression Pipeline"; "turbo-attn
+// 0.24.0", "How it works"; "5x Faster LLM Inference? ...", "Example 4:
+// Kernel-Level Operations"):
+//   n = ||k||, t = sqrt(d) R k / n, idx_j = #{i : beta_i < t_j},
+//   rho = t - c[idx], gamma = ||rho||, z_j = [(S rho)_j >= 0];
+//   stored: packed idx, packed z, fp16 n, fp16 gamma.
+// Values ("How 0xsero/turboquant works", "Value Compression"; "tiny-turboquant
+// 0.18.0", "Measured quality": groups of 32 with their own scale/zero):
+//   v' = R v; per 32-wide group scale = fp16((max-min)/(2^b-1)), zero = fp16(min),
+//   code = clamp(rint((v' - zero)/scale), 0, 2^b-1)  (0 when scale == 0).
+//
+// One workgroup of 128 lanes per (token, KV head); lane i owns coordinate i.
+// Dot products accumulate in eight interleaved float32 partial sums.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+
+struct CompressArgs {
+  const void* k;
+  const void* v;
+  long long k_stride;
+  long long v_stride;
+  const long long* slots;
+  unsigned char* pool;
+  const float* RT;  // [H][128][128], RT[h][j][i] = R_h[i][j]
+  const float* ST;  // [H][128][128], ST[h][j][i] = S_h[i][j]
+  int H;
+  unsigned block_bytes;
+  unsigned off_kc, off_ks, off_kn, off_vc, off_vsz;
+  float cent[16];
+  float bnd[16];
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, long long idx) {
+  if constexpr (BF16) {
+    const unsigned short b = static_cast<const unsigned short*>(p)[idx];
+    return __uint_as_float(static_cast<unsigned>(b) << 16);
+  } else {
+    return static_cast<const float*>(p)[idx];
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Sum over the 128 lanes of the workgroup; every lane gets the result.
+__device__ __forceinline__ float block_sum128(float x, float* scratch2) {
+  x = wave_sum(x);
+  if ((threadIdx.x & 63) == 0) scratch2[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = scratch2[0] + scratch2[1];
+  __syncthreads();
+  return r;
+}
+
+// 32-bit word w of the LSB-first bitstream of 128 b-bit codes.
+template <int B>
+__device__ __forceinline__ unsigned pack_word(const unsigned char* codes, int w) {
+  unsigned word = 0;
+  const int first = (32 * w) / B;
+  const int last = (32 * w + 31) / B;
+  for (int j = first; j <= last && j < 128; ++j) {
+    const int shift = B * j - 32 * w;
+    const unsigned c = codes[j];
+    word |= (shift >= 0) ? (c << shift) : (c >> (-shift));
+  }
+  return word;
+}
+
+// Dot product of column i of a transposed 128x128 matrix with x (in LDS):
+// sum_j M[i][j] x[j], eight interleaved partial sums.
+__device__ __forceinline__ float matvec_row(const float* __restrict__ MT, const float* x, int i) {
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
+  for (int j = 0; j < 128; j += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = fmaf(MT[(j + u) * 128 + i], x[j + u], acc[u]);
+  }
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+template <bool BF16, int KB, int VB>
+__global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
+  const long long tok = blockIdx.x;
+  const int h = blockIdx.y;
+  const int i = threadIdx.x;
+  const long long slot = a.slots[tok];
+  if (slot < 0) return;
+
+  __shared__ float sk[128], sv[128], srho[128], red[2];
+  __shared__ unsigned char ck[128], cv[128];
+  __shared__ unsigned sbits[4];
+  __shared__ __half sgroup[8];
+
+  const float kx = load_elem<BF16>(a.k, tok * a.k_stride + h * 128 + i);
+  const float vx = load_elem<BF16>(a.v, tok * a.v_stride + h * 128 + i);
+  sk[i] = kx;
+  sv[i] = vx;
+  const float n2 = block_sum128(kx * kx, red);  // also orders the sk/sv writes
+
+  const float* RT = a.RT + static_cast<size_t>(h) * 128 * 128;
+  const float* ST = a.ST + static_cast<size_t>(h) * 128 * 128;
+  const float rk = matvec_row(RT, sk, i);
+  const float rv = matvec_row(RT, sv, i);
+
+  // keys: standardise, quantise, residual
+  const float n = sqrtf(n2);
+  const float t = (n > 0.0f) ? rk * (sqrtf(128.0f) / n) : 0.0f;
+  int idx = 0;
+#pragma unroll
+  for (int b = 0; b < (1 << KB) - 1; ++b) idx += (a.bnd[b] < t) ? 1 : 0;
+  const float rho = t - a.cent[idx];
+  ck[i] = static_cast<unsigned char>(idx);
+  srho[i] = rho;
+  const float g2 = block_sum128(rho * rho, red);
+  const float y = matvec_row(ST, srho, i);
+  const unsigned long long bal = __ballot(y >= 0.0f);
+  if ((i & 63) == 0) {
+    sbits[(i >> 6) * 2] = static_cast<unsigned>(bal);
+    sbits[(i >> 6) * 2 + 1] = static_cast<unsigned>(bal >> 32);
+  }
+
+  // values: group min/max over 32 lanes
+  float mn = rv, mx = rv;
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+  }
+  constexpr float top = static_cast<float>((1 << VB) - 1);
+  const __half s16 = __float2half_rn((mx - mn) / top);
+  const __half z16 = __float2half_rn(mn);
+  const float s = __half2float(s16);
+  const float z = __half2float(z16);
+  int code = 0;
+  if (s > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((rv - z) / s), 0.0f), top));
+  cv[i] = static_cast<unsigned char>(code);
+  if ((i & 31) == 0) {
+    sgroup[(i >> 5) * 2] = s16;
+    sgroup[(i >> 5) * 2 + 1] = z16;
+  }
+  __syncthreads();
+
+  unsigned char* base = a.pool + (static_cast<size_t>(slot >> 4) * a.H + h) * a.block_bytes;
+  const int off = static_cast<int>(slot & 15);
+  if (i < 4 * KB) {
+    reinterpret_cast<unsigned*>(base + a.off_kc + off * (16 * KB))[i] = pack_word<KB>(ck, i);
+  } else if (i >= 32 && i < 32 + 4 * VB) {
+    reinterpret_cast<unsigned*>(base + a.off_vc + off * (16 * VB))[i - 32] = pack_word<VB>(cv, i - 32);
+  } else if (i >= 64 && i < 68) {
+    reinterpret_cast<unsigned*>(base + a.off_ks + off * 16)[i - 64] = sbits[i - 64];
+  } else if (i == 68) {
+    const __half hn = __float2half_rn(n);
+    const __half hg = __float2half_rn(sqrtf(g2));
+    const unsigned w = static_cast<unsigned>(__half_as_ushort(hn)) |
+                       (static_cast<unsigned>(__half_as_ushort(hg)) << 16);
+    *reinterpret_cast<unsigned*>(base + a.off_kn + off * 4) = w;
+  } else if (i >= 72 && i < 76) {
+    const int g = i - 72;
+    const unsigned w = static_cast<unsigned>(__half_as_ushort(sgroup[2 * g])) |
+                       (static_cast<unsigned>(__half_as_ushort(sgroup[2 * g + 1])) << 16);
+    reinterpret_cast<unsigned*>(base + a.off_vsz + off * 16)[g] = w;
+  }
+}
+
+// Uncompressed (bf16) layers: copy one (token, head) of K and V into the page.
+__global__ __launch_bounds__(64) void store_bypass_kernel(const unsigned short* k, const unsigned short* v,
+                                                          long long k_stride, long long v_stride,
+                                                          const long long* slots, unsigned char* pool,
+                                                          int H, unsigned block_bytes) {
+  const long long tok = blockIdx.x;
+  const int h = blockIdx.y;
+  const long long slot = slots[tok];
+  if (slot < 0) return;
+  const int i = threadIdx.x;  // 2 elements each
+  unsigned char* base = pool + (static_cast<size_t>(slot >> 4) * H + h) * block_bytes;
+  const int off = static_cast<int>(slot & 15);
+  const unsigned* ks = reinterpret_cast<const unsigned*>(k + tok * k_stride + h * 128);
+  const unsigned* vs = reinterpret_cast<const unsigned*>(v + tok * v_stride + h * 128);
+  reinterpret_cast<unsigned*>(base + off * 256)[i] = ks[i];
+  reinterpret_cast<unsigned*>(base + 4096 + off * 256)[i] = vs[i];
+}
+
+template <bool BF16, int KB>
+void* pick_vb(int vb) {
+  switch (vb) {
+    case 2: return reinterpret_cast<void*>(&compress_kernel<BF16, KB, 2>);
+    case 3: return reinterpret_cast<void*>(&compress_kernel<BF16, KB, 3>);
+    case 4: return reinterpret_cast<void*>(&compress_kernel<BF16, KB, 4>);
+  }
+  return nullptr;
+}
+
+template <bool BF16>
+void* pick(int kb, int vb) {
+  switch (kb) {
+    case 2: return pick_vb<BF16, 2>(vb);
+    case 3: return pick_vb<BF16, 3>(vb);
+    case 4: return pick_vb<BF16, 4>(vb);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype,
+                          long long n_tokens, long long k_stride, long long v_stride,
+                          const long long* slots, void* pool, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tokens * 128 >= (1LL << 32)) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
+  const dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(L->cfg.n_kv_heads));
+  ProfScope prof(kKCompress, stream);
+  if (L->cfg.bypass) {
+    if ((k_stride | v_stride) & 1)
+      return fail(TQ_ERR_UNSUPPORTED, "bypass compress needs even token strides");
+    hipLaunchKernelGGL(store_bypass_kernel, grid, dim3(64), 0, s,
+                       static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
+                       k_stride, v_stride, slots, static_cast<unsigned char*>(pool),
+                       L->cfg.n_kv_heads, static_cast<unsigned>(L->lay.block_bytes));
+  } else {
+    CompressArgs a;
+    a.k = k;
+    a.v = v;
+    a.k_stride = k_stride;
+    a.v_stride = v_stride;
+    a.slots = slots;
+    a.pool = static_cast<unsigned char*>(pool);
+    a.RT = L->dRT;
+    a.ST = L->dST;
+    a.H = L->cfg.n_kv_heads;
+    a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
+    a.off_kc = static_cast<unsigned>(L->lay.off_kc);
+    a.off_ks = static_cast<unsigned>(L->lay.off_ks);
+    a.off_kn = static_cast<unsigned>(L->lay.off_kn);
+    a.off_vc = static_cast<unsigned>(L->lay.off_vc);
+    a.off_vsz = static_cast<unsigned>(L->lay.off_vsz);
+    for (int i = 0; i < 16; ++i) {
+      a.cent[i] = L->centroids[i];
+      a.bnd[i] = L->boundaries[i];
+    }
+    void* fn = (in_dtype == TQ_BF16) ? pick<true>(L->cfg.k_bits, L->cfg.v_bits)
+                                     : pick<false>(L->cfg.k_bits, L->cfg.v_bits);
+    if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
+    void* args[] = {&a};
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(128), args, 0, s);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
+  return TQ_OK;
+}
+
+}  // namespace tq

@@ -1,0 +1,99 @@
+// Internal declarations shared by the host code and the kernel launchers of libtq.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kDim = 128;     // head_dim supported by the kernels
+constexpr int kPage = 16;     // tokens per block
+constexpr int kGroup = 32;    // value group width
+
+// ---------------------------------------------------------------- errors
+tq_status fail(tq_status st, const char* fmt, ...);
+void clear_error();
+
+// ------------------------------------------------------------ random state
+uint64_t mix64(uint64_t z);
+uint64_t stream_key(uint64_t seed, uint64_t layer, uint64_t head, uint64_t tag);
+void gaussians(uint64_t seed, uint64_t layer, uint64_t head, uint64_t tag, size_t count,
+               double* out);
+constexpr uint64_t kTagRotation = 1;
+constexpr uint64_t kTagProjection = 2;
+
+// Haar rotation (row-major d x d, float64) for (seed, layer, head).
+void haar_rotation(uint64_t seed, int layer, int head, int d, double* out);
+
+// Lloyd-Max codebook; returns TQ_OK or an error status.
+tq_status lloyd_max(int bits, tq_dist dist, int dim, double* centroids, double* boundaries,
+                    double* mse);
+
+// ---------------------------------------------------------------- layout
+struct Layout {
+  bool bypass = false;
+  int k_bits = 0, v_bits = 0;
+  int kc_bytes = 0, ks_bytes = 0, kn_bytes = 0, vc_bytes = 0, vsz_bytes = 0;  // per token
+  size_t off_kc = 0, off_ks = 0, off_kn = 0, off_vc = 0, off_vsz = 0;         // per block
+  size_t block_bytes = 0;
+};
+tq_status make_layout(const tq_layer_config* cfg, Layout* out);
+tq_status validate_config(const tq_layer_config* cfg);
+
+// ------------------------------------------------------------- profiling
+enum KernelId { kKCompress = 0, kKPrologue = 1, kKSplitK = 2, kKCombine = 3, kKCount = 4 };
+// Brackets one launch with HIP events when timing of `id` is enabled.
+class ProfScope {
+ public:
+  ProfScope(int id, void* stream);
+  ~ProfScope();
+
+ private:
+  int slot_ = -1;
+  void* stream_;
+};
+
+}  // namespace tq
+
+// ------------------------------------------------------------------ layer
+struct tq_layer {
+  tq_layer_config cfg;
+  tq::Layout lay;
+  int device = 0;
+  int cu_count = 0;
+  // Device state (float32).  R and S row-major [H][128][128]; RT = R^T per head.
+  float* dR = nullptr;
+  float* dRT = nullptr;
+  float* dST = nullptr;
+  float centroids[16] = {0};
+  float boundaries[16] = {0};
+  int levels = 0;
+};
+
+namespace tq {
+
+// Kernel launchers (defined in the .hip files).  Arguments already validated.
+tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype,
+                          long long n_tokens, long long k_stride, long long v_stride,
+                          const long long* slots, void* pool, void* stream);
+
+struct DecodePlan {
+  int batch = 0, n_q_heads = 0, rep = 0;
+  int split_tokens = 0;   // tokens per split (multiple of 64)
+  int n_splits = 0;       // splits per sequence (grid x)
+  size_t ws_qu = 0;       // byte offset of q'/u in the workspace
+  size_t ws_part = 0;     // byte offset of split partials
+  size_t ws_bytes = 0;    // total
+};
+tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_len,
+                      int num_splits, DecodePlan* plan);
+tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
+                        const void* pool, const int* block_table, int max_blocks_per_seq,
+                        const int* seq_lens, float softmax_scale, void* out, tq_dtype out_dtype,
+                        void* workspace, void* stream);
+
+}  // namespace tq

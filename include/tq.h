@@ -1,0 +1,217 @@
+/*
+ * tq.h -- C ABI of libtq, TurboQuant-style compressed KV cache for MI355X (gfx950).
+ *
+ * Two operations, both hand-written HIP kernels for gfx950:
+ *
+ *  1. tq_compress_kv: fused compression of key/value head vectors into a paged
+ *     store.  Keys: norm, random orthogonal rotation, Lloyd-Max scalar codebook,
+ *     1-bit QJL sign of the residual.  Values: the same rotation, then group
+ *     scale/zero low-bit quantisation.  All payloads bit-packed.
+ *       - "How 0xsero/turboquant works", sections "Compression Pipeline" and
+ *         "Value Compression".
+ *       - "5x Faster LLM Inference? This KV Cache Hack Changes Everything",
+ *         "Example 4: Kernel-Level Operations" (normalise, rotate, Lloyd-Max
+ *         quantise, pack; one fused launch for K and V).
+ *       - "turbo-attn 0.24.0" (PyPI), "How it works" (rotate, store the
+ *         magnitude, quantise to a shared codebook).
+ *
+ *  2. tq_decode_attn: split-K paged decode attention that scores queries against
+ *     the compressed keys and accumulates the compressed values, dequantising
+ *     inside the loop (no expanded float cache).
+ *       - "turbo-attn 0.24.0", "How it works" (query rotated once, attention in
+ *         the rotated space, one fused unpack/dequant/QK/online-softmax/PV pass)
+ *         and "Configuration" (TKV_DECODE_SPLITS: split count autotuned or forced;
+ *         TKV_NO_JIT: a missing variant is a hard error).
+ *       - "How 0xsero/turboquant works", "Key Storage and Attention Scoring".
+ *       - "tiny-turboquant 0.18.0", "Fused decode-attention path" (a partials
+ *         launch, then a combine launch).
+ *
+ * Conventions
+ *   - Every function returns tq_status; TQ_OK == 0.  On any other status a
+ *     thread-local message is available from tq_last_error().  Nothing is ever
+ *     silently degraded: an unsupported variant is TQ_ERR_UNSUPPORTED.
+ *   - "device pointer" means memory on the current HIP device (hipMalloc,
+ *     torch CUDA tensors); "host pointer" means ordinary CPU memory.
+ *   - The caller owns every buffer passed in.  The library owns only tq_layer
+ *     objects (rotation, projection and codebook state on the device).
+ *   - Host-visible arguments are validated synchronously.  Kernels are enqueued
+ *     asynchronously on the caller's stream (hipStream_t passed as void*, NULL =
+ *     the null stream); a launch failure is reported as TQ_ERR_HIP.  The compress
+ *     and decode entry points never allocate and never synchronise.
+ *   - Contents of device buffers (slot ids, block ids, sequence lengths) are the
+ *     caller's contract; they are not range-checked on the device.
+ *   - Supported: head_dim = 128, block_size = 16, v_group = 32,
+ *     k_bits in {2,3,4}, v_bits in {2,3,4}, query heads per KV head in {1,2,4,8}.
+ *
+ * Store format (one pool per layer; exported by tq_store_layout)
+ *   pool = uint8[num_blocks][n_kv_heads][block_bytes], 16 tokens per block,
+ *   slot = block * 16 + offset.  Inside one (block, head) region, five
+ *   token-major fields:
+ *     Kc  [16][16*k_bits]  key codebook indices, LSB-first bitstream
+ *                          (index j at bits [k_bits*j, k_bits*j + k_bits))
+ *     Ks  [16][16]         QJL sign bits, bit j = 1 <=> (S rho)_j >= 0
+ *     Kn  [16][2] fp16     ||k|| then gamma = ||rho||
+ *     Vc  [16][16*v_bits]  value codes, LSB-first bitstream
+ *     Vsz [16][4][2] fp16  per 32-wide group: scale then zero
+ *   Bypass (uncompressed) layers: region = K [16][128] bf16, then V [16][128] bf16.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent sizes     */
+  TQ_ERR_UNSUPPORTED = 2,      /* a shape / bit width / dtype this build has no kernel for */
+  TQ_ERR_OUT_OF_MEMORY = 3,    /* device allocation in tq_layer_create failed         */
+  TQ_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed           */
+  TQ_ERR_NOT_CONVERGED = 5     /* Lloyd-Max iteration hit its iteration cap           */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* Density the key codebook is optimal for, in units of the standardised rotated
+ * coordinate t = sqrt(d) (R k)_j / ||k||:
+ *   TQ_DIST_GAUSSIAN: N(0,1)   ("5x Faster LLM Inference? ...", "What is TurboQuant-GPU?":
+ *                               rotated coordinates are approximately Gaussian)
+ *   TQ_DIST_SPHERE:   the exact marginal sqrt(d) u_j of u uniform on S^{d-1}
+ *                     ("tiny-turboquant 0.18.0", "The algorithm in three lines":
+ *                      the Beta-distribution codebook of the original method). */
+typedef enum { TQ_DIST_GAUSSIAN = 0, TQ_DIST_SPHERE = 1 } tq_dist;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* tq_last_error(void);
+
+/* Returns TQ_ABI_VERSION of the built library. */
+int tq_abi_version(void);
+
+/* Lloyd-Max codebook ("How 0xsero/turboquant works", "Compression Pipeline":
+ * Lloyd-Max codebooks precomputed per dimension and bit width).  Host only,
+ * float64, no device needed.
+ *   bits        1..8 (levels L = 2^bits)
+ *   dist, dim   density (dim used by TQ_DIST_SPHERE; must be >= 3 there)
+ *   centroids   host out [L], ascending
+ *   boundaries  host out [L-1], boundaries[i] = (centroids[i] + centroids[i+1]) / 2
+ *   mse         host out, nullable: expected squared error per coordinate
+ * Iterates Lloyd's conditions from the quantile midpoints to max|delta c| < 1e-14. */
+tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids,
+                            double* boundaries, double* mse);
+
+typedef struct {
+  int head_dim;             /* d; must be 128                                   */
+  int n_kv_heads;           /* KV heads of the layer, >= 1                      */
+  int k_bits;               /* key codebook bits, 2..4 (QJL adds 1 bit/coord)   */
+  int v_bits;               /* value group-quantiser bits, 2..4                 */
+  int v_group;              /* value group width; must be 32                    */
+  int block_size;           /* tokens per page; must be 16                      */
+  int layer;                /* layer index, part of the random-state key        */
+  tq_dist dist;             /* key codebook density                             */
+  unsigned long long seed;  /* random-state seed                                */
+  int bypass;               /* 1: uncompressed bf16 layer (bits/dist ignored)   */
+} tq_layer_config;
+
+/* Opaque per-layer state.  Holds, on the device, for every KV head g:
+ *   R_g  d x d Haar-random orthogonal rotation (float32), and
+ *   S_g  d x d i.i.d. N(0,1) QJL projection (float32),
+ * both drawn from SplitMix64 + Box-Muller streams keyed by (seed, layer, g, tag)
+ * ("5x Faster LLM Inference? ...", "Example 1": a rotation precomputed and fixed
+ * per head), plus the key codebook rounded to float32.  Read-only after create;
+ * may be used from several streams at once. */
+typedef struct tq_layer tq_layer;
+
+/* The state a layer would hold, computed on the host only (no device needed).
+ *   R, S        host out [n_kv_heads][128][128] float32, row-major (nullable)
+ *   centroids   host out [2^k_bits] float32 (nullable)
+ *   boundaries  host out [2^k_bits - 1] float32 (nullable) */
+tq_status tq_layer_state_host(const tq_layer_config* cfg, float* R, float* S, float* centroids,
+                              float* boundaries);
+
+/* Build the state on the host and upload it to the current device.  Allocates
+ * device memory (owned by the layer until tq_layer_destroy) and synchronises
+ * `hip_stream` once.  *out receives the new layer. */
+tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer** out);
+
+/* Frees the layer's device memory.  NULL is accepted.  The caller must ensure no
+ * kernel using the layer is still running. */
+tq_status tq_layer_destroy(tq_layer* layer);
+
+/* Byte layout of one (block, head) region of the pool.
+ *   block_bytes    host out
+ *   field_offsets  host out [5] (Kc, Ks, Kn, Vc, Vsz); for bypass layers
+ *                  [K, V, 0, 0, 0]; nullable */
+tq_status tq_store_layout(const tq_layer_config* cfg, size_t* block_bytes, size_t* field_offsets);
+
+/* Fused K+V compression into the paged pool.
+ *   k, v             device [n_tokens][n_kv_heads][128] of in_dtype (F32 or BF16);
+ *                    token t of head g at k + t*k_token_stride + g*128 (elements)
+ *   slot_mapping     device int64 [n_tokens]; slot < 0 skips the token
+ *   pool             device uint8 [num_blocks][n_kv_heads][block_bytes]
+ * Requires 0 <= slot < num_blocks*16 for every non-negative slot (not checked on
+ * the device).  Tokens with equal slots race.  Bypass layers copy bf16 K/V (in_dtype
+ * must be BF16 there). */
+tq_status tq_compress_kv(const tq_layer* layer, const void* k, const void* v, tq_dtype in_dtype,
+                         long long n_tokens, long long k_token_stride, long long v_token_stride,
+                         const long long* slot_mapping, void* pool, long long num_blocks,
+                         void* hip_stream);
+
+/* Bytes of device workspace tq_decode_attn needs for this shape (num_splits as
+ * passed to tq_decode_attn, 0 = automatic). */
+tq_status tq_decode_workspace_size(const tq_layer* layer, int batch, int n_q_heads,
+                                   int max_seq_len, int num_splits, size_t* bytes);
+
+/* Paged decode attention over the compressed store, output in the original
+ * (un-rotated) basis:
+ *   out[b][h][:] = sum_i p_i * vhat_i over tokens i < seq_lens[b] of sequence b,
+ *   p = softmax(s), s_i = softmax_scale * (||k_i||16 / sqrt d) *
+ *       (q'.c[idx_i] + sqrt(pi/2)/128 * gamma_i * (S_g q').(2 z_i - 1)),  q' = R_g q,
+ *   vhat_i = R_g^T (zero + scale * code_i),  g = h / (n_q_heads / n_kv_heads).
+ * Arguments:
+ *   q            device [batch][n_q_heads][128] of q_dtype (F32 or BF16)
+ *   pool         device pool written by tq_compress_kv
+ *   block_table  device int32 [batch][max_blocks_per_seq]: logical block j of
+ *                sequence b -> physical block id in [0, num_blocks)
+ *   seq_lens     device int32 [batch], 0 <= seq_lens[b] <= min(max_seq_len,
+ *                16*max_blocks_per_seq); 0 gives a zero output row
+ *   max_seq_len  host bound on seq_lens, used to plan the split-K grid
+ *   softmax_scale  0 selects 1/sqrt(128)
+ *   num_splits   0 = automatic (from max_seq_len, batch, heads and the CU count);
+ *                otherwise the number of context splits per sequence.  The
+ *                environment variable TQ_DECODE_SPLITS overrides 0.
+ *   out          device [batch][n_q_heads][128] of out_dtype (F32 or BF16, RNE)
+ *   workspace    device scratch of at least tq_decode_workspace_size() bytes,
+ *                256-byte aligned; contents need not be initialised
+ * Three launches on hip_stream: query prologue, split-K mainloop, combine +
+ * un-rotation epilogue. */
+tq_status tq_decode_attn(const tq_layer* layer, const void* q, tq_dtype q_dtype, int batch,
+                         int n_q_heads, const void* pool, long long num_blocks,
+                         const int* block_table, int max_blocks_per_seq, const int* seq_lens,
+                         int max_seq_len, float softmax_scale, int num_splits, void* out,
+                         tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
+/* Kernel timing, a profiling aid (off by default).
+ * Kernel ids: 0 = compress, 1 = decode prologue, 2 = decode split-K mainloop,
+ * 3 = decode combine/epilogue.
+ * tq_profile_enable(mask): while bit i of mask is set, every launch of kernel i
+ *   is bracketed by two HIP events recorded on the caller's stream (mask 0 turns
+ *   timing off).  Not thread-safe; meant for benchmarks.
+ * tq_profile_read(kernel, total_ms, launches): waits for the recorded events and
+ *   returns the summed kernel time (host out, milliseconds) and the number of
+ *   timed launches (host out) since the last reset.
+ * tq_profile_reset(): forgets all records (events are recycled, not freed). */
+tq_status tq_profile_enable(unsigned mask);
+tq_status tq_profile_read(int kernel, double* total_ms, long long* launches);
+tq_status tq_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

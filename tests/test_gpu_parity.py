@@ -1,0 +1,268 @@
+"""GPU parity: libtq's HIP kernels (through the C ABI) against the oracle."""
+
+import numpy as np
+import pytest
+
+import compressed_decode_attention_tq_amd as tq
+from compressed_decode_attention_tq_amd import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    tq.lib()  # fails loudly if the library is missing
+    return torch
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ compress
+def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16"):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer))
+    k = torch.from_numpy(np.ascontiguousarray(K)).to("cuda", tdt)
+    v = torch.from_numpy(np.ascontiguousarray(V)).to("cuda", tdt)
+    pool = layer_obj.new_pool(num_blocks)
+    tq.compress_kv(layer_obj, k, v, torch.from_numpy(np.asarray(slots, np.int64)).cuda(), pool)
+    torch.cuda.synchronize()
+    out = pool.cpu().numpy()
+    layer_obj.close()
+    return out
+
+
+def _check_compress(gpu_pool, res, st, layout, n_heads, slots, V, kb, vb):
+    keep = np.asarray(slots) >= 0
+    sl = np.asarray(slots)[keep]
+    for h in range(n_heads):
+        f = parity.fields_at(gpu_pool, layout, n_heads, sl, h)
+        ck, cv = res[h]
+        stats = parity.compare_compress(f, ck, cv, st.S[h], st.boundaries, V[keep][:, h], vb)
+        print("head", h, stats)
+        parity.assert_compress_ok(stats)
+
+
+def test_compress_tiny_fp32():
+    """1 KV head, 1024 tokens, fp32 N(0,1), keys 2-bit + QJL, values 3-bit g32."""
+    torch = _torch()
+    say("compress tiny fp32 K2/V3")
+    K, V = synth.kv_host(101, 1024, 1, dtype="f32")
+    slots = np.arange(1024)
+    gpu = _gpu_compress(torch, K, V, slots, 64, 1, 2, 3, 201, dtype="f32")
+    st, layout, pool, res = parity.oracle_store(K, V, slots, 64, 1, 2, 3, 201)
+    _check_compress(gpu, res, st, layout, 1, slots, V, 2, 3)
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 2), (3, 2), (3, 3), (4, 3), (4, 4), (2, 4)])
+def test_compress_bits_ragged_slots(kb, vb):
+    """8 heads, bf16 with outlier channels, shuffled slots with skipped (-1) tokens."""
+    torch = _torch()
+    say("compress ragged", kb, vb)
+    n = 301
+    K, V = synth.kv_host(110 + kb * 10 + vb, n, 8, outliers=4)
+    rng = np.random.default_rng(kb * 7 + vb)
+    slots = rng.permutation(40 * 16)[:n].astype(np.int64)
+    slots[rng.choice(n, 20, replace=False)] = -1
+    gpu = _gpu_compress(torch, K, V, slots, 40, 8, kb, vb, 210, layer=kb + vb)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, 40, 8, kb, vb, 210, layer=kb + vb)
+    _check_compress(gpu, res, st, layout, 8, slots, V, kb, vb)
+    # slots nobody wrote stay untouched
+    written = set((slots[slots >= 0] // 16).tolist())
+    untouched = [b for b in range(40) if b not in written]
+    for b in untouched:
+        assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
+
+
+def test_compress_full_size_sampled():
+    """1,048,576 tokens x 8 KV heads bf16 (K2+QJL / V3), checked on 2048 sampled tokens."""
+    torch = _torch()
+    say("compress 1M tokens x 8 heads")
+    N, H = 1 << 20, 8
+    k, v = synth.kv_device(103, N, H)
+    layer = tq.Layer(tq.config(H, 2, 3, seed=203))
+    pool = layer.new_pool(N // 16)
+    slots = torch.arange(N, dtype=torch.int64, device="cuda")
+    tq.compress_kv(layer, k, v, slots, pool)
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(0).choice(N, 2048, replace=False))
+    ti = torch.from_numpy(idx).cuda()
+    K = k[ti].float().cpu().numpy()
+    V = v[ti].float().cpu().numpy()
+    lay_bytes = layer.block_bytes * H
+    # gather the sampled tokens' blocks from the GPU pool
+    blocks = np.unique(idx // 16)
+    sub = pool.view(-1, lay_bytes)[torch.from_numpy(blocks).cuda()].cpu().numpy().ravel()
+    remap = {b: i for i, b in enumerate(blocks)}
+    local = np.array([remap[s // 16] * 16 + s % 16 for s in idx])
+    st, layout, opool, res = parity.oracle_store(K, V, local, len(blocks), H, 2, 3, 203)
+    _check_compress(sub, res, st, layout, H, local, V, 2, 3)
+    layer.close()
+
+
+# -------------------------------------------------------------------- decode
+def _gpu_decode(torch, layer_cfg, pool_np, q, table, lens, max_len, out_dtype="f32", num_splits=0,
+                scale=0.0, q_dtype="bf16"):
+    layer = tq.Layer(layer_cfg)
+    pool = torch.from_numpy(pool_np).cuda()
+    qdt = torch.bfloat16 if q_dtype == "bf16" else torch.float32
+    qt = torch.from_numpy(np.ascontiguousarray(q)).to("cuda", qdt)
+    bt = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
+    sl = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = tq.decode_attn(layer, qt, pool, bt, sl, max_len, out_dtype=odt, num_splits=num_splits,
+                         softmax_scale=scale)
+    torch.cuda.synchronize()
+    res = out.float().cpu().numpy()
+    layer.close()
+    return res
+
+
+def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_dtype="bf16",
+                 outliers=4, out_dtypes=("f32", "bf16"), num_splits=0, scale=0.0, layer=0, bypass=False):
+    lens = np.asarray(lens, dtype=np.int32)
+    maxb = max(1, (int(lens.max()) + 15) // 16)
+    table = synth.block_table(seed, B, maxb, table_kind)
+    nblk = B * maxb
+    K, V, slots = [], [], []
+    for b in range(B):
+        kk, vv = synth.kv_host(seed * 1000 + b, int(lens[b]), Hkv, outliers=outliers,
+                               dtype="bf16" if q_dtype == "bf16" else "f32")
+        pos = np.arange(int(lens[b]))
+        K.append(kk)
+        V.append(vv)
+        slots.append(table[b][pos // 16].astype(np.int64) * 16 + pos % 16)
+    K = np.concatenate(K) if K else np.zeros((0, Hkv, 128), np.float32)
+    V = np.concatenate(V) if V else np.zeros((0, Hkv, 128), np.float32)
+    slots = np.concatenate(slots)
+    if bypass:
+        st, layout, pool, _ = parity.oracle_store(None, None, slots, nblk, Hkv, 4, 4, seed, bypass=True,
+                                                  K_bits16=synth.bf16_bits(K), V_bits16=synth.bf16_bits(V))
+    else:
+        st, layout, pool, _ = parity.oracle_store(K, V, slots, nblk, Hkv, kb, vb, seed, layer=layer, keep=False)
+    q = synth.queries_host(seed, B, Hq, dtype=q_dtype)
+    ref = parity.oracle_decode(q.astype(np.float64), pool, layout, Hkv, table, lens, st,
+                               scale=scale if scale else None)
+    cfg = tq.config(Hkv, kb, vb, seed=seed, layer=layer, bypass=bypass)
+    results = {}
+    for od in out_dtypes:
+        got = _gpu_decode(torch, cfg, pool, q, table, lens, int(lens.max()), od, num_splits, scale,
+                          q_dtype=q_dtype)
+        err = parity.rel_l2(got, ref)
+        results[od] = err
+        print("decode", od, "rel L2 %.3e" % err)
+        assert err <= (1e-3 if od == "f32" else 1e-2), (od, err)
+    return results
+
+
+def test_decode_tiny_fp32():
+    """1 head, 1024 tokens, fp32 q/K/V, K2/V3, identity table."""
+    torch = _torch()
+    say("decode tiny fp32")
+    _decode_case(torch, 1, 1, 1, [1024], 2, 3, 201, table_kind="identity", q_dtype="f32", outliers=0)
+
+
+def test_decode_llama_layer_full():
+    """B=16, 32/8 heads, ctx 4096, bf16 with outliers, K4/V4, identity table."""
+    torch = _torch()
+    say("decode B16 ctx4096 K4V4")
+    _decode_case(torch, 16, 32, 8, [4096] * 16, 4, 4, 202, table_kind="identity")
+
+
+def test_decode_long_context_full():
+    """B=1, 32/8 heads, ctx 131072, bf16 with outliers, K3/V2, random block table."""
+    torch = _torch()
+    say("decode B1 ctx131072 K3V2")
+    _decode_case(torch, 1, 32, 8, [131072], 3, 2, 204, out_dtypes=("f32",))
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (4, 3), (3, 3), (3, 2), (2, 3), (2, 2)])
+def test_decode_ragged_bits(kb, vb):
+    """Ragged lengths with tails, a zero-length row, every supported bit pair."""
+    torch = _torch()
+    say("decode ragged", kb, vb)
+    _decode_case(torch, 6, 8, 2, [1, 0, 17, 64, 300, 1000], kb, vb, 220 + kb * 10 + vb)
+
+
+@pytest.mark.parametrize("rep", [1, 2, 8])
+def test_decode_gqa_ratios(rep):
+    torch = _torch()
+    say("decode rep", rep)
+    _decode_case(torch, 3, 2 * rep, 2, [33, 513, 257], 4, 3, 230 + rep)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 64])
+def test_decode_forced_splits_and_scale(splits):
+    torch = _torch()
+    say("decode splits", splits)
+    _decode_case(torch, 2, 8, 2, [700, 1500], 3, 3, 240 + splits, num_splits=splits, scale=0.05)
+
+
+def test_decode_bypass_layer():
+    torch = _torch()
+    say("decode bypass")
+    _decode_case(torch, 3, 8, 2, [16, 200, 1031], 0, 0, 250, bypass=True)
+
+
+def test_decode_ragged_serving_sampled():
+    """64 sequences with lengths U{512..32768}, 32/8 heads; the oracle fills only
+    sequences 0, 31, 63 and the outputs of those are compared."""
+    torch = _torch()
+    say("decode ragged serving sample")
+    B, Hq, Hkv = 64, 32, 8
+    lens = synth.ragged_lengths(505, B, 512, 32768)
+    maxb = (int(lens.max()) + 15) // 16
+    table = synth.block_table(305, B, maxb, "random")
+    sample = [0, 31, 63]
+    for kb, vb in [(4, 4), (3, 2)]:
+        K, V, slots = [], [], []
+        for b in sample:
+            kk, vv = synth.kv_host(105000 + b, int(lens[b]), Hkv, outliers=4)
+            pos = np.arange(int(lens[b]))
+            K.append(kk)
+            V.append(vv)
+            slots.append(table[b][pos // 16].astype(np.int64) * 16 + pos % 16)
+        K, V, slots = np.concatenate(K), np.concatenate(V), np.concatenate(slots)
+        st, layout, pool, _ = parity.oracle_store(K, V, slots, B * maxb, Hkv, kb, vb, 205, layer=kb + vb,
+                                                  keep=False)
+        q = synth.queries_host(205, B, Hq)
+        sub_lens = np.zeros(B, np.int32)
+        sub_lens[sample] = lens[sample]
+        ref = parity.oracle_decode(q.astype(np.float64), pool, layout, Hkv, table, sub_lens, st)
+        got = _gpu_decode(torch, tq.config(Hkv, kb, vb, seed=205, layer=kb + vb), pool, q, table, lens,
+                          int(lens.max()))
+        err = parity.rel_l2(got[sample], ref[sample])
+        print("ragged serving", kb, vb, "rel L2 %.3e" % err)
+        assert err <= 1e-3
+
+
+def test_end_to_end_gpu_compress_then_decode():
+    """GPU compress -> GPU decode against oracle compress -> oracle decode."""
+    torch = _torch()
+    say("end to end")
+    B, Hq, Hkv, T = 4, 16, 4, 777
+    lens = np.full(B, T, np.int32)
+    maxb = (T + 15) // 16
+    table = synth.block_table(260, B, maxb, "random")
+    K, V = synth.kv_host(160, B * T, Hkv, outliers=4)
+    pos = np.tile(np.arange(T), B)
+    seq = np.repeat(np.arange(B), T)
+    slots = table[seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    st, layout, opool, _ = parity.oracle_store(K, V, slots, B * maxb, Hkv, 3, 3, 260, keep=False)
+    q = synth.queries_host(260, B, Hq)
+    ref = parity.oracle_decode(q.astype(np.float64), opool, layout, Hkv, table, lens, st)
+    layer = tq.Layer(tq.config(Hkv, 3, 3, seed=260))
+    pool = layer.new_pool(B * maxb)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    out = tq.decode_attn(layer, torch.from_numpy(q).to("cuda", torch.bfloat16), pool,
+                         torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(), T)
+    torch.cuda.synchronize()
+    err = parity.rel_l2(out.cpu().numpy(), ref)
+    print("end-to-end rel L2 %.3e" % err)
+    assert err <= 2e-3
+    layer.close()

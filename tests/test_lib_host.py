@@ -1,0 +1,110 @@
+"""libtq on the CPU: exported symbols, host state against the oracle, error paths.
+
+No compute call here touches a device.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_decode_attention_tq_amd as tq
+from oracle import codebook, layout, state
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:tq_status|const char\*|int)\s+(tq_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tq.lib()
+    names = _declared_symbols()
+    assert len(names) == 13
+    assert sorted(names) == sorted(tq.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.tq_abi_version() == 1
+
+
+@pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(bits, dist, name):
+    c, b, mse = tq.codebook_build(bits, dist, 128)
+    oc, ob, om = codebook.lloyd_max(bits, name, 128)
+    assert np.max(np.abs(c - oc)) < 1e-12
+    assert np.max(np.abs(b - ob)) < 1e-12
+    assert abs(mse - om) < 1e-12
+    # the float32 codebook the kernels use is identical
+    assert np.array_equal(c.astype(np.float32), oc.astype(np.float32))
+    assert np.array_equal(b.astype(np.float32), ob.astype(np.float32))
+
+
+@pytest.mark.parametrize("layer,heads,kb", [(0, 1, 2), (3, 8, 4), (17, 2, 3)])
+def test_layer_state_matches_oracle(layer, heads, kb):
+    cfg = tq.config(heads, kb, 3, seed=205, layer=layer)
+    R, S, c, b = tq.layer_state_host(cfg)
+    st = state.LayerState(205, layer, heads, 128, kb, 3, 32)
+    # same generators, same float32 rounding: bit-identical except at rare rounding ties
+    assert np.count_nonzero(R.astype(np.float64) != st.R) <= 2
+    assert np.max(np.abs(R - st.R)) <= 1.2e-7
+    assert np.array_equal(S.astype(np.float64), st.S)
+    assert np.array_equal(c.astype(np.float64), st.centroids)
+    assert np.array_equal(b.astype(np.float64), st.boundaries)
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 2), (2, 3), (3, 2), (3, 3), (4, 3), (4, 4)])
+def test_store_layout_matches_oracle(kb, vb):
+    bb, offs = tq.store_layout(tq.config(8, kb, vb))
+    lay = layout.StoreLayout(128, kb, vb, 32)
+    assert bb == lay.block_bytes
+    assert offs == lay.field_offsets()
+    bb, offs = tq.store_layout(tq.config(8, bypass=True))
+    lay = layout.StoreLayout(bypass=True)
+    assert bb == lay.block_bytes and offs[:2] == lay.field_offsets()
+
+
+def _status_of(fn):
+    with pytest.raises(tq.TQError) as e:
+        fn()
+    assert str(e.value)
+    return e.value.status
+
+
+def test_config_errors():
+    bad = [
+        (dict(head_dim=64), tq.ERR_UNSUPPORTED), (dict(k_bits=5), tq.ERR_UNSUPPORTED),
+        (dict(k_bits=1), tq.ERR_UNSUPPORTED), (dict(v_bits=1), tq.ERR_UNSUPPORTED),
+        (dict(v_group=16), tq.ERR_UNSUPPORTED), (dict(block_size=32), tq.ERR_UNSUPPORTED),
+        (dict(n_kv_heads=0), tq.ERR_INVALID_ARGUMENT), (dict(layer=-1), tq.ERR_INVALID_ARGUMENT),
+        (dict(dist=7), tq.ERR_INVALID_ARGUMENT),
+    ]
+    for kw, want in bad:
+        args = dict(n_kv_heads=8)
+        args.update(kw)
+        cfg = tq.config(**args)
+        assert _status_of(lambda: tq.store_layout(cfg)) == want, kw
+        assert _status_of(lambda: tq.layer_state_host(cfg)) == want, kw
+
+
+def test_codebook_errors():
+    assert _status_of(lambda: tq.codebook_build(0)) == tq.ERR_INVALID_ARGUMENT
+    assert _status_of(lambda: tq.codebook_build(9)) == tq.ERR_INVALID_ARGUMENT
+    assert _status_of(lambda: tq.codebook_build(2, tq.DIST_SPHERE, 2)) == tq.ERR_INVALID_ARGUMENT
+
+
+def test_null_and_bad_arguments_on_device_entry_points():
+    lib = tq.lib()
+    vp = ctypes.c_void_p
+    assert lib.tq_compress_kv(None, vp(1), vp(1), tq.BF16, 1, 1024, 1024, vp(1), vp(1), 1, None) == tq.ERR_INVALID_ARGUMENT
+    assert b"null layer" in lib.tq_last_error()
+    out = ctypes.c_size_t(0)
+    assert lib.tq_decode_workspace_size(None, 1, 1, 1, 0, ctypes.byref(out)) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_decode_attn(None, vp(1), tq.BF16, 1, 1, vp(1), 1, vp(1), 1, vp(1), 16, 0.0, 0,
+                              vp(1), tq.F32, vp(256), 1 << 20, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_layer_destroy(None) == tq.OK
+    assert lib.tq_layer_create(None, None, ctypes.byref(vp())) == tq.ERR_INVALID_ARGUMENT
