@@ -105,9 +105,14 @@ tq_status build_state(const tq_layer_config* cfg, std::vector<float>* R, std::ve
     double c[256], b[255];
     tq_status st = lloyd_max(cfg->k_bits, cfg->dist, d, c, b, nullptr);
     if (st != TQ_OK) return st;
+    // Stored codebook: centroids rounded to float16 (the decode kernels' MFMA
+    // operand type), boundaries at the exact midpoints of the stored centroids.
     const int L = 1 << cfg->k_bits;
-    for (int i = 0; i < L; ++i) cent[i] = static_cast<float>(c[i]);
-    for (int i = 0; i + 1 < L; ++i) bnd[i] = static_cast<float>(b[i]);
+    double c16[256];
+    for (int i = 0; i < L; ++i) c16[i] = static_cast<double>(static_cast<_Float16>(c[i]));
+    for (int i = 0; i < L; ++i) cent[i] = static_cast<float>(c16[i]);
+    for (int i = 0; i + 1 < L; ++i) bnd[i] = static_cast<float>(0.5 * (c16[i] + c16[i + 1]));
+    (void)b;
     *levels = L;
   }
   return TQ_OK;

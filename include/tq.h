@@ -122,14 +122,15 @@ typedef struct {
  *   S_g  d x d i.i.d. N(0,1) QJL projection (float32),
  * both drawn from SplitMix64 + Box-Muller streams keyed by (seed, layer, g, tag)
  * ("5x Faster LLM Inference? ...", "Example 1": a rotation precomputed and fixed
- * per head), plus the key codebook rounded to float32.  Read-only after create;
+ * per head), plus the key codebook: Lloyd-Max centroids rounded to float16 and
+ * the exact midpoints between them as decision boundaries.  Read-only after create;
  * may be used from several streams at once. */
 typedef struct tq_layer tq_layer;
 
 /* The state a layer would hold, computed on the host only (no device needed).
  *   R, S        host out [n_kv_heads][128][128] float32, row-major (nullable)
- *   centroids   host out [2^k_bits] float32 (nullable)
- *   boundaries  host out [2^k_bits - 1] float32 (nullable) */
+ *   centroids   host out [2^k_bits] float32 (nullable): float16-rounded Lloyd-Max centroids
+ *   boundaries  host out [2^k_bits - 1] float32 (nullable): midpoints of the centroids */
 tq_status tq_layer_state_host(const tq_layer_config* cfg, float* R, float* S, float* centroids,
                               float* boundaries);
 

@@ -14,6 +14,11 @@ S: an m x d matrix of i.i.d. N(0,1) entries from the projection stream, m = d
 
 Both are stored, and used by every consumer, as float32-rounded values; the
 oracle then computes in float64 on exactly those numbers.
+
+Codebook state: the Lloyd-Max centroids (solved in float64) are stored rounded
+to float16, and the decision boundaries are the exact midpoints of the stored
+centroids (exactly representable in float32).  Compression and decode both use
+these stored values, so the quantiser and the estimator see the same codebook.
 """
 
 import numpy as np
@@ -48,12 +53,17 @@ class LayerState:
     """All state of one compressed layer: R and S per KV head plus the key codebook."""
 
     def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian"):
-        from . import codebook
-
         self.seed, self.layer, self.n_kv_heads, self.d = seed, layer, n_kv_heads, d
         self.k_bits, self.v_bits, self.group, self.dist = k_bits, v_bits, group, dist
         self.R = np.stack([haar_rotation(seed, layer, h, d) for h in range(n_kv_heads)])
         self.S = np.stack([qjl_projection(seed, layer, h, d) for h in range(n_kv_heads)])
-        c64, b64, _ = codebook.lloyd_max(k_bits, dist, d)
-        self.centroids = c64.astype(np.float32).astype(np.float64)
-        self.boundaries = b64.astype(np.float32).astype(np.float64)
+        self.centroids, self.boundaries = stored_codebook(k_bits, dist, d)
+
+
+def stored_codebook(bits, dist="gaussian", d=128):
+    """float16-rounded Lloyd-Max centroids and the midpoints between them (float64 values)."""
+    from . import codebook
+
+    c64, _, _ = codebook.lloyd_max(bits, dist, d)
+    c16 = c64.astype(np.float16).astype(np.float64)
+    return c16, 0.5 * (c16[:-1] + c16[1:])

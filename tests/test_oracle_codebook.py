@@ -92,3 +92,20 @@ def test_quantize_index_nearest_centroid():
     assert np.array_equal(idx, brute)
     # ties go to the lower cell
     assert np.array_equal(codebook.quantize_index(b, b), np.arange(len(b)))
+
+
+@pytest.mark.parametrize("dist", ["gaussian", "sphere"])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_stored_codebook(bits, dist):
+    """The stored codebook: float16-rounded centroids, boundaries at their exact
+    midpoints; its distortion is within a second-order hair of the optimum."""
+    from oracle import state
+
+    c, b = state.stored_codebook(bits, dist, 128)
+    c64, b64, mse = codebook.lloyd_max(bits, dist, 128)
+    assert np.array_equal(c, c.astype(np.float16).astype(np.float64))
+    assert np.max(np.abs(c - c64) / np.abs(c64)) <= 2.0 ** -11
+    assert np.array_equal(b, b.astype(np.float32).astype(np.float64))
+    assert np.array_equal(b, (c[:-1] + c[1:]) / 2)
+    d16 = codebook.distortion(c, b, dist, 128)
+    assert mse <= d16 <= mse * (1 + 1e-5)

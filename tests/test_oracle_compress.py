@@ -11,8 +11,8 @@ D = 128
 
 
 def _cb(bits):
-    c, b, mse = codebook.lloyd_max(bits, "gaussian", D)
-    return c.astype(np.float32).astype(np.float64), b.astype(np.float32).astype(np.float64), mse
+    c, b = state.stored_codebook(bits, "gaussian", D)
+    return c, b, codebook.distortion(c, b, "gaussian", D)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
