@@ -19,7 +19,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I
           "--offload-arch=gfx950"]
 # Packed fp32 VALU forms are kept out of the generated code.
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
-SOURCES = ["api.cpp", "host_state.cpp", "host_codebook.cpp", "profile.cpp", "compress.hip", "decode.hip"]
+SOURCES = ["api.cpp", "host_state.cpp", "host_codebook.cpp", "profile.cpp", "compress.hip", "decode.hip", "decode_mainloop.hip"]
 
 
 def _compile(src):

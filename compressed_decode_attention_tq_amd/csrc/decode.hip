@@ -13,10 +13,9 @@
 //
 // Launch 1 (prologue): q', u per (sequence, query head) into the workspace.
 // Launch 2 (split-K):  one workgroup per (split, KV head, sequence) serves all
-//   query heads of its KV head so the compressed KV is read once.  Four waves
-//   take 64-token chunks in turn; within a chunk a lane scores one token, then
-//   the chunk's values are accumulated with lanes owning 2 coordinates each.
-//   Online softmax keeps a running max/sum per head (wave reductions).
+//   query heads of its KV head so the compressed KV is read once (the
+//   compressed mainloop is in decode_mainloop.hip; uncompressed layers use the
+//   bypass loop below).
 // Launch 3 (combine): merge the split partials with the running-max rescaling,
 //   un-rotate o = R_g^T o', cast and store.
 #include <hip/hip_fp16.h>
@@ -40,8 +39,7 @@ struct DecodeArgs {
   long long max_blocks;
   int Hq, Hkv, n_splits, split_tokens;
   float scale;
-  unsigned block_bytes, off_kc, off_ks, off_kn, off_vc, off_vsz;
-  float cent[16];
+  unsigned block_bytes;
 };
 
 __device__ __forceinline__ float half_lo(unsigned w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xffffu))); }
@@ -56,16 +54,6 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
-}
-
-// Code j (0..127) of a B-bit LSB-first bitstream held in 32-bit words.
-template <int B>
-__device__ __forceinline__ int code_at(const unsigned* w, int j) {
-  const int bit = B * j;
-  const int wi = bit >> 5, sh = bit & 31;
-  unsigned x = w[wi] >> sh;
-  if (sh + B > 32) x |= w[wi + 1] << (32 - sh);
-  return static_cast<int>(x & ((1u << B) - 1u));
 }
 
 // ---------------------------------------------------------------- prologue
@@ -102,10 +90,14 @@ __global__ __launch_bounds__(128) void prologue_kernel(const void* q, const floa
   }
 }
 
-// ----------------------------------------------------------------- split-K
-// KB == 0 selects the uncompressed bf16 (bypass) page format.
-template <int NREP, int KB, int VB>
-__global__ __launch_bounds__(256) void splitk_kernel(DecodeArgs a) {
+// ------------------------------------------------------ split-K (bypass)
+// Uncompressed bf16 pages ("tiny-turboquant 0.18.0", "Knobs that actually move
+// the needle": protected boundary layers stay at full precision).  Same split-K
+// structure as the compressed mainloop: four waves take 64-token chunks in
+// turn; a lane scores one token, then the chunk's values are accumulated with
+// lanes owning two coordinates each.
+template <int NREP>
+__global__ __launch_bounds__(256) void splitk_bypass_kernel(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = a.seq_lens[b];
   const int start = split * a.split_tokens;
@@ -113,24 +105,17 @@ __global__ __launch_bounds__(256) void splitk_kernel(DecodeArgs a) {
   const int end = min(T, start + a.split_tokens);
 
   __shared__ float qs[NREP][128];
-  __shared__ float us[NREP][128];
-  __shared__ float cb[16];
   __shared__ float wm[4][NREP], wl[4][NREP];
   __shared__ float wacc[4][NREP][128];
 
   const int h0 = g * NREP;
   for (int x = threadIdx.x; x < NREP * 128; x += 256) {
     const int r = x >> 7, d = x & 127;
-    const float* src = a.qu + static_cast<size_t>(b * a.Hq + h0 + r) * 256;
-    qs[r][d] = src[d];
-    us[r][d] = src[128 + d];
+    qs[r][d] = a.qu[static_cast<size_t>(b * a.Hq + h0 + r) * 256 + d];
   }
-  if (threadIdx.x < 16) cb[threadIdx.x] = a.cent[threadIdx.x];
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float kappa = 0.0097916396f;  // sqrt(pi/2) / 128
-  const float inv_sqrt_d = 0.08838834764831845f;
   float m[NREP], l[NREP], acc[NREP][2];
 #pragma unroll
   for (int r = 0; r < NREP; ++r) {
@@ -149,55 +134,23 @@ __global__ __launch_bounds__(256) void splitk_kernel(DecodeArgs a) {
       const int blk = a.block_table[b * a.max_blocks + (tok >> 4)];
       off = tok & 15;
       rbase = (static_cast<long long>(blk) * a.Hkv + g) * a.block_bytes;
-      const unsigned char* rec = a.pool + rbase;
-      if constexpr (KB == 0) {
-        const unsigned* kw = reinterpret_cast<const unsigned*>(rec + off * 256);
-        float A[NREP];
+      const unsigned* kw = reinterpret_cast<const unsigned*>(a.pool + rbase + off * 256);
+      float A[NREP];
 #pragma unroll
-        for (int r = 0; r < NREP; ++r) A[r] = 0.0f;
+      for (int r = 0; r < NREP; ++r) A[r] = 0.0f;
 #pragma unroll 8
-        for (int d2 = 0; d2 < 64; ++d2) {
-          const unsigned w = kw[d2];
-          const float k0 = bf16_lo(w), k1 = bf16_hi(w);
+      for (int d2 = 0; d2 < 64; ++d2) {
+        const unsigned w = kw[d2];
+        const float k0 = bf16_lo(w), k1 = bf16_hi(w);
 #pragma unroll
-          for (int r = 0; r < NREP; ++r) A[r] = fmaf(qs[r][2 * d2 + 1], k1, fmaf(qs[r][2 * d2], k0, A[r]));
-        }
-#pragma unroll
-        for (int r = 0; r < NREP; ++r) s[r] = a.scale * A[r];
-      } else {
-        const unsigned* kc = reinterpret_cast<const unsigned*>(rec + a.off_kc + off * (16 * KB));
-        const unsigned* ks = reinterpret_cast<const unsigned*>(rec + a.off_ks + off * 16);
-        const unsigned kn = *reinterpret_cast<const unsigned*>(rec + a.off_kn + off * 4);
-        unsigned w[4 * KB + 1];
-#pragma unroll
-        for (int x = 0; x < 4 * KB; ++x) w[x] = kc[x];
-        w[4 * KB] = 0;
-        unsigned sw[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) sw[x] = ks[x];
-        float A[NREP], Bs[NREP];
-#pragma unroll
-        for (int r = 0; r < NREP; ++r) A[r] = Bs[r] = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 128; ++d) {
-          const float c = cb[code_at<KB>(w, d)];
-          const bool bit = (sw[d >> 5] >> (d & 31)) & 1u;
-#pragma unroll
-          for (int r = 0; r < NREP; ++r) {
-            A[r] = fmaf(qs[r][d], c, A[r]);
-            Bs[r] += bit ? us[r][d] : -us[r][d];
-          }
-        }
-        const float nn = half_lo(kn), gg = half_hi(kn);
-#pragma unroll
-        for (int r = 0; r < NREP; ++r) s[r] = a.scale * (nn * inv_sqrt_d) * (A[r] + kappa * gg * Bs[r]);
+        for (int r = 0; r < NREP; ++r) A[r] = fmaf(qs[r][2 * d2 + 1], k1, fmaf(qs[r][2 * d2], k0, A[r]));
       }
+#pragma unroll
+      for (int r = 0; r < NREP; ++r) s[r] = a.scale * A[r];
     } else {
 #pragma unroll
       for (int r = 0; r < NREP; ++r) s[r] = -INFINITY;
     }
-
-    // online softmax (lane 0 of the chunk is always a valid token)
 #pragma unroll
     for (int r = 0; r < NREP; ++r) {
       const float mnew = fmaxf(m[r], wave_max(s[r]));
@@ -209,31 +162,12 @@ __global__ __launch_bounds__(256) void splitk_kernel(DecodeArgs a) {
       m[r] = mnew;
       s[r] = p;
     }
-
-    // values: lane owns coordinates 2*lane, 2*lane+1
     const int ntok = min(64, end - c0);
     for (int j = 0; j < ntok; ++j) {
       const long long rb = __shfl(rbase, j, 64);
       const int oj = __shfl(off, j, 64);
-      const unsigned char* rec = a.pool + rb;
-      float v0, v1;
-      if constexpr (KB == 0) {
-        const unsigned w = reinterpret_cast<const unsigned*>(rec + 4096 + oj * 256)[lane];
-        v0 = bf16_lo(w);
-        v1 = bf16_hi(w);
-      } else {
-        const unsigned char* vc = rec + a.off_vc + oj * (16 * VB);
-        const int bit = VB * 2 * lane;
-        unsigned two = vc[bit >> 3];
-        if ((bit & 7) + 2 * VB > 8) two |= static_cast<unsigned>(vc[(bit >> 3) + 1]) << 8;
-        two >>= (bit & 7);
-        const float c0v = static_cast<float>(two & ((1u << VB) - 1u));
-        const float c1v = static_cast<float>((two >> VB) & ((1u << VB) - 1u));
-        const unsigned sz = reinterpret_cast<const unsigned*>(rec + a.off_vsz + oj * 16)[(2 * lane) >> 5];
-        const float sc = half_lo(sz), ze = half_hi(sz);
-        v0 = fmaf(sc, c0v, ze);
-        v1 = fmaf(sc, c1v, ze);
-      }
+      const unsigned w = reinterpret_cast<const unsigned*>(a.pool + rb + 4096 + oj * 256)[lane];
+      const float v0 = bf16_lo(w), v1 = bf16_hi(w);
 #pragma unroll
       for (int r = 0; r < NREP; ++r) {
         const float p = __shfl(s[r], j, 64);
@@ -243,7 +177,6 @@ __global__ __launch_bounds__(256) void splitk_kernel(DecodeArgs a) {
     }
   }
 
-  // merge the four waves
 #pragma unroll
   for (int r = 0; r < NREP; ++r) {
     if (lane == 0) {
@@ -318,37 +251,12 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* part, const i
   }
 }
 
-template <int NREP, int KB>
-void* pick_splitk_vb(int vb) {
-  if constexpr (KB == 0) {
-    return reinterpret_cast<void*>(&splitk_kernel<NREP, 0, 0>);
-  } else {
-    switch (vb) {
-      case 2: return reinterpret_cast<void*>(&splitk_kernel<NREP, KB, 2>);
-      case 3: return reinterpret_cast<void*>(&splitk_kernel<NREP, KB, 3>);
-      case 4: return reinterpret_cast<void*>(&splitk_kernel<NREP, KB, 4>);
-    }
-  }
-  return nullptr;
-}
-
-template <int NREP>
-void* pick_splitk_kb(int kb, int vb) {
-  switch (kb) {
-    case 0: return pick_splitk_vb<NREP, 0>(vb);
-    case 2: return pick_splitk_vb<NREP, 2>(vb);
-    case 3: return pick_splitk_vb<NREP, 3>(vb);
-    case 4: return pick_splitk_vb<NREP, 4>(vb);
-  }
-  return nullptr;
-}
-
-void* pick_splitk(int rep, int kb, int vb) {
+void* pick_bypass(int rep) {
   switch (rep) {
-    case 1: return pick_splitk_kb<1>(kb, vb);
-    case 2: return pick_splitk_kb<2>(kb, vb);
-    case 4: return pick_splitk_kb<4>(kb, vb);
-    case 8: return pick_splitk_kb<8>(kb, vb);
+    case 1: return reinterpret_cast<void*>(&splitk_bypass_kernel<1>);
+    case 2: return reinterpret_cast<void*>(&splitk_bypass_kernel<2>);
+    case 4: return reinterpret_cast<void*>(&splitk_bypass_kernel<4>);
+    case 8: return reinterpret_cast<void*>(&splitk_bypass_kernel<8>);
   }
   return nullptr;
 }
@@ -382,7 +290,12 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));
   }
   // 2. split-K mainloop
-  {
+  if (!bypass) {
+    ProfScope prof(kKSplitK, stream);
+    tq_status st = launch_splitk_tq(L, plan, pool, block_table, max_blocks_per_seq, seq_lens, softmax_scale, qu,
+                                    part, stream);
+    if (st != TQ_OK) return st;
+  } else {
     DecodeArgs a;
     a.pool = static_cast<const unsigned char*>(pool);
     a.block_table = block_table;
@@ -396,13 +309,7 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     a.split_tokens = plan.split_tokens;
     a.scale = softmax_scale;
     a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
-    a.off_kc = static_cast<unsigned>(L->lay.off_kc);
-    a.off_ks = static_cast<unsigned>(L->lay.off_ks);
-    a.off_kn = static_cast<unsigned>(L->lay.off_kn);
-    a.off_vc = static_cast<unsigned>(L->lay.off_vc);
-    a.off_vsz = static_cast<unsigned>(L->lay.off_vsz);
-    for (int i = 0; i < 16; ++i) a.cent[i] = L->centroids[i];
-    void* fn = pick_splitk(plan.rep, bypass ? 0 : L->cfg.k_bits, bypass ? 0 : L->cfg.v_bits);
+    void* fn = pick_bypass(plan.rep);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for this variant");
     void* args[] = {&a};
     const dim3 grid(plan.n_splits, L->cfg.n_kv_heads, plan.batch);

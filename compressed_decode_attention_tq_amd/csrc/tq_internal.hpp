@@ -91,6 +91,9 @@ struct DecodePlan {
 };
 tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_len,
                       int num_splits, DecodePlan* plan);
+tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void* pool, const int* block_table,
+                           int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const float* qu,
+                           float* part, void* stream);
 tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
                         const void* pool, const int* block_table, int max_blocks_per_seq,
                         const int* seq_lens, float softmax_scale, void* out, tq_dtype out_dtype,
