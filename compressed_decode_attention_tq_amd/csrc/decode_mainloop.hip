@@ -13,12 +13,13 @@
 //    codebook values c[idx] (exact) and the +-1 signs (exact), dequantised from
 //    the packed codes through LDS lookup tables.  Rows = query heads of the GQA
 //    group (head h at row 4(h%4) + h/4), columns = 16 tokens, K = 32 dims.
-//  * P.V: A = the value codes as float16 integers (bias exponent OR-ed onto the
-//    masked code bits, then one packed subtract -- exact); B = w = p * scale
-//    split into two float16 pieces.  Rows = 16 coordinates,
-//    columns = query heads, K = 32 tokens (two pages).  The per-group zero
-//    term sum_i p_i zero_i is accumulated on the vector ALU, together with
-//    the float16 splitting residual of w taken at the mid code.
+//  * P.V: A = the centred value codes, code - 2^(b-1), as float16 integers
+//    (a bias exponent OR-ed onto the masked code bits, then one packed
+//    subtract -- exact); B = w = p * scale split into two float16 pieces.  Rows = 16 coordinates,
+//    columns = query heads, K = 32 tokens (two pages).  The per-group offset
+//    sum_i p_i (zero_i + 2^(b-1) scale_i) is accumulated on the vector ALU.
+//    Centring keeps both sums free of a large cancelling offset, which
+//    matters because the matrix-core accumulate truncates.
 // A wave takes a 32-token chunk (two 16-token pages) at a time; the four waves
 // of a workgroup take chunks in turn and merge at the end.  Online softmax keeps
 // a running max per head (16-lane row reductions), rescaling only when the max
@@ -41,7 +42,6 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPart = kDim + 4;
 constexpr float kRescale = 3.0f;   // tolerated growth of the running max (natural log units)
-constexpr int kDrain = 4;          // chunks between drains of the P.V matrix-core accumulators
 constexpr float kKappa = 0.0097916396f;  // sqrt(pi/2) / 128
 constexpr float kInvSqrtD = 0.08838834764831845f;
 
@@ -94,7 +94,16 @@ __device__ __forceinline__ unsigned bias_bits(int p) {
   const unsigned e = static_cast<unsigned>(25 - p) << 10;
   return e | (e << 16);
 }
-// Packed float16 subtract of the bias (both halves): exact for the small integers here.
+// float16 bits (both halves) of bias + 2^(VB-1): subtracting them from (bias + code)
+// leaves the centred code, code - 2^(VB-1), exactly.
+template <int VB>
+__device__ __forceinline__ unsigned centre_bits(unsigned bias) {
+  const float v = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(bias & 0xffffu))) +
+                  static_cast<float>(1 << (VB - 1));
+  const unsigned h = __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+  return h | (h << 16);
+}
+// Packed float16 subtract (both halves): exact for the small integers here.
 __device__ __forceinline__ unsigned sub_bias(unsigned x, unsigned bias) {
   const half2v r = __builtin_bit_cast(half2v, x) - __builtin_bit_cast(half2v, bias);
   return __builtin_bit_cast(unsigned, r);
@@ -137,12 +146,62 @@ __device__ __forceinline__ int v_dim(int row, int a) {
   if constexpr (VB == 2) return 4 * (row & 7) + 2 * a + (row >> 3);
   return 2 * row + a;
 }
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+typedef __attribute__((address_space(3))) unsigned char lbyte;
+
+// Byte layout of one (block, head) page; the host checks that it matches the
+// store layout before launching.
+template <int KB, int VB>
+struct PageLayout {
+  static constexpr int kc = 0;
+  static constexpr int ks = 256 * KB;
+  static constexpr int kn = ks + 256;
+  static constexpr int vc = kn + 64;
+  static constexpr int vsz = vc + 256 * VB;
+  static constexpr int bytes = vsz + 256;
+  static constexpr int copies = (bytes + 1023) / 1024;  // 64 lanes x 16 B per copy
+  static constexpr int lds = 1024 * copies;
+};
+
+// s_waitcnt with vmcnt <= n (lgkmcnt and expcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // The memory clobber keeps every LDS read of the staged page below the wait.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Copy one page from global memory straight into LDS (no registers): each
+// instruction moves 64 lanes x 16 B to dst + 16*lane; lanes past the page end
+// re-read the page start and only fill the LDS padding.
+template <int KB, int VB>
+__device__ __forceinline__ void stage_page(const unsigned char* page, unsigned char* dst, int lane) {
+  using PL = PageLayout<KB, VB>;
+#pragma unroll
+  for (int i = 0; i < PL::copies; ++i) {
+    const int off = 1024 * i + 16 * lane;
+    const unsigned char* src = page + (off < PL::bytes ? off : 0);
+    // Issued as inline asm on purpose: the compiler's wait insertion treats an
+    // LDS-DMA copy it can see as aliasing every later LDS read and drains the
+    // vector-memory counter before the first one, which serialises the double
+    // buffer.  Completion of these copies is awaited explicitly (wait_vmcnt).
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(unsigned long)(lbyte*)(dst + 1024 * i));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 ::"v"(src), "s"(m0) : "memory", "m0");
+  }
+}
+
+// The block table comes as its own read-only, non-aliased parameter so that the
+// wave-uniform block-id reads become scalar loads (they must not wait on the
+// vector-memory counter that tracks the page copies in flight).
 template <int NREP, int KB, int VB>
-__global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
+__global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int* __restrict__ btab) {
+  using PL = PageLayout<KB, VB>;
   constexpr int HPL = NREP > 4 ? 2 : 1;           // heads per lane in the score layout
   constexpr int VC = 16 * VB;                      // value-code bytes per token
   constexpr int LUTC = (KB == 4) ? 256 : (KB == 2 ? 512 : 64);  // dwords
-  constexpr float kMidCode = 0.5f * static_cast<float>((1 << VB) - 1);
+  constexpr float kMidCode = static_cast<float>(1 << (VB - 1));
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = a.seq_lens[b];
   const int start = split * a.split_tokens;
@@ -151,15 +210,36 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
 
   __shared__ unsigned lut_c[LUTC];
   __shared__ u32x4 lut_s[256];
-  __shared__ __attribute__((aligned(16))) unsigned char vst[4][2][16 * VC];       // staged value codes
+  // per wave, two stages of two pages each (the chunk being processed and the next)
+  __shared__ __attribute__((aligned(16))) unsigned char stg[4][2][2][PL::lds];
   __shared__ __attribute__((aligned(16))) unsigned short wl[4][4][2][NREP][32];  // P.V weights (fp16)
   __shared__ __attribute__((aligned(16))) unsigned zero16[4];
   __shared__ float mg_m[4][NREP], mg_l[4][NREP];
   __shared__ float mg_z[4][NREP][4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, kg = lane >> 4;
+  const long long tbl = static_cast<long long>(b) * a.max_blocks;
+  auto page_ptr = [&](int blk) {
+    return a.pool + (static_cast<long long>(blk) * a.Hkv + g) * a.block_bytes;
+  };
+
+  // first chunk of this wave: start its copy before the table/operand setup
+  int c0 = start + wave * 32;
+  int nb0 = 0, nb1 = 0;
+  if (c0 < end) {
+    const int b0 = btab[tbl + (c0 >> 4)];
+    const int b1 = (c0 + 16 < end) ? btab[tbl + (c0 >> 4) + 1] : b0;
+    stage_page<KB, VB>(page_ptr(b0), &stg[wave][0][0][0], lane);
+    stage_page<KB, VB>(page_ptr(b1), &stg[wave][0][1][0], lane);
+    const int cn = c0 + 128;
+    if (cn < end) {
+      nb0 = btab[tbl + (cn >> 4)];
+      nb1 = (cn + 16 < end) ? btab[tbl + (cn >> 4) + 1] : nb0;
+    }
+  }
 
   // ---- tables
   {
@@ -189,14 +269,21 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
     const int r = col & 3, g4 = col >> 2;
     const int h = g4 + 4 * r;
     const bool has = (h < NREP) && (NREP > 4 || r == 0);
-    const float* src = a.qu + static_cast<size_t>(b * a.Hq + g * NREP + (has ? h : 0)) * 256;
+    // unconditional vector loads from a valid row, then zero the rows without a head
+    const float* src = a.qu + static_cast<size_t>(b * a.Hq + g * NREP + (has ? h : 0)) * 256 + 32 * kg;
+    const float keep = has ? 1.0f : 0.0f;
+    floatx4 qv[8], uv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qv[i] = reinterpret_cast<const floatx4*>(src)[i];
+      uv[i] = reinterpret_cast<const floatx4*>(src + 128)[i];
+    }
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int d = 32 * kg + 8 * kc + j;
-        const float q = has ? src[d] : 0.0f;
-        const float u = has ? src[128 + d] : 0.0f;
+        const float q = keep * qv[2 * kc + (j >> 2)][j & 3];
+        const float u = keep * uv[2 * kc + (j >> 2)][j & 3];
         const _Float16 qh = static_cast<_Float16>(q);
         qhi[kc][j] = qh;
         qlo[kc][j] = static_cast<_Float16>(q - static_cast<float>(qh));
@@ -215,60 +302,40 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
 #pragma unroll
     for (int G = 0; G < 4; ++G) zacc[hs][G] = 0.0f;
   }
-  // accv: matrix-core accumulators, drained every kDrain chunks into accf
-  // (float32 vector adds, round to nearest) so that no matrix-core running sum
-  // spans more than kDrain*32 tokens.
-  floatx4 accv[8], accf[8];
+  floatx4 accv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) accv[i] = accf[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  int it = 0;
+  for (int i = 0; i < 8; ++i) accv[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const long long tbl = static_cast<long long>(b) * a.max_blocks;
-  unsigned char* myvst = &vst[wave][0][0];
-
-  for (int c0 = start + wave * 32; c0 < end; c0 += 128) {
-    const int pg = c0 >> 4;
-    const bool has1 = (c0 + 16) < end;
-    const int blk0 = a.block_table[tbl + pg];
-    const int blk1 = has1 ? a.block_table[tbl + pg + 1] : blk0;
-    const unsigned char* P[2] = {
-        a.pool + (static_cast<long long>(blk0) * a.Hkv + g) * a.block_bytes,
-        a.pool + (static_cast<long long>(blk1) * a.Hkv + g) * a.block_bytes};
-
-    // value codes of both pages -> LDS (whole pages, coalesced)
-    if constexpr (VB == 4) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(P[t] + a.off_vc + lane * 16);
-        *reinterpret_cast<u32x4*>(myvst + t * 16 * VC + lane * 16) = v;
+  // Pipeline: while a chunk is processed from one LDS stage, the next chunk's
+  // pages are already being copied into the other; block ids run one further.
+  int stage = 0;
+  for (; c0 < end; c0 += 128, stage ^= 1) {
+    const int cn = c0 + 128;
+    if (cn < end) {
+      stage_page<KB, VB>(page_ptr(nb0), &stg[wave][stage ^ 1][0][0], lane);
+      stage_page<KB, VB>(page_ptr(nb1), &stg[wave][stage ^ 1][1][0], lane);
+      const int cnn = cn + 128;
+      if (cnn < end) {
+        nb0 = btab[tbl + (cnn >> 4)];
+        nb1 = (cnn + 16 < end) ? btab[tbl + (cnn >> 4) + 1] : nb0;
       }
-    } else if constexpr (VB == 2) {
-      const int t = lane >> 5;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(P[t] + a.off_vc + (lane & 31) * 16);
-      *reinterpret_cast<u32x4*>(myvst + t * 16 * VC + (lane & 31) * 16) = v;
+      wait_vmcnt<2 * PL::copies>();
     } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const unsigned* src = reinterpret_cast<const unsigned*>(P[t] + a.off_vc + lane * 12);
-        unsigned* dst = reinterpret_cast<unsigned*>(myvst + t * 16 * VC + lane * 12);
-        dst[0] = src[0];
-        dst[1] = src[1];
-        dst[2] = src[2];
-      }
+      wait_vmcnt<0>();
     }
+    const unsigned char* pg[2] = {&stg[wave][stage][0][0], &stg[wave][stage][1][0]};
 
     // ---- scores: one 16-token tile per page
     float s[2][HPL];
-    unsigned vsz[2][4];
     bool valid[2];
+    unsigned vsz[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const unsigned char* pk = P[t];
+      const unsigned* kp = reinterpret_cast<const unsigned*>(pg[t] + PL::kc + col * (16 * KB) + kg * (4 * KB));
       unsigned kcw[KB];
-      const unsigned* kp = reinterpret_cast<const unsigned*>(pk + a.off_kc + col * (16 * KB) + kg * (4 * KB));
 #pragma unroll
       for (int i = 0; i < KB; ++i) kcw[i] = kp[i];
-      const unsigned ksw = *reinterpret_cast<const unsigned*>(pk + a.off_ks + col * 16 + kg * 4);
+      const unsigned ksw = *reinterpret_cast<const unsigned*>(pg[t] + PL::ks + col * 16 + kg * 4);
       floatx4 acca = {0.0f, 0.0f, 0.0f, 0.0f}, accb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
@@ -279,8 +346,8 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
         accb = mfma(qu16[kc], bs, accb);
       }
       // score layout: lane (token col, row group kg) holds head kg + 4*hs in slot hs
-      const unsigned kn = *reinterpret_cast<const unsigned*>(pk + a.off_kn + col * 4);
-      const u32x4 sz = *reinterpret_cast<const u32x4*>(pk + a.off_vsz + col * 16);
+      const unsigned kn = *reinterpret_cast<const unsigned*>(pg[t] + PL::kn + col * 4);
+      const u32x4 sz = *reinterpret_cast<const u32x4*>(pg[t] + PL::vsz + col * 16);
       vsz[t][0] = sz[0]; vsz[t][1] = sz[1]; vsz[t][2] = sz[2]; vsz[t][3] = sz[3];
       valid[t] = (c0 + 16 * t + col) < end;
       const float alpha = a.scale * kInvSqrtD * h_lo(kn);
@@ -321,10 +388,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
       }
       if (col >= NREP) fc = 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        accv[i] *= fc;
-        accf[i] *= fc;
-      }
+      for (int i = 0; i < 8; ++i) accv[i] *= fc;
     }
 #pragma unroll
     for (int hs = 0; hs < HPL; ++hs) {
@@ -344,14 +408,11 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
           const float w1 = valid[1] ? p[1][hs] * h_lo(vsz[1][G]) : 0.0f;
           const float z0 = valid[0] ? p[0][hs] * h_hi(vsz[0][G]) : 0.0f;
           const float z1 = valid[1] ? p[1][hs] * h_hi(vsz[1][G]) : 0.0f;
+          // value = (zero + mid*scale) + scale*(code - mid): the matrix cores take the
+          // centred part, so neither sum carries a large cancelling offset
+          zacc[hs][G] += z0 + z1 + kMidCode * (w0 + w1);
           const unsigned hi = pk_rtz(w0, w1);
-          const float e0 = w0 - h_lo(hi), e1 = w1 - h_hi(hi);
-          const unsigned lo = pk_rtz(e0, e1);
-          // The matrix cores see w' = hi + lo; the residual w - w' (exact in
-          // float32) is added back at the mid code, so the remaining error is
-          // sum (w - w')(code - mid), whose terms carry random signs.
-          const float r = (e0 - h_lo(lo)) + (e1 - h_hi(lo));
-          zacc[hs][G] += z0 + z1 + kMidCode * r;
+          const unsigned lo = pk_rtz(w0 - h_lo(hi), w1 - h_hi(hi));
           *reinterpret_cast<unsigned*>(&wl[wave][G][0][h][2 * col]) = hi;
           *reinterpret_cast<unsigned*>(&wl[wave][G][1][h][2 * col]) = lo;
         }
@@ -384,15 +445,16 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
           b0 = bias_bits(2 * f0);
           b1 = bias_bits(2 * (2 + f0));
         }
+        const unsigned c0s = centre_bits<VB>(b0), c1s = centre_bits<VB>(b1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int t = 4 * kg + q;
           u16x2 pr;
-          pr[0] = myvst[t * VC + byte];
-          pr[1] = myvst[16 * VC + t * VC + byte];
+          pr[0] = pg[0][PL::vc + t * VC + byte];
+          pr[1] = pg[1][PL::vc + t * VC + byte];
           const unsigned xv = __builtin_bit_cast(unsigned, pr);
-          x0[q] = sub_bias((xv & m0) | b0, b0);
-          x1[q] = sub_bias((xv & m1) | b1, b1);
+          x0[q] = sub_bias((xv & m0) | b0, c0s);
+          x1[q] = sub_bias((xv & m1) | b1, c1s);
         }
       } else {  // VB == 3: dims (2 col, 2 col + 1) of group G = bits 6 col .. +5 of the group's 96
         const int bit = 6 * col;
@@ -401,12 +463,12 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int t = 4 * kg + q;
-          const unsigned* g0 = reinterpret_cast<const unsigned*>(myvst + t * VC + 12 * G);
-          const unsigned* g1 = reinterpret_cast<const unsigned*>(myvst + 16 * VC + t * VC + 12 * G);
+          const unsigned* g0 = reinterpret_cast<const unsigned*>(pg[0] + PL::vc + t * VC + 12 * G);
+          const unsigned* g1 = reinterpret_cast<const unsigned*>(pg[1] + PL::vc + t * VC + 12 * G);
           const unsigned y0 = __builtin_amdgcn_alignbit(g0[w2], g0[w], sh);
           const unsigned y1 = __builtin_amdgcn_alignbit(g1[w2], g1[w], sh);
-          x0[q] = sub_bias((y0 & 7u) | ((y1 & 7u) << 16) | 0x64006400u, 0x64006400u);
-          x1[q] = sub_bias(((y0 >> 3) & 7u) | (((y1 >> 3) & 7u) << 16) | 0x64006400u, 0x64006400u);
+          x0[q] = sub_bias((y0 & 7u) | ((y1 & 7u) << 16) | 0x64006400u, centre_bits<VB>(0x64006400u));
+          x1[q] = sub_bias(((y0 >> 3) & 7u) | (((y1 >> 3) & 7u) << 16) | 0x64006400u, centre_bits<VB>(0x64006400u));
         }
       }
       const half8 a0 = as_h8(x0), a1 = as_h8(x1);
@@ -415,16 +477,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
       accv[2 * G + 1] = mfma(a1, whi, accv[2 * G + 1]);
       accv[2 * G + 1] = mfma(a1, wlo, accv[2 * G + 1]);
     }
-    if ((++it & (kDrain - 1)) == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        accf[i] += accv[i];
-        accv[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-    }
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) accf[i] += accv[i];
 
   // ---- per-wave results -> LDS, then merge the four waves
 #pragma unroll
@@ -457,7 +510,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int row = 4 * kg + r;
           const int d = 32 * G + v_dim<VB>(row, aa);
-          mbuf[(wave * NREP + h) * 128 + d] = accf[2 * G + aa][r] + z;
+          mbuf[(wave * NREP + h) * 128 + d] = accv[2 * G + aa][r] + z;
         }
       }
     }
@@ -509,6 +562,13 @@ void* pick_kb(int kb, int vb) {
 tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void* pool, const int* block_table,
                            int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const float* qu,
                            float* part, void* stream) {
+  {
+    const unsigned kb = L->cfg.k_bits, vb = L->cfg.v_bits;
+    const tq::Layout& ly = L->lay;
+    if (ly.off_kc != 0 || ly.off_ks != 256 * kb || ly.off_kn != 256 * kb + 256 || ly.off_vc != 256 * kb + 320 ||
+        ly.off_vsz != 256 * (kb + vb) + 320 || ly.block_bytes != 256 * (kb + vb) + 576)
+      return fail(TQ_ERR_UNSUPPORTED, "store layout does not match the decode kernels' page layout");
+  }
   MainArgs a;
   a.pool = static_cast<const unsigned char*>(pool);
   a.block_table = block_table;
@@ -537,7 +597,8 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
   }
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for rep=%d k_bits=%d v_bits=%d", plan.rep,
                        L->cfg.k_bits, L->cfg.v_bits);
-  void* args[] = {&a};
+  const int* btab = block_table;
+  void* args[] = {&a, &btab};
   const dim3 grid(plan.n_splits, L->cfg.n_kv_heads, plan.batch);
   hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode split-K launch: %s", hipGetErrorString(e));
