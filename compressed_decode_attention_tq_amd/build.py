@@ -17,8 +17,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", SRC,
           "--offload-arch=gfx950"]
-# Packed fp32 VALU forms are kept out of the generated code.
-DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
+# Packed fp32 VALU forms are kept out of the generated code.  Matrix-core
+# accumulators are kept in ordinary VGPRs (gfx950 MFMAs read and write them
+# directly), so loop-carried accumulators are not copied to and from AGPRs.
+DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = ["api.cpp", "host_state.cpp", "host_codebook.cpp", "profile.cpp", "compress.hip", "decode.hip", "decode_mainloop.hip"]
 
 

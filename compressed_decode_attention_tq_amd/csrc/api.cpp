@@ -144,10 +144,11 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   if (splits > 0) {
     split_tokens = ((ctx + splits - 1) / splits + 63) / 64 * 64;
   } else {
-    // Automatic: aim for ~4 workgroups per CU over (batch x kv_heads x splits),
-    // each split 256..4096 tokens (whole 64-token chunks).
+    // Automatic: one wave of workgroups, ~2 per CU (the mainloop's LDS use
+    // allows two resident per CU) over (batch x kv_heads x splits), each split
+    // 256..4096 tokens (whole 64-token chunks).
     const long long pairs = static_cast<long long>(batch) * L->cfg.n_kv_heads;
-    const long long target = 4LL * (L->cu_count > 0 ? L->cu_count : 256);
+    const long long target = 2LL * (L->cu_count > 0 ? L->cu_count : 256);
     const long long want = pairs > 0 ? (target + pairs - 1) / pairs : 1;
     long long t = (ctx + want - 1) / want;
     t = (t + 63) / 64 * 64;
@@ -162,7 +163,10 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   p.ws_qu = 0;
   p.ws_part = align(bh * 2 * kDim * sizeof(float));
-  p.ws_bytes = p.ws_part + align(bh * static_cast<size_t>(p.n_splits) * (kDim + 4) * sizeof(float));
+  p.ws_qa = p.ws_part + align(bh * static_cast<size_t>(p.n_splits) * (kDim + 4) * sizeof(float));
+  // Q.K operand: per (sequence, KV head) 1 or 2 tiles x 4 K-steps x 64 lanes x 8 float16
+  const size_t sets = p.rep == 8 ? 2 : 1;
+  p.ws_bytes = p.ws_qa + align(static_cast<size_t>(batch) * L->cfg.n_kv_heads * sets * 4 * 64 * 8 * 2);
   if (p.ws_bytes == 0) p.ws_bytes = 256;
   *plan = p;
   return TQ_OK;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
   if (slot < 0) return;
 
   __shared__ float sk[128], sv[128], srho[128], red[2];
-  __shared__ unsigned char ck[128], cv[128];
+  __shared__ unsigned char ck[128];
   __shared__ unsigned sbits[4];
   __shared__ __half sgroup[8];
 
@@ -143,7 +143,6 @@ __global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
   const float z = __half2float(z16);
   int code = 0;
   if (s > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((rv - z) / s), 0.0f), top));
-  cv[i] = static_cast<unsigned char>(code);
   if ((i & 31) == 0) {
     sgroup[(i >> 5) * 2] = s16;
     sgroup[(i >> 5) * 2 + 1] = z16;
@@ -152,12 +151,29 @@ __global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
 
   unsigned char* base = a.pool + (static_cast<size_t>(slot >> 4) * a.H + h) * a.block_bytes;
   const int off = static_cast<int>(slot & 15);
+  // value code of coordinate i: bits [(16 i + off) v_bits, +v_bits) of the
+  // dimension-major Vc stream.  Neighbouring tokens of the page share these
+  // words, so the field is cleared and set with atomics on disjoint bit masks.
+  {
+    unsigned* vw = reinterpret_cast<unsigned*>(base + a.off_vc);
+    const unsigned bit = static_cast<unsigned>(16 * i + off) * VB;
+    const unsigned w = bit >> 5, sh = bit & 31;
+    const unsigned mask = (1u << VB) - 1u;
+    const unsigned c = static_cast<unsigned>(code);
+    atomicAnd(&vw[w], ~(mask << sh));
+    atomicOr(&vw[w], c << sh);
+    if (sh + VB > 32) {
+      atomicAnd(&vw[w + 1], ~(mask >> (32 - sh)));
+      atomicOr(&vw[w + 1], c >> (32 - sh));
+    }
+  }
   if (i < 4 * KB) {
-    reinterpret_cast<unsigned*>(base + a.off_kc + off * (16 * KB))[i] = pack_word<KB>(ck, i);
-  } else if (i >= 32 && i < 32 + 4 * VB) {
-    reinterpret_cast<unsigned*>(base + a.off_vc + off * (16 * VB))[i - 32] = pack_word<VB>(cv, i - 32);
+    // word i of the 128-code key stream lies in 32-dim block i / KB
+    const int blk = i / KB, wi = i % KB;
+    reinterpret_cast<unsigned*>(base + a.off_kc + (blk * 16 + off) * (4 * KB))[wi] = pack_word<KB>(ck, i);
   } else if (i >= 64 && i < 68) {
-    reinterpret_cast<unsigned*>(base + a.off_ks + off * 16)[i - 64] = sbits[i - 64];
+    const int blk = i - 64;
+    *reinterpret_cast<unsigned*>(base + a.off_ks + (blk * 16 + off) * 4) = sbits[blk];
   } else if (i == 68) {
     const __half hn = __float2half_rn(n);
     const __half hg = __float2half_rn(sqrtf(g2));

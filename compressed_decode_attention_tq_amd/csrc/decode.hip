@@ -57,9 +57,18 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // ---------------------------------------------------------------- prologue
+// q' = R_g q and u = S_g q' in float32 (qu), and for compressed layers the
+// Q.K operand of the split-K mainloop (qa): q' and kappa*u split into float16
+// hi + lo pieces, placed as rows of the matrix-core A operand.  Dim i of a row
+// sits in lane row + 16 (i / 32), K-step (i % 32) / 8, element i % 8.
+// Rows (R = query heads per KV head, h = head within the group):
+//   R <= 4: one tile, rows part*R + h for parts q' hi, q' lo, ku hi, ku lo
+//           (rows 4R..15 zero)
+//   R == 8: tile 0 rows h / 8+h = q' hi / lo, tile 1 the same for kappa*u.
 template <bool QBF16, bool BYPASS>
 __global__ __launch_bounds__(128) void prologue_kernel(const void* q, const float* RT, const float* ST,
-                                                       float* qu, int Hq, int rep) {
+                                                       float* qu, unsigned short* qa, int Hq, int rep,
+                                                       float kappa) {
   const int bh = blockIdx.x;
   const int g = (bh % Hq) / rep;
   const int i = threadIdx.x;
@@ -87,6 +96,31 @@ __global__ __launch_bounds__(128) void prologue_kernel(const void* q, const floa
     for (int j = 0; j < 128; ++j) u = fmaf(st[j * 128 + i], sp[j], u);
     qu[bh * 256 + i] = a;
     qu[bh * 256 + 128 + i] = u;
+
+    const int b = bh / Hq, h = (bh % Hq) % rep, Hkv = Hq / rep;
+    const int nset = rep == 8 ? 2 : 1;
+    const int kgi = i >> 5, ks = (i >> 3) & 3, j = i & 7;
+    const float ku = kappa * u;
+    const _Float16 qh = static_cast<_Float16>(a), uh = static_cast<_Float16>(ku);
+    const _Float16 ql = static_cast<_Float16>(a - static_cast<float>(qh));
+    const _Float16 ul = static_cast<_Float16>(ku - static_cast<float>(uh));
+    auto put = [&](int set, int row, _Float16 v) {
+      const size_t at = ((((static_cast<size_t>(b) * Hkv + g) * nset + set) * 4 + ks) * 64 + row + 16 * kgi) * 8 + j;
+      qa[at] = __builtin_bit_cast(unsigned short, v);
+    };
+    if (rep == 8) {
+      put(0, h, qh);
+      put(0, 8 + h, ql);
+      put(1, h, uh);
+      put(1, 8 + h, ul);
+    } else {
+      put(0, h, qh);
+      put(0, rep + h, ql);
+      put(0, 2 * rep + h, uh);
+      put(0, 3 * rep + h, ul);
+      if (h == 0)
+        for (int row = 4 * rep; row < 16; ++row) put(0, row, static_cast<_Float16>(0.0f));
+    }
   }
 }
 
@@ -283,8 +317,10 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
                                    : reinterpret_cast<void*>(&prologue_kernel<false, false>);
     const float* RT = L->dRT;
     const float* ST = L->dST;
+    unsigned short* qa = reinterpret_cast<unsigned short*>(ws + plan.ws_qa);
     int Hq = plan.n_q_heads, rep = plan.rep;
-    void* args[] = {const_cast<void**>(&q), &RT, &ST, &qu, &Hq, &rep};
+    float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / kDim);  // sqrt(pi/2) / m, m = d
+    void* args[] = {const_cast<void**>(&q), &RT, &ST, &qu, &qa, &Hq, &rep, &kappa};
     ProfScope prof(kKPrologue, stream);
     hipError_t e = hipLaunchKernel(fn, dim3(bh), dim3(128), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));
@@ -292,8 +328,8 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   // 2. split-K mainloop
   if (!bypass) {
     ProfScope prof(kKSplitK, stream);
-    tq_status st = launch_splitk_tq(L, plan, pool, block_table, max_blocks_per_seq, seq_lens, softmax_scale, qu,
-                                    part, stream);
+    tq_status st = launch_splitk_tq(L, plan, pool, block_table, max_blocks_per_seq, seq_lens, softmax_scale,
+                                    ws + plan.ws_qa, part, stream);
     if (st != TQ_OK) return st;
   } else {
     DecodeArgs a;

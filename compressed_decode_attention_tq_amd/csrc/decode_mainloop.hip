@@ -7,23 +7,32 @@
 // Values ("How 0xsero/turboquant works", "Value Compression"):
 //   o' = sum_i p_i (zero_i + scale_i * code_i), per 32-wide group.
 //
-// Both contractions run on v_mfma_f32_16x16x32_f16 with float32 accumulation:
-//  * Q.K: A = q' split into two float16 pieces (hi + lo, 22 significant bits)
-//    and u in float16 (the QJL term is ~10% of a score); B = the float16 stored
-//    codebook values c[idx] (exact) and the +-1 signs (exact), dequantised from
-//    the packed codes through LDS lookup tables.  Rows = query heads of the GQA
-//    group (head h at row 4(h%4) + h/4), columns = 16 tokens, K = 32 dims.
-//  * P.V: A = the centred value codes, code - 2^(b-1), as float16 integers
-//    (a bias exponent OR-ed onto the masked code bits, then one packed
-//    subtract -- exact); B = w = p * scale split into two float16 pieces.  Rows = 16 coordinates,
-//    columns = query heads, K = 32 tokens (two pages).  The per-group offset
-//    sum_i p_i (zero_i + 2^(b-1) scale_i) is accumulated on the vector ALU.
-//    Centring keeps both sums free of a large cancelling offset, which
-//    matters because the matrix-core accumulate truncates.
+// Both contractions run on v_mfma_f32_16x16x32_f16 with float32 accumulation.
+//
+// Q.K: A = the query operand prepared by the prologue: q' and kappa*u, each
+// split into two float16 pieces (hi + lo, 22 significant bits), stacked as
+// rows of the 16-row tile (4 query heads: rows 0-3 q' hi, 4-7 q' lo, 8-11
+// kappa u hi, 12-15 kappa u lo; 8 heads use two tiles, q' and kappa u).
+// B = 16 tokens x 32 dims: the float16 stored codebook values c[idx] (exact)
+// in four K-steps, then the +-1 signs (exact) in four more, dequantised from
+// the packed codes through LDS lookup tables.  The code steps and the sign
+// steps accumulate separately; the rows are folded into one score per
+// (token, head) with cross-lane swaps, gamma applied to the sign part.
+//
+// P.V: A = 16 coordinates x 32 token slots: the centred value codes
+// code - 2^(b-1) as float16 integers (a bias exponent OR-ed onto the masked
+// code bits, then one packed subtract -- exact).  B = 32 token slots x 16
+// columns: w = p * scale in two float16 pieces, hi in columns 0..R-1 and lo in
+// columns R..2R-1 (R query heads), so one instruction takes both.  The
+// per-group offset sum_i p_i (zero_i + 2^(b-1) scale_i) is accumulated on the
+// vector ALU.  Centring keeps both sums free of a large cancelling offset,
+// which matters because the matrix-core accumulate truncates.
+//
 // A wave takes a 32-token chunk (two 16-token pages) at a time; the four waves
-// of a workgroup take chunks in turn and merge at the end.  Online softmax keeps
-// a running max per head (16-lane row reductions), rescaling only when the max
-// grows by more than kRescale (the factor is folded into the final merge).
+// of a workgroup take chunks in turn and merge at the end.  While a chunk is
+// processed from one LDS stage, the next chunk's pages are copied into the
+// other straight from global memory.  Online softmax keeps a running max per
+// head, rescaling only when it grows by more than kRescale.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -37,24 +46,23 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kPart = kDim + 4;
-constexpr float kRescale = 3.0f;   // tolerated growth of the running max (natural log units)
-constexpr float kKappa = 0.0097916396f;  // sqrt(pi/2) / 128
+constexpr float kRescale = 3.0f;  // tolerated growth of the running max (natural log units)
 constexpr float kInvSqrtD = 0.08838834764831845f;
 
 struct MainArgs {
   const unsigned char* pool;
-  const int* block_table;
   const int* seq_lens;
-  const float* qu;  // [B*Hq][2][128]: q' then u
+  const u32x4* qa;  // prologue output: [B*Hkv][sets][4 K-steps][64 lanes] x 8 float16
   float* part;      // [B*Hq][n_splits][kPart]
   long long max_blocks;
   int Hq, Hkv, n_splits, split_tokens;
   float scale;
-  unsigned block_bytes, off_kc, off_ks, off_kn, off_vc, off_vsz;
+  unsigned block_bytes;
   float cent[16];
 };
 
@@ -62,76 +70,107 @@ __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const fl
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ half8 as_h8(u32x4 v) { return __builtin_bit_cast(half8, v); }
-__device__ __forceinline__ float h_lo(unsigned w) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w & 0xffffu))); }
-__device__ __forceinline__ float h_hi(unsigned w) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16))); }
-__device__ __forceinline__ unsigned h_bits(float x) { return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x)); }
+__device__ __forceinline__ float h_lo(unsigned w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w & 0xffffu)));
+}
+__device__ __forceinline__ float h_hi(unsigned w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16)));
+}
+__device__ __forceinline__ unsigned h_bits(float x) {
+  return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
+}
 
-// Max over the 16 lanes of a row (lanes 16r..16r+15).
+// Max / sum over the 16 lanes of a row (lanes 16r..16r+15); every lane gets it.
+// One DPP-sourced VALU op per step; each step is preceded by the two wait
+// states a DPP read of a just-written VGPR needs.
+#define TQ_ROW_STEP(op, ctrl) \
+  asm volatile("s_nop 1\n\t" op " %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf" : "=v"(x) : "v"(x))
 __device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, __shfl_xor(x, 1, 64));
-  x = fmaxf(x, __shfl_xor(x, 2, 64));
-  x = fmaxf(x, __shfl_xor(x, 4, 64));
-  x = fmaxf(x, __shfl_xor(x, 8, 64));
+  TQ_ROW_STEP("v_max_f32_dpp", "quad_perm:[1,0,3,2]");
+  TQ_ROW_STEP("v_max_f32_dpp", "quad_perm:[2,3,0,1]");
+  TQ_ROW_STEP("v_max_f32_dpp", "row_ror:4");
+  TQ_ROW_STEP("v_max_f32_dpp", "row_ror:8");
   return x;
 }
 __device__ __forceinline__ float row_sum16(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  TQ_ROW_STEP("v_add_f32_dpp", "quad_perm:[1,0,3,2]");
+  TQ_ROW_STEP("v_add_f32_dpp", "quad_perm:[2,3,0,1]");
+  TQ_ROW_STEP("v_add_f32_dpp", "row_ror:4");
+  TQ_ROW_STEP("v_add_f32_dpp", "row_ror:8");
   return x;
 }
+// x + (x of the lane NREP columns further along the 16-lane row).
+template <int NREP>
+__device__ __forceinline__ float add_from_col(float x) {
+  float r;
+  if constexpr (NREP == 8)
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  else if constexpr (NREP == 4)
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:12 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  else if constexpr (NREP == 2)
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:14 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  else
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:15 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  return r;
+}
+#undef TQ_ROW_STEP
 
-// Packed float16 pair of (a, b), round toward zero; the remainder is exact in float32.
-__device__ __forceinline__ unsigned pk_rtz(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+// Cross-row exchanges (gfx950).  swap32(a, b): lanes 32..63 of a trade places
+// with lanes 0..31 of b.  swap16(a, b): odd 16-lane rows of a trade places with
+// the even rows of b.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                  false, false);
+  a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+  b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                  false, false);
+  a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
+  b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
 }
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+// (x & m) | b and (a << 16) | b in one instruction each (VOP3 takes at most one
+// scalar or literal operand on gfx950, so the constants are kept in VGPRs).
+__device__ __forceinline__ unsigned and_or(unsigned x, unsigned m, unsigned b) {
+  unsigned r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(b));
+  return r;
+}
+__device__ __forceinline__ unsigned hi16_or(unsigned a, unsigned b) {
+  unsigned r;
+  asm("v_lshl_or_b32 %0, %1, 16, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
-// float16 exponent bits (both halves) whose mantissa step at bit p is 1: value 2^(10-p).
-__device__ __forceinline__ unsigned bias_bits(int p) {
-  const unsigned e = static_cast<unsigned>(25 - p) << 10;
-  return e | (e << 16);
-}
-// float16 bits (both halves) of bias + 2^(VB-1): subtracting them from (bias + code)
-// leaves the centred code, code - 2^(VB-1), exactly.
-template <int VB>
-__device__ __forceinline__ unsigned centre_bits(unsigned bias) {
-  const float v = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(bias & 0xffffu))) +
-                  static_cast<float>(1 << (VB - 1));
-  const unsigned h = __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
-  return h | (h << 16);
-}
 // Packed float16 subtract (both halves): exact for the small integers here.
-__device__ __forceinline__ unsigned sub_bias(unsigned x, unsigned bias) {
-  const half2v r = __builtin_bit_cast(half2v, x) - __builtin_bit_cast(half2v, bias);
+__device__ __forceinline__ unsigned sub_h2(unsigned x, unsigned y) {
+  const half2v r = __builtin_bit_cast(half2v, x) - __builtin_bit_cast(half2v, y);
   return __builtin_bit_cast(unsigned, r);
 }
 
-// B operand of the Q.K product for K-chunk kc: the float16 codebook values of
-// the lane's 8 dims (32kg + 8kc .. +7), from the packed codes of those 32 dims.
+// B operand of the Q.K product for K-step s: the float16 codebook values of the
+// lane's 8 dims (32kg + 8s .. +7), from the packed codes of its 32-dim block.
 template <int KB>
-__device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int chunk, const unsigned* lut) {
+__device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const unsigned* lut) {
   u32x4 r;
   if constexpr (KB == 4) {
-    const unsigned x = kc[chunk];  // 8 nibbles = dims 8*chunk .. +7
+    const unsigned x = kc[s];  // 8 nibbles
     r[0] = lut[x & 0xffu];
     r[1] = lut[(x >> 8) & 0xffu];
     r[2] = lut[(x >> 16) & 0xffu];
     r[3] = lut[x >> 24];
   } else if constexpr (KB == 2) {
-    const unsigned x = kc[chunk >> 1] >> (16 * (chunk & 1));  // 16 bits = 8 dims
+    const unsigned x = kc[s >> 1] >> (16 * (s & 1));  // 16 bits = 8 dims
     const u32x2* l2 = reinterpret_cast<const u32x2*>(lut);
     const u32x2 a = l2[x & 0xffu];
     const u32x2 b = l2[(x >> 8) & 0xffu];
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  } else {  // KB == 3: 24 bits at bit 24*chunk of the lane's 96
-    const int bit = 24 * chunk;
+  } else {  // KB == 3: 24 bits at bit 24 s of the block's 96
+    const int bit = 24 * s;
     const int w = bit >> 5, sh = bit & 31;
-    const unsigned lo = kc[w];
-    const unsigned hi = (w + 1 < 3) ? kc[w + 1] : 0u;
-    const unsigned x = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
+    const unsigned x = (w + 1 < 3) ? __builtin_amdgcn_alignbit(kc[w + 1], kc[w], sh) : (kc[w] >> sh);
     r[0] = lut[x & 63u];
     r[1] = lut[(x >> 6) & 63u];
     r[2] = lut[(x >> 12) & 63u];
@@ -140,14 +179,54 @@ __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int chunk, con
   return as_h8(r);
 }
 
-// Row of a P.V tile holds dim 32G + dim_in_group(row, a).
-template <int VB>
-__device__ __forceinline__ int v_dim(int row, int a) {
-  if constexpr (VB == 2) return 4 * (row & 7) + 2 * a + (row >> 3);
-  return 2 * row + a;
+// float16 bits (both halves) whose exponent makes mantissa bit p weigh 1:
+// OR-ed onto a code field masked at bits p.., the value is 2^(10-p) + code.
+constexpr unsigned bias_bits(int p) { return static_cast<unsigned>(25 - p) * 0x04000400u; }
+// float16 bits (both halves) of 2^(10-p) + 2^(VB-1): subtracting them leaves the
+// centred code exactly.
+constexpr unsigned centre_bits(int p, int vb) {
+  return (static_cast<unsigned>(25 - p) * 0x0400u + ((1u << (vb - 1)) << p)) * 0x10001u;
 }
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
+
+// A operand of the P.V product for one 16-coordinate tile: coordinate d of
+// tokens 4kg .. 4kg+3 of both pages, slot 2cc + page.  Value codes are
+// dimension-major: coordinate d, token t at bits (16 d + t) v_bits of Vc.
+template <int VB>
+__device__ __forceinline__ half8 value_operand(const unsigned char* v0, const unsigned char* v1, int d, int kg) {
+  unsigned x;
+  if constexpr (VB == 4) {
+    const unsigned a = *reinterpret_cast<const unsigned short*>(v0 + 8 * d + 2 * kg);
+    const unsigned b = *reinterpret_cast<const unsigned short*>(v1 + 8 * d + 2 * kg);
+    x = hi16_or(b, a);
+  } else if constexpr (VB == 2) {
+    x = hi16_or(v1[4 * d + kg], v0[4 * d + kg]);
+  } else {  // VB == 3: 12 bits at bit 48 d + 12 kg (may straddle two words)
+    const int bit = 48 * d + 12 * kg;
+    const int w = bit >> 5, sh = bit & 31;
+    const unsigned* a = reinterpret_cast<const unsigned*>(v0) + w;
+    const unsigned* b = reinterpret_cast<const unsigned*>(v1) + w;
+    const unsigned fa = __builtin_amdgcn_alignbit(a[1], a[0], sh) & 0xfffu;
+    const unsigned fb = __builtin_amdgcn_alignbit(b[1], b[0], sh) & 0xfffu;
+    x = hi16_or(fb, fa);
+  }
+  // Field cc sits at bit VB*cc of each half.  Fields that end inside the
+  // float16 mantissa (bits 0..9) are used in place with a matching exponent;
+  // the others are shifted down by 8 first.
+  constexpr unsigned m = (1u << VB) - 1u;
+  u32x4 r;
+  const unsigned x8 = x >> 8;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const int p = VB * cc;
+    const bool fits = p + VB <= 10;
+    const int q = fits ? p : p - 8;
+    const unsigned src = fits ? x : x8;
+    const unsigned mask = (m << q) * 0x10001u;
+    r[cc] = sub_h2(and_or(src, mask, bias_bits(q)), centre_bits(q, VB));
+  }
+  return as_h8(r);
+}
+
 typedef __attribute__((address_space(3))) unsigned char lbyte;
 
 // Byte layout of one (block, head) page; the host checks that it matches the
@@ -186,9 +265,72 @@ __device__ __forceinline__ void stage_page(const unsigned char* page, unsigned c
     // vector-memory counter before the first one, which serialises the double
     // buffer.  Completion of these copies is awaited explicitly (wait_vmcnt).
     const unsigned m0 = __builtin_amdgcn_readfirstlane(
-        (unsigned)(unsigned long)(lbyte*)(dst + 1024 * i));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 ::"v"(src), "s"(m0) : "memory", "m0");
+        static_cast<unsigned>(reinterpret_cast<unsigned long>((lbyte*)(dst + 1024 * i))));  // LDS address
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  }
+}
+
+// Query heads of the group held by a lane of the score layout: lane (token
+// col, row group kg) holds head head(kg, hs) in slot hs.
+template <int NREP>
+struct ScoreMap {
+  static constexpr int HPL = NREP == 8 ? 2 : 1;  // heads per lane
+  static __device__ __forceinline__ int head(int kg, int hs) {
+    if constexpr (NREP == 8) return 4 * (kg & 1) + 2 * (kg >> 1) + hs;
+    if constexpr (NREP == 4 || NREP == 2) return kg;
+    return 0;
+  }
+  static __device__ __forceinline__ bool active(int kg) {
+    if constexpr (NREP >= 4) return true;
+    if constexpr (NREP == 2) return kg < 2;
+    return kg == 0;
+  }
+  // row group holding head h, and its slot
+  static __device__ __forceinline__ int kg_of(int h) {
+    if constexpr (NREP == 8) return ((h >> 2) & 1) | (((h >> 1) & 1) << 1);
+    if constexpr (NREP == 4 || NREP == 2) return h;
+    return 0;
+  }
+  static __device__ __forceinline__ int hs_of(int h) {
+    if constexpr (NREP == 8) return h & 1;
+    return 0;
+  }
+};
+
+// Fold the Q.K accumulators of one 16-token tile into scores (before the
+// per-token factor alpha): acc1 = code steps, acc2 = sign steps, g = gamma.
+template <int NREP>
+__device__ __forceinline__ void fold_scores(const floatx4& acc1, const floatx4& acc2, float g, int kg,
+                                            float (&out)[ScoreMap<NREP>::HPL]) {
+  if constexpr (NREP == 8) {
+    // tile 1 (q') rows 0-7 hi, 8-15 lo; tile 2 (kappa u) the same; row group kg
+    // holds rows 4kg..4kg+3 -> hi/lo halves are lanes l and l+32
+    float x0 = fmaf(g, acc2[0], acc1[0]), x1 = fmaf(g, acc2[1], acc1[1]);
+    float x2 = fmaf(g, acc2[2], acc1[2]), x3 = fmaf(g, acc2[3], acc1[3]);
+    swap32(x0, x2);
+    swap32(x1, x3);
+    out[0] = x0 + x2;
+    out[1] = x1 + x3;
+  } else if constexpr (NREP == 4) {
+    // row group kg: 0 q' hi, 1 q' lo, 2 kappa u hi, 3 kappa u lo; slot r = head
+    const bool sgn = kg >= 2;
+    float x0 = sgn ? g * acc2[0] : acc1[0], x1 = sgn ? g * acc2[1] : acc1[1];
+    float x2 = sgn ? g * acc2[2] : acc1[2], x3 = sgn ? g * acc2[3] : acc1[3];
+    swap32(x0, x2);
+    swap32(x1, x3);
+    float y0 = x0 + x2, y1 = x1 + x3;
+    swap16(y0, y1);
+    out[0] = y0 + y1;
+  } else if constexpr (NREP == 2) {
+    // rows 0-1 q' hi, 2-3 q' lo (row group 0), 4-5 kappa u hi, 6-7 lo (group 1)
+    float x0 = (kg == 1) ? g * (acc2[0] + acc2[2]) : acc1[0] + acc1[2];
+    float x1 = (kg == 1) ? g * (acc2[1] + acc2[3]) : acc1[1] + acc1[3];
+    swap16(x0, x1);
+    out[0] = x0 + x1;
+  } else {
+    // rows 0 q' hi, 1 q' lo, 2 kappa u hi, 3 kappa u lo (row group 0)
+    out[0] = (acc1[0] + acc1[1]) + g * (acc2[2] + acc2[3]);
   }
 }
 
@@ -198,8 +340,10 @@ __device__ __forceinline__ void stage_page(const unsigned char* page, unsigned c
 template <int NREP, int KB, int VB>
 __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int* __restrict__ btab) {
   using PL = PageLayout<KB, VB>;
-  constexpr int HPL = NREP > 4 ? 2 : 1;           // heads per lane in the score layout
-  constexpr int VC = 16 * VB;                      // value-code bytes per token
+  using SM = ScoreMap<NREP>;
+  constexpr int HPL = SM::HPL;
+  constexpr int NSET = NREP == 8 ? 2 : 1;
+  constexpr int WC = 2 * NREP;  // used P.V columns (hi, lo per head)
   constexpr int LUTC = (KB == 4) ? 256 : (KB == 2 ? 512 : 64);  // dwords
   constexpr float kMidCode = static_cast<float>(1 << (VB - 1));
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -212,7 +356,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   __shared__ u32x4 lut_s[256];
   // per wave, two stages of two pages each (the chunk being processed and the next)
   __shared__ __attribute__((aligned(16))) unsigned char stg[4][2][2][PL::lds];
-  __shared__ __attribute__((aligned(16))) unsigned short wl[4][4][2][NREP][32];  // P.V weights (fp16)
+  __shared__ __attribute__((aligned(16))) unsigned short wl[4][4][WC][32];  // P.V weights (float16)
   __shared__ __attribute__((aligned(16))) unsigned zero16[4];
   __shared__ float mg_m[4][NREP], mg_l[4][NREP];
   __shared__ float mg_z[4][NREP][4];
@@ -241,6 +385,16 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     }
   }
 
+  // ---- query operand (prepared by the prologue)
+  half8 qa[NSET][4];
+  {
+    const u32x4* src = a.qa + static_cast<size_t>(b * a.Hkv + g) * NSET * 4 * 64 + lane;
+#pragma unroll
+    for (int st = 0; st < NSET; ++st)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qa[st][s] = as_h8(src[(st * 4 + s) * 64]);
+  }
+
   // ---- tables
   {
     const int e = tid;  // 256 threads, 256 entries
@@ -262,38 +416,18 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     }
     if (tid < 4) zero16[tid] = 0u;
   }
-
-  // ---- Q.K A operands: row = l%16 -> head g4 + 4r (if any), dims 32kg + 8kc + j
-  half8 qhi[4], qlo[4], qu16[4];
-  {
-    const int r = col & 3, g4 = col >> 2;
-    const int h = g4 + 4 * r;
-    const bool has = (h < NREP) && (NREP > 4 || r == 0);
-    // unconditional vector loads from a valid row, then zero the rows without a head
-    const float* src = a.qu + static_cast<size_t>(b * a.Hq + g * NREP + (has ? h : 0)) * 256 + 32 * kg;
-    const float keep = has ? 1.0f : 0.0f;
-    floatx4 qv[8], uv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qv[i] = reinterpret_cast<const floatx4*>(src)[i];
-      uv[i] = reinterpret_cast<const floatx4*>(src + 128)[i];
-    }
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float q = keep * qv[2 * kc + (j >> 2)][j & 3];
-        const float u = keep * uv[2 * kc + (j >> 2)][j & 3];
-        const _Float16 qh = static_cast<_Float16>(q);
-        qhi[kc][j] = qh;
-        qlo[kc][j] = static_cast<_Float16>(q - static_cast<float>(qh));
-        qu16[kc][j] = static_cast<_Float16>(u);
-      }
-    }
-  }
   __syncthreads();
+  // Consume the query operand once here: the compiler then waits for its loads
+  // before the loop (together with the first page copies, which are needed
+  // anyway).  Left to the loop, that wait would also cover the next chunk's
+  // copies, which the compiler cannot tell apart, in every iteration.
+#pragma unroll
+  for (int st = 0; st < NSET; ++st)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(qa[st][s]));
 
-  // ---- per-wave running state
+  // ---- per-wave running state (score layout: slot hs = head SM::head(kg, hs))
+  const bool active = SM::active(kg);
   float m_used[HPL], lsum[HPL], zacc[HPL][4];
 #pragma unroll
   for (int hs = 0; hs < HPL; ++hs) {
@@ -305,9 +439,8 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   floatx4 accv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) accv[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float sc = a.scale * kInvSqrtD;
 
-  // Pipeline: while a chunk is processed from one LDS stage, the next chunk's
-  // pages are already being copied into the other; block ids run one further.
   int stage = 0;
   for (; c0 < end; c0 += 128, stage ^= 1) {
     const int cn = c0 + 128;
@@ -331,32 +464,34 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     unsigned vsz[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const unsigned* kp = reinterpret_cast<const unsigned*>(pg[t] + PL::kc + col * (16 * KB) + kg * (4 * KB));
+      const unsigned* kp = reinterpret_cast<const unsigned*>(pg[t] + PL::kc + (kg * 16 + col) * (4 * KB));
       unsigned kcw[KB];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) kcw[i] = kp[i];
-      const unsigned ksw = *reinterpret_cast<const unsigned*>(pg[t] + PL::ks + col * 16 + kg * 4);
-      floatx4 acca = {0.0f, 0.0f, 0.0f, 0.0f}, accb = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const half8 bc = dequant_keys<KB>(kcw, kc, lut_c);
-        const half8 bs = as_h8(lut_s[(ksw >> (8 * kc)) & 0xffu]);
-        acca = mfma(qhi[kc], bc, acca);
-        acca = mfma(qlo[kc], bc, acca);
-        accb = mfma(qu16[kc], bs, accb);
+      if constexpr (KB == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(kp);
+        kcw[0] = v[0]; kcw[1] = v[1]; kcw[2] = v[2]; kcw[3] = v[3];
+      } else if constexpr (KB == 3) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(kp);
+        kcw[0] = v[0]; kcw[1] = v[1]; kcw[2] = v[2];
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(kp);
+        kcw[0] = v[0]; kcw[1] = v[1];
       }
-      // score layout: lane (token col, row group kg) holds head kg + 4*hs in slot hs
+      const unsigned ksw = *reinterpret_cast<const unsigned*>(pg[t] + PL::ks + (kg * 16 + col) * 4);
+      floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f}, acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        acc1 = mfma(qa[0][st], dequant_keys<KB>(kcw, st, lut_c), acc1);
+        acc2 = mfma(qa[NSET - 1][st], as_h8(lut_s[(ksw >> (8 * st)) & 0xffu]), acc2);
+      }
       const unsigned kn = *reinterpret_cast<const unsigned*>(pg[t] + PL::kn + col * 4);
       const u32x4 sz = *reinterpret_cast<const u32x4*>(pg[t] + PL::vsz + col * 16);
       vsz[t][0] = sz[0]; vsz[t][1] = sz[1]; vsz[t][2] = sz[2]; vsz[t][3] = sz[3];
-      valid[t] = (c0 + 16 * t + col) < end;
-      const float alpha = a.scale * kInvSqrtD * h_lo(kn);
-      const float kgam = kKappa * h_hi(kn);
+      valid[t] = active && (c0 + 16 * t + col) < end;
+      float f[HPL];
+      fold_scores<NREP>(acc1, acc2, h_hi(kn), kg, f);
+      const float alpha = sc * h_lo(kn);
 #pragma unroll
-      for (int hs = 0; hs < HPL; ++hs) {
-        const float v = alpha * (acca[hs] + kgam * accb[hs]);
-        s[t][hs] = valid[t] ? v : -INFINITY;
-      }
+      for (int hs = 0; hs < HPL; ++hs) s[t][hs] = valid[t] ? alpha * f[hs] : -INFINITY;
     }
 
     // ---- online softmax (running max per head, lazy rescale)
@@ -379,14 +514,16 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
 #pragma unroll
         for (int G = 0; G < 4; ++G) zacc[hs][G] *= fac[hs];
       }
-      // P.V accumulators: column = head; its factor lives in score-layout row group h%4
-      float f0 = __shfl(fac[0], 16 * (col & 3), 64);
-      float fc = f0;
+      // P.V column col holds head col % NREP (hi, then lo); its factor lives in
+      // row group kg_of(head), slot hs_of(head)
+      const int hc = col % NREP;
+      const int srcl = 16 * SM::kg_of(hc);
+      float fc = __shfl(fac[0], srcl, 64);
       if constexpr (HPL == 2) {
-        const float f1 = __shfl(fac[1], 16 * (col & 3), 64);
-        fc = (col >= 4) ? f1 : f0;
+        const float f1 = __shfl(fac[1], srcl, 64);
+        fc = SM::hs_of(hc) ? f1 : fc;
       }
-      if (col >= NREP) fc = 1.0f;
+      if (col >= WC) fc = 1.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) accv[i] *= fc;
     }
@@ -397,122 +534,77 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       lsum[hs] += p[0][hs] + p[1][hs];
     }
 
-    // ---- P.V weights w = p * scale (two float16 pieces) -> LDS, zero term on the VALU
+    // ---- P.V weights w = p * scale in two float16 pieces -> LDS (slot 2 col + page);
+    //      offset term p (zero + mid scale) on the VALU
+    if (active) {
 #pragma unroll
-    for (int hs = 0; hs < HPL; ++hs) {
-      const int h = kg + 4 * hs;
-      if (h < NREP) {
+      for (int hs = 0; hs < HPL; ++hs) {
+        const int h = SM::head(kg, hs);
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
-          const float w0 = valid[0] ? p[0][hs] * h_lo(vsz[0][G]) : 0.0f;
-          const float w1 = valid[1] ? p[1][hs] * h_lo(vsz[1][G]) : 0.0f;
-          const float z0 = valid[0] ? p[0][hs] * h_hi(vsz[0][G]) : 0.0f;
-          const float z1 = valid[1] ? p[1][hs] * h_hi(vsz[1][G]) : 0.0f;
-          // value = (zero + mid*scale) + scale*(code - mid): the matrix cores take the
-          // centred part, so neither sum carries a large cancelling offset
-          zacc[hs][G] += z0 + z1 + kMidCode * (w0 + w1);
-          const unsigned hi = pk_rtz(w0, w1);
-          const unsigned lo = pk_rtz(w0 - h_lo(hi), w1 - h_hi(hi));
-          *reinterpret_cast<unsigned*>(&wl[wave][G][0][h][2 * col]) = hi;
-          *reinterpret_cast<unsigned*>(&wl[wave][G][1][h][2 * col]) = lo;
+          const _Float16 s0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[0][G] & 0xffffu));
+          const _Float16 s1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[1][G] & 0xffffu));
+          const _Float16 z0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[0][G] >> 16));
+          const _Float16 z1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[1][G] >> 16));
+          const float w0 = p[0][hs] * static_cast<float>(s0);
+          const float w1 = p[1][hs] * static_cast<float>(s1);
+          const _Float16 hi0 = static_cast<_Float16>(w0), hi1 = static_cast<_Float16>(w1);
+          const _Float16 lo0 = static_cast<_Float16>(fmaf(p[0][hs], static_cast<float>(s0), -static_cast<float>(hi0)));
+          const _Float16 lo1 = static_cast<_Float16>(fmaf(p[1][hs], static_cast<float>(s1), -static_cast<float>(hi1)));
+          zacc[hs][G] = fmaf(p[0][hs], fmaf(kMidCode, static_cast<float>(s0), static_cast<float>(z0)), zacc[hs][G]);
+          zacc[hs][G] = fmaf(p[1][hs], fmaf(kMidCode, static_cast<float>(s1), static_cast<float>(z1)), zacc[hs][G]);
+          const half2v hv = {hi0, hi1}, lv = {lo0, lo1};
+          *reinterpret_cast<half2v*>(&wl[wave][G][h][2 * col]) = hv;
+          *reinterpret_cast<half2v*>(&wl[wave][G][NREP + h][2 * col]) = lv;
         }
       }
     }
 
-    // ---- P.V on the matrix cores
+    // ---- P.V on the matrix cores: tile i = coordinates 16i .. 16i+15 (group i/2)
+    const unsigned char* v0 = pg[0] + PL::vc;
+    const unsigned char* v1 = pg[1] + PL::vc;
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
-      const u32x4* wsrc_hi = (col < NREP) ? reinterpret_cast<const u32x4*>(&wl[wave][G][0][col][8 * kg])
-                                          : reinterpret_cast<const u32x4*>(zero16);
-      const u32x4* wsrc_lo = (col < NREP) ? reinterpret_cast<const u32x4*>(&wl[wave][G][1][col][8 * kg])
-                                          : reinterpret_cast<const u32x4*>(zero16);
-      const half8 whi = as_h8(*wsrc_hi);
-      const half8 wlo = as_h8(*wsrc_lo);
-      u32x4 x0, x1;  // A operands of the group's two row tiles (codes as float16 integers)
-      if constexpr (VB == 4 || VB == 2) {
-        const int byte = (VB == 4) ? (16 * G + col) : (8 * G + (col & 7));
-        // field of tile a at bit p of each 16-bit half; OR-ing the float16
-        // exponent whose mantissa step at bit p is 1 gives (2^(10-p) + code),
-        // exactly; the packed subtract then leaves the code.
-        unsigned m0, m1, b0, b1;
-        if constexpr (VB == 4) {
-          m0 = 0x000F000Fu; b0 = 0x64006400u;   // bit 0: 1024 + code
-          m1 = 0x00F000F0u; b1 = 0x54005400u;   // bit 4:   64 + code
-        } else {
-          const int f0 = col >> 3;
-          m0 = 0x00030003u << (2 * f0);
-          m1 = 0x00030003u << (2 * (2 + f0));
-          b0 = bias_bits(2 * f0);
-          b1 = bias_bits(2 * (2 + f0));
-        }
-        const unsigned c0s = centre_bits<VB>(b0), c1s = centre_bits<VB>(b1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = 4 * kg + q;
-          u16x2 pr;
-          pr[0] = pg[0][PL::vc + t * VC + byte];
-          pr[1] = pg[1][PL::vc + t * VC + byte];
-          const unsigned xv = __builtin_bit_cast(unsigned, pr);
-          x0[q] = sub_bias((xv & m0) | b0, c0s);
-          x1[q] = sub_bias((xv & m1) | b1, c1s);
-        }
-      } else {  // VB == 3: dims (2 col, 2 col + 1) of group G = bits 6 col .. +5 of the group's 96
-        const int bit = 6 * col;
-        const int w = bit >> 5, sh = bit & 31;
-        const int w2 = (sh > 26) ? w + 1 : w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = 4 * kg + q;
-          const unsigned* g0 = reinterpret_cast<const unsigned*>(pg[0] + PL::vc + t * VC + 12 * G);
-          const unsigned* g1 = reinterpret_cast<const unsigned*>(pg[1] + PL::vc + t * VC + 12 * G);
-          const unsigned y0 = __builtin_amdgcn_alignbit(g0[w2], g0[w], sh);
-          const unsigned y1 = __builtin_amdgcn_alignbit(g1[w2], g1[w], sh);
-          x0[q] = sub_bias((y0 & 7u) | ((y1 & 7u) << 16) | 0x64006400u, centre_bits<VB>(0x64006400u));
-          x1[q] = sub_bias(((y0 >> 3) & 7u) | (((y1 >> 3) & 7u) << 16) | 0x64006400u, centre_bits<VB>(0x64006400u));
-        }
-      }
-      const half8 a0 = as_h8(x0), a1 = as_h8(x1);
-      accv[2 * G] = mfma(a0, whi, accv[2 * G]);
-      accv[2 * G] = mfma(a0, wlo, accv[2 * G]);
-      accv[2 * G + 1] = mfma(a1, whi, accv[2 * G + 1]);
-      accv[2 * G + 1] = mfma(a1, wlo, accv[2 * G + 1]);
+      const u32x4* wsrc = (col < WC) ? reinterpret_cast<const u32x4*>(&wl[wave][G][col][8 * kg])
+                                     : reinterpret_cast<const u32x4*>(zero16);
+      const half8 w = as_h8(*wsrc);
+      accv[2 * G] = mfma(value_operand<VB>(v0, v1, 32 * G + col, kg), w, accv[2 * G]);
+      accv[2 * G + 1] = mfma(value_operand<VB>(v0, v1, 32 * G + 16 + col, kg), w, accv[2 * G + 1]);
     }
   }
 
   // ---- per-wave results -> LDS, then merge the four waves
 #pragma unroll
   for (int hs = 0; hs < HPL; ++hs) {
-    const int h = kg + 4 * hs;
+    const int h = SM::head(kg, hs);
     const float ls = row_sum16(lsum[hs]);
     float zs[4];
 #pragma unroll
     for (int G = 0; G < 4; ++G) zs[G] = row_sum16(zacc[hs][G]);
-    if (h < NREP && col == 0) {
+    if (active && col == 0) {
       mg_m[wave][h] = m_used[hs];
       mg_l[wave][h] = ls;
 #pragma unroll
       for (int G = 0; G < 4; ++G) mg_z[wave][h][G] = zs[G];
     }
   }
-  __syncthreads();
-  // reuse the weight area (each wave's slice is its own former weight slice):
-  // acc [4 waves][NREP][128] floats
-  static_assert(sizeof(wl) == 4 * NREP * 128 * sizeof(float), "merge area size");
-  float* mbuf = reinterpret_cast<float*>(&wl[0][0][0][0][0]);
+  // P.V accumulators: lane (col, kg) holds coordinate 16i + 4kg + r of column
+  // col; add the lo column (col + NREP) onto the hi column
+  // (row rotate by 16 - NREP: lane c of a 16-lane row reads lane c + NREP)
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accv[i][r] = add_from_col<NREP>(accv[i][r]);
+  __syncthreads();  // every wave is past its loop: the staging area is free
+  float* mbuf = reinterpret_cast<float*>(&stg[0][0][0][0]);  // [4 waves][NREP][128]
+  static_assert(sizeof(stg) >= 4 * NREP * 128 * sizeof(float), "merge area size");
   if (col < NREP) {
     const int h = col;
 #pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      const float z = mg_z[wave][h][G];
+    for (int i = 0; i < 8; ++i) {
+      const float z = mg_z[wave][h][i >> 1];
 #pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * kg + r;
-          const int d = 32 * G + v_dim<VB>(row, aa);
-          mbuf[(wave * NREP + h) * 128 + d] = accv[2 * G + aa][r] + z;
-        }
-      }
+      for (int r = 0; r < 4; ++r) mbuf[(wave * NREP + h) * 128 + 16 * i + 4 * kg + r] = accv[i][r] + z;
     }
   }
   __syncthreads();
@@ -560,7 +652,7 @@ void* pick_kb(int kb, int vb) {
 }  // namespace
 
 tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void* pool, const int* block_table,
-                           int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const float* qu,
+                           int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const void* qa,
                            float* part, void* stream) {
   {
     const unsigned kb = L->cfg.k_bits, vb = L->cfg.v_bits;
@@ -571,9 +663,8 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
   }
   MainArgs a;
   a.pool = static_cast<const unsigned char*>(pool);
-  a.block_table = block_table;
   a.seq_lens = seq_lens;
-  a.qu = qu;
+  a.qa = static_cast<const u32x4*>(qa);
   a.part = part;
   a.max_blocks = max_blocks_per_seq;
   a.Hq = plan.n_q_heads;
@@ -582,11 +673,6 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
   a.split_tokens = plan.split_tokens;
   a.scale = softmax_scale;
   a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
-  a.off_kc = static_cast<unsigned>(L->lay.off_kc);
-  a.off_ks = static_cast<unsigned>(L->lay.off_ks);
-  a.off_kn = static_cast<unsigned>(L->lay.off_kn);
-  a.off_vc = static_cast<unsigned>(L->lay.off_vc);
-  a.off_vsz = static_cast<unsigned>(L->lay.off_vsz);
   for (int i = 0; i < 16; ++i) a.cent[i] = L->centroids[i];
   void* fn = nullptr;
   switch (plan.rep) {

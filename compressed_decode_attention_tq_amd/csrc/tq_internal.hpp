@@ -87,12 +87,13 @@ struct DecodePlan {
   int n_splits = 0;       // splits per sequence (grid x)
   size_t ws_qu = 0;       // byte offset of q'/u in the workspace
   size_t ws_part = 0;     // byte offset of split partials
+  size_t ws_qa = 0;       // byte offset of the Q.K matrix-core operand (compressed layers)
   size_t ws_bytes = 0;    // total
 };
 tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_len,
                       int num_splits, DecodePlan* plan);
 tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void* pool, const int* block_table,
-                           int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const float* qu,
+                           int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const void* qa,
                            float* part, void* stream);
 tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
                         const void* pool, const int* block_table, int max_blocks_per_seq,

@@ -45,14 +45,20 @@
  *
  * Store format (one pool per layer; exported by tq_store_layout)
  *   pool = uint8[num_blocks][n_kv_heads][block_bytes], 16 tokens per block,
- *   slot = block * 16 + offset.  Inside one (block, head) region, five
- *   token-major fields:
- *     Kc  [16][16*k_bits]  key codebook indices, LSB-first bitstream
- *                          (index j at bits [k_bits*j, k_bits*j + k_bits))
- *     Ks  [16][16]         QJL sign bits, bit j = 1 <=> (S rho)_j >= 0
- *     Kn  [16][2] fp16     ||k|| then gamma = ||rho||
- *     Vc  [16][16*v_bits]  value codes, LSB-first bitstream
- *     Vsz [16][4][2] fp16  per 32-wide group: scale then zero
+ *   slot = block * 16 + offset.  Inside one (block, head) region ("page"),
+ *   five fields.  Bit packing is LSB-first: element i of a b-bit stream
+ *   occupies stream bits [b*i, b*i + b), stream bit k being bit k%8 of byte k/8.
+ *     Kc  [4][16][4*k_bits]  key codebook indices: for 32-dim block j and token
+ *                            t, the k_bits stream of dims 32j .. 32j+31
+ *     Ks  [4][16][4]         QJL sign bits (1 <=> (S rho)_j >= 0), same blocking
+ *     Kn  [16][2] fp16       ||k|| then gamma = ||rho||
+ *     Vc  [128][16] v_bits   value codes, dimension-major: one stream over
+ *                            (dim, token) in the order dim*16 + token
+ *     Vsz [16][4][2] fp16    per 32-wide group: scale then zero
+ *   Key fields are blocked so that a 32-dim slice of one token is contiguous;
+ *   value codes are dimension-major so that one coordinate of consecutive
+ *   tokens is contiguous (the decode contraction runs over tokens).  A single
+ *   token appended to a page therefore shares Vc bytes with its neighbours.
  *   Bypass (uncompressed) layers: region = K [16][128] bf16, then V [16][128] bf16.
  */
 #ifndef TQ_H

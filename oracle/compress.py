@@ -28,7 +28,7 @@ import math
 
 import numpy as np
 
-from . import bits, codebook, layout as lay
+from . import codebook, layout as lay
 
 
 def compress_keys(K, R, S, centroids, boundaries):
@@ -93,19 +93,13 @@ def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     valid = slots >= 0
     K, V, slots = K[valid], V[valid], slots[valid]
     n_tok, H, d = K.shape
-    blocks, offs = np.divmod(slots, lay.P)
     out = {}
     for h in range(H):
         ck = compress_keys(K[:, h], state.R[h], state.S[h], state.centroids, state.boundaries)
         cv = compress_values(V[:, h], state.R[h], layout.v_bits, layout.group)
-        base = (blocks * H + h) * layout.block_bytes
-        _scatter(pool, base + layout.off_kc + offs * layout.kc_bytes, bits.pack(ck["idx"], layout.k_bits))
-        _scatter(pool, base + layout.off_ks + offs * layout.ks_bytes, bits.pack(ck["z"], 1))
-        kn = np.stack([ck["n16"], ck["gamma16"]], axis=-1).view(np.uint8)
-        _scatter(pool, base + layout.off_kn + offs * layout.kn_bytes, kn)
-        _scatter(pool, base + layout.off_vc + offs * layout.vc_bytes, bits.pack(cv["codes"], layout.v_bits))
-        sz = np.stack([cv["scale16"], cv["zero16"]], axis=-1).reshape(n_tok, -1).view(np.uint8)
-        _scatter(pool, base + layout.off_vsz + offs * layout.vsz_bytes, sz)
+        lay.put_records(pool, layout, H, slots, h, {
+            "idx": ck["idx"], "z": ck["z"], "n16": ck["n16"], "g16": ck["gamma16"],
+            "vcode": cv["codes"], "scale16": cv["scale16"], "zero16": cv["zero16"]})
         if keep:
             out[h] = (ck, cv)
     return out

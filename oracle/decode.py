@@ -26,7 +26,7 @@ import math
 
 import numpy as np
 
-from . import bits, layout as lay
+from . import layout as lay
 
 
 def gather(pool, layout, n_kv_heads, block_table_row, seq_len, head):
@@ -44,16 +44,11 @@ def gather(pool, layout, n_kv_heads, block_table_row, seq_len, head):
         kb = field(layout.off_kb, layout.kb_bytes).view(np.uint16)
         vb = field(layout.off_vb, layout.kb_bytes).view(np.uint16)
         return {"k": lay.bf16_bits_to_f64(kb), "v": lay.bf16_bits_to_f64(vb)}
-    kn = field(layout.off_kn, 4).view(np.float16).astype(np.float64)
-    sz = field(layout.off_vsz, layout.vsz_bytes).view(np.float16).astype(np.float64)
-    sz = sz.reshape(seq_len, -1, 2)
-    return {
-        "idx": bits.unpack(field(layout.off_kc, layout.kc_bytes), layout.k_bits, layout.d),
-        "z": bits.unpack(field(layout.off_ks, layout.ks_bytes), 1, layout.m),
-        "n16": kn[:, 0], "g16": kn[:, 1],
-        "vcode": bits.unpack(field(layout.off_vc, layout.vc_bytes), layout.v_bits, layout.d),
-        "scale16": sz[:, :, 0], "zero16": sz[:, :, 1],
-    }
+    slots = blocks * lay.P + offs
+    r = lay.get_records(pool, layout, n_kv_heads, slots, head)
+    for k in ("n16", "g16", "scale16", "zero16"):
+        r[k] = r[k].astype(np.float64)
+    return r
 
 
 def dequant_values(f, group):

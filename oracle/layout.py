@@ -11,12 +11,16 @@ this is the format both the oracle and the library write and read:
   pool = uint8[num_blocks][n_kv_heads][block_bytes],  P = 16 tokens per block,
   slot = block * P + offset.
 
-Inside one (block, head) region, five fields, each token-major:
-  Kc  [P][d*k_bits/8]    key codebook indices, LSB-first bitstream
-  Ks  [P][m/8]           QJL sign bits (bit j = 1 <=> y_j >= 0)
-  Kn  [P][2] fp16        ||k|| then gamma = ||rho||   (little-endian)
-  Vc  [P][d*v_bits/8]    value codes, LSB-first bitstream
-  Vsz [P][d/G][2] fp16   per group: scale then zero
+Inside one (block, head) region (a "page"), five fields.  All bit packing is
+LSB-first: element i of a b-bit stream occupies bits [b*i, b*i + b) of the
+stream, bit k of the stream being bit k%8 of byte k//8.
+  Kc  [d/32][P][4*k_bits]  key codebook indices: for each 32-dim block j and
+                           token t, the b-bit stream of dims 32j .. 32j+31
+  Ks  [m/32][P][4]         QJL sign bits (bit = 1 <=> y >= 0), same blocking
+  Kn  [P][2] fp16          ||k|| then gamma = ||rho||   (little-endian)
+  Vc  [d][P] x v_bits      value codes, dimension-major: one b-bit stream over
+                           (dim, token) pairs in the order dim*P + token
+  Vsz [P][d/G][2] fp16     per group: scale then zero
 Bypass (uncompressed) layers: region = Kb [P][d] bf16 followed by Vb [P][d] bf16.
 """
 
@@ -80,27 +84,80 @@ def f16_bytes(values):
     return np.asarray(values, dtype=np.float16).view(np.uint8)
 
 
-def write_compressed(pool, layout, n_kv_heads, slot, head, kc, ks, n16, g16, vc, scale16, zero16):
-    """Store one compressed (token, head) record.  kc/ks/vc are packed bytes."""
-    base, o = layout.region(n_kv_heads, slot, head)
-    _put(pool, base + layout.off_kc + o * layout.kc_bytes, kc)
-    _put(pool, base + layout.off_ks + o * layout.ks_bytes, ks)
-    _put(pool, base + layout.off_kn + o * layout.kn_bytes, f16_bytes([n16, g16]))
-    _put(pool, base + layout.off_vc + o * layout.vc_bytes, vc)
-    sz = np.stack([np.asarray(scale16, np.float16), np.asarray(zero16, np.float16)], axis=-1)
-    _put(pool, base + layout.off_vsz + o * layout.vsz_bytes, sz.view(np.uint8))
+def _bit_read(pool, bitpos, nbits):
+    """Unsigned ints from LSB-first bit fields starting at absolute bit positions."""
+    bitpos = np.asarray(bitpos, dtype=np.int64)
+    k = bitpos[..., None] + np.arange(nbits)
+    b = (pool[k // 8] >> (k % 8).astype(np.uint8)) & 1
+    return np.sum(b.astype(np.int64) << np.arange(nbits), axis=-1)
 
 
-def read_compressed(pool, layout, n_kv_heads, slot, head):
-    """Return the raw fields of one record: (kc, ks, n16, g16, vc, scale16, zero16)."""
-    base, o = layout.region(n_kv_heads, slot, head)
-    kc = _get(pool, base + layout.off_kc + o * layout.kc_bytes, layout.kc_bytes)
-    ks = _get(pool, base + layout.off_ks + o * layout.ks_bytes, layout.ks_bytes)
-    kn = _get(pool, base + layout.off_kn + o * layout.kn_bytes, 4).view(np.float16).astype(np.float64)
-    vc = _get(pool, base + layout.off_vc + o * layout.vc_bytes, layout.vc_bytes)
-    sz = _get(pool, base + layout.off_vsz + o * layout.vsz_bytes, layout.vsz_bytes)
-    sz = sz.view(np.float16).astype(np.float64).reshape(-1, 2)
-    return kc, ks, kn[0], kn[1], vc, sz[:, 0], sz[:, 1]
+def _bit_write(pool, bitpos, nbits, values):
+    """Write LSB-first bit fields (duplicate bytes across fields handled exactly)."""
+    bitpos = np.asarray(bitpos, dtype=np.int64)
+    values = np.broadcast_to(np.asarray(values, dtype=np.int64), bitpos.shape)
+    k = (bitpos[..., None] + np.arange(nbits)).ravel()
+    v = ((values[..., None] >> np.arange(nbits)) & 1).ravel().astype(np.uint8)
+    byte, bit = k // 8, (k % 8).astype(np.uint8)
+    np.bitwise_and.at(pool, byte, np.uint8(0xFF) ^ (np.uint8(1) << bit))
+    np.bitwise_or.at(pool, byte, v << bit)
+
+
+def _field_bits(layout, base, offs, name):
+    """Absolute bit positions [N, n] of every element of one field of tokens (base, offs)."""
+    base = np.asarray(base, dtype=np.int64)[:, None]
+    offs = np.asarray(offs, dtype=np.int64)[:, None]
+    if name == "idx":      # [N, d]: block j = dim // 32, element dim % 32 within the block's stream
+        dim = np.arange(layout.d)[None, :]
+        rec = (dim // 32) * P + offs
+        return (base + layout.off_kc) * 8 + rec * (32 * layout.k_bits) + (dim % 32) * layout.k_bits
+    if name == "z":        # [N, m]
+        j = np.arange(layout.m)[None, :]
+        rec = (j // 32) * P + offs
+        return (base + layout.off_ks) * 8 + rec * 32 + (j % 32)
+    if name == "vcode":    # [N, d]: dimension-major stream
+        dim = np.arange(layout.d)[None, :]
+        return (base + layout.off_vc) * 8 + (dim * P + offs) * layout.v_bits
+    raise KeyError(name)
+
+
+def put_records(pool, layout, n_kv_heads, slots, head, rec):
+    """Store compressed records of one KV head at `slots`.
+
+    rec: idx [N, d] and z [N, m] (ints), n16, g16 [N] (float16),
+    vcode [N, d] (ints), scale16, zero16 [N, d/G] (float16).
+    """
+    slots = np.asarray(slots, dtype=np.int64)
+    blocks, offs = np.divmod(slots, P)
+    base = (blocks * n_kv_heads + head) * layout.block_bytes
+    _bit_write(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits, rec["idx"])
+    _bit_write(pool, _field_bits(layout, base, offs, "z"), 1, rec["z"])
+    _bit_write(pool, _field_bits(layout, base, offs, "vcode"), layout.v_bits, rec["vcode"])
+    kn = np.stack([np.asarray(rec["n16"], np.float16), np.asarray(rec["g16"], np.float16)], axis=-1)
+    at = (base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(4)
+    pool[at] = kn.view(np.uint8).reshape(len(slots), 4)
+    sz = np.stack([np.asarray(rec["scale16"], np.float16), np.asarray(rec["zero16"], np.float16)], axis=-1)
+    at = (base + layout.off_vsz + offs * layout.vsz_bytes)[:, None] + np.arange(layout.vsz_bytes)
+    pool[at] = sz.reshape(len(slots), -1).view(np.uint8)
+
+
+def get_records(pool, layout, n_kv_heads, slots, head):
+    """Read the compressed records of one KV head at `slots` (fields as in put_records;
+    n16, g16, scale16, zero16 returned as float16)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    blocks, offs = np.divmod(slots, P)
+    base = (blocks * n_kv_heads + head) * layout.block_bytes
+    kn = pool[(base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(4)]
+    kn = np.ascontiguousarray(kn).view(np.float16)
+    sz = pool[(base + layout.off_vsz + offs * layout.vsz_bytes)[:, None] + np.arange(layout.vsz_bytes)]
+    sz = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots), -1, 2)
+    return {
+        "idx": _bit_read(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits),
+        "z": _bit_read(pool, _field_bits(layout, base, offs, "z"), 1),
+        "n16": kn[:, 0], "g16": kn[:, 1],
+        "vcode": _bit_read(pool, _field_bits(layout, base, offs, "vcode"), layout.v_bits),
+        "scale16": sz[:, :, 0], "zero16": sz[:, :, 1],
+    }
 
 
 def write_bypass(pool, layout, n_kv_heads, slot, head, k_bf16_bits, v_bf16_bits):

@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-from oracle import bits, compress, decode, layout as lay, state as ostate
+from oracle import compress, decode, layout as lay, state as ostate
 
 BAND = 1e-6
 
@@ -40,22 +40,7 @@ def f16_ulps(a, b):
 
 def fields_at(pool_bytes, layout, n_heads, slots, head):
     """Parse the records at `slots` (one head) out of raw pool bytes."""
-    slots = np.asarray(slots, dtype=np.int64)
-    blocks, offs = np.divmod(slots, lay.P)
-    base = (blocks * n_heads + head) * layout.block_bytes
-
-    def field(off, n):
-        return pool_bytes[(base + off + offs * n)[:, None] + np.arange(n)]
-
-    kn = field(layout.off_kn, 4).view(np.float16)
-    sz = field(layout.off_vsz, layout.vsz_bytes).view(np.float16).reshape(len(slots), -1, 2)
-    return {
-        "idx": bits.unpack(field(layout.off_kc, layout.kc_bytes), layout.k_bits, layout.d),
-        "z": bits.unpack(field(layout.off_ks, layout.ks_bytes), 1, layout.m),
-        "n16": kn[:, 0], "g16": kn[:, 1],
-        "vcode": bits.unpack(field(layout.off_vc, layout.vc_bytes), layout.v_bits, layout.d),
-        "scale16": sz[:, :, 0], "zero16": sz[:, :, 1],
-    }
+    return lay.get_records(pool_bytes, layout, n_heads, slots, head)
 
 
 def compare_compress(gpu, ck, cv, S, boundaries, V, v_bits, group=32):

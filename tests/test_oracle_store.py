@@ -46,21 +46,79 @@ def test_block_and_record_bytes():
     assert abs(metrics.compression_ratio(blog) - ref["blog_ratio"]) < 1e-4
 
 
-def test_record_round_trip():
-    lay = layout.StoreLayout(128, 3, 2, 32)
-    pool = layout.new_pool(4, 2, lay)
-    rng = np.random.default_rng(0)
-    kc = rng.integers(0, 256, lay.kc_bytes)
-    ks = rng.integers(0, 256, lay.ks_bytes)
-    vc = rng.integers(0, 256, lay.vc_bytes)
-    sc = np.float16([0.5, 0.25, 2.0, 1.5])
-    ze = np.float16([-1.0, -2.0, 0.125, 3.0])
-    layout.write_compressed(pool, lay, 2, 37, 1, kc, ks, 3.5, 0.75, vc, sc, ze)
-    got = layout.read_compressed(pool, lay, 2, 37, 1)
-    assert np.array_equal(got[0], kc) and np.array_equal(got[1], ks) and np.array_equal(got[4], vc)
-    assert got[2] == 3.5 and got[3] == 0.75
-    assert np.array_equal(got[5], sc) and np.array_equal(got[6], ze)
-    # slot 37 = block 2, offset 5, head 1 -> region 5
-    base = (2 * 2 + 1) * lay.block_bytes
-    assert pool[base + lay.off_kc + 5 * lay.kc_bytes] == kc[0]
-    assert np.count_nonzero(pool[:base]) == 0
+def _records(lay, n, seed):
+    rng = np.random.default_rng(seed)
+    G = lay.d // lay.group
+    return {
+        "idx": rng.integers(0, 1 << lay.k_bits, (n, lay.d)),
+        "z": rng.integers(0, 2, (n, lay.m)),
+        "n16": rng.standard_normal(n).astype(np.float16),
+        "g16": rng.standard_normal(n).astype(np.float16),
+        "vcode": rng.integers(0, 1 << lay.v_bits, (n, lay.d)),
+        "scale16": rng.standard_normal((n, G)).astype(np.float16),
+        "zero16": rng.standard_normal((n, G)).astype(np.float16),
+    }
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2), (2, 3)])
+def test_record_round_trip(kb, vb):
+    """Records written at scattered slots (several sharing pages) read back exactly,
+    and neighbouring tokens of a page are not disturbed."""
+    lay = layout.StoreLayout(128, kb, vb, 32)
+    pool = layout.new_pool(6, 2, lay)
+    slots = np.array([37, 5, 36, 80, 38, 0, 95, 17])
+    rec = _records(lay, len(slots), kb * 10 + vb)
+    layout.put_records(pool, lay, 2, slots, 1, rec)
+    got = layout.get_records(pool, lay, 2, slots, 1)
+    for k in rec:
+        assert np.array_equal(got[k], rec[k]), k
+    # rewriting one token leaves the others of its page intact
+    rec2 = _records(lay, 1, 99)
+    layout.put_records(pool, lay, 2, [36], 1, rec2)
+    again = layout.get_records(pool, lay, 2, slots, 1)
+    for k in rec:
+        assert np.array_equal(np.delete(again[k], 2, axis=0), np.delete(rec[k], 2, axis=0)), k
+        assert np.array_equal(again[k][2], rec2[k][0]), k
+    # head 0 untouched
+    for b in range(6):
+        base = (b * 2) * lay.block_bytes
+        assert np.count_nonzero(pool[base: base + lay.block_bytes]) == 0
+
+
+def test_record_placement_by_hand():
+    """Hand-computed positions of single set bits (K3/V3 store, slot 37 = block 2
+    offset 5, head 1 of 2 -> region 5)."""
+    lay = layout.StoreLayout(128, 3, 3, 32)
+    base = 5 * lay.block_bytes
+    zero = {k: np.zeros_like(v) for k, v in _records(lay, 1, 0).items()}
+    # key dim 33 = block 1, element 1, code 0b100 -> stream bit 3*1 + 2 = 5 of
+    # record (block 1, token 5) = record index 1*16 + 5 = 21, 12 bytes each
+    r = dict(zero, idx=zero["idx"].copy())
+    r["idx"][0, 33] = 4
+    pool = layout.new_pool(3, 2, lay)
+    layout.put_records(pool, lay, 2, [37], 1, r)
+    nz = np.flatnonzero(pool)
+    assert list(nz) == [base + lay.off_kc + 21 * 12] and pool[nz[0]] == 1 << 5
+    # sign 70 = block 2, element 6 -> record 2*16 + 5 = 37 (4 bytes), bit 6
+    r = dict(zero, z=zero["z"].copy())
+    r["z"][0, 70] = 1
+    pool = layout.new_pool(3, 2, lay)
+    layout.put_records(pool, lay, 2, [37], 1, r)
+    nz = np.flatnonzero(pool)
+    assert list(nz) == [base + lay.off_ks + 37 * 4] and pool[nz[0]] == 1 << 6
+    # value dim 9, code 0b010: stream element 9*16 + 5 = 149, bits 447..449 -> bit 448
+    r = dict(zero, vcode=zero["vcode"].copy())
+    r["vcode"][0, 9] = 2
+    pool = layout.new_pool(3, 2, lay)
+    layout.put_records(pool, lay, 2, [37], 1, r)
+    nz = np.flatnonzero(pool)
+    assert list(nz) == [base + lay.off_vc + 56] and pool[nz[0]] == 1 << 0
+    # norms and group metadata are token-major fp16 pairs
+    r = dict(zero, n16=np.float16([1.0]), zero16=zero["zero16"].copy())
+    r["zero16"][0, 2] = np.float16(-2.0)
+    pool = layout.new_pool(3, 2, lay)
+    layout.put_records(pool, lay, 2, [37], 1, r)
+    assert pool[base + lay.off_kn + 20: base + lay.off_kn + 22].view(np.float16)[0] == 1.0
+    at = base + lay.off_vsz + 5 * 16 + 2 * 4 + 2
+    assert pool[at: at + 2].view(np.float16)[0] == -2.0
+    assert np.count_nonzero(pool) == 2      # 0x3C00 and 0xC000: one nonzero byte each
