@@ -269,6 +269,32 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
                          static_cast<hipStream_t>(hip_stream));
       if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
     }
+    // float16 hi + lo split of R and S (x = hi + lo to 22 bits), in the matrix-core
+    // A-operand order the compressor loads per wave
+    const size_t nop = static_cast<size_t>(H) * 8 * 4 * 4 * 64 * 8;
+    std::vector<unsigned short> opa(nop);
+    for (int h = 0; h < H; ++h)
+      for (int w = 0; w < 8; ++w)
+        for (int set = 0; set < 4; ++set)
+          for (int ks = 0; ks < 4; ++ks)
+            for (int l = 0; l < 64; ++l)
+              for (int j = 0; j < 8; ++j) {
+                const int row = 16 * w + l % 16, col = 32 * ks + 8 * (l / 16) + j;
+                const std::vector<float>& M = (set < 2) ? R : S;
+                const float x = M[(static_cast<size_t>(h) * d + row) * d + col];
+                const _Float16 hi = static_cast<_Float16>(x);
+                const _Float16 v = (set % 2 == 0) ? hi : static_cast<_Float16>(x - static_cast<float>(hi));
+                const size_t at = (((((static_cast<size_t>(h) * 8 + w) * 4 + set) * 4 + ks) * 64 + l) * 8) + j;
+                opa[at] = __builtin_bit_cast(unsigned short, v);
+              }
+    e = hipMalloc(reinterpret_cast<void**>(&L->dOpA), nop * sizeof(unsigned short));
+    if (e != hipSuccess) {
+      tq_layer_destroy(L);
+      return fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc of layer state failed: %s", hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(L->dOpA, opa.data(), nop * sizeof(unsigned short), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
     e = hipStreamSynchronize(static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipStreamSynchronize"); }
   }
@@ -282,10 +308,12 @@ tq_status tq_layer_destroy(tq_layer* L) {
   hipError_t e1 = L->dR ? hipFree(L->dR) : hipSuccess;
   hipError_t e2 = L->dRT ? hipFree(L->dRT) : hipSuccess;
   hipError_t e3 = L->dST ? hipFree(L->dST) : hipSuccess;
+  hipError_t e4 = L->dOpA ? hipFree(L->dOpA) : hipSuccess;
   delete L;
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
   if (e3 != hipSuccess) return hip_fail(e3, "hipFree");
+  if (e4 != hipSuccess) return hip_fail(e4, "hipFree");
   return TQ_OK;
 }
 

@@ -25,8 +25,9 @@
 // columns: w = p * scale in two float16 pieces, hi in columns 0..R-1 and lo in
 // columns R..2R-1 (R query heads), so one instruction takes both.  The
 // per-group offset sum_i p_i (zero_i + 2^(b-1) scale_i) is accumulated on the
-// vector ALU.  Centring keeps both sums free of a large cancelling offset,
-// which matters because the matrix-core accumulate truncates.
+// vector ALU.  Centring keeps both sums free of a large cancelling offset (each
+// accumulate rounds at the accumulator's magnitude, so a 1024-biased code would
+// bury the signal).
 //
 // A wave takes a 32-token chunk (two 16-token pages) at a time; the four waves
 // of a workgroup take chunks in turn and merge at the end.  While a chunk is

@@ -69,6 +69,10 @@ struct tq_layer {
   float* dR = nullptr;
   float* dRT = nullptr;
   float* dST = nullptr;
+  // Matrix-core A operands of R and S for the compressor, float16 bit patterns:
+  // [H][8 row tiles][4 sets: R hi, R lo, S hi, S lo][4 K-steps][64 lanes][8],
+  // lane l of (tile w, step s) holding M[16w + l%16][32s + 8(l/16) .. +7].
+  unsigned short* dOpA = nullptr;
   float centroids[16] = {0};
   float boundaries[16] = {0};
   int levels = 0;
@@ -80,6 +84,12 @@ namespace tq {
 tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype,
                           long long n_tokens, long long k_stride, long long v_stride,
                           const long long* slots, void* pool, void* stream);
+// Matrix-core compressor (bf16 inputs, 64+ tokens, 16-byte aligned rows).
+bool compress_mfma_applies(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype, long long n_tokens,
+                           long long k_stride, long long v_stride);
+tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, long long n_tokens,
+                               long long k_stride, long long v_stride, const long long* slots, void* pool,
+                               void* stream);
 
 struct DecodePlan {
   int batch = 0, n_q_heads = 0, rep = 0;

@@ -78,6 +78,24 @@ def test_compress_bits_ragged_slots(kb, vb):
         assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
 
+@pytest.mark.parametrize("kb,vb,n,offset", [(4, 4, 2000, 37), (3, 2, 1000, 0), (2, 3, 777, 16)])
+def test_compress_page_runs(kb, vb, n, offset):
+    """bf16 runs of consecutive slots: whole aligned pages (stored whole), a ragged
+    last tile, and runs that start mid-page (every tile scattered token by token)."""
+    torch = _torch()
+    say("compress page runs", kb, vb, n, offset)
+    K, V = synth.kv_host(150 + kb * 10 + vb, n, 8, outliers=4)
+    slots = np.arange(n, dtype=np.int64) + offset
+    nb = (n + offset + 15) // 16 + 1
+    gpu = _gpu_compress(torch, K, V, slots, nb, 8, kb, vb, 220, layer=kb * vb)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, 8, kb, vb, 220, layer=kb * vb)
+    _check_compress(gpu, res, st, layout, 8, slots, V, kb, vb)
+    # pages before the run and after it are untouched
+    first, last = offset // 16, (n + offset - 1) // 16
+    assert not gpu[:first * 8 * layout.block_bytes].any()
+    assert not gpu[(last + 1) * 8 * layout.block_bytes:].any()
+
+
 def test_compress_full_size_sampled():
     """1,048,576 tokens x 8 KV heads bf16 (K2+QJL / V3), checked on 2048 sampled tokens."""
     torch = _torch()
