@@ -269,24 +269,36 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
                          static_cast<hipStream_t>(hip_stream));
       if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
     }
-    // float16 hi + lo split of R and S (x = hi + lo to 22 bits), in the matrix-core
-    // A-operand order the compressor loads per wave
-    const size_t nop = static_cast<size_t>(H) * 8 * 4 * 4 * 64 * 8;
+    // Matrix-core A operands for the compressor: R as three bf16 pieces
+    // (hi + mid + lo = R exactly) and S as two float16 pieces (22 bits), in the
+    // order the compressor loads per wave.
+    auto bf16_rne = [](float x) -> unsigned short {
+      const unsigned u = __builtin_bit_cast(unsigned, x);
+      return static_cast<unsigned short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    };
+    auto bf16_val = [](unsigned short b) { return __builtin_bit_cast(float, static_cast<unsigned>(b) << 16); };
+    const size_t nop = static_cast<size_t>(H) * 8 * kOpSets * 4 * 64 * 8;
     std::vector<unsigned short> opa(nop);
     for (int h = 0; h < H; ++h)
       for (int w = 0; w < 8; ++w)
-        for (int set = 0; set < 4; ++set)
-          for (int ks = 0; ks < 4; ++ks)
-            for (int l = 0; l < 64; ++l)
-              for (int j = 0; j < 8; ++j) {
-                const int row = 16 * w + l % 16, col = 32 * ks + 8 * (l / 16) + j;
-                const std::vector<float>& M = (set < 2) ? R : S;
-                const float x = M[(static_cast<size_t>(h) * d + row) * d + col];
-                const _Float16 hi = static_cast<_Float16>(x);
-                const _Float16 v = (set % 2 == 0) ? hi : static_cast<_Float16>(x - static_cast<float>(hi));
-                const size_t at = (((((static_cast<size_t>(h) * 8 + w) * 4 + set) * 4 + ks) * 64 + l) * 8) + j;
-                opa[at] = __builtin_bit_cast(unsigned short, v);
+        for (int ks = 0; ks < 4; ++ks)
+          for (int l = 0; l < 64; ++l)
+            for (int j = 0; j < 8; ++j) {
+              const int row = 16 * w + l % 16, col = 32 * ks + 8 * (l / 16) + j;
+              const float r = R[(static_cast<size_t>(h) * d + row) * d + col];
+              const float sv = S[(static_cast<size_t>(h) * d + row) * d + col];
+              const unsigned short r0 = bf16_rne(r);
+              const unsigned short r1 = bf16_rne(r - bf16_val(r0));
+              const unsigned short r2 = bf16_rne(r - bf16_val(r0) - bf16_val(r1));
+              const _Float16 s0 = static_cast<_Float16>(sv);
+              const _Float16 s1 = static_cast<_Float16>(sv - static_cast<float>(s0));
+              const unsigned short v[kOpSets] = {r0, r1, r2, __builtin_bit_cast(unsigned short, s0),
+                                                 __builtin_bit_cast(unsigned short, s1)};
+              for (int set = 0; set < kOpSets; ++set) {
+                const size_t at = (((((static_cast<size_t>(h) * 8 + w) * kOpSets + set) * 4 + ks) * 64 + l) * 8) + j;
+                opa[at] = v[set];
               }
+            }
     e = hipMalloc(reinterpret_cast<void**>(&L->dOpA), nop * sizeof(unsigned short));
     if (e != hipSuccess) {
       tq_layer_destroy(L);

@@ -8,20 +8,22 @@
 //   values: v' = R v; per 32-group scale16 = fp16((max-min)/(2^b-1)), zero16 = fp16(min),
 //           code = clamp(rint((v' - zero16)/scale16), 0, 2^b-1)  (0 when scale16 == 0)
 //
-// The three 128x128 contractions (R k, R v, S rho) are v_mfma_f32_16x16x32_f16
-// tiles: 16 output coordinates x 16 tokens x 32 inputs.  float16 operands carry
-// float32 precision by splitting: R = R_hi + R_lo and S = S_hi + S_lo (22
-// significant bits, prepared once per layer), rho = rho_hi + rho_lo; bf16 inputs
-// are exact in float16 after a power-of-two scale per vector (the norm's
-// exponent).  Products are exact, each instruction sums exactly and rounds once
-// to nearest, so every contraction chains its split passes into one float32
-// accumulator: R k = R_hi k + R_lo k, S rho = S_hi rho_hi + S_hi rho_lo + S_lo rho_hi.
+// The three 128x128 contractions are 16x16x32 matrix-core tiles (16 output
+// coordinates x 16 tokens x 32 inputs).  The matrix core forms exact products,
+// sums them exactly and rounds once to nearest per instruction, so split
+// operands give float32-faithful results chained in one accumulator:
+//  * R k and R v on the bf16 MFMA: the bf16 inputs are the B operand as they
+//    are, R is three bf16 pieces (hi + mid + lo = R exactly);
+//  * S rho on the float16 MFMA: S and rho as float16 hi + lo pieces (22 bits),
+//    S rho = S_hi rho_hi + S_hi rho_lo + S_lo rho_hi.
 //
 // A workgroup is 8 waves and serves one KV head: wave w owns output rows
-// 16w..16w+15 and keeps its R and S operands in registers for the whole launch.
-// Tiles of 16 tokens stream through: their K and V rows are copied straight into
-// LDS (double-buffered), scaled to float16 operands once, contracted, quantised,
-// and the results assembled into a page image in LDS.  A tile that is one whole
+// 16w..16w+15 and keeps its R operands (and S_lo) in registers, S_hi in LDS, for
+// the whole launch.  Tiles of 16 tokens stream through: their K and V rows are
+// copied straight into a ring of LDS slots several tiles ahead (each row rotated
+// by its token index so that the lanes reading one 32-dim slice hit distinct
+// banks), contracted, quantised, and the packed fields written into a page
+// image in LDS.  A tile that is one whole
 // aligned page (16 consecutive slots from a multiple of 16) is stored with
 // coalesced 16-byte writes; any other tile is scattered token by token, with the
 // dimension-major value codes set by atomic clear/set of their bits.
@@ -36,12 +38,13 @@ namespace tq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lbyte;
 
-constexpr int kRow = 136;  // float16 elements per LDS operand row (128 + pad)
+constexpr int kRow = 136;      // float16 elements per LDS operand row (128 + pad)
 constexpr int kCodeRow = 132;  // bytes per LDS code row (128 + pad)
 
 struct CArgs {
@@ -58,25 +61,34 @@ struct CArgs {
   float bnd[16];
 };
 
-__device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
+__device__ __forceinline__ floatx4 mfma_h(const half8& a, const half8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ half8 as_h8(u32x4 v) { return __builtin_bit_cast(half8, v); }
+__device__ __forceinline__ floatx4 mfma_b(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
-// Cross-row exchanges (gfx950): see the decode mainloop.
+// Cross-row exchanges (gfx950): swap32(a, b) trades lanes 32..63 of a with
+// lanes 0..31 of b; swap16(a, b) trades the odd 16-lane rows of a with the even
+// rows of b.
 __device__ __forceinline__ void swap32(float& a, float& b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
                                                   false, false);
   a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
   b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
 }
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
-                                                  false, false);
-  a = __builtin_bit_cast(float, static_cast<unsigned>(r[0]));
-  b = __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+__device__ __forceinline__ void swap16u(unsigned& a, unsigned& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = static_cast<unsigned>(r[0]);
+  b = static_cast<unsigned>(r[1]);
 }
-// Sum / min / max over the four 16-lane rows (every lane gets the result for its column).
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  unsigned x = __builtin_bit_cast(unsigned, a), y = __builtin_bit_cast(unsigned, b);
+  swap16u(x, y);
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+// Sum / min / max over the four 16-lane rows (every lane gets its column's result).
 __device__ __forceinline__ float rows_sum(float x) {
   float a = x, b = x;
   swap32(a, b);
@@ -97,15 +109,6 @@ __device__ __forceinline__ float rows_max(float x) {
   float y = fmaxf(a, b), c = y, d = y;
   swap16(c, d);
   return fmaxf(c, d);
-}
-// Sum over the 32 lanes of each half-wave (lanes 32q..32q+31).
-__device__ __forceinline__ float half_sum(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
-  x += __shfl_xor(x, 16, 64);
-  return x;
 }
 
 template <int N>
@@ -132,154 +135,211 @@ struct Page {
   static constexpr int bytes = vsz + 256;
 };
 
+// Outstanding vector-memory operations of this wave allowed to remain (the
+// count is a wave-uniform value; above 15 it is treated as 15).  Loads and stores
+// retire in issue order on this counter, so "at most n left" means every
+// operation issued before the last n has completed.
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n < 0 ? 0 : (n > 15 ? 15 : n)) {
+    case 15: wait_vmcnt<15>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 // Slot ids come as their own read-only, non-aliased parameter: the reads are
 // wave-uniform and become scalar loads, which do not wait on the tile copies.
-template <int KB, int VB>
-__global__ __launch_bounds__(512) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
+//
+// The K/V rows of P tiles are in flight at once (a ring of P LDS slots): HBM
+// latency is covered by P tiles of work instead of one.  Every wave issues
+// exactly one copy per tile it fetches and, for a whole-page tile, exactly one
+// 16-byte page store, so the wait for tile k counts the operations issued after
+// that tile's copy: 2P - 1 in steady state (the P - 1 later copies and the P
+// page stores in between).  When a store was scattered or a copy skipped within
+// that window, the wait counts only the copies known to follow, which is never
+// more than what is outstanding.
+template <int KB, int VB, int P>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
   using PG = Page<KB, VB>;
-  constexpr int LEVELS = 1 << KB;
+  constexpr int HALF = 1 << (KB - 1);  // codebook levels per sign
   constexpr float kTop = static_cast<float>((1 << VB) - 1);
+  constexpr int kChunks = PG::bytes / 16;  // 16-byte chunks of a page (at most 164 = 8 waves x 21 lanes)
+  static_assert(PG::bytes % 16 == 0 && kChunks <= 8 * 64, "page store mapping");
+  static_assert(P >= 1 && 2 * P - 1 <= 15, "copy ring depth");
   const int h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, kg = lane >> 4;
+  const int lane0 = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 
-  __shared__ __attribute__((aligned(16))) unsigned short kv_in[2][2][16][128];  // [stage][K,V][token][dim] bf16
-  __shared__ __attribute__((aligned(16))) _Float16 opk[16][kRow];   // scaled float16 key operand
-  __shared__ __attribute__((aligned(16))) _Float16 opv[16][kRow];   // scaled float16 value operand
-  __shared__ __attribute__((aligned(16))) _Float16 orh[16][kRow];   // rho hi
-  __shared__ __attribute__((aligned(16))) _Float16 orl[16][kRow];   // rho lo
-  __shared__ __attribute__((aligned(16))) unsigned char kcode[16][kCodeRow];
-  __shared__ __attribute__((aligned(16))) unsigned char zbit[16][kCodeRow];
+  __shared__ __attribute__((aligned(16))) unsigned short kv_in[P][2][16][128];  // [slot][K,V][token][dim] bf16
+  __shared__ __attribute__((aligned(16))) _Float16 orh[16][kRow];  // rho hi
+  __shared__ __attribute__((aligned(16))) _Float16 orl[16][kRow];  // rho lo
   __shared__ __attribute__((aligned(16))) unsigned char vcode[16][kCodeRow];
   __shared__ __attribute__((aligned(16))) unsigned char img[PG::bytes];
-  __shared__ float fk[16], fv[16], gpart[8][16], vmin[8][16], vmax[8][16];
+  __shared__ float fk[16], gpart[8][16], vmin[8][16], vmax[8][16];
   __shared__ unsigned short n16s[16];
+  __shared__ __attribute__((aligned(16))) u32x4 s_hi[8][4][64];  // S_hi operands per wave and K-step
 
   // ---- this wave's R and S operands (row tile w), kept for the whole launch
-  half8 Rhi[4], Rlo[4], Shi[4], Slo[4];
+  bf16x8 R0[4], R1[4], R2[4];
+  half8 S1[4];
   {
-    const u32x4* op = a.opa + static_cast<size_t>(h * 8 + w) * 4 * 4 * 64 + lane;
+    const u32x4* op = a.opa + static_cast<size_t>(h * 8 + w) * kOpSets * 4 * 64 + lane0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      Rhi[s] = as_h8(op[(0 * 4 + s) * 64]);
-      Rlo[s] = as_h8(op[(1 * 4 + s) * 64]);
-      Shi[s] = as_h8(op[(2 * 4 + s) * 64]);
-      Slo[s] = as_h8(op[(3 * 4 + s) * 64]);
+      R0[s] = __builtin_bit_cast(bf16x8, op[(0 * 4 + s) * 64]);
+      R1[s] = __builtin_bit_cast(bf16x8, op[(1 * 4 + s) * 64]);
+      R2[s] = __builtin_bit_cast(bf16x8, op[(2 * 4 + s) * 64]);
+      s_hi[w][s][lane0] = op[(3 * 4 + s) * 64];
+      S1[s] = __builtin_bit_cast(half8, op[(4 * 4 + s) * 64]);
     }
   }
-
-  // Consume the operands once here so the compiler's wait for these loads is not
-  // placed inside the tile loop, where it would also cover the tile copies.
+  // Consume the operands here so that the compiler's wait for these loads is
+  // not placed inside the tile loop, where it would also drain the copy ring.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(Rhi[s]), "v"(Rlo[s]), "v"(Shi[s]), "v"(Slo[s]));
+  for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(R0[s]), "v"(R1[s]), "v"(R2[s]), "v"(S1[s]));
+  wait_vmcnt<0>();
 
-  // K/V rows of a tile into LDS: waves 0-3 copy K tokens 4w..4w+3, waves 4-7 the
-  // V tokens; lane covers 16 B of a 256 B row.  Tokens past the end re-read token 0.
-  auto stage_tile = [&](long long tile, int st) {
+  // K/V rows of one tile into ring slot `slot`: waves 0-3 copy K tokens 4w..4w+3,
+  // waves 4-7 the V tokens.  Lane c of token row t fetches 16-byte chunk
+  // (c - t) mod 16 of the row, so LDS position p of row t holds chunk
+  // (p - t) mod 16.  Tokens past the end re-read token 0.
+  auto stage = [&](long long tile, int slot, int lane) {
     const int kv = w >> 2;
-    const int tok = 4 * (w & 3) + (lane >> 4);
-    long long n = tile * 16 + tok;
-    if (n >= a.n_tokens) n = 0;
+    const int t = 4 * (w & 3) + (lane >> 4);
+    const int q = ((lane & 15) - t) & 15;
     const unsigned short* base = kv ? a.v : a.k;
     const long long stride = kv ? a.v_stride : a.k_stride;
-    const unsigned short* src = base + n * stride + static_cast<long long>(h) * 128 + (lane & 15) * 8;
-    copy_to_lds(src, &kv_in[st][kv][4 * (w & 3)][0]);
+    long long n = tile * 16 + t;
+    if (n >= a.n_tokens) n = 0;
+    copy_to_lds(base + n * stride + static_cast<long long>(h) * 128 + q * 8, &kv_in[slot][kv][4 * (w & 3)][0]);
   };
 
-  long long tile = blockIdx.x;
-  int st = 0;
-  if (tile < a.n_tiles) stage_tile(tile, 0);
-  for (; tile < a.n_tiles; tile += gridDim.x, st ^= 1) {
-    const long long next = tile + gridDim.x;
-    if (next < a.n_tiles) {
-      stage_tile(next, st ^ 1);
-      wait_vmcnt<1>();
+  const long long first = blockIdx.x, step = gridDim.x;
+  const long long mine = first < a.n_tiles ? (a.n_tiles - 1 - first) / step + 1 : 0;  // tiles of this workgroup
+  const long long pro = mine < P ? mine : P;
+  for (int j = 0; j < pro; ++j) stage(first + j * step, j, lane0);
+  unsigned clean = 0;  // bit i: iteration k-1-i issued one copy and one page store
+  for (long long k = 0; k < mine; ++k) {
+    const long long tile = first + k * step;
+    const int slot = static_cast<int>(k % P);
+    // Lane-dependent addresses are recomputed in every iteration from an opaque
+    // copy of the lane index: kept live across the loop they would not fit in
+    // the 128 registers that let two workgroups share a CU.
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int tid = 64 * w + lane;
+    const int col = lane & 15, kg = lane >> 4;
+    int after;  // operations known to be issued after this tile's copy
+    if (k < P) {
+      after = static_cast<int>(pro - 1 - k);
+    } else if ((clean & ((1u << P) - 1)) == (1u << P) - 1) {
+      after = 2 * P - 1;
     } else {
-      wait_vmcnt<0>();
+      const long long last = (k - 1 < mine - 1 - P) ? k - 1 : mine - 1 - P;
+      after = static_cast<int>(last - (k - P + 1) + 1);
     }
-    // ---- slots of this tile (scalar), whole-page test
+    wait_vmcnt_upto(after);
+    // ---- slots of the tile (scalar loads), whole-page test
     long long sl[16];
-    bool full = true;
+    {
+      const long long n0 = tile * 16;
+      if (n0 + 16 <= a.n_tokens) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      sl[j] = (tile * 16 + j < a.n_tokens) ? slots[tile * 16 + j] : -1;
-      full = full && sl[j] == sl[0] + j;
+        for (int j = 0; j < 16; ++j) sl[j] = slots[n0 + j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sl[j] = (n0 + j < a.n_tokens) ? slots[n0 + j] : -1;
+      }
     }
-    full = full && sl[0] >= 0 && (sl[0] & 15) == 0;
+    bool full = sl[0] >= 0 && (sl[0] & 15) == 0;
+#pragma unroll
+    for (int j = 1; j < 16; ++j) full = full && sl[j] == sl[0] + j;
     __syncthreads();  // tile rows in LDS (every wave waited on its copy)
 
-    // ---- A: norms, power-of-two scales, float16 operands (thread: token tid/32, dims 4p..4p+3)
+    // ---- B1: T = R k, V = R v (row tile w, 16 tokens); wave 0 also takes ||k||.
+    // The K/V operands are read one K-step at a time (8 registers live, not 32).
+    floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f}, V = {0.0f, 0.0f, 0.0f, 0.0f};
     {
-      const int tk = tid >> 5, p = tid & 31;
-      const u32x2 kr = *reinterpret_cast<const u32x2*>(&kv_in[st][0][tk][4 * p]);
-      const u32x2 vr = *reinterpret_cast<const u32x2*>(&kv_in[st][1][tk][4 * p]);
-      float kx[4], vx[4];
-      kx[0] = __uint_as_float(kr[0] << 16); kx[1] = __uint_as_float(kr[0] & 0xffff0000u);
-      kx[2] = __uint_as_float(kr[1] << 16); kx[3] = __uint_as_float(kr[1] & 0xffff0000u);
-      vx[0] = __uint_as_float(vr[0] << 16); vx[1] = __uint_as_float(vr[0] & 0xffff0000u);
-      vx[2] = __uint_as_float(vr[1] << 16); vx[3] = __uint_as_float(vr[1] & 0xffff0000u);
-      float k2 = 0.0f, v2 = 0.0f;
+      float k2 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        k2 = fmaf(kx[i], kx[i], k2);
-        v2 = fmaf(vx[i], vx[i], v2);
-      }
-      k2 = half_sum(k2);
-      v2 = half_sum(v2);
-      const float n = sqrtf(k2), nv = sqrtf(v2);
-      // scale 2^-e with n in [2^e, 2^(e+1)): every scaled entry lies in (-2, 2)
-      const int ek = (n > 0.0f) ? ilogbf(n) : 0;
-      const int ev = (nv > 0.0f) ? ilogbf(nv) : 0;
-      const float sk = ldexpf(1.0f, -ek), sv = ldexpf(1.0f, -ev);
-      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-      half4 hk, hv;
+      for (int s = 0; s < 4; ++s) {
+        const int pos = (4 * s + kg + col) & 15;  // chunk 4s + kg of token col
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][0][col][8 * pos]);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][1][col][8 * pos]);
+        T = mfma_b(R0[s], kb, T);
+        V = mfma_b(R0[s], vb, V);
+        T = mfma_b(R1[s], kb, T);
+        V = mfma_b(R1[s], vb, V);
+        T = mfma_b(R2[s], kb, T);
+        V = mfma_b(R2[s], vb, V);
+        if (w == 0) {
+          // ||k||^2 in float32 from the exact bf16 inputs (the lane holds 32 dims of token col)
+          const u32x4 x = __builtin_bit_cast(u32x4, kb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hk[i] = static_cast<_Float16>(kx[i] * sk);
-        hv[i] = static_cast<_Float16>(vx[i] * sv);
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xffff0000u);
+            k2 = fmaf(lo, lo, k2);
+            k2 = fmaf(hi, hi, k2);
+          }
+        }
       }
-      *reinterpret_cast<half4*>(&opk[tk][4 * p]) = hk;
-      *reinterpret_cast<half4*>(&opv[tk][4 * p]) = hv;
-      if (p == 0) {
-        // t = sqrt(d) R k / n = sqrt(d) 2^e / n * (R k_scaled); zero norm -> t = 0
-        fk[tk] = (n > 0.0f) ? ldexpf(sqrtf(128.0f) / n, ek) : 0.0f;
-        fv[tk] = ldexpf(1.0f, ev);
-        n16s[tk] = __half_as_ushort(__float2half_rn(n));
+      if (w == 0) {
+        k2 = rows_sum(k2);
+        if (kg == 0) {
+          const float n = sqrtf(k2);
+          fk[col] = (n > 0.0f) ? sqrtf(128.0f) / n : 0.0f;  // zero norm: t = 0
+          n16s[col] = __half_as_ushort(__float2half_rn(n));
+        }
+      }
+      if constexpr (KB == 3) {  // key-code words are OR-ed together below
+        for (int i = tid; i < PG::ks / 4; i += 512) reinterpret_cast<unsigned*>(img)[i] = 0u;
       }
     }
-    __syncthreads();
+    __syncthreads();  // every wave has its operands: ring slot `slot` may be refilled
+    const bool fetch = k + P < mine;
+    if (fetch) stage(first + (k + P) * step, slot, lane);
 
-    // ---- B: t = R k, codes, residual; v' = R v and its group extremes (row tile w)
+    // ---- B2: t, codes, residual (rho -> LDS), key codes -> image; value extremes
     float vp[4];
     {
-      floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f};
-      half8 kb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kb[s] = *reinterpret_cast<const half8*>(&opk[col][32 * s + 8 * kg]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) T = mfma(Rhi[s], kb[s], T);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) T = mfma(Rlo[s], kb[s], T);
       const float f = fk[col];
       float rho[4], g2 = 0.0f;
       unsigned codes = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float t = T[r] * f;
-        int idx = 0;
+        // symmetric codebook: cnt = #{positive boundaries below |t|}, ties to the
+        // lower cell (so for t <= 0 compare against the next float above |t|)
+        const float m = fabsf(t);
+        const float mq = (t > 0.0f) ? m : __uint_as_float(__float_as_uint(m) + 1u);
+        int cnt = 0;
+        float cp = a.cent[HALF];
 #pragma unroll
-        for (int i = 0; i < LEVELS - 1; ++i) idx += (a.bnd[i] < t) ? 1 : 0;
-        float c = a.cent[0];
-#pragma unroll
-        for (int i = 1; i < LEVELS; ++i) c = (idx == i) ? a.cent[i] : c;
-        rho[r] = t - c;
+        for (int j = 0; j < HALF - 1; ++j) {
+          const bool above = a.bnd[HALF + j] < mq;
+          cnt += above ? 1 : 0;
+          cp = above ? a.cent[HALF + j + 1] : cp;
+        }
+        const int idx = (t > 0.0f) ? HALF + cnt : HALF - 1 - cnt;
+        rho[r] = t - ((t > 0.0f) ? cp : -cp);
         g2 = fmaf(rho[r], rho[r], g2);
-        codes |= static_cast<unsigned>(idx) << (8 * r);
+        codes |= static_cast<unsigned>(idx) << (KB * r);
       }
       g2 = rows_sum(g2);
       if (kg == 0) gpart[w][col] = g2;
-      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
       half4 rh, rl;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -289,21 +349,24 @@ __global__ __launch_bounds__(512) void compress_mfma_kernel(CArgs a, const long 
       const int d0 = 16 * w + 4 * kg;
       *reinterpret_cast<half4*>(&orh[col][d0]) = rh;
       *reinterpret_cast<half4*>(&orl[col][d0]) = rl;
-      *reinterpret_cast<unsigned*>(&kcode[col][d0]) = codes;
+      // key codes of dims d0..d0+3 = elements e0..e0+3 of block w/2 (4 KB bits)
+      const int b = w >> 1, e0 = 16 * (w & 1) + 4 * kg;
+      unsigned char* rec = &img[PG::kc + (b * 16 + col) * 4 * KB];
+      if constexpr (KB == 2) {
+        rec[e0 / 4] = static_cast<unsigned char>(codes);
+      } else if constexpr (KB == 4) {
+        *reinterpret_cast<unsigned short*>(rec + e0 / 2) = static_cast<unsigned short>(codes);
+      } else {
+        const int bit = 3 * e0, wi = bit >> 5, sh = bit & 31;
+        unsigned* rw = reinterpret_cast<unsigned*>(rec);
+        atomicOr(&rw[wi], codes << sh);
+        if (sh + 12 > 32) atomicOr(&rw[wi + 1], codes >> (32 - sh));
+      }
 
-      floatx4 V = {0.0f, 0.0f, 0.0f, 0.0f};
-      half8 vb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) vb[s] = *reinterpret_cast<const half8*>(&opv[col][32 * s + 8 * kg]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) V = mfma(Rhi[s], vb[s], V);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) V = mfma(Rlo[s], vb[s], V);
-      const float g = fv[col];
       float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        vp[r] = V[r] * g;
+        vp[r] = V[r];
         mn = fminf(mn, vp[r]);
         mx = fmaxf(mx, vp[r]);
       }
@@ -316,41 +379,46 @@ __global__ __launch_bounds__(512) void compress_mfma_kernel(CArgs a, const long 
     }
     __syncthreads();
 
-    // ---- C: y = S rho -> signs; value codes; per-token metadata into the page image
+    // ---- C: y = S rho -> sign bits; value codes; per-token metadata
     {
       floatx4 Y = {0.0f, 0.0f, 0.0f, 0.0f};
-      half8 rh[4], rl[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        rh[s] = *reinterpret_cast<const half8*>(&orh[col][32 * s + 8 * kg]);
-        rl[s] = *reinterpret_cast<const half8*>(&orl[col][32 * s + 8 * kg]);
+        const half8 sh = __builtin_bit_cast(half8, s_hi[w][s][lane]);
+        const half8 rh = *reinterpret_cast<const half8*>(&orh[col][32 * s + 8 * kg]);
+        const half8 rl = *reinterpret_cast<const half8*>(&orl[col][32 * s + 8 * kg]);
+        Y = mfma_h(sh, rh, Y);
+        Y = mfma_h(sh, rl, Y);
+        Y = mfma_h(S1[s], rh, Y);
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Y = mfma(Shi[s], rh[s], Y);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Y = mfma(Shi[s], rl[s], Y);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Y = mfma(Slo[s], rh[s], Y);
-      unsigned zb = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) zb |= (Y[r] >= 0.0f ? 1u : 0u) << (8 * r);
-      const int d0 = 16 * w + 4 * kg;
-      *reinterpret_cast<unsigned*>(&zbit[col][d0]) = zb;
-
       const int G = w >> 1;
+      // sign nibble of dims d0..d0+3 (bit r = dim d0 + r); two row groups make a byte
+      unsigned nib = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nib |= (Y[r] >= 0.0f ? 1u : 0u) << r;
+      unsigned ea = nib, eb = nib;
+      swap16u(ea, eb);  // even row groups: ea = own, eb = the next group's nibble
+      if ((kg & 1) == 0)
+        img[PG::ks + ((w >> 1) * 16 + col) * 4 + 2 * (w & 1) + (kg >> 1)] = static_cast<unsigned char>(ea | (eb << 4));
+
       const float mn = fminf(vmin[2 * G][col], vmin[2 * G + 1][col]);
       const float mx = fmaxf(vmax[2 * G][col], vmax[2 * G + 1][col]);
       const __half s16 = __float2half_rn((mx - mn) / kTop);
       const __half z16 = __float2half_rn(mn);
       const float sc = __half2float(s16), zr = __half2float(z16);
+      // quotient by reciprocal and one correction step (faithful to the division)
+      const float inv0 = __builtin_amdgcn_rcpf(sc);
+      const float inv = fmaf(fmaf(-sc, inv0, 1.0f), inv0, inv0);
       unsigned vc = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        int code = 0;
-        if (sc > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((vp[r] - zr) / sc), 0.0f), kTop));
-        vc |= static_cast<unsigned>(code) << (8 * r);
+        const float dlt = vp[r] - zr;
+        const float q0 = dlt * inv;
+        const float q = fmaf(fmaf(-q0, sc, dlt), inv, q0);
+        const float c = (sc > 0.0f) ? __builtin_amdgcn_fmed3f(rintf(q), 0.0f, kTop) : 0.0f;
+        vc |= static_cast<unsigned>(c) << (8 * r);
       }
-      *reinterpret_cast<unsigned*>(&vcode[col][d0]) = vc;
+      *reinterpret_cast<unsigned*>(&vcode[col][16 * w + 4 * kg]) = vc;
       if ((w & 1) == 0 && kg == 0)
         *reinterpret_cast<unsigned*>(&img[PG::vsz + col * 16 + G * 4]) =
             static_cast<unsigned>(__half_as_ushort(s16)) | (static_cast<unsigned>(__half_as_ushort(z16)) << 16);
@@ -365,40 +433,9 @@ __global__ __launch_bounds__(512) void compress_mfma_kernel(CArgs a, const long 
     }
     __syncthreads();
 
-    // ---- D: pack codes and signs into the page image
-    if (tid < 64) {
-      // key codes: token t, 32-dim block b -> 4*KB bytes of LSB-first b-bit codes
-      const int t = tid & 15, b = tid >> 4;
-      unsigned wd[KB];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) wd[i] = 0u;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const unsigned x = *reinterpret_cast<const unsigned*>(&kcode[t][32 * b + 4 * q]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * q + r, bit = KB * e;
-          const unsigned c = (x >> (8 * r)) & 0xffu;
-          wd[bit >> 5] |= c << (bit & 31);
-          if ((bit & 31) + KB > 32) wd[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-        }
-      }
-      unsigned* dst = reinterpret_cast<unsigned*>(&img[PG::kc + (b * 16 + t) * 4 * KB]);
-#pragma unroll
-      for (int i = 0; i < KB; ++i) dst[i] = wd[i];
-    } else if (tid < 128) {
-      // sign bits: token t, block b -> one word
-      const int t = tid & 15, b = (tid >> 4) & 3;
-      unsigned wd = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const unsigned x = *reinterpret_cast<const unsigned*>(&zbit[t][32 * b + 4 * q]);
-        wd |= ((x & 1u) | ((x >> 7) & 2u) | ((x >> 14) & 4u) | ((x >> 21) & 8u)) << (4 * q);
-      }
-      *reinterpret_cast<unsigned*>(&img[PG::ks + (b * 16 + t) * 4]) = wd;
-    } else if (tid < 256) {
-      // value codes: dimension row d = 16 tokens x VB bits
-      const int d = tid - 128;
+    // ---- D: value-code rows (coordinate d: 16 tokens x VB bits) into the image
+    if (tid < 128) {
+      const int d = tid;
       unsigned long long row = 0;
 #pragma unroll
       for (int t = 0; t < 16; ++t) row |= static_cast<unsigned long long>(vcode[t][d]) << (VB * t);
@@ -418,9 +455,10 @@ __global__ __launch_bounds__(512) void compress_mfma_kernel(CArgs a, const long 
 
     // ---- E: store
     if (full) {
+      // one 16-byte store per wave: chunk w + 8 * lane (lane 0 is always in range)
       unsigned char* page = a.pool + (static_cast<size_t>(sl[0] >> 4) * a.H + h) * a.block_bytes;
-      for (int o = 16 * tid; o < PG::bytes; o += 16 * 512)
-        *reinterpret_cast<u32x4*>(page + o) = *reinterpret_cast<const u32x4*>(&img[o]);
+      const int c = w + 8 * lane;
+      if (c < kChunks) *reinterpret_cast<u32x4*>(page + 16 * c) = *reinterpret_cast<const u32x4*>(&img[16 * c]);
     } else {
       // token by token: fixed-size fields copied, value-code bits set atomically
 #pragma unroll 1
@@ -459,16 +497,19 @@ __global__ __launch_bounds__(512) void compress_mfma_kernel(CArgs a, const long 
         }
       }
     }
-    __syncthreads();  // the next tile rewrites slots, codes and the image
+    clean = (clean << 1) | ((fetch && full) ? 1u : 0u);
+    __syncthreads();  // the next tile rewrites codes and the image
   }
+  wait_vmcnt<0>();
 }
 
+constexpr int kRing = 3;  // tiles in flight per workgroup
 template <int KB>
 void* pick_v(int vb) {
   switch (vb) {
-    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2>);
-    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3>);
-    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4>);
+    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing>);
+    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing>);
+    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing>);
   }
   return nullptr;
 }
@@ -513,9 +554,12 @@ tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, 
   }
   void* fn = pick_kv(L->cfg.k_bits, L->cfg.v_bits);
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
-  // one resident workgroup per CU per head share, each looping over its tiles
+  // Workgroups loop over their tiles: as many as fit on the chip at once over all
+  // heads (resident workgroups per CU from the kernel's register and LDS use).
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, 0) != hipSuccess || per_cu < 1) per_cu = 1;
   const int cus = L->cu_count > 0 ? L->cu_count : 256;
-  long long gx = (static_cast<long long>(cus) * 2 + a.H - 1) / a.H;
+  long long gx = (static_cast<long long>(cus) * per_cu + a.H - 1) / a.H;
   if (gx > a.n_tiles) gx = a.n_tiles;
   if (gx < 1) gx = 1;
   const long long* sp = slots;

@@ -10,6 +10,7 @@
 
 namespace tq {
 
+constexpr int kOpSets = 5;  // compressor operand sets per row tile
 constexpr int kDim = 128;     // head_dim supported by the kernels
 constexpr int kPage = 16;     // tokens per block
 constexpr int kGroup = 32;    // value group width
@@ -69,8 +70,8 @@ struct tq_layer {
   float* dR = nullptr;
   float* dRT = nullptr;
   float* dST = nullptr;
-  // Matrix-core A operands of R and S for the compressor, float16 bit patterns:
-  // [H][8 row tiles][4 sets: R hi, R lo, S hi, S lo][4 K-steps][64 lanes][8],
+  // Matrix-core A operands of R and S for the compressor (16-bit patterns):
+  // [H][8 row tiles][kOpSets: R bf16 hi, mid, lo; S fp16 hi, lo][4 K-steps][64 lanes][8],
   // lane l of (tile w, step s) holding M[16w + l%16][32s + 8(l/16) .. +7].
   unsigned short* dOpA = nullptr;
   float centroids[16] = {0};
