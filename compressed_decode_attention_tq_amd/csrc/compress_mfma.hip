@@ -96,19 +96,31 @@ __device__ __forceinline__ float rows_sum(float x) {
   swap16(c, d);
   return c + d;
 }
+// The combining min / max are plain instructions: the operands are ordinary
+// values already, so no quieting of signalling NaNs is wanted around them.
+__device__ __forceinline__ float min_raw(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float rows_min(float x) {
   float a = x, b = x;
   swap32(a, b);
-  float y = fminf(a, b), c = y, d = y;
+  float y = min_raw(a, b), c = y, d = y;
   swap16(c, d);
-  return fminf(c, d);
+  return min_raw(c, d);
 }
 __device__ __forceinline__ float rows_max(float x) {
   float a = x, b = x;
   swap32(a, b);
-  float y = fmaxf(a, b), c = y, d = y;
+  float y = max_raw(a, b), c = y, d = y;
   swap16(c, d);
-  return fmaxf(c, d);
+  return max_raw(c, d);
 }
 
 template <int N>
@@ -135,29 +147,18 @@ struct Page {
   static constexpr int bytes = vsz + 256;
 };
 
-// Outstanding vector-memory operations of this wave allowed to remain (the
-// count is a wave-uniform value; above 15 it is treated as 15).  Loads and stores
+// Wait until at most n of this wave's vector-memory operations are outstanding,
+// for n rounded down to 2P - 1, P - 1 or 0 (wave-uniform n).  Loads and stores
 // retire in issue order on this counter, so "at most n left" means every
 // operation issued before the last n has completed.
+template <int P>
 __device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  switch (n < 0 ? 0 : (n > 15 ? 15 : n)) {
-    case 15: wait_vmcnt<15>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
+  if (n >= 2 * P - 1)
+    wait_vmcnt<2 * P - 1>();
+  else if (n >= P - 1)
+    wait_vmcnt<P - 1>();
+  else
+    wait_vmcnt<0>();
 }
 
 // Slot ids come as their own read-only, non-aliased parameter: the reads are
@@ -228,13 +229,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   };
 
   const long long first = blockIdx.x, step = gridDim.x;
-  const long long mine = first < a.n_tiles ? (a.n_tiles - 1 - first) / step + 1 : 0;  // tiles of this workgroup
-  const long long pro = mine < P ? mine : P;
+  // tiles of this workgroup (fewer than 2^31: the grid has at least one workgroup per CU and head)
+  const int mine = first < a.n_tiles ? static_cast<int>((a.n_tiles - 1 - first) / step + 1) : 0;
+  const int pro = mine < P ? mine : P;
   for (int j = 0; j < pro; ++j) stage(first + j * step, j, lane0);
   unsigned clean = 0;  // bit i: iteration k-1-i issued one copy and one page store
-  for (long long k = 0; k < mine; ++k) {
-    const long long tile = first + k * step;
-    const int slot = static_cast<int>(k % P);
+  int slot = 0;  // k mod P
+  for (int k = 0; k < mine; ++k, slot = (slot == P - 1) ? 0 : slot + 1) {
+    const long long tile = first + static_cast<long long>(k) * step;
     // Lane-dependent addresses are recomputed in every iteration from an opaque
     // copy of the lane index: kept live across the loop they would not fit in
     // the 128 registers that let two workgroups share a CU.
@@ -244,14 +246,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int col = lane & 15, kg = lane >> 4;
     int after;  // operations known to be issued after this tile's copy
     if (k < P) {
-      after = static_cast<int>(pro - 1 - k);
+      after = pro - 1 - k;
     } else if ((clean & ((1u << P) - 1)) == (1u << P) - 1) {
       after = 2 * P - 1;
     } else {
-      const long long last = (k - 1 < mine - 1 - P) ? k - 1 : mine - 1 - P;
-      after = static_cast<int>(last - (k - P + 1) + 1);
+      const int last = (k - 1 < mine - 1 - P) ? k - 1 : mine - 1 - P;
+      after = last - (k - P + 1) + 1;
     }
-    wait_vmcnt_upto(after);
+    wait_vmcnt_upto<P>(after);
     // ---- slots of the tile (scalar loads), whole-page test
     long long sl[16];
     {
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     __syncthreads();  // every wave has its operands: ring slot `slot` may be refilled
     const bool fetch = k + P < mine;
-    if (fetch) stage(first + (k + P) * step, slot, lane);
+    if (fetch) stage(first + static_cast<long long>(k + P) * step, slot, lane);
 
     // ---- B2: t, codes, residual (rho -> LDS), key codes -> image; value extremes
     float vp[4];
@@ -403,7 +405,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
       const float mn = fminf(vmin[2 * G][col], vmin[2 * G + 1][col]);
       const float mx = fmaxf(vmax[2 * G][col], vmax[2 * G + 1][col]);
-      const __half s16 = __float2half_rn((mx - mn) / kTop);
+      // (mx - mn) / kTop as the correctly rounded float32 quotient: product by
+      // the rounded reciprocal, then one residual step (exact residual by fma)
+      const float span = mx - mn;
+      const float q0s = span * (1.0f / kTop);
+      const __half s16 = __float2half_rn(fmaf(fmaf(-q0s, kTop, span), 1.0f / kTop, q0s));
       const __half z16 = __float2half_rn(mn);
       const float sc = __half2float(s16), zr = __half2float(z16);
       // quotient by reciprocal and one correction step (faithful to the division)
