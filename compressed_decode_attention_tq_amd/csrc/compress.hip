@@ -11,8 +11,6 @@
 //   v' = R v; per 32-wide group scale = fp16((max-min)/(2^b-1)), zero = fp16(min),
 //   code = clamp(rint((v' - zero)/scale), 0, 2^b-1)  (0 when scale == 0).
 //
-// One workgroup of 128 lanes per (token, KV head); lane i owns coordinate i.
-// Dot products accumulate in eight interleaved float32 partial sums.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -52,16 +50,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Sum over the 128 lanes of the workgroup; every lane gets the result.
-__device__ __forceinline__ float block_sum128(float x, float* scratch2) {
-  x = wave_sum(x);
-  if ((threadIdx.x & 63) == 0) scratch2[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const float r = scratch2[0] + scratch2[1];
-  __syncthreads();
-  return r;
-}
-
 // 32-bit word w of the LSB-first bitstream of 128 b-bit codes.
 template <int B>
 __device__ __forceinline__ unsigned pack_word(const unsigned char* codes, int w) {
@@ -76,78 +64,110 @@ __device__ __forceinline__ unsigned pack_word(const unsigned char* codes, int w)
   return word;
 }
 
-// Dot product of column i of a transposed 128x128 matrix with x (in LDS):
-// sum_j M[i][j] x[j], eight interleaved partial sums.
-__device__ __forceinline__ float matvec_row(const float* __restrict__ MT, const float* x, int i) {
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int j = 0; j < 128; j += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = fmaf(MT[(j + u) * 128 + i], x[j + u], acc[u]);
-  }
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-}
-
+// One workgroup of 512 lanes per (token, KV head).  Lane (c, i) = (lane / 128,
+// lane % 128) holds column i of rows 32c..32c+31 of R^T and S^T (loaded before
+// anything else, so the loads overlap) and forms that quarter of each dot
+// product; the quarters are summed through LDS in a fixed order.  Lanes 0..127
+// then own coordinate i for the scalar work.
 template <bool BF16, int KB, int VB>
-__global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
   const long long tok = blockIdx.x;
   const int h = blockIdx.y;
-  const int i = threadIdx.x;
+  const int tid = threadIdx.x, c = tid >> 7, i = tid & 127;
   const long long slot = a.slots[tok];
   if (slot < 0) return;
 
-  __shared__ float sk[128], sv[128], srho[128], red[2];
+  __shared__ float sk[128], sv[128], srho[128], red[4];
+  __shared__ float pk[4][128], pv[4][128];
   __shared__ unsigned char ck[128];
   __shared__ unsigned sbits[4];
   __shared__ __half sgroup[8];
 
-  const float kx = load_elem<BF16>(a.k, tok * a.k_stride + h * 128 + i);
-  const float vx = load_elem<BF16>(a.v, tok * a.v_stride + h * 128 + i);
-  sk[i] = kx;
-  sv[i] = vx;
-  const float n2 = block_sum128(kx * kx, red);  // also orders the sk/sv writes
-
-  const float* RT = a.RT + static_cast<size_t>(h) * 128 * 128;
-  const float* ST = a.ST + static_cast<size_t>(h) * 128 * 128;
-  const float rk = matvec_row(RT, sk, i);
-  const float rv = matvec_row(RT, sv, i);
-
-  // keys: standardise, quantise, residual
-  const float n = sqrtf(n2);
-  const float t = (n > 0.0f) ? rk * (sqrtf(128.0f) / n) : 0.0f;
-  int idx = 0;
+  float rt[32], st[32];
+  {
+    const float* r = a.RT + static_cast<size_t>(h) * 128 * 128 + (32 * c) * 128 + i;
+    const float* s = a.ST + static_cast<size_t>(h) * 128 * 128 + (32 * c) * 128 + i;
 #pragma unroll
-  for (int b = 0; b < (1 << KB) - 1; ++b) idx += (a.bnd[b] < t) ? 1 : 0;
-  const float rho = t - a.cent[idx];
-  ck[i] = static_cast<unsigned char>(idx);
-  srho[i] = rho;
-  const float g2 = block_sum128(rho * rho, red);
-  const float y = matvec_row(ST, srho, i);
-  const unsigned long long bal = __ballot(y >= 0.0f);
-  if ((i & 63) == 0) {
-    sbits[(i >> 6) * 2] = static_cast<unsigned>(bal);
-    sbits[(i >> 6) * 2 + 1] = static_cast<unsigned>(bal >> 32);
+    for (int u = 0; u < 32; ++u) {
+      rt[u] = r[u * 128];
+      st[u] = s[u * 128];
+    }
   }
-
-  // values: group min/max over 32 lanes
-  float mn = rv, mx = rv;
-#pragma unroll
-  for (int off = 16; off > 0; off >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, off, 32));
-  }
-  constexpr float top = static_cast<float>((1 << VB) - 1);
-  const __half s16 = __float2half_rn((mx - mn) / top);
-  const __half z16 = __float2half_rn(mn);
-  const float s = __half2float(s16);
-  const float z = __half2float(z16);
-  int code = 0;
-  if (s > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((rv - z) / s), 0.0f), top));
-  if ((i & 31) == 0) {
-    sgroup[(i >> 5) * 2] = s16;
-    sgroup[(i >> 5) * 2 + 1] = z16;
+  float kx = 0.0f;
+  if (c == 0) {
+    kx = load_elem<BF16>(a.k, tok * a.k_stride + h * 128 + i);
+    sk[i] = kx;
+    const float w2 = wave_sum(kx * kx);
+    if ((i & 63) == 0) red[i >> 6] = w2;
+  } else if (c == 1) {
+    sv[i] = load_elem<BF16>(a.v, tok * a.v_stride + h * 128 + i);
   }
   __syncthreads();
+  {
+    float ak = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      ak = fmaf(rt[u], sk[32 * c + u], ak);
+      av = fmaf(rt[u], sv[32 * c + u], av);
+    }
+    pk[c][i] = ak;
+    pv[c][i] = av;
+  }
+  __syncthreads();
+
+  constexpr float top = static_cast<float>((1 << VB) - 1);
+  float n = 0.0f, rv = 0.0f;
+  int code = 0;
+  __half s16, z16;
+  if (c == 0) {
+    const float rk = (pk[0][i] + pk[1][i]) + (pk[2][i] + pk[3][i]);
+    rv = (pv[0][i] + pv[1][i]) + (pv[2][i] + pv[3][i]);
+    // keys: standardise, quantise, residual
+    n = sqrtf(red[0] + red[1]);
+    const float t = (n > 0.0f) ? rk * (sqrtf(128.0f) / n) : 0.0f;
+    int idx = 0;
+#pragma unroll
+    for (int b = 0; b < (1 << KB) - 1; ++b) idx += (a.bnd[b] < t) ? 1 : 0;
+    const float rho = t - a.cent[idx];
+    ck[i] = static_cast<unsigned char>(idx);
+    srho[i] = rho;
+    const float g2 = wave_sum(rho * rho);
+    if ((i & 63) == 0) red[2 + (i >> 6)] = g2;
+    // values: group min/max over 32 lanes
+    float mn = rv, mx = rv;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+    }
+    s16 = __float2half_rn((mx - mn) / top);
+    z16 = __float2half_rn(mn);
+    const float s = __half2float(s16);
+    const float z = __half2float(z16);
+    if (s > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((rv - z) / s), 0.0f), top));
+    if ((i & 31) == 0) {
+      sgroup[(i >> 5) * 2] = s16;
+      sgroup[(i >> 5) * 2 + 1] = z16;
+    }
+  }
+  __syncthreads();
+  {
+    float ay = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) ay = fmaf(st[u], srho[32 * c + u], ay);
+    pk[c][i] = ay;
+  }
+  __syncthreads();
+  if (c == 0) {
+    const float y = (pk[0][i] + pk[1][i]) + (pk[2][i] + pk[3][i]);
+    const unsigned long long bal = __ballot(y >= 0.0f);
+    if ((i & 63) == 0) {
+      sbits[(i >> 6) * 2] = static_cast<unsigned>(bal);
+      sbits[(i >> 6) * 2 + 1] = static_cast<unsigned>(bal >> 32);
+    }
+  }
+  __syncthreads();
+  if (c != 0) return;  // lanes 0..127 store the record
 
   unsigned char* base = a.pool + (static_cast<size_t>(slot >> 4) * a.H + h) * a.block_bytes;
   const int off = static_cast<int>(slot & 15);
@@ -159,12 +179,12 @@ __global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
     const unsigned bit = static_cast<unsigned>(16 * i + off) * VB;
     const unsigned w = bit >> 5, sh = bit & 31;
     const unsigned mask = (1u << VB) - 1u;
-    const unsigned c = static_cast<unsigned>(code);
+    const unsigned cc = static_cast<unsigned>(code);
     atomicAnd(&vw[w], ~(mask << sh));
-    atomicOr(&vw[w], c << sh);
+    atomicOr(&vw[w], cc << sh);
     if (sh + VB > 32) {
       atomicAnd(&vw[w + 1], ~(mask >> (32 - sh)));
-      atomicOr(&vw[w + 1], c >> (32 - sh));
+      atomicOr(&vw[w + 1], cc >> (32 - sh));
     }
   }
   if (i < 4 * KB) {
@@ -176,7 +196,7 @@ __global__ __launch_bounds__(128) void compress_kernel(CompressArgs a) {
     *reinterpret_cast<unsigned*>(base + a.off_ks + (blk * 16 + off) * 4) = sbits[blk];
   } else if (i == 68) {
     const __half hn = __float2half_rn(n);
-    const __half hg = __float2half_rn(sqrtf(g2));
+    const __half hg = __float2half_rn(sqrtf(red[2] + red[3]));
     const unsigned w = static_cast<unsigned>(__half_as_ushort(hn)) |
                        (static_cast<unsigned>(__half_as_ushort(hg)) << 16);
     *reinterpret_cast<unsigned*>(base + a.off_kn + off * 4) = w;
@@ -270,7 +290,7 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
                                      : pick<false>(L->cfg.k_bits, L->cfg.v_bits);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
     void* args[] = {&a};
-    hipError_t e = hipLaunchKernel(fn, grid, dim3(128), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(512), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
   }
   hipError_t e = hipGetLastError();

@@ -65,61 +65,95 @@ __device__ __forceinline__ float wave_sum(float x) {
 //   R <= 4: one tile, rows part*R + h for parts q' hi, q' lo, ku hi, ku lo
 //           (rows 4R..15 zero)
 //   R == 8: tile 0 rows h / 8+h = q' hi / lo, tile 1 the same for kappa*u.
+//
+// One workgroup of 512 lanes per (KV head g, sequence b) serves the group's
+// query heads.  Lane (c, i) = (lane / 128, lane % 128) holds column i of rows
+// 32c..32c+31 of R_g^T and S_g^T, loaded once, and forms that quarter of every
+// head's dot products; the quarters are summed through LDS in a fixed order.
 template <bool QBF16, bool BYPASS>
-__global__ __launch_bounds__(128) void prologue_kernel(const void* q, const float* RT, const float* ST,
+__global__ __launch_bounds__(512) void prologue_kernel(const void* q, const float* RT, const float* ST,
                                                        float* qu, unsigned short* qa, int Hq, int rep,
                                                        float kappa) {
-  const int bh = blockIdx.x;
-  const int g = (bh % Hq) / rep;
-  const int i = threadIdx.x;
-  __shared__ float sq[128], sp[128];
-  float x;
-  if constexpr (QBF16) {
-    x = __uint_as_float(static_cast<unsigned>(static_cast<const unsigned short*>(q)[bh * 128 + i]) << 16);
-  } else {
-    x = static_cast<const float*>(q)[bh * 128 + i];
-  }
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int Hkv = gridDim.x;
+  const int tid = threadIdx.x, c = tid >> 7, i = tid & 127;
+  const int n = rep * 128;  // outputs of this group
+  const int bh0 = b * Hq + g * rep;
+  auto load_q = [&](int h, int d) -> float {
+    const size_t at = static_cast<size_t>(bh0 + h) * 128 + d;
+    if constexpr (QBF16) return __uint_as_float(static_cast<unsigned>(static_cast<const unsigned short*>(q)[at]) << 16);
+    else return static_cast<const float*>(q)[at];
+  };
   if constexpr (BYPASS) {
-    qu[bh * 256 + i] = x;
-    qu[bh * 256 + 128 + i] = 0.0f;
+    for (int o = tid; o < n; o += 512) {
+      const int h = o >> 7, d = o & 127;
+      qu[static_cast<size_t>(bh0 + h) * 256 + d] = load_q(h, d);
+      qu[static_cast<size_t>(bh0 + h) * 256 + 128 + d] = 0.0f;
+    }
     return;
   } else {
-    sq[i] = x;
+    __shared__ float sq[8][128], sa[8][128], part[4][8][128];
+    float rt[32], st[32];
+    {
+      const float* r = RT + static_cast<size_t>(g) * 128 * 128 + (32 * c) * 128 + i;
+      const float* t = ST + static_cast<size_t>(g) * 128 * 128 + (32 * c) * 128 + i;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        rt[u] = r[u * 128];
+        st[u] = t[u * 128];
+      }
+    }
+    for (int o = tid; o < n; o += 512) sq[o >> 7][o & 127] = load_q(o >> 7, o & 127);
     __syncthreads();
-    const float* rt = RT + static_cast<size_t>(g) * 128 * 128;
-    const float* st = ST + static_cast<size_t>(g) * 128 * 128;
-    float a = 0.0f;
-    for (int j = 0; j < 128; ++j) a = fmaf(rt[j * 128 + i], sq[j], a);
-    sp[i] = a;
+    for (int h = 0; h < rep; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) acc = fmaf(rt[u], sq[h][32 * c + u], acc);
+      part[c][h][i] = acc;
+    }
     __syncthreads();
-    float u = 0.0f;
-    for (int j = 0; j < 128; ++j) u = fmaf(st[j * 128 + i], sp[j], u);
-    qu[bh * 256 + i] = a;
-    qu[bh * 256 + 128 + i] = u;
-
-    const int b = bh / Hq, h = (bh % Hq) % rep, Hkv = Hq / rep;
+    for (int o = tid; o < n; o += 512) {
+      const int h = o >> 7, d = o & 127;
+      const float a = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
+      sa[h][d] = a;
+      qu[static_cast<size_t>(bh0 + h) * 256 + d] = a;
+    }
+    __syncthreads();
+    for (int h = 0; h < rep; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) acc = fmaf(st[u], sa[h][32 * c + u], acc);
+      part[c][h][i] = acc;
+    }
+    __syncthreads();
     const int nset = rep == 8 ? 2 : 1;
-    const int kgi = i >> 5, ks = (i >> 3) & 3, j = i & 7;
-    const float ku = kappa * u;
-    const _Float16 qh = static_cast<_Float16>(a), uh = static_cast<_Float16>(ku);
-    const _Float16 ql = static_cast<_Float16>(a - static_cast<float>(qh));
-    const _Float16 ul = static_cast<_Float16>(ku - static_cast<float>(uh));
-    auto put = [&](int set, int row, _Float16 v) {
-      const size_t at = ((((static_cast<size_t>(b) * Hkv + g) * nset + set) * 4 + ks) * 64 + row + 16 * kgi) * 8 + j;
-      qa[at] = __builtin_bit_cast(unsigned short, v);
-    };
-    if (rep == 8) {
-      put(0, h, qh);
-      put(0, 8 + h, ql);
-      put(1, h, uh);
-      put(1, 8 + h, ul);
-    } else {
-      put(0, h, qh);
-      put(0, rep + h, ql);
-      put(0, 2 * rep + h, uh);
-      put(0, 3 * rep + h, ul);
-      if (h == 0)
-        for (int row = 4 * rep; row < 16; ++row) put(0, row, static_cast<_Float16>(0.0f));
+    for (int o = tid; o < n; o += 512) {
+      const int h = o >> 7, d = o & 127;
+      const float a = sa[h][d];
+      const float u = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
+      qu[static_cast<size_t>(bh0 + h) * 256 + 128 + d] = u;
+      const int kgi = d >> 5, ks = (d >> 3) & 3, j = d & 7;
+      const float ku = kappa * u;
+      const _Float16 qh = static_cast<_Float16>(a), uh = static_cast<_Float16>(ku);
+      const _Float16 ql = static_cast<_Float16>(a - static_cast<float>(qh));
+      const _Float16 ul = static_cast<_Float16>(ku - static_cast<float>(uh));
+      auto put = [&](int set, int row, _Float16 v) {
+        const size_t at = ((((static_cast<size_t>(b) * Hkv + g) * nset + set) * 4 + ks) * 64 + row + 16 * kgi) * 8 + j;
+        qa[at] = __builtin_bit_cast(unsigned short, v);
+      };
+      if (rep == 8) {
+        put(0, h, qh);
+        put(0, 8 + h, ql);
+        put(1, h, uh);
+        put(1, 8 + h, ul);
+      } else {
+        put(0, h, qh);
+        put(0, rep + h, ql);
+        put(0, 2 * rep + h, uh);
+        put(0, 3 * rep + h, ul);
+        if (h == 0)
+          for (int row = 4 * rep; row < 16; ++row) put(0, row, static_cast<_Float16>(0.0f));
+      }
     }
   }
 }
@@ -244,44 +278,67 @@ __global__ __launch_bounds__(256) void splitk_bypass_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- combine
+// One workgroup of 512 lanes per (KV head g, sequence b): merge each query
+// head's split partials with the running-max rescaling, then o = R_g^T o'
+// (compressed layers; lane (c, i) holds column i of rows 32c..32c+31 of R_g
+// and the quarters are summed through LDS in a fixed order), cast and store.
 template <bool OUT_BF16, bool BYPASS>
-__global__ __launch_bounds__(128) void combine_kernel(const float* part, const int* seq_lens, const float* R,
+__global__ __launch_bounds__(512) void combine_kernel(const float* part, const int* seq_lens, const float* R,
                                                       void* out, int Hq, int rep, int n_splits,
                                                       int split_tokens) {
-  const int bh = blockIdx.x;
-  const int b = bh / Hq;
-  const int g = (bh % Hq) / rep;
-  const int i = threadIdx.x;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, c = tid >> 7, i = tid & 127;
+  const int n = rep * 128;
+  const int bh0 = b * Hq + g * rep;
   const int T = seq_lens[b];
-  __shared__ float so[128];
-  float o = 0.0f;
-  if (T > 0) {
-    const int ns = (T + split_tokens - 1) / split_tokens;
-    const float* p = part + static_cast<size_t>(bh) * n_splits * kPart;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * kPart + 128]);
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float e = __expf(p[s * kPart + 128] - M);
-      num += e * p[s * kPart + i];
-      den += e * p[s * kPart + 129];
-    }
-    o = num / den;
-    if constexpr (!BYPASS) {
-      so[i] = o;
-      __syncthreads();
-      const float* r = R + static_cast<size_t>(g) * 128 * 128;
-      float a = 0.0f;
-      for (int j = 0; j < 128; ++j) a = fmaf(r[j * 128 + i], so[j], a);
-      o = a;
-    }
+  const int ns = T > 0 ? (T + split_tokens - 1) / split_tokens : 0;
+  __shared__ float so[8][128], pr[4][8][128];
+  float rr[32];
+  if constexpr (!BYPASS) {
+    const float* r = R + static_cast<size_t>(g) * 128 * 128 + (32 * c) * 128 + i;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) rr[u] = r[u * 128];
   }
-  if constexpr (OUT_BF16) {
-    const unsigned u = __float_as_uint(o);
-    const unsigned r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    static_cast<unsigned short*>(out)[bh * 128 + i] = static_cast<unsigned short>(r);
-  } else {
-    static_cast<float*>(out)[bh * 128 + i] = o;
+  auto store = [&](int h, int d, float o) {
+    const size_t at = static_cast<size_t>(bh0 + h) * 128 + d;
+    if constexpr (OUT_BF16) {
+      const unsigned u = __float_as_uint(o);
+      static_cast<unsigned short*>(out)[at] = static_cast<unsigned short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    } else {
+      static_cast<float*>(out)[at] = o;
+    }
+  };
+  for (int o = tid; o < n; o += 512) {
+    const int h = o >> 7, d = o & 127;
+    float v = 0.0f;
+    if (ns > 0) {
+      const float* p = part + static_cast<size_t>(bh0 + h) * n_splits * kPart;
+      float M = -INFINITY;
+      for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * kPart + 128]);
+      float num = 0.0f, den = 0.0f;
+      for (int s = 0; s < ns; ++s) {
+        const float e = __expf(p[s * kPart + 128] - M);
+        num += e * p[s * kPart + d];
+        den += e * p[s * kPart + 129];
+      }
+      v = num / den;
+    }
+    if constexpr (BYPASS) store(h, d, v);
+    else so[h][d] = v;
+  }
+  if constexpr (!BYPASS) {
+    __syncthreads();
+    for (int h = 0; h < rep; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) acc = fmaf(rr[u], so[h][32 * c + u], acc);
+      pr[c][h][i] = acc;
+    }
+    __syncthreads();
+    for (int o = tid; o < n; o += 512) {
+      const int h = o >> 7, d = o & 127;
+      store(h, d, (pr[0][h][d] + pr[1][h][d]) + (pr[2][h][d] + pr[3][h][d]));
+    }
   }
 }
 
@@ -306,7 +363,6 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   char* ws = static_cast<char*>(workspace);
   float* qu = reinterpret_cast<float*>(ws + plan.ws_qu);
   float* part = reinterpret_cast<float*>(ws + plan.ws_part);
-  const int bh = plan.batch * plan.n_q_heads;
 
   // 1. prologue
   {
@@ -322,7 +378,7 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / kDim);  // sqrt(pi/2) / m, m = d
     void* args[] = {const_cast<void**>(&q), &RT, &ST, &qu, &qa, &Hq, &rep, &kappa};
     ProfScope prof(kKPrologue, stream);
-    hipError_t e = hipLaunchKernel(fn, dim3(bh), dim3(128), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, plan.batch), dim3(512), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));
   }
   // 2. split-K mainloop
@@ -364,7 +420,7 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     int Hq = plan.n_q_heads, rep = plan.rep, ns = plan.n_splits, st = plan.split_tokens;
     void* args[] = {&part, const_cast<int**>(&seq_lens), &R, &out, &Hq, &rep, &ns, &st};
     ProfScope prof(kKCombine, stream);
-    hipError_t e = hipLaunchKernel(fn, dim3(bh), dim3(128), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, plan.batch), dim3(512), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode combine launch: %s", hipGetErrorString(e));
   }
   hipError_t e = hipGetLastError();
