@@ -29,18 +29,105 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--pools", type=int, default=6, help="store copies rotated to defeat the cache")
     ap.add_argument("--compress-iters", type=int, default=5)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=256,
+                    help="size of one plain device copy run before the workloads (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_llama3_8b_layer_and_compress_1m.txt")
+# kernels whose HBM traffic is taken from counters, with the sources that define them
+TRAFFIC_KERNELS = {
+    "splitk_mfma_kernel<4, 4, 4>": ["decode_mainloop.hip"],
+    "compress_mfma_kernel<2, 3, 3>": ["compress_mfma.hip"],
+}
+
+
+def sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "compressed_decode_attention_tq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe(torch, mib):
+    """One plain device copy (elementwise negate) of a known size: reads and writes
+    mib MiB.  Its FETCH_SIZE / WRITE_SIZE calibrate the counters of a run."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def traffic_summary(fetch_csv, write_csv, mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the traffic kernels, scaled by
+    what the same counters read for the copy probe (known bytes)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (name, _), v in vals.items():
+            out.setdefault(name, []).append(v * 1024.0)
+        return out
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    probe = [n for n in fetch if "neg" in n and "elementwise" in n]
+    if not probe:
+        raise SystemExit("copy probe kernel not found in " + fetch_csv)
+    nbytes = mib * (1 << 20)
+    f_scale = nbytes / statistics.median(fetch[probe[0]])
+    w_scale = nbytes / statistics.median(write[probe[0]])
+    lines = ["copy_probe bytes=%d fetch_factor=%.4f write_factor=%.4f" % (nbytes, f_scale, w_scale)]
+    for short, files in TRAFFIC_KERNELS.items():
+        names = [n for n in fetch if short.replace(" ", "") in n.replace(" ", "")]
+        if not names:
+            continue
+        fb = statistics.median(fetch[names[0]]) * f_scale
+        wb = statistics.median(write[names[0]]) * w_scale
+        lines.append("kernel=%s sources_sha=%s fetch_bytes=%d write_bytes=%d traffic_bytes=%d dispatches=%d"
+                     % (short.replace(" ", ""), sources_sha(files), fb, wb, fb + wb, len(fetch[names[0]])))
+    return lines
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel's sources changed since the counters were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    key = kernel.replace(" ", "")
+    for ln in lines:
+        f = dict(x.split("=", 1) for x in ln.split() if "=" in x)
+        if f.get("kernel") == key:
+            if f.get("sources_sha") != sources_sha(TRAFFIC_KERNELS[kernel]):
+                return None
+            return int(f["traffic_bytes"])
+    return None
 
 
 def decode_workload(torch, tq, synth, args):
@@ -109,7 +196,8 @@ def decode_workload(torch, tq, synth, args):
         "step_hbm_gbs": step_bytes / (ms / 1e3) / 1e9,
         "append_us": round(append_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("splitk_mfma_kernel<4, 4, 4>"),
                      "kernel": "splitk_mfma_kernel<4,4,4>", "avg_us": round(sk_avg_s * 1e6, 3),
                      "launches": sk_n, "bytes_per_launch": splitk_bytes},
         "config": {"workload": W["name"], "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
@@ -150,7 +238,8 @@ def compress_workload(torch, tq, synth, args):
             "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel": "compress_mfma_kernel<2,3,3>",
+                         "traffic": traffic_for("compress_mfma_kernel<2, 3, 3>"),
+                         "kernel": "compress_mfma_kernel<2,3,3>",
                          "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
 
 
@@ -193,6 +282,9 @@ def cpu_baseline(torch, synth, ctx, budget_s):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        print("\n".join(traffic_summary(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the compressed-KV path runs on one device per process and "
               "this build has no multi-GPU path (--gpus %d refused)" % args.gpus, file=sys.stderr)
@@ -206,6 +298,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     tq.lib()
+    if args.copy_probe_mib > 0:
+        copy_probe(torch, args.copy_probe_mib)
     log("decode workload")
     dec, ctx = decode_workload(torch, tq, synth, args)
     comp = None
