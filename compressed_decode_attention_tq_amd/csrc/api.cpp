@@ -143,6 +143,7 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   int split_tokens;
   if (splits > 0) {
     split_tokens = ((ctx + splits - 1) / splits + 63) / 64 * 64;
+    if (split_tokens > kMaxSplitTokens) split_tokens = kMaxSplitTokens;  // the mainloop's per-wave chunk limit
   } else {
     // Automatic: one wave of workgroups, ~2 per CU (the mainloop's LDS use
     // allows two resident per CU) over (batch x kv_heads x splits), each split
@@ -153,7 +154,7 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
     long long t = (ctx + want - 1) / want;
     t = (t + 63) / 64 * 64;
     if (t < 256) t = 256;
-    if (t > 4096) t = 4096;
+    if (t > kMaxSplitTokens) t = kMaxSplitTokens;
     if (t > ctx64) t = ctx64;
     split_tokens = static_cast<int>(t);
   }

@@ -50,6 +50,16 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Element index of the value code of (coordinate dim, in-page token t) in the
+// page's Vc stream: lane block 16 (t / 8) + dim % 16, group 2 (dim / 16) + (t % 8) / 4
+// of four codes, element t % 4.  The eight codes of (tile dim / 16, column,
+// token half) form one contiguous run, which the decode loads as a whole.
+__device__ __forceinline__ unsigned vcode_elem(int dim, int t) {
+  const unsigned block = 16u * static_cast<unsigned>(t >> 3) + static_cast<unsigned>(dim & 15);
+  const unsigned group = 2u * static_cast<unsigned>(dim >> 4) + static_cast<unsigned>((t & 7) >> 2);
+  return (block * 16u + group) * 4u + static_cast<unsigned>(t & 3);
+}
+
 // 32-bit word w of the LSB-first bitstream of 128 b-bit codes.
 template <int B>
 __device__ __forceinline__ unsigned pack_word(const unsigned char* codes, int w) {
@@ -171,12 +181,13 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
 
   unsigned char* base = a.pool + (static_cast<size_t>(slot >> 4) * a.H + h) * a.block_bytes;
   const int off = static_cast<int>(slot & 15);
-  // value code of coordinate i: bits [(16 i + off) v_bits, +v_bits) of the
-  // dimension-major Vc stream.  Neighbouring tokens of the page share these
-  // words, so the field is cleared and set with atomics on disjoint bit masks.
+  // value code of coordinate i in the lane-blocked Vc stream (element
+  // ((16 (off / 8) + i % 16) 16 + 2 (i / 16) + (off % 8) / 4) 4 + off % 4).
+  // Neighbouring tokens of the page share these words, so the field is cleared
+  // and set with atomics on disjoint bit masks.
   {
     unsigned* vw = reinterpret_cast<unsigned*>(base + a.off_vc);
-    const unsigned bit = static_cast<unsigned>(16 * i + off) * VB;
+    const unsigned bit = vcode_elem(i, off) * VB;
     const unsigned w = bit >> 5, sh = bit & 31;
     const unsigned mask = (1u << VB) - 1u;
     const unsigned cc = static_cast<unsigned>(code);

@@ -26,7 +26,7 @@
 // image in LDS.  A tile that is one whole
 // aligned page (16 consecutive slots from a multiple of 16) is stored with
 // coalesced 16-byte writes; any other tile is scattered token by token, with the
-// dimension-major value codes set by atomic clear/set of their bits.
+// lane-blocked value codes set by atomic clear/set of their bits.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -439,22 +439,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     __syncthreads();
 
-    // ---- D: value-code rows (coordinate d: 16 tokens x VB bits) into the image
-    if (tid < 128) {
-      const int d = tid;
-      unsigned long long row = 0;
+    // ---- D: value codes into the image's Vc field, in lane blocks: lane
+    // (h, c, i) packs the codes of tokens 8h..8h+7 of coordinate 16i + c (token
+    // 8h + k at bit k VB) into the VB bytes at (16h + c) 8VB + VB i.
+    if (tid < 256) {
+      const int h = tid >> 7, c = (tid >> 3) & 15, i = tid & 7;
+      const int d = 16 * i + c;
+      unsigned run = 0;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) row |= static_cast<unsigned long long>(vcode[t][d]) << (VB * t);
-      unsigned char* dst = &img[PG::vc + d * 2 * VB];
-      if constexpr (VB == 2) {
-        *reinterpret_cast<unsigned*>(dst) = static_cast<unsigned>(row);
-      } else if constexpr (VB == 4) {
-        *reinterpret_cast<unsigned long long*>(dst) = row;
+      for (int k = 0; k < 8; ++k) run |= static_cast<unsigned>(vcode[8 * h + k][d]) << (VB * k);
+      unsigned char* dst = &img[PG::vc + (16 * h + c) * 8 * VB + VB * i];
+      if constexpr (VB == 4) {
+        *reinterpret_cast<unsigned*>(dst) = run;
+      } else if constexpr (VB == 2) {
+        *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(run);
       } else {
-        unsigned short* d16 = reinterpret_cast<unsigned short*>(dst);
-        d16[0] = static_cast<unsigned short>(row);
-        d16[1] = static_cast<unsigned short>(row >> 16);
-        d16[2] = static_cast<unsigned short>(row >> 32);
+        dst[0] = static_cast<unsigned char>(run);
+        dst[1] = static_cast<unsigned char>(run >> 8);
+        dst[2] = static_cast<unsigned char>(run >> 16);
       }
     }
     __syncthreads();
@@ -492,7 +494,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           const int d = f - 128;
           unsigned* vw = reinterpret_cast<unsigned*>(page + PG::vc);
           const unsigned c = vcode[t][d];
-          const unsigned bit = static_cast<unsigned>(16 * d + o) * VB;
+          // lane-blocked Vc stream: block 16 (o / 8) + d % 16, group 2 (d / 16) + (o % 8) / 4
+          const unsigned elem = ((16u * (o >> 3) + (d & 15)) * 16u + 2u * (d >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
+          const unsigned bit = elem * VB;
           const unsigned wi = bit >> 5, sh = bit & 31, mask = (1u << VB) - 1u;
           atomicAnd(&vw[wi], ~(mask << sh));
           atomicOr(&vw[wi], c << sh);

@@ -151,31 +151,55 @@ __device__ __forceinline__ unsigned sub_h2(unsigned x, unsigned y) {
   return __builtin_bit_cast(unsigned, r);
 }
 
+// Lookup tables in LDS, one copy per lane of a bank-parallel group, so that
+// the random code-indexed reads of a wave do not collide.  Entry e of both
+// tables shares the 256 bytes at 256 e, so that a lookup address is the code
+// byte in bits 8..15 and the lane's copy offset in bits 0..7 (one byte permute):
+//   bytes   0..127: key entry (KB 4: byte of two codes -> two float16 values,
+//                   32 copies of 4 bytes; KB 2: byte of four codes -> four
+//                   float16 values, 16 copies of 8 bytes; KB 3: 6 bits of two
+//                   codes, entries 0..63 only, 32 copies of 4 bytes);
+//   bytes 128..255: sign entry (byte of 8 sign bits -> eight float16 +-1,
+//                   8 copies of 16 bytes).
+constexpr int kLutEntry = 256;
+template <int KB>
+struct KeyLut {
+  static constexpr int copy_bytes = KB == 2 ? 8 : 4;
+  static constexpr int copies = 128 / copy_bytes;
+};
+constexpr int kSignBase = 128, kSignCopies = 8;
+
+// LDS address of entry `byte k of x` for a lane whose copy offset is `off`
+// (< 256): one v_perm_b32 puts off in byte 0 and the code byte in byte 1.
+template <int K>
+__device__ __forceinline__ unsigned lut_addr(unsigned x, unsigned off) {
+  return __builtin_amdgcn_perm(x, off, 0x0C0C0000u | ((4u + K) << 8));
+}
+
 // B operand of the Q.K product for K-step s: the float16 codebook values of the
 // lane's 8 dims (32kg + 8s .. +7), from the packed codes of its 32-dim block.
+// lut: the table's LDS base; koff: the lane's key copy offset.
 template <int KB>
-__device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const unsigned* lut) {
+__device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const unsigned char* lut, unsigned koff) {
   u32x4 r;
   if constexpr (KB == 4) {
     const unsigned x = kc[s];  // 8 nibbles
-    r[0] = lut[x & 0xffu];
-    r[1] = lut[(x >> 8) & 0xffu];
-    r[2] = lut[(x >> 16) & 0xffu];
-    r[3] = lut[x >> 24];
+    r[0] = *reinterpret_cast<const unsigned*>(lut + lut_addr<0>(x, koff));
+    r[1] = *reinterpret_cast<const unsigned*>(lut + lut_addr<1>(x, koff));
+    r[2] = *reinterpret_cast<const unsigned*>(lut + lut_addr<2>(x, koff));
+    r[3] = *reinterpret_cast<const unsigned*>(lut + lut_addr<3>(x, koff));
   } else if constexpr (KB == 2) {
-    const unsigned x = kc[s >> 1] >> (16 * (s & 1));  // 16 bits = 8 dims
-    const u32x2* l2 = reinterpret_cast<const u32x2*>(lut);
-    const u32x2 a = l2[x & 0xffu];
-    const u32x2 b = l2[(x >> 8) & 0xffu];
+    const unsigned x = kc[s >> 1];  // bytes 2(s%2), 2(s%2)+1 = 8 dims
+    const u32x2 a = *reinterpret_cast<const u32x2*>(lut + ((s & 1) ? lut_addr<2>(x, koff) : lut_addr<0>(x, koff)));
+    const u32x2 b = *reinterpret_cast<const u32x2*>(lut + ((s & 1) ? lut_addr<3>(x, koff) : lut_addr<1>(x, koff)));
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   } else {  // KB == 3: 24 bits at bit 24 s of the block's 96
     const int bit = 24 * s;
     const int w = bit >> 5, sh = bit & 31;
     const unsigned x = (w + 1 < 3) ? __builtin_amdgcn_alignbit(kc[w + 1], kc[w], sh) : (kc[w] >> sh);
-    r[0] = lut[x & 63u];
-    r[1] = lut[(x >> 6) & 63u];
-    r[2] = lut[(x >> 12) & 63u];
-    r[3] = lut[(x >> 18) & 63u];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = *reinterpret_cast<const unsigned*>(lut + ((((x >> (6 * q)) & 63u) << 8) | koff));
   }
   return as_h8(r);
 }
@@ -189,26 +213,23 @@ constexpr unsigned centre_bits(int p, int vb) {
   return (static_cast<unsigned>(25 - p) * 0x0400u + ((1u << (vb - 1)) << p)) * 0x10001u;
 }
 
-// A operand of the P.V product for one 16-coordinate tile: coordinate d of
-// tokens 4kg .. 4kg+3 of both pages, slot 2cc + page.  Value codes are
-// dimension-major: coordinate d, token t at bits (16 d + t) v_bits of Vc.
+// A operand of the P.V product for tile i (coordinates 16i .. 16i+15): the
+// lane's run of 8 codes of coordinate 16i + col (tokens 8(kg%2) .. +7 of page
+// kg/2, token 8(kg%2) + k at bit VB k of the run).  Element pair cc of the
+// operand is (token cc, token 4 + cc): the run's two 4-code groups go to the
+// two float16 halves, each code becomes a centred float16 integer exactly.
 template <int VB>
-__device__ __forceinline__ half8 value_operand(const unsigned char* v0, const unsigned char* v1, int d, int kg) {
+__device__ __forceinline__ half8 value_operand(const unsigned* vc, int i) {
   unsigned x;
   if constexpr (VB == 4) {
-    const unsigned a = *reinterpret_cast<const unsigned short*>(v0 + 8 * d + 2 * kg);
-    const unsigned b = *reinterpret_cast<const unsigned short*>(v1 + 8 * d + 2 * kg);
-    x = hi16_or(b, a);
+    x = vc[i];
   } else if constexpr (VB == 2) {
-    x = hi16_or(v1[4 * d + kg], v0[4 * d + kg]);
-  } else {  // VB == 3: 12 bits at bit 48 d + 12 kg (may straddle two words)
-    const int bit = 48 * d + 12 * kg;
-    const int w = bit >> 5, sh = bit & 31;
-    const unsigned* a = reinterpret_cast<const unsigned*>(v0) + w;
-    const unsigned* b = reinterpret_cast<const unsigned*>(v1) + w;
-    const unsigned fa = __builtin_amdgcn_alignbit(a[1], a[0], sh) & 0xfffu;
-    const unsigned fb = __builtin_amdgcn_alignbit(b[1], b[0], sh) & 0xfffu;
-    x = hi16_or(fb, fa);
+    // bytes 2(i%2), 2(i%2)+1 of the dword -> bytes 0 and 2 (zeros between)
+    x = __builtin_amdgcn_perm(vc[i >> 1], vc[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
+  } else {  // VB == 3: 24 bits at bit 24 i of the lane's 192
+    const int bit = 24 * i, w = bit >> 5, sh = bit & 31;
+    const unsigned f = (sh <= 8) ? (vc[w] >> sh) : __builtin_amdgcn_alignbit(vc[w + 1], vc[w], sh);
+    x = hi16_or((f >> 12) & 0xfffu, f & 0xfffu);
   }
   // Field cc sits at bit VB*cc of each half.  Fields that end inside the
   // float16 mantissa (bits 0..9) are used in place with a matching exponent;
@@ -228,7 +249,11 @@ __device__ __forceinline__ half8 value_operand(const unsigned char* v0, const un
   return as_h8(r);
 }
 
-typedef __attribute__((address_space(3))) unsigned char lbyte;
+// P.V operand slot of (page pg, in-page token t): the inverse of value_operand's
+// element order (slot 8kg + j holds page kg/2, token 8(kg%2) + j/2 + 4(j%2)).
+__device__ __forceinline__ int pv_slot(int pg, int t) {
+  return 16 * pg + 8 * (t >> 3) + 2 * (t & 3) + ((t >> 2) & 1);
+}
 
 // Byte layout of one (block, head) page; the host checks that it matches the
 // store layout before launching.
@@ -240,35 +265,75 @@ struct PageLayout {
   static constexpr int vc = kn + 64;
   static constexpr int vsz = vc + 256 * VB;
   static constexpr int bytes = vsz + 256;
-  static constexpr int copies = (bytes + 1023) / 1024;  // 64 lanes x 16 B per copy
-  static constexpr int lds = 1024 * copies;
 };
 
-// s_waitcnt with vmcnt <= n (lgkmcnt and expcnt not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // The memory clobber keeps every LDS read of the staged page below the wait.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Copy one page from global memory straight into LDS (no registers): each
-// instruction moves 64 lanes x 16 B to dst + 16*lane; lanes past the page end
-// re-read the page start and only fill the LDS padding.
+// Dword-aligned vector types for the global loads.
+typedef unsigned u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef unsigned u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+typedef unsigned u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+
+// One lane's share of one 32-token chunk (pages 0 and 1), loaded from the pool
+// straight into registers: every field is stored so that this share is one
+// contiguous read per field.
 template <int KB, int VB>
-__device__ __forceinline__ void stage_page(const unsigned char* page, unsigned char* dst, int lane) {
+struct Chunk {
+  unsigned kc[2][KB];   // key codes of 32-dim block kg of token col
+  unsigned ks[2];       // their sign bits
+  unsigned kn[2];       // float16 n, gamma of token col
+  u32x4 sz[2];          // float16 scale, zero of token col's 4 groups
+  unsigned vc[2 * VB];  // value-code runs of lane block 16(kg%2) + col of page kg/2
+};
+
+// The lane's byte offsets of its fields inside a page (loop-invariant).
+struct LaneOffsets {
+  unsigned kc, ks, kn, sz, vc;
+};
+template <int KB, int VB>
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   using PL = PageLayout<KB, VB>;
+  const unsigned col = lane & 15, kg = lane >> 4;
+  return LaneOffsets{PL::kc + static_cast<unsigned>(lane) * (4 * KB), PL::ks + 4u * lane, PL::kn + 4u * col,
+                     PL::vsz + 16u * col, PL::vc + (16u * (kg & 1u) + col) * (8 * VB)};
+}
+
+// Loads of one lane: a page base common to the wave plus a 32-bit lane offset.
+template <int KB, int VB>
+__device__ __forceinline__ void load_chunk(Chunk<KB, VB>& c, const unsigned char* p0, const unsigned char* p1,
+                                           const LaneOffsets& o, bool second_page_values) {
+  const unsigned char* pg[2] = {p0, p1};
 #pragma unroll
-  for (int i = 0; i < PL::copies; ++i) {
-    const int off = 1024 * i + 16 * lane;
-    const unsigned char* src = page + (off < PL::bytes ? off : 0);
-    // Issued as inline asm on purpose: the compiler's wait insertion treats an
-    // LDS-DMA copy it can see as aliasing every later LDS read and drains the
-    // vector-memory counter before the first one, which serialises the double
-    // buffer.  Completion of these copies is awaited explicitly (wait_vmcnt).
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(
-        static_cast<unsigned>(reinterpret_cast<unsigned long>((lbyte*)(dst + 1024 * i))));  // LDS address
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
-                 : "memory", "m0");
+  for (int t = 0; t < 2; ++t) {
+    const unsigned char* kp = pg[t] + o.kc;
+    if constexpr (KB == 4) {
+      const u32x4a v = *reinterpret_cast<const u32x4a*>(kp);
+      c.kc[t][0] = v[0]; c.kc[t][1] = v[1]; c.kc[t][2] = v[2]; c.kc[t][3] = v[3];
+    } else if constexpr (KB == 3) {
+      const u32x3a v = *reinterpret_cast<const u32x3a*>(kp);
+      c.kc[t][0] = v[0]; c.kc[t][1] = v[1]; c.kc[t][2] = v[2];
+    } else {
+      const u32x2a v = *reinterpret_cast<const u32x2a*>(kp);
+      c.kc[t][0] = v[0]; c.kc[t][1] = v[1];
+    }
+    c.ks[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.ks);
+    c.kn[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.kn);
+    c.sz[t] = *reinterpret_cast<const u32x4*>(pg[t] + o.sz);
+  }
+  const unsigned char* vp = (second_page_values ? p1 : p0) + o.vc;
+  if constexpr (VB == 4) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(vp);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(vp + 16);
+    c.vc[0] = a[0]; c.vc[1] = a[1]; c.vc[2] = a[2]; c.vc[3] = a[3];
+    c.vc[4] = b[0]; c.vc[5] = b[1]; c.vc[6] = b[2]; c.vc[7] = b[3];
+  } else if constexpr (VB == 2) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(vp);
+    c.vc[0] = a[0]; c.vc[1] = a[1]; c.vc[2] = a[2]; c.vc[3] = a[3];
+  } else {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const u32x2a a = *reinterpret_cast<const u32x2a*>(vp + 8 * u);
+      c.vc[2 * u] = a[0];
+      c.vc[2 * u + 1] = a[1];
+    }
   }
 }
 
@@ -335,17 +400,20 @@ __device__ __forceinline__ void fold_scores(const floatx4& acc1, const floatx4& 
   }
 }
 
-// The block table comes as its own read-only, non-aliased parameter so that the
-// wave-uniform block-id reads become scalar loads (they must not wait on the
-// vector-memory counter that tracks the page copies in flight).
+
+// Chunks in flight per wave: the pages of the next kRing - 1 chunks are being
+// read while one is processed.
+constexpr int kRing = 3;
+
+// The block table comes as its own read-only, non-aliased parameter.
 template <int NREP, int KB, int VB>
 __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int* __restrict__ btab) {
   using PL = PageLayout<KB, VB>;
   using SM = ScoreMap<NREP>;
+  using KL = KeyLut<KB>;
   constexpr int HPL = SM::HPL;
   constexpr int NSET = NREP == 8 ? 2 : 1;
   constexpr int WC = 2 * NREP;  // used P.V columns (hi, lo per head)
-  constexpr int LUTC = (KB == 4) ? 256 : (KB == 2 ? 512 : 64);  // dwords
   constexpr float kMidCode = static_cast<float>(1 << (VB - 1));
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = a.seq_lens[b];
@@ -353,10 +421,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   if (start >= T) return;
   const int end = min(T, start + a.split_tokens);
 
-  __shared__ unsigned lut_c[LUTC];
-  __shared__ u32x4 lut_s[256];
-  // per wave, two stages of two pages each (the chunk being processed and the next)
-  __shared__ __attribute__((aligned(16))) unsigned char stg[4][2][2][PL::lds];
+  __shared__ __attribute__((aligned(16))) unsigned char lut[256 * kLutEntry];
   __shared__ __attribute__((aligned(16))) unsigned short wl[4][4][WC][32];  // P.V weights (float16)
   __shared__ __attribute__((aligned(16))) unsigned zero16[4];
   __shared__ float mg_m[4][NREP], mg_l[4][NREP];
@@ -371,22 +436,14 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     return a.pool + (static_cast<long long>(blk) * a.Hkv + g) * a.block_bytes;
   };
 
-  // first chunk of this wave: start its copy before the table/operand setup
-  int c0 = start + wave * 32;
-  int nb0 = 0, nb1 = 0;
-  if (c0 < end) {
-    const int b0 = btab[tbl + (c0 >> 4)];
-    const int b1 = (c0 + 16 < end) ? btab[tbl + (c0 >> 4) + 1] : b0;
-    stage_page<KB, VB>(page_ptr(b0), &stg[wave][0][0][0], lane);
-    stage_page<KB, VB>(page_ptr(b1), &stg[wave][0][1][0], lane);
-    const int cn = c0 + 128;
-    if (cn < end) {
-      nb0 = btab[tbl + (cn >> 4)];
-      nb1 = (cn + 16 < end) ? btab[tbl + (cn >> 4) + 1] : nb0;
-    }
+  // Block ids of this wave's pages, one per lane: lane 2j + p holds page p of
+  // the wave's chunk j (chunk j = tokens start + 32 (wave + 4j) .. +31; at most
+  // 32 chunks per wave).  The query operand (prepared by the prologue) follows.
+  int ids = 0;
+  {
+    const int tok = start + 32 * (wave + 4 * (lane >> 1)) + 16 * (lane & 1);
+    if (tok < end) ids = btab[tbl + (tok >> 4)];
   }
-
-  // ---- query operand (prepared by the prologue)
   half8 qa[NSET][4];
   {
     const u32x4* src = a.qa + static_cast<size_t>(b * a.Hkv + g) * NSET * 4 * 64 + lane;
@@ -395,37 +452,64 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
 #pragma unroll
       for (int s = 0; s < 4; ++s) qa[st][s] = as_h8(src[(st * 4 + s) * 64]);
   }
-
-  // ---- tables
-  {
-    const int e = tid;  // 256 threads, 256 entries
-    u32x4 w;
+  const LaneOffsets lofs = lane_offsets<KB, VB>(lane);
+  const int span = end - start - 32 * wave;
+  const int nch = span > 0 ? (span + 127) / 128 : 0;  // chunks of this wave
+  auto load = [&](Chunk<KB, VB>& c, int j) {
+    const int c0 = start + 32 * (wave + 4 * j);
+    const int b0 = __builtin_amdgcn_readlane(ids, 2 * j);
+    const int b1 = (c0 + 16 < end) ? __builtin_amdgcn_readlane(ids, 2 * j + 1) : b0;
+    load_chunk<KB, VB>(c, page_ptr(b0), page_ptr(b1), lofs, kg >= 2);
+  };
+  // Every step loads one chunk (past the wave's last chunk, the last one again:
+  // a few cached re-reads) so that the number of loads in flight is the same on
+  // every path, and each wait leaves the two younger chunks outstanding.
+  const int jmax = nch > 0 ? nch - 1 : 0;
+  Chunk<KB, VB> ring[kRing];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned lo = ((e >> (2 * i)) & 1) ? 0x3C00u : 0xBC00u;
-      const unsigned hi = ((e >> (2 * i + 1)) & 1) ? 0x3C00u : 0xBC00u;
-      w[i] = lo | (hi << 16);
-    }
-    lut_s[e] = w;
+  for (int r = 0; r < kRing; ++r) load(ring[r], r < jmax ? r : jmax);
+
+  // ---- tables (lane copies); the codebook is staged in LDS from scalar
+  //      registers so that no vector load joins the chunk loads in flight
+  __shared__ unsigned short cent_h[16];
+  if (tid == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cent_h[e] = static_cast<unsigned short>(h_bits(a.cent[e]));
+  }
+  __syncthreads();
+  {
+    // lane tid fills entry tid of both tables, all copies (16-byte stores)
+    const int e = tid;
+    u32x4 kv = {0u, 0u, 0u, 0u};
     if constexpr (KB == 4) {
-      lut_c[e] = h_bits(a.cent[e & 15]) | (h_bits(a.cent[e >> 4]) << 16);
+      const unsigned v = cent_h[e & 15] | (static_cast<unsigned>(cent_h[e >> 4]) << 16);
+      kv = u32x4{v, v, v, v};
     } else if constexpr (KB == 2) {
-      lut_c[2 * e] = h_bits(a.cent[e & 3]) | (h_bits(a.cent[(e >> 2) & 3]) << 16);
-      lut_c[2 * e + 1] = h_bits(a.cent[(e >> 4) & 3]) | (h_bits(a.cent[e >> 6]) << 16);
+      const unsigned v0 = cent_h[e & 3] | (static_cast<unsigned>(cent_h[(e >> 2) & 3]) << 16);
+      const unsigned v1 = cent_h[(e >> 4) & 3] | (static_cast<unsigned>(cent_h[e >> 6]) << 16);
+      kv = u32x4{v0, v1, v0, v1};
     } else {
-      if (e < 64) lut_c[e] = h_bits(a.cent[e & 7]) | (h_bits(a.cent[e >> 3]) << 16);
+      const unsigned v = cent_h[e & 7] | (static_cast<unsigned>(cent_h[(e >> 3) & 7]) << 16);
+      kv = u32x4{v, v, v, v};
+    }
+    u32x4 sv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned lo = ((e >> (2 * q)) & 1) ? 0x3C00u : 0xBC00u;
+      const unsigned hi = ((e >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u;
+      sv[q] = lo | (hi << 16);
+    }
+    u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * kLutEntry]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ent[q] = kv;      // key copies
+      ent[8 + q] = sv;  // sign copies
     }
     if (tid < 4) zero16[tid] = 0u;
   }
   __syncthreads();
-  // Consume the query operand once here: the compiler then waits for its loads
-  // before the loop (together with the first page copies, which are needed
-  // anyway).  Left to the loop, that wait would also cover the next chunk's
-  // copies, which the compiler cannot tell apart, in every iteration.
-#pragma unroll
-  for (int st = 0; st < NSET; ++st)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(qa[st][s]));
+  const unsigned koff = static_cast<unsigned>((lane % KL::copies) * KL::copy_bytes);
+  const unsigned soff = static_cast<unsigned>(kSignBase + (lane % kSignCopies) * 16);
 
   // ---- per-wave running state (score layout: slot hs = head SM::head(kg, hs))
   const bool active = SM::active(kg);
@@ -441,58 +525,28 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
 #pragma unroll
   for (int i = 0; i < 8; ++i) accv[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float sc = a.scale * kInvSqrtD;
+  const int slot0 = pv_slot(0, col);
 
-  int stage = 0;
-  for (; c0 < end; c0 += 128, stage ^= 1) {
-    const int cn = c0 + 128;
-    if (cn < end) {
-      stage_page<KB, VB>(page_ptr(nb0), &stg[wave][stage ^ 1][0][0], lane);
-      stage_page<KB, VB>(page_ptr(nb1), &stg[wave][stage ^ 1][1][0], lane);
-      const int cnn = cn + 128;
-      if (cnn < end) {
-        nb0 = btab[tbl + (cnn >> 4)];
-        nb1 = (cnn + 16 < end) ? btab[tbl + (cnn >> 4) + 1] : nb0;
-      }
-      wait_vmcnt<2 * PL::copies>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    const unsigned char* pg[2] = {&stg[wave][stage][0][0], &stg[wave][stage][1][0]};
-
+  auto process = [&](const Chunk<KB, VB>& c, int c0) {
     // ---- scores: one 16-token tile per page
     float s[2][HPL];
-    bool valid[2];
-    unsigned vsz[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const unsigned* kp = reinterpret_cast<const unsigned*>(pg[t] + PL::kc + (kg * 16 + col) * (4 * KB));
-      unsigned kcw[KB];
-      if constexpr (KB == 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(kp);
-        kcw[0] = v[0]; kcw[1] = v[1]; kcw[2] = v[2]; kcw[3] = v[3];
-      } else if constexpr (KB == 3) {
-        const u32x3 v = *reinterpret_cast<const u32x3*>(kp);
-        kcw[0] = v[0]; kcw[1] = v[1]; kcw[2] = v[2];
-      } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(kp);
-        kcw[0] = v[0]; kcw[1] = v[1];
-      }
-      const unsigned ksw = *reinterpret_cast<const unsigned*>(pg[t] + PL::ks + (kg * 16 + col) * 4);
       floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f}, acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        acc1 = mfma(qa[0][st], dequant_keys<KB>(kcw, st, lut_c), acc1);
-        acc2 = mfma(qa[NSET - 1][st], as_h8(lut_s[(ksw >> (8 * st)) & 0xffu]), acc2);
+        acc1 = mfma(qa[0][st], dequant_keys<KB>(c.kc[t], st, lut, koff), acc1);
+        const unsigned sa = (st == 0) ? lut_addr<0>(c.ks[t], soff)
+                          : (st == 1) ? lut_addr<1>(c.ks[t], soff)
+                          : (st == 2) ? lut_addr<2>(c.ks[t], soff) : lut_addr<3>(c.ks[t], soff);
+        acc2 = mfma(qa[NSET - 1][st], as_h8(*reinterpret_cast<const u32x4*>(lut + sa)), acc2);
       }
-      const unsigned kn = *reinterpret_cast<const unsigned*>(pg[t] + PL::kn + col * 4);
-      const u32x4 sz = *reinterpret_cast<const u32x4*>(pg[t] + PL::vsz + col * 16);
-      vsz[t][0] = sz[0]; vsz[t][1] = sz[1]; vsz[t][2] = sz[2]; vsz[t][3] = sz[3];
-      valid[t] = active && (c0 + 16 * t + col) < end;
+      const bool valid = active && (c0 + 16 * t + col) < end;
       float f[HPL];
-      fold_scores<NREP>(acc1, acc2, h_hi(kn), kg, f);
-      const float alpha = sc * h_lo(kn);
+      fold_scores<NREP>(acc1, acc2, h_hi(c.kn[t]), kg, f);
+      const float alpha = sc * h_lo(c.kn[t]);
 #pragma unroll
-      for (int hs = 0; hs < HPL; ++hs) s[t][hs] = valid[t] ? alpha * f[hs] : -INFINITY;
+      for (int hs = 0; hs < HPL; ++hs) s[t][hs] = valid ? alpha * f[hs] : -INFINITY;
     }
 
     // ---- online softmax (running max per head, lazy rescale)
@@ -535,18 +589,18 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       lsum[hs] += p[0][hs] + p[1][hs];
     }
 
-    // ---- P.V weights w = p * scale in two float16 pieces -> LDS (slot 2 col + page);
-    //      offset term p (zero + mid scale) on the VALU
+    // ---- P.V weights w = p * scale in two float16 pieces -> LDS (slots
+    //      pv_slot(page, col)); offset term p (zero + mid scale) on the VALU
     if (active) {
 #pragma unroll
       for (int hs = 0; hs < HPL; ++hs) {
         const int h = SM::head(kg, hs);
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
-          const _Float16 s0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[0][G] & 0xffffu));
-          const _Float16 s1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[1][G] & 0xffffu));
-          const _Float16 z0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[0][G] >> 16));
-          const _Float16 z1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(vsz[1][G] >> 16));
+          const _Float16 s0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[0][G] & 0xffffu));
+          const _Float16 s1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[1][G] & 0xffffu));
+          const _Float16 z0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[0][G] >> 16));
+          const _Float16 z1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[1][G] >> 16));
           const float w0 = p[0][hs] * static_cast<float>(s0);
           const float w1 = p[1][hs] * static_cast<float>(s1);
           const _Float16 hi0 = static_cast<_Float16>(w0), hi1 = static_cast<_Float16>(w1);
@@ -554,25 +608,41 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
           const _Float16 lo1 = static_cast<_Float16>(fmaf(p[1][hs], static_cast<float>(s1), -static_cast<float>(hi1)));
           zacc[hs][G] = fmaf(p[0][hs], fmaf(kMidCode, static_cast<float>(s0), static_cast<float>(z0)), zacc[hs][G]);
           zacc[hs][G] = fmaf(p[1][hs], fmaf(kMidCode, static_cast<float>(s1), static_cast<float>(z1)), zacc[hs][G]);
-          const half2v hv = {hi0, hi1}, lv = {lo0, lo1};
-          *reinterpret_cast<half2v*>(&wl[wave][G][h][2 * col]) = hv;
-          *reinterpret_cast<half2v*>(&wl[wave][G][NREP + h][2 * col]) = lv;
+          unsigned short* wh = &wl[wave][G][h][0];
+          unsigned short* wo = &wl[wave][G][NREP + h][0];
+          wh[slot0] = __builtin_bit_cast(unsigned short, hi0);
+          wh[slot0 + 16] = __builtin_bit_cast(unsigned short, hi1);
+          wo[slot0] = __builtin_bit_cast(unsigned short, lo0);
+          wo[slot0 + 16] = __builtin_bit_cast(unsigned short, lo1);
         }
       }
     }
 
     // ---- P.V on the matrix cores: tile i = coordinates 16i .. 16i+15 (group i/2)
-    const unsigned char* v0 = pg[0] + PL::vc;
-    const unsigned char* v1 = pg[1] + PL::vc;
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
       const u32x4* wsrc = (col < WC) ? reinterpret_cast<const u32x4*>(&wl[wave][G][col][8 * kg])
                                      : reinterpret_cast<const u32x4*>(zero16);
       const half8 w = as_h8(*wsrc);
-      accv[2 * G] = mfma(value_operand<VB>(v0, v1, 32 * G + col, kg), w, accv[2 * G]);
-      accv[2 * G + 1] = mfma(value_operand<VB>(v0, v1, 32 * G + 16 + col, kg), w, accv[2 * G + 1]);
+      accv[2 * G] = mfma(value_operand<VB>(c.vc, 2 * G), w, accv[2 * G]);
+      accv[2 * G + 1] = mfma(value_operand<VB>(c.vc, 2 * G + 1), w, accv[2 * G + 1]);
+    }
+  };
+
+  // Whole rounds of kRing chunks (every step processes one and loads one),
+  // then the last nch % kRing chunks, already in flight.
+  int j0 = 0;
+  for (; j0 + kRing <= nch; j0 += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      const int j = j0 + r;
+      process(ring[r], start + 32 * (wave + 4 * j));
+      load(ring[r], j + kRing < jmax ? j + kRing : jmax);
     }
   }
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r)
+    if (j0 + r < nch) process(ring[r], start + 32 * (wave + 4 * (j0 + r)));
 
   // ---- per-wave results -> LDS, then merge the four waves
 #pragma unroll
@@ -596,9 +666,9 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) accv[i][r] = add_from_col<NREP>(accv[i][r]);
-  __syncthreads();  // every wave is past its loop: the staging area is free
-  float* mbuf = reinterpret_cast<float*>(&stg[0][0][0][0]);  // [4 waves][NREP][128]
-  static_assert(sizeof(stg) >= 4 * NREP * 128 * sizeof(float), "merge area size");
+  __syncthreads();  // every wave is past its loop: the tables' space is free
+  float* mbuf = reinterpret_cast<float*>(&lut[0]);  // [4 waves][NREP][128]
+  static_assert(sizeof(lut) >= 4 * NREP * 128 * sizeof(float), "merge area size");
   if (col < NREP) {
     const int h = col;
 #pragma unroll

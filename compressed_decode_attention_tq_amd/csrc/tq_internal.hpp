@@ -14,6 +14,9 @@ constexpr int kOpSets = 5;  // compressor operand sets per row tile
 constexpr int kDim = 128;     // head_dim supported by the kernels
 constexpr int kPage = 16;     // tokens per block
 constexpr int kGroup = 32;    // value group width
+// Longest context span of one split-K workgroup: its four waves take 32-token
+// chunks in turn, at most 32 each (one block id per lane of a 64-lane wave).
+constexpr int kMaxSplitTokens = 4096;
 
 // ---------------------------------------------------------------- errors
 tq_status fail(tq_status st, const char* fmt, ...);

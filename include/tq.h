@@ -52,13 +52,17 @@
  *                            t, the k_bits stream of dims 32j .. 32j+31
  *     Ks  [4][16][4]         QJL sign bits (1 <=> (S rho)_j >= 0), same blocking
  *     Kn  [16][2] fp16       ||k|| then gamma = ||rho||
- *     Vc  [128][16] v_bits   value codes, dimension-major: one stream over
- *                            (dim, token) in the order dim*16 + token
+ *     Vc  [32][64] v_bits    value codes in 32 lane blocks: for dim = 16i + c
+ *                            and token t = 8h + k, block 16h + c, group
+ *                            2i + k/4 of four codes, element k % 4 (one stream
+ *                            in the order block, group, element)
  *     Vsz [16][4][2] fp16    per 32-wide group: scale then zero
- *   Key fields are blocked so that a 32-dim slice of one token is contiguous;
- *   value codes are dimension-major so that one coordinate of consecutive
- *   tokens is contiguous (the decode contraction runs over tokens).  A single
- *   token appended to a page therefore shares Vc bytes with its neighbours.
+ *   Every field is laid out so that one lane of the decode's 64-lane wave
+ *   loads its share of a page with one contiguous read: key fields are blocked
+ *   so that a 32-dim slice of one token is contiguous, and the value codes of
+ *   8 tokens of one coordinate (one matrix-core operand row) are one run of
+ *   8*v_bits bits, the 8 runs of a lane block adjacent.  A single token
+ *   appended to a page therefore shares Vc bytes with its neighbours.
  *   Bypass (uncompressed) layers: region = K [16][128] bf16, then V [16][128] bf16.
  */
 #ifndef TQ_H
@@ -189,8 +193,9 @@ tq_status tq_decode_workspace_size(const tq_layer* layer, int batch, int n_q_hea
  *   max_seq_len  host bound on seq_lens, used to plan the split-K grid
  *   softmax_scale  0 selects 1/sqrt(128)
  *   num_splits   0 = automatic (from max_seq_len, batch, heads and the CU count);
- *                otherwise the number of context splits per sequence.  The
- *                environment variable TQ_DECODE_SPLITS overrides 0.
+ *                otherwise the number of context splits per sequence, raised
+ *                where needed so that no split spans more than 4096 tokens.
+ *                The environment variable TQ_DECODE_SPLITS overrides 0.
  *   out          device [batch][n_q_heads][128] of out_dtype (F32 or BF16, RNE)
  *   workspace    device scratch of at least tq_decode_workspace_size() bytes,
  *                256-byte aligned; contents need not be initialised

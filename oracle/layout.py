@@ -18,8 +18,10 @@ stream, bit k of the stream being bit k%8 of byte k//8.
                            token t, the b-bit stream of dims 32j .. 32j+31
   Ks  [m/32][P][4]         QJL sign bits (bit = 1 <=> y >= 0), same blocking
   Kn  [P][2] fp16          ||k|| then gamma = ||rho||   (little-endian)
-  Vc  [d][P] x v_bits      value codes, dimension-major: one b-bit stream over
-                           (dim, token) pairs in the order dim*P + token
+  Vc  [2P][d/2] x v_bits   value codes in 32 lane blocks: for dim = 16i + c
+                           and token t = 8h + k, block 16h + c, group
+                           2i + k//4 of four codes, element k % 4; one b-bit
+                           stream in the order (block, group, element)
   Vsz [P][d/G][2] fp16     per group: scale then zero
 Bypass (uncompressed) layers: region = Kb [P][d] bf16 followed by Vb [P][d] bf16.
 """
@@ -115,9 +117,14 @@ def _field_bits(layout, base, offs, name):
         j = np.arange(layout.m)[None, :]
         rec = (j // 32) * P + offs
         return (base + layout.off_ks) * 8 + rec * 32 + (j % 32)
-    if name == "vcode":    # [N, d]: dimension-major stream
+    if name == "vcode":    # [N, d]: lane blocks of 8 tokens x 16-dim tiles
         dim = np.arange(layout.d)[None, :]
-        return (base + layout.off_vc) * 8 + (dim * P + offs) * layout.v_bits
+        i, c = dim // 16, dim % 16
+        h, k = offs // 8, offs % 8
+        block = 16 * h + c
+        group = 2 * i + k // 4
+        elem = (block * (layout.d // 16) * 2 + group) * 4 + k % 4
+        return (base + layout.off_vc) * 8 + elem * layout.v_bits
     raise KeyError(name)
 
 

@@ -106,13 +106,15 @@ def test_record_placement_by_hand():
     layout.put_records(pool, lay, 2, [37], 1, r)
     nz = np.flatnonzero(pool)
     assert list(nz) == [base + lay.off_ks + 37 * 4] and pool[nz[0]] == 1 << 6
-    # value dim 9, code 0b010: stream element 9*16 + 5 = 149, bits 447..449 -> bit 448
+    # value dim 9 = tile 0, column 9; token 5 = half 0, element 5: block 9, group
+    # 0*2 + 5//4 = 1, element 1 -> stream element (9*16 + 1)*4 + 1 = 581, bits
+    # 1743..1745; code 0b010 -> bit 1744 = byte 218, bit 0
     r = dict(zero, vcode=zero["vcode"].copy())
     r["vcode"][0, 9] = 2
     pool = layout.new_pool(3, 2, lay)
     layout.put_records(pool, lay, 2, [37], 1, r)
     nz = np.flatnonzero(pool)
-    assert list(nz) == [base + lay.off_vc + 56] and pool[nz[0]] == 1 << 0
+    assert list(nz) == [base + lay.off_vc + 218] and pool[nz[0]] == 1 << 0
     # norms and group metadata are token-major fp16 pairs
     r = dict(zero, n16=np.float16([1.0]), zero16=zero["zero16"].copy())
     r["zero16"][0, 2] = np.float16(-2.0)
@@ -122,3 +124,20 @@ def test_record_placement_by_hand():
     at = base + lay.off_vsz + 5 * 16 + 2 * 4 + 2
     assert pool[at: at + 2].view(np.float16)[0] == -2.0
     assert np.count_nonzero(pool) == 2      # 0x3C00 and 0xC000: one nonzero byte each
+
+
+@pytest.mark.parametrize("vb", [2, 3, 4])
+def test_value_code_map_is_a_bijection(vb):
+    """Every bit of a page's Vc field is taken by exactly one (token, dim, bit) and
+    the 8 codes of (tile i, column c, half h) are one contiguous v_bits*8-bit run."""
+    lay = layout.StoreLayout(128, 2, vb, 32)
+    offs = np.arange(16)
+    bits = layout._field_bits(lay, np.zeros(16, np.int64), offs, "vcode") - lay.off_vc * 8   # [16, 128]
+    allbits = (bits[..., None] + np.arange(vb)).ravel()
+    assert np.array_equal(np.sort(allbits), np.arange(16 * 128 * vb))
+    for h in range(2):
+        for c in (0, 7, 15):
+            for i in (0, 5, 7):
+                run = bits[8 * h: 8 * h + 8, 16 * i + c]
+                start = ((16 * h + c) * 8 + i) * 8 * vb
+                assert list(run) == [start + k * vb for k in range(8)]
