@@ -220,6 +220,14 @@ def test_decode_forced_splits_and_scale(splits):
     _decode_case(torch, 2, 8, 2, [700, 1500], 3, 3, 240 + splits, num_splits=splits, scale=0.05)
 
 
+def test_decode_split_cap():
+    """One requested split over 20000 tokens: the library raises the split count so
+    that no split spans more than 4096 tokens (five splits here)."""
+    torch = _torch()
+    say("decode split cap")
+    _decode_case(torch, 1, 8, 2, [20000], 4, 4, 245, num_splits=1, out_dtypes=("f32",))
+
+
 def test_decode_bypass_layer():
     torch = _torch()
     say("decode bypass")
