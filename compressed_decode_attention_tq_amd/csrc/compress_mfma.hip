@@ -123,6 +123,16 @@ __device__ __forceinline__ float rows_max(float x) {
   return max_raw(c, d);
 }
 
+// float16(x - hi) for the float16 hi = float16(x): one mixed-precision fma that
+// reads hi as float16 (x - hi is exact in float32, so this is the float16
+// rounding of the exact residual).
+__device__ __forceinline__ _Float16 f16_residual(float x, _Float16 hi) {
+  unsigned r;
+  const unsigned hb = __builtin_bit_cast(unsigned short, hi);
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(x), "v"(hb));
+  return __builtin_bit_cast(_Float16, static_cast<unsigned short>(r & 0xffffu));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -223,9 +233,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int q = ((lane & 15) - t) & 15;
     const unsigned short* base = kv ? a.v : a.k;
     const long long stride = kv ? a.v_stride : a.k_stride;
-    long long n = tile * 16 + t;
-    if (n >= a.n_tokens) n = 0;
-    copy_to_lds(base + n * stride + static_cast<long long>(h) * 128 + q * 8, &kv_in[slot][kv][4 * (w & 3)][0]);
+    void* dst = &kv_in[slot][kv][4 * (w & 3)][0];
+    if (tile * 16 + 16 <= a.n_tokens) {
+      // whole tile: the tile's first row (wave-uniform) plus a 32-bit lane offset
+      const unsigned short* row0 = base + tile * 16 * stride + static_cast<long long>(h) * 128;
+      copy_to_lds(row0 + (static_cast<unsigned>(t) * static_cast<unsigned>(stride) + static_cast<unsigned>(q) * 8u), dst);
+    } else {
+      long long n = tile * 16 + t;
+      if (n >= a.n_tokens) n = 0;
+      copy_to_lds(base + n * stride + static_cast<long long>(h) * 128 + q * 8, dst);
+    }
   };
 
   const long long first = blockIdx.x, step = gridDim.x;
@@ -346,7 +363,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         rh[r] = static_cast<_Float16>(rho[r]);
-        rl[r] = static_cast<_Float16>(rho[r] - static_cast<float>(rh[r]));
+        rl[r] = f16_residual(rho[r], rh[r]);
       }
       const int d0 = 16 * w + 4 * kg;
       *reinterpret_cast<half4*>(&orh[col][d0]) = rh;
@@ -540,6 +557,8 @@ bool compress_mfma_applies(const tq_layer* L, const void* k, const void* v, tq_d
   if (n_tokens < 64) return false;  // a handful of appended tokens: the per-token kernel is quicker
   // 16-byte aligned rows for the direct-to-LDS copies
   if ((k_stride % 8) || (v_stride % 8)) return false;
+  // a tile's row offsets (15 strides) are 32-bit
+  if (k_stride > (1LL << 26) || v_stride > (1LL << 26) || k_stride < 0 || v_stride < 0) return false;
   if ((reinterpret_cast<unsigned long>(k) | reinterpret_cast<unsigned long>(v)) & 15) return false;
   return true;
 }
