@@ -42,6 +42,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lbyte;
 
 constexpr int kRow = 136;      // float16 elements per LDS operand row (128 + pad)
@@ -123,14 +124,22 @@ __device__ __forceinline__ float rows_max(float x) {
   return max_raw(c, d);
 }
 
-// float16(x - hi) for the float16 hi = float16(x): one mixed-precision fma that
-// reads hi as float16 (x - hi is exact in float32, so this is the float16
-// rounding of the exact residual).
-__device__ __forceinline__ _Float16 f16_residual(float x, _Float16 hi) {
+// Two floats as float16 (RNE), packed lo | hi << 16.
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
   unsigned r;
-  const unsigned hb = __builtin_bit_cast(unsigned short, hi);
-  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(x), "v"(hb));
-  return __builtin_bit_cast(_Float16, static_cast<unsigned short>(r & 0xffffu));
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// float16(x - hi) for each half, hi = the packed float16 roundings of (a, b):
+// one mixed-precision fma per half reads its hi as float16 and writes the
+// result's half (a - hi is exact in float32, so each is the float16 rounding
+// of the exact residual).
+__device__ __forceinline__ unsigned residual_pair(float a, float b, unsigned hi) {
+  unsigned r;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(r) : "v"(a), "v"(b), "v"(hi));
+  return r;
 }
 
 template <int N>
@@ -359,15 +368,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
       g2 = rows_sum(g2);
       if (kg == 0) gpart[w][col] = g2;
-      half4 rh, rl;
+      // rho as float16 hi (RNE) and lo = float16(rho - hi), two coordinates per word
+      u32x2 rh, rl;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rh[r] = static_cast<_Float16>(rho[r]);
-        rl[r] = f16_residual(rho[r], rh[r]);
+      for (int r = 0; r < 2; ++r) {
+        rh[r] = pack_f16(rho[2 * r], rho[2 * r + 1]);
+        rl[r] = residual_pair(rho[2 * r], rho[2 * r + 1], rh[r]);
       }
       const int d0 = 16 * w + 4 * kg;
-      *reinterpret_cast<half4*>(&orh[col][d0]) = rh;
-      *reinterpret_cast<half4*>(&orl[col][d0]) = rl;
+      *reinterpret_cast<u32x2*>(&orh[col][d0]) = rh;
+      *reinterpret_cast<u32x2*>(&orl[col][d0]) = rl;
       // key codes of dims d0..d0+3 = elements e0..e0+3 of block w/2 (4 KB bits)
       const int b = w >> 1, e0 = 16 * (w & 1) + 4 * kg;
       unsigned char* rec = &img[PG::kc + (b * 16 + col) * 4 * KB];
@@ -429,15 +439,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const __half s16 = __float2half_rn(fmaf(fmaf(-q0s, kTop, span), 1.0f / kTop, q0s));
       const __half z16 = __float2half_rn(mn);
       const float sc = __half2float(s16), zr = __half2float(z16);
-      // quotient by reciprocal and one correction step (faithful to the division)
+      // reciprocal of the scale with one correction step
       const float inv0 = __builtin_amdgcn_rcpf(sc);
       const float inv = fmaf(fmaf(-sc, inv0, 1.0f), inv0, inv0);
       unsigned vc = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float dlt = vp[r] - zr;
-        const float q0 = dlt * inv;
-        const float q = fmaf(fmaf(-q0, sc, dlt), inv, q0);
+        // quotient to a couple of float32 ulps: a code can move only within
+        // ~1e-7 relative of a rounding midpoint
+        const float q = (vp[r] - zr) * inv;
         const float c = (sc > 0.0f) ? __builtin_amdgcn_fmed3f(rintf(q), 0.0f, kTop) : 0.0f;
         vc |= static_cast<unsigned>(c) << (8 * r);
       }
