@@ -401,9 +401,10 @@ __device__ __forceinline__ void fold_scores(const floatx4& acc1, const floatx4& 
 }
 
 
-// Chunks in flight per wave: the pages of the next kRing - 1 chunks are being
-// read while one is processed.
-constexpr int kRing = 3;
+// Chunks held per wave: the pages of the next kRing - 1 chunks are being read
+// while one is processed (two measured faster than three: fewer registers,
+// same streaming rate).
+constexpr int kRing = 2;
 
 // The block table comes as its own read-only, non-aliased parameter.
 template <int NREP, int KB, int VB>
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   };
   // Every step loads one chunk (past the wave's last chunk, the last one again:
   // a few cached re-reads) so that the number of loads in flight is the same on
-  // every path, and each wait leaves the two younger chunks outstanding.
+  // every path, and each wait leaves the younger chunks' loads outstanding.
   const int jmax = nch > 0 ? nch - 1 : 0;
   Chunk<KB, VB> ring[kRing];
 #pragma unroll
