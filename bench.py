@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="size of one plain device copy run before the workloads (counter calibration)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time the tiny, long-context and ragged mixed-bit serving workloads")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) and exit")
     return ap.parse_args()
@@ -243,6 +245,134 @@ def compress_workload(torch, tq, synth, args):
                          "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
 
 
+def _time_steps(torch, fn, n):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _record_bytes(kb, vb, bypass=False):
+    return 512 if bypass else kb * 16 + 20 + vb * 16 + 16
+
+
+def _compact_table(seed, lens):
+    """Block table [B, max_blocks] whose sequences own a seeded random permutation of
+    exactly the blocks they need (unused entries 0)."""
+    import numpy as np
+    nb = (np.asarray(lens, dtype=np.int64) + 15) // 16
+    perm = np.random.default_rng(seed).permutation(int(nb.sum()))
+    table = np.zeros((len(lens), int(nb.max())), dtype=np.int32)
+    o = 0
+    for b, n in enumerate(nb):
+        table[b, :n] = perm[o:o + n]
+        o += n
+    return table, int(nb.sum())
+
+
+def _fill(torch, tq, synth, layer, table, lens, Hkv, seed, outliers, dtype="bf16"):
+    """Compress synthetic K/V of every sequence into a new pool (token-major order)."""
+    import numpy as np
+    nblocks = int(table.max()) + 1
+    pool = layer.new_pool(nblocks)
+    N = int(np.sum(lens))
+    k, v = synth.kv_device(seed, N, Hkv, outliers=outliers, dtype=dtype)
+    b_of = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    slots = table[b_of, pos // 16].astype(np.int64) * 16 + pos % 16
+    tq.compress_kv(layer, k, v, torch.from_numpy(slots).cuda(), pool)
+    torch.cuda.synchronize()
+    del k, v
+    return pool
+
+
+def extra_workloads(torch, tq, synth, args):
+    """The tiny, long-context and serving workloads, each as decode-step figures."""
+    import numpy as np
+    res = {}
+    # tiny: 1 head, 1024 tokens, fp32 -- launch-latency bound
+    W, sd = synth.WORKLOADS[1], synth.seeds(1)
+    layer = tq.Layer(tq.config(W["Hkv"], W["k_bits"], W["v_bits"], seed=sd["state"]))
+    table = synth.block_table(sd["table"], 1, W["ctx"] // 16, "identity")
+    pool = _fill(torch, tq, synth, layer, table, [W["ctx"]], W["Hkv"], sd["data"], 0, dtype="f32")
+    q = torch.from_numpy(synth.queries_host(sd["data"], 1, W["Hq"], dtype="f32")).cuda()
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.full((1,), W["ctx"], dtype=torch.int32, device="cuda")
+    ws = tq.new_workspace(layer, 1, W["Hq"], W["ctx"])
+    out = torch.empty((1, W["Hq"], 128), dtype=torch.float32, device="cuda")
+    step = lambda i: tq.decode_attn(layer, q, pool, bt, sl, W["ctx"], out=out, workspace=ws)
+    _time_steps(torch, step, 20)
+    ms = _time_steps(torch, step, 200)
+    res[W["name"]] = {"decode_us": round(ms * 1e3, 2)}
+    layer.close()
+    # long context: B = 1, ctx 131072, K3/V2, random table; three store copies rotated
+    W, sd = synth.WORKLOADS[4], synth.seeds(4)
+    T, Hkv, Hq = W["ctx"], W["Hkv"], W["Hq"]
+    layer = tq.Layer(tq.config(Hkv, W["k_bits"], W["v_bits"], seed=sd["state"]))
+    table = synth.block_table(sd["table"], 1, T // 16, "random")
+    pool0 = _fill(torch, tq, synth, layer, table, [T], Hkv, sd["data"], W["outliers"])
+    pools = [pool0] + [pool0.clone() for _ in range(2)]
+    q = torch.from_numpy(synth.queries_host(sd["data"], 1, Hq)).to("cuda", torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    ws = tq.new_workspace(layer, 1, Hq, T)
+    out = torch.empty((1, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    step = lambda i: tq.decode_attn(layer, q, pools[i % 3], bt, sl, T, out=out, workspace=ws)
+    _time_steps(torch, step, 10)
+    ms = _time_steps(torch, step, 60)
+    tq.profile_reset()
+    tq.profile_enable(1 << tq.K_SPLITK)
+    _time_steps(torch, step, 60)
+    sk_ms, sk_n = tq.profile_read(tq.K_SPLITK)
+    tq.profile_enable(0)
+    nbytes = T * Hkv * _record_bytes(W["k_bits"], W["v_bits"]) + (T // 16) * 4 + 4 + Hq * 2 * 128 * 4
+    sk_s = sk_ms / max(sk_n, 1) / 1e3
+    res[W["name"]] = {"decode_us": round(ms * 1e3, 2), "decode_tok_s": round(1 / (ms / 1e3), 1),
+                      "kv_tok_s": round(T / (ms / 1e3), 1), "splitk_us": round(sk_s * 1e6, 2),
+                      "splitk_gbs": round(nbytes / sk_s / 1e9, 1),
+                      "splitk_frac": round(nbytes / sk_s / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
+    layer.close()
+    del pools, pool0
+    torch.cuda.empty_cache()
+    # ragged mixed-bit serving: 32 layers, B = 64, seq_lens U{512..32768}
+    W, sd = synth.WORKLOADS[5], synth.seeds(5)
+    B, Hq, Hkv = W["B"], W["Hq"], W["Hkv"]
+    lens = synth.ragged_lengths(sd["lens"], B, W["min_len"], W["max_len"])
+    alloc = synth.mixed_bit_allocation(sd["alloc"], W["layers"])
+    table, _ = _compact_table(sd["table"], lens)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(lens).cuda()
+    maxlen = int(lens.max())
+    q = torch.from_numpy(synth.queries_host(sd["data"], B, Hq)).to("cuda", torch.bfloat16)
+    layers, pools, outs, wss = [], [], [], []
+    nbytes = 0
+    for li, kv in enumerate(alloc):
+        kb, vb = kv if kv else (4, 4)
+        lay = tq.Layer(tq.config(Hkv, kb, vb, seed=sd["state"], layer=li, bypass=kv is None))
+        layers.append(lay)
+        pools.append(_fill(torch, tq, synth, lay, table, lens, Hkv, sd["data"] * 100 + li, W["outliers"]))
+        outs.append(torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda"))
+        wss.append(tq.new_workspace(lay, B, Hq, maxlen))
+        nbytes += int(lens.sum()) * Hkv * _record_bytes(kb, vb, kv is None)
+    def step(i):
+        for li in range(len(layers)):
+            tq.decode_attn(layers[li], q, pools[li], bt, sl, maxlen, out=outs[li], workspace=wss[li])
+    _time_steps(torch, step, 2)
+    ms = _time_steps(torch, step, 5)
+    res[W["name"]] = {"step_ms": round(ms, 3), "decode_tok_s": round(B / (ms / 1e3), 1),
+                      "kv_tok_s": round(float(lens.sum()) * len(layers) / (ms / 1e3), 1),
+                      "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+                      "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "record_bytes_per_step": nbytes, "tokens": int(lens.sum())}
+    for lay in layers:
+        lay.close()
+    return res
+
+
 def cpu_baseline(torch, synth, ctx, budget_s):
     """The float64 oracle on the headline workload, one sequence at a time, until
     the time budget is spent.  Setup (compressing each sampled sequence's context)
@@ -306,6 +436,10 @@ def main():
     if not args.no_compress:
         log("compress workload")
         comp = compress_workload(torch, tq, synth, args)
+    extra = None
+    if args.all_configs:
+        log("tiny, long-context and serving workloads")
+        extra = extra_workloads(torch, tq, synth, args)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -332,6 +466,8 @@ def main():
         "append_us": dec["append_us"],
         "compress": comp,
     }
+    if extra is not None:
+        line["other_workloads"] = extra
     print(json.dumps(line), flush=True)
 
 

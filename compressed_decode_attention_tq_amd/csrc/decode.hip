@@ -278,6 +278,41 @@ __global__ __launch_bounds__(256) void splitk_bypass_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- combine
+// o'[d] of one query head from its ns split partials p[s] = (acc[128], m, l):
+// sum_s e^{m_s - M} acc_s[d] / sum_s e^{m_s - M} l_s.  Splits are taken 8 at a
+// time with all of a group's reads issued before any is used (one memory round
+// trip per group), merged with a running max.
+__device__ __forceinline__ float merge_partials(const float* p, int ns, int d) {
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float m8[8], l8[8], a8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* q = p + (s0 + u < ns ? s0 + u : s0) * kPart;
+      m8[u] = q[128];
+      l8[u] = q[129];
+      a8[u] = q[d];
+    }
+    float mg = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < ns) mg = fmaxf(mg, m8[u]);
+    const float f = (M == -INFINITY) ? 0.0f : __expf(M - mg);
+    num *= f;
+    den *= f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < ns) {
+        const float e = __expf(m8[u] - mg);
+        num = fmaf(e, a8[u], num);
+        den = fmaf(e, l8[u], den);
+      }
+    M = mg;
+  }
+  return num / den;
+}
+
+
 // One workgroup of 512 lanes per (KV head g, sequence b): merge each query
 // head's split partials with the running-max rescaling, then o = R_g^T o'
 // (compressed layers; lane (c, i) holds column i of rows 32c..32c+31 of R_g
@@ -310,19 +345,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* part, const i
   };
   for (int o = tid; o < n; o += 512) {
     const int h = o >> 7, d = o & 127;
-    float v = 0.0f;
-    if (ns > 0) {
-      const float* p = part + static_cast<size_t>(bh0 + h) * n_splits * kPart;
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * kPart + 128]);
-      float num = 0.0f, den = 0.0f;
-      for (int s = 0; s < ns; ++s) {
-        const float e = __expf(p[s * kPart + 128] - M);
-        num += e * p[s * kPart + d];
-        den += e * p[s * kPart + 129];
-      }
-      v = num / den;
-    }
+    const float v = ns > 0 ? merge_partials(part + static_cast<size_t>(bh0 + h) * n_splits * kPart, ns, d) : 0.0f;
     if constexpr (BYPASS) store(h, d, v);
     else so[h][d] = v;
   }
