@@ -22,7 +22,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I
 # directly), so loop-carried accumulators are not copied to and from AGPRs.
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast",
           "-mllvm", "-amdgpu-mfma-vgpr-form"]
-SOURCES = ["api.cpp", "host_state.cpp", "host_codebook.cpp", "profile.cpp", "compress.hip", "compress_mfma.hip", "decode.hip", "decode_mainloop.hip"]
+SOURCES = ["api.cpp", "host_state.cpp", "host_codebook.cpp", "profile.cpp", "compress.hip", "compress_mfma.hip", "decode.hip", "decode_mainloop.hip",
+           "decode_bypass.hip"]
 
 
 def _compile(src):

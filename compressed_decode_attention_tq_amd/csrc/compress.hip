@@ -219,7 +219,9 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
   }
 }
 
-// Uncompressed (bf16) layers: copy one (token, head) of K and V into the page.
+// Uncompressed (bf16) layers: copy one (token, head) of K and V into the page,
+// keys as the token's row of K [16][128], values as the token's column of the
+// dim-major V^T [128][16].
 __global__ __launch_bounds__(64) void store_bypass_kernel(const unsigned short* k, const unsigned short* v,
                                                           long long k_stride, long long v_stride,
                                                           const long long* slots, unsigned char* pool,
@@ -234,7 +236,10 @@ __global__ __launch_bounds__(64) void store_bypass_kernel(const unsigned short* 
   const unsigned* ks = reinterpret_cast<const unsigned*>(k + tok * k_stride + h * 128);
   const unsigned* vs = reinterpret_cast<const unsigned*>(v + tok * v_stride + h * 128);
   reinterpret_cast<unsigned*>(base + off * 256)[i] = ks[i];
-  reinterpret_cast<unsigned*>(base + 4096 + off * 256)[i] = vs[i];
+  const unsigned w = vs[i];
+  unsigned short* vt = reinterpret_cast<unsigned short*>(base + 4096) + off;
+  vt[(2 * i) * 16] = static_cast<unsigned short>(w & 0xffffu);
+  vt[(2 * i + 1) * 16] = static_cast<unsigned short>(w >> 16);
 }
 
 template <bool BF16, int KB>

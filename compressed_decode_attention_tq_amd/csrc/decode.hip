@@ -11,11 +11,11 @@
 //   s_i = scale * (n_i / sqrt d) * (q'.c[idx_i] + sqrt(pi/2)/m * gamma_i * u.(2 z_i - 1)),
 //   q' = R_g q, u = S_g q'  (QJL residual estimator).
 //
-// Launch 1 (prologue): q', u per (sequence, query head) into the workspace.
+// Launch 1 (prologue, compressed layers): q', u per (sequence, query head)
+//   into the workspace.
 // Launch 2 (split-K):  one workgroup per (split, KV head, sequence) serves all
-//   query heads of its KV head so the compressed KV is read once (the
-//   compressed mainloop is in decode_mainloop.hip; uncompressed layers use the
-//   bypass loop below).
+//   query heads of its KV head so the KV is read once (the compressed mainloop
+//   is in decode_mainloop.hip, the uncompressed one in decode_bypass.hip).
 // Launch 3 (combine): merge the split partials with the running-max rescaling,
 //   un-rotate o = R_g^T o', cast and store.
 #include <hip/hip_fp16.h>
@@ -29,32 +29,6 @@ namespace tq {
 namespace {
 
 constexpr int kPart = kDim + 4;  // acc[128], m, l, pad, pad
-
-struct DecodeArgs {
-  const unsigned char* pool;
-  const int* block_table;
-  const int* seq_lens;
-  const float* qu;  // [B*Hq][2][128]
-  float* part;      // [B*Hq][n_splits][kPart]
-  long long max_blocks;
-  int Hq, Hkv, n_splits, split_tokens;
-  float scale;
-  unsigned block_bytes;
-};
-
-__device__ __forceinline__ float half_lo(unsigned w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xffffu))); }
-__device__ __forceinline__ float half_hi(unsigned w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16))); }
-__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float wave_max(float x) {
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
 
 // ---------------------------------------------------------------- prologue
 // q' = R_g q and u = S_g q' in float32 (qu), and for compressed layers the
@@ -70,7 +44,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // query heads.  Lane (c, i) = (lane / 128, lane % 128) holds column i of rows
 // 32c..32c+31 of R_g^T and S_g^T, loaded once, and forms that quarter of every
 // head's dot products; the quarters are summed through LDS in a fixed order.
-template <bool QBF16, bool BYPASS>
+template <bool QBF16>
 __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const float* RT, const float* ST,
                                                        float* qu, unsigned short* qa, int Hq, int rep,
                                                        float kappa) {
@@ -84,14 +58,7 @@ __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const floa
     if constexpr (QBF16) return __uint_as_float(static_cast<unsigned>(static_cast<const unsigned short*>(q)[at]) << 16);
     else return static_cast<const float*>(q)[at];
   };
-  if constexpr (BYPASS) {
-    for (int o = tid; o < n; o += 512) {
-      const int h = o >> 7, d = o & 127;
-      qu[static_cast<size_t>(bh0 + h) * 256 + d] = load_q(h, d);
-      qu[static_cast<size_t>(bh0 + h) * 256 + 128 + d] = 0.0f;
-    }
-    return;
-  } else {
+  {
     __shared__ float sq[8][128], sa[8][128], part[4][8][128];
     float rt[32], st[32];
     {
@@ -154,125 +121,6 @@ __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const floa
         if (h == 0)
           for (int row = 4 * rep; row < 16; ++row) put(0, row, static_cast<_Float16>(0.0f));
       }
-    }
-  }
-}
-
-// ------------------------------------------------------ split-K (bypass)
-// Uncompressed bf16 pages ("tiny-turboquant 0.18.0", "Knobs that actually move
-// the needle": protected boundary layers stay at full precision).  Same split-K
-// structure as the compressed mainloop: four waves take 64-token chunks in
-// turn; a lane scores one token, then the chunk's values are accumulated with
-// lanes owning two coordinates each.
-template <int NREP>
-__global__ __launch_bounds__(256) void splitk_bypass_kernel(DecodeArgs a) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int T = a.seq_lens[b];
-  const int start = split * a.split_tokens;
-  if (start >= T) return;
-  const int end = min(T, start + a.split_tokens);
-
-  __shared__ float qs[NREP][128];
-  __shared__ float wm[4][NREP], wl[4][NREP];
-  __shared__ float wacc[4][NREP][128];
-
-  const int h0 = g * NREP;
-  for (int x = threadIdx.x; x < NREP * 128; x += 256) {
-    const int r = x >> 7, d = x & 127;
-    qs[r][d] = a.qu[static_cast<size_t>(b * a.Hq + h0 + r) * 256 + d];
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float m[NREP], l[NREP], acc[NREP][2];
-#pragma unroll
-  for (int r = 0; r < NREP; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.0f;
-    acc[r][0] = acc[r][1] = 0.0f;
-  }
-
-  for (int c0 = start + wave * 64; c0 < end; c0 += 256) {
-    const int tok = c0 + lane;
-    const bool valid = tok < end;
-    long long rbase = 0;
-    int off = 0;
-    float s[NREP];
-    if (valid) {
-      const int blk = a.block_table[b * a.max_blocks + (tok >> 4)];
-      off = tok & 15;
-      rbase = (static_cast<long long>(blk) * a.Hkv + g) * a.block_bytes;
-      const unsigned* kw = reinterpret_cast<const unsigned*>(a.pool + rbase + off * 256);
-      float A[NREP];
-#pragma unroll
-      for (int r = 0; r < NREP; ++r) A[r] = 0.0f;
-#pragma unroll 8
-      for (int d2 = 0; d2 < 64; ++d2) {
-        const unsigned w = kw[d2];
-        const float k0 = bf16_lo(w), k1 = bf16_hi(w);
-#pragma unroll
-        for (int r = 0; r < NREP; ++r) A[r] = fmaf(qs[r][2 * d2 + 1], k1, fmaf(qs[r][2 * d2], k0, A[r]));
-      }
-#pragma unroll
-      for (int r = 0; r < NREP; ++r) s[r] = a.scale * A[r];
-    } else {
-#pragma unroll
-      for (int r = 0; r < NREP; ++r) s[r] = -INFINITY;
-    }
-#pragma unroll
-    for (int r = 0; r < NREP; ++r) {
-      const float mnew = fmaxf(m[r], wave_max(s[r]));
-      const float alpha = (m[r] == -INFINITY) ? 0.0f : __expf(m[r] - mnew);
-      const float p = valid ? __expf(s[r] - mnew) : 0.0f;
-      l[r] = l[r] * alpha + wave_sum(p);
-      acc[r][0] *= alpha;
-      acc[r][1] *= alpha;
-      m[r] = mnew;
-      s[r] = p;
-    }
-    const int ntok = min(64, end - c0);
-    for (int j = 0; j < ntok; ++j) {
-      const long long rb = __shfl(rbase, j, 64);
-      const int oj = __shfl(off, j, 64);
-      const unsigned w = reinterpret_cast<const unsigned*>(a.pool + rb + 4096 + oj * 256)[lane];
-      const float v0 = bf16_lo(w), v1 = bf16_hi(w);
-#pragma unroll
-      for (int r = 0; r < NREP; ++r) {
-        const float p = __shfl(s[r], j, 64);
-        acc[r][0] = fmaf(p, v0, acc[r][0]);
-        acc[r][1] = fmaf(p, v1, acc[r][1]);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int r = 0; r < NREP; ++r) {
-    if (lane == 0) {
-      wm[wave][r] = m[r];
-      wl[wave][r] = l[r];
-    }
-    wacc[wave][r][2 * lane] = acc[r][0];
-    wacc[wave][r][2 * lane + 1] = acc[r][1];
-  }
-  __syncthreads();
-  for (int x = threadIdx.x; x < NREP * 128; x += 256) {
-    const int r = x >> 7, d = x & 127;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][r]);
-    float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (wm[w][r] == -INFINITY) continue;
-      const float e = __expf(wm[w][r] - M);
-      num += e * wacc[w][r][d];
-      den += e * wl[w][r];
-    }
-    float* dst = a.part + (static_cast<size_t>(b * a.Hq + h0 + r) * a.n_splits + split) * kPart;
-    dst[d] = num;
-    if (d == 0) {
-      dst[128] = M;
-      dst[129] = den;
     }
   }
 }
@@ -365,16 +213,6 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* part, const i
   }
 }
 
-void* pick_bypass(int rep) {
-  switch (rep) {
-    case 1: return reinterpret_cast<void*>(&splitk_bypass_kernel<1>);
-    case 2: return reinterpret_cast<void*>(&splitk_bypass_kernel<2>);
-    case 4: return reinterpret_cast<void*>(&splitk_bypass_kernel<4>);
-    case 8: return reinterpret_cast<void*>(&splitk_bypass_kernel<8>);
-  }
-  return nullptr;
-}
-
 }  // namespace
 
 tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
@@ -387,13 +225,10 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   float* qu = reinterpret_cast<float*>(ws + plan.ws_qu);
   float* part = reinterpret_cast<float*>(ws + plan.ws_part);
 
-  // 1. prologue
-  {
-    void* fn;
-    if (bypass) fn = (q_dtype == TQ_BF16) ? reinterpret_cast<void*>(&prologue_kernel<true, true>)
-                                          : reinterpret_cast<void*>(&prologue_kernel<false, true>);
-    else fn = (q_dtype == TQ_BF16) ? reinterpret_cast<void*>(&prologue_kernel<true, false>)
-                                   : reinterpret_cast<void*>(&prologue_kernel<false, false>);
+  // 1. prologue (compressed layers; the bypass kernel reads q itself)
+  if (!bypass) {
+    void* fn = (q_dtype == TQ_BF16) ? reinterpret_cast<void*>(&prologue_kernel<true>)
+                                    : reinterpret_cast<void*>(&prologue_kernel<false>);
     const float* RT = L->dRT;
     const float* ST = L->dST;
     unsigned short* qa = reinterpret_cast<unsigned short*>(ws + plan.ws_qa);
@@ -405,32 +240,13 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));
   }
   // 2. split-K mainloop
-  if (!bypass) {
+  {
     ProfScope prof(kKSplitK, stream);
-    tq_status st = launch_splitk_tq(L, plan, pool, block_table, max_blocks_per_seq, seq_lens, softmax_scale,
-                                    ws + plan.ws_qa, part, stream);
+    tq_status st = bypass ? launch_splitk_bypass(L, plan, q, q_dtype, pool, block_table, max_blocks_per_seq,
+                                                 seq_lens, softmax_scale, part, stream)
+                          : launch_splitk_tq(L, plan, pool, block_table, max_blocks_per_seq, seq_lens,
+                                             softmax_scale, ws + plan.ws_qa, part, stream);
     if (st != TQ_OK) return st;
-  } else {
-    DecodeArgs a;
-    a.pool = static_cast<const unsigned char*>(pool);
-    a.block_table = block_table;
-    a.seq_lens = seq_lens;
-    a.qu = qu;
-    a.part = part;
-    a.max_blocks = max_blocks_per_seq;
-    a.Hq = plan.n_q_heads;
-    a.Hkv = L->cfg.n_kv_heads;
-    a.n_splits = plan.n_splits;
-    a.split_tokens = plan.split_tokens;
-    a.scale = softmax_scale;
-    a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
-    void* fn = pick_bypass(plan.rep);
-    if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for this variant");
-    void* args[] = {&a};
-    const dim3 grid(plan.n_splits, L->cfg.n_kv_heads, plan.batch);
-    ProfScope prof(kKSplitK, stream);
-    hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
-    if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode split-K launch: %s", hipGetErrorString(e));
   }
   // 3. combine + un-rotation
   {

@@ -591,17 +591,25 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     }
 
     // ---- P.V weights w = p * scale in two float16 pieces -> LDS (slots
-    //      pv_slot(page, col)); offset term p (zero + mid scale) on the VALU
+    //      pv_slot(page, col)); offset term p (zero + mid scale) on the VALU.
+    //      Past the context end (slots never written may hold any bits) the
+    //      scale and zero are taken as 0, so that p = 0 gives exact zeros.
+    u32x4 sz[2] = {c.sz[0], c.sz[1]};
+    if (c0 + 32 > end) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        if (c0 + 16 * t + col >= end) sz[t] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (active) {
 #pragma unroll
       for (int hs = 0; hs < HPL; ++hs) {
         const int h = SM::head(kg, hs);
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
-          const _Float16 s0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[0][G] & 0xffffu));
-          const _Float16 s1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[1][G] & 0xffffu));
-          const _Float16 z0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[0][G] >> 16));
-          const _Float16 z1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(c.sz[1][G] >> 16));
+          const _Float16 s0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(sz[0][G] & 0xffffu));
+          const _Float16 s1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(sz[1][G] & 0xffffu));
+          const _Float16 z0 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(sz[0][G] >> 16));
+          const _Float16 z1 = __builtin_bit_cast(_Float16, static_cast<unsigned short>(sz[1][G] >> 16));
           const float w0 = p[0][hs] * static_cast<float>(s0);
           const float w1 = p[1][hs] * static_cast<float>(s1);
           const _Float16 hi0 = static_cast<_Float16>(w0), hi1 = static_cast<_Float16>(w1);

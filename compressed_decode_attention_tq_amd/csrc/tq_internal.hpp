@@ -109,6 +109,10 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
 tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void* pool, const int* block_table,
                            int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const void* qa,
                            float* part, void* stream);
+// Uncompressed (bypass) layers: reads q directly (no prologue launch).
+tq_status launch_splitk_bypass(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
+                               const void* pool, const int* block_table, int max_blocks_per_seq,
+                               const int* seq_lens, float softmax_scale, float* part, void* stream);
 tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
                         const void* pool, const int* block_table, int max_blocks_per_seq,
                         const int* seq_lens, float softmax_scale, void* out, tq_dtype out_dtype,

@@ -63,7 +63,8 @@
  *   8 tokens of one coordinate (one matrix-core operand row) are one run of
  *   8*v_bits bits, the 8 runs of a lane block adjacent.  A single token
  *   appended to a page therefore shares Vc bytes with its neighbours.
- *   Bypass (uncompressed) layers: region = K [16][128] bf16, then V [16][128] bf16.
+ *   Bypass (uncompressed) layers: region = K [16][128] bf16 (token-major), then
+ *   V^T [128][16] bf16 (dim-major: the 16 tokens' values of one dim together).
  */
 #ifndef TQ_H
 #define TQ_H

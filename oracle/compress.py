@@ -75,12 +75,6 @@ def compress_values(V, R, v_bits, group):
     return {"vrot": vrot, "codes": codes, "scale16": scale16, "zero16": zero16}
 
 
-def _scatter(pool, starts, data):
-    data = np.asarray(data, dtype=np.uint8)
-    idx = np.asarray(starts, dtype=np.int64)[:, None] + np.arange(data.shape[-1])
-    pool[idx] = data
-
-
 def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     """Compress K, V [N, H_kv, d] (float64 values of the inputs) into `pool` at `slots` [N].
 
@@ -114,5 +108,6 @@ def store_bypass(K_bits16, V_bits16, slots, pool, layout, n_kv_heads):
     blocks, offs = np.divmod(slots[keep], lay.P)
     for h in range(n_kv_heads):
         base = (blocks * n_kv_heads + h) * layout.block_bytes
-        _scatter(pool, base + layout.off_kb + offs * layout.kb_bytes, Kb[:, h].view(np.uint8).reshape(len(offs), -1))
-        _scatter(pool, base + layout.off_vb + offs * layout.kb_bytes, Vb[:, h].view(np.uint8).reshape(len(offs), -1))
+        k_at, v_at = lay.bypass_byte_index(layout, base, offs)
+        pool[k_at] = np.ascontiguousarray(Kb[:, h]).view(np.uint8).reshape(len(offs), -1)
+        pool[v_at] = np.ascontiguousarray(Vb[:, h]).view(np.uint8).reshape(len(offs), -1)

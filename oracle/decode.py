@@ -41,8 +41,9 @@ def gather(pool, layout, n_kv_heads, block_table_row, seq_len, head):
         return pool[idx]
 
     if layout.bypass:
-        kb = field(layout.off_kb, layout.kb_bytes).view(np.uint16)
-        vb = field(layout.off_vb, layout.kb_bytes).view(np.uint16)
+        k_at, v_at = lay.bypass_byte_index(layout, base, offs)
+        kb = np.ascontiguousarray(pool[k_at]).view(np.uint16)
+        vb = np.ascontiguousarray(pool[v_at]).view(np.uint16)
         return {"k": lay.bf16_bits_to_f64(kb), "v": lay.bf16_bits_to_f64(vb)}
     slots = blocks * lay.P + offs
     r = lay.get_records(pool, layout, n_kv_heads, slots, head)

@@ -23,7 +23,10 @@ stream, bit k of the stream being bit k%8 of byte k//8.
                            2i + k//4 of four codes, element k % 4; one b-bit
                            stream in the order (block, group, element)
   Vsz [P][d/G][2] fp16     per group: scale then zero
-Bypass (uncompressed) layers: region = Kb [P][d] bf16 followed by Vb [P][d] bf16.
+Bypass (uncompressed) layers: region = Kb [P][d] bf16 (token-major: one token's
+d keys together) followed by Vb [d][P] bf16 (dim-major: the P tokens' values of
+one dim together), so that a page's values load as the matrix-core operand of
+P.V with one contiguous run per lane.
 """
 
 import numpy as np
@@ -76,10 +79,6 @@ def new_pool(num_blocks, n_kv_heads, layout):
 def _put(pool, at, data):
     data = np.asarray(data, dtype=np.uint8).ravel()
     pool[at: at + data.size] = data
-
-
-def _get(pool, at, n):
-    return pool[at: at + n]
 
 
 def f16_bytes(values):
@@ -167,11 +166,25 @@ def get_records(pool, layout, n_kv_heads, slots, head):
     }
 
 
+def bypass_byte_index(layout, base, offs):
+    """Byte positions of the keys and of the values of tokens at in-page offsets
+    `offs` [N] in the pages starting at `base` [N]: two [N, 2d] index arrays, bf16
+    element e of a token at columns 2e (low byte) and 2e + 1."""
+    base = np.asarray(base, dtype=np.int64)[:, None]
+    offs = np.asarray(offs, dtype=np.int64)[:, None]
+    byte = np.arange(2 * layout.d)
+    k_at = base + layout.off_kb + offs * layout.kb_bytes + byte
+    # value element e of token t: row e of the dim-major table, column t
+    v_at = base + layout.off_vb + (byte // 2) * (2 * P) + 2 * offs + byte % 2
+    return k_at, v_at
+
+
 def write_bypass(pool, layout, n_kv_heads, slot, head, k_bf16_bits, v_bf16_bits):
     """Store raw bf16 K and V (given as uint16 bit patterns) of one (token, head)."""
     base, o = layout.region(n_kv_heads, slot, head)
-    _put(pool, base + layout.off_kb + o * layout.kb_bytes, np.asarray(k_bf16_bits, np.uint16).view(np.uint8))
-    _put(pool, base + layout.off_vb + o * layout.kb_bytes, np.asarray(v_bf16_bits, np.uint16).view(np.uint8))
+    k_at, v_at = bypass_byte_index(layout, [base], [o])
+    pool[k_at[0]] = np.asarray(k_bf16_bits, np.uint16).view(np.uint8)
+    pool[v_at[0]] = np.asarray(v_bf16_bits, np.uint16).view(np.uint8)
 
 
 def bf16_bits_to_f64(bits16):
@@ -181,6 +194,7 @@ def bf16_bits_to_f64(bits16):
 
 def read_bypass(pool, layout, n_kv_heads, slot, head):
     base, o = layout.region(n_kv_heads, slot, head)
-    k = _get(pool, base + layout.off_kb + o * layout.kb_bytes, layout.kb_bytes).view(np.uint16)
-    v = _get(pool, base + layout.off_vb + o * layout.kb_bytes, layout.kb_bytes).view(np.uint16)
+    k_at, v_at = bypass_byte_index(layout, [base], [o])
+    k = np.ascontiguousarray(pool[k_at[0]]).view(np.uint16)
+    v = np.ascontiguousarray(pool[v_at[0]]).view(np.uint16)
     return bf16_bits_to_f64(k), bf16_bits_to_f64(v)

@@ -106,10 +106,12 @@ def rel_l2(got, ref):
 
 
 def oracle_store(K, V, slots, num_blocks, n_heads, k_bits, v_bits, seed, layer=0, bypass=False,
-                 K_bits16=None, V_bits16=None, keep=True):
-    """Oracle state + pool for the given inputs (float arrays [N, H, d])."""
+                 K_bits16=None, V_bits16=None, keep=True, fill=0):
+    """Oracle state + pool for the given inputs (float arrays [N, H, d]); every
+    pool byte starts as `fill` (0xFF: all-ones fields, NaN norms and values)."""
     layout = lay.StoreLayout(128, k_bits, v_bits, 32, bypass=bypass)
     pool = lay.new_pool(num_blocks, n_heads, layout)
+    pool[:] = fill
     if bypass:
         compress.store_bypass(K_bits16, V_bits16, slots, pool, layout, n_heads)
         return None, layout, pool, None

@@ -122,6 +122,30 @@ def test_compress_full_size_sampled():
     layer.close()
 
 
+def test_compress_bypass_bit_exact():
+    """Bypass layers store the bf16 key rows and the dim-major value table: the
+    GPU pool equals the oracle's byte for byte (shuffled slots, skipped tokens,
+    untouched slots left as they were)."""
+    torch = _torch()
+    say("compress bypass")
+    n, H, nb = 300, 4, 30
+    K, V = synth.kv_host(280, n, H, outliers=4)
+    rng = np.random.default_rng(280)
+    slots = rng.permutation(nb * 16)[:n].astype(np.int64)
+    slots[rng.choice(n, 10, replace=False)] = -1
+    layer = tq.Layer(tq.config(H, seed=280, bypass=True))
+    pool = layer.new_pool(nb)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    torch.cuda.synchronize()
+    got = pool.cpu().numpy()
+    layer.close()
+    _, _, ref, _ = parity.oracle_store(None, None, slots, nb, H, 4, 4, 280, bypass=True,
+                                       K_bits16=synth.bf16_bits(K), V_bits16=synth.bf16_bits(V))
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref), int(np.count_nonzero(got != ref))
+
+
 # -------------------------------------------------------------------- decode
 def _gpu_decode(torch, layer_cfg, pool_np, q, table, lens, max_len, out_dtype="f32", num_splits=0,
                 scale=0.0, q_dtype="bf16"):
@@ -141,7 +165,8 @@ def _gpu_decode(torch, layer_cfg, pool_np, q, table, lens, max_len, out_dtype="f
 
 
 def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_dtype="bf16",
-                 outliers=4, out_dtypes=("f32", "bf16"), num_splits=0, scale=0.0, layer=0, bypass=False):
+                 outliers=4, out_dtypes=("f32", "bf16"), num_splits=0, scale=0.0, layer=0, bypass=False,
+                 fill=0):
     lens = np.asarray(lens, dtype=np.int32)
     maxb = max(1, (int(lens.max()) + 15) // 16)
     table = synth.block_table(seed, B, maxb, table_kind)
@@ -159,9 +184,11 @@ def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_d
     slots = np.concatenate(slots)
     if bypass:
         st, layout, pool, _ = parity.oracle_store(None, None, slots, nblk, Hkv, 4, 4, seed, bypass=True,
-                                                  K_bits16=synth.bf16_bits(K), V_bits16=synth.bf16_bits(V))
+                                                  K_bits16=synth.bf16_bits(K), V_bits16=synth.bf16_bits(V),
+                                                  fill=fill)
     else:
-        st, layout, pool, _ = parity.oracle_store(K, V, slots, nblk, Hkv, kb, vb, seed, layer=layer, keep=False)
+        st, layout, pool, _ = parity.oracle_store(K, V, slots, nblk, Hkv, kb, vb, seed, layer=layer, keep=False,
+                                                  fill=fill)
     q = synth.queries_host(seed, B, Hq, dtype=q_dtype)
     ref = parity.oracle_decode(q.astype(np.float64), pool, layout, Hkv, table, lens, st,
                                scale=scale if scale else None)
@@ -232,6 +259,26 @@ def test_decode_bypass_layer():
     torch = _torch()
     say("decode bypass")
     _decode_case(torch, 3, 8, 2, [16, 200, 1031], 0, 0, 250, bypass=True)
+
+
+@pytest.mark.parametrize("rep,q_dtype,splits", [(1, "bf16", 0), (2, "f32", 3), (8, "bf16", 0), (4, "f32", 64)])
+def test_decode_bypass_variants(rep, q_dtype, splits):
+    """Bypass layers: every GQA ratio, float32 and bf16 queries, forced splits,
+    ragged lengths with a zero-length row and page tails."""
+    torch = _torch()
+    say("decode bypass", rep, q_dtype, splits)
+    _decode_case(torch, 4, 2 * rep, 2, [0, 15, 333, 2100], 0, 0, 260 + rep, q_dtype=q_dtype, num_splits=splits,
+                 bypass=True)
+
+
+@pytest.mark.parametrize("bypass", [False, True])
+def test_decode_ignores_unwritten_slots(bypass):
+    """Pool bytes all 0xFF before the records are written: the slots past each
+    context end hold NaN norms, scales, zeros and values, which must not reach
+    the output (page and chunk tails of every length class)."""
+    torch = _torch()
+    say("decode unwritten slots, bypass", bypass)
+    _decode_case(torch, 5, 8, 2, [1, 17, 40, 129, 1000], 3, 2, 270, bypass=bypass, fill=0xFF)
 
 
 def test_decode_ragged_serving_sampled():

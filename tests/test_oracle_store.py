@@ -141,3 +141,29 @@ def test_value_code_map_is_a_bijection(vb):
                 run = bits[8 * h: 8 * h + 8, 16 * i + c]
                 start = ((16 * h + c) * 8 + i) * 8 * vb
                 assert list(run) == [start + k * vb for k in range(8)]
+
+
+def test_bypass_placement_by_hand():
+    """Bypass pages: keys token-major, values dim-major.  Token 5 of block 2, head 1
+    of 3: page base (2*3 + 1) * 8192; key e at base + 5*256 + 2e, value e at
+    base + 4096 + 32e + 2*5 (little-endian bf16 patterns)."""
+    lay = layout.StoreLayout(bypass=True)
+    assert lay.block_bytes == 8192
+    pool = layout.new_pool(4, 3, lay)
+    kbits = np.arange(128, dtype=np.uint16) + 0x3f00
+    vbits = np.arange(128, dtype=np.uint16) + 0x4100
+    layout.write_bypass(pool, lay, 3, 2 * 16 + 5, 1, kbits, vbits)
+    base = 7 * 8192
+    for e in (0, 1, 77, 127):
+        ka, va = base + 5 * 256 + 2 * e, base + 4096 + 32 * e + 10
+        assert pool[ka] == (0x3f00 + e) & 0xff and pool[ka + 1] == 0x3f
+        assert pool[va] == (0x4100 + e) & 0xff and pool[va + 1] == 0x41
+    assert np.count_nonzero(pool) == np.count_nonzero(kbits.view(np.uint8)) + np.count_nonzero(vbits.view(np.uint8))
+    k, v = layout.read_bypass(pool, lay, 3, 2 * 16 + 5, 1)
+    assert np.array_equal(k, layout.bf16_bits_to_f64(kbits))
+    assert np.array_equal(v, layout.bf16_bits_to_f64(vbits))
+    # a neighbouring token's values interleave with these, one bf16 apart
+    layout.write_bypass(pool, lay, 3, 2 * 16 + 6, 1, kbits, vbits + 1)
+    assert pool[base + 4096 + 32 * 3 + 12] == (0x4100 + 3 + 1) & 0xff
+    k2, v2 = layout.read_bypass(pool, lay, 3, 2 * 16 + 5, 1)
+    assert np.array_equal(v2, v)
