@@ -226,7 +226,7 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   float* part = reinterpret_cast<float*>(ws + plan.ws_part);
 
   // 1. prologue (compressed layers; the bypass kernel reads q itself)
-  if (!bypass) {
+  if (!bypass && max_blocks_per_seq > 0) {
     void* fn = (q_dtype == TQ_BF16) ? reinterpret_cast<void*>(&prologue_kernel<true>)
                                     : reinterpret_cast<void*>(&prologue_kernel<false>);
     const float* RT = L->dRT;
@@ -239,8 +239,9 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, plan.batch), dim3(512), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));
   }
-  // 2. split-K mainloop
-  {
+  // 2. split-K mainloop (a table with no blocks per row means every sequence is
+  //    empty: the combine alone writes the zero output)
+  if (max_blocks_per_seq > 0) {
     ProfScope prof(kKSplitK, stream);
     tq_status st = bypass ? launch_splitk_bypass(L, plan, q, q_dtype, pool, block_table, max_blocks_per_seq,
                                                  seq_lens, softmax_scale, part, stream)

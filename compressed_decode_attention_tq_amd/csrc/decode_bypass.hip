@@ -108,10 +108,7 @@ struct Page {
 template <int NREP, bool QBF16>
 __global__ __launch_bounds__(256) void splitk_bypass_kernel(BypassArgs a, const int* __restrict__ btab) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int T = a.seq_lens[b];
   const int start = split * a.split_tokens;
-  if (start >= T) return;
-  const int end = min(T, start + a.split_tokens);
 
   __shared__ __attribute__((aligned(16))) float mbuf[4][NREP][kDim];
   __shared__ float mg_m[4][NREP], mg_l[4][NREP];
@@ -125,33 +122,56 @@ __global__ __launch_bounds__(256) void splitk_bypass_kernel(BypassArgs a, const 
   const bool live = head < NREP;
 
   // Block ids of this wave's pages, one per lane (at most 64: a split spans at
-  // most 4096 tokens = 256 pages over four waves).
-  const int npg = (end - start + kPage - 1) / kPage;
-  const int nj = npg > wave ? (npg - wave + 3) >> 2 : 0;
-  int ids = 0;
-  if (lane < nj) ids = btab[static_cast<long long>(b) * a.max_blocks + start / kPage + wave + 4 * lane];
-
-  // Query operand: K-step s holds dims 32s + 8kg .. +7 of column col.
-  bf16x8 qb[4];
+  // most 4096 tokens = 256 pages over four waves), read before the sequence
+  // length is known so that the two reads overlap; table entries past the
+  // context (the index clamped to the row) are read but never used.
+  // (The host launches no split kernel for a table of zero blocks per row.)
+  int ids;
   {
-    const size_t qrow = (static_cast<size_t>(b) * a.Hq + g * NREP + (live ? head : 0)) * kDim;
+    const long long pg = start / kPage + wave + 4 * lane;
+    ids = btab[static_cast<long long>(b) * a.max_blocks + (pg < a.max_blocks ? pg : a.max_blocks - 1)];
+  }
+
+  // Query operand: K-step s holds dims 32s + 8kg .. +7 of column col (all
+  // four K-steps' reads issued, then the sequence length tested, before any is
+  // used).
+  bf16x8 qb[4];
+  int T;
+  {
+    const size_t qrow = (static_cast<size_t>(b) * a.Hq + g * NREP + (live ? head : 0)) * kDim + 8 * kg;
+    constexpr int NW = QBF16 ? 1 : 2;  // 16-byte reads per K-step
+    u32x4 raw[4][NW];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+        if constexpr (QBF16)
+          raw[s][u] = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(a.q) + qrow + 32 * s);
+        else
+          raw[s][u] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + qrow + 32 * s + 4 * u);
+      }
+    T = a.seq_lens[b];
+    if (start >= T) {
+      // the reads above stay ahead of this test (their results are not needed here)
+      asm volatile("" ::"v"(ids));
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < NW; ++u) asm volatile("" ::"v"(raw[s][u]));
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int d0 = 32 * s + 8 * kg;
       float x[8];
-      if constexpr (QBF16) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(a.q) + qrow + d0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = __uint_as_float(w[e] << 16);
-          x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (QBF16) {
+          x[2 * e] = __uint_as_float(raw[s][0][e] << 16);
+          x[2 * e + 1] = __uint_as_float(raw[s][0][e] & 0xffff0000u);
+        } else {
+          x[e] = __uint_as_float(raw[s][0][e]);
+          x[4 + e] = __uint_as_float(raw[s][NW - 1][e]);
         }
-      } else {
-        const float* src = static_cast<const float*>(a.q) + qrow + d0;
-        const float4 u0 = *reinterpret_cast<const float4*>(src);
-        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-        x[0] = u0.x, x[1] = u0.y, x[2] = u0.z, x[3] = u0.w;
-        x[4] = u1.x, x[5] = u1.y, x[6] = u1.z, x[7] = u1.w;
       }
       unsigned h16[8];
 #pragma unroll
@@ -167,6 +187,10 @@ __global__ __launch_bounds__(256) void splitk_bypass_kernel(BypassArgs a, const 
       qb[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
+
+  const int end = min(T, start + a.split_tokens);
+  const int npg = (end - start + kPage - 1) / kPage;
+  const int nj = npg > wave ? (npg - wave + 3) >> 2 : 0;
 
   const unsigned koff = col * 256 + kg * 16;
   const unsigned voff = kValOff + col * 32 + kg * 8;

@@ -417,10 +417,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   constexpr int WC = 2 * NREP;  // used P.V columns (hi, lo per head)
   constexpr float kMidCode = static_cast<float>(1 << (VB - 1));
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int T = a.seq_lens[b];
   const int start = split * a.split_tokens;
-  if (start >= T) return;
-  const int end = min(T, start + a.split_tokens);
 
   __shared__ __attribute__((aligned(16))) unsigned char lut[256 * kLutEntry];
   __shared__ __attribute__((aligned(16))) unsigned short wl[4][4][WC][32];  // P.V weights (float16)
@@ -439,11 +436,16 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
 
   // Block ids of this wave's pages, one per lane: lane 2j + p holds page p of
   // the wave's chunk j (chunk j = tokens start + 32 (wave + 4j) .. +31; at most
-  // 32 chunks per wave).  The query operand (prepared by the prologue) follows.
-  int ids = 0;
+  // 32 chunks per wave).  They and the query operand (prepared by the prologue)
+  // are read before the sequence length is known, so that the three reads
+  // overlap instead of forming a chain; table entries past the context (the
+  // index clamped to the row) are read but never used.
+  // (The host launches no split kernel for a table of zero blocks per row.)
+  int ids;
   {
     const int tok = start + 32 * (wave + 4 * (lane >> 1)) + 16 * (lane & 1);
-    if (tok < end) ids = btab[tbl + (tok >> 4)];
+    const long long pg = static_cast<long long>(tok >> 4);
+    ids = btab[tbl + (pg < a.max_blocks ? pg : a.max_blocks - 1)];
   }
   half8 qa[NSET][4];
   {
@@ -453,6 +455,17 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
 #pragma unroll
       for (int s = 0; s < 4; ++s) qa[st][s] = as_h8(src[(st * 4 + s) * 64]);
   }
+  const int T = a.seq_lens[b];
+  if (start >= T) {
+    // the reads above stay ahead of this test (their results are not needed here)
+    asm volatile("" ::"v"(ids));
+#pragma unroll
+    for (int st = 0; st < NSET; ++st)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(qa[st][s]));
+    return;
+  }
+  const int end = min(T, start + a.split_tokens);
   const LaneOffsets lofs = lane_offsets<KB, VB>(lane);
   const int span = end - start - 32 * wave;
   const int nch = span > 0 ? (span + 127) / 128 : 0;  // chunks of this wave

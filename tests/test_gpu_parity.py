@@ -272,6 +272,28 @@ def test_decode_bypass_variants(rep, q_dtype, splits):
 
 
 @pytest.mark.parametrize("bypass", [False, True])
+def test_decode_empty_table(bypass):
+    """Every sequence empty and a block table of zero blocks per row: no split
+    kernel runs and the output is exact zeros."""
+    torch = _torch()
+    say("decode empty table, bypass", bypass)
+    layer = tq.Layer(tq.config(2, 4, 4, seed=1, bypass=bypass))
+    pool = layer.new_pool(1)
+    q = torch.randn(3, 8, 128, device="cuda").to(torch.bfloat16)
+    bt = torch.zeros((3, 1), dtype=torch.int32, device="cuda")  # passed with 0 blocks per row
+    sl = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out = torch.full((3, 8, 128), float("nan"), device="cuda")
+    ws = tq.new_workspace(layer, 3, 8, 0)
+    st = tq.lib().tq_decode_attn(layer.handle, tq._ptr(q), tq._dtype_code(q), 3, 8, tq._ptr(pool), 1,
+                                 tq._ptr(bt), 0, tq._ptr(sl), 0, 0.0, 0, tq._ptr(out), tq._dtype_code(out),
+                                 tq._ptr(ws), ws.numel(), tq._stream(None))
+    assert st == 0, tq.lib().tq_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    layer.close()
+
+
+@pytest.mark.parametrize("bypass", [False, True])
 def test_decode_ignores_unwritten_slots(bypass):
     """Pool bytes all 0xFF before the records are written: the slots past each
     context end hold NaN norms, scales, zeros and values, which must not reach
