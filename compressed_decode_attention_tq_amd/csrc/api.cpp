@@ -162,8 +162,7 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   p.n_splits = (ctx + split_tokens - 1) / split_tokens;
   const size_t bh = static_cast<size_t>(batch) * n_q_heads;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
-  p.ws_qu = 0;
-  p.ws_part = align(bh * 2 * kDim * sizeof(float));
+  p.ws_part = 0;
   p.ws_qa = p.ws_part + align(bh * static_cast<size_t>(p.n_splits) * (kDim + 4) * sizeof(float));
   // Q.K operand: per (sequence, KV head) 1 or 2 tiles x 4 K-steps x 64 lanes x 8 float16
   const size_t sets = p.rep == 8 ? 2 : 1;

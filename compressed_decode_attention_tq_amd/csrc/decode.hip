@@ -31,9 +31,9 @@ namespace {
 constexpr int kPart = kDim + 4;  // acc[128], m, l, pad, pad
 
 // ---------------------------------------------------------------- prologue
-// q' = R_g q and u = S_g q' in float32 (qu), and for compressed layers the
-// Q.K operand of the split-K mainloop (qa): q' and kappa*u split into float16
-// hi + lo pieces, placed as rows of the matrix-core A operand.  Dim i of a row
+// q' = R_g q and u = S_g q' in float32, written as the Q.K operand of the
+// split-K mainloop (qa): q' and kappa*u split into float16 hi + lo pieces,
+// placed as rows of the matrix-core A operand.  Dim i of a row
 // sits in lane row + 16 (i / 32), K-step (i % 32) / 8, element i % 8.
 // Rows (R = query heads per KV head, h = head within the group):
 //   R <= 4: one tile, rows part*R + h for parts q' hi, q' lo, ku hi, ku lo
@@ -46,7 +46,7 @@ constexpr int kPart = kDim + 4;  // acc[128], m, l, pad, pad
 // head's dot products; the quarters are summed through LDS in a fixed order.
 template <bool QBF16>
 __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const float* RT, const float* ST,
-                                                       float* qu, unsigned short* qa, int Hq, int rep,
+                                                       unsigned short* qa, int Hq, int rep,
                                                        float kappa) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int Hkv = gridDim.x;
@@ -83,7 +83,6 @@ __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const floa
       const int h = o >> 7, d = o & 127;
       const float a = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
       sa[h][d] = a;
-      qu[static_cast<size_t>(bh0 + h) * 256 + d] = a;
     }
     __syncthreads();
     for (int h = 0; h < rep; ++h) {
@@ -98,7 +97,6 @@ __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const floa
       const int h = o >> 7, d = o & 127;
       const float a = sa[h][d];
       const float u = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
-      qu[static_cast<size_t>(bh0 + h) * 256 + 128 + d] = u;
       const int kgi = d >> 5, ks = (d >> 3) & 3, j = d & 7;
       const float ku = kappa * u;
       const _Float16 qh = static_cast<_Float16>(a), uh = static_cast<_Float16>(ku);
@@ -130,32 +128,45 @@ __global__ __launch_bounds__(512) void prologue_kernel(const void* q, const floa
 // sum_s e^{m_s - M} acc_s[d] / sum_s e^{m_s - M} l_s.  Splits are taken 8 at a
 // time with all of a group's reads issued before any is used (one memory round
 // trip per group), merged with a running max.
-__device__ __forceinline__ float merge_partials(const float* p, int ns, int d) {
-  float M = -INFINITY, num = 0.0f, den = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float m8[8], l8[8], a8[8];
+struct Group8 {
+  float m[8], l[8], a[8];
+};
+// Reads of splits s0 .. s0+7 (indices clamped to below `lim`; entries past the
+// sequence's splits are read but never used).
+__device__ __forceinline__ void read_group(const float* p, int s0, int lim, int d, Group8& g) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* q = p + (s0 + u < ns ? s0 + u : s0) * kPart;
-      m8[u] = q[128];
-      l8[u] = q[129];
-      a8[u] = q[d];
+  for (int u = 0; u < 8; ++u) {
+    const float* q = p + (s0 + u < lim ? s0 + u : s0) * kPart;
+    g.m[u] = q[128];
+    g.l[u] = q[129];
+    g.a[u] = q[d];
+  }
+}
+__device__ __forceinline__ void merge_group(const Group8& g, int s0, int ns, float& M, float& num, float& den) {
+  float mg = M;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (s0 + u < ns) mg = fmaxf(mg, g.m[u]);
+  const float f = (M == -INFINITY) ? 0.0f : __expf(M - mg);
+  num *= f;
+  den *= f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (s0 + u < ns) {
+      const float e = __expf(g.m[u] - mg);
+      num = fmaf(e, g.a[u], num);
+      den = fmaf(e, g.l[u], den);
     }
-    float mg = M;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < ns) mg = fmaxf(mg, m8[u]);
-    const float f = (M == -INFINITY) ? 0.0f : __expf(M - mg);
-    num *= f;
-    den *= f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < ns) {
-        const float e = __expf(m8[u] - mg);
-        num = fmaf(e, a8[u], num);
-        den = fmaf(e, l8[u], den);
-      }
-    M = mg;
+  M = mg;
+}
+// `first` holds the reads of splits 0..7, issued before ns was known.
+__device__ __forceinline__ float merge_partials(const float* p, int ns, int d, const Group8& first) {
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+  merge_group(first, 0, ns, M, num, den);
+  for (int s0 = 8; s0 < ns; s0 += 8) {
+    Group8 g;
+    read_group(p, s0, ns, d, g);
+    merge_group(g, s0, ns, M, num, den);
   }
   return num / den;
 }
@@ -173,8 +184,18 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* part, const i
   const int tid = threadIdx.x, c = tid >> 7, i = tid & 127;
   const int n = rep * 128;
   const int bh0 = b * Hq + g * rep;
+  // The first group of partials (at most two outputs per lane: rep <= 8) is
+  // read before the sequence length, so that the two reads overlap.
+  Group8 first[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int o = tid + 512 * k;
+    if (o < n)
+      read_group(part + static_cast<size_t>(bh0 + (o >> 7)) * n_splits * kPart, 0, n_splits, o & 127, first[k]);
+  }
   const int T = seq_lens[b];
-  const int ns = T > 0 ? (T + split_tokens - 1) / split_tokens : 0;
+  // (a length above max_seq_len, a caller error, reads no partial past the workspace)
+  const int ns = T > 0 ? min((T + split_tokens - 1) / split_tokens, n_splits) : 0;
   __shared__ float so[8][128], pr[4][8][128];
   float rr[32];
   if constexpr (!BYPASS) {
@@ -191,11 +212,16 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* part, const i
       static_cast<float*>(out)[at] = o;
     }
   };
-  for (int o = tid; o < n; o += 512) {
-    const int h = o >> 7, d = o & 127;
-    const float v = ns > 0 ? merge_partials(part + static_cast<size_t>(bh0 + h) * n_splits * kPart, ns, d) : 0.0f;
-    if constexpr (BYPASS) store(h, d, v);
-    else so[h][d] = v;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int o = tid + 512 * k;
+    if (o < n) {
+      const int h = o >> 7, d = o & 127;
+      const float v =
+          ns > 0 ? merge_partials(part + static_cast<size_t>(bh0 + h) * n_splits * kPart, ns, d, first[k]) : 0.0f;
+      if constexpr (BYPASS) store(h, d, v);
+      else so[h][d] = v;
+    }
   }
   if constexpr (!BYPASS) {
     __syncthreads();
@@ -222,7 +248,6 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bypass = L->cfg.bypass != 0;
   char* ws = static_cast<char*>(workspace);
-  float* qu = reinterpret_cast<float*>(ws + plan.ws_qu);
   float* part = reinterpret_cast<float*>(ws + plan.ws_part);
 
   // 1. prologue (compressed layers; the bypass kernel reads q itself)
@@ -234,7 +259,7 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     unsigned short* qa = reinterpret_cast<unsigned short*>(ws + plan.ws_qa);
     int Hq = plan.n_q_heads, rep = plan.rep;
     float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / kDim);  // sqrt(pi/2) / m, m = d
-    void* args[] = {const_cast<void**>(&q), &RT, &ST, &qu, &qa, &Hq, &rep, &kappa};
+    void* args[] = {const_cast<void**>(&q), &RT, &ST, &qa, &Hq, &rep, &kappa};
     ProfScope prof(kKPrologue, stream);
     hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, plan.batch), dim3(512), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));

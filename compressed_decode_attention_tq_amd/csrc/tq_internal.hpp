@@ -99,7 +99,6 @@ struct DecodePlan {
   int batch = 0, n_q_heads = 0, rep = 0;
   int split_tokens = 0;   // tokens per split (multiple of 64)
   int n_splits = 0;       // splits per sequence (grid x)
-  size_t ws_qu = 0;       // byte offset of q'/u in the workspace
   size_t ws_part = 0;     // byte offset of split partials
   size_t ws_qa = 0;       // byte offset of the Q.K matrix-core operand (compressed layers)
   size_t ws_bytes = 0;    // total
