@@ -46,7 +46,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lbyte;
 
 constexpr int kRow = 136;      // float16 elements per LDS operand row (128 + pad)
-constexpr int kCodeRow = 132;  // bytes per LDS code row (128 + pad)
 
 struct CArgs {
   const unsigned short* k;  // bf16 bits
@@ -206,10 +205,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ __attribute__((aligned(16))) unsigned short kv_in[P][2][16][128];  // [slot][K,V][token][dim] bf16
   __shared__ __attribute__((aligned(16))) _Float16 orh[16][kRow];  // rho hi
   __shared__ __attribute__((aligned(16))) _Float16 orl[16][kRow];  // rho lo
-  __shared__ __attribute__((aligned(16))) unsigned char vcode[16][kCodeRow];
   __shared__ __attribute__((aligned(16))) unsigned char img[PG::bytes];
-  __shared__ float fk[16], gpart[8][16], vmin[8][16], vmax[8][16];
-  __shared__ unsigned short n16s[16];
+  __shared__ float gpart[8][16], vmin[8][16], vmax[8][16];
   __shared__ __attribute__((aligned(16))) u32x4 s_hi[8][4][64];  // S_hi operands per wave and K-step
 
   // ---- this wave's R and S operands (row tile w), kept for the whole launch
@@ -259,6 +256,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int mine = first < a.n_tiles ? static_cast<int>((a.n_tiles - 1 - first) / step + 1) : 0;
   const int pro = mine < P ? mine : P;
   for (int j = 0; j < pro; ++j) stage(first + j * step, j, lane0);
+  if constexpr (KB == 3) {  // key-code words are OR-ed into; each tile's store clears them again
+    for (int i = static_cast<int>(threadIdx.x); i < PG::ks / 4; i += 512) reinterpret_cast<unsigned*>(img)[i] = 0u;
+  }
   unsigned clean = 0;  // bit i: iteration k-1-i issued one copy and one page store
   int slot = 0;  // k mod P
   for (int k = 0; k < mine; ++k, slot = (slot == P - 1) ? 0 : slot + 1) {
@@ -297,53 +297,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int j = 1; j < 16; ++j) full = full && sl[j] == sl[0] + j;
     __syncthreads();  // tile rows in LDS (every wave waited on its copy)
 
-    // ---- B1: T = R k, V = R v (row tile w, 16 tokens); wave 0 also takes ||k||.
-    // The K/V operands are read one K-step at a time (8 registers live, not 32).
-    floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f}, V = {0.0f, 0.0f, 0.0f, 0.0f};
-    {
-      float k2 = 0.0f;
+    // ---- B1: T = R k, V = R v (row tile w, 16 tokens), and every wave's own
+    // ||k||^2: the Gram product of the tile's key rows with themselves, whose
+    // diagonal is the squared norms (bf16 products are exact and each
+    // instruction rounds its 32-term sum once).  The K/V operands are read one
+    // K-step at a time (8 registers live, not 32); the key chunk a lane holds
+    // is both the A row (token col) and the B column (token col) of the step.
+    floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f}, V = {0.0f, 0.0f, 0.0f, 0.0f}, NK = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int pos = (4 * s + kg + col) & 15;  // chunk 4s + kg of token col
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][0][col][8 * pos]);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][1][col][8 * pos]);
-        T = mfma_b(R0[s], kb, T);
-        V = mfma_b(R0[s], vb, V);
-        T = mfma_b(R1[s], kb, T);
-        V = mfma_b(R1[s], vb, V);
-        T = mfma_b(R2[s], kb, T);
-        V = mfma_b(R2[s], vb, V);
-        if (w == 0) {
-          // ||k||^2 in float32 from the exact bf16 inputs (the lane holds 32 dims of token col)
-          const u32x4 x = __builtin_bit_cast(u32x4, kb);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xffff0000u);
-            k2 = fmaf(lo, lo, k2);
-            k2 = fmaf(hi, hi, k2);
-          }
-        }
-      }
-      if (w == 0) {
-        k2 = rows_sum(k2);
-        if (kg == 0) {
-          const float n = sqrtf(k2);
-          fk[col] = (n > 0.0f) ? sqrtf(128.0f) / n : 0.0f;  // zero norm: t = 0
-          n16s[col] = __half_as_ushort(__float2half_rn(n));
-        }
-      }
-      if constexpr (KB == 3) {  // key-code words are OR-ed together below
-        for (int i = tid; i < PG::ks / 4; i += 512) reinterpret_cast<unsigned*>(img)[i] = 0u;
-      }
+    for (int s = 0; s < 4; ++s) {
+      const int pos = (4 * s + kg + col) & 15;  // chunk 4s + kg of token col
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][0][col][8 * pos]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][1][col][8 * pos]);
+      T = mfma_b(R0[s], kb, T);
+      V = mfma_b(R0[s], vb, V);
+      NK = mfma_b(kb, kb, NK);
+      T = mfma_b(R1[s], kb, T);
+      V = mfma_b(R1[s], vb, V);
+      T = mfma_b(R2[s], kb, T);
+      V = mfma_b(R2[s], vb, V);
     }
-    __syncthreads();  // every wave has its operands: ring slot `slot` may be refilled
-    const bool fetch = k + P < mine;
-    if (fetch) stage(first + static_cast<long long>(k + P) * step, slot, lane);
+    // Gram entry (col, col) sits in lane col + 16 (col / 4), element col % 4.
+    // The standardising factor sqrt(d)/n comes from the reciprocal square root
+    // (within an ulp or so, like the quotient of rounded roots); the stored
+    // norm n16 is taken from the correctly rounded root by the wave storing it.
+    float f, k2;
+    {
+      const int e = col & 3;
+      const float d01 = (e & 1) ? NK[1] : NK[0];
+      const float d23 = (e & 1) ? NK[3] : NK[2];
+      k2 = __shfl((e & 2) ? d23 : d01, col + 16 * (col >> 2), 64);
+      f = (k2 >= 1.17549435e-38f) ? sqrtf(128.0f) * __builtin_amdgcn_rsqf(k2)
+                                  : (k2 > 0.0f ? sqrtf(128.0f) / sqrtf(k2) : 0.0f);  // zero norm: t = 0
+    }
 
     // ---- B2: t, codes, residual (rho -> LDS), key codes -> image; value extremes
     float vp[4];
     {
-      const float f = fk[col];
       float rho[4], g2 = 0.0f;
       unsigned codes = 0;
 #pragma unroll
@@ -406,7 +396,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         vmax[w][col] = mx;
       }
     }
-    __syncthreads();
+    __syncthreads();  // rho, norms and extremes in LDS; every wave is past B1, so
+                      // ring slot `slot` may be refilled
+    const bool fetch = k + P < mine;
+    if (fetch) stage(first + static_cast<long long>(k + P) * step, slot, lane);
 
     // ---- C: y = S rho -> sign bits; value codes; per-token metadata
     {
@@ -442,16 +435,57 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       // reciprocal of the scale with one correction step
       const float inv0 = __builtin_amdgcn_rcpf(sc);
       const float inv = fmaf(fmaf(-sc, inv0, 1.0f), inv0, inv0);
-      unsigned vc = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      const float invz = (sc > 0.0f) ? inv : 0.0f;  // a zero scale gives code 0
+      unsigned x0, x1, x2, x3;
+      {
         // quotient to a couple of float32 ulps: a code can move only within
         // ~1e-7 relative of a rounding midpoint
-        const float q = (vp[r] - zr) * inv;
-        const float c = (sc > 0.0f) ? __builtin_amdgcn_fmed3f(rintf(q), 0.0f, kTop) : 0.0f;
-        vc |= static_cast<unsigned>(c) << (8 * r);
+        const unsigned sh = VB * (col & 7);
+        x0 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[0] - zr) * invz), 0.0f, kTop)) << sh;
+        x1 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[1] - zr) * invz), 0.0f, kTop)) << sh;
+        x2 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[2] - zr) * invz), 0.0f, kTop)) << sh;
+        x3 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[3] - zr) * invz), 0.0f, kTop)) << sh;
       }
-      *reinterpret_cast<unsigned*>(&vcode[col][16 * w + 4 * kg]) = vc;
+      // Value codes into the image's Vc field, in lane blocks: the run of
+      // block (h, c, i) holds tokens 8h..8h+7 of coordinate 16i + c (token
+      // 8h + j at bit VB j), VB bytes at (16h + c) 8VB + VB i.  This wave holds
+      // coordinates 16w + 4kg + r of token col (x_r, already at bit VB (col % 8)),
+      // i.e. block i = w: each run is an OR over the 8 lanes of a half row
+      // (lane ^ 1, lane ^ 2, then the mirrored lane of the half row), and lane
+      // j < 4 of the half row stores run r = j.  One DPP instruction per step;
+      // the four runs interleave, so each step reads a result written three
+      // instructions before (the first one after the required two wait states).
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_or_b32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %3, %3, %3 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %2, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %3, %3, %3 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %2, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+          "v_or_b32_dpp %3, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xf"
+          : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+      {
+        const int j = col & 7;
+        if (j < 4) {
+          const unsigned x = (j & 2) ? ((j & 1) ? x3 : x2) : ((j & 1) ? x1 : x0);
+          unsigned char* dst = &img[PG::vc + (16 * (col >> 3) + 4 * kg + j) * 8 * VB + VB * w];
+          if constexpr (VB == 4) {
+            *reinterpret_cast<unsigned*>(dst) = x;
+          } else if constexpr (VB == 2) {
+            *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(x);
+          } else {
+            dst[0] = static_cast<unsigned char>(x);
+            dst[1] = static_cast<unsigned char>(x >> 8);
+            dst[2] = static_cast<unsigned char>(x >> 16);
+          }
+        }
+      }
       if ((w & 1) == 0 && kg == 0)
         *reinterpret_cast<unsigned*>(&img[PG::vsz + col * 16 + G * 4]) =
             static_cast<unsigned>(__half_as_ushort(s16)) | (static_cast<unsigned>(__half_as_ushort(z16)) << 16);
@@ -460,40 +494,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
         for (int i = 0; i < 8; ++i) g2 += gpart[i][col];
         const unsigned short g16 = __half_as_ushort(__float2half_rn(sqrtf(g2)));
+        const unsigned short n16 = __half_as_ushort(__float2half_rn(sqrtf(k2)));
         *reinterpret_cast<unsigned*>(&img[PG::kn + col * 4]) =
-            static_cast<unsigned>(n16s[col]) | (static_cast<unsigned>(g16) << 16);
+            static_cast<unsigned>(n16) | (static_cast<unsigned>(g16) << 16);
       }
     }
-    __syncthreads();
-
-    // ---- D: value codes into the image's Vc field, in lane blocks: lane
-    // (h, c, i) packs the codes of tokens 8h..8h+7 of coordinate 16i + c (token
-    // 8h + k at bit k VB) into the VB bytes at (16h + c) 8VB + VB i.
-    if (tid < 256) {
-      const int h = tid >> 7, c = (tid >> 3) & 15, i = tid & 7;
-      const int d = 16 * i + c;
-      unsigned run = 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) run |= static_cast<unsigned>(vcode[8 * h + k][d]) << (VB * k);
-      unsigned char* dst = &img[PG::vc + (16 * h + c) * 8 * VB + VB * i];
-      if constexpr (VB == 4) {
-        *reinterpret_cast<unsigned*>(dst) = run;
-      } else if constexpr (VB == 2) {
-        *reinterpret_cast<unsigned short*>(dst) = static_cast<unsigned short>(run);
-      } else {
-        dst[0] = static_cast<unsigned char>(run);
-        dst[1] = static_cast<unsigned char>(run >> 8);
-        dst[2] = static_cast<unsigned char>(run >> 16);
-      }
-    }
-    __syncthreads();
+    __syncthreads();  // the page image is complete
 
     // ---- E: store
     if (full) {
       // one 16-byte store per wave: chunk w + 8 * lane (lane 0 is always in range)
       unsigned char* page = a.pool + (static_cast<size_t>(sl[0] >> 4) * a.H + h) * a.block_bytes;
       const int c = w + 8 * lane;
-      if (c < kChunks) *reinterpret_cast<u32x4*>(page + 16 * c) = *reinterpret_cast<const u32x4*>(&img[16 * c]);
+      if (c < kChunks) {
+        *reinterpret_cast<u32x4*>(page + 16 * c) = *reinterpret_cast<const u32x4*>(&img[16 * c]);
+        if constexpr (KB == 3) {  // key-code words are OR-ed into: clear what this lane read
+          if (c < PG::ks / 16) *reinterpret_cast<u32x4*>(&img[16 * c]) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     } else {
       // token by token: fixed-size fields copied, value-code bits set atomically
 #pragma unroll 1
@@ -520,7 +538,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         } else if (f >= 128 && f < 256) {
           const int d = f - 128;
           unsigned* vw = reinterpret_cast<unsigned*>(page + PG::vc);
-          const unsigned c = vcode[t][d];
+          // token t's code of coordinate d, read from its run in the image
+          const unsigned et = ((16u * (t >> 3) + (d & 15)) * 16u + 2u * (d >> 4) + ((t & 7) >> 2)) * 4u + (t & 3);
+          const unsigned bt = et * VB;
+          const unsigned xb = img[PG::vc + (bt >> 3)] | (static_cast<unsigned>(img[PG::vc + (bt >> 3) + 1]) << 8);
+          const unsigned c = (xb >> (bt & 7)) & ((1u << VB) - 1u);
           // lane-blocked Vc stream: block 16 (o / 8) + d % 16, group 2 (d / 16) + (o % 8) / 4
           const unsigned elem = ((16u * (o >> 3) + (d & 15)) * 16u + 2u * (d >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
           const unsigned bit = elem * VB;
@@ -533,9 +555,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           }
         }
       }
+      if constexpr (KB == 3) {  // clear the key-code words this thread read
+        if (tid < 4 * KB) {
+#pragma unroll 1
+          for (int t = 0; t < 16; ++t)
+            reinterpret_cast<unsigned*>(&img[PG::kc + ((tid / KB) * 16 + t) * 4 * KB])[tid % KB] = 0u;
+        }
+      }
     }
     clean = (clean << 1) | ((fetch && full) ? 1u : 0u);
-    __syncthreads();  // the next tile rewrites codes and the image
+    // (the next tile writes LDS only after its first barrier, which every wave
+    //  reaches after this store's image reads)
   }
   wait_vmcnt<0>();
 }
