@@ -307,6 +307,45 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
     e = hipMemcpyAsync(L->dOpA, opa.data(), nop * sizeof(unsigned short), hipMemcpyHostToDevice,
                        static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
+    // Matrix-core B operands for the decode prologue: W = [R; P] with P = S R
+    // (the exact product of the stored float32 R and S, formed in float64), so
+    // that q' = R q and u = S q' = P q are independent products of q.  Each entry
+    // is split into float16 hi + lo pieces.
+    const size_t nq = static_cast<size_t>(H) * 16 * 4 * 2 * 64 * 8;
+    std::vector<unsigned short> opq(nq);
+    {
+      std::vector<double> W(static_cast<size_t>(2 * d) * d);
+      for (int h = 0; h < H; ++h) {
+        const float* Rh = R.data() + static_cast<size_t>(h) * d * d;
+        const float* Sh = S.data() + static_cast<size_t>(h) * d * d;
+        for (int i = 0; i < d; ++i)
+          for (int j = 0; j < d; ++j) {
+            W[static_cast<size_t>(i) * d + j] = Rh[i * d + j];
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += static_cast<double>(Sh[i * d + k]) * static_cast<double>(Rh[k * d + j]);
+            W[static_cast<size_t>(d + i) * d + j] = acc;
+          }
+        for (int t = 0; t < 16; ++t)
+          for (int ks = 0; ks < 4; ++ks)
+            for (int l = 0; l < 64; ++l)
+              for (int j = 0; j < 8; ++j) {
+                const double w = W[static_cast<size_t>(16 * t + l % 16) * d + 32 * ks + 8 * (l / 16) + j];
+                const _Float16 hi = static_cast<_Float16>(w);
+                const _Float16 lo = static_cast<_Float16>(w - static_cast<double>(hi));
+                const size_t at = ((((static_cast<size_t>(h) * 16 + t) * 4 + ks) * 2) * 64 + l) * 8 + j;
+                opq[at] = __builtin_bit_cast(unsigned short, hi);
+                opq[at + 64 * 8] = __builtin_bit_cast(unsigned short, lo);
+              }
+      }
+    }
+    e = hipMalloc(reinterpret_cast<void**>(&L->dOpQ), nq * sizeof(unsigned short));
+    if (e != hipSuccess) {
+      tq_layer_destroy(L);
+      return fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc of layer state failed: %s", hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(L->dOpQ, opq.data(), nq * sizeof(unsigned short), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
     e = hipStreamSynchronize(static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipStreamSynchronize"); }
   }
@@ -321,11 +360,13 @@ tq_status tq_layer_destroy(tq_layer* L) {
   hipError_t e2 = L->dRT ? hipFree(L->dRT) : hipSuccess;
   hipError_t e3 = L->dST ? hipFree(L->dST) : hipSuccess;
   hipError_t e4 = L->dOpA ? hipFree(L->dOpA) : hipSuccess;
+  hipError_t e5 = L->dOpQ ? hipFree(L->dOpQ) : hipSuccess;
   delete L;
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
   if (e3 != hipSuccess) return hip_fail(e3, "hipFree");
   if (e4 != hipSuccess) return hip_fail(e4, "hipFree");
+  if (e5 != hipSuccess) return hip_fail(e5, "hipFree");
   return TQ_OK;
 }
 
@@ -396,6 +437,8 @@ tq_status tq_decode_attn(const tq_layer* L, const void* q, tq_dtype q_dtype, int
   if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
   DecodePlan p;
   tq_status st = plan_decode(L, batch, n_q_heads, max_seq_len, num_splits, &p);
   if (st != TQ_OK) return st;

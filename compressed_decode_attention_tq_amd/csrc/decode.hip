@@ -31,94 +31,125 @@ namespace {
 constexpr int kPart = kDim + 4;  // acc[128], m, l, pad, pad
 
 // ---------------------------------------------------------------- prologue
-// q' = R_g q and u = S_g q' in float32, written as the Q.K operand of the
-// split-K mainloop (qa): q' and kappa*u split into float16 hi + lo pieces,
-// placed as rows of the matrix-core A operand.  Dim i of a row
-// sits in lane row + 16 (i / 32), K-step (i % 32) / 8, element i % 8.
-// Rows (R = query heads per KV head, h = head within the group):
+// q' = R_g q and u = S_g q' = (S_g R_g) q: both are products of q itself with
+// a fixed matrix, W = [R_g; P_g] (256 x 128, P_g = S_g R_g formed once per
+// layer), so they run side by side on the matrix core with no dependency
+// between them.  The outputs are written as the Q.K operand of the split-K
+// mainloop (qa): q' and kappa*u split into float16 hi + lo pieces, placed as
+// rows of the matrix-core A operand.  Dim i of a row sits in lane
+// row + 16 (i / 32), K-step (i % 32) / 8, element i % 8.  Rows (R = query heads
+// per KV head, h = head within the group):
 //   R <= 4: one tile, rows part*R + h for parts q' hi, q' lo, ku hi, ku lo
 //           (rows 4R..15 zero)
 //   R == 8: tile 0 rows h / 8+h = q' hi / lo, tile 1 the same for kappa*u.
 //
-// One workgroup of 512 lanes per (KV head g, sequence b) serves the group's
-// query heads.  Lane (c, i) = (lane / 128, lane % 128) holds column i of rows
-// 32c..32c+31 of R_g^T and S_g^T, loaded once, and forms that quarter of every
-// head's dot products; the quarters are summed through LDS in a fixed order.
+// Out = Q W^T on v_mfma_f32_16x16x32_f16: the 16 rows of a tile are 16 / R
+// sequences x R query heads of KV head g; column tile t (16 of them) is
+// output coordinates 16t..16t+15 of W.  Q and W are split into float16 hi + lo
+// pieces (22 significant bits) and Q_hi W_hi + Q_hi W_lo + Q_lo W_hi is
+// accumulated in float32 (each instruction sums its exact products and rounds
+// once).  Workgroup (g, sequence group, z) is four independent waves, wave w
+// taking column tile 4z + w: twelve matrix-core instructions, no LDS, no
+// barrier.  W's pieces are stored per (head, tile, K-step, piece) in the
+// lane order of the B operand, one 16-byte read per lane.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <bool QBF16>
-__global__ __launch_bounds__(512) void prologue_kernel(const void* q, const float* RT, const float* ST,
-                                                       unsigned short* qa, int Hq, int rep,
-                                                       float kappa) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int Hkv = gridDim.x;
-  const int tid = threadIdx.x, c = tid >> 7, i = tid & 127;
-  const int n = rep * 128;  // outputs of this group
-  const int bh0 = b * Hq + g * rep;
-  auto load_q = [&](int h, int d) -> float {
-    const size_t at = static_cast<size_t>(bh0 + h) * 128 + d;
-    if constexpr (QBF16) return __uint_as_float(static_cast<unsigned>(static_cast<const unsigned short*>(q)[at]) << 16);
-    else return static_cast<const float*>(q)[at];
-  };
+__global__ __launch_bounds__(256) void prologue_kernel(const void* q, const u32x4* __restrict__ opq,
+                                                       unsigned short* qa, int B, int Hq, int rep, float kappa) {
+  const int g = blockIdx.x, Hkv = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  const int t = 4 * blockIdx.z + (threadIdx.x >> 6);  // column tile
+  const int col = lane & 15, kg = lane >> 4;
+  const int spg = 16 / rep;  // sequences per tile
+  const int b0 = blockIdx.y * spg;
+  // W pieces of this tile: [4 K-steps][hi, lo], issued first
+  u32x4 wv[4][2];
   {
-    __shared__ float sq[8][128], sa[8][128], part[4][8][128];
-    float rt[32], st[32];
-    {
-      const float* r = RT + static_cast<size_t>(g) * 128 * 128 + (32 * c) * 128 + i;
-      const float* t = ST + static_cast<size_t>(g) * 128 * 128 + (32 * c) * 128 + i;
+    const u32x4* src = opq + (static_cast<size_t>(g) * 16 + t) * 4 * 2 * 64 + lane;
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        rt[u] = r[u * 128];
-        st[u] = t[u * 128];
-      }
+    for (int s = 0; s < 4; ++s) {
+      wv[s][0] = src[(2 * s) * 64];
+      wv[s][1] = src[(2 * s + 1) * 64];
     }
-    for (int o = tid; o < n; o += 512) sq[o >> 7][o & 127] = load_q(o >> 7, o & 127);
-    __syncthreads();
-    for (int h = 0; h < rep; ++h) {
-      float acc = 0.0f;
+  }
+  // Q row m = lane % 16: sequence b0 + m / rep, head g*rep + m % rep; dims 32s + 8kg .. +7
+  half8 qh[4], ql[4];
+  {
+    const int bq = b0 + col / rep;
+    const bool ok = bq < B;
+    const size_t row = static_cast<size_t>(ok ? bq : 0) * Hq + g * rep + col % rep;
 #pragma unroll
-      for (int u = 0; u < 32; ++u) acc = fmaf(rt[u], sq[h][32 * c + u], acc);
-      part[c][h][i] = acc;
-    }
-    __syncthreads();
-    for (int o = tid; o < n; o += 512) {
-      const int h = o >> 7, d = o & 127;
-      const float a = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
-      sa[h][d] = a;
-    }
-    __syncthreads();
-    for (int h = 0; h < rep; ++h) {
-      float acc = 0.0f;
+    for (int s = 0; s < 4; ++s) {
+      float x[8];
+      if constexpr (QBF16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(q) + row * 128 + 32 * s + 8 * kg);
 #pragma unroll
-      for (int u = 0; u < 32; ++u) acc = fmaf(st[u], sa[h][32 * c + u], acc);
-      part[c][h][i] = acc;
-    }
-    __syncthreads();
-    const int nset = rep == 8 ? 2 : 1;
-    for (int o = tid; o < n; o += 512) {
-      const int h = o >> 7, d = o & 127;
-      const float a = sa[h][d];
-      const float u = (part[0][h][d] + part[1][h][d]) + (part[2][h][d] + part[3][h][d]);
-      const int kgi = d >> 5, ks = (d >> 3) & 3, j = d & 7;
-      const float ku = kappa * u;
-      const _Float16 qh = static_cast<_Float16>(a), uh = static_cast<_Float16>(ku);
-      const _Float16 ql = static_cast<_Float16>(a - static_cast<float>(qh));
-      const _Float16 ul = static_cast<_Float16>(ku - static_cast<float>(uh));
-      auto put = [&](int set, int row, _Float16 v) {
-        const size_t at = ((((static_cast<size_t>(b) * Hkv + g) * nset + set) * 4 + ks) * 64 + row + 16 * kgi) * 8 + j;
-        qa[at] = __builtin_bit_cast(unsigned short, v);
-      };
-      if (rep == 8) {
-        put(0, h, qh);
-        put(0, 8 + h, ql);
-        put(1, h, uh);
-        put(1, 8 + h, ul);
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(v[e] << 16);
+          x[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+        }
       } else {
-        put(0, h, qh);
-        put(0, rep + h, ql);
-        put(0, 2 * rep + h, uh);
-        put(0, 3 * rep + h, ul);
-        if (h == 0)
-          for (int row = 4 * rep; row < 16; ++row) put(0, row, static_cast<_Float16>(0.0f));
+        const float* p = static_cast<const float*>(q) + row * 128 + 32 * s + 8 * kg;
+        const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+        const floatx4 c = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = a[e];
+          x[4 + e] = c[e];
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ok ? x[e] : 0.0f;
+        const _Float16 hi = static_cast<_Float16>(v);
+        qh[s][e] = hi;
+        ql[s][e] = static_cast<_Float16>(v - static_cast<float>(hi));
+      }
+    }
+  }
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const half8 wh = __builtin_bit_cast(half8, wv[s][0]);
+    const half8 wl = __builtin_bit_cast(half8, wv[s][1]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[s], wh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[s], wl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[s], wh, acc, 0, 0, 0);
+  }
+  // lane (col, kg) holds rows 4kg + r of column 16t + col
+  const bool is_u = t >= 8;
+  const int d = 16 * (t & 7) + col;
+  const int nset = rep == 8 ? 2 : 1;
+  const int kgi = d >> 5, ks = (d >> 3) & 3, j = d & 7;
+  auto put = [&](int b, int set, int row, _Float16 v) {
+    const size_t at = ((((static_cast<size_t>(b) * Hkv + g) * nset + set) * 4 + ks) * 64 + row + 16 * kgi) * 8 + j;
+    qa[at] = __builtin_bit_cast(unsigned short, v);
+  };
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * kg + r;
+    const int b = b0 + m / rep, h = m % rep;
+    if (b >= B) continue;
+    const float v = is_u ? kappa * acc[r] : acc[r];
+    const _Float16 hi = static_cast<_Float16>(v);
+    const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+    if (rep == 8) {
+      put(b, is_u ? 1 : 0, h, hi);
+      put(b, is_u ? 1 : 0, 8 + h, lo);
+    } else {
+      put(b, 0, (is_u ? 2 * rep : 0) + h, hi);
+      put(b, 0, (is_u ? 3 * rep : rep) + h, lo);
+    }
+  }
+  // rows 4R..15 of a one-tile operand are zero (column tiles 0..7 cover the dims)
+  if (rep < 4 && !is_u) {
+    const int nz = 16 - 4 * rep;
+    for (int x = kg; x < spg * nz; x += 4) {
+      const int b = b0 + x / nz, row = 4 * rep + x % nz;
+      if (b < B) put(b, 0, row, static_cast<_Float16>(0.0f));
     }
   }
 }
@@ -254,14 +285,14 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   if (!bypass && max_blocks_per_seq > 0) {
     void* fn = (q_dtype == TQ_BF16) ? reinterpret_cast<void*>(&prologue_kernel<true>)
                                     : reinterpret_cast<void*>(&prologue_kernel<false>);
-    const float* RT = L->dRT;
-    const float* ST = L->dST;
+    const u32x4* opq = reinterpret_cast<const u32x4*>(L->dOpQ);
     unsigned short* qa = reinterpret_cast<unsigned short*>(ws + plan.ws_qa);
-    int Hq = plan.n_q_heads, rep = plan.rep;
+    int B = plan.batch, Hq = plan.n_q_heads, rep = plan.rep;
     float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / kDim);  // sqrt(pi/2) / m, m = d
-    void* args[] = {const_cast<void**>(&q), &RT, &ST, &qa, &Hq, &rep, &kappa};
+    void* args[] = {const_cast<void**>(&q), &opq, &qa, &B, &Hq, &rep, &kappa};
+    const int spg = 16 / rep;
     ProfScope prof(kKPrologue, stream);
-    hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, plan.batch), dim3(512), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, (plan.batch + spg - 1) / spg, 4), dim3(256), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode prologue launch: %s", hipGetErrorString(e));
   }
   // 2. split-K mainloop (a table with no blocks per row means every sequence is

@@ -77,6 +77,10 @@ struct tq_layer {
   // [H][8 row tiles][kOpSets: R bf16 hi, mid, lo; S fp16 hi, lo][4 K-steps][64 lanes][8],
   // lane l of (tile w, step s) holding M[16w + l%16][32s + 8(l/16) .. +7].
   unsigned short* dOpA = nullptr;
+  // Matrix-core B operands of W = [R; S R] (256 x 128) for the decode prologue
+  // (float16 bits): [H][16 column tiles][4 K-steps][hi, lo][64 lanes][8], lane l
+  // of (tile t, step s) holding W[16t + l%16][32s + 8(l/16) .. +7].
+  unsigned short* dOpQ = nullptr;
   float centroids[16] = {0};
   float boundaries[16] = {0};
   int levels = 0;

@@ -185,7 +185,8 @@ tq_status tq_decode_workspace_size(const tq_layer* layer, int batch, int n_q_hea
  *       (q'.c[idx_i] + sqrt(pi/2)/128 * gamma_i * (S_g q').(2 z_i - 1)),  q' = R_g q,
  *   vhat_i = R_g^T (zero + scale * code_i),  g = h / (n_q_heads / n_kv_heads).
  * Arguments:
- *   q            device [batch][n_q_heads][128] of q_dtype (F32 or BF16)
+ *   q            device [batch][n_q_heads][128] of q_dtype (F32 or BF16), 16-byte
+ *                aligned (rows are read with 16-byte loads)
  *   pool         device pool written by tq_compress_kv
  *   block_table  device int32 [batch][max_blocks_per_seq]: logical block j of
  *                sequence b -> physical block id in [0, num_blocks)
