@@ -12,6 +12,17 @@ plus a 1-bit QJL residual sign):
     y     = S rho,   z_j = [y_j >= 0]                1 sign bit per coordinate
 The code decisions use the unrounded n and gamma.
 
+Key modes without the residual projection ("turbo-attn 0.24.0", "How it
+works": normalise, store a single magnitude, quantise each rotated coordinate
+to a shared codebook; "Configuration", TKV_K_NC: norm-correction of K reads):
+    "mse"     the same n, t, idx; no residual signs (z = 0) and gamma = 0, so
+              the decoder's QJL term vanishes and the score is the inner
+              product with the codebook reconstruction (n/sqrt d) R^T c[idx]
+    "mse_nc"  as "mse" with the stored magnitude n * sqrt(d) / ||c[idx]||: the
+              reconstruction then has the key's own norm n (up to the fp16
+              rounding of the stored value); the correction is folded into the
+              stored magnitude, so the read path is the same for every mode
+
 Values ("How 0xsero/turboquant works", "Value Compression": group
 quantisation with per-group scale/zero; "tiny-turboquant 0.18.0",
 "Measured quality": groups of 32 channels, each with its own scale/zero):
@@ -31,8 +42,14 @@ import numpy as np
 from . import codebook, layout as lay
 
 
-def compress_keys(K, R, S, centroids, boundaries):
-    """K: [n, d] float64 (exact input values).  Returns a dict of per-vector arrays."""
+KEY_MODES = ("qjl", "mse", "mse_nc")
+
+
+def compress_keys(K, R, S, centroids, boundaries, key_mode="qjl"):
+    """K: [n, d] float64 (exact input values).  Returns a dict of per-vector arrays
+    ("n16"/"gamma16" are what the store holds for the given key mode)."""
+    if key_mode not in KEY_MODES:
+        raise ValueError("unknown key mode %r" % (key_mode,))
     K = np.asarray(K, dtype=np.float64)
     d = K.shape[-1]
     n = np.sqrt(np.sum(K * K, axis=-1))
@@ -42,12 +59,23 @@ def compress_keys(K, R, S, centroids, boundaries):
     idx = codebook.quantize_index(t, boundaries)
     chat = np.asarray(centroids)[idx]
     rho = t - chat
-    gamma = np.sqrt(np.sum(rho * rho, axis=-1))
-    y = rho @ S.T
-    z = (y >= 0.0).astype(np.int64)
+    if key_mode == "qjl":
+        gamma = np.sqrt(np.sum(rho * rho, axis=-1))
+        y = rho @ S.T
+        z = (y >= 0.0).astype(np.int64)
+        n_store = n
+    else:
+        gamma = np.zeros_like(n)
+        y = np.zeros_like(rho)
+        z = np.zeros(rho.shape, dtype=np.int64)
+        if key_mode == "mse":
+            n_store = n
+        else:
+            # ||c[idx]|| > 0: the centroids of an even number of levels are all nonzero
+            n_store = n * math.sqrt(d) / np.sqrt(np.sum(chat * chat, axis=-1))
     return {
         "n": n, "t": t, "idx": idx, "rho": rho, "gamma": gamma, "y": y, "z": z,
-        "n16": n.astype(np.float16), "gamma16": gamma.astype(np.float16),
+        "n16": n_store.astype(np.float16), "gamma16": gamma.astype(np.float16),
     }
 
 
@@ -89,7 +117,8 @@ def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     n_tok, H, d = K.shape
     out = {}
     for h in range(H):
-        ck = compress_keys(K[:, h], state.R[h], state.S[h], state.centroids, state.boundaries)
+        ck = compress_keys(K[:, h], state.R[h], state.S[h], state.centroids, state.boundaries,
+                           getattr(state, "key_mode", "qjl"))
         cv = compress_values(V[:, h], state.R[h], layout.v_bits, layout.group)
         lay.put_records(pool, layout, H, slots, h, {
             "idx": ck["idx"], "z": ck["z"], "n16": ck["n16"], "g16": ck["gamma16"],

@@ -52,9 +52,10 @@ def qjl_projection(seed, layer, head, d, m=None):
 class LayerState:
     """All state of one compressed layer: R and S per KV head plus the key codebook."""
 
-    def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian"):
+    def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian", key_mode="qjl"):
         self.seed, self.layer, self.n_kv_heads, self.d = seed, layer, n_kv_heads, d
         self.k_bits, self.v_bits, self.group, self.dist = k_bits, v_bits, group, dist
+        self.key_mode = key_mode  # "qjl", "mse" or "mse_nc" (see compress.compress_keys)
         self.R = np.stack([haar_rotation(seed, layer, h, d) for h in range(n_kv_heads)])
         self.S = np.stack([qjl_projection(seed, layer, h, d) for h in range(n_kv_heads)])
         self.centroids, self.boundaries = stored_codebook(k_bits, dist, d)

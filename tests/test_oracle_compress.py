@@ -119,3 +119,32 @@ def test_zero_norm_key():
     assert ck["n16"][0] == 0 and np.all(ck["t"] == 0)
     assert np.all(ck["idx"] == np.sum(b < 0))
     assert np.isfinite(ck["gamma"][0])
+
+
+def test_norm_corrected_keys_keep_their_norm_and_direction():
+    """Norm-corrected magnitude: the reconstruction (n16/sqrt d) R^T c[idx] has the
+    key's own norm (to the fp16 rounding of the stored value, 2^-11 relative) and
+    the direction of the plain codebook reconstruction (same codes)."""
+    rng = np.random.default_rng(31)
+    K = rng.standard_normal((300, D))
+    K[:, 7] *= 10.0
+    K[0] = 0.0  # zero-norm key: stored magnitude 0
+    st = state.LayerState(41, 0, 1, D, 3, 3, 32)
+    plain = compress.compress_keys(K, st.R[0], st.S[0], st.centroids, st.boundaries, "mse")
+    nc = compress.compress_keys(K, st.R[0], st.S[0], st.centroids, st.boundaries, "mse_nc")
+    assert np.array_equal(plain["idx"], nc["idx"])
+    kp = metrics.reconstruct_keys_mse(plain, st.R[0], st.centroids, D)
+    kn = metrics.reconstruct_keys_mse(nc, st.R[0], st.centroids, D)
+    n = np.linalg.norm(K, axis=1)
+    assert float(nc["n16"][0]) == 0.0 and not kn[0].any()
+    rel = np.abs(np.linalg.norm(kn[1:], axis=1) - n[1:]) / n[1:]
+    assert rel.max() <= 2.0 ** -11
+    assert np.max(np.abs(metrics.cosine_rows(kp[1:], kn[1:]) - 1.0)) < 1e-12
+    # the plain reconstruction is shorter on average (Lloyd-Max centroids shrink)
+    assert np.mean(np.linalg.norm(kp[1:], axis=1) / n[1:]) < 1.0
+
+
+def test_key_mode_rejects_unknown():
+    st = state.LayerState(41, 0, 1, D, 3, 3, 32)
+    with pytest.raises(ValueError):
+        compress.compress_keys(np.ones((2, D)), st.R[0], st.S[0], st.centroids, st.boundaries, "qjl_off")

@@ -10,8 +10,8 @@ from oracle import compress, decode, layout, metrics, state
 D = 128
 
 
-def _setup(k_bits=3, v_bits=2, B=2, Hq=4, Hkv=2, lens=(40, 17), seed=0, bypass=False):
-    st = state.LayerState(200 + seed, 0, Hkv, D, k_bits, v_bits, 32)
+def _setup(k_bits=3, v_bits=2, B=2, Hq=4, Hkv=2, lens=(40, 17), seed=0, bypass=False, key_mode="qjl"):
+    st = state.LayerState(200 + seed, 0, Hkv, D, k_bits, v_bits, 32, key_mode=key_mode)
     lay = layout.StoreLayout(D, k_bits, v_bits, 32, bypass=bypass)
     maxb = (max(lens) + 15) // 16
     table = np.random.default_rng(seed).permutation(B * maxb).reshape(B, maxb)
@@ -129,3 +129,26 @@ def test_quality_against_uncompressed_attention_reported():
     rel = math.sqrt(num / den)
     print("K4/V4 rel L2 vs exact attention: %.4f" % rel)
     assert rel < 0.35
+
+
+@pytest.mark.parametrize("key_mode", ["mse", "mse_nc"])
+def test_mse_key_modes_are_attention_over_codebook_reconstruction(key_mode):
+    """Without the residual projection the decode is textbook attention in the
+    original basis over k_hat = (n16/sqrt d) R^T c[idx] (no QJL term), with the
+    same values; the store holds zero sign bits and gamma = 0."""
+    st, lay, table, pool, lens, q, KV = _setup(k_bits=4, v_bits=3, key_mode=key_mode)
+    out = decode.decode(q, pool, lay, 2, table, lens, st)
+    rep = 2
+    for b, T in enumerate(lens):
+        for g in range(2):
+            ck, cv = KV[b][2][g]
+            assert not ck["z"].any() and not ck["gamma16"].any()
+            f = decode.gather(pool, lay, 2, table[b], T, g)
+            assert not f["z"].any() and not f["g16"].astype(np.float64).any()
+            Kh = metrics.reconstruct_keys_mse(ck, st.R[g], st.centroids, D)
+            Vh = metrics.reconstruct_values(cv, st.R[g], 32)
+            for h in range(g * rep, (g + 1) * rep):
+                s = Kh @ q[b, h] / math.sqrt(D)
+                w = np.exp(s - s.max())
+                ref = (w / w.sum()) @ Vh
+                assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * max(1.0, np.abs(ref).max())
