@@ -47,6 +47,8 @@ tq_status validate_config(const tq_layer_config* cfg) {
     return fail(TQ_ERR_UNSUPPORTED, "v_group %d not supported (only %d)", cfg->v_group, kGroup);
   if (cfg->dist != TQ_DIST_GAUSSIAN && cfg->dist != TQ_DIST_SPHERE)
     return fail(TQ_ERR_INVALID_ARGUMENT, "unknown codebook density %d", static_cast<int>(cfg->dist));
+  if (cfg->key_mode != TQ_KEY_QJL && cfg->key_mode != TQ_KEY_MSE && cfg->key_mode != TQ_KEY_MSE_NC)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "unknown key mode %d", static_cast<int>(cfg->key_mode));
   return TQ_OK;
 }
 

@@ -29,6 +29,7 @@ struct CompressArgs {
   const float* RT;  // [H][128][128], RT[h][j][i] = R_h[i][j]
   const float* ST;  // [H][128][128], ST[h][j][i] = S_h[i][j]
   int H;
+  int km;  // key mode: 0 QJL, 1 codebook only, 2 codebook only with norm-corrected magnitude
   unsigned block_bytes;
   unsigned off_kc, off_ks, off_kn, off_vc, off_vsz;
   float cent[16];
@@ -141,7 +142,9 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     const float rho = t - a.cent[idx];
     ck[i] = static_cast<unsigned char>(idx);
     srho[i] = rho;
-    const float g2 = wave_sum(rho * rho);
+    // squared norm of the residual (QJL) or of the centroid vector (norm correction)
+    const float gt = (a.km == 2) ? a.cent[idx] : rho;
+    const float g2 = wave_sum(gt * gt);
     if ((i & 63) == 0) red[2 + (i >> 6)] = g2;
     // values: group min/max over 32 lanes
     float mn = rv, mx = rv;
@@ -161,20 +164,24 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     }
   }
   __syncthreads();
-  {
-    float ay = 0.0f;
+  if (a.km == 0) {  // QJL residual signs (workgroup-uniform branch)
+    {
+      float ay = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) ay = fmaf(st[u], srho[32 * c + u], ay);
-    pk[c][i] = ay;
-  }
-  __syncthreads();
-  if (c == 0) {
-    const float y = (pk[0][i] + pk[1][i]) + (pk[2][i] + pk[3][i]);
-    const unsigned long long bal = __ballot(y >= 0.0f);
-    if ((i & 63) == 0) {
-      sbits[(i >> 6) * 2] = static_cast<unsigned>(bal);
-      sbits[(i >> 6) * 2 + 1] = static_cast<unsigned>(bal >> 32);
+      for (int u = 0; u < 32; ++u) ay = fmaf(st[u], srho[32 * c + u], ay);
+      pk[c][i] = ay;
     }
+    __syncthreads();
+    if (c == 0) {
+      const float y = (pk[0][i] + pk[1][i]) + (pk[2][i] + pk[3][i]);
+      const unsigned long long bal = __ballot(y >= 0.0f);
+      if ((i & 63) == 0) {
+        sbits[(i >> 6) * 2] = static_cast<unsigned>(bal);
+        sbits[(i >> 6) * 2 + 1] = static_cast<unsigned>(bal >> 32);
+      }
+    }
+  } else if (tid < 4) {
+    sbits[tid] = 0u;
   }
   __syncthreads();
   if (c != 0) return;  // lanes 0..127 store the record
@@ -206,8 +213,10 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     const int blk = i - 64;
     *reinterpret_cast<unsigned*>(base + a.off_ks + (blk * 16 + off) * 4) = sbits[blk];
   } else if (i == 68) {
-    const __half hn = __float2half_rn(n);
-    const __half hg = __float2half_rn(sqrtf(red[2] + red[3]));
+    const float g2 = red[2] + red[3];
+    // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction; gamma 0 without QJL
+    const __half hn = __float2half_rn(a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n);
+    const __half hg = __float2half_rn(a.km == 0 ? sqrtf(g2) : 0.0f);
     const unsigned w = static_cast<unsigned>(__half_as_ushort(hn)) |
                        (static_cast<unsigned>(__half_as_ushort(hg)) << 16);
     *reinterpret_cast<unsigned*>(base + a.off_kn + off * 4) = w;
@@ -293,6 +302,7 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
     a.ST = L->dST;
     a.H = L->cfg.n_kv_heads;
     a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
+    a.km = static_cast<int>(L->cfg.key_mode);
     a.off_kc = static_cast<unsigned>(L->lay.off_kc);
     a.off_ks = static_cast<unsigned>(L->lay.off_ks);
     a.off_kn = static_cast<unsigned>(L->lay.off_kn);

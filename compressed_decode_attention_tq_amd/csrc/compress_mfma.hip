@@ -56,6 +56,7 @@ struct CArgs {
   long long n_tokens;
   long long n_tiles;
   int H;
+  int km;  // key mode: 0 QJL, 1 codebook only, 2 codebook only with norm-corrected magnitude
   unsigned block_bytes;
   float cent[16];
   float bnd[16];
@@ -353,7 +354,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         }
         const int idx = (t > 0.0f) ? HALF + cnt : HALF - 1 - cnt;
         rho[r] = t - ((t > 0.0f) ? cp : -cp);
-        g2 = fmaf(rho[r], rho[r], g2);
+        // squared norm of the residual (QJL) or of the centroid vector (norm correction)
+        const float gt = (a.km == 2) ? cp : rho[r];
+        g2 = fmaf(gt, gt, g2);
         codes |= static_cast<unsigned>(idx) << (KB * r);
       }
       g2 = rows_sum(g2);
@@ -366,8 +369,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         rl[r] = residual_pair(rho[2 * r], rho[2 * r + 1], rh[r]);
       }
       const int d0 = 16 * w + 4 * kg;
-      *reinterpret_cast<u32x2*>(&orh[col][d0]) = rh;
-      *reinterpret_cast<u32x2*>(&orl[col][d0]) = rl;
+      if (a.km == 0) {  // the residual feeds the QJL projection only
+        *reinterpret_cast<u32x2*>(&orh[col][d0]) = rh;
+        *reinterpret_cast<u32x2*>(&orl[col][d0]) = rl;
+      }
       // key codes of dims d0..d0+3 = elements e0..e0+3 of block w/2 (4 KB bits)
       const int b = w >> 1, e0 = 16 * (w & 1) + 4 * kg;
       unsigned char* rec = &img[PG::kc + (b * 16 + col) * 4 * KB];
@@ -403,21 +408,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
     // ---- C: y = S rho -> sign bits; value codes; per-token metadata
     {
-      floatx4 Y = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const half8 sh = __builtin_bit_cast(half8, s_hi[w][s][lane]);
-        const half8 rh = *reinterpret_cast<const half8*>(&orh[col][32 * s + 8 * kg]);
-        const half8 rl = *reinterpret_cast<const half8*>(&orl[col][32 * s + 8 * kg]);
-        Y = mfma_h(sh, rh, Y);
-        Y = mfma_h(sh, rl, Y);
-        Y = mfma_h(S1[s], rh, Y);
-      }
       const int G = w >> 1;
-      // sign nibble of dims d0..d0+3 (bit r = dim d0 + r); two row groups make a byte
+      // sign nibble of dims d0..d0+3 (bit r = dim d0 + r); two row groups make a
+      // byte (zero bits without QJL)
       unsigned nib = 0;
+      if (a.km == 0) {
+        floatx4 Y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nib |= (Y[r] >= 0.0f ? 1u : 0u) << r;
+        for (int s = 0; s < 4; ++s) {
+          const half8 sh = __builtin_bit_cast(half8, s_hi[w][s][lane]);
+          const half8 rh = *reinterpret_cast<const half8*>(&orh[col][32 * s + 8 * kg]);
+          const half8 rl = *reinterpret_cast<const half8*>(&orl[col][32 * s + 8 * kg]);
+          Y = mfma_h(sh, rh, Y);
+          Y = mfma_h(sh, rl, Y);
+          Y = mfma_h(S1[s], rh, Y);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nib |= (Y[r] >= 0.0f ? 1u : 0u) << r;
+      }
       unsigned ea = nib, eb = nib;
       swap16u(ea, eb);  // even row groups: ea = own, eb = the next group's nibble
       if ((kg & 1) == 0)
@@ -493,8 +501,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         float g2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) g2 += gpart[i][col];
-        const unsigned short g16 = __half_as_ushort(__float2half_rn(sqrtf(g2)));
-        const unsigned short n16 = __half_as_ushort(__float2half_rn(sqrtf(k2)));
+        // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction; gamma 0 without QJL
+        const float n = sqrtf(k2);
+        const unsigned short g16 = __half_as_ushort(__float2half_rn(a.km == 0 ? sqrtf(g2) : 0.0f));
+        const unsigned short n16 =
+            __half_as_ushort(__float2half_rn(a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n));
         *reinterpret_cast<unsigned*>(&img[PG::kn + col * 4]) =
             static_cast<unsigned>(n16) | (static_cast<unsigned>(g16) << 16);
       }
@@ -616,6 +627,7 @@ tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, 
   a.n_tokens = n_tokens;
   a.n_tiles = (n_tokens + 15) / 16;
   a.H = L->cfg.n_kv_heads;
+  a.km = static_cast<int>(L->cfg.key_mode);
   a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
   for (int i = 0; i < 16; ++i) {
     a.cent[i] = L->centroids[i];

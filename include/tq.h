@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum {
   TQ_OK = 0,
@@ -115,6 +115,23 @@ int tq_abi_version(void);
 tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids,
                             double* boundaries, double* mse);
 
+/* Key estimator of a compressed layer.
+ *   TQ_KEY_QJL     codebook codes plus the 1-bit QJL residual signs and the
+ *                  residual norm gamma ("How 0xsero/turboquant works",
+ *                  "Compression Pipeline" and "Key Storage and Attention Scoring").
+ *   TQ_KEY_MSE     codebook codes and the vector norm only: no residual signs
+ *                  (stored as zero bits) and gamma stored as 0, so the score
+ *                  is the plain inner product with the codebook reconstruction
+ *                  ("turbo-attn 0.24.0", "How it works": normalise, store one
+ *                  magnitude, quantise each rotated coordinate to a shared codebook).
+ *   TQ_KEY_MSE_NC  as TQ_KEY_MSE, with the stored magnitude norm-corrected to
+ *                  n * sqrt(d) / ||c[idx]||, so that the reconstruction
+ *                  (n16 / sqrt d) R^T c[idx] has the key's own norm ("turbo-attn
+ *                  0.24.0", "Configuration", TKV_K_NC: norm-correction of K reads).
+ * The page layout is the same for all three (the sign field is kept), so the
+ * decode kernels serve every mode unchanged. */
+typedef enum { TQ_KEY_QJL = 0, TQ_KEY_MSE = 1, TQ_KEY_MSE_NC = 2 } tq_key_mode;
+
 typedef struct {
   int head_dim;             /* d; must be 128                                   */
   int n_kv_heads;           /* KV heads of the layer, >= 1                      */
@@ -126,6 +143,7 @@ typedef struct {
   tq_dist dist;             /* key codebook density                             */
   unsigned long long seed;  /* random-state seed                                */
   int bypass;               /* 1: uncompressed bf16 layer (bits/dist ignored)   */
+  tq_key_mode key_mode;     /* key estimator (compressed layers)                */
 } tq_layer_config;
 
 /* Opaque per-layer state.  Holds, on the device, for every KV head g:

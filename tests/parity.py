@@ -43,11 +43,19 @@ def fields_at(pool_bytes, layout, n_heads, slots, head):
     return lay.get_records(pool_bytes, layout, n_heads, slots, head)
 
 
-def compare_compress(gpu, ck, cv, S, boundaries, V, v_bits, group=32):
-    """Apply the protocol to one head's records.  Returns a dict of counts."""
+def compare_compress(gpu, ck, cv, S, boundaries, V, v_bits, group=32, centroids=None, key_mode="qjl"):
+    """Apply the protocol to one head's records.  Returns a dict of counts.
+
+    With the norm-corrected magnitude (key_mode "mse_nc") the stored n16 depends on
+    the codes, so for a vector whose codes differ (inside the decision band) the
+    expected value is recomputed from the GPU's codes, as the signs are."""
     n, d = ck["idx"].shape
     st = {"vectors": n}
-    st["n16_ulps"] = int(f16_ulps(gpu["n16"], ck["n16"]).max(initial=0))
+    n16_ref = ck["n16"]
+    if key_mode == "mse_nc":
+        chat = np.asarray(centroids)[gpu["idx"]]
+        n16_ref = (ck["n"] * math.sqrt(d) / np.sqrt(np.sum(chat * chat, axis=-1))).astype(np.float16)
+    st["n16_ulps"] = int(f16_ulps(gpu["n16"], n16_ref).max(initial=0))
     st["g16_ulps"] = int(f16_ulps(gpu["g16"], ck["gamma16"]).max(initial=0))
     # key codes
     kmis = gpu["idx"] != ck["idx"]

@@ -23,9 +23,9 @@ def say(*a):
 
 
 # ------------------------------------------------------------------ compress
-def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16"):
+def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16", key_mode=0):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer))
+    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer, key_mode=key_mode))
     k = torch.from_numpy(np.ascontiguousarray(K)).to("cuda", tdt)
     v = torch.from_numpy(np.ascontiguousarray(V)).to("cuda", tdt)
     pool = layer_obj.new_pool(num_blocks)
@@ -42,7 +42,8 @@ def _check_compress(gpu_pool, res, st, layout, n_heads, slots, V, kb, vb):
     for h in range(n_heads):
         f = parity.fields_at(gpu_pool, layout, n_heads, sl, h)
         ck, cv = res[h]
-        stats = parity.compare_compress(f, ck, cv, st.S[h], st.boundaries, V[keep][:, h], vb)
+        stats = parity.compare_compress(f, ck, cv, st.S[h], st.boundaries, V[keep][:, h], vb,
+                                        centroids=st.centroids, key_mode=st.key_mode)
         print("head", h, stats)
         parity.assert_compress_ok(stats)
 
@@ -360,4 +361,65 @@ def test_end_to_end_gpu_compress_then_decode():
     err = parity.rel_l2(out.cpu().numpy(), ref)
     print("end-to-end rel L2 %.3e" % err)
     assert err <= 2e-3
+    layer.close()
+
+
+KEY_MODE_NAMES = {tq.KEY_QJL: "qjl", tq.KEY_MSE: "mse", tq.KEY_MSE_NC: "mse_nc"}
+
+
+@pytest.mark.parametrize("key_mode,kb,vb,n,dtype", [
+    (tq.KEY_MSE, 4, 4, 700, "bf16"), (tq.KEY_MSE_NC, 3, 2, 700, "bf16"),
+    (tq.KEY_MSE_NC, 2, 3, 1024, "f32"), (tq.KEY_MSE, 3, 3, 40, "bf16")])
+def test_compress_key_modes(key_mode, kb, vb, n, dtype):
+    """Keys without the residual projection (plain and norm-corrected magnitude):
+    the matrix-core compressor (bf16: whole pages and a ragged last tile) and the
+    per-token one (fp32 inputs; a 40-token append)."""
+    torch = _torch()
+    say("compress key mode", key_mode, kb, vb, n, dtype)
+    H = 8 if dtype == "bf16" else 1
+    K, V = synth.kv_host(170 + key_mode, n, H, dtype=dtype, outliers=4 if dtype == "bf16" else 0)
+    slots = np.arange(n, dtype=np.int64)
+    nb = (n + 15) // 16
+    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, 230, layer=key_mode, dtype=dtype, key_mode=key_mode)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, H, kb, vb, 230, layer=key_mode,
+                                                key_mode=KEY_MODE_NAMES[key_mode])
+    _check_compress(gpu, res, st, layout, H, slots, V, kb, vb)
+    # no residual signs and gamma 0 in the store
+    for h in range(H):
+        f = parity.fields_at(gpu, layout, H, slots, h)
+        assert not np.asarray(f["z"]).any() and not np.asarray(f["g16"], np.float64).any()
+
+
+@pytest.mark.parametrize("key_mode", [tq.KEY_MSE, tq.KEY_MSE_NC])
+def test_end_to_end_key_modes(key_mode):
+    """GPU compress -> GPU decode against the oracle for the key modes without QJL
+    (the decode kernels read the same page layout; gamma 0 removes the QJL term)."""
+    torch = _torch()
+    say("end to end key mode", key_mode)
+    B, Hq, Hkv, T = 3, 16, 4, 613
+    lens = np.array([T, 400, 97], np.int32)
+    maxb = (T + 15) // 16
+    table = synth.block_table(270 + key_mode, B, maxb, "random")
+    K, V = synth.kv_host(180 + key_mode, B * T, Hkv, outliers=4)
+    pos = np.tile(np.arange(T), B)
+    seq = np.repeat(np.arange(B), T)
+    slots = table[seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    st, layout, opool, _ = parity.oracle_store(K, V, slots, B * maxb, Hkv, 4, 3, 270, keep=False,
+                                               key_mode=KEY_MODE_NAMES[key_mode])
+    q = synth.queries_host(270, B, Hq)
+    ref = parity.oracle_decode(q.astype(np.float64), opool, layout, Hkv, table, lens, st)
+    layer = tq.Layer(tq.config(Hkv, 4, 3, seed=270, key_mode=key_mode))
+    pool = layer.new_pool(B * maxb)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    qt = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(lens).cuda()
+    out = tq.decode_attn(layer, qt, pool, bt, sl, T)
+    out_o = tq.decode_attn(layer, qt, torch.from_numpy(opool).cuda(), bt, sl, T)
+    torch.cuda.synchronize()
+    same = parity.rel_l2(out_o.cpu().numpy(), ref)
+    err = parity.rel_l2(out.cpu().numpy(), ref)
+    print("key mode %d: decode on oracle store rel L2 %.3e, end-to-end %.3e" % (key_mode, same, err))
+    assert same <= 1e-3 and err <= 2e-3
     layer.close()

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tq_abi_version() == 1
+    assert lib.tq_abi_version() == 2
 
 
 @pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
@@ -80,7 +80,8 @@ def test_config_errors():
         (dict(k_bits=1), tq.ERR_UNSUPPORTED), (dict(v_bits=1), tq.ERR_UNSUPPORTED),
         (dict(v_group=16), tq.ERR_UNSUPPORTED), (dict(block_size=32), tq.ERR_UNSUPPORTED),
         (dict(n_kv_heads=0), tq.ERR_INVALID_ARGUMENT), (dict(layer=-1), tq.ERR_INVALID_ARGUMENT),
-        (dict(dist=7), tq.ERR_INVALID_ARGUMENT),
+        (dict(dist=7), tq.ERR_INVALID_ARGUMENT), (dict(key_mode=3), tq.ERR_INVALID_ARGUMENT),
+        (dict(key_mode=-1), tq.ERR_INVALID_ARGUMENT),
     ]
     for kw, want in bad:
         args = dict(n_kv_heads=8)
@@ -107,3 +108,11 @@ def test_null_and_bad_arguments_on_device_entry_points():
                               vp(1), tq.F32, vp(256), 1 << 20, None) == tq.ERR_INVALID_ARGUMENT
     assert lib.tq_layer_destroy(None) == tq.OK
     assert lib.tq_layer_create(None, None, ctypes.byref(vp())) == tq.ERR_INVALID_ARGUMENT
+
+
+def test_key_modes_share_the_page_layout():
+    """The key modes change what is stored in the fields, not the fields."""
+    for kb, vb in ((2, 3), (4, 4)):
+        ref = tq.store_layout(tq.config(8, kb, vb))
+        for km in (tq.KEY_MSE, tq.KEY_MSE_NC):
+            assert tq.store_layout(tq.config(8, kb, vb, key_mode=km)) == ref
