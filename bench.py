@@ -210,11 +210,11 @@ def decode_workload(torch, tq, synth, args):
     return res, ctx
 
 
-def compress_workload(torch, tq, synth, args):
+def compress_workload(torch, tq, synth, args, key_mode=0):
     W = synth.WORKLOADS[3]
     sd = synth.seeds(3)
     N, H = W["N"], W["Hkv"]
-    layer = tq.Layer(tq.config(H, W["k_bits"], W["v_bits"], seed=sd["state"]))
+    layer = tq.Layer(tq.config(H, W["k_bits"], W["v_bits"], seed=sd["state"], key_mode=key_mode))
     k, v = synth.kv_device(sd["data"], N, H)
     pool = layer.new_pool(N // 16)
     slots = torch.arange(N, dtype=torch.int64, device="cuda")
@@ -236,6 +236,10 @@ def compress_workload(torch, tq, synth, args):
     avg_s = c_ms / max(c_n, 1) / 1e3
     layer.close()
     del k, v, pool
+    if key_mode:
+        return {"workload": W["name"], "key_mode": ["qjl", "mse", "mse_nc"][key_mode], "ms": round(ms, 4),
+                "mtok_s": round(N / (ms / 1e3) / 1e6, 2), "gbs": round(nbytes / avg_s / 1e9, 1),
+                "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
     return {"workload": W["name"], "tokens": N, "kv_heads": H, "k_bits": W["k_bits"], "v_bits": W["v_bits"],
             "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
@@ -440,6 +444,10 @@ def main():
     if args.all_configs:
         log("tiny, long-context and serving workloads")
         extra = extra_workloads(torch, tq, synth, args)
+        if not args.no_compress:
+            log("compress workload, key modes without QJL")
+            extra["fused-compress-key-mse"] = compress_workload(torch, tq, synth, args, key_mode=tq.KEY_MSE)
+            extra["fused-compress-key-mse-nc"] = compress_workload(torch, tq, synth, args, key_mode=tq.KEY_MSE_NC)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
