@@ -30,6 +30,7 @@ MASK64 = (1 << 64) - 1
 GOLDEN_GAMMA = 0x9E3779B97F4A7C15
 TAG_ROTATION = 1
 TAG_PROJECTION = 2
+TAG_SIGNS = 3  # random sign diagonal of the structured (Hadamard) rotation
 
 
 def mix64(z):
@@ -70,3 +71,10 @@ def gaussians(seed, layer, head, tag, count):
         out.append(r * math.cos(theta))
         out.append(r * math.sin(theta))
     return out[:count]
+
+
+def random_signs(seed, layer, head, count):
+    """count values in {+1, -1} from the tag-3 stream: +1 when the top bit of the
+    next SplitMix64 output is 0."""
+    g = SplitMix64(stream_key(seed, layer, head, TAG_SIGNS))
+    return [1.0 if (g.next_u64() >> 63) == 0 else -1.0 for _ in range(count)]

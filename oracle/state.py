@@ -12,6 +12,12 @@ makes the factor unique and Haar distributed.
 S: an m x d matrix of i.i.d. N(0,1) entries from the projection stream, m = d
 (the QJL residual-sign projection of the same sections).
 
+Structured alternative ("turbo-attn 0.24.0", "How it works": rotate each KV
+vector with a fast Walsh-Hadamard transform): R = H D / sqrt(d), H the
+Sylvester-ordered Hadamard matrix, H[i][j] = (-1)^popcount(i & j), and D a
+diagonal of random signs from the tag-3 stream (a randomised Hadamard
+transform).  Every entry of R is +-1/sqrt(d).
+
 Both are stored, and used by every consumer, as float32-rounded values; the
 oracle then computes in float64 on exactly those numbers.
 
@@ -43,6 +49,35 @@ def haar_rotation(seed, layer, head, d):
     return haar_rotation_f64(seed, layer, head, d).astype(np.float32).astype(np.float64)
 
 
+def sylvester_hadamard(d):
+    """H[i][j] = (-1)^popcount(i & j) for d a power of two."""
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    par = np.zeros_like(bits)
+    while bits.any():
+        par ^= bits & 1
+        bits >>= 1
+    return np.where(par == 1, -1.0, 1.0)
+
+
+def hadamard_rotation(seed, layer, head, d):
+    """float32-rounded randomised Hadamard rotation H D / sqrt(d), as float64 values."""
+    signs = np.array(rng.random_signs(seed, layer, head, d))
+    r = sylvester_hadamard(d) * signs[None, :] / np.sqrt(d)
+    return r.astype(np.float32).astype(np.float64)
+
+
+ROTATIONS = ("haar", "hadamard")
+
+
+def rotation(kind, seed, layer, head, d):
+    if kind == "haar":
+        return haar_rotation(seed, layer, head, d)
+    if kind == "hadamard":
+        return hadamard_rotation(seed, layer, head, d)
+    raise ValueError("unknown rotation %r" % (kind,))
+
+
 def qjl_projection(seed, layer, head, d, m=None):
     m = d if m is None else m
     s = gaussian_matrix(seed, layer, head, rng.TAG_PROJECTION, m, d)
@@ -52,11 +87,13 @@ def qjl_projection(seed, layer, head, d, m=None):
 class LayerState:
     """All state of one compressed layer: R and S per KV head plus the key codebook."""
 
-    def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian", key_mode="qjl"):
+    def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian", key_mode="qjl",
+                 rotation_kind="haar"):
         self.seed, self.layer, self.n_kv_heads, self.d = seed, layer, n_kv_heads, d
         self.k_bits, self.v_bits, self.group, self.dist = k_bits, v_bits, group, dist
         self.key_mode = key_mode  # "qjl", "mse" or "mse_nc" (see compress.compress_keys)
-        self.R = np.stack([haar_rotation(seed, layer, h, d) for h in range(n_kv_heads)])
+        self.rotation_kind = rotation_kind  # "haar" or "hadamard"
+        self.R = np.stack([rotation(rotation_kind, seed, layer, h, d) for h in range(n_kv_heads)])
         self.S = np.stack([qjl_projection(seed, layer, h, d) for h in range(n_kv_heads)])
         self.centroids, self.boundaries = stored_codebook(k_bits, dist, d)
 

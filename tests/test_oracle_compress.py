@@ -148,3 +148,15 @@ def test_key_mode_rejects_unknown():
     st = state.LayerState(41, 0, 1, D, 3, 3, 32)
     with pytest.raises(ValueError):
         compress.compress_keys(np.ones((2, D)), st.R[0], st.S[0], st.centroids, st.boundaries, "qjl_off")
+
+
+def test_hadamard_rotation_reconstruction_cosine():
+    """The randomised Hadamard rotation spreads coordinates like the Haar one:
+    the mean cosine of the 3-bit codebook reconstruction stays near sqrt(1 - D_3)."""
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((2000, D))
+    K[:, 3] *= 10.0
+    st = state.LayerState(77, 0, 1, D, 3, 3, 32, rotation_kind="hadamard")
+    ck = compress.compress_keys(K, st.R[0], st.S[0], st.centroids, st.boundaries)
+    cos = metrics.cosine_rows(K, metrics.reconstruct_keys_mse(ck, st.R[0], st.centroids, D)).mean()
+    assert abs(cos - math.sqrt(1.0 - 0.03455)) < 0.004

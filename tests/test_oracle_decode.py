@@ -10,8 +10,10 @@ from oracle import compress, decode, layout, metrics, state
 D = 128
 
 
-def _setup(k_bits=3, v_bits=2, B=2, Hq=4, Hkv=2, lens=(40, 17), seed=0, bypass=False, key_mode="qjl"):
-    st = state.LayerState(200 + seed, 0, Hkv, D, k_bits, v_bits, 32, key_mode=key_mode)
+def _setup(k_bits=3, v_bits=2, B=2, Hq=4, Hkv=2, lens=(40, 17), seed=0, bypass=False, key_mode="qjl",
+           rotation_kind="haar"):
+    st = state.LayerState(200 + seed, 0, Hkv, D, k_bits, v_bits, 32, key_mode=key_mode,
+                          rotation_kind=rotation_kind)
     lay = layout.StoreLayout(D, k_bits, v_bits, 32, bypass=bypass)
     maxb = (max(lens) + 15) // 16
     table = np.random.default_rng(seed).permutation(B * maxb).reshape(B, maxb)
@@ -43,10 +45,11 @@ def test_split_k_equals_one_pass():
         assert np.max(np.abs(one - two)) < 1e-12
 
 
-def test_equals_attention_over_reconstructed_keys():
+@pytest.mark.parametrize("rotation_kind", ["haar", "hadamard"])
+def test_equals_attention_over_reconstructed_keys(rotation_kind):
     """Decode in the rotated space == textbook attention in the original basis over
     k_hat = (n/sqrt d) R^T (c[idx] + sqrt(pi/2)/m gamma S^T sigma) and v_hat = R^T v_hat'."""
-    st, lay, table, pool, lens, q, KV = _setup(k_bits=4, v_bits=3)
+    st, lay, table, pool, lens, q, KV = _setup(k_bits=4, v_bits=3, rotation_kind=rotation_kind)
     out = decode.decode(q, pool, lay, 2, table, lens, st)
     rep = 2
     for b, T in enumerate(lens):

@@ -78,3 +78,42 @@ def test_projection_gaussian():
     # independent of the same head's rotation stream
     g = state.gaussian_matrix(200, 0, 0, rng.TAG_ROTATION, 128, 128)
     assert abs(np.corrcoef(g.ravel(), z)[0, 1]) < 5 / np.sqrt(z.size)
+
+
+def _fwht(x):
+    """In-place fast Walsh-Hadamard butterflies (natural / Sylvester order), unnormalised."""
+    x = np.array(x, dtype=np.float64)
+    h = 1
+    while h < len(x):
+        for i in range(0, len(x), 2 * h):
+            a = x[i:i + h].copy()
+            b = x[i + h:i + 2 * h].copy()
+            x[i:i + h] = a + b
+            x[i + h:i + 2 * h] = a - b
+        h *= 2
+    return x
+
+
+@pytest.mark.parametrize("d", [2, 8, 128])
+def test_hadamard_rotation_is_the_fast_transform(d):
+    """R x = FWHT(D x) / sqrt(d) for the butterfly algorithm (a different
+    computation from the matrix definition), R is orthogonal, and every entry
+    is +-1/sqrt(d) in float32."""
+    r = state.hadamard_rotation(200, 3, 1, d)
+    signs = np.array(rng.random_signs(200, 3, 1, d))
+    x = np.random.default_rng(d).standard_normal(d)
+    assert np.abs(r @ x - _fwht(signs * x) / np.sqrt(d)).max() < 1e-6 * np.abs(x).sum()
+    assert np.abs(r @ r.T - np.eye(d)).max() < 1e-6
+    assert np.all(np.abs(r) == np.float32(1.0 / np.sqrt(d)))
+    if d == 2:
+        assert np.array_equal(np.sign(r) * signs[None, :], np.array([[1.0, 1.0], [1.0, -1.0]]))
+
+
+def test_random_signs_balanced_and_keyed():
+    s = np.array(rng.random_signs(9, 2, 4, 4096))
+    assert set(np.unique(s)) == {-1.0, 1.0}
+    assert abs(s.mean()) < 5 / np.sqrt(s.size)
+    assert rng.random_signs(9, 2, 4, 64) != rng.random_signs(9, 2, 5, 64)
+    # first output of the tag-3 stream: its top bit is the first sign
+    g = rng.SplitMix64(rng.stream_key(9, 2, 4, rng.TAG_SIGNS))
+    assert s[0] == (1.0 if (g.next_u64() >> 63) == 0 else -1.0)
