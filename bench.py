@@ -210,11 +210,12 @@ def decode_workload(torch, tq, synth, args):
     return res, ctx
 
 
-def compress_workload(torch, tq, synth, args, key_mode=0):
+def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
     W = synth.WORKLOADS[3]
     sd = synth.seeds(3)
     N, H = W["N"], W["Hkv"]
-    layer = tq.Layer(tq.config(H, W["k_bits"], W["v_bits"], seed=sd["state"], key_mode=key_mode))
+    layer = tq.Layer(tq.config(H, W["k_bits"], W["v_bits"], seed=sd["state"], key_mode=key_mode,
+                               rotation=rotation))
     k, v = synth.kv_device(sd["data"], N, H)
     pool = layer.new_pool(N // 16)
     slots = torch.arange(N, dtype=torch.int64, device="cuda")
@@ -236,8 +237,9 @@ def compress_workload(torch, tq, synth, args, key_mode=0):
     avg_s = c_ms / max(c_n, 1) / 1e3
     layer.close()
     del k, v, pool
-    if key_mode:
-        return {"workload": W["name"], "key_mode": ["qjl", "mse", "mse_nc"][key_mode], "ms": round(ms, 4),
+    if key_mode or rotation:
+        return {"workload": W["name"], "key_mode": ["qjl", "mse", "mse_nc"][key_mode],
+                "rotation": ["haar", "hadamard"][rotation], "ms": round(ms, 4),
                 "mtok_s": round(N / (ms / 1e3) / 1e6, 2), "gbs": round(nbytes / avg_s / 1e9, 1),
                 "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
     return {"workload": W["name"], "tokens": N, "kv_heads": H, "k_bits": W["k_bits"], "v_bits": W["v_bits"],
@@ -448,6 +450,10 @@ def main():
             log("compress workload, key modes without QJL")
             extra["fused-compress-key-mse"] = compress_workload(torch, tq, synth, args, key_mode=tq.KEY_MSE)
             extra["fused-compress-key-mse-nc"] = compress_workload(torch, tq, synth, args, key_mode=tq.KEY_MSE_NC)
+            log("compress workload, randomised Hadamard rotation")
+            extra["fused-compress-hadamard"] = compress_workload(torch, tq, synth, args, rotation=tq.ROT_HADAMARD)
+            extra["fused-compress-hadamard-key-mse-nc"] = compress_workload(
+                torch, tq, synth, args, key_mode=tq.KEY_MSE_NC, rotation=tq.ROT_HADAMARD)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")

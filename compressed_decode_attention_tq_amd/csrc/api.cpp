@@ -49,6 +49,8 @@ tq_status validate_config(const tq_layer_config* cfg) {
     return fail(TQ_ERR_INVALID_ARGUMENT, "unknown codebook density %d", static_cast<int>(cfg->dist));
   if (cfg->key_mode != TQ_KEY_QJL && cfg->key_mode != TQ_KEY_MSE && cfg->key_mode != TQ_KEY_MSE_NC)
     return fail(TQ_ERR_INVALID_ARGUMENT, "unknown key mode %d", static_cast<int>(cfg->key_mode));
+  if (cfg->rotation != TQ_ROT_HAAR && cfg->rotation != TQ_ROT_HADAMARD)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "unknown rotation family %d", static_cast<int>(cfg->rotation));
   return TQ_OK;
 }
 
@@ -93,7 +95,10 @@ tq_status build_state(const tq_layer_config* cfg, std::vector<float>* R, std::ve
   std::vector<double> tmp(static_cast<size_t>(d) * d);
   for (int h = 0; h < H; ++h) {
     if (R) {
-      haar_rotation(cfg->seed, cfg->layer, h, d, tmp.data());
+      if (!cfg->bypass && cfg->rotation == TQ_ROT_HADAMARD)
+        hadamard_rotation(cfg->seed, cfg->layer, h, d, tmp.data());
+      else
+        haar_rotation(cfg->seed, cfg->layer, h, d, tmp.data());
       for (size_t i = 0; i < tmp.size(); ++i) (*R)[h * tmp.size() + i] = static_cast<float>(tmp[i]);
     }
     if (S) {
@@ -279,6 +284,7 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
       return static_cast<unsigned short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
     };
     auto bf16_val = [](unsigned short b) { return __builtin_bit_cast(float, static_cast<unsigned>(b) << 16); };
+    if (cfg->rotation == TQ_ROT_HADAMARD) L->r_scale = std::fabs(R[0]);
     const size_t nop = static_cast<size_t>(H) * 8 * kOpSets * 4 * 64 * 8;
     std::vector<unsigned short> opa(nop);
     for (int h = 0; h < H; ++h)
@@ -289,9 +295,11 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
               const int row = 16 * w + l % 16, col = 32 * ks + 8 * (l / 16) + j;
               const float r = R[(static_cast<size_t>(h) * d + row) * d + col];
               const float sv = S[(static_cast<size_t>(h) * d + row) * d + col];
-              const unsigned short r0 = bf16_rne(r);
-              const unsigned short r1 = bf16_rne(r - bf16_val(r0));
-              const unsigned short r2 = bf16_rne(r - bf16_val(r0) - bf16_val(r1));
+              // Hadamard: the exact sign pattern (bf16 +-1), the magnitude applied after
+              const bool had = cfg->rotation == TQ_ROT_HADAMARD;
+              const unsigned short r0 = had ? bf16_rne(r < 0.0f ? -1.0f : 1.0f) : bf16_rne(r);
+              const unsigned short r1 = had ? 0 : bf16_rne(r - bf16_val(r0));
+              const unsigned short r2 = had ? 0 : bf16_rne(r - bf16_val(r0) - bf16_val(r1));
               const _Float16 s0 = static_cast<_Float16>(sv);
               const _Float16 s1 = static_cast<_Float16>(sv - static_cast<float>(s0));
               const unsigned short v[kOpSets] = {r0, r1, r2, __builtin_bit_cast(unsigned short, s0),

@@ -57,6 +57,7 @@ struct CArgs {
   long long n_tiles;
   int H;
   int km;  // key mode: 0 QJL, 1 codebook only, 2 codebook only with norm-corrected magnitude
+  float rscale;  // Hadamard layers: |R_ij| (the A operand holds the +-1 pattern)
   unsigned block_bytes;
   float cent[16];
   float bnd[16];
@@ -191,7 +192,10 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // page stores in between).  When a store was scattered or a copy skipped within
 // that window, the wait counts only the copies known to follow, which is never
 // more than what is outstanding.
-template <int KB, int VB, int P>
+//
+// HAD: the layer's rotation is a randomised Hadamard matrix, all entries
+// +-rscale: R k = rscale (sign pattern) k, one exact bf16 pass instead of three.
+template <int KB, int VB, int P, bool HAD>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
   using PG = Page<KB, VB>;
   constexpr int HALF = 1 << (KB - 1);  // codebook levels per sign
@@ -211,15 +215,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ __attribute__((aligned(16))) u32x4 s_hi[8][4][64];  // S_hi operands per wave and K-step
 
   // ---- this wave's R and S operands (row tile w), kept for the whole launch
-  bf16x8 R0[4], R1[4], R2[4];
+  bf16x8 R0[4], R1[HAD ? 1 : 4], R2[HAD ? 1 : 4];
   half8 S1[4];
   {
     const u32x4* op = a.opa + static_cast<size_t>(h * 8 + w) * kOpSets * 4 * 64 + lane0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       R0[s] = __builtin_bit_cast(bf16x8, op[(0 * 4 + s) * 64]);
-      R1[s] = __builtin_bit_cast(bf16x8, op[(1 * 4 + s) * 64]);
-      R2[s] = __builtin_bit_cast(bf16x8, op[(2 * 4 + s) * 64]);
+      if constexpr (!HAD) {
+        R1[s] = __builtin_bit_cast(bf16x8, op[(1 * 4 + s) * 64]);
+        R2[s] = __builtin_bit_cast(bf16x8, op[(2 * 4 + s) * 64]);
+      }
       s_hi[w][s][lane0] = op[(3 * 4 + s) * 64];
       S1[s] = __builtin_bit_cast(half8, op[(4 * 4 + s) * 64]);
     }
@@ -227,7 +233,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // Consume the operands here so that the compiler's wait for these loads is
   // not placed inside the tile loop, where it would also drain the copy ring.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(R0[s]), "v"(R1[s]), "v"(R2[s]), "v"(S1[s]));
+  for (int s = 0; s < 4; ++s) {
+    asm volatile("" ::"v"(R0[s]), "v"(S1[s]));
+    if constexpr (!HAD) asm volatile("" ::"v"(R1[s]), "v"(R2[s]));
+  }
   wait_vmcnt<0>();
 
   // K/V rows of one tile into ring slot `slot`: waves 0-3 copy K tokens 4w..4w+3,
@@ -313,10 +322,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       T = mfma_b(R0[s], kb, T);
       V = mfma_b(R0[s], vb, V);
       NK = mfma_b(kb, kb, NK);
-      T = mfma_b(R1[s], kb, T);
-      V = mfma_b(R1[s], vb, V);
-      T = mfma_b(R2[s], kb, T);
-      V = mfma_b(R2[s], vb, V);
+      if constexpr (!HAD) {
+        T = mfma_b(R1[s], kb, T);
+        V = mfma_b(R1[s], vb, V);
+        T = mfma_b(R2[s], kb, T);
+        V = mfma_b(R2[s], vb, V);
+      }
+    }
+    if constexpr (HAD) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V[r] *= a.rscale;  // v' = rscale (sign pattern) v
     }
     // Gram entry (col, col) sits in lane col + 16 (col / 4), element col % 4.
     // The standardising factor sqrt(d)/n comes from the reciprocal square root
@@ -330,6 +345,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       k2 = __shfl((e & 2) ? d23 : d01, col + 16 * (col >> 2), 64);
       f = (k2 >= 1.17549435e-38f) ? sqrtf(128.0f) * __builtin_amdgcn_rsqf(k2)
                                   : (k2 > 0.0f ? sqrtf(128.0f) / sqrtf(k2) : 0.0f);  // zero norm: t = 0
+      if constexpr (HAD) f *= a.rscale;  // t = (sqrt(d) / n) rscale (sign pattern) k
     }
 
     // ---- B2: t, codes, residual (rho -> LDS), key codes -> image; value extremes
@@ -582,20 +598,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 }
 
 constexpr int kRing = 3;  // tiles in flight per workgroup
-template <int KB>
+template <int KB, bool HAD>
 void* pick_v(int vb) {
   switch (vb) {
-    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing>);
-    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing>);
-    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing>);
+    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing, HAD>);
+    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing, HAD>);
+    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing, HAD>);
   }
   return nullptr;
 }
+template <bool HAD>
 void* pick_kv(int kb, int vb) {
   switch (kb) {
-    case 2: return pick_v<2>(vb);
-    case 3: return pick_v<3>(vb);
-    case 4: return pick_v<4>(vb);
+    case 2: return pick_v<2, HAD>(vb);
+    case 3: return pick_v<3, HAD>(vb);
+    case 4: return pick_v<4, HAD>(vb);
   }
   return nullptr;
 }
@@ -628,12 +645,14 @@ tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, 
   a.n_tiles = (n_tokens + 15) / 16;
   a.H = L->cfg.n_kv_heads;
   a.km = static_cast<int>(L->cfg.key_mode);
+  a.rscale = L->r_scale;
   a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
   for (int i = 0; i < 16; ++i) {
     a.cent[i] = L->centroids[i];
     a.bnd[i] = L->boundaries[i];
   }
-  void* fn = pick_kv(L->cfg.k_bits, L->cfg.v_bits);
+  void* fn = L->cfg.rotation == TQ_ROT_HADAMARD ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits)
+                                                 : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
   // Workgroups loop over their tiles: as many as fit on the chip at once over all
   // heads (resident workgroups per CU from the kernel's register and LDS use).

@@ -1,5 +1,5 @@
-// Host-side random state of a compressed layer: SplitMix64 + Box-Muller streams
-// and the Haar-random rotation.
+// Host-side random state of a compressed layer: SplitMix64 + Box-Muller streams,
+// the Haar-random rotation and the randomised Hadamard rotation.
 //
 // The method keeps one random orthogonal rotation and one Gaussian projection per
 // head, fixed for the life of the cache ("5x Faster LLM Inference? This KV Cache
@@ -100,6 +100,21 @@ void haar_rotation(uint64_t seed, int layer, int head, int d, double* out) {
     const double s = (rdiag[j] < 0.0) ? -1.0 : 1.0;
     for (int i = 0; i < d; ++i) out[i * d + j] = q[i * d + j] * s;
   }
+}
+
+// R = H D / sqrt(d): H[i][j] = (-1)^popcount(i & j) (Sylvester order), D[j] = +1
+// when the top bit of the j-th output of the tag-3 SplitMix64 stream is 0, else -1.
+void hadamard_rotation(uint64_t seed, int layer, int head, int d, double* out) {
+  uint64_t state = stream_key(seed, static_cast<uint64_t>(layer), static_cast<uint64_t>(head), kTagSigns);
+  std::vector<double> sgn(d);
+  for (int j = 0; j < d; ++j) {
+    state += 0x9E3779B97F4A7C15ULL;
+    sgn[j] = (mix64(state) >> 63) == 0 ? 1.0 : -1.0;
+  }
+  const double inv = 1.0 / std::sqrt(static_cast<double>(d));
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j)
+      out[i * d + j] = ((__builtin_popcount(static_cast<unsigned>(i & j)) & 1) ? -inv : inv) * sgn[j];
 }
 
 }  // namespace tq

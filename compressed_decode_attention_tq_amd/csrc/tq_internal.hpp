@@ -29,9 +29,12 @@ void gaussians(uint64_t seed, uint64_t layer, uint64_t head, uint64_t tag, size_
                double* out);
 constexpr uint64_t kTagRotation = 1;
 constexpr uint64_t kTagProjection = 2;
+constexpr uint64_t kTagSigns = 3;
 
 // Haar rotation (row-major d x d, float64) for (seed, layer, head).
 void haar_rotation(uint64_t seed, int layer, int head, int d, double* out);
+// Randomised Hadamard rotation H D / sqrt(d) (row-major d x d, float64), d a power of two.
+void hadamard_rotation(uint64_t seed, int layer, int head, int d, double* out);
 
 // Lloyd-Max codebook; returns TQ_OK or an error status.
 tq_status lloyd_max(int bits, tq_dist dist, int dim, double* centroids, double* boundaries,
@@ -77,6 +80,9 @@ struct tq_layer {
   // [H][8 row tiles][kOpSets: R bf16 hi, mid, lo; S fp16 hi, lo][4 K-steps][64 lanes][8],
   // lane l of (tile w, step s) holding M[16w + l%16][32s + 8(l/16) .. +7].
   unsigned short* dOpA = nullptr;
+  // Hadamard layers: the compressor's A operands hold the exact +-1 pattern of R
+  // (piece 0; pieces 1 and 2 zero) and the products are scaled by r_scale = |R_ij|.
+  float r_scale = 1.0f;
   // Matrix-core B operands of W = [R; S R] (256 x 128) for the decode prologue
   // (float16 bits): [H][16 column tiles][4 K-steps][hi, lo][64 lanes][8], lane l
   // of (tile t, step s) holding W[16t + l%16][32s + 8(l/16) .. +7].

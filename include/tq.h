@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum {
   TQ_OK = 0,
@@ -132,6 +132,18 @@ tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids,
  * decode kernels serve every mode unchanged. */
 typedef enum { TQ_KEY_QJL = 0, TQ_KEY_MSE = 1, TQ_KEY_MSE_NC = 2 } tq_key_mode;
 
+/* Rotation family of a compressed layer (per KV head g).
+ *   TQ_ROT_HAAR      dense Haar-random orthogonal R_g (default; QR of a Gaussian
+ *                    matrix from the tag-1 stream, Mezzadri's sign fix).
+ *   TQ_ROT_HADAMARD  randomised Hadamard R_g = H D / sqrt(d): H the Sylvester
+ *                    Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), D a diagonal
+ *                    of random signs (+1 when the top bit of the tag-3 SplitMix64
+ *                    output is 0) ("turbo-attn 0.24.0", "How it works": rotate each
+ *                    KV vector with a fast Walsh-Hadamard transform).  Every entry
+ *                    is +-1/sqrt(d), so the compressor's rotations take one
+ *                    matrix-core pass on the exact +-1 pattern instead of three. */
+typedef enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 } tq_rotation;
+
 typedef struct {
   int head_dim;             /* d; must be 128                                   */
   int n_kv_heads;           /* KV heads of the layer, >= 1                      */
@@ -144,10 +156,11 @@ typedef struct {
   unsigned long long seed;  /* random-state seed                                */
   int bypass;               /* 1: uncompressed bf16 layer (bits/dist ignored)   */
   tq_key_mode key_mode;     /* key estimator (compressed layers)                */
+  tq_rotation rotation;     /* rotation family (compressed layers)              */
 } tq_layer_config;
 
 /* Opaque per-layer state.  Holds, on the device, for every KV head g:
- *   R_g  d x d Haar-random orthogonal rotation (float32), and
+ *   R_g  d x d random orthogonal rotation of the chosen family (float32), and
  *   S_g  d x d i.i.d. N(0,1) QJL projection (float32),
  * both drawn from SplitMix64 + Box-Muller streams keyed by (seed, layer, g, tag)
  * ("5x Faster LLM Inference? ...", "Example 1": a rotation precomputed and fixed

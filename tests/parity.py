@@ -114,7 +114,7 @@ def rel_l2(got, ref):
 
 
 def oracle_store(K, V, slots, num_blocks, n_heads, k_bits, v_bits, seed, layer=0, bypass=False,
-                 K_bits16=None, V_bits16=None, keep=True, fill=0, key_mode="qjl"):
+                 K_bits16=None, V_bits16=None, keep=True, fill=0, key_mode="qjl", rotation_kind="haar"):
     """Oracle state + pool for the given inputs (float arrays [N, H, d]); every
     pool byte starts as `fill` (0xFF: all-ones fields, NaN norms and values)."""
     layout = lay.StoreLayout(128, k_bits, v_bits, 32, bypass=bypass)
@@ -123,7 +123,8 @@ def oracle_store(K, V, slots, num_blocks, n_heads, k_bits, v_bits, seed, layer=0
     if bypass:
         compress.store_bypass(K_bits16, V_bits16, slots, pool, layout, n_heads)
         return None, layout, pool, None
-    st = ostate.LayerState(seed, layer, n_heads, 128, k_bits, v_bits, 32, key_mode=key_mode)
+    st = ostate.LayerState(seed, layer, n_heads, 128, k_bits, v_bits, 32, key_mode=key_mode,
+                           rotation_kind=rotation_kind)
     res = compress.compress_into_pool(K, V, slots, pool, layout, st, keep=keep)
     return st, layout, pool, res
 

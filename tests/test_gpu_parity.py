@@ -23,9 +23,10 @@ def say(*a):
 
 
 # ------------------------------------------------------------------ compress
-def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16", key_mode=0):
+def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16", key_mode=0,
+                  rotation=0):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer, key_mode=key_mode))
+    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer, key_mode=key_mode, rotation=rotation))
     k = torch.from_numpy(np.ascontiguousarray(K)).to("cuda", tdt)
     v = torch.from_numpy(np.ascontiguousarray(V)).to("cuda", tdt)
     pool = layer_obj.new_pool(num_blocks)
@@ -421,5 +422,57 @@ def test_end_to_end_key_modes(key_mode):
     same = parity.rel_l2(out_o.cpu().numpy(), ref)
     err = parity.rel_l2(out.cpu().numpy(), ref)
     print("key mode %d: decode on oracle store rel L2 %.3e, end-to-end %.3e" % (key_mode, same, err))
+    assert same <= 1e-3 and err <= 2e-3
+    layer.close()
+
+
+@pytest.mark.parametrize("kb,vb,n,dtype,key_mode", [
+    (4, 4, 700, "bf16", tq.KEY_QJL), (2, 3, 500, "bf16", tq.KEY_MSE_NC), (3, 2, 300, "f32", tq.KEY_QJL)])
+def test_compress_hadamard_rotation(kb, vb, n, dtype, key_mode):
+    """Randomised Hadamard layers: the matrix-core compressor's one-pass +-1 rotation
+    (bf16, whole pages and a ragged tile) and the per-token compressor (fp32)."""
+    torch = _torch()
+    say("compress hadamard", kb, vb, n, dtype, key_mode)
+    H = 8 if dtype == "bf16" else 2
+    K, V = synth.kv_host(190 + kb, n, H, dtype=dtype, outliers=4)
+    slots = np.arange(n, dtype=np.int64)
+    nb = (n + 15) // 16
+    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, 240, layer=kb, dtype=dtype, key_mode=key_mode,
+                        rotation=tq.ROT_HADAMARD)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, H, kb, vb, 240, layer=kb,
+                                                key_mode=KEY_MODE_NAMES[key_mode], rotation_kind="hadamard")
+    _check_compress(gpu, res, st, layout, H, slots, V, kb, vb)
+
+
+def test_end_to_end_hadamard_rotation():
+    """GPU compress -> GPU decode on a randomised Hadamard layer against the oracle
+    (the decode prologue and epilogue use the layer's R as stored)."""
+    torch = _torch()
+    say("end to end hadamard")
+    B, Hq, Hkv, T = 2, 32, 8, 1000
+    lens = np.array([T, 333], np.int32)
+    maxb = (T + 15) // 16
+    table = synth.block_table(280, B, maxb, "random")
+    K, V = synth.kv_host(200, B * T, Hkv, outliers=4)
+    pos = np.tile(np.arange(T), B)
+    seq = np.repeat(np.arange(B), T)
+    slots = table[seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    st, layout, opool, _ = parity.oracle_store(K, V, slots, B * maxb, Hkv, 4, 4, 280, keep=False,
+                                               rotation_kind="hadamard")
+    q = synth.queries_host(280, B, Hq)
+    ref = parity.oracle_decode(q.astype(np.float64), opool, layout, Hkv, table, lens, st)
+    layer = tq.Layer(tq.config(Hkv, 4, 4, seed=280, rotation=tq.ROT_HADAMARD))
+    pool = layer.new_pool(B * maxb)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    qt = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(lens).cuda()
+    out = tq.decode_attn(layer, qt, pool, bt, sl, T)
+    out_o = tq.decode_attn(layer, qt, torch.from_numpy(opool).cuda(), bt, sl, T)
+    torch.cuda.synchronize()
+    same = parity.rel_l2(out_o.cpu().numpy(), ref)
+    err = parity.rel_l2(out.cpu().numpy(), ref)
+    print("hadamard: decode on oracle store rel L2 %.3e, end-to-end %.3e" % (same, err))
     assert same <= 1e-3 and err <= 2e-3
     layer.close()

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tq_abi_version() == 2
+    assert lib.tq_abi_version() == 3
 
 
 @pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
@@ -81,7 +81,7 @@ def test_config_errors():
         (dict(v_group=16), tq.ERR_UNSUPPORTED), (dict(block_size=32), tq.ERR_UNSUPPORTED),
         (dict(n_kv_heads=0), tq.ERR_INVALID_ARGUMENT), (dict(layer=-1), tq.ERR_INVALID_ARGUMENT),
         (dict(dist=7), tq.ERR_INVALID_ARGUMENT), (dict(key_mode=3), tq.ERR_INVALID_ARGUMENT),
-        (dict(key_mode=-1), tq.ERR_INVALID_ARGUMENT),
+        (dict(key_mode=-1), tq.ERR_INVALID_ARGUMENT), (dict(rotation=2), tq.ERR_INVALID_ARGUMENT),
     ]
     for kw, want in bad:
         args = dict(n_kv_heads=8)
@@ -116,3 +116,12 @@ def test_key_modes_share_the_page_layout():
         ref = tq.store_layout(tq.config(8, kb, vb))
         for km in (tq.KEY_MSE, tq.KEY_MSE_NC):
             assert tq.store_layout(tq.config(8, kb, vb, key_mode=km)) == ref
+
+
+@pytest.mark.parametrize("layer,heads", [(0, 1), (5, 3)])
+def test_hadamard_layer_state_matches_oracle(layer, heads):
+    cfg = tq.config(heads, 3, 3, seed=207, layer=layer, rotation=tq.ROT_HADAMARD)
+    R, S, c, b = tq.layer_state_host(cfg)
+    st = state.LayerState(207, layer, heads, 128, 3, 3, 32, rotation_kind="hadamard")
+    assert np.array_equal(R.astype(np.float64), st.R)
+    assert np.array_equal(S.astype(np.float64), st.S)
