@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_llama3_8b_layer_and_c
 # kernels whose HBM traffic is taken from counters, with the sources that define them
 TRAFFIC_KERNELS = {
     "splitk_mfma_kernel<4, 4, 4>": ["decode_mainloop.hip"],
-    "compress_mfma_kernel<2, 3, 3>": ["compress_mfma.hip"],
+    "compress_mfma_kernel<2, 3, 3, false, true>": ["compress_mfma.hip"],
 }
 
 
@@ -246,8 +246,8 @@ def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
             "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": traffic_for("compress_mfma_kernel<2, 3, 3>"),
-                         "kernel": "compress_mfma_kernel<2,3,3>",
+                         "traffic": traffic_for("compress_mfma_kernel<2, 3, 3, false, true>"),
+                         "kernel": "compress_mfma_kernel<2,3,3,false,true>",
                          "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
 
 

@@ -195,7 +195,9 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 //
 // HAD: the layer's rotation is a randomised Hadamard matrix, all entries
 // +-rscale: R k = rscale (sign pattern) k, one exact bf16 pass instead of three.
-template <int KB, int VB, int P, bool HAD>
+// QJL: keys get the residual signs and gamma (key mode 0); otherwise the key
+// mode (1 or 2: plain or norm-corrected magnitude) comes from a.km.
+template <int KB, int VB, int P, bool HAD, bool QJL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
   using PG = Page<KB, VB>;
   constexpr int HALF = 1 << (KB - 1);  // codebook levels per sign
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const int idx = (t > 0.0f) ? HALF + cnt : HALF - 1 - cnt;
         rho[r] = t - ((t > 0.0f) ? cp : -cp);
         // squared norm of the residual (QJL) or of the centroid vector (norm correction)
-        const float gt = (a.km == 2) ? cp : rho[r];
+        const float gt = QJL ? rho[r] : (a.km == 2 ? cp : 0.0f);
         g2 = fmaf(gt, gt, g2);
         codes |= static_cast<unsigned>(idx) << (KB * r);
       }
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         rl[r] = residual_pair(rho[2 * r], rho[2 * r + 1], rh[r]);
       }
       const int d0 = 16 * w + 4 * kg;
-      if (a.km == 0) {  // the residual feeds the QJL projection only
+      if constexpr (QJL) {  // the residual feeds the QJL projection only
         *reinterpret_cast<u32x2*>(&orh[col][d0]) = rh;
         *reinterpret_cast<u32x2*>(&orl[col][d0]) = rl;
       }
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       // sign nibble of dims d0..d0+3 (bit r = dim d0 + r); two row groups make a
       // byte (zero bits without QJL)
       unsigned nib = 0;
-      if (a.km == 0) {
+      if constexpr (QJL) {
         floatx4 Y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -519,9 +521,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int i = 0; i < 8; ++i) g2 += gpart[i][col];
         // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction; gamma 0 without QJL
         const float n = sqrtf(k2);
-        const unsigned short g16 = __half_as_ushort(__float2half_rn(a.km == 0 ? sqrtf(g2) : 0.0f));
+        const unsigned short g16 = __half_as_ushort(__float2half_rn(QJL ? sqrtf(g2) : 0.0f));
         const unsigned short n16 =
-            __half_as_ushort(__float2half_rn(a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n));
+            __half_as_ushort(__float2half_rn(!QJL && a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n));
         *reinterpret_cast<unsigned*>(&img[PG::kn + col * 4]) =
             static_cast<unsigned>(n16) | (static_cast<unsigned>(g16) << 16);
       }
@@ -598,21 +600,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 }
 
 constexpr int kRing = 3;  // tiles in flight per workgroup
-template <int KB, bool HAD>
+template <int KB, bool HAD, bool QJL>
 void* pick_v(int vb) {
   switch (vb) {
-    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing, HAD>);
-    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing, HAD>);
-    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing, HAD>);
+    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing, HAD, QJL>);
+    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing, HAD, QJL>);
+    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing, HAD, QJL>);
   }
   return nullptr;
 }
-template <bool HAD>
+template <bool HAD, bool QJL>
 void* pick_kv(int kb, int vb) {
   switch (kb) {
-    case 2: return pick_v<2, HAD>(vb);
-    case 3: return pick_v<3, HAD>(vb);
-    case 4: return pick_v<4, HAD>(vb);
+    case 2: return pick_v<2, HAD, QJL>(vb);
+    case 3: return pick_v<3, HAD, QJL>(vb);
+    case 4: return pick_v<4, HAD, QJL>(vb);
   }
   return nullptr;
 }
@@ -651,8 +653,11 @@ tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, 
     a.cent[i] = L->centroids[i];
     a.bnd[i] = L->boundaries[i];
   }
-  void* fn = L->cfg.rotation == TQ_ROT_HADAMARD ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits)
-                                                 : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
+  const bool had = L->cfg.rotation == TQ_ROT_HADAMARD, qjl = L->cfg.key_mode == TQ_KEY_QJL;
+  void* fn = had ? (qjl ? pick_kv<true, true>(L->cfg.k_bits, L->cfg.v_bits)
+                        : pick_kv<true, false>(L->cfg.k_bits, L->cfg.v_bits))
+                 : (qjl ? pick_kv<false, true>(L->cfg.k_bits, L->cfg.v_bits)
+                        : pick_kv<false, false>(L->cfg.k_bits, L->cfg.v_bits));
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
   // Workgroups loop over their tiles: as many as fit on the chip at once over all
   // heads (resident workgroups per CU from the kernel's register and LDS use).
