@@ -155,3 +155,29 @@ def test_mse_key_modes_are_attention_over_codebook_reconstruction(key_mode):
                 w = np.exp(s - s.max())
                 ref = (w / w.sum()) @ Vh
                 assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("key_mode,bypass", [("qjl", False), ("mse_nc", False), ("qjl", True)])
+def test_decompressed_store_gives_the_decode(key_mode, bypass):
+    """Textbook attention in the original basis over the decompressed K, V equals
+    the decode in the rotated space (a different computation: q' and u there,
+    R^T and S^T applied to the records here); a one-token sequence gives its
+    decompressed value."""
+    from oracle import decompress
+    st, lay, table, pool, lens, q, KV = _setup(k_bits=3, v_bits=3, key_mode=key_mode, bypass=bypass)
+    out = decode.decode(q, pool, lay, 2, table, lens, None if bypass else st)
+    for b, T in enumerate(lens):
+        pos = np.arange(T)
+        slots = table[b][pos // 16] * 16 + pos % 16
+        Kd, Vd = decompress.decompress(pool, lay, 2, slots, None if bypass else st)
+        if bypass:
+            assert np.array_equal(Kd, KV[b][0]) and np.array_equal(Vd, KV[b][1])
+        for h in range(4):
+            g = h // 2
+            s = Kd[:, g] @ q[b, h] / math.sqrt(D)
+            w = np.exp(s - s.max())
+            ref = (w / w.sum()) @ Vd[:, g]
+            assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * max(1.0, np.abs(ref).max())
+    # negative slots give zero rows
+    Kd, Vd = decompress.decompress(pool, lay, 2, np.array([-1, table[0][0] * 16]), None if bypass else st)
+    assert not Kd[0].any() and not Vd[0].any() and Vd[1].any()
