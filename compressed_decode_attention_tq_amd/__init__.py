@@ -22,7 +22,7 @@ EXPORTED = [
     "tq_last_error", "tq_abi_version", "tq_codebook_build", "tq_layer_state_host",
     "tq_layer_create", "tq_layer_destroy", "tq_store_layout", "tq_compress_kv",
     "tq_decode_workspace_size", "tq_decode_attn", "tq_profile_enable", "tq_profile_read",
-    "tq_profile_reset",
+    "tq_profile_reset", "tq_decompress_kv",
 ]
 K_COMPRESS, K_PROLOGUE, K_SPLITK, K_COMBINE = range(4)
 
@@ -69,6 +69,7 @@ def lib():
     L.tq_layer_destroy.argtypes = [vp]
     L.tq_store_layout.argtypes = [ctypes.POINTER(LayerConfig), ctypes.POINTER(c_size), ctypes.POINTER(c_size)]
     L.tq_compress_kv.argtypes = [vp, vp, vp, c_int, c_ll, c_ll, c_ll, vp, vp, c_ll, vp]
+    L.tq_decompress_kv.argtypes = [vp, vp, c_ll, vp, c_ll, vp, vp, c_int, vp]
     L.tq_decode_workspace_size.argtypes = [vp, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)]
     L.tq_decode_attn.argtypes = [vp, vp, c_int, c_int, c_int, vp, c_ll, vp, c_int, vp, c_int,
                                  ctypes.c_float, c_int, vp, c_int, vp, c_size, vp]
@@ -184,6 +185,23 @@ def compress_kv(layer, k, v, slot_mapping, pool, stream=None):
     num_blocks = pool.numel() // (layer.cfg.n_kv_heads * layer.block_bytes)
     _check(lib().tq_compress_kv(layer.handle, _ptr(k), _ptr(v), _dtype_code(k), n, k.stride(0), v.stride(0),
                                 _ptr(slot_mapping), _ptr(pool), num_blocks, _stream(stream)))
+
+
+def decompress_kv(layer, pool, slot_mapping, out_dtype=None, k_out=None, v_out=None, stream=None):
+    """K, V [N, H_kv, 128] (f32 or bf16) reconstructed from the store at slot_mapping int64 [N]."""
+    torch = _torch()
+    assert slot_mapping.dtype == torch.int64 and pool.dtype == torch.uint8
+    n, H = slot_mapping.shape[0], layer.cfg.n_kv_heads
+    dt = out_dtype or torch.float32
+    if k_out is None:
+        k_out = torch.empty((n, H, 128), dtype=dt, device=pool.device)
+    if v_out is None:
+        v_out = torch.empty((n, H, 128), dtype=dt, device=pool.device)
+    assert k_out.is_contiguous() and v_out.is_contiguous() and k_out.dtype == v_out.dtype
+    num_blocks = pool.numel() // (H * layer.block_bytes)
+    _check(lib().tq_decompress_kv(layer.handle, _ptr(pool), num_blocks, _ptr(slot_mapping), n, _ptr(k_out),
+                                  _ptr(v_out), _dtype_code(k_out), _stream(stream)))
+    return k_out, v_out
 
 
 def decode_workspace_size(layer, batch, n_q_heads, max_seq_len, num_splits=0):

@@ -23,7 +23,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast",
           "-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = ["api.cpp", "host_state.cpp", "host_codebook.cpp", "profile.cpp", "compress.hip", "compress_mfma.hip", "decode.hip", "decode_mainloop.hip",
-           "decode_bypass.hip"]
+           "decode_bypass.hip", "decompress.hip"]
 
 
 def _compile(src):

@@ -323,6 +323,9 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
     // is split into float16 hi + lo pieces.
     const size_t nq = static_cast<size_t>(H) * 16 * 4 * 2 * 64 * 8;
     std::vector<unsigned short> opq(nq);
+    // Decompress B operands: R[k][n] and P[k][n] (P = S R) as float16 hi + lo.
+    const size_t nd = static_cast<size_t>(H) * 8 * 4 * 4 * 64 * 8;
+    std::vector<unsigned short> opd(nd);
     {
       std::vector<double> W(static_cast<size_t>(2 * d) * d);
       for (int h = 0; h < H; ++h) {
@@ -346,8 +349,30 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
                 opq[at] = __builtin_bit_cast(unsigned short, hi);
                 opq[at + 64 * 8] = __builtin_bit_cast(unsigned short, lo);
               }
+        for (int t = 0; t < 8; ++t)
+          for (int ks = 0; ks < 4; ++ks)
+            for (int l = 0; l < 64; ++l)
+              for (int j = 0; j < 8; ++j) {
+                const int k = 32 * ks + 8 * (l / 16) + j, n = 16 * t + l % 16;
+                const double mv[2] = {W[static_cast<size_t>(k) * d + n], W[static_cast<size_t>(d + k) * d + n]};
+                for (int m = 0; m < 2; ++m) {
+                  const _Float16 hi = static_cast<_Float16>(mv[m]);
+                  const _Float16 lo = static_cast<_Float16>(mv[m] - static_cast<double>(hi));
+                  const size_t at = ((((static_cast<size_t>(h) * 8 + t) * 4 + ks) * 4 + 2 * m) * 64 + l) * 8 + j;
+                  opd[at] = __builtin_bit_cast(unsigned short, hi);
+                  opd[at + 64 * 8] = __builtin_bit_cast(unsigned short, lo);
+                }
+              }
       }
     }
+    e = hipMalloc(reinterpret_cast<void**>(&L->dOpD), nd * sizeof(unsigned short));
+    if (e != hipSuccess) {
+      tq_layer_destroy(L);
+      return fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc of layer state failed: %s", hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(L->dOpD, opd.data(), nd * sizeof(unsigned short), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) { tq_layer_destroy(L); return hip_fail(e, "hipMemcpyAsync"); }
     e = hipMalloc(reinterpret_cast<void**>(&L->dOpQ), nq * sizeof(unsigned short));
     if (e != hipSuccess) {
       tq_layer_destroy(L);
@@ -371,12 +396,14 @@ tq_status tq_layer_destroy(tq_layer* L) {
   hipError_t e3 = L->dST ? hipFree(L->dST) : hipSuccess;
   hipError_t e4 = L->dOpA ? hipFree(L->dOpA) : hipSuccess;
   hipError_t e5 = L->dOpQ ? hipFree(L->dOpQ) : hipSuccess;
+  hipError_t e6 = L->dOpD ? hipFree(L->dOpD) : hipSuccess;
   delete L;
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
   if (e3 != hipSuccess) return hip_fail(e3, "hipFree");
   if (e4 != hipSuccess) return hip_fail(e4, "hipFree");
   if (e5 != hipSuccess) return hip_fail(e5, "hipFree");
+  if (e6 != hipSuccess) return hip_fail(e6, "hipFree");
   return TQ_OK;
 }
 
@@ -401,6 +428,20 @@ tq_status tq_compress_kv(const tq_layer* L, const void* k, const void* v, tq_dty
   if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
   return launch_compress(L, k, v, in_dtype, n_tokens, k_token_stride, v_token_stride, slot_mapping,
                          pool, hip_stream);
+}
+
+tq_status tq_decompress_kv(const tq_layer* L, const void* pool, long long num_blocks, const long long* slot_mapping,
+                           long long n_tokens, void* k_out, void* v_out, tq_dtype out_dtype, void* hip_stream) {
+  clear_error();
+  if (!L) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer");
+  if (n_tokens < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0");
+  if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "decompress output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
+  if (n_tokens == 0) return TQ_OK;
+  if (!pool || !slot_mapping || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
+  return launch_decompress(L, pool, slot_mapping, n_tokens, k_out, v_out, out_dtype, hip_stream);
 }
 
 tq_status tq_decode_workspace_size(const tq_layer* L, int batch, int n_q_heads, int max_seq_len,

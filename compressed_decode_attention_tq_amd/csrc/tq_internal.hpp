@@ -87,6 +87,10 @@ struct tq_layer {
   // (float16 bits): [H][16 column tiles][4 K-steps][hi, lo][64 lanes][8], lane l
   // of (tile t, step s) holding W[16t + l%16][32s + 8(l/16) .. +7].
   unsigned short* dOpQ = nullptr;
+  // Matrix-core B operands of R and P = S R for the decompress kernel (float16 bits):
+  // [H][8 column tiles][4 K-steps][R hi, R lo, P hi, P lo][64 lanes][8], lane l of
+  // (tile t, step s) holding M[32s + 8(l/16) .. +7][16t + l%16].
+  unsigned short* dOpD = nullptr;
   float centroids[16] = {0};
   float boundaries[16] = {0};
   int levels = 0;
@@ -122,6 +126,8 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
 tq_status launch_splitk_bypass(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
                                const void* pool, const int* block_table, int max_blocks_per_seq,
                                const int* seq_lens, float softmax_scale, float* part, void* stream);
+tq_status launch_decompress(const tq_layer* L, const void* pool, const long long* slots, long long n_tokens,
+                            void* k_out, void* v_out, tq_dtype out_dtype, void* stream);
 tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
                         const void* pool, const int* block_table, int max_blocks_per_seq,
                         const int* seq_lens, float softmax_scale, void* out, tq_dtype out_dtype,

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
 
 typedef enum {
   TQ_OK = 0,
@@ -203,6 +203,25 @@ tq_status tq_compress_kv(const tq_layer* layer, const void* k, const void* v, tq
                          long long n_tokens, long long k_token_stride, long long v_token_stride,
                          const long long* slot_mapping, void* pool, long long num_blocks,
                          void* hip_stream);
+
+/* Keys and values of n_tokens tokens reconstructed from the store, in the original
+ * (un-rotated) basis ("turbo-attn 0.24.0", "How it works": a decompress path for
+ * attention kernels that cannot read the codec; "tiny-turboquant 0.18.0", "Fused
+ * decode-attention path"):
+ *   khat = (n16 / sqrt d) R_g^T (c[idx] + sqrt(pi/2)/128 * gamma16 * S_g^T (2 z - 1))
+ *   vhat = R_g^T (zero16 + scale16 * code)
+ * so that softmax_scale * (q . khat) is the score tq_decode_attn forms for the
+ * token (the QJL term is 0 in the key modes without QJL).  Bypass layers return
+ * their stored bf16 values.
+ *   pool          device pool written by tq_compress_kv (num_blocks blocks)
+ *   slot_mapping  device int64 [n_tokens]: slot of each token; < 0 gives zero rows
+ *   k_out, v_out  device [n_tokens][n_kv_heads][128] of out_dtype (F32, or BF16
+ *                 rounded to nearest even); caller-owned
+ * One launch on hip_stream; nothing is allocated.  Slots must be < 16*num_blocks
+ * (the caller's contract, not checked on the device). */
+tq_status tq_decompress_kv(const tq_layer* layer, const void* pool, long long num_blocks,
+                           const long long* slot_mapping, long long n_tokens, void* k_out, void* v_out,
+                           tq_dtype out_dtype, void* hip_stream);
 
 /* Bytes of device workspace tq_decode_attn needs for this shape (num_splits as
  * passed to tq_decode_attn, 0 = automatic). */

@@ -476,3 +476,63 @@ def test_end_to_end_hadamard_rotation():
     print("hadamard: decode on oracle store rel L2 %.3e, end-to-end %.3e" % (same, err))
     assert same <= 1e-3 and err <= 2e-3
     layer.close()
+
+
+@pytest.mark.parametrize("kb,vb,key_mode,rotation,out_dtype", [
+    (4, 4, tq.KEY_QJL, tq.ROT_HAAR, "f32"), (3, 2, tq.KEY_MSE_NC, tq.ROT_HADAMARD, "f32"),
+    (2, 3, tq.KEY_QJL, tq.ROT_HAAR, "bf16")])
+def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype):
+    """Keys and values reconstructed from a GPU-written store (shuffled slots, some
+    negative: zero rows) against the oracle's reconstruction of the same bytes."""
+    from oracle import decompress as odec
+    torch = _torch()
+    say("decompress", kb, vb, key_mode, rotation, out_dtype)
+    H, n = 8, 613
+    K, V = synth.kv_host(300 + kb, n, H, outliers=4)
+    rng = np.random.default_rng(kb)
+    slots = rng.permutation(48 * 16)[:n].astype(np.int64)
+    layer = tq.Layer(tq.config(H, kb, vb, seed=290, layer=kb, key_mode=key_mode, rotation=rotation))
+    pool = layer.new_pool(48)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    q_slots = slots.copy()
+    q_slots[rng.choice(n, 9, replace=False)] = -1
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    kd, vd = tq.decompress_kv(layer, pool, torch.from_numpy(q_slots).cuda(), out_dtype=tdt)
+    torch.cuda.synchronize()
+    kd, vd = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    st = parity.ostate.LayerState(290, kb, H, 128, kb, vb, 32, key_mode=KEY_MODE_NAMES[key_mode],
+                                  rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard")
+    layout = parity.lay.StoreLayout(128, kb, vb, 32)
+    kr, vr = odec.decompress(pool.cpu().numpy(), layout, H, q_slots, st)
+    neg = q_slots < 0
+    assert not kd[neg].any() and not vd[neg].any()
+    for got, ref, name in ((kd, kr, "K"), (vd, vr, "V")):
+        err = np.abs(got - ref)
+        scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+        if out_dtype == "f32":
+            print(name, "max err / row max %.2e, rel L2 %.2e" % ((err / scale).max(), parity.rel_l2(got, ref)))
+            assert (err / scale).max() <= 2e-6 and parity.rel_l2(got, ref) <= 1e-6
+        else:
+            # bf16 of the fp32 result: within one bf16 rounding of the exact value
+            assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-6 * scale), name
+            print(name, "bf16 rel L2 %.2e" % parity.rel_l2(got, ref))
+    layer.close()
+
+
+def test_decompress_bypass_exact():
+    """Bypass layers return their stored bf16 values bit for bit."""
+    torch = _torch()
+    say("decompress bypass")
+    H, n = 4, 100
+    K, V = synth.kv_host(310, n, H, outliers=4)
+    slots = np.random.default_rng(3).permutation(8 * 16)[:n].astype(np.int64)
+    layer = tq.Layer(tq.config(H, seed=311, bypass=True))
+    pool = layer.new_pool(8)
+    kt = torch.from_numpy(K).to("cuda", torch.bfloat16)
+    vt = torch.from_numpy(V).to("cuda", torch.bfloat16)
+    tq.compress_kv(layer, kt, vt, torch.from_numpy(slots).cuda(), pool)
+    kd, vd = tq.decompress_kv(layer, pool, torch.from_numpy(slots).cuda(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(kd, kt) and torch.equal(vd, vt)
+    layer.close()

@@ -24,11 +24,11 @@ def _declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = tq.lib()
     names = _declared_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tq_abi_version() == 3
+    assert lib.tq_abi_version() == 4
 
 
 @pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
@@ -106,6 +106,7 @@ def test_null_and_bad_arguments_on_device_entry_points():
     assert lib.tq_decode_workspace_size(None, 1, 1, 1, 0, ctypes.byref(out)) == tq.ERR_INVALID_ARGUMENT
     assert lib.tq_decode_attn(None, vp(1), tq.BF16, 1, 1, vp(1), 1, vp(1), 1, vp(1), 16, 0.0, 0,
                               vp(1), tq.F32, vp(256), 1 << 20, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_decompress_kv(None, vp(1), 1, vp(1), 1, vp(1), vp(1), tq.F32, None) == tq.ERR_INVALID_ARGUMENT
     assert lib.tq_layer_destroy(None) == tq.OK
     assert lib.tq_layer_create(None, None, ctypes.byref(vp())) == tq.ERR_INVALID_ARGUMENT
 
