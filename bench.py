@@ -296,6 +296,35 @@ def _fill(torch, tq, synth, layer, table, lens, Hkv, seed, outliers, dtype="bf16
     return pool
 
 
+def decompress_workload(torch, tq, synth, args):
+    """The headline store (16 x 4096 tokens x 8 KV heads, K4/V4) reconstructed to bf16 K and V."""
+    W, sd = synth.WORKLOADS[2], synth.seeds(2)
+    B, Hkv, T = W["B"], W["Hkv"], W["ctx"]
+    layer = tq.Layer(tq.config(Hkv, W["k_bits"], W["v_bits"], seed=sd["state"]))
+    table = synth.block_table(sd["table"], B, T // 16, W["table"])
+    pool = _fill(torch, tq, synth, layer, table, [T] * B, Hkv, sd["data"], W["outliers"])
+    import numpy as np
+    b_of = np.repeat(np.arange(B), T)
+    pos = np.tile(np.arange(T), B)
+    slots = torch.from_numpy(table[b_of, pos // 16].astype(np.int64) * 16 + pos % 16).cuda()
+    N = B * T
+    kd = torch.empty((N, Hkv, 128), dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    step = lambda i: tq.decompress_kv(layer, pool, slots, k_out=kd, v_out=vd)
+    _time_steps(torch, step, 5)
+    ms = _time_steps(torch, step, 50)
+    layer.close()
+    rec = _record_bytes(W["k_bits"], W["v_bits"])
+    nbytes = N * Hkv * (rec + 512) + N * 8
+    # matrix-core floor: 7 passes x 4 K-steps x 8 column tiles per 16 token-heads,
+    # 16 cycles each at 1024 SIMDs x 2.4 GHz
+    mfma_us = N * Hkv / 16 * 224 * 16 / (1024 * 2.4e9) * 1e6
+    return {"workload": "decompress-llama3-8b-layer-store", "token_heads": N * Hkv, "out_dtype": "bf16",
+            "ms": round(ms, 4), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+            "mfma_floor_us": round(mfma_us, 1)}
+
+
 def extra_workloads(torch, tq, synth, args):
     """The tiny, long-context and serving workloads, each as decode-step figures."""
     import numpy as np
@@ -454,6 +483,8 @@ def main():
             extra["fused-compress-hadamard"] = compress_workload(torch, tq, synth, args, rotation=tq.ROT_HADAMARD)
             extra["fused-compress-hadamard-key-mse-nc"] = compress_workload(
                 torch, tq, synth, args, key_mode=tq.KEY_MSE_NC, rotation=tq.ROT_HADAMARD)
+        log("decompress workload")
+        extra["decompress"] = decompress_workload(torch, tq, synth, args)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")

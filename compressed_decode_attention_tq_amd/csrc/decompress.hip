@@ -29,6 +29,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kARow = 136;  // float16 elements per LDS operand row (128 + pad)
+constexpr int kMaxPage = 256 * 8 + 576;  // bytes of a K4/V4 page, the largest
 
 struct DArgs {
   const unsigned char* pool;
@@ -48,6 +49,25 @@ __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const fl
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Eight consecutive outputs from LDS as one 16-byte (bf16, nearest even) or two
+// 16-byte (fp32) stores.
+template <bool BF16>
+__device__ __forceinline__ void store8(void* out, size_t at, const float* src) {
+  if constexpr (BF16) {
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned lo = __float_as_uint(src[2 * i]), hi = __float_as_uint(src[2 * i + 1]);
+      pk[i] = ((lo + 0x7fffu + ((lo >> 16) & 1u)) >> 16) | (((hi + 0x7fffu + ((hi >> 16) & 1u)) >> 16) << 16);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at) = pk;
+  } else {
+    float* o = static_cast<float*>(out) + at;
+    *reinterpret_cast<floatx4*>(o) = *reinterpret_cast<const floatx4*>(src);
+    *reinterpret_cast<floatx4*>(o + 4) = *reinterpret_cast<const floatx4*>(src + 4);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void put(void* out, size_t at, float x) {
   if constexpr (BF16) {
@@ -55,6 +75,44 @@ __device__ __forceinline__ void put(void* out, size_t at, float x) {
     static_cast<unsigned short*>(out)[at] = static_cast<unsigned short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
   } else {
     static_cast<float*>(out)[at] = x;
+  }
+}
+
+// Expand dims d0..d0+7 of in-page token o (o = t for a whole-page tile) from
+// `page` (global memory or an LDS copy) into the tile's A operands.
+template <int KB, int VB, typename Row, typename Scal>
+__device__ __forceinline__ void expand(const DArgs& a, const unsigned char* page, int t, int d0, int tid, Row ac, Row az,
+                                       Row avh, Row avl, Scal sn, Scal sg, int o = -1) {
+  if (o < 0) o = t;
+  const int blk = d0 >> 5, e0 = d0 & 31;
+  // key codes: 8 codes of KB bits at bit e0*KB of the token's 32-dim block record
+  const unsigned char* kc = page + a.off_kc + (blk * 16 + o) * 4 * KB + (e0 / 8) * KB;
+  unsigned x = 0;
+#pragma unroll
+  for (int b = 0; b < KB; ++b) x |= static_cast<unsigned>(kc[b]) << (8 * b);
+  const unsigned zb = page[a.off_ks + (blk * 16 + o) * 4 + e0 / 8];  // sign bits of dims d0..d0+7
+  const unsigned kn = *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4);
+  const unsigned sz = *reinterpret_cast<const unsigned*>(page + a.off_vsz + o * 16 + (d0 >> 5) * 4);
+  const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
+  const float zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ac[t][d0 + i] = static_cast<_Float16>(a.cent[(x >> (KB * i)) & ((1u << KB) - 1u)]);
+    az[t][d0 + i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+    // value code of (dim d0 + i, token o) in the lane-blocked stream
+    const int j = d0 + i;
+    const unsigned e = ((16u * (o >> 3) + (j & 15)) * 16u + 2u * (j >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
+    const unsigned bit = e * VB;
+    const unsigned char* vb = page + a.off_vc + (bit >> 3);
+    const unsigned w = static_cast<unsigned>(vb[0]) | (static_cast<unsigned>(vb[1]) << 8);
+    const float v = fmaf(sc, static_cast<float>((w >> (bit & 7)) & ((1u << VB) - 1u)), zr);
+    const _Float16 h = static_cast<_Float16>(v);
+    avh[t][d0 + i] = h;
+    avl[t][d0 + i] = static_cast<_Float16>(v - static_cast<float>(h));
+  }
+  if ((tid & 15) == 0) {
+    sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
+    sg[t] = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
   }
 }
 
@@ -68,56 +126,38 @@ __global__ __launch_bounds__(256) void decompress_kernel(DArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 avh[16][kARow];  // v' hi
   __shared__ __attribute__((aligned(16))) _Float16 avl[16][kARow];  // v' lo
   __shared__ float sn[16], sg[16];
+  __shared__ __attribute__((aligned(16))) float stk[4][16][36], stv[4][16][36];  // per-wave output staging
 
-  // ---- expand the records: thread (t, c) = (tid / 16, tid % 16) takes dims 8c..8c+7 of token t
-  {
-    const int t = tid >> 4, d0 = 8 * (tid & 15);
+  // ---- expand the records: thread (t, c) = (tid / 16, tid % 16) takes dims 8c..8c+7 of token t.
+  // A tile that is one whole aligned page (16 consecutive slots from a multiple
+  // of 16) is first copied into LDS with one 16-byte read per thread; other
+  // tiles read each token's fields from its own page.
+  __shared__ __attribute__((aligned(16))) unsigned char pg[kMaxPage];
+  const int t = tid >> 4, d0 = 8 * (tid & 15);
+  bool whole = t0 + 16 <= a.n_tokens;
+  long long s0 = -1;
+  if (whole) {
+    s0 = a.slots[t0];
+    whole = s0 >= 0 && (s0 & 15) == 0;
+#pragma unroll
+    for (int j = 1; j < 16; ++j) whole = whole && a.slots[t0 + j] == s0 + j;
+  }
+  if (whole) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.pool + (static_cast<size_t>(s0 >> 4) * a.H + g) * a.block_bytes);
+    if (tid * 16 < static_cast<int>(a.block_bytes)) reinterpret_cast<u32x4*>(pg)[tid] = src[tid];
+    __syncthreads();
+    expand<KB, VB>(a, pg, t, d0, tid, ac, az, avh, avl, sn, sg);
+  } else {
     const long long slot = (t0 + t < a.n_tokens) ? a.slots[t0 + t] : -1;
-    _Float16 c8[8], z8[8], h8[8], l8[8];
     if (slot >= 0) {
-      const unsigned char* page = a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * a.block_bytes;
-      const int o = static_cast<int>(slot & 15);
-      const int blk = d0 >> 5, e0 = d0 & 31;
-      // key codes: 8 codes of KB bits at bit e0*KB of the token's 32-dim block record
-      const unsigned char* kc = page + a.off_kc + (blk * 16 + o) * 4 * KB + (e0 / 8) * KB;
-      unsigned x = 0;
-#pragma unroll
-      for (int b = 0; b < KB; ++b) x |= static_cast<unsigned>(kc[b]) << (8 * b);
-      const unsigned zb = page[a.off_ks + (blk * 16 + o) * 4 + e0 / 8];  // sign bits of dims d0..d0+7
-      const unsigned kn = *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4);
-      const unsigned sz = *reinterpret_cast<const unsigned*>(page + a.off_vsz + o * 16 + (d0 >> 5) * 4);
-      const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
-      const float zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        c8[i] = static_cast<_Float16>(a.cent[(x >> (KB * i)) & ((1u << KB) - 1u)]);
-        z8[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-        // value code of (dim d0 + i, token o) in the lane-blocked stream
-        const int j = d0 + i;
-        const unsigned e = ((16u * (o >> 3) + (j & 15)) * 16u + 2u * (j >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
-        const unsigned bit = e * VB;
-        const unsigned char* vb = page + a.off_vc + (bit >> 3);
-        const unsigned w = static_cast<unsigned>(vb[0]) | (static_cast<unsigned>(vb[1]) << 8);
-        const float code = static_cast<float>((w >> (bit & 7)) & ((1u << VB) - 1u));
-        const float v = fmaf(sc, code, zr);
-        h8[i] = static_cast<_Float16>(v);
-        l8[i] = static_cast<_Float16>(v - static_cast<float>(h8[i]));
-      }
-      if ((tid & 15) == 0) {
-        sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
-        sg[t] = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
-      }
+      expand<KB, VB>(a, a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * a.block_bytes + 0, t, d0, tid, ac, az,
+                     avh, avl, sn, sg, static_cast<int>(slot & 15));
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c8[i] = z8[i] = h8[i] = l8[i] = static_cast<_Float16>(0.0f);
+      for (int i = 0; i < 8; ++i) {
+        ac[t][d0 + i] = az[t][d0 + i] = avh[t][d0 + i] = avl[t][d0 + i] = static_cast<_Float16>(0.0f);
+      }
       if ((tid & 15) == 0) sn[t] = sg[t] = 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ac[t][d0 + i] = c8[i];
-      az[t][d0 + i] = z8[i];
-      avh[t][d0 + i] = h8[i];
-      avl[t][d0 + i] = l8[i];
     }
   }
   __syncthreads();
@@ -149,14 +189,23 @@ __global__ __launch_bounds__(256) void decompress_kernel(DArgs a) {
       vv = mfma(xh, rl, vv);
       vv = mfma(xl, rh, vv);
     }
-    // lane (col, kg) holds tokens 4kg + r of output dim 16 nt + col
+    // lane (col, kg) holds tokens 4kg + r of output dim 16 nt + col: into this
+    // wave's staging tile (tokens x its 32 dims)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * kg + r;
-      if (t0 + t >= a.n_tokens) continue;
-      const size_t at = (static_cast<size_t>(t0 + t) * a.H + g) * 128 + 16 * nt + col;
-      put<OUT_BF16>(a.kout, at, sn[t] * fmaf(sg[t], k2[r], k1[r]));
-      put<OUT_BF16>(a.vout, at, vv[r]);
+      stk[w][t][16 * u + col] = sn[t] * fmaf(sg[t], k2[r], k1[r]);
+      stv[w][t][16 * u + col] = vv[r];
+    }
+  }
+  // lane (token l / 4, segment l % 4) stores 8 consecutive dims of K and of V
+  // (the staging tile is this wave's own: its LDS writes and reads stay in order)
+  {
+    const int t = lane >> 2, c8 = 8 * (lane & 3);
+    if (t0 + t < a.n_tokens) {
+      const size_t at = (static_cast<size_t>(t0 + t) * a.H + g) * 128 + 32 * w + c8;
+      store8<OUT_BF16>(a.kout, at, &stk[w][t][c8]);
+      store8<OUT_BF16>(a.vout, at, &stv[w][t][c8]);
     }
   }
 }
