@@ -536,3 +536,55 @@ def test_decompress_bypass_exact():
     torch.cuda.synchronize()
     assert torch.equal(kd, kt) and torch.equal(vd, vt)
     layer.close()
+
+
+def test_decode_step_graph_capture():
+    """Appending a token and decoding allocate and synchronise nothing, so the step
+    can be captured in a HIP graph: every replay, with eager work between replays,
+    gives the eager step's output bit for bit."""
+    torch = _torch()
+    say("graph capture of append + decode")
+    B, Hq, Hkv, T = 4, 32, 8, 1000
+    maxb = (T + 15) // 16
+    table = synth.block_table(320, B, maxb, "random")
+    K, V = synth.kv_host(320, B * T, Hkv, outliers=4)
+    pos = np.tile(np.arange(T), B)
+    seq = np.repeat(np.arange(B), T)
+    slots = torch.from_numpy(table[seq, pos // 16].astype(np.int64) * 16 + pos % 16).cuda()
+    kt = torch.from_numpy(K).to("cuda", torch.bfloat16)
+    vt = torch.from_numpy(V).to("cuda", torch.bfloat16)
+    layer = tq.Layer(tq.config(Hkv, 4, 4, seed=320))
+    pool = layer.new_pool(B * maxb)
+    tq.compress_kv(layer, kt, vt, slots, pool)  # the whole context; the step re-appends the last token
+    last = torch.arange(B, device="cuda") * T + (T - 1)
+    k_new, v_new, s_new = kt[last].contiguous(), vt[last].contiguous(), slots[last].contiguous()
+    q = torch.from_numpy(synth.queries_host(320, B, Hq)).to("cuda", torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    ws = tq.new_workspace(layer, B, Hq, T)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+
+    def step():
+        tq.compress_kv(layer, k_new, v_new, s_new, pool)
+        tq.decode_attn(layer, q, pool, bt, sl, T, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    x = torch.randn(512, 512, device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        y = x @ x  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        assert torch.isfinite(y).all()
+    layer.close()
