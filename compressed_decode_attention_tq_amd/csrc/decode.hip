@@ -190,14 +190,20 @@ __device__ __forceinline__ void merge_group(const Group8& g, int s0, int ns, flo
     }
   M = mg;
 }
-// `first` holds the reads of splits 0..7, issued before ns was known.
+// `first` holds the reads of splits 0..7, issued before ns was known.  The
+// rest are read four groups (32 splits) at a time, all reads of a round issued
+// before any is merged: one memory round trip per 32 splits.
 __device__ __forceinline__ float merge_partials(const float* p, int ns, int d, const Group8& first) {
   float M = -INFINITY, num = 0.0f, den = 0.0f;
   merge_group(first, 0, ns, M, num, den);
-  for (int s0 = 8; s0 < ns; s0 += 8) {
-    Group8 g;
-    read_group(p, s0, ns, d, g);
-    merge_group(g, s0, ns, M, num, den);
+  for (int s0 = 8; s0 < ns; s0 += 32) {
+    Group8 g[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + 8 * u < ns) read_group(p, s0 + 8 * u, ns, d, g[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + 8 * u < ns) merge_group(g[u], s0 + 8 * u, ns, M, num, den);
   }
   return num / den;
 }
