@@ -78,6 +78,25 @@ def copy_probe(torch, mib):
     del src, dst
 
 
+def copy_bandwidth(torch, mib=1024, reps=10):
+    """Achievable HBM bandwidth on this device: a plain device-to-device copy of
+    mib MiB (read + write), timed over reps copies with events."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * mib * (1 << 20) / (ms / 1e3) / 1e9
+
+
 def traffic_summary(fetch_csv, write_csv, mib):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the traffic kernels, scaled by
     what the same counters read for the copy probe (known bytes)."""
@@ -465,6 +484,7 @@ def main():
     tq.lib()
     if args.copy_probe_mib > 0:
         copy_probe(torch, args.copy_probe_mib)
+    copy_gbs = copy_bandwidth(torch)
     log("decode workload")
     dec, ctx = decode_workload(torch, tq, synth, args)
     comp = None
@@ -509,6 +529,9 @@ def main():
         "step_hbm_gbs": round(dec["step_hbm_gbs"], 1),
         "step_hbm_frac": round(dec["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
         "append_us": dec["append_us"],
+        "device_copy_gbs": round(copy_gbs, 1),
+        "splitk_frac_of_copy": round(dec["roofline"]["achieved"] / copy_gbs, 4),
+        "compress_frac_of_copy": round(comp["roofline"]["achieved"] / copy_gbs, 4) if comp else None,
         "compress": comp,
     }
     if extra is not None:
