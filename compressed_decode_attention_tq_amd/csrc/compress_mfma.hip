@@ -198,7 +198,7 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // QJL: keys get the residual signs and gamma (key mode 0); otherwise the key
 // mode (1 or 2: plain or norm-corrected magnitude) comes from a.km.
 template <int KB, int VB, int P, bool HAD, bool QJL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 : 8))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
   using PG = Page<KB, VB>;
   constexpr int HALF = 1 << (KB - 1);  // codebook levels per sign
   constexpr float kTop = static_cast<float>((1 << VB) - 1);
@@ -228,15 +228,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         R1[s] = __builtin_bit_cast(bf16x8, op[(1 * 4 + s) * 64]);
         R2[s] = __builtin_bit_cast(bf16x8, op[(2 * 4 + s) * 64]);
       }
-      s_hi[w][s][lane0] = op[(3 * 4 + s) * 64];
-      S1[s] = __builtin_bit_cast(half8, op[(4 * 4 + s) * 64]);
+      if constexpr (QJL) {  // the projection operands serve the residual signs only
+        s_hi[w][s][lane0] = op[(3 * 4 + s) * 64];
+        S1[s] = __builtin_bit_cast(half8, op[(4 * 4 + s) * 64]);
+      }
     }
   }
   // Consume the operands here so that the compiler's wait for these loads is
   // not placed inside the tile loop, where it would also drain the copy ring.
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    asm volatile("" ::"v"(R0[s]), "v"(S1[s]));
+    asm volatile("" ::"v"(R0[s]));
+    if constexpr (QJL) asm volatile("" ::"v"(S1[s]));
     if constexpr (!HAD) asm volatile("" ::"v"(R1[s]), "v"(R2[s]));
   }
   wait_vmcnt<0>();
