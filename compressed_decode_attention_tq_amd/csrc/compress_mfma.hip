@@ -149,6 +149,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 // One 64-lane x 16 B copy from global memory into LDS at dst + 16*lane (inline
 // asm so the compiler's waits do not drain on it; awaited with wait_vmcnt).
+// M0 is set inside the same asm statement that uses it; the compiler warns that
+// it treats M0 as reserved, and this kernel's own code uses M0 nowhere else
+// (checked in the generated code), so nothing else depends on its value.
 __device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<unsigned long>((lbyte*)dst)));

@@ -409,7 +409,6 @@ constexpr int kRing = 2;
 // The block table comes as its own read-only, non-aliased parameter.
 template <int NREP, int KB, int VB>
 __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int* __restrict__ btab) {
-  using PL = PageLayout<KB, VB>;
   using SM = ScoreMap<NREP>;
   using KL = KeyLut<KB>;
   constexpr int HPL = SM::HPL;
