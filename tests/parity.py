@@ -16,7 +16,10 @@ next to a decision boundary):
     value lies within 1e-6 ||v|| of the midpoint between the two codes; in groups
     whose fp16 scale/zero differ by an ulp, the GPU's code must be the nearest grid
     point of the GPU's own scale/zero (checked against the oracle's rotated value).
-  * all mismatches together: rate <= 1e-5.
+  * all mismatches together: rate <= 1e-5.  Every mismatch must already lie in
+    one of the bands above; the rate bounds how often that happens on a large
+    sample.  On a sample too small for one allowed (in-band) mismatch to stay
+    under the rate, up to two in-band mismatches are accepted.
 Decode protocol: both sides read the same (oracle-written) pool; relative L2 of
 the whole output <= 1e-3 (float32 output) or <= 1e-2 (bf16 output).
 """
@@ -104,7 +107,9 @@ def assert_compress_ok(st):
     assert st["value_out_of_band"] == 0, st
     assert st["value_invalid_other_meta"] == 0, st
     assert st["value_code_range"], st
-    assert st["mismatch_rate"] <= 1e-5, st
+    n_mis = st["key_mismatch"] + st["sign_mismatch"] + st["value_mismatch"]
+    total = 3 * st["vectors"] * 128
+    assert st["mismatch_rate"] <= 1e-5 or n_mis <= max(2, 1e-5 * total), st
 
 
 def rel_l2(got, ref):

@@ -588,3 +588,66 @@ def test_decode_step_graph_capture():
         assert torch.equal(out, ref), i
         assert torch.isfinite(y).all()
     layer.close()
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_layer_configurations(case):
+    """Seeded random layers: KV heads, GQA ratio, bit widths, key mode, rotation,
+    ragged lengths (some zero), a random block table, K/V rows with a token stride
+    wider than the row, split count, query and output types: GPU compress against
+    the oracle's store, then GPU decode of the GPU store against the oracle decode."""
+    torch = _torch()
+    rng = np.random.default_rng(1000 + case)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    rep = int(rng.choice([1, 2, 4, 8]))
+    Hq = Hkv * rep
+    kb, vb = int(rng.choice([2, 3, 4])), int(rng.choice([2, 3, 4]))
+    key_mode = int(rng.choice([tq.KEY_QJL, tq.KEY_MSE, tq.KEY_MSE_NC]))
+    rotation = int(rng.choice([tq.ROT_HAAR, tq.ROT_HADAMARD]))
+    B = int(rng.integers(1, 5))
+    lens = rng.integers(1, 700, B).astype(np.int32)
+    lens[rng.random(B) < 0.2] = 0
+    splits = int(rng.choice([0, 0, 1, 3, 8]))
+    q_dtype = str(rng.choice(["bf16", "f32"]))
+    out_dtype = str(rng.choice(["f32", "bf16"]))
+    say("random layer", case, dict(Hkv=Hkv, rep=rep, kb=kb, vb=vb, key_mode=key_mode, rotation=rotation,
+                                   lens=lens.tolist(), splits=splits, q=q_dtype, out=out_dtype))
+    maxb = max(1, int((lens.max() + 15) // 16) + 1)
+    table = rng.permutation(B * maxb).reshape(B, maxb).astype(np.int32)
+    N = int(lens.sum())
+    K, V = synth.kv_host(2000 + case, max(N, 1), Hkv, outliers=4)
+    K, V = K[:N], V[:N]
+    seq = np.repeat(np.arange(B), lens)
+    pos = np.concatenate([np.arange(n) for n in lens]) if N else np.zeros(0, np.int64)
+    slots = (table[seq, pos // 16].astype(np.int64) * 16 + pos % 16) if N else np.zeros(0, np.int64)
+    layer = tq.Layer(tq.config(Hkv, kb, vb, seed=3000 + case, layer=case, key_mode=key_mode, rotation=rotation))
+    pool = layer.new_pool(B * maxb)
+    if N:
+        # K and V as views into wider rows: token stride (Hkv + 1) * 128
+        kw = torch.zeros((N, Hkv + 1, 128), dtype=torch.bfloat16, device="cuda")
+        vw = torch.zeros_like(kw)
+        kw[:, :Hkv] = torch.from_numpy(K).to("cuda", torch.bfloat16)
+        vw[:, 1:] = torch.from_numpy(V).to("cuda", torch.bfloat16)
+        tq.compress_kv(layer, kw[:, :Hkv], vw[:, 1:], torch.from_numpy(slots).cuda(), pool)
+    torch.cuda.synchronize()
+    gpu_pool = pool.cpu().numpy()
+    st, layout, opool, res = parity.oracle_store(K, V, slots, B * maxb, Hkv, kb, vb, 3000 + case, layer=case,
+                                                 key_mode=KEY_MODE_NAMES[key_mode],
+                                                 rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard")
+    if N:
+        _check_compress(gpu_pool, res, st, layout, Hkv, slots, V, kb, vb)
+    q = synth.queries_host(4000 + case, B, Hq, dtype=q_dtype)
+    ref = parity.oracle_decode(q.astype(np.float64), gpu_pool, layout, Hkv, table, lens, st)
+    tq_dt = torch.bfloat16 if q_dtype == "bf16" else torch.float32
+    od = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = tq.decode_attn(layer, torch.from_numpy(q).to("cuda", tq_dt), pool, torch.from_numpy(table).cuda(),
+                         torch.from_numpy(lens).cuda(), max(int(lens.max()), 1), num_splits=splits, out_dtype=od)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert not got[lens == 0].any()
+    live = lens > 0
+    if live.any():
+        err = parity.rel_l2(got[live], ref[live])
+        print("decode rel L2 %.3e" % err)
+        assert err <= (1e-3 if out_dtype == "f32" else 1e-2), err
+    layer.close()
