@@ -111,7 +111,9 @@ int tq_abi_version(void);
  *   centroids   host out [L], ascending
  *   boundaries  host out [L-1], boundaries[i] = (centroids[i] + centroids[i+1]) / 2
  *   mse         host out, nullable: expected squared error per coordinate
- * Iterates Lloyd's conditions from the quantile midpoints to max|delta c| < 1e-14. */
+ * Iterates Lloyd's conditions from the quantile midpoints to max|delta c| < 1e-14,
+ * at most 200,000 times; the 8-bit N(0,1) codebook does not reach that tolerance
+ * within the cap and returns TQ_ERR_NOT_CONVERGED (the kernels use 2..4 bits). */
 tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids,
                             double* boundaries, double* mse);
 
