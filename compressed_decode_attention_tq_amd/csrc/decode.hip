@@ -21,6 +21,7 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "tq_internal.hpp"
@@ -164,10 +165,11 @@ struct Group8 {
 };
 // Reads of splits s0 .. s0+7 (indices clamped to below `lim`; entries past the
 // sequence's splits are read but never used).
-__device__ __forceinline__ void read_group(const float* p, int s0, int lim, int d, Group8& g) {
+// `stride` is the distance in floats between consecutive splits of p.
+__device__ __forceinline__ void read_group(const float* p, int s0, int lim, int d, Group8& g, int stride = kPart) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const float* q = p + (s0 + u < lim ? s0 + u : s0) * kPart;
+    const float* q = p + (s0 + u < lim ? s0 + u : s0) * stride;
     g.m[u] = q[128];
     g.l[u] = q[129];
     g.a[u] = q[d];
@@ -276,6 +278,94 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* part, const i
   }
 }
 
+// Small batches over many splits: one 512-lane workgroup per (KV head g,
+// sequence b, query head h).  Quarter c of the lanes (lane (c, i) holds dim i)
+// merges the head's splits c, c + 4, c + 8, ...: its first 16 splits are read
+// before the sequence length and the rest 32 at a time, so up to 64 splits take
+// one memory round trip.  The four quarters' running maxima and sums are merged
+// in LDS, then o = R_g^T o' is formed as in combine_kernel (lane (c, i) holds a
+// quarter of column i of R_g, the quarters summed in LDS in a fixed order).
+template <bool OUT_BF16, bool BYPASS>
+__global__ __launch_bounds__(512) void combine_head_kernel(const float* part, const int* seq_lens, const float* R,
+                                                           void* out, int Hq, int rep, int n_splits,
+                                                           int split_tokens) {
+  const int g = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x, c = tid >> 7, i = tid & 127;
+  const int bh = b * Hq + g * rep + h;
+  // quarter c's splits c + 4j: a slice of the head's partials with a 4-split stride
+  const float* p = part + (static_cast<size_t>(bh) * n_splits + c) * kPart;
+  const int stride = 4 * kPart;
+  const int lim = n_splits > c ? (n_splits - c + 3) / 4 : 0;  // quarter c's splits in the workspace
+  Group8 first[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (8 * k < lim) read_group(p, 8 * k, lim, i, first[k], stride);
+  float rr[32];
+  if constexpr (!BYPASS) {
+    const float* r = R + static_cast<size_t>(g) * 128 * 128 + (32 * c) * 128 + i;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) rr[u] = r[u * 128];
+  }
+  const int T = seq_lens[b];
+  // (a length above max_seq_len, a caller error, reads no partial past the workspace)
+  const int ns = T > 0 ? min((T + split_tokens - 1) / split_tokens, n_splits) : 0;
+  const int nq = ns > c ? (ns - c + 3) / 4 : 0;  // quarter c's splits of this sequence (nq <= lim)
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (8 * k < nq) merge_group(first[k], 8 * k, nq, M, num, den);
+  for (int s0 = 16; s0 < nq; s0 += 32) {
+    Group8 gr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + 8 * u < nq) read_group(p, s0 + 8 * u, nq, i, gr[u], stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + 8 * u < nq) merge_group(gr[u], s0 + 8 * u, nq, M, num, den);
+  }
+  __shared__ float qm[4], qd[4], qn[4][128], so[128], pr[4][128];
+  if (i == 0) {
+    qm[c] = M;
+    qd[c] = den;
+  }
+  qn[c][i] = num;
+  __syncthreads();
+  // every quarter forms o'[i] from the same LDS values; quarter 0 keeps it
+  float o = 0.0f;
+  const float Mx = fmaxf(fmaxf(qm[0], qm[1]), fmaxf(qm[2], qm[3]));
+  if (Mx > -INFINITY) {
+    float nn = 0.0f, dd = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float e = qm[k] == -INFINITY ? 0.0f : __expf(qm[k] - Mx);
+      nn = fmaf(e, qn[k][i], nn);
+      dd = fmaf(e, qd[k], dd);
+    }
+    o = nn / dd;
+  }
+  auto store = [&](float v) {
+    const size_t at = static_cast<size_t>(bh) * 128 + i;
+    if constexpr (OUT_BF16) {
+      const unsigned u = __float_as_uint(v);
+      static_cast<unsigned short*>(out)[at] = static_cast<unsigned short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    } else {
+      static_cast<float*>(out)[at] = v;
+    }
+  };
+  if constexpr (BYPASS) {
+    if (c == 0) store(o);
+  } else {
+    if (c == 0) so[i] = o;
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) acc = fmaf(rr[u], so[32 * c + u], acc);
+    pr[c][i] = acc;
+    __syncthreads();
+    if (c == 0) store((pr[0][i] + pr[1][i]) + (pr[2][i] + pr[3][i]));
+  }
+}
+
 }  // namespace
 
 tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q, tq_dtype q_dtype,
@@ -311,18 +401,30 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
                                              softmax_scale, ws + plan.ws_qa, part, stream);
     if (st != TQ_OK) return st;
   }
-  // 3. combine + un-rotation
+  // 3. combine + un-rotation.  Many splits over few (sequence, query head)
+  // rows: one workgroup per query head, the splits shared by four lane quarters;
+  // otherwise one workgroup per (sequence, KV head).
   {
+    const bool per_head =
+        plan.n_splits > 8 && static_cast<long long>(plan.batch) * plan.n_q_heads <= 2LL * std::max(L->cu_count, 1);
     void* fn;
-    if (bypass) fn = (out_dtype == TQ_BF16) ? reinterpret_cast<void*>(&combine_kernel<true, true>)
-                                            : reinterpret_cast<void*>(&combine_kernel<false, true>);
-    else fn = (out_dtype == TQ_BF16) ? reinterpret_cast<void*>(&combine_kernel<true, false>)
-                                     : reinterpret_cast<void*>(&combine_kernel<false, false>);
+    if (per_head) {
+      if (bypass) fn = (out_dtype == TQ_BF16) ? reinterpret_cast<void*>(&combine_head_kernel<true, true>)
+                                              : reinterpret_cast<void*>(&combine_head_kernel<false, true>);
+      else fn = (out_dtype == TQ_BF16) ? reinterpret_cast<void*>(&combine_head_kernel<true, false>)
+                                       : reinterpret_cast<void*>(&combine_head_kernel<false, false>);
+    } else {
+      if (bypass) fn = (out_dtype == TQ_BF16) ? reinterpret_cast<void*>(&combine_kernel<true, true>)
+                                              : reinterpret_cast<void*>(&combine_kernel<false, true>);
+      else fn = (out_dtype == TQ_BF16) ? reinterpret_cast<void*>(&combine_kernel<true, false>)
+                                       : reinterpret_cast<void*>(&combine_kernel<false, false>);
+    }
     const float* R = L->dR;
     int Hq = plan.n_q_heads, rep = plan.rep, ns = plan.n_splits, st = plan.split_tokens;
     void* args[] = {&part, const_cast<int**>(&seq_lens), &R, &out, &Hq, &rep, &ns, &st};
+    const dim3 grid = per_head ? dim3(L->cfg.n_kv_heads, plan.batch, plan.rep) : dim3(L->cfg.n_kv_heads, plan.batch);
     ProfScope prof(kKCombine, stream);
-    hipError_t e = hipLaunchKernel(fn, dim3(L->cfg.n_kv_heads, plan.batch), dim3(512), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(512), args, 0, s);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode combine launch: %s", hipGetErrorString(e));
   }
   hipError_t e = hipGetLastError();

@@ -249,6 +249,17 @@ def test_decode_forced_splits_and_scale(splits):
     _decode_case(torch, 2, 8, 2, [700, 1500], 3, 3, 240 + splits, num_splits=splits, scale=0.05)
 
 
+@pytest.mark.parametrize("rep,bypass", [(1, False), (8, False), (8, True)])
+def test_decode_many_splits_per_head_combine(rep, bypass):
+    """A small batch over many splits (40 requested, 21 made): the combine runs one
+    workgroup per query head, the splits shared by four lane quarters. GQA ratios 1
+    and 8, a one-split row (three empty quarters) and an empty row."""
+    torch = _torch()
+    say("decode per-head combine", rep, bypass)
+    kb, vb = (0, 0) if bypass else (4, 4)
+    _decode_case(torch, 3, 2 * rep, 2, [0, 15, 2600], kb, vb, 290 + rep, num_splits=40, bypass=bypass)
+
+
 def test_decode_split_cap():
     """One requested split over 20000 tokens: the library raises the split count so
     that no split spans more than 4096 tokens (five splits here)."""
