@@ -549,6 +549,60 @@ def test_decompress_bypass_exact():
     layer.close()
 
 
+def test_store_past_4gib():
+    """A 4.6 GiB store with every record in its top 66 blocks, so that each page
+    address is past 2^32 bytes: the GPU compress of those pages against the
+    oracle, the decode over them and the decompress from them against the
+    oracle on the same pages gathered into a small store."""
+    from oracle import decompress as odec
+    torch = _torch()
+    say("store past 4 GiB")
+    H, kb, vb, B, seed = 2, 4, 4, 2, 320
+    layer = tq.Layer(tq.config(H, kb, vb, seed=seed))
+    lay_bytes = layer.block_bytes * H
+    nblk = int(4.6 * 2 ** 30) // lay_bytes + 1
+    lens = np.array([300, 517], np.int32)
+    maxb = (int(lens.max()) + 15) // 16
+    rng = np.random.default_rng(seed)
+    ids = (nblk - 1 - rng.permutation(B * maxb)).reshape(B, maxb).astype(np.int32)
+    assert int(ids.min()) * lay_bytes > 2 ** 32
+    N = int(lens.sum())
+    K, V = synth.kv_host(seed + 1, N, H, outliers=4)
+    seq = np.repeat(np.arange(B), lens)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    slots = ids[seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    pool = layer.new_pool(nblk)
+    assert pool.numel() > 2 ** 32
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    torch.cuda.synchronize()
+    # the used pages, gathered into a small store with renumbered blocks
+    used = np.unique(ids)
+    remap = {int(b): i for i, b in enumerate(used)}
+    sub = pool.view(-1, lay_bytes)[torch.from_numpy(used.astype(np.int64)).cuda()].cpu().numpy().ravel()
+    local_slots = np.array([remap[int(x) // 16] * 16 + int(x) % 16 for x in slots], np.int64)
+    local_ids = np.vectorize(lambda b: remap[int(b)])(ids).astype(np.int32)
+    st, layout, _, res = parity.oracle_store(K, V, local_slots, len(used), H, kb, vb, seed)
+    _check_compress(sub, res, st, layout, H, local_slots, V, kb, vb)
+    # decode over the top of the store
+    q = synth.queries_host(seed + 2, B, 4 * H)
+    ref = parity.oracle_decode(q.astype(np.float64), sub, layout, H, local_ids, lens, st)
+    out = tq.decode_attn(layer, torch.from_numpy(q).to("cuda", torch.bfloat16), pool, torch.from_numpy(ids).cuda(),
+                         torch.from_numpy(lens).cuda(), int(lens.max()))
+    torch.cuda.synchronize()
+    err = parity.rel_l2(out.float().cpu().numpy(), ref)
+    print("decode rel L2 %.3e" % err)
+    assert err <= 1e-3, err
+    # decompress from the top of the store
+    kd, vd = tq.decompress_kv(layer, pool, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kr, vr = odec.decompress(sub, layout, H, local_slots, st)
+    for got, want, name in ((kd.cpu().numpy(), kr, "K"), (vd.cpu().numpy(), vr, "V")):
+        assert parity.rel_l2(got, want) <= 1e-6, name
+    del pool
+    layer.close()
+
+
 def test_decode_step_graph_capture():
     """Appending a token and decoding allocate and synchronise nothing, so the step
     can be captured in a HIP graph: every replay, with eager work between replays,
