@@ -531,6 +531,46 @@ def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype):
     layer.close()
 
 
+def test_decompress_full_size_sampled():
+    """The headline store (16 x 4096 tokens x 8 KV heads, K4/V4, outlier channels,
+    random block table) written by the GPU compressor, all 65,536 tokens
+    reconstructed to bf16 in one launch in page order (every tile one whole page,
+    as timed), checked on 1024 sampled tokens against the oracle's reconstruction
+    of their pages gathered into a small store."""
+    from oracle import decompress as odec
+    torch = _torch()
+    say("decompress full size")
+    B, T, H, kb, vb, seed = 16, 4096, 8, 4, 4, 330
+    N = B * T
+    k, v = synth.kv_device(seed, N, H, outliers=4)
+    layer = tq.Layer(tq.config(H, kb, vb, seed=seed))
+    pool = layer.new_pool(N // 16)
+    table = synth.block_table(seed, B, T // 16, "random")
+    b_of = np.repeat(np.arange(B), T)
+    pos = np.tile(np.arange(T), B)
+    slots = table[b_of, pos // 16].astype(np.int64) * 16 + pos % 16
+    slots_t = torch.from_numpy(slots).cuda()
+    tq.compress_kv(layer, k, v, slots_t, pool)
+    kd, vd = tq.decompress_kv(layer, pool, slots_t, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(seed).choice(N, 1024, replace=False))
+    lay_bytes = layer.block_bytes * H
+    blocks = np.unique(slots[idx] // 16)
+    sub = pool.view(-1, lay_bytes)[torch.from_numpy(blocks).cuda()].cpu().numpy().ravel()
+    remap = {int(b): i for i, b in enumerate(blocks)}
+    local = np.array([remap[int(x) // 16] * 16 + int(x) % 16 for x in slots[idx]], np.int64)
+    st = parity.ostate.LayerState(seed, 0, H, 128, kb, vb, 32)
+    layout = parity.lay.StoreLayout(128, kb, vb, 32)
+    kr, vr = odec.decompress(sub, layout, H, local, st)
+    ti = torch.from_numpy(idx).cuda()
+    for got, ref, name in ((kd[ti].float().cpu().numpy(), kr, "K"), (vd[ti].float().cpu().numpy(), vr, "V")):
+        scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+        # bf16 of the fp32 result: within one bf16 rounding of the exact value
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * scale), name
+        print(name, "bf16 rel L2 %.2e" % parity.rel_l2(got, ref))
+    layer.close()
+
+
 def test_decompress_bypass_exact():
     """Bypass layers return their stored bf16 values bit for bit."""
     torch = _torch()
