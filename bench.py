@@ -516,7 +516,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the compressed-KV path runs on one device per process and "
-              "this build has no multi-GPU path (--gpus %d refused)" % args.gpus, file=sys.stderr)
+              "the library has no multi-GPU path (--gpus %d refused)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -80,7 +80,7 @@ extern "C" {
 typedef enum {
   TQ_OK = 0,
   TQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent sizes     */
-  TQ_ERR_UNSUPPORTED = 2,      /* a shape / bit width / dtype this build has no kernel for */
+  TQ_ERR_UNSUPPORTED = 2,      /* a shape / bit width / dtype the library has no kernel for */
   TQ_ERR_OUT_OF_MEMORY = 3,    /* device allocation in tq_layer_create failed         */
   TQ_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed           */
   TQ_ERR_NOT_CONVERGED = 5     /* Lloyd-Max iteration hit its iteration cap           */
