@@ -33,6 +33,15 @@ quantisation with per-group scale/zero; "tiny-turboquant 0.18.0",
              (code_j = 0 when scale == 0)
 The codes are computed from the stored (fp16) scale and zero so that the
 decoder's zero + scale * code is the nearest grid point.
+
+Values coded like the keys' codebook part (value mode "mse"; "5x Faster LLM
+Inference? ...", "What is TurboQuant-GPU?": 3-bit MSE values, and "Example 4:
+Kernel-Level Operations": normalise -> rotate -> Lloyd-Max quantise -> pack for
+both K and V), with the b_v-bit codebook of the same family:
+    nv    = ||v||                                    stored as fp16
+    t     = sqrt(d) * R v / nv       (t = 0 if nv = 0)
+    idx_j = #{i : beta_i < t_j}
+and the decoder's value is (nv16 / sqrt d) c[idx] in the rotated basis.
 """
 
 import math
@@ -43,6 +52,7 @@ from . import codebook, layout as lay
 
 
 KEY_MODES = ("qjl", "mse", "mse_nc")
+VALUE_MODES = ("group", "mse")
 
 
 def compress_keys(K, R, S, centroids, boundaries, key_mode="qjl"):
@@ -103,6 +113,18 @@ def compress_values(V, R, v_bits, group):
     return {"vrot": vrot, "codes": codes, "scale16": scale16, "zero16": zero16}
 
 
+def compress_values_mse(V, R, centroids, boundaries):
+    """Values coded like the keys' codebook part: V [n, d] float64."""
+    V = np.asarray(V, dtype=np.float64)
+    d = V.shape[-1]
+    n = np.sqrt(np.sum(V * V, axis=-1))
+    vrot = V @ R.T
+    safe = np.where(n > 0.0, n, 1.0)
+    t = np.where((n > 0.0)[:, None], (math.sqrt(d) / safe)[:, None] * vrot, 0.0)
+    idx = codebook.quantize_index(t, boundaries)
+    return {"vrot": vrot, "n": n, "t": t, "codes": idx, "n16": n.astype(np.float16)}
+
+
 def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     """Compress K, V [N, H_kv, d] (float64 values of the inputs) into `pool` at `slots` [N].
 
@@ -115,14 +137,21 @@ def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     valid = slots >= 0
     K, V, slots = K[valid], V[valid], slots[valid]
     n_tok, H, d = K.shape
+    value_mode = getattr(state, "value_mode", "group")
+    if value_mode != layout.value_mode:
+        raise ValueError("layer state (%s values) and layout (%s values) disagree" % (value_mode, layout.value_mode))
     out = {}
     for h in range(H):
         ck = compress_keys(K[:, h], state.R[h], state.S[h], state.centroids, state.boundaries,
                            getattr(state, "key_mode", "qjl"))
-        cv = compress_values(V[:, h], state.R[h], layout.v_bits, layout.group)
-        lay.put_records(pool, layout, H, slots, h, {
-            "idx": ck["idx"], "z": ck["z"], "n16": ck["n16"], "g16": ck["gamma16"],
-            "vcode": cv["codes"], "scale16": cv["scale16"], "zero16": cv["zero16"]})
+        rec = {"idx": ck["idx"], "z": ck["z"], "n16": ck["n16"], "g16": ck["gamma16"]}
+        if value_mode == "mse":
+            cv = compress_values_mse(V[:, h], state.R[h], state.v_centroids, state.v_boundaries)
+            rec.update(vcode=cv["codes"], vn16=cv["n16"])
+        else:
+            cv = compress_values(V[:, h], state.R[h], layout.v_bits, layout.group)
+            rec.update(vcode=cv["codes"], scale16=cv["scale16"], zero16=cv["zero16"])
+        lay.put_records(pool, layout, H, slots, h, rec)
         if keep:
             out[h] = (ck, cv)
     return out

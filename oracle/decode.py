@@ -16,6 +16,7 @@ For query head h of sequence b, KV head g = h // (H_q / H_kv):
           sigma_ij = 2 z_ij - 1,   kappa = sqrt(pi/2) / m,   tau = 1/sqrt(d) by default
     p   = softmax(s)
     o'  = sum_i p_i * vhat'_i,     vhat'_ij = zero16_{i,g(j)} + scale16_{i,g(j)} * code_ij
+                                   (with MSE values: vhat'_i = (nv16_i / sqrt d) c_v[code_i])
     out = R_g^T o'
 The QJL term is the estimator <rho, q'> ~ ||rho|| sqrt(pi/2)/m <S q', sign(S rho)>
 of the residual's inner product (QJL / TurboQuant, cited by the pages).
@@ -47,9 +48,17 @@ def gather(pool, layout, n_kv_heads, block_table_row, seq_len, head):
         return {"k": lay.bf16_bits_to_f64(kb), "v": lay.bf16_bits_to_f64(vb)}
     slots = blocks * lay.P + offs
     r = lay.get_records(pool, layout, n_kv_heads, slots, head)
-    for k in ("n16", "g16", "scale16", "zero16"):
-        r[k] = r[k].astype(np.float64)
+    for k in ("n16", "g16", "scale16", "zero16", "vn16"):
+        if k in r:
+            r[k] = r[k].astype(np.float64)
     return r
+
+
+def value_rows(f, layout, state):
+    """The gathered tokens' values in the rotated basis (group grid or MSE codebook)."""
+    if layout.value_mode == "mse":
+        return (f["vn16"] / math.sqrt(layout.d))[:, None] * np.asarray(state.v_centroids)[f["vcode"]]
+    return dequant_values(f, layout.group)
 
 
 def dequant_values(f, group):
@@ -110,7 +119,7 @@ def decode(q, pool, layout, n_kv_heads, block_table, seq_lens, state=None,
             if layout.bypass:
                 vals = f["v"]
             else:
-                vals = dequant_values(f, layout.group)
+                vals = value_rows(f, layout, state)
             for h in range(g * rep, (g + 1) * rep):
                 if layout.bypass:
                     s = tau * (f["k"] @ q[b, h])

@@ -8,6 +8,7 @@ for token i of KV head g,
     khat_i = (n16_i / sqrt d) R_g^T ( c[idx_i] + kappa * gamma16_i * S_g^T sigma_i ),
              sigma_ij = 2 z_ij - 1,  kappa = sqrt(pi/2) / m
     vhat_i = R_g^T ( zero16 + scale16 * code_i )          (per 32-wide group)
+             or (nv16_i / sqrt d) R_g^T c_v[code_i]       (MSE values)
 so q . khat_i = (n16_i / sqrt d) ( q'.c[idx_i] + kappa gamma16_i (S_g q').sigma_i )
 with q' = R_g q, the score of "How 0xsero/turboquant works", "Key Storage and
 Attention Scoring" before the softmax scale.  Without QJL (gamma16 = 0) khat is
@@ -49,7 +50,11 @@ def decompress(pool, layout, n_kv_heads, slots, state=None):
         kappa = math.sqrt(math.pi / 2.0) / state.S[g].shape[0]
         inner = chat + kappa * g16[:, None] * (sigma @ state.S[g])
         K[keep, g] = (n16 / math.sqrt(d))[:, None] * (inner @ state.R[g])
-        scale = np.repeat(r["scale16"].astype(np.float64), layout.group, axis=1)
-        zero = np.repeat(r["zero16"].astype(np.float64), layout.group, axis=1)
-        V[keep, g] = (zero + scale * r["vcode"]) @ state.R[g]
+        if layout.value_mode == "mse":
+            vn16 = r["vn16"].astype(np.float64)
+            V[keep, g] = (vn16 / math.sqrt(d))[:, None] * (np.asarray(state.v_centroids)[r["vcode"]] @ state.R[g])
+        else:
+            scale = np.repeat(r["scale16"].astype(np.float64), layout.group, axis=1)
+            zero = np.repeat(r["zero16"].astype(np.float64), layout.group, axis=1)
+            V[keep, g] = (zero + scale * r["vcode"]) @ state.R[g]
     return K, V

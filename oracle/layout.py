@@ -23,6 +23,11 @@ stream, bit k of the stream being bit k%8 of byte k//8.
                            2i + k//4 of four codes, element k % 4; one b-bit
                            stream in the order (block, group, element)
   Vsz [P][d/G][2] fp16     per group: scale then zero
+With MSE values (value_mode "mse": values coded like the keys' codebook part,
+"5x Faster LLM Inference? ...", "What is TurboQuant-GPU?") Vc holds b_v-bit
+codebook indices in the same stream order and the last field is
+  Vn  [P] fp16             ||v||
+so that K2 + QJL / V3 is 102 bytes per (token, head) and 1632 per page.
 Bypass (uncompressed) layers: region = Kb [P][d] bf16 (token-major: one token's
 d keys together) followed by Vb [d][P] bf16 (dim-major: the P tokens' values of
 one dim together), so that a page's values load as the matrix-core operand of
@@ -32,11 +37,15 @@ P.V with one contiguous run per lane.
 import numpy as np
 
 P = 16
+VALUE_MODES = ("group", "mse")
 
 
 class StoreLayout:
-    def __init__(self, d=128, k_bits=4, v_bits=4, group=32, bypass=False, m=None):
+    def __init__(self, d=128, k_bits=4, v_bits=4, group=32, bypass=False, m=None, value_mode="group"):
+        if value_mode not in VALUE_MODES:
+            raise ValueError("unknown value mode %r" % (value_mode,))
         self.d, self.k_bits, self.v_bits, self.group, self.bypass = d, k_bits, v_bits, group, bypass
+        self.value_mode = value_mode
         self.m = d if m is None else m
         if bypass:
             self.kb_bytes = d * 2
@@ -48,7 +57,8 @@ class StoreLayout:
         self.ks_bytes = self.m // 8
         self.kn_bytes = 4
         self.vc_bytes = d * v_bits // 8
-        self.vsz_bytes = 4 * (d // group)
+        # the last field: group scale/zero, or one fp16 norm with MSE values
+        self.vsz_bytes = 4 * (d // group) if value_mode == "group" else 2
         sizes = [self.kc_bytes, self.ks_bytes, self.kn_bytes, self.vc_bytes, self.vsz_bytes]
         offs, o = [], 0
         for s in sizes:
@@ -131,7 +141,8 @@ def put_records(pool, layout, n_kv_heads, slots, head, rec):
     """Store compressed records of one KV head at `slots`.
 
     rec: idx [N, d] and z [N, m] (ints), n16, g16 [N] (float16),
-    vcode [N, d] (ints), scale16, zero16 [N, d/G] (float16).
+    vcode [N, d] (ints), scale16, zero16 [N, d/G] (float16); with MSE values
+    vn16 [N] (float16) in place of scale16 and zero16.
     """
     slots = np.asarray(slots, dtype=np.int64)
     blocks, offs = np.divmod(slots, P)
@@ -142,28 +153,35 @@ def put_records(pool, layout, n_kv_heads, slots, head, rec):
     kn = np.stack([np.asarray(rec["n16"], np.float16), np.asarray(rec["g16"], np.float16)], axis=-1)
     at = (base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(4)
     pool[at] = kn.view(np.uint8).reshape(len(slots), 4)
-    sz = np.stack([np.asarray(rec["scale16"], np.float16), np.asarray(rec["zero16"], np.float16)], axis=-1)
+    if layout.value_mode == "mse":
+        sz = np.asarray(rec["vn16"], np.float16).reshape(len(slots), 1)
+    else:
+        sz = np.stack([np.asarray(rec["scale16"], np.float16), np.asarray(rec["zero16"], np.float16)], axis=-1)
     at = (base + layout.off_vsz + offs * layout.vsz_bytes)[:, None] + np.arange(layout.vsz_bytes)
-    pool[at] = sz.reshape(len(slots), -1).view(np.uint8)
+    pool[at] = np.ascontiguousarray(sz.reshape(len(slots), -1)).view(np.uint8)
 
 
 def get_records(pool, layout, n_kv_heads, slots, head):
     """Read the compressed records of one KV head at `slots` (fields as in put_records;
-    n16, g16, scale16, zero16 returned as float16)."""
+    n16, g16, scale16, zero16 or vn16 returned as float16)."""
     slots = np.asarray(slots, dtype=np.int64)
     blocks, offs = np.divmod(slots, P)
     base = (blocks * n_kv_heads + head) * layout.block_bytes
     kn = pool[(base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(4)]
     kn = np.ascontiguousarray(kn).view(np.float16)
     sz = pool[(base + layout.off_vsz + offs * layout.vsz_bytes)[:, None] + np.arange(layout.vsz_bytes)]
-    sz = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots), -1, 2)
-    return {
+    out = {
         "idx": _bit_read(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits),
         "z": _bit_read(pool, _field_bits(layout, base, offs, "z"), 1),
         "n16": kn[:, 0], "g16": kn[:, 1],
         "vcode": _bit_read(pool, _field_bits(layout, base, offs, "vcode"), layout.v_bits),
-        "scale16": sz[:, :, 0], "zero16": sz[:, :, 1],
     }
+    if layout.value_mode == "mse":
+        out["vn16"] = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots))
+    else:
+        sz = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots), -1, 2)
+        out["scale16"], out["zero16"] = sz[:, :, 0], sz[:, :, 1]
+    return out
 
 
 def bypass_byte_index(layout, base, offs):

@@ -32,16 +32,24 @@ def reconstruct_values(cv, R, group):
     return (zero + scale * cv["codes"]) @ R
 
 
+def reconstruct_values_mse(cv, R, centroids, d):
+    """v_hat = (nv16 / sqrt(d)) R^T c[idx] for values coded like the keys' codebook part."""
+    chat = np.asarray(centroids)[cv["codes"]]
+    return (cv["n16"].astype(np.float64) / math.sqrt(d))[:, None] * (chat @ R)
+
+
 def cosine_rows(a, b):
     num = np.sum(a * b, axis=-1)
     den = np.linalg.norm(a, axis=-1) * np.linalg.norm(b, axis=-1)
     return num / den
 
 
-def record_bytes(d, k_bits, v_bits, group, m=None):
-    """Bytes per (token, head): K codes + signs + 2 fp16 norms, V codes + fp16 scale/zero per group."""
+def record_bytes(d, k_bits, v_bits, group, m=None, value_mode="group"):
+    """Bytes per (token, head): K codes + signs + 2 fp16 norms, V codes + fp16 scale/zero per
+    group (or one fp16 norm with MSE values)."""
     m = d if m is None else m
-    return d * k_bits // 8 + m // 8 + 4 + d * v_bits // 8 + 4 * (d // group)
+    v_meta = 4 * (d // group) if value_mode == "group" else 2
+    return d * k_bits // 8 + m // 8 + 4 + d * v_bits // 8 + v_meta
 
 
 def compression_ratio(record, d=128, baseline_bits=16):

@@ -85,10 +85,11 @@ def qjl_projection(seed, layer, head, d, m=None):
 
 
 class LayerState:
-    """All state of one compressed layer: R and S per KV head plus the key codebook."""
+    """All state of one compressed layer: R and S per KV head plus the key codebook
+    (and, with MSE values, the b_v-bit value codebook of the same family)."""
 
     def __init__(self, seed, layer, n_kv_heads, d, k_bits, v_bits, group, dist="gaussian", key_mode="qjl",
-                 rotation_kind="haar"):
+                 rotation_kind="haar", value_mode="group"):
         self.seed, self.layer, self.n_kv_heads, self.d = seed, layer, n_kv_heads, d
         self.k_bits, self.v_bits, self.group, self.dist = k_bits, v_bits, group, dist
         self.key_mode = key_mode  # "qjl", "mse" or "mse_nc" (see compress.compress_keys)
@@ -96,6 +97,11 @@ class LayerState:
         self.R = np.stack([rotation(rotation_kind, seed, layer, h, d) for h in range(n_kv_heads)])
         self.S = np.stack([qjl_projection(seed, layer, h, d) for h in range(n_kv_heads)])
         self.centroids, self.boundaries = stored_codebook(k_bits, dist, d)
+        if value_mode not in ("group", "mse"):
+            raise ValueError("unknown value mode %r" % (value_mode,))
+        self.value_mode = value_mode
+        if value_mode == "mse":
+            self.v_centroids, self.v_boundaries = stored_codebook(v_bits, dist, d)
 
 
 def stored_codebook(bits, dist="gaussian", d=128):

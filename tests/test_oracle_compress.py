@@ -160,3 +160,56 @@ def test_hadamard_rotation_reconstruction_cosine():
     ck = compress.compress_keys(K, st.R[0], st.S[0], st.centroids, st.boundaries)
     cos = metrics.cosine_rows(K, metrics.reconstruct_keys_mse(ck, st.R[0], st.centroids, D)).mean()
     assert abs(cos - math.sqrt(1.0 - 0.03455)) < 0.004
+
+
+# ------------------------------------------------ values coded like the keys
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("outliers", [False, True])
+def test_mse_values_reconstruction_cosine(bits, outliers):
+    """Values normalised, rotated and Lloyd-Max quantised: mean cos(v, v_hat) ->
+    sqrt(1 - D_b) (D_b the codebook's distortion, a closed-form integral); at 3 bits
+    the 0.98 cosine the pages give for their 3-bit values."""
+    rng = np.random.default_rng(100 + bits)
+    V = rng.standard_normal((4096, D))
+    if outliers:
+        V[:, rng.choice(D, 4, replace=False)] *= 10.0
+    R = state.haar_rotation(12, 0, 1, D)
+    c, b, mse = _cb(bits)
+    cv = compress.compress_values_mse(V, R, c, b)
+    cos = metrics.cosine_rows(V, metrics.reconstruct_values_mse(cv, R, c, D)).mean()
+    assert abs(cos - math.sqrt(1.0 - mse)) < 3e-3
+    if bits == 3:
+        assert cos >= 0.98
+
+
+def test_mse_value_codes_are_nearest_centroid_of_rotated_standardised_value():
+    """Brute force with pure-Python loops from the definitions: unit vector,
+    rotation, nearest 3-bit centroid; the stored norm is fp16(||v||)."""
+    rng = np.random.default_rng(15)
+    V = rng.standard_normal((48, D)) * rng.uniform(0.05, 40.0, (48, 1))
+    R = state.haar_rotation(4, 2, 0, D)
+    c, b, _ = _cb(3)
+    cv = compress.compress_values_mse(V, R, c, b)
+    for i in range(48):
+        unit = V[i] / math.sqrt(sum(x * x for x in V[i]))
+        t = [math.sqrt(D) * sum(R[r, j] * unit[j] for j in range(D)) for r in range(D)]
+        idx = [min(range(len(c)), key=lambda e: abs(tj - c[e])) for tj in t]
+        assert idx == list(cv["codes"][i])
+    assert np.array_equal(cv["n16"], np.linalg.norm(V, axis=1).astype(np.float16))
+
+
+def test_mse_values_zero_vector():
+    """A zero value vector stores norm 0, so its reconstruction is exactly zero."""
+    c, b, _ = _cb(3)
+    R = state.haar_rotation(1, 0, 0, D)
+    cv = compress.compress_values_mse(np.zeros((2, D)), R, c, b)
+    assert not cv["n16"].any()
+    assert not metrics.reconstruct_values_mse(cv, R, c, D).any()
+
+
+def test_value_mode_rejects_unknown():
+    from oracle import layout
+    with pytest.raises(ValueError):
+        layout.StoreLayout(128, 2, 3, 32, value_mode="fp8")
+    with pytest.raises(ValueError):
+        state.LayerState(1, 0, 1, D, 2, 3, 32, value_mode="fp8")

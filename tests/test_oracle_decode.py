@@ -11,10 +11,10 @@ D = 128
 
 
 def _setup(k_bits=3, v_bits=2, B=2, Hq=4, Hkv=2, lens=(40, 17), seed=0, bypass=False, key_mode="qjl",
-           rotation_kind="haar"):
+           rotation_kind="haar", value_mode="group"):
     st = state.LayerState(200 + seed, 0, Hkv, D, k_bits, v_bits, 32, key_mode=key_mode,
-                          rotation_kind=rotation_kind)
-    lay = layout.StoreLayout(D, k_bits, v_bits, 32, bypass=bypass)
+                          rotation_kind=rotation_kind, value_mode=value_mode)
+    lay = layout.StoreLayout(D, k_bits, v_bits, 32, bypass=bypass, value_mode=value_mode)
     maxb = (max(lens) + 15) // 16
     table = np.random.default_rng(seed).permutation(B * maxb).reshape(B, maxb)
     pool = layout.new_pool(B * maxb, Hkv, lay)
@@ -181,3 +181,48 @@ def test_decompressed_store_gives_the_decode(key_mode, bypass):
     # negative slots give zero rows
     Kd, Vd = decompress.decompress(pool, lay, 2, np.array([-1, table[0][0] * 16]), None if bypass else st)
     assert not Kd[0].any() and not Vd[0].any() and Vd[1].any()
+
+
+@pytest.mark.parametrize("k_bits,v_bits", [(2, 3), (4, 4)])
+def test_mse_values_attention_over_reconstruction(k_bits, v_bits):
+    """With MSE values the decode is textbook attention in the original basis over
+    the reconstructed keys and v_hat = (nv16/sqrt d) R^T c_v[idx] (its own b_v-bit
+    codebook); split-K partials merge to the one-pass result."""
+    st, lay, table, pool, lens, q, KV = _setup(k_bits=k_bits, v_bits=v_bits, value_mode="mse")
+    out = decode.decode(q, pool, lay, 2, table, lens, st)
+    for b, T in enumerate(lens):
+        for g in range(2):
+            ck, cv = KV[b][2][g]
+            Kh = metrics.reconstruct_keys_qjl(ck, st.R[g], st.S[g], st.centroids, D)
+            Vh = metrics.reconstruct_values_mse(cv, st.R[g], st.v_centroids, D)
+            for h in range(2 * g, 2 * g + 2):
+                s = Kh @ q[b, h] / math.sqrt(D)
+                w = np.exp(s - s.max())
+                ref = (w / w.sum()) @ Vh
+                assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * max(1.0, np.abs(ref).max())
+    two = decode.decode(q, pool, lay, 2, table, lens, st, split_tokens=7)
+    assert np.max(np.abs(out - two)) < 1e-12
+
+
+def test_mse_values_decompressed_store_gives_the_decode():
+    """Textbook attention over the decompressed store (MSE values) equals the decode."""
+    from oracle import decompress
+    st, lay, table, pool, lens, q, _ = _setup(k_bits=2, v_bits=3, value_mode="mse")
+    out = decode.decode(q, pool, lay, 2, table, lens, st)
+    for b, T in enumerate(lens):
+        pos = np.arange(T)
+        slots = table[b][pos // 16] * 16 + pos % 16
+        Kd, Vd = decompress.decompress(pool, lay, 2, slots, st)
+        for h in range(4):
+            g = h // 2
+            s = Kd[:, g] @ q[b, h] / math.sqrt(D)
+            w = np.exp(s - s.max())
+            ref = (w / w.sum()) @ Vd[:, g]
+            assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * max(1.0, np.abs(ref).max())
+
+
+def test_mse_values_state_and_layout_must_agree():
+    st = state.LayerState(1, 0, 1, D, 2, 3, 32, value_mode="mse")
+    lay = layout.StoreLayout(D, 2, 3, 32)
+    with pytest.raises(ValueError):
+        compress.compress_into_pool(np.ones((1, 1, D)), np.ones((1, 1, D)), [0], layout.new_pool(1, 1, lay), lay, st)

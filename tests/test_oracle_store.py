@@ -167,3 +167,57 @@ def test_bypass_placement_by_hand():
     assert pool[base + 4096 + 32 * 3 + 12] == (0x4100 + 3 + 1) & 0xff
     k2, v2 = layout.read_bypass(pool, lay, 3, 2 * 16 + 5, 1)
     assert np.array_equal(v2, v)
+
+
+def test_mse_value_layout_is_the_pages_102_byte_record():
+    """K2 + QJL / V3 with MSE values: the worked 102-byte record and 5.02x of the
+    byte-accounting fixture; the key fields keep their offsets."""
+    ref = json.load(open(os.path.join(GOLDEN, "byte_accounting.json")))
+    lay = layout.StoreLayout(128, 2, 3, 32, value_mode="mse")
+    assert lay.record_bytes() == ref["blog_layout_bytes"]
+    assert lay.block_bytes == 16 * ref["blog_layout_bytes"]
+    assert metrics.record_bytes(128, 2, 3, 32, value_mode="mse") == ref["blog_layout_bytes"]
+    assert abs(metrics.compression_ratio(lay.record_bytes()) - ref["blog_ratio"]) < 1e-4
+    assert all(o % 64 == 0 for o in lay.field_offsets())
+    assert lay.field_offsets()[:4] == layout.StoreLayout(128, 2, 3, 32).field_offsets()[:4]
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 3), (4, 4)])
+def test_mse_value_record_round_trip(kb, vb):
+    """MSE-value records (codes + one fp16 norm) at scattered slots read back exactly;
+    rewriting one token leaves its page neighbours intact."""
+    lay = layout.StoreLayout(128, kb, vb, 32, value_mode="mse")
+    pool = layout.new_pool(6, 2, lay)
+    slots = np.array([37, 5, 36, 80, 38, 0, 95, 17])
+    rng = np.random.default_rng(kb * 7 + vb)
+
+    def recs(n):
+        return {"idx": rng.integers(0, 1 << kb, (n, 128)), "z": rng.integers(0, 2, (n, 128)),
+                "n16": rng.standard_normal(n).astype(np.float16), "g16": rng.standard_normal(n).astype(np.float16),
+                "vcode": rng.integers(0, 1 << vb, (n, 128)), "vn16": rng.standard_normal(n).astype(np.float16)}
+
+    rec = recs(len(slots))
+    layout.put_records(pool, lay, 2, slots, 0, rec)
+    got = layout.get_records(pool, lay, 2, slots, 0)
+    assert set(got) == set(rec)
+    for k in rec:
+        assert np.array_equal(got[k], rec[k]), k
+    rec2 = recs(1)
+    layout.put_records(pool, lay, 2, [36], 0, rec2)
+    again = layout.get_records(pool, lay, 2, slots, 0)
+    for k in rec:
+        assert np.array_equal(np.delete(again[k], 2, axis=0), np.delete(rec[k], 2, axis=0)), k
+        assert np.array_equal(again[k][2], rec2[k][0]), k
+
+
+def test_mse_value_norm_placement_by_hand():
+    """The fp16 norm of slot 21 (block 1, offset 5) of head 1 of 2, K2/V3: region
+    3 (1632 bytes each), field offset 1600, token offset 2 * 5."""
+    lay = layout.StoreLayout(128, 2, 3, 32, value_mode="mse")
+    pool = layout.new_pool(2, 2, lay)
+    rec = {"idx": np.zeros((1, 128), int), "z": np.zeros((1, 128), int), "n16": np.zeros(1, np.float16),
+           "g16": np.zeros(1, np.float16), "vcode": np.zeros((1, 128), int), "vn16": np.array([1.5], np.float16)}
+    layout.put_records(pool, lay, 2, [21], 1, rec)
+    at = 3 * 1632 + 1600 + 10
+    assert list(np.nonzero(pool)[0]) == [at + 1]  # 1.5 = 0x3E00: low byte 0, high byte 0x3E
+    assert pool[at + 1] == 0x3E
