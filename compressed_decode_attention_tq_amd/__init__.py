@@ -18,6 +18,7 @@ F32, BF16, F16 = 0, 1, 2
 DIST_GAUSSIAN, DIST_SPHERE = 0, 1
 KEY_QJL, KEY_MSE, KEY_MSE_NC = 0, 1, 2  # key estimator (tq_key_mode)
 ROT_HAAR, ROT_HADAMARD = 0, 1  # rotation family (tq_rotation)
+VAL_GROUP, VAL_MSE = 0, 1  # value coding (tq_value_mode)
 EXPORTED = [
     "tq_last_error", "tq_abi_version", "tq_codebook_build", "tq_layer_state_host",
     "tq_layer_create", "tq_layer_destroy", "tq_store_layout", "tq_compress_kv",
@@ -39,13 +40,14 @@ class LayerConfig(ctypes.Structure):
         ("v_bits", ctypes.c_int), ("v_group", ctypes.c_int), ("block_size", ctypes.c_int),
         ("layer", ctypes.c_int), ("dist", ctypes.c_int), ("seed", ctypes.c_ulonglong),
         ("bypass", ctypes.c_int), ("key_mode", ctypes.c_int), ("rotation", ctypes.c_int),
+        ("value_mode", ctypes.c_int),
     ]
 
 
 def config(n_kv_heads, k_bits=4, v_bits=4, seed=0, layer=0, dist=DIST_GAUSSIAN, bypass=False,
-           head_dim=128, v_group=32, block_size=16, key_mode=KEY_QJL, rotation=ROT_HAAR):
+           head_dim=128, v_group=32, block_size=16, key_mode=KEY_QJL, rotation=ROT_HAAR, value_mode=VAL_GROUP):
     return LayerConfig(head_dim, n_kv_heads, k_bits, v_bits, v_group, block_size, layer, dist, seed,
-                       int(bool(bypass)), key_mode, rotation)
+                       int(bool(bypass)), key_mode, rotation, value_mode)
 
 
 _LIB = None

@@ -51,6 +51,8 @@ tq_status validate_config(const tq_layer_config* cfg) {
     return fail(TQ_ERR_INVALID_ARGUMENT, "unknown key mode %d", static_cast<int>(cfg->key_mode));
   if (cfg->rotation != TQ_ROT_HAAR && cfg->rotation != TQ_ROT_HADAMARD)
     return fail(TQ_ERR_INVALID_ARGUMENT, "unknown rotation family %d", static_cast<int>(cfg->rotation));
+  if (cfg->value_mode != TQ_VAL_GROUP && cfg->value_mode != TQ_VAL_MSE)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "unknown value mode %d", static_cast<int>(cfg->value_mode));
   return TQ_OK;
 }
 
@@ -72,7 +74,8 @@ tq_status make_layout(const tq_layer_config* cfg, Layout* out) {
   l.ks_bytes = kDim / 8;
   l.kn_bytes = 4;
   l.vc_bytes = kDim * cfg->v_bits / 8;
-  l.vsz_bytes = 4 * (kDim / kGroup);
+  // last field: per-group fp16 scale/zero, or one fp16 norm with MSE values
+  l.vsz_bytes = cfg->value_mode == TQ_VAL_MSE ? 2 : 4 * (kDim / kGroup);
   size_t o = 0;
   l.off_kc = o; o += static_cast<size_t>(kPage) * l.kc_bytes;
   l.off_ks = o; o += static_cast<size_t>(kPage) * l.ks_bytes;
@@ -85,6 +88,21 @@ tq_status make_layout(const tq_layer_config* cfg, Layout* out) {
 }
 
 namespace {
+
+// Stored codebook of `bits` bits: Lloyd-Max centroids rounded to float16 (the
+// decode kernels' MFMA operand type), boundaries at the exact midpoints of the
+// stored centroids, both as float32 values.
+tq_status stored_codebook(int bits, tq_dist dist, float* cent, float* bnd) {
+  double c[256], b[255];
+  tq_status st = lloyd_max(bits, dist, kDim, c, b, nullptr);
+  if (st != TQ_OK) return st;
+  const int L = 1 << bits;
+  double c16[256];
+  for (int i = 0; i < L; ++i) c16[i] = static_cast<double>(static_cast<_Float16>(c[i]));
+  for (int i = 0; i < L; ++i) cent[i] = static_cast<float>(c16[i]);
+  for (int i = 0; i + 1 < L; ++i) bnd[i] = static_cast<float>(0.5 * (c16[i] + c16[i + 1]));
+  return TQ_OK;
+}
 
 // Host state of one layer: R, S (float32, [H][d][d]) and the float32 codebook.
 tq_status build_state(const tq_layer_config* cfg, std::vector<float>* R, std::vector<float>* S,
@@ -109,18 +127,9 @@ tq_status build_state(const tq_layer_config* cfg, std::vector<float>* R, std::ve
   }
   *levels = 0;
   if (!cfg->bypass) {
-    double c[256], b[255];
-    tq_status st = lloyd_max(cfg->k_bits, cfg->dist, d, c, b, nullptr);
+    tq_status st = stored_codebook(cfg->k_bits, cfg->dist, cent, bnd);
     if (st != TQ_OK) return st;
-    // Stored codebook: centroids rounded to float16 (the decode kernels' MFMA
-    // operand type), boundaries at the exact midpoints of the stored centroids.
-    const int L = 1 << cfg->k_bits;
-    double c16[256];
-    for (int i = 0; i < L; ++i) c16[i] = static_cast<double>(static_cast<_Float16>(c[i]));
-    for (int i = 0; i < L; ++i) cent[i] = static_cast<float>(c16[i]);
-    for (int i = 0; i + 1 < L; ++i) bnd[i] = static_cast<float>(0.5 * (c16[i] + c16[i + 1]));
-    (void)b;
-    *levels = L;
+    *levels = 1 << cfg->k_bits;
   }
   return TQ_OK;
 }
@@ -250,6 +259,10 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
   std::vector<float> R, S;
   st = build_state(cfg, &R, cfg->bypass ? nullptr : &S, L->centroids, L->boundaries, &L->levels);
   if (st != TQ_OK) { delete L; return st; }
+  if (!cfg->bypass && cfg->value_mode == TQ_VAL_MSE) {
+    st = stored_codebook(cfg->v_bits, cfg->dist, L->v_centroids, L->v_boundaries);
+    if (st != TQ_OK) { delete L; return st; }
+  }
   hipError_t e = hipGetDevice(&L->device);
   if (e != hipSuccess) { delete L; return hip_fail(e, "hipGetDevice"); }
   e = hipDeviceGetAttribute(&L->cu_count, hipDeviceAttributeMultiprocessorCount, L->device);
@@ -438,6 +451,8 @@ tq_status tq_decompress_kv(const tq_layer* L, const void* pool, long long num_bl
   if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
     return fail(TQ_ERR_UNSUPPORTED, "decompress output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
+  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE)
+    return fail(TQ_ERR_UNSUPPORTED, "decompress of layers with MSE-coded values is not built");
   if (n_tokens == 0) return TQ_OK;
   if (!pool || !slot_mapping || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
   if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
@@ -475,6 +490,8 @@ tq_status tq_decode_attn(const tq_layer* L, const void* q, tq_dtype q_dtype, int
     return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head = %d not supported (1, 2, 4, 8)", rep);
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16)
     return fail(TQ_ERR_UNSUPPORTED, "query dtype %d not supported (F32, BF16)", static_cast<int>(q_dtype));
+  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE)
+    return fail(TQ_ERR_UNSUPPORTED, "decode of layers with MSE-coded values is not built");
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
     return fail(TQ_ERR_UNSUPPORTED, "output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
   if (static_cast<long long>(max_blocks_per_seq) * kPage < max_seq_len)

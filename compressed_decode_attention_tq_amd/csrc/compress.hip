@@ -10,6 +10,9 @@
 // 0.18.0", "Measured quality": groups of 32 with their own scale/zero):
 //   v' = R v; per 32-wide group scale = fp16((max-min)/(2^b-1)), zero = fp16(min),
 //   code = clamp(rint((v' - zero)/scale), 0, 2^b-1)  (0 when scale == 0).
+// Values coded like the keys' codebook part ("5x Faster LLM Inference? ...",
+// "What is TurboQuant-GPU?": 3-bit MSE values), with their own codebook:
+//   nv = ||v||, t = sqrt(d) v' / nv, code = #{i : vbeta_i < t}; stored fp16 nv.
 //
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -30,10 +33,13 @@ struct CompressArgs {
   const float* ST;  // [H][128][128], ST[h][j][i] = S_h[i][j]
   int H;
   int km;  // key mode: 0 QJL, 1 codebook only, 2 codebook only with norm-corrected magnitude
+  int vm;  // value mode: 0 group scale/zero, 1 codebook codes and one fp16 norm
   unsigned block_bytes;
   unsigned off_kc, off_ks, off_kn, off_vc, off_vsz;
   float cent[16];
   float bnd[16];
+  float vcent[16];  // value codebook (vm == 1)
+  float vbnd[16];
 };
 
 template <bool BF16>
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
   const long long slot = a.slots[tok];
   if (slot < 0) return;
 
-  __shared__ float sk[128], sv[128], srho[128], red[4];
+  __shared__ float sk[128], sv[128], srho[128], red[4], redv[2];
   __shared__ float pk[4][128], pv[4][128];
   __shared__ unsigned char ck[128];
   __shared__ unsigned sbits[4];
@@ -111,7 +117,10 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     const float w2 = wave_sum(kx * kx);
     if ((i & 63) == 0) red[i >> 6] = w2;
   } else if (c == 1) {
-    sv[i] = load_elem<BF16>(a.v, tok * a.v_stride + h * 128 + i);
+    const float vx = load_elem<BF16>(a.v, tok * a.v_stride + h * 128 + i);
+    sv[i] = vx;
+    const float w2 = wave_sum(vx * vx);  // ||v||^2 (used with codebook-coded values)
+    if ((i & 63) == 0) redv[i >> 6] = w2;
   }
   __syncthreads();
   {
@@ -146,21 +155,30 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     const float gt = (a.km == 2) ? a.cent[idx] : rho;
     const float g2 = wave_sum(gt * gt);
     if ((i & 63) == 0) red[2 + (i >> 6)] = g2;
-    // values: group min/max over 32 lanes
-    float mn = rv, mx = rv;
+    if (a.vm == 1) {
+      // values: standardise by the vector norm, then the value codebook
+      const float nv = sqrtf(redv[0] + redv[1]);
+      const float tv = (nv > 0.0f) ? rv * (sqrtf(128.0f) / nv) : 0.0f;
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off, 32));
-      mx = fmaxf(mx, __shfl_xor(mx, off, 32));
-    }
-    s16 = __float2half_rn((mx - mn) / top);
-    z16 = __float2half_rn(mn);
-    const float s = __half2float(s16);
-    const float z = __half2float(z16);
-    if (s > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((rv - z) / s), 0.0f), top));
-    if ((i & 31) == 0) {
-      sgroup[(i >> 5) * 2] = s16;
-      sgroup[(i >> 5) * 2 + 1] = z16;
+      for (int b = 0; b < (1 << VB) - 1; ++b) code += (a.vbnd[b] < tv) ? 1 : 0;
+      if (i == 0) sgroup[0] = __float2half_rn(nv);
+    } else {
+      // values: group min/max over 32 lanes
+      float mn = rv, mx = rv;
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+      }
+      s16 = __float2half_rn((mx - mn) / top);
+      z16 = __float2half_rn(mn);
+      const float s = __half2float(s16);
+      const float z = __half2float(z16);
+      if (s > 0.0f) code = static_cast<int>(fminf(fmaxf(rintf((rv - z) / s), 0.0f), top));
+      if ((i & 31) == 0) {
+        sgroup[(i >> 5) * 2] = s16;
+        sgroup[(i >> 5) * 2 + 1] = z16;
+      }
     }
   }
   __syncthreads();
@@ -220,7 +238,10 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     const unsigned w = static_cast<unsigned>(__half_as_ushort(hn)) |
                        (static_cast<unsigned>(__half_as_ushort(hg)) << 16);
     *reinterpret_cast<unsigned*>(base + a.off_kn + off * 4) = w;
-  } else if (i >= 72 && i < 76) {
+  } else if (a.vm == 1 && i == 72) {
+    // the token's fp16 value norm (two bytes of its own)
+    *reinterpret_cast<unsigned short*>(base + a.off_vsz + off * 2) = __half_as_ushort(sgroup[0]);
+  } else if (a.vm == 0 && i >= 72 && i < 76) {
     const int g = i - 72;
     const unsigned w = static_cast<unsigned>(__half_as_ushort(sgroup[2 * g])) |
                        (static_cast<unsigned>(__half_as_ushort(sgroup[2 * g + 1])) << 16);
@@ -303,6 +324,7 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
     a.H = L->cfg.n_kv_heads;
     a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
     a.km = static_cast<int>(L->cfg.key_mode);
+    a.vm = L->cfg.value_mode == TQ_VAL_MSE ? 1 : 0;
     a.off_kc = static_cast<unsigned>(L->lay.off_kc);
     a.off_ks = static_cast<unsigned>(L->lay.off_ks);
     a.off_kn = static_cast<unsigned>(L->lay.off_kn);
@@ -311,6 +333,8 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
     for (int i = 0; i < 16; ++i) {
       a.cent[i] = L->centroids[i];
       a.bnd[i] = L->boundaries[i];
+      a.vcent[i] = L->v_centroids[i];
+      a.vbnd[i] = L->v_boundaries[i];
     }
     void* fn = (in_dtype == TQ_BF16) ? pick<true>(L->cfg.k_bits, L->cfg.v_bits)
                                      : pick<false>(L->cfg.k_bits, L->cfg.v_bits);

@@ -94,6 +94,9 @@ struct tq_layer {
   float centroids[16] = {0};
   float boundaries[16] = {0};
   int levels = 0;
+  // value codebook (layers with MSE-coded values): v_bits-bit, same density
+  float v_centroids[16] = {0};
+  float v_boundaries[16] = {0};
 };
 
 namespace tq {

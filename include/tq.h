@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 4
+#define TQ_ABI_VERSION 5
 
 typedef enum {
   TQ_OK = 0,
@@ -146,11 +146,28 @@ typedef enum { TQ_KEY_QJL = 0, TQ_KEY_MSE = 1, TQ_KEY_MSE_NC = 2 } tq_key_mode;
  *                    matrix-core pass on the exact +-1 pattern instead of three. */
 typedef enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 } tq_rotation;
 
+/* Value coding of a compressed layer.
+ *   TQ_VAL_GROUP  v' = R_g v quantised per 32-wide group with its own fp16
+ *                 scale and zero ("How 0xsero/turboquant works", "Value
+ *                 Compression"); last page field Vsz [16][4][2] fp16.
+ *   TQ_VAL_MSE    values coded like the keys' codebook part ("5x Faster LLM
+ *                 Inference? ...", "What is TurboQuant-GPU?": 3-bit MSE values;
+ *                 "Example 4": normalise -> rotate -> Lloyd-Max quantise -> pack):
+ *                 nv = ||v||, t = sqrt(d) R_g v / nv, codes = v_bits-bit indices
+ *                 into the stored Lloyd-Max codebook of the same density (float16
+ *                 centroids, midpoint boundaries), value (nv16 / sqrt d) c[code];
+ *                 the Vc stream keeps its order and the last field is Vn [16]
+ *                 fp16 (K2 + QJL / V3: 102 bytes per token-head, 1632 per page).
+ *                 tq_compress_kv writes such layers (with the per-token
+ *                 compressor); tq_decode_attn and tq_decompress_kv return
+ *                 TQ_ERR_UNSUPPORTED for them. */
+typedef enum { TQ_VAL_GROUP = 0, TQ_VAL_MSE = 1 } tq_value_mode;
+
 typedef struct {
   int head_dim;             /* d; must be 128                                   */
   int n_kv_heads;           /* KV heads of the layer, >= 1                      */
   int k_bits;               /* key codebook bits, 2..4 (QJL adds 1 bit/coord)   */
-  int v_bits;               /* value group-quantiser bits, 2..4                 */
+  int v_bits;               /* value code bits, 2..4                            */
   int v_group;              /* value group width; must be 32                    */
   int block_size;           /* tokens per page; must be 16                      */
   int layer;                /* layer index, part of the random-state key        */
@@ -159,6 +176,7 @@ typedef struct {
   int bypass;               /* 1: uncompressed bf16 layer (bits/dist ignored)   */
   tq_key_mode key_mode;     /* key estimator (compressed layers)                */
   tq_rotation rotation;     /* rotation family (compressed layers)              */
+  tq_value_mode value_mode; /* value coding (compressed layers)                 */
 } tq_layer_config;
 
 /* Opaque per-layer state.  Holds, on the device, for every KV head g:

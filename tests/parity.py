@@ -46,7 +46,8 @@ def fields_at(pool_bytes, layout, n_heads, slots, head):
     return lay.get_records(pool_bytes, layout, n_heads, slots, head)
 
 
-def compare_compress(gpu, ck, cv, S, boundaries, V, v_bits, group=32, centroids=None, key_mode="qjl"):
+def compare_compress(gpu, ck, cv, S, boundaries, V, v_bits, group=32, centroids=None, key_mode="qjl",
+                     v_boundaries=None):
     """Apply the protocol to one head's records.  Returns a dict of counts.
 
     With the norm-corrected magnitude (key_mode "mse_nc") the stored n16 depends on
@@ -75,6 +76,20 @@ def compare_compress(gpu, ck, cv, S, boundaries, V, v_bits, group=32, centroids=
     st["sign_rows_skipped"] = int(np.sum(~rows))
     # values
     top = (1 << v_bits) - 1
+    if "vn16" in gpu:
+        # codebook-coded values: codes as the keys' (band around the value
+        # boundaries), the stored norm within an ulp
+        st["meta_ulps"] = int(f16_ulps(gpu["vn16"], cv["n16"]).max(initial=0))
+        vmis = gpu["vcode"] != cv["codes"]
+        tv = cv["t"][vmis]
+        near = np.min(np.abs(tv[:, None] - np.asarray(v_boundaries)[None, :]), axis=1) if tv.size else tv
+        st["value_mismatch"] = int(vmis.sum())
+        st["value_out_of_band"] = int(np.sum(near > BAND))
+        st["value_meta_differs"] = 0
+        st["value_invalid_other_meta"] = 0
+        st["value_code_range"] = bool(gpu["vcode"].min(initial=0) >= 0 and gpu["vcode"].max(initial=0) <= top)
+        st["mismatch_rate"] = (st["key_mismatch"] + st["sign_mismatch"] + st["value_mismatch"]) / max(3 * n * d, 1)
+        return st
     st["meta_ulps"] = int(max(f16_ulps(gpu["scale16"], cv["scale16"]).max(initial=0),
                               f16_ulps(gpu["zero16"], cv["zero16"]).max(initial=0)))
     same = (gpu["scale16"] == cv["scale16"]) & (gpu["zero16"] == cv["zero16"])
@@ -119,17 +134,18 @@ def rel_l2(got, ref):
 
 
 def oracle_store(K, V, slots, num_blocks, n_heads, k_bits, v_bits, seed, layer=0, bypass=False,
-                 K_bits16=None, V_bits16=None, keep=True, fill=0, key_mode="qjl", rotation_kind="haar"):
+                 K_bits16=None, V_bits16=None, keep=True, fill=0, key_mode="qjl", rotation_kind="haar",
+                 value_mode="group"):
     """Oracle state + pool for the given inputs (float arrays [N, H, d]); every
     pool byte starts as `fill` (0xFF: all-ones fields, NaN norms and values)."""
-    layout = lay.StoreLayout(128, k_bits, v_bits, 32, bypass=bypass)
+    layout = lay.StoreLayout(128, k_bits, v_bits, 32, bypass=bypass, value_mode=value_mode)
     pool = lay.new_pool(num_blocks, n_heads, layout)
     pool[:] = fill
     if bypass:
         compress.store_bypass(K_bits16, V_bits16, slots, pool, layout, n_heads)
         return None, layout, pool, None
     st = ostate.LayerState(seed, layer, n_heads, 128, k_bits, v_bits, 32, key_mode=key_mode,
-                           rotation_kind=rotation_kind)
+                           rotation_kind=rotation_kind, value_mode=value_mode)
     res = compress.compress_into_pool(K, V, slots, pool, layout, st, keep=keep)
     return st, layout, pool, res
 

@@ -24,9 +24,10 @@ def say(*a):
 
 # ------------------------------------------------------------------ compress
 def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16", key_mode=0,
-                  rotation=0):
+                  rotation=0, value_mode=0):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer, key_mode=key_mode, rotation=rotation))
+    layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer, key_mode=key_mode, rotation=rotation,
+                                   value_mode=value_mode))
     k = torch.from_numpy(np.ascontiguousarray(K)).to("cuda", tdt)
     v = torch.from_numpy(np.ascontiguousarray(V)).to("cuda", tdt)
     pool = layer_obj.new_pool(num_blocks)
@@ -44,7 +45,8 @@ def _check_compress(gpu_pool, res, st, layout, n_heads, slots, V, kb, vb):
         f = parity.fields_at(gpu_pool, layout, n_heads, sl, h)
         ck, cv = res[h]
         stats = parity.compare_compress(f, ck, cv, st.S[h], st.boundaries, V[keep][:, h], vb,
-                                        centroids=st.centroids, key_mode=st.key_mode)
+                                        centroids=st.centroids, key_mode=st.key_mode,
+                                        v_boundaries=getattr(st, "v_boundaries", None))
         print("head", h, stats)
         parity.assert_compress_ok(stats)
 
@@ -78,6 +80,53 @@ def test_compress_bits_ragged_slots(kb, vb):
     untouched = [b for b in range(40) if b not in written]
     for b in untouched:
         assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
+
+
+@pytest.mark.parametrize("kb,vb,n,dtype", [(2, 3, 301, "bf16"), (4, 4, 500, "bf16"), (3, 2, 200, "f32")])
+def test_compress_mse_values(kb, vb, n, dtype):
+    """Values coded like the keys' codebook part (the 102-byte record at K2/V3): 8
+    heads with outlier channels, shuffled slots with skipped tokens, bf16 (more
+    than 64 tokens, which the matrix-core compressor would otherwise take) and
+    fp32. Codes as the keys' protocol, the value norm within an fp16 ulp, slots
+    nobody wrote untouched."""
+    torch = _torch()
+    say("compress mse values", kb, vb, n, dtype)
+    K, V = synth.kv_host(340 + kb * 10 + vb, n, 8, outliers=4, dtype=dtype)
+    rng = np.random.default_rng(340 + kb)
+    slots = rng.permutation(40 * 16)[:n].astype(np.int64)
+    slots[rng.choice(n, 15, replace=False)] = -1
+    gpu = _gpu_compress(torch, K, V, slots, 40, 8, kb, vb, 341, layer=kb, dtype=dtype, value_mode=tq.VAL_MSE)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, 40, 8, kb, vb, 341, layer=kb, value_mode="mse")
+    assert layout.record_bytes() == 16 * kb + 16 + 4 + 16 * vb + 2
+    _check_compress(gpu, res, st, layout, 8, slots, V, kb, vb)
+    written = set((slots[slots >= 0] // 16).tolist())
+    for b in range(40):
+        if b not in written:
+            assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
+
+
+def test_mse_value_layers_refuse_decode_and_decompress():
+    """Decode and decompress of MSE-value layers are not built: both return
+    TQ_ERR_UNSUPPORTED before any launch (no silent fallback)."""
+    torch = _torch()
+    say("mse values: decode and decompress refused")
+    layer = tq.Layer(tq.config(2, 2, 3, seed=5, value_mode=tq.VAL_MSE))
+    pool = layer.new_pool(4)
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    sl = torch.full((1,), 16, dtype=torch.int32, device="cuda")
+    out = torch.zeros((1, 8, 128), device="cuda")
+    ws = tq.new_workspace(layer, 1, 8, 64)
+    st = tq.lib().tq_decode_attn(layer.handle, tq._ptr(q), tq._dtype_code(q), 1, 8, tq._ptr(pool), 4,
+                                 tq._ptr(bt), 4, tq._ptr(sl), 64, 0.0, 0, tq._ptr(out), tq._dtype_code(out),
+                                 tq._ptr(ws), ws.numel(), tq._stream(None))
+    assert st == tq.ERR_UNSUPPORTED and b"MSE" in tq.lib().tq_last_error()
+    with pytest.raises(tq.TQError) as e:
+        tq.decompress_kv(layer, pool, torch.zeros(3, dtype=torch.int64, device="cuda"))
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert not out.any()
+    layer.close()
 
 
 @pytest.mark.parametrize("kb,vb,n,offset", [(4, 4, 2000, 37), (3, 2, 1000, 0), (2, 3, 777, 16)])

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tq_abi_version() == 4
+    assert lib.tq_abi_version() == 5
 
 
 @pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
@@ -82,6 +82,7 @@ def test_config_errors():
         (dict(n_kv_heads=0), tq.ERR_INVALID_ARGUMENT), (dict(layer=-1), tq.ERR_INVALID_ARGUMENT),
         (dict(dist=7), tq.ERR_INVALID_ARGUMENT), (dict(key_mode=3), tq.ERR_INVALID_ARGUMENT),
         (dict(key_mode=-1), tq.ERR_INVALID_ARGUMENT), (dict(rotation=2), tq.ERR_INVALID_ARGUMENT),
+        (dict(value_mode=2), tq.ERR_INVALID_ARGUMENT),
     ]
     for kw, want in bad:
         args = dict(n_kv_heads=8)
@@ -126,3 +127,15 @@ def test_hadamard_layer_state_matches_oracle(layer, heads):
     st = state.LayerState(207, layer, heads, 128, 3, 3, 32, rotation_kind="hadamard")
     assert np.array_equal(R.astype(np.float64), st.R)
     assert np.array_equal(S.astype(np.float64), st.S)
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 3), (4, 4), (3, 2)])
+def test_mse_value_layout_matches_oracle(kb, vb):
+    """Values coded like the keys: the library's page layout equals the oracle's
+    (one fp16 norm per token in the last field; 102 bytes per token-head at K2/V3)."""
+    bb, offs = tq.store_layout(tq.config(8, kb, vb, value_mode=tq.VAL_MSE))
+    lay = layout.StoreLayout(128, kb, vb, 32, value_mode="mse")
+    assert bb == lay.block_bytes
+    assert offs == lay.field_offsets()
+    if (kb, vb) == (2, 3):
+        assert bb == 16 * 102
