@@ -308,7 +308,8 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
                        static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
                        k_stride, v_stride, slots, static_cast<unsigned char*>(pool),
                        L->cfg.n_kv_heads, static_cast<unsigned>(L->lay.block_bytes));
-  } else if (compress_mfma_applies(L, k, v, in_dtype, n_tokens, k_stride, v_stride)) {
+  } else if (L->cfg.value_mode == TQ_VAL_GROUP &&  // MSE-coded values: the per-token kernel below
+             compress_mfma_applies(L, k, v, in_dtype, n_tokens, k_stride, v_stride)) {
     tq_status st = launch_compress_mfma(L, k, v, n_tokens, k_stride, v_stride, slots, pool, stream);
     if (st != TQ_OK) return st;
   } else {

@@ -630,7 +630,6 @@ void* pick_kv(int kb, int vb) {
 bool compress_mfma_applies(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype, long long n_tokens,
                            long long k_stride, long long v_stride) {
   if (L->cfg.bypass || in_dtype != TQ_BF16 || !L->dOpA) return false;
-  if (L->cfg.value_mode != TQ_VAL_GROUP) return false;  // MSE-coded values: the per-token kernel
   if (n_tokens < 64) return false;  // a handful of appended tokens: the per-token kernel is quicker
   // 16-byte aligned rows for the direct-to-LDS copies
   if ((k_stride % 8) || (v_stride % 8)) return false;
