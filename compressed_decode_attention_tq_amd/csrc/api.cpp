@@ -451,8 +451,6 @@ tq_status tq_decompress_kv(const tq_layer* L, const void* pool, long long num_bl
   if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
     return fail(TQ_ERR_UNSUPPORTED, "decompress output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
-  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE)
-    return fail(TQ_ERR_UNSUPPORTED, "decompress of layers with MSE-coded values is not built");
   if (n_tokens == 0) return TQ_OK;
   if (!pool || !slot_mapping || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
   if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");

@@ -43,6 +43,8 @@ struct DArgs {
   unsigned off_kc, off_ks, off_kn, off_vc, off_vsz;
   float kappa;
   float cent[16];
+  int vm;           // value mode: 0 group scale/zero, 1 codebook codes and one fp16 norm
+  float vcent[16];  // value codebook (vm == 1)
 };
 
 __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
@@ -92,9 +94,18 @@ __device__ __forceinline__ void expand(const DArgs& a, const unsigned char* page
   for (int b = 0; b < KB; ++b) x |= static_cast<unsigned>(kc[b]) << (8 * b);
   const unsigned zb = page[a.off_ks + (blk * 16 + o) * 4 + e0 / 8];  // sign bits of dims d0..d0+7
   const unsigned kn = *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4);
-  const unsigned sz = *reinterpret_cast<const unsigned*>(page + a.off_vsz + o * 16 + (d0 >> 5) * 4);
-  const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
-  const float zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
+  // value metadata: the group's scale and zero, or (codebook-coded values) the
+  // token's norm / sqrt(d), read from a last field of 32 bytes per page
+  float sc, zr;
+  if (a.vm == 1) {
+    const unsigned short vn = *reinterpret_cast<const unsigned short*>(page + a.off_vsz + o * 2);
+    sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
+    zr = 0.0f;
+  } else {
+    const unsigned sz = *reinterpret_cast<const unsigned*>(page + a.off_vsz + o * 16 + (d0 >> 5) * 4);
+    sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
+    zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     ac[t][d0 + i] = static_cast<_Float16>(a.cent[(x >> (KB * i)) & ((1u << KB) - 1u)]);
@@ -105,7 +116,8 @@ __device__ __forceinline__ void expand(const DArgs& a, const unsigned char* page
     const unsigned bit = e * VB;
     const unsigned char* vb = page + a.off_vc + (bit >> 3);
     const unsigned w = static_cast<unsigned>(vb[0]) | (static_cast<unsigned>(vb[1]) << 8);
-    const float v = fmaf(sc, static_cast<float>((w >> (bit & 7)) & ((1u << VB) - 1u)), zr);
+    const unsigned code = (w >> (bit & 7)) & ((1u << VB) - 1u);
+    const float v = (a.vm == 1) ? sc * a.vcent[code] : fmaf(sc, static_cast<float>(code), zr);
     const _Float16 h = static_cast<_Float16>(v);
     avh[t][d0 + i] = h;
     avl[t][d0 + i] = static_cast<_Float16>(v - static_cast<float>(h));
@@ -280,7 +292,11 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
     a.off_vc = static_cast<unsigned>(L->lay.off_vc);
     a.off_vsz = static_cast<unsigned>(L->lay.off_vsz);
     a.kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / kDim);
-    for (int i = 0; i < 16; ++i) a.cent[i] = L->centroids[i];
+    for (int i = 0; i < 16; ++i) {
+      a.cent[i] = L->centroids[i];
+      a.vcent[i] = L->v_centroids[i];
+    }
+    a.vm = L->cfg.value_mode == TQ_VAL_MSE ? 1 : 0;
     void* fn = bf ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits) : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
                          L->cfg.v_bits);

@@ -159,8 +159,8 @@ typedef enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 } tq_rotation;
  *                 the Vc stream keeps its order and the last field is Vn [16]
  *                 fp16 (K2 + QJL / V3: 102 bytes per token-head, 1632 per page).
  *                 tq_compress_kv writes such layers (with the per-token
- *                 compressor); tq_decode_attn and tq_decompress_kv return
- *                 TQ_ERR_UNSUPPORTED for them. */
+ *                 compressor) and tq_decompress_kv reads them; tq_decode_attn
+ *                 returns TQ_ERR_UNSUPPORTED for them. */
 typedef enum { TQ_VAL_GROUP = 0, TQ_VAL_MSE = 1 } tq_value_mode;
 
 typedef struct {

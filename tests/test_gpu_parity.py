@@ -105,11 +105,11 @@ def test_compress_mse_values(kb, vb, n, dtype):
             assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
 
-def test_mse_value_layers_refuse_decode_and_decompress():
-    """Decode and decompress of MSE-value layers are not built: both return
-    TQ_ERR_UNSUPPORTED before any launch (no silent fallback)."""
+def test_mse_value_layers_refuse_decode():
+    """Decode of MSE-value layers is not built: it returns TQ_ERR_UNSUPPORTED
+    before any launch (no silent fallback)."""
     torch = _torch()
-    say("mse values: decode and decompress refused")
+    say("mse values: decode refused")
     layer = tq.Layer(tq.config(2, 2, 3, seed=5, value_mode=tq.VAL_MSE))
     pool = layer.new_pool(4)
     q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
@@ -121,11 +121,46 @@ def test_mse_value_layers_refuse_decode_and_decompress():
                                  tq._ptr(bt), 4, tq._ptr(sl), 64, 0.0, 0, tq._ptr(out), tq._dtype_code(out),
                                  tq._ptr(ws), ws.numel(), tq._stream(None))
     assert st == tq.ERR_UNSUPPORTED and b"MSE" in tq.lib().tq_last_error()
-    with pytest.raises(tq.TQError) as e:
-        tq.decompress_kv(layer, pool, torch.zeros(3, dtype=torch.int64, device="cuda"))
-    assert e.value.status == tq.ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert not out.any()
+    layer.close()
+
+
+@pytest.mark.parametrize("kb,vb,out_dtype", [(2, 3, "f32"), (4, 4, "bf16"), (3, 2, "f32")])
+def test_decompress_mse_values(kb, vb, out_dtype):
+    """MSE-value stores written by the GPU (shuffled slots; some read slots
+    negative: zero rows; tiles mixing whole pages and scattered tokens),
+    reconstructed on the GPU against the oracle's reconstruction of the same bytes."""
+    from oracle import decompress as odec
+    torch = _torch()
+    say("decompress mse values", kb, vb, out_dtype)
+    H, n = 8, 517
+    K, V = synth.kv_host(350 + kb, n, H, outliers=4)
+    rng = np.random.default_rng(350 + vb)
+    slots = np.concatenate([np.arange(64), 64 + rng.permutation(40 * 16)[: n - 64]]).astype(np.int64)
+    layer = tq.Layer(tq.config(H, kb, vb, seed=351, layer=kb, value_mode=tq.VAL_MSE))
+    pool = layer.new_pool(45)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    q_slots = slots.copy()
+    q_slots[rng.choice(np.arange(64, n), 9, replace=False)] = -1
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    kd, vd = tq.decompress_kv(layer, pool, torch.from_numpy(q_slots).cuda(), out_dtype=tdt)
+    torch.cuda.synchronize()
+    kd, vd = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    st = parity.ostate.LayerState(351, kb, H, 128, kb, vb, 32, value_mode="mse")
+    layout = parity.lay.StoreLayout(128, kb, vb, 32, value_mode="mse")
+    kr, vr = odec.decompress(pool.cpu().numpy(), layout, H, q_slots, st)
+    neg = q_slots < 0
+    assert not kd[neg].any() and not vd[neg].any()
+    for got, ref, name in ((kd, kr, "K"), (vd, vr, "V")):
+        err = np.abs(got - ref)
+        scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+        if out_dtype == "f32":
+            print(name, "max err / row max %.2e, rel L2 %.2e" % ((err / scale).max(), parity.rel_l2(got, ref)))
+            assert (err / scale).max() <= 2e-6 and parity.rel_l2(got, ref) <= 1e-6
+        else:
+            assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-6 * scale), name
     layer.close()
 
 
