@@ -344,6 +344,34 @@ def decompress_workload(torch, tq, synth, args):
             "mfma_floor_us": round(mfma_us, 1)}
 
 
+def mse_values_workload(torch, tq, synth, args):
+    """The headline store's shape (16 x 4096 tokens x 8 KV heads) with 2-bit keys + QJL and
+    3-bit values coded like the keys (the 102-byte record): the per-token fused compress
+    into the store, then the decompress to bf16 K and V."""
+    B, Hkv, T = 16, 8, 4096
+    N = B * T
+    layer = tq.Layer(tq.config(Hkv, 2, 3, seed=361, value_mode=tq.VAL_MSE))
+    k, v = synth.kv_device(362, N, Hkv, outliers=4)
+    pool = layer.new_pool(N // 16)
+    slots = torch.arange(N, dtype=torch.int64, device="cuda")
+    comp = lambda i: tq.compress_kv(layer, k, v, slots, pool)
+    _time_steps(torch, comp, 2)
+    ms_c = _time_steps(torch, comp, 10)
+    kd = torch.empty((N, Hkv, 128), dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    dec = lambda i: tq.decompress_kv(layer, pool, slots, k_out=kd, v_out=vd)
+    _time_steps(torch, dec, 5)
+    ms_d = _time_steps(torch, dec, 50)
+    rec = layer.block_bytes // 16
+    layer.close()
+    nbytes = N * Hkv * (512 + rec) + N * 8  # bf16 K+V and the record, either direction, + slots
+    return {"workload": "mse-values-k2qjl-v3-store", "token_heads": N * Hkv, "record_bytes": rec,
+            "compress_ms": round(ms_c, 4), "compress_gbs": round(nbytes / (ms_c / 1e3) / 1e9, 1),
+            "compress_frac": round(nbytes / (ms_c / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decompress_ms": round(ms_d, 4), "decompress_gbs": round(nbytes / (ms_d / 1e3) / 1e9, 1),
+            "decompress_frac": round(nbytes / (ms_d / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
+
+
 def extra_workloads(torch, tq, synth, args):
     """The tiny, long-context and serving workloads, each as decode-step figures."""
     import numpy as np
@@ -550,6 +578,8 @@ def main():
                 torch, tq, synth, args, key_mode=tq.KEY_MSE_NC, rotation=tq.ROT_HADAMARD)
         log("decompress workload")
         extra["decompress"] = decompress_workload(torch, tq, synth, args)
+        log("mse values")
+        extra["mse_values"] = mse_values_workload(torch, tq, synth, args)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
