@@ -82,7 +82,8 @@ def test_compress_bits_ragged_slots(kb, vb):
         assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
 
-@pytest.mark.parametrize("kb,vb,n,dtype", [(2, 3, 301, "bf16"), (4, 4, 500, "bf16"), (3, 2, 200, "f32")])
+@pytest.mark.parametrize("kb,vb,n,dtype", [(2, 3, 301, "bf16"), (4, 4, 500, "bf16"), (3, 2, 200, "f32"),
+                                           (2, 3, 2003, "bf16")])
 def test_compress_mse_values(kb, vb, n, dtype):
     """Values coded like the keys' codebook part (the 102-byte record at K2/V3): 8
     heads with outlier channels, shuffled slots with skipped tokens, bf16 (more
@@ -93,14 +94,15 @@ def test_compress_mse_values(kb, vb, n, dtype):
     say("compress mse values", kb, vb, n, dtype)
     K, V = synth.kv_host(340 + kb * 10 + vb, n, 8, outliers=4, dtype=dtype)
     rng = np.random.default_rng(340 + kb)
-    slots = rng.permutation(40 * 16)[:n].astype(np.int64)
+    nb = max(40, (n + 15) // 16 + 4)  # 2003 tokens: 16 per workgroup, a ragged last run
+    slots = rng.permutation(nb * 16)[:n].astype(np.int64)
     slots[rng.choice(n, 15, replace=False)] = -1
-    gpu = _gpu_compress(torch, K, V, slots, 40, 8, kb, vb, 341, layer=kb, dtype=dtype, value_mode=tq.VAL_MSE)
-    st, layout, pool, res = parity.oracle_store(K, V, slots, 40, 8, kb, vb, 341, layer=kb, value_mode="mse")
+    gpu = _gpu_compress(torch, K, V, slots, nb, 8, kb, vb, 341, layer=kb, dtype=dtype, value_mode=tq.VAL_MSE)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, 8, kb, vb, 341, layer=kb, value_mode="mse")
     assert layout.record_bytes() == 16 * kb + 16 + 4 + 16 * vb + 2
     _check_compress(gpu, res, st, layout, 8, slots, V, kb, vb)
     written = set((slots[slots >= 0] // 16).tolist())
-    for b in range(40):
+    for b in range(nb):
         if b not in written:
             assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
