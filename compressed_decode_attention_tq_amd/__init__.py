@@ -19,6 +19,7 @@ DIST_GAUSSIAN, DIST_SPHERE = 0, 1
 KEY_QJL, KEY_MSE, KEY_MSE_NC = 0, 1, 2  # key estimator (tq_key_mode)
 ROT_HAAR, ROT_HADAMARD = 0, 1  # rotation family (tq_rotation)
 VAL_GROUP, VAL_MSE = 0, 1  # value coding (tq_value_mode)
+ABI_VERSION = 5  # TQ_ABI_VERSION of include/tq.h that this binding mirrors
 EXPORTED = [
     "tq_last_error", "tq_abi_version", "tq_codebook_build", "tq_layer_state_host",
     "tq_layer_create", "tq_layer_destroy", "tq_store_layout", "tq_compress_kv",
@@ -65,6 +66,10 @@ def lib():
     dp, fp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)
     L.tq_last_error.restype = ctypes.c_char_p
     L.tq_abi_version.restype = c_int
+    if L.tq_abi_version() != ABI_VERSION:
+        # the config struct and entry points of another version would be misread
+        raise RuntimeError("libtq.so has ABI %d, this binding expects %d: rebuild it"
+                           % (L.tq_abi_version(), ABI_VERSION))
     L.tq_codebook_build.argtypes = [c_int, c_int, c_int, dp, dp, dp]
     L.tq_layer_state_host.argtypes = [ctypes.POINTER(LayerConfig), fp, fp, fp, fp]
     L.tq_layer_create.argtypes = [ctypes.POINTER(LayerConfig), vp, ctypes.POINTER(vp)]

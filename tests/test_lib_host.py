@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tq_abi_version() == 5
+    assert lib.tq_abi_version() == tq.ABI_VERSION == 5
 
 
 @pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
