@@ -21,7 +21,8 @@ random-number generator), written step by step from the pages it follows:
 * "5x Faster LLM Inference? This KV Cache Hack Changes Everything", sections
   "What is TurboQuant-GPU?" and "Example 4: Kernel-Level Operations":
   normalise -> rotate -> Lloyd-Max quantise -> pack; a rotation fixed per head
-  applied to both keys and values; fused attention over compressed K/V.
+  applied to both keys and values; fused attention over compressed K/V; 3-bit
+  MSE-coded values beside 2-bit keys with QJL (the value mode "mse").
 * "tiny-turboquant 0.18.0", sections "Knobs that actually move the needle"
   and "Measured quality": the K4/V4 ... K3/V2 presets, value groups of 32.
 

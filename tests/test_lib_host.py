@@ -139,3 +139,15 @@ def test_mse_value_layout_matches_oracle(kb, vb):
     assert offs == lay.field_offsets()
     if (kb, vb) == (2, 3):
         assert bb == 16 * 102
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says why,
+    before any device is touched."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+    assert r.stdout == ""
