@@ -82,14 +82,16 @@ def test_compress_bits_ragged_slots(kb, vb):
         assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
 
-@pytest.mark.parametrize("kb,vb,n,dtype", [(2, 3, 301, "bf16"), (4, 4, 500, "bf16"), (3, 2, 200, "f32"),
-                                           (2, 3, 2003, "bf16")])
-def test_compress_mse_values(kb, vb, n, dtype):
+@pytest.mark.parametrize("kb,vb,n,dtype,key_mode,rotation", [
+    (2, 3, 301, "bf16", 0, 0), (4, 4, 500, "bf16", 0, 0), (3, 2, 200, "f32", 0, 0), (2, 3, 2003, "bf16", 0, 0),
+    (3, 3, 300, "bf16", 2, 1)])
+def test_compress_mse_values(kb, vb, n, dtype, key_mode, rotation):
     """Values coded like the keys' codebook part (the 102-byte record at K2/V3): 8
     heads with outlier channels, shuffled slots with skipped tokens, bf16 (more
     than 64 tokens, which the matrix-core compressor would otherwise take) and
-    fp32. Codes as the keys' protocol, the value norm within an fp16 ulp, slots
-    nobody wrote untouched."""
+    fp32; and together with norm-corrected keys and the Hadamard rotation. Codes as
+    the keys' protocol, the value norm within an fp16 ulp, slots nobody wrote
+    untouched."""
     torch = _torch()
     say("compress mse values", kb, vb, n, dtype)
     K, V = synth.kv_host(340 + kb * 10 + vb, n, 8, outliers=4, dtype=dtype)
@@ -97,8 +99,11 @@ def test_compress_mse_values(kb, vb, n, dtype):
     nb = max(40, (n + 15) // 16 + 4)  # 2003 tokens: 16 per workgroup, a ragged last run
     slots = rng.permutation(nb * 16)[:n].astype(np.int64)
     slots[rng.choice(n, 15, replace=False)] = -1
-    gpu = _gpu_compress(torch, K, V, slots, nb, 8, kb, vb, 341, layer=kb, dtype=dtype, value_mode=tq.VAL_MSE)
-    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, 8, kb, vb, 341, layer=kb, value_mode="mse")
+    gpu = _gpu_compress(torch, K, V, slots, nb, 8, kb, vb, 341, layer=kb, dtype=dtype, key_mode=key_mode,
+                        rotation=rotation, value_mode=tq.VAL_MSE)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, 8, kb, vb, 341, layer=kb, value_mode="mse",
+                                                key_mode=KEY_MODE_NAMES[key_mode],
+                                                rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard")
     assert layout.record_bytes() == 16 * kb + 16 + 4 + 16 * vb + 2
     _check_compress(gpu, res, st, layout, 8, slots, V, kb, vb)
     written = set((slots[slots >= 0] // 16).tolist())

@@ -213,3 +213,17 @@ def test_value_mode_rejects_unknown():
         layout.StoreLayout(128, 2, 3, 32, value_mode="fp8")
     with pytest.raises(ValueError):
         state.LayerState(1, 0, 1, D, 2, 3, 32, value_mode="fp8")
+
+
+def test_mse_values_under_hadamard_rotation_cosine():
+    """The randomised Hadamard rotation Gaussianises values as well: mean cos(v, v_hat)
+    at 3 bits stays at sqrt(1 - D_3) within the same tolerance, outlier channels
+    included."""
+    rng = np.random.default_rng(77)
+    V = rng.standard_normal((4096, D))
+    V[:, rng.choice(D, 4, replace=False)] *= 10.0
+    R = state.hadamard_rotation(13, 0, 2, D)
+    c, b, mse = _cb(3)
+    cv = compress.compress_values_mse(V, R, c, b)
+    cos = metrics.cosine_rows(V, metrics.reconstruct_values_mse(cv, R, c, D)).mean()
+    assert abs(cos - math.sqrt(1.0 - mse)) < 3e-3
