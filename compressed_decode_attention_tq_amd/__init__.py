@@ -19,13 +19,14 @@ DIST_GAUSSIAN, DIST_SPHERE = 0, 1
 KEY_QJL, KEY_MSE, KEY_MSE_NC = 0, 1, 2  # key estimator (tq_key_mode)
 ROT_HAAR, ROT_HADAMARD = 0, 1  # rotation family (tq_rotation)
 VAL_GROUP, VAL_MSE = 0, 1  # value coding (tq_value_mode)
-ABI_VERSION = 5  # TQ_ABI_VERSION of include/tq.h that this binding mirrors
+ABI_VERSION = 6  # TQ_ABI_VERSION of include/tq.h that this binding mirrors
 EXPORTED = [
     "tq_last_error", "tq_abi_version", "tq_codebook_build", "tq_layer_state_host",
     "tq_layer_create", "tq_layer_destroy", "tq_store_layout", "tq_compress_kv",
     "tq_decode_workspace_size", "tq_decode_attn", "tq_profile_enable", "tq_profile_read",
-    "tq_profile_reset", "tq_decompress_kv",
+    "tq_profile_reset", "tq_decompress_kv", "tq_layer_export", "tq_layer_export_operands",
 ]
+OPERANDS_COMPRESS, OPERANDS_PROLOGUE, OPERANDS_DECOMPRESS = range(3)  # tq_operands
 K_COMPRESS, K_PROLOGUE, K_SPLITK, K_COMBINE = range(4)
 
 
@@ -80,12 +81,15 @@ def lib():
     L.tq_decode_workspace_size.argtypes = [vp, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)]
     L.tq_decode_attn.argtypes = [vp, vp, c_int, c_int, c_int, vp, c_ll, vp, c_int, vp, c_int,
                                  ctypes.c_float, c_int, vp, c_int, vp, c_size, vp]
+    L.tq_layer_export.argtypes = [vp, fp, fp, fp, fp, fp, fp, vp]
+    L.tq_layer_export_operands.argtypes = [vp, c_int, vp, c_size, ctypes.POINTER(c_size), vp]
     L.tq_profile_enable.argtypes = [ctypes.c_uint]
     L.tq_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_ll)]
     L.tq_profile_reset.argtypes = []
     for name in ["tq_codebook_build", "tq_layer_state_host", "tq_layer_create", "tq_layer_destroy",
                  "tq_store_layout", "tq_compress_kv", "tq_decode_workspace_size", "tq_decode_attn",
-                 "tq_profile_enable", "tq_profile_read", "tq_profile_reset"]:
+                 "tq_profile_enable", "tq_profile_read", "tq_profile_reset", "tq_layer_export",
+                 "tq_layer_export_operands", "tq_decompress_kv"]:
         getattr(L, name).restype = c_int
     _LIB = L
     return L
@@ -179,17 +183,68 @@ class Layer:
         except Exception:
             pass
 
+    def export(self, stream=None):
+        """(R, S, centroids, boundaries, v_centroids, v_boundaries) as the device holds them."""
+        cfg = self.cfg
+        H = cfg.n_kv_heads
+        R = np.zeros((H, 128, 128), np.float32)
+        S = np.zeros((H, 128, 128), np.float32)
+        nk = 0 if cfg.bypass else 1 << cfg.k_bits
+        nv = (1 << cfg.v_bits) if (not cfg.bypass and cfg.value_mode == VAL_MSE) else 0
+        c, b = np.zeros(max(nk, 1), np.float32), np.zeros(max(nk - 1, 1), np.float32)
+        vc, vb = np.zeros(max(nv, 1), np.float32), np.zeros(max(nv - 1, 1), np.float32)
+        _check(lib().tq_layer_export(self.handle, _fptr(R), _fptr(S), _fptr(c), _fptr(b), _fptr(vc), _fptr(vb),
+                                     _stream(stream)))
+        return R, S, c[:nk], b[:max(nk - 1, 0)], vc[:nv], vb[:max(nv - 1, 0)]
+
+    def export_operands(self, which, stream=None):
+        """One matrix-core operand buffer of the layer as uint16 words (tq_layer_export_operands)."""
+        n = ctypes.c_size_t(0)
+        _check(lib().tq_layer_export_operands(self.handle, which, None, 0, ctypes.byref(n), _stream(stream)))
+        out = np.zeros(n.value // 2, np.uint16)
+        _check(lib().tq_layer_export_operands(self.handle, which, out.ctypes.data_as(ctypes.c_void_p), n.value,
+                                              ctypes.byref(n), _stream(stream)))
+        return out
+
     def new_pool(self, num_blocks):
         torch = _torch()
         return torch.zeros(num_blocks * self.cfg.n_kv_heads * self.block_bytes, dtype=torch.uint8, device="cuda")
 
 
+def _require(cond, msg):
+    if not cond:
+        raise TQError(ERR_INVALID_ARGUMENT, msg)
+
+
+def _check_pool(layer, pool):
+    torch = _torch()
+    _require(pool.dtype == torch.uint8 and pool.is_contiguous(), "pool must be a contiguous uint8 tensor")
+    per_block = layer.cfg.n_kv_heads * layer.block_bytes
+    _require(pool.numel() % per_block == 0 and pool.numel() > 0,
+             "pool size %d is not a positive multiple of n_kv_heads*block_bytes = %d" % (pool.numel(), per_block))
+    return pool.numel() // per_block
+
+
+def _check_rows(name, t, n, H):
+    """[n, H, 128] with unit element stride and head stride 128 (any token stride)."""
+    _require(t.dim() == 3 and tuple(t.shape[1:]) == (H, 128),
+             "%s must have shape [N, %d, 128], got %s" % (name, H, tuple(t.shape)))
+    _require(t.shape[0] == n, "%s has %d rows, slot_mapping has %d" % (name, t.shape[0], n))
+    _require(t.stride(2) == 1 and t.stride(1) == 128,
+             "%s must have element stride 1 and head stride 128, got strides %s" % (name, tuple(t.stride())))
+
+
 def compress_kv(layer, k, v, slot_mapping, pool, stream=None):
     """k, v: [N, H_kv, 128] (f32 or bf16, token stride = k.stride(0)); slot_mapping int64 [N]."""
     torch = _torch()
-    assert slot_mapping.dtype == torch.int64 and pool.dtype == torch.uint8
-    n = k.shape[0]
-    num_blocks = pool.numel() // (layer.cfg.n_kv_heads * layer.block_bytes)
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous(),
+             "slot_mapping must be a contiguous 1-D int64 tensor")
+    n = slot_mapping.shape[0]
+    H = layer.cfg.n_kv_heads
+    _check_rows("k", k, n, H)
+    _check_rows("v", v, n, H)
+    _require(k.dtype == v.dtype, "k and v must have the same dtype (%s vs %s)" % (k.dtype, v.dtype))
+    num_blocks = _check_pool(layer, pool)
     _check(lib().tq_compress_kv(layer.handle, _ptr(k), _ptr(v), _dtype_code(k), n, k.stride(0), v.stride(0),
                                 _ptr(slot_mapping), _ptr(pool), num_blocks, _stream(stream)))
 
@@ -197,15 +252,19 @@ def compress_kv(layer, k, v, slot_mapping, pool, stream=None):
 def decompress_kv(layer, pool, slot_mapping, out_dtype=None, k_out=None, v_out=None, stream=None):
     """K, V [N, H_kv, 128] (f32 or bf16) reconstructed from the store at slot_mapping int64 [N]."""
     torch = _torch()
-    assert slot_mapping.dtype == torch.int64 and pool.dtype == torch.uint8
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous(),
+             "slot_mapping must be a contiguous 1-D int64 tensor")
     n, H = slot_mapping.shape[0], layer.cfg.n_kv_heads
-    dt = out_dtype or torch.float32
+    dt = out_dtype or (k_out.dtype if k_out is not None else torch.float32)
     if k_out is None:
         k_out = torch.empty((n, H, 128), dtype=dt, device=pool.device)
     if v_out is None:
         v_out = torch.empty((n, H, 128), dtype=dt, device=pool.device)
-    assert k_out.is_contiguous() and v_out.is_contiguous() and k_out.dtype == v_out.dtype
-    num_blocks = pool.numel() // (H * layer.block_bytes)
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        _require(t.is_contiguous() and tuple(t.shape) == (n, H, 128),
+                 "%s must be a contiguous [%d, %d, 128] tensor" % (name, n, H))
+    _require(k_out.dtype == v_out.dtype, "k_out and v_out must have the same dtype")
+    num_blocks = _check_pool(layer, pool)
     _check(lib().tq_decompress_kv(layer.handle, _ptr(pool), num_blocks, _ptr(slot_mapping), n, _ptr(k_out),
                                   _ptr(v_out), _dtype_code(k_out), _stream(stream)))
     return k_out, v_out
@@ -224,17 +283,32 @@ def new_workspace(layer, batch, n_q_heads, max_seq_len, num_splits=0):
     return torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
 
+def _check_decode_args(layer, q, pool, block_table, seq_lens, out):
+    torch = _torch()
+    _require(q.dim() == 3 and q.shape[2] == 128 and q.is_contiguous(),
+             "q must be a contiguous [B, H_q, 128] tensor, got shape %s strides %s" % (tuple(q.shape), tuple(q.stride())))
+    B, Hq = q.shape[0], q.shape[1]
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+             and block_table.shape[0] == B, "block_table must be a contiguous int32 [%d, max_blocks] tensor" % B)
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1 and seq_lens.is_contiguous()
+             and seq_lens.shape[0] == B, "seq_lens must be a contiguous int32 [%d] tensor" % B)
+    if out is not None:
+        _require(out.is_contiguous() and tuple(out.shape) == (B, Hq, 128),
+                 "out must be a contiguous [%d, %d, 128] tensor" % (B, Hq))
+    return _check_pool(layer, pool)
+
+
 def decode_attn(layer, q, pool, block_table, seq_lens, max_seq_len, out=None, workspace=None,
                 softmax_scale=0.0, num_splits=0, out_dtype=None, stream=None):
     """q: [B, H_q, 128]; block_table int32 [B, max_blocks]; seq_lens int32 [B]."""
     torch = _torch()
-    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    num_blocks = _check_decode_args(layer, q, pool, block_table, seq_lens, out)
     B, Hq = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((B, Hq, 128), dtype=out_dtype or torch.float32, device=q.device)
     if workspace is None:
         workspace = new_workspace(layer, B, Hq, max_seq_len, num_splits)
-    num_blocks = pool.numel() // (layer.cfg.n_kv_heads * layer.block_bytes)
+    _require(workspace.dtype == torch.uint8 and workspace.is_contiguous(), "workspace must be a contiguous uint8 tensor")
     _check(lib().tq_decode_attn(layer.handle, _ptr(q), _dtype_code(q), B, Hq, _ptr(pool), num_blocks,
                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
                                 float(softmax_scale), num_splits, _ptr(out), _dtype_code(out),

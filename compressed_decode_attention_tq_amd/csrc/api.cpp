@@ -188,6 +188,54 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   return TQ_OK;
 }
 
+tq_status check_slots(const long long* slots, long long n, long long num_blocks) {
+  for (long long i = 0; i < n; ++i)
+    if (slots[i] >= num_blocks * kPage)
+      return fail(TQ_ERR_INVALID_ARGUMENT, "slot_mapping[%lld] = %lld is past the pool (%lld blocks of %d)", i,
+                  slots[i], num_blocks, kPage);
+  return TQ_OK;
+}
+
+tq_status check_decode_tables(const int* seq_lens, const int* block_table, int batch, int max_blocks,
+                              int max_seq_len, long long num_blocks) {
+  for (int b = 0; b < batch; ++b) {
+    const int T = seq_lens[b];
+    if (T < 0 || T > max_seq_len || static_cast<long long>(T) > static_cast<long long>(max_blocks) * kPage)
+      return fail(TQ_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d outside [0, min(max_seq_len %d, 16*max_blocks %d)]",
+                  b, T, max_seq_len, max_blocks);
+    const int pages = (T + kPage - 1) / kPage;
+    for (int j = 0; j < pages; ++j) {
+      const int id = block_table[static_cast<size_t>(b) * max_blocks + j];
+      if (id < 0 || id >= num_blocks)
+        return fail(TQ_ERR_INVALID_ARGUMENT, "block_table[%d][%d] = %d outside [0, %lld)", b, j, id, num_blocks);
+    }
+  }
+  return TQ_OK;
+}
+
+bool debug_checks() {
+  const char* e = std::getenv("TQ_DEBUG_CHECKS");  // read per call: a few hundred ns at most
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+namespace {
+
+// Copies `bytes` of device memory to `host` on `stream` and waits for it.
+tq_status fetch(void* host, const void* dev, size_t bytes, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "debug check copy");
+}
+
+tq_status debug_check_slots(const long long* slots, long long n, long long num_blocks, void* stream) {
+  std::vector<long long> h(static_cast<size_t>(n));
+  tq_status st = fetch(h.data(), slots, h.size() * sizeof(long long), stream);
+  return st != TQ_OK ? st : check_slots(h.data(), n, num_blocks);
+}
+
+}  // namespace
+
 }  // namespace tq
 
 using namespace tq;
@@ -420,6 +468,69 @@ tq_status tq_layer_destroy(tq_layer* L) {
   return TQ_OK;
 }
 
+tq_status tq_layer_export(const tq_layer* L, float* R, float* S, float* centroids, float* boundaries,
+                          float* v_centroids, float* v_boundaries, void* hip_stream) {
+  clear_error();
+  if (!L) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer");
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int d = kDim, H = L->cfg.n_kv_heads;
+  const size_t n = static_cast<size_t>(H) * d * d;
+  std::vector<float> st;
+  if (!L->cfg.bypass) {
+    if (R) {
+      hipError_t e = hipMemcpyAsync(R, L->dR, n * sizeof(float), hipMemcpyDeviceToHost, s);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    }
+    if (S) {
+      st.resize(n);
+      hipError_t e = hipMemcpyAsync(st.data(), L->dST, n * sizeof(float), hipMemcpyDeviceToHost, s);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    }
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (S)
+      for (int h = 0; h < H; ++h)
+        for (int i = 0; i < d; ++i)
+          for (int j = 0; j < d; ++j)
+            S[(static_cast<size_t>(h) * d + i) * d + j] = st[(static_cast<size_t>(h) * d + j) * d + i];
+  }
+  if (L->levels) {
+    if (centroids) std::memcpy(centroids, L->centroids, L->levels * sizeof(float));
+    if (boundaries) std::memcpy(boundaries, L->boundaries, (L->levels - 1) * sizeof(float));
+  }
+  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE) {
+    const int lv = 1 << L->cfg.v_bits;
+    if (v_centroids) std::memcpy(v_centroids, L->v_centroids, lv * sizeof(float));
+    if (v_boundaries) std::memcpy(v_boundaries, L->v_boundaries, (lv - 1) * sizeof(float));
+  }
+  return TQ_OK;
+}
+
+tq_status tq_layer_export_operands(const tq_layer* L, tq_operands which, void* host_out, size_t capacity,
+                                   size_t* bytes, void* hip_stream) {
+  clear_error();
+  if (!L || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "null argument");
+  if (L->cfg.bypass) return fail(TQ_ERR_UNSUPPORTED, "bypass layers hold no matrix-core operands");
+  const size_t H = static_cast<size_t>(L->cfg.n_kv_heads);
+  const unsigned short* src = nullptr;
+  size_t count = 0;
+  switch (which) {
+    case TQ_OPERANDS_COMPRESS: src = L->dOpA; count = H * 8 * kOpSets * 4 * 64 * 8; break;
+    case TQ_OPERANDS_PROLOGUE: src = L->dOpQ; count = H * 16 * 4 * 2 * 64 * 8; break;
+    case TQ_OPERANDS_DECOMPRESS: src = L->dOpD; count = H * 8 * 4 * 4 * 64 * 8; break;
+    default: return fail(TQ_ERR_INVALID_ARGUMENT, "unknown operand buffer %d", static_cast<int>(which));
+  }
+  *bytes = count * sizeof(unsigned short);
+  if (!host_out) return TQ_OK;
+  if (capacity < *bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "capacity %zu < %zu bytes", capacity, *bytes);
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipMemcpyAsync(host_out, src, *bytes, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return TQ_OK;
+}
+
 tq_status tq_compress_kv(const tq_layer* L, const void* k, const void* v, tq_dtype in_dtype,
                          long long n_tokens, long long k_token_stride, long long v_token_stride,
                          const long long* slot_mapping, void* pool, long long num_blocks,
@@ -439,6 +550,10 @@ tq_status tq_compress_kv(const tq_layer* L, const void* k, const void* v, tq_dty
   if (n_tokens == 0) return TQ_OK;
   if (!k || !v || !slot_mapping || !pool) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
   if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
+  if (debug_checks()) {
+    tq_status st = debug_check_slots(slot_mapping, n_tokens, num_blocks, hip_stream);
+    if (st != TQ_OK) return st;
+  }
   return launch_compress(L, k, v, in_dtype, n_tokens, k_token_stride, v_token_stride, slot_mapping,
                          pool, hip_stream);
 }
@@ -454,6 +569,10 @@ tq_status tq_decompress_kv(const tq_layer* L, const void* pool, long long num_bl
   if (n_tokens == 0) return TQ_OK;
   if (!pool || !slot_mapping || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
   if (n_tokens > (1LL << 31) - 1) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
+  if (debug_checks()) {
+    tq_status st = debug_check_slots(slot_mapping, n_tokens, num_blocks, hip_stream);
+    if (st != TQ_OK) return st;
+  }
   return launch_decompress(L, pool, slot_mapping, n_tokens, k_out, v_out, out_dtype, hip_stream);
 }
 
@@ -511,6 +630,13 @@ tq_status tq_decode_attn(const tq_layer* L, const void* q, tq_dtype q_dtype, int
   if (workspace_bytes < p.ws_bytes)
     return fail(TQ_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", workspace_bytes, p.ws_bytes);
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kDim));
+  if (debug_checks()) {
+    std::vector<int> hl(static_cast<size_t>(batch)), ht(static_cast<size_t>(batch) * max_blocks_per_seq);
+    st = fetch(hl.data(), seq_lens, hl.size() * sizeof(int), hip_stream);
+    if (st == TQ_OK && !ht.empty()) st = fetch(ht.data(), block_table, ht.size() * sizeof(int), hip_stream);
+    if (st == TQ_OK) st = check_decode_tables(hl.data(), ht.data(), batch, max_blocks_per_seq, max_seq_len, num_blocks);
+    if (st != TQ_OK) return st;
+  }
   return launch_decode(L, p, q, q_dtype, pool, block_table, max_blocks_per_seq, seq_lens, scale, out,
                        out_dtype, workspace, hip_stream);
 }

@@ -298,28 +298,20 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
                           long long n_tokens, long long k_stride, long long v_stride,
                           const long long* slots, void* pool, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (n_tokens * 128 >= (1LL << 32)) return fail(TQ_ERR_UNSUPPORTED, "n_tokens too large for one launch");
-  const dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(L->cfg.n_kv_heads));
   ProfScope prof(kKCompress, stream);
-  if (L->cfg.bypass) {
-    if ((k_stride | v_stride) & 1)
-      return fail(TQ_ERR_UNSUPPORTED, "bypass compress needs even token strides");
-    hipLaunchKernelGGL(store_bypass_kernel, grid, dim3(64), 0, s,
-                       static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
-                       k_stride, v_stride, slots, static_cast<unsigned char*>(pool),
-                       L->cfg.n_kv_heads, static_cast<unsigned>(L->lay.block_bytes));
-  } else if (L->cfg.value_mode == TQ_VAL_GROUP &&  // MSE-coded values: the per-token kernel below
-             compress_mfma_applies(L, k, v, in_dtype, n_tokens, k_stride, v_stride)) {
+  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_GROUP &&  // MSE-coded values: the per-token kernel below
+      compress_mfma_applies(L, k, v, in_dtype, n_tokens, k_stride, v_stride)) {
     tq_status st = launch_compress_mfma(L, k, v, n_tokens, k_stride, v_stride, slots, pool, stream);
     if (st != TQ_OK) return st;
-  } else {
-    CompressArgs a;
-    a.k = k;
-    a.v = v;
-    a.k_stride = k_stride;
-    a.v_stride = v_stride;
-    a.slots = slots;
-    a.pool = static_cast<unsigned char*>(pool);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
+    return TQ_OK;
+  }
+  if (L->cfg.bypass && ((k_stride | v_stride) & 1))
+    return fail(TQ_ERR_UNSUPPORTED, "bypass compress needs even token strides");
+  void* fn = nullptr;
+  CompressArgs a;
+  if (!L->cfg.bypass) {
     a.RT = L->dRT;
     a.ST = L->dST;
     a.H = L->cfg.n_kv_heads;
@@ -337,15 +329,39 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
       a.vcent[i] = L->v_centroids[i];
       a.vbnd[i] = L->v_boundaries[i];
     }
-    void* fn = (in_dtype == TQ_BF16) ? pick<true>(L->cfg.k_bits, L->cfg.v_bits)
-                                     : pick<false>(L->cfg.k_bits, L->cfg.v_bits);
+    fn = (in_dtype == TQ_BF16) ? pick<true>(L->cfg.k_bits, L->cfg.v_bits) : pick<false>(L->cfg.k_bits, L->cfg.v_bits);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
-    void* args[] = {&a};
-    hipError_t e = hipLaunchKernel(fn, grid, dim3(512), args, 0, s);
+  }
+  // One workgroup per (token, head) (512 lanes; 64 for bypass layers): launched
+  // over token ranges of at most 2^22, so that no launch exceeds 2^31 work-items
+  // in the token dimension.
+  constexpr long long kRange = 1LL << 22;
+  const size_t esz = in_dtype == TQ_BF16 ? 2 : 4;
+  for (long long t0 = 0; t0 < n_tokens; t0 += kRange) {
+    const long long n = n_tokens - t0 < kRange ? n_tokens - t0 : kRange;
+    const dim3 grid(static_cast<unsigned>(n), static_cast<unsigned>(L->cfg.n_kv_heads));
+    const void* kr = static_cast<const unsigned char*>(k) + static_cast<size_t>(t0) * k_stride * esz;
+    const void* vr = static_cast<const unsigned char*>(v) + static_cast<size_t>(t0) * v_stride * esz;
+    const long long* sr = slots + t0;
+    if (L->cfg.bypass) {
+      hipLaunchKernelGGL(store_bypass_kernel, grid, dim3(64), 0, s,
+                         static_cast<const unsigned short*>(kr), static_cast<const unsigned short*>(vr),
+                         k_stride, v_stride, sr, static_cast<unsigned char*>(pool),
+                         L->cfg.n_kv_heads, static_cast<unsigned>(L->lay.block_bytes));
+    } else {
+      a.k = kr;
+      a.v = vr;
+      a.k_stride = k_stride;
+      a.v_stride = v_stride;
+      a.slots = sr;
+      a.pool = static_cast<unsigned char*>(pool);
+      void* args[] = {&a};
+      hipError_t e = hipLaunchKernel(fn, grid, dim3(512), args, 0, s);
+      if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
+    }
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TQ_ERR_HIP, "compress launch: %s", hipGetErrorString(e));
   return TQ_OK;
 }
 

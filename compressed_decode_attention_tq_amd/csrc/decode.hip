@@ -1,8 +1,9 @@
 // Split-K paged decode attention over the compressed store (gfx950).
 //
-// "turbo-attn 0.24.0", "How it works": the query is rotated once by the head's
-// rotation and attention runs in the rotated space; decode unpacks, dequantises
-// and runs Q.K, online softmax and P.V in one pass with no decompress buffer.
+// "turbo-attn 0.24.0", "How it works": since the head's rotation is orthogonal,
+// attention of the rotated query over the rotated store equals the original
+// attention; the decode reads the packed records and forms scores, softmax and
+// the value sum in one kernel, never writing an expanded copy of the cache.
 // "turbo-attn 0.24.0", "Configuration" (TKV_DECODE_SPLITS) and "tiny-turboquant
 // 0.18.0", "Fused decode-attention path": the context is split across
 // workgroups whose partials are merged by a second launch.

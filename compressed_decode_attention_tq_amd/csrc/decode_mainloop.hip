@@ -1,8 +1,8 @@
 // Split-K mainloop of paged decode attention over the compressed store (gfx950).
 //
 // Scores ("How 0xsero/turboquant works", "Key Storage and Attention Scoring";
-// "turbo-attn 0.24.0", "How it works": query rotated once, attention in the
-// rotated space, one pass with no decompress buffer):
+// "turbo-attn 0.24.0", "How it works": the query is rotated once and the packed
+// records are read directly, with no expanded copy of the cache):
 //   s_i = scale * (n_i / sqrt d) * (q'.c[idx_i] + sqrt(pi/2)/128 * gamma_i * u.(2 z_i - 1)).
 // Values ("How 0xsero/turboquant works", "Value Compression"):
 //   o' = sum_i p_i (zero_i + scale_i * code_i), per 32-wide group.
@@ -437,8 +437,11 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   // the wave's chunk j (chunk j = tokens start + 32 (wave + 4j) .. +31; at most
   // 32 chunks per wave).  They and the query operand (prepared by the prologue)
   // are read before the sequence length is known, so that the three reads
-  // overlap instead of forming a chain; table entries past the context (the
-  // index clamped to the row) are read but never used.
+  // overlap instead of forming a chain.  Table entries past the context (the
+  // index clamped to the row) are read but never dereferenced: a page id is
+  // used only for a chunk whose first token lies inside the context, and a
+  // second page only when its first token does too, so padding entries of a
+  // row may hold anything (-1 included).
   // (The host launches no split kernel for a table of zero blocks per row.)
   int ids;
   {
@@ -470,8 +473,11 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   const int nch = span > 0 ? (span + 127) / 128 : 0;  // chunks of this wave
   auto load = [&](Chunk<KB, VB>& c, int j) {
     const int c0 = start + 32 * (wave + 4 * j);
-    const int b0 = __builtin_amdgcn_readlane(ids, 2 * j);
-    const int b1 = (c0 + 16 < end) ? __builtin_amdgcn_readlane(ids, 2 * j + 1) : b0;
+    // A wave with no chunk in the context (its first chunk starts at or past
+    // the end) still issues the ring's loads, from block 0 (the pool holds at
+    // least one block), so that no table entry past the context is used.
+    const int b0 = nch > 0 ? __builtin_amdgcn_readlane(ids, 2 * j) : 0;
+    const int b1 = (nch > 0 && c0 + 16 < end) ? __builtin_amdgcn_readlane(ids, 2 * j + 1) : b0;
     load_chunk<KB, VB>(c, page_ptr(b0), page_ptr(b1), lofs, kg >= 2);
   };
   // Every step loads one chunk (past the wave's last chunk, the last one again:

@@ -268,22 +268,19 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = out_dtype == TQ_BF16;
   const int H = L->cfg.n_kv_heads;
-  hipError_t e;
+  const size_t row_bytes = static_cast<size_t>(H) * kDim * (bf ? 2 : 4);  // output bytes per token
+  // Launched over token ranges (multiples of 16) small enough that no launch
+  // exceeds 2^31 work-items in the token dimension: 128 lanes per token for
+  // bypass layers, 256 per 16-token tile otherwise.
+  const long long range = L->cfg.bypass ? (1LL << 24) : (1LL << 27);
+  void* fn = nullptr;
+  DArgs a;
   if (L->cfg.bypass) {
-    void* fn = bf ? reinterpret_cast<void*>(&decompress_bypass_kernel<true>)
-                  : reinterpret_cast<void*>(&decompress_bypass_kernel<false>);
-    const unsigned char* p = static_cast<const unsigned char*>(pool);
-    unsigned bb = static_cast<unsigned>(L->lay.block_bytes);
-    void* args[] = {&p, const_cast<long long**>(&slots), &k_out, &v_out, const_cast<int*>(&H), &bb};
-    e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(n_tokens), H), dim3(128), args, 0, s);
+    fn = bf ? reinterpret_cast<void*>(&decompress_bypass_kernel<true>)
+            : reinterpret_cast<void*>(&decompress_bypass_kernel<false>);
   } else {
-    DArgs a;
     a.pool = static_cast<const unsigned char*>(pool);
-    a.slots = slots;
-    a.kout = k_out;
-    a.vout = v_out;
     a.opd = reinterpret_cast<const u32x4*>(L->dOpD);
-    a.n_tokens = n_tokens;
     a.H = H;
     a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
     a.off_kc = static_cast<unsigned>(L->lay.off_kc);
@@ -297,13 +294,32 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
       a.vcent[i] = L->v_centroids[i];
     }
     a.vm = L->cfg.value_mode == TQ_VAL_MSE ? 1 : 0;
-    void* fn = bf ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits) : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
+    fn = bf ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits) : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
                          L->cfg.v_bits);
-    void* args[] = {&a};
-    e = hipLaunchKernel(fn, dim3(static_cast<unsigned>((n_tokens + 15) / 16), H), dim3(256), args, 0, s);
   }
-  if (e != hipSuccess) return fail(TQ_ERR_HIP, "decompress launch: %s", hipGetErrorString(e));
+  for (long long t0 = 0; t0 < n_tokens; t0 += range) {
+    const long long n = n_tokens - t0 < range ? n_tokens - t0 : range;
+    const long long* sr = slots + t0;
+    void* kr = static_cast<unsigned char*>(k_out) + static_cast<size_t>(t0) * row_bytes;
+    void* vr = static_cast<unsigned char*>(v_out) + static_cast<size_t>(t0) * row_bytes;
+    hipError_t e;
+    if (L->cfg.bypass) {
+      const unsigned char* p = static_cast<const unsigned char*>(pool);
+      unsigned bb = static_cast<unsigned>(L->lay.block_bytes);
+      int hh = H;
+      void* args[] = {&p, &sr, &kr, &vr, &hh, &bb};
+      e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(n), H), dim3(128), args, 0, s);
+    } else {
+      a.slots = sr;
+      a.kout = kr;
+      a.vout = vr;
+      a.n_tokens = n;
+      void* args[] = {&a};
+      e = hipLaunchKernel(fn, dim3(static_cast<unsigned>((n + 15) / 16), H), dim3(256), args, 0, s);
+    }
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "decompress launch: %s", hipGetErrorString(e));
+  }
   return TQ_OK;
 }
 

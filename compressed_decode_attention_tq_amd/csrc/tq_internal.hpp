@@ -51,6 +51,14 @@ struct Layout {
 tq_status make_layout(const tq_layer_config* cfg, Layout* out);
 tq_status validate_config(const tq_layer_config* cfg);
 
+// ------------------------------------------------------- debug checks
+// Host-side validation of index arrays (the TQ_DEBUG_CHECKS=1 option copies
+// them from the device first).  Return TQ_OK or TQ_ERR_INVALID_ARGUMENT.
+tq_status check_slots(const long long* slots, long long n, long long num_blocks);
+tq_status check_decode_tables(const int* seq_lens, const int* block_table, int batch, int max_blocks,
+                              int max_seq_len, long long num_blocks);
+bool debug_checks();
+
 // ------------------------------------------------------------- profiling
 enum KernelId { kKCompress = 0, kKPrologue = 1, kKSplitK = 2, kKCombine = 3, kKCount = 4 };
 // Brackets one launch with HIP events when timing of `id` is enabled.

@@ -39,7 +39,15 @@
  *     the null stream); a launch failure is reported as TQ_ERR_HIP.  The compress
  *     and decode entry points never allocate and never synchronise.
  *   - Contents of device buffers (slot ids, block ids, sequence lengths) are the
- *     caller's contract; they are not range-checked on the device.
+ *     caller's contract; they are not range-checked on the device.  Debug
+ *     option: while the environment variable TQ_DEBUG_CHECKS is set (to
+ *     anything but "0"; read at every call), tq_compress_kv and
+ *     tq_decompress_kv copy slot_mapping, and tq_decode_attn copies seq_lens and
+ *     the used block-table entries, to host memory (synchronising the stream)
+ *     and return TQ_ERR_INVALID_ARGUMENT before any launch if a slot is past the
+ *     pool, a length is outside [0, min(max_seq_len, 16*max_blocks_per_seq)] or
+ *     a block id of a used page is outside [0, num_blocks).  Off by default: it
+ *     allocates host memory and synchronises, which the hot path never does.
  *   - Supported: head_dim = 128, block_size = 16, v_group = 32,
  *     k_bits in {2,3,4}, v_bits in {2,3,4}, query heads per KV head in {1,2,4,8}.
  *
@@ -75,7 +83,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 5
+#define TQ_ABI_VERSION 6
 
 typedef enum {
   TQ_OK = 0,
@@ -140,8 +148,8 @@ typedef enum { TQ_KEY_QJL = 0, TQ_KEY_MSE = 1, TQ_KEY_MSE_NC = 2 } tq_key_mode;
  *   TQ_ROT_HADAMARD  randomised Hadamard R_g = H D / sqrt(d): H the Sylvester
  *                    Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), D a diagonal
  *                    of random signs (+1 when the top bit of the tag-3 SplitMix64
- *                    output is 0) ("turbo-attn 0.24.0", "How it works": rotate each
- *                    KV vector with a fast Walsh-Hadamard transform).  Every entry
+ *                    output is 0) ("turbo-attn 0.24.0", "How it works": the KV rotation
+ *                    is a fast Walsh-Hadamard transform).  Every entry
  *                    is +-1/sqrt(d), so the compressor's rotations take one
  *                    matrix-core pass on the exact +-1 pattern instead of three. */
 typedef enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 } tq_rotation;
@@ -204,6 +212,48 @@ tq_status tq_layer_create(const tq_layer_config* cfg, void* hip_stream, tq_layer
 /* Frees the layer's device memory.  NULL is accepted.  The caller must ensure no
  * kernel using the layer is still running. */
 tq_status tq_layer_destroy(tq_layer* layer);
+
+/* The state a created layer actually holds, copied back from the device (the
+ * rotation/projection state and the codebooks of "How 0xsero/turboquant works",
+ * "Compression Pipeline"):
+ *   R, S          host out [n_kv_heads][128][128] float32, row-major (nullable):
+ *                 the device copies of R_g and S_g the kernels read (S is held
+ *                 transposed on the device and returned untransposed; a bypass
+ *                 layer holds neither and leaves them untouched)
+ *   centroids     host out [2^k_bits] float32 (nullable): the stored key codebook
+ *   boundaries    host out [2^k_bits - 1] float32 (nullable)
+ *   v_centroids   host out [2^v_bits] float32 (nullable): the stored value
+ *                 codebook of a TQ_VAL_MSE layer (untouched otherwise)
+ *   v_boundaries  host out [2^v_bits - 1] float32 (nullable)
+ * Device-to-host copies on hip_stream, then one synchronisation of it; nothing is
+ * allocated on the device.  Errors: TQ_ERR_INVALID_ARGUMENT for a null layer,
+ * TQ_ERR_HIP if a copy fails. */
+tq_status tq_layer_export(const tq_layer* layer, float* R, float* S, float* centroids, float* boundaries,
+                          float* v_centroids, float* v_boundaries, void* hip_stream);
+
+/* The matrix-core operand buffers a created layer derived from R and S, copied
+ * back byte for byte (test and inspection aid):
+ *   which = TQ_OPERANDS_COMPRESS    R as three bf16 pieces and S as two float16
+ *           pieces, [H][8 row tiles][5 pieces][4 K-steps][64 lanes][8] uint16;
+ *           lane l of (tile w, step s) holds M[16w + l%16][32s + 8(l/16) + j]
+ *           (Hadamard layers: piece 0 the exact +-1 sign pattern of R, pieces
+ *           1 and 2 zero)
+ *         = TQ_OPERANDS_PROLOGUE    W = [R; S R] (the float64 product of the
+ *           stored float32 matrices) as float16 hi + lo,
+ *           [H][16 column tiles][4 K-steps][hi, lo][64 lanes][8] uint16; lane l
+ *           of (tile t, step s) holds W[16t + l%16][32s + 8(l/16) + j]
+ *         = TQ_OPERANDS_DECOMPRESS  R and P = S R as float16 hi + lo,
+ *           [H][8 column tiles][4 K-steps][R hi, R lo, P hi, P lo][64 lanes][8]
+ *           uint16; lane l of (tile t, step s) holds M[32s + 8(l/16) + j][16t + l%16]
+ *   host_out   host out, nullable (then only *bytes is set)
+ *   capacity   bytes available at host_out
+ *   bytes      host out: the buffer's size
+ * TQ_ERR_INVALID_ARGUMENT if capacity < the size (host_out non-null) or `which`
+ * is unknown, TQ_ERR_UNSUPPORTED for a bypass layer (no operands), TQ_ERR_HIP if
+ * the copy fails.  Synchronises hip_stream once. */
+typedef enum { TQ_OPERANDS_COMPRESS = 0, TQ_OPERANDS_PROLOGUE = 1, TQ_OPERANDS_DECOMPRESS = 2 } tq_operands;
+tq_status tq_layer_export_operands(const tq_layer* layer, tq_operands which, void* host_out, size_t capacity,
+                                   size_t* bytes, void* hip_stream);
 
 /* Byte layout of one (block, head) region of the pool.
  *   block_bytes    host out

@@ -1,7 +1,8 @@
 """LSB-first bit packing of per-vector code and sign fields.
 
-"How 0xsero/turboquant works", "Value Compression": packed low-bit payloads,
-four 2-bit values or two 4-bit values per byte.  "5x Faster LLM Inference?
+"How 0xsero/turboquant works", "Value Compression": value payloads are stored
+bit-packed, with several low-bit codes sharing a byte (a byte holds 4 codes at
+2 bits, 2 at 4 bits).  "5x Faster LLM Inference?
 ...", "Example 4: Kernel-Level Operations": the last compression step packs the
 bits.  The pages fix no 3-bit format; the reading used everywhere here is a
 little-endian bitstream per field: element j of a b-bit field occupies stream

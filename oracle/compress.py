@@ -70,9 +70,8 @@ def compress_keys(K, R, S, centroids, boundaries, key_mode="qjl"):
     chat = np.asarray(centroids)[idx]
     rho = t - chat
     if key_mode == "qjl":
-        gamma = np.sqrt(np.sum(rho * rho, axis=-1))
-        y = rho @ S.T
-        z = (y >= 0.0).astype(np.int64)
+        q = qjl_signs(t, idx, S, centroids)
+        gamma, y, z = q["gamma"], q["y"], q["z"]
         n_store = n
     else:
         gamma = np.zeros_like(n)
@@ -89,6 +88,18 @@ def compress_keys(K, R, S, centroids, boundaries, key_mode="qjl"):
     }
 
 
+def qjl_signs(t, idx, S, centroids):
+    """The QJL step for given codebook decisions: rho = t - c[idx], gamma = ||rho||,
+    y = S rho, z_j = [y_j >= 0] ("How 0xsero/turboquant works", "Compression
+    Pipeline": the 1-bit sign sketch of the quantisation residual).  t: [n, d]
+    standardised rotated coordinates, idx: [n, d] codes (any codes, not only the
+    nearest ones: a checker uses it to recompute the signs that follow from codes
+    taken elsewhere)."""
+    rho = np.asarray(t, dtype=np.float64) - np.asarray(centroids, dtype=np.float64)[np.asarray(idx)]
+    y = rho @ np.asarray(S, dtype=np.float64).T
+    return {"rho": rho, "gamma": np.sqrt(np.sum(rho * rho, axis=-1)), "y": y, "z": (y >= 0.0).astype(np.int64)}
+
+
 def quantize_groups(vrot, v_bits, group):
     """Group scale/zero quantisation of rotated values vrot: [n, d]."""
     n, d = vrot.shape
@@ -103,14 +114,14 @@ def quantize_groups(vrot, v_bits, group):
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint((g - z) / np.where(s > 0.0, s, 1.0))
     codes = np.where(s > 0.0, np.clip(q, 0, top), 0).astype(np.int64)
-    return codes.reshape(n, d), scale16, zero16
+    return codes.reshape(n, d), scale16, zero16, mn, mx
 
 
 def compress_values(V, R, v_bits, group):
     V = np.asarray(V, dtype=np.float64)
     vrot = V @ R.T
-    codes, scale16, zero16 = quantize_groups(vrot, v_bits, group)
-    return {"vrot": vrot, "codes": codes, "scale16": scale16, "zero16": zero16}
+    codes, scale16, zero16, mn, mx = quantize_groups(vrot, v_bits, group)
+    return {"vrot": vrot, "codes": codes, "scale16": scale16, "zero16": zero16, "mn": mn, "mx": mx}
 
 
 def compress_values_mse(V, R, centroids, boundaries):

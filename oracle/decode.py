@@ -1,11 +1,10 @@
 """Paged decode attention over the compressed store, float64.
 
-"turbo-attn 0.24.0", "How it works": attention on rotated K/V equals attention
-on the originals when the query is rotated by the same matrix; the query is
-rotated once and everything runs in the rotated space; the decode path unpacks,
-dequantises and runs Q.K, online softmax and P.V in one pass.  "How 0xsero/
-turboquant works", "Key Storage and Attention Scoring": scores are approximated
-from the compressed keys without the originals.  "turbo-attn 0.24.0",
+"turbo-attn 0.24.0", "How it works": an orthogonal rotation applied to the
+keys, the values and the query leaves attention unchanged, so the query is
+rotated once per step and the scores, softmax and value sum are formed on the
+rotated, compressed store in a single kernel.  "How 0xsero/turboquant works",
+"Key Storage and Attention Scoring": the scores use only the compressed keys.  "turbo-attn 0.24.0",
 "Configuration" (TKV_DECODE_SPLITS) and "tiny-turboquant 0.18.0", "Fused
 decode-attention path": the context is split, partial results combined.
 

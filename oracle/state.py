@@ -12,8 +12,8 @@ makes the factor unique and Haar distributed.
 S: an m x d matrix of i.i.d. N(0,1) entries from the projection stream, m = d
 (the QJL residual-sign projection of the same sections).
 
-Structured alternative ("turbo-attn 0.24.0", "How it works": rotate each KV
-vector with a fast Walsh-Hadamard transform): R = H D / sqrt(d), H the
+Structured alternative ("turbo-attn 0.24.0", "How it works": there the KV
+rotation is a fast Walsh-Hadamard transform): R = H D / sqrt(d), H the
 Sylvester-ordered Hadamard matrix, H[i][j] = (-1)^popcount(i & j), and D a
 diagonal of random signs from the tag-3 stream (a randomised Hadamard
 transform).  Every entry of R is +-1/sqrt(d).

@@ -24,11 +24,18 @@ def _declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = tq.lib()
     names = _declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tq_abi_version() == tq.ABI_VERSION == 5
+    assert lib.tq_abi_version() == tq.ABI_VERSION == 6
+
+
+def test_export_error_paths_without_a_device():
+    lib = tq.lib()
+    assert lib.tq_layer_export(None, None, None, None, None, None, None, None) == tq.ERR_INVALID_ARGUMENT
+    n = ctypes.c_size_t(0)
+    assert lib.tq_layer_export_operands(None, 0, None, 0, ctypes.byref(n), None) == tq.ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.parametrize("dist,name", [(tq.DIST_GAUSSIAN, "gaussian"), (tq.DIST_SPHERE, "sphere")])
