@@ -25,6 +25,7 @@ EXPORTED = [
     "tq_layer_create", "tq_layer_destroy", "tq_store_layout", "tq_compress_kv",
     "tq_decode_workspace_size", "tq_decode_attn", "tq_profile_enable", "tq_profile_read",
     "tq_profile_reset", "tq_decompress_kv", "tq_layer_export", "tq_layer_export_operands",
+    "tq_decode_attn_noalloc",
 ]
 OPERANDS_COMPRESS, OPERANDS_PROLOGUE, OPERANDS_DECOMPRESS = range(3)  # tq_operands
 K_COMPRESS, K_PROLOGUE, K_SPLITK, K_COMBINE = range(4)
@@ -81,6 +82,8 @@ def lib():
     L.tq_decode_workspace_size.argtypes = [vp, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)]
     L.tq_decode_attn.argtypes = [vp, vp, c_int, c_int, c_int, vp, c_ll, vp, c_int, vp, c_int,
                                  ctypes.c_float, c_int, vp, c_int, vp, c_size, vp]
+    L.tq_decode_attn_noalloc.argtypes = [vp, vp, c_int, c_int, c_int, vp, c_ll, vp, c_int, vp, c_int,
+                                         ctypes.c_float, c_int, vp, c_int, vp]
     L.tq_layer_export.argtypes = [vp, fp, fp, fp, fp, fp, fp, vp]
     L.tq_layer_export_operands.argtypes = [vp, c_int, vp, c_size, ctypes.POINTER(c_size), vp]
     L.tq_profile_enable.argtypes = [ctypes.c_uint]
@@ -89,7 +92,7 @@ def lib():
     for name in ["tq_codebook_build", "tq_layer_state_host", "tq_layer_create", "tq_layer_destroy",
                  "tq_store_layout", "tq_compress_kv", "tq_decode_workspace_size", "tq_decode_attn",
                  "tq_profile_enable", "tq_profile_read", "tq_profile_reset", "tq_layer_export",
-                 "tq_layer_export_operands", "tq_decompress_kv"]:
+                 "tq_layer_export_operands", "tq_decompress_kv", "tq_decode_attn_noalloc"]:
         getattr(L, name).restype = c_int
     _LIB = L
     return L
@@ -313,6 +316,18 @@ def decode_attn(layer, q, pool, block_table, seq_lens, max_seq_len, out=None, wo
                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
                                 float(softmax_scale), num_splits, _ptr(out), _dtype_code(out),
                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_attn_noalloc(layer, q, pool, block_table, seq_lens, max_seq_len, out, softmax_scale=0.0, num_splits=0,
+                        stream=None):
+    """decode_attn with the library's static per-GPU workspace (tq_decode_attn_noalloc):
+    nothing is allocated, `out` is required."""
+    num_blocks = _check_decode_args(layer, q, pool, block_table, seq_lens, out)
+    _check(lib().tq_decode_attn_noalloc(layer.handle, _ptr(q), _dtype_code(q), q.shape[0], q.shape[1], _ptr(pool),
+                                        num_blocks, _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                        max_seq_len, float(softmax_scale), num_splits, _ptr(out), _dtype_code(out),
+                                        _stream(stream)))
     return out
 
 

@@ -188,6 +188,40 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   return TQ_OK;
 }
 
+tq_status prepare_decode(const tq_layer* L, const void* q, tq_dtype q_dtype, int batch, int n_q_heads,
+                         const void* pool, long long num_blocks, const int* block_table, int max_blocks_per_seq,
+                         const int* seq_lens, int max_seq_len, float softmax_scale, int num_splits, void* out,
+                         tq_dtype out_dtype, DecodePlan* plan, float* scale) {
+  if (!L) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer");
+  if (batch < 0 || n_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_blocks_per_seq < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "negative size");
+  if (n_q_heads % L->cfg.n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
+                L->cfg.n_kv_heads);
+  const int rep = n_q_heads / L->cfg.n_kv_heads;
+  if (rep != 1 && rep != 2 && rep != 4 && rep != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head = %d not supported (1, 2, 4, 8)", rep);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "query dtype %d not supported (F32, BF16)", static_cast<int>(q_dtype));
+  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE)
+    return fail(TQ_ERR_UNSUPPORTED, "decode of layers with MSE-coded values is not built");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
+    return fail(TQ_ERR_UNSUPPORTED, "output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
+  if (static_cast<long long>(max_blocks_per_seq) * kPage < max_seq_len)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "max_blocks_per_seq*16 = %lld < max_seq_len %d",
+                static_cast<long long>(max_blocks_per_seq) * kPage, max_seq_len);
+  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (batch == 0) return TQ_OK;
+  if (!q || !pool || !block_table || !seq_lens || !out) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return fail(TQ_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
+  tq_status st = plan_decode(L, batch, n_q_heads, max_seq_len, num_splits, plan);
+  if (st != TQ_OK) return st;
+  *scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kDim));
+  return TQ_OK;
+}
+
 tq_status check_slots(const long long* slots, long long n, long long num_blocks) {
   for (long long i = 0; i < n; ++i)
     if (slots[i] >= num_blocks * kPage)
@@ -596,40 +630,16 @@ tq_status tq_decode_attn(const tq_layer* L, const void* q, tq_dtype q_dtype, int
                          tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
                          void* hip_stream) {
   clear_error();
-  if (!L) return fail(TQ_ERR_INVALID_ARGUMENT, "null layer");
-  if (batch < 0 || n_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_blocks_per_seq < 0)
-    return fail(TQ_ERR_INVALID_ARGUMENT, "negative size");
-  if (n_q_heads % L->cfg.n_kv_heads != 0)
-    return fail(TQ_ERR_INVALID_ARGUMENT, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
-                L->cfg.n_kv_heads);
-  const int rep = n_q_heads / L->cfg.n_kv_heads;
-  if (rep != 1 && rep != 2 && rep != 4 && rep != 8)
-    return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head = %d not supported (1, 2, 4, 8)", rep);
-  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16)
-    return fail(TQ_ERR_UNSUPPORTED, "query dtype %d not supported (F32, BF16)", static_cast<int>(q_dtype));
-  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE)
-    return fail(TQ_ERR_UNSUPPORTED, "decode of layers with MSE-coded values is not built");
-  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
-    return fail(TQ_ERR_UNSUPPORTED, "output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
-  if (static_cast<long long>(max_blocks_per_seq) * kPage < max_seq_len)
-    return fail(TQ_ERR_INVALID_ARGUMENT, "max_blocks_per_seq*16 = %lld < max_seq_len %d",
-                static_cast<long long>(max_blocks_per_seq) * kPage, max_seq_len);
-  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
-    return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
-  if (batch == 0) return TQ_OK;
-  if (!q || !pool || !block_table || !seq_lens || !out || !workspace)
-    return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
-  if (num_blocks <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_blocks must be > 0");
+  DecodePlan p;
+  float scale = 0.0f;
+  tq_status st = prepare_decode(L, q, q_dtype, batch, n_q_heads, pool, num_blocks, block_table, max_blocks_per_seq,
+                                seq_lens, max_seq_len, softmax_scale, num_splits, out, out_dtype, &p, &scale);
+  if (st != TQ_OK || batch == 0) return st;
+  if (!workspace) return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
-    return fail(TQ_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
-  DecodePlan p;
-  tq_status st = plan_decode(L, batch, n_q_heads, max_seq_len, num_splits, &p);
-  if (st != TQ_OK) return st;
   if (workspace_bytes < p.ws_bytes)
     return fail(TQ_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", workspace_bytes, p.ws_bytes);
-  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kDim));
   if (debug_checks()) {
     std::vector<int> hl(static_cast<size_t>(batch)), ht(static_cast<size_t>(batch) * max_blocks_per_seq);
     st = fetch(hl.data(), seq_lens, hl.size() * sizeof(int), hip_stream);

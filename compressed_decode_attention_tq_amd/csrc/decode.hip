@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "tq_internal.hpp"
 
@@ -433,4 +434,63 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
   return TQ_OK;
 }
 
+// ------------------------------------------------ allocation-free decode
+// The decode workspace of tq_decode_attn_noalloc: a fixed array in device
+// memory, one per GPU the library runs on, held until the process ends.  Host
+// code never uses the array's name as an address (in host code it is only a
+// stand-in for the symbol): the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept in g_scratch_ptr.
+// Every call on a GPU uses that GPU's array, so calls that overlap on one GPU
+// (on different streams) race; nothing in it needs clearing between calls (each
+// launch writes what the next one reads: the prologue all query operands, each
+// split its partials, and the combine reads only the splits that ran).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+tq_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TQ_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TQ_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+}  // namespace
+
 }  // namespace tq
+
+extern "C" tq_status tq_decode_attn_noalloc(const tq_layer* L, const void* q, tq_dtype q_dtype, int batch,
+                                            int n_q_heads, const void* pool, long long num_blocks,
+                                            const int* block_table, int max_blocks_per_seq, const int* seq_lens,
+                                            int max_seq_len, float softmax_scale, int num_splits, void* out,
+                                            tq_dtype out_dtype, void* hip_stream) {
+  using namespace tq;
+  clear_error();
+  DecodePlan p;
+  float scale = 0.0f;
+  tq_status st = prepare_decode(L, q, q_dtype, batch, n_q_heads, pool, num_blocks, block_table, max_blocks_per_seq,
+                                seq_lens, max_seq_len, softmax_scale, num_splits, out, out_dtype, &p, &scale);
+  if (st != TQ_OK || batch == 0) return st;
+  if (p.ws_bytes > kScratchBytes)
+    return fail(TQ_ERR_UNSUPPORTED,
+                "decode workspace of %zu bytes exceeds the %zu-byte static scratch of tq_decode_attn_noalloc "
+                "(use tq_decode_attn with a caller workspace)", p.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != TQ_OK) return st;
+  return launch_decode(L, p, q, q_dtype, pool, block_table, max_blocks_per_seq, seq_lens, scale, out, out_dtype,
+                       ws, hip_stream);
+}

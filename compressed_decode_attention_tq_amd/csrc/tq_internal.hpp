@@ -130,6 +130,12 @@ struct DecodePlan {
 };
 tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_len,
                       int num_splits, DecodePlan* plan);
+// Argument checks shared by the decode entry points (everything but the
+// workspace); on TQ_OK with batch > 0, *plan and *scale are set.
+tq_status prepare_decode(const tq_layer* L, const void* q, tq_dtype q_dtype, int batch, int n_q_heads,
+                         const void* pool, long long num_blocks, const int* block_table, int max_blocks_per_seq,
+                         const int* seq_lens, int max_seq_len, float softmax_scale, int num_splits, void* out,
+                         tq_dtype out_dtype, DecodePlan* plan, float* scale);
 tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void* pool, const int* block_table,
                            int max_blocks_per_seq, const int* seq_lens, float softmax_scale, const void* qa,
                            float* part, void* stream);

@@ -330,6 +330,24 @@ tq_status tq_decode_attn(const tq_layer* layer, const void* q, tq_dtype q_dtype,
                          tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
                          void* hip_stream);
 
+/* tq_decode_attn without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, kernels and result as tq_decode_attn;
+ * the workspace is instead a fixed 16 MiB array in device memory, one per GPU
+ * the library runs on, held until the process ends.  It allocates nothing and
+ * synchronises nothing (the first call on a device looks up that device's array
+ * address once).  Returns TQ_ERR_UNSUPPORTED, before any launch, when the shape
+ * needs a larger workspace than 16 MiB (tq_decode_workspace_size tells; e.g.
+ * batch 64 x 32 query heads x 8 splits needs 8.9 MB).  All calls on one GPU share
+ * its array: calls that overlap on one GPU (different streams) race, so they
+ * must be ordered by the caller.  TQ_DEBUG_CHECKS is not honoured here (it
+ * would allocate host memory). */
+tq_status tq_decode_attn_noalloc(const tq_layer* layer, const void* q, tq_dtype q_dtype, int batch,
+                                 int n_q_heads, const void* pool, long long num_blocks,
+                                 const int* block_table, int max_blocks_per_seq, const int* seq_lens,
+                                 int max_seq_len, float softmax_scale, int num_splits, void* out,
+                                 tq_dtype out_dtype, void* hip_stream);
+
 /* Kernel timing, a profiling aid (off by default).
  * Kernel ids: 0 = compress, 1 = decode prologue, 2 = decode split-K mainloop,
  * 3 = decode combine/epilogue.

@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = tq.lib()
     names = _declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(names) == sorted(tq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
