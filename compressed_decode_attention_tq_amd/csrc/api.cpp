@@ -39,8 +39,8 @@ tq_status validate_config(const tq_layer_config* cfg) {
     return fail(TQ_ERR_UNSUPPORTED, "block_size %d not supported (only %d)", cfg->block_size, kPage);
   if (cfg->layer < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "layer index must be >= 0");
   if (cfg->bypass) return TQ_OK;
-  if (cfg->k_bits < 2 || cfg->k_bits > 4)
-    return fail(TQ_ERR_UNSUPPORTED, "k_bits %d not supported (2..4)", cfg->k_bits);
+  if (cfg->k_bits < 1 || cfg->k_bits > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "k_bits %d not supported (1..4)", cfg->k_bits);
   if (cfg->v_bits < 2 || cfg->v_bits > 4)
     return fail(TQ_ERR_UNSUPPORTED, "v_bits %d not supported (2..4)", cfg->v_bits);
   if (cfg->v_group != kGroup)

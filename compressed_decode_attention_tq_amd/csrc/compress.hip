@@ -285,6 +285,7 @@ void* pick_vb(int vb) {
 template <bool BF16>
 void* pick(int kb, int vb) {
   switch (kb) {
+    case 1: return pick_vb<BF16, 1>(vb);
     case 2: return pick_vb<BF16, 2>(vb);
     case 3: return pick_vb<BF16, 3>(vb);
     case 4: return pick_vb<BF16, 4>(vb);

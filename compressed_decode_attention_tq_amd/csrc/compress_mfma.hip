@@ -274,7 +274,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
   const int mine = first < a.n_tiles ? static_cast<int>((a.n_tiles - 1 - first) / step + 1) : 0;
   const int pro = mine < P ? mine : P;
   for (int j = 0; j < pro; ++j) stage(first + j * step, j, lane0);
-  if constexpr (KB == 3) {  // key-code words are OR-ed into; each tile's store clears them again
+  if constexpr (KB == 1 || KB == 3) {  // key-code words are OR-ed into; each tile's store clears them again
     for (int i = static_cast<int>(threadIdx.x); i < PG::ks / 4; i += 512) reinterpret_cast<unsigned*>(img)[i] = 0u;
   }
   unsigned clean = 0;  // bit i: iteration k-1-i issued one copy and one page store
@@ -404,11 +404,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
         rec[e0 / 4] = static_cast<unsigned char>(codes);
       } else if constexpr (KB == 4) {
         *reinterpret_cast<unsigned short*>(rec + e0 / 2) = static_cast<unsigned short>(codes);
-      } else {
-        const int bit = 3 * e0, wi = bit >> 5, sh = bit & 31;
+      } else {  // 1 or 3 bits: the four codes' field may share a word with other lanes' (or straddle two)
+        const int bit = KB * e0, wi = bit >> 5, sh = bit & 31;
         unsigned* rw = reinterpret_cast<unsigned*>(rec);
         atomicOr(&rw[wi], codes << sh);
-        if (sh + 12 > 32) atomicOr(&rw[wi + 1], codes >> (32 - sh));
+        if (sh + 4 * KB > 32) atomicOr(&rw[wi + 1], codes >> (32 - sh));
       }
 
       float mn = INFINITY, mx = -INFINITY;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       const int c = w + 8 * lane;
       if (c < kChunks) {
         *reinterpret_cast<u32x4*>(page + 16 * c) = *reinterpret_cast<const u32x4*>(&img[16 * c]);
-        if constexpr (KB == 3) {  // key-code words are OR-ed into: clear what this lane read
+        if constexpr (KB == 1 || KB == 3) {  // key-code words are OR-ed into: clear what this lane read
           if (c < PG::ks / 16) *reinterpret_cast<u32x4*>(&img[16 * c]) = u32x4{0u, 0u, 0u, 0u};
         }
       }
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
           }
         }
       }
-      if constexpr (KB == 3) {  // clear the key-code words this thread read
+      if constexpr (KB == 1 || KB == 3) {  // clear the key-code words this thread read
         if (tid < 4 * KB) {
 #pragma unroll 1
           for (int t = 0; t < 16; ++t)
@@ -618,6 +618,7 @@ void* pick_v(int vb) {
 template <bool HAD, bool QJL>
 void* pick_kv(int kb, int vb) {
   switch (kb) {
+    case 1: return pick_v<1, HAD, QJL>(vb);
     case 2: return pick_v<2, HAD, QJL>(vb);
     case 3: return pick_v<3, HAD, QJL>(vb);
     case 4: return pick_v<4, HAD, QJL>(vb);

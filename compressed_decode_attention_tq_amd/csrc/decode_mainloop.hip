@@ -158,13 +158,14 @@ __device__ __forceinline__ unsigned sub_h2(unsigned x, unsigned y) {
 //   bytes   0..127: key entry (KB 4: byte of two codes -> two float16 values,
 //                   32 copies of 4 bytes; KB 2: byte of four codes -> four
 //                   float16 values, 16 copies of 8 bytes; KB 3: 6 bits of two
-//                   codes, entries 0..63 only, 32 copies of 4 bytes);
+//                   codes, entries 0..63 only, 32 copies of 4 bytes; KB 1: byte
+//                   of eight codes -> eight float16 values, 8 copies of 16 bytes);
 //   bytes 128..255: sign entry (byte of 8 sign bits -> eight float16 +-1,
 //                   8 copies of 16 bytes).
 constexpr int kLutEntry = 256;
 template <int KB>
 struct KeyLut {
-  static constexpr int copy_bytes = KB == 2 ? 8 : 4;
+  static constexpr int copy_bytes = KB == 1 ? 16 : KB == 2 ? 8 : 4;
   static constexpr int copies = 128 / copy_bytes;
 };
 constexpr int kSignBase = 128, kSignCopies = 8;
@@ -182,7 +183,13 @@ __device__ __forceinline__ unsigned lut_addr(unsigned x, unsigned off) {
 template <int KB>
 __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const unsigned char* lut, unsigned koff) {
   u32x4 r;
-  if constexpr (KB == 4) {
+  if constexpr (KB == 1) {
+    // byte s of the block's 32 one-bit codes = dims 8s .. 8s+7: one 16-byte entry
+    return as_h8(*reinterpret_cast<const u32x4*>(lut + ((s == 0)   ? lut_addr<0>(kc[0], koff)
+                                                         : (s == 1) ? lut_addr<1>(kc[0], koff)
+                                                         : (s == 2) ? lut_addr<2>(kc[0], koff)
+                                                                    : lut_addr<3>(kc[0], koff))));
+  } else if constexpr (KB == 4) {
     const unsigned x = kc[s];  // 8 nibbles
     r[0] = *reinterpret_cast<const unsigned*>(lut + lut_addr<0>(x, koff));
     r[1] = *reinterpret_cast<const unsigned*>(lut + lut_addr<1>(x, koff));
@@ -310,6 +317,8 @@ __device__ __forceinline__ void load_chunk(Chunk<KB, VB>& c, const unsigned char
     } else if constexpr (KB == 3) {
       const u32x3a v = *reinterpret_cast<const u32x3a*>(kp);
       c.kc[t][0] = v[0]; c.kc[t][1] = v[1]; c.kc[t][2] = v[2];
+    } else if constexpr (KB == 1) {
+      c.kc[t][0] = *reinterpret_cast<const unsigned*>(kp);
     } else {
       const u32x2a v = *reinterpret_cast<const u32x2a*>(kp);
       c.kc[t][0] = v[0]; c.kc[t][1] = v[1];
@@ -500,7 +509,11 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     // lane tid fills entry tid of both tables, all copies (16-byte stores)
     const int e = tid;
     u32x4 kv = {0u, 0u, 0u, 0u};
-    if constexpr (KB == 4) {
+    if constexpr (KB == 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        kv[q] = cent_h[(e >> (2 * q)) & 1] | (static_cast<unsigned>(cent_h[(e >> (2 * q + 1)) & 1]) << 16);
+    } else if constexpr (KB == 4) {
       const unsigned v = cent_h[e & 15] | (static_cast<unsigned>(cent_h[e >> 4]) << 16);
       kv = u32x4{v, v, v, v};
     } else if constexpr (KB == 2) {
@@ -740,6 +753,7 @@ void* pick_vb(int vb) {
 template <int NREP>
 void* pick_kb(int kb, int vb) {
   switch (kb) {
+    case 1: return pick_vb<NREP, 1>(vb);
     case 2: return pick_vb<NREP, 2>(vb);
     case 3: return pick_vb<NREP, 3>(vb);
     case 4: return pick_vb<NREP, 4>(vb);

@@ -254,6 +254,7 @@ void* pick_v(int vb) {
 template <bool BF>
 void* pick_kv(int kb, int vb) {
   switch (kb) {
+    case 1: return pick_v<1, BF>(vb);
     case 2: return pick_v<2, BF>(vb);
     case 3: return pick_v<3, BF>(vb);
     case 4: return pick_v<4, BF>(vb);

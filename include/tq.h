@@ -49,7 +49,7 @@
  *     a block id of a used page is outside [0, num_blocks).  Off by default: it
  *     allocates host memory and synchronises, which the hot path never does.
  *   - Supported: head_dim = 128, block_size = 16, v_group = 32,
- *     k_bits in {2,3,4}, v_bits in {2,3,4}, query heads per KV head in {1,2,4,8}.
+ *     k_bits in {1,2,3,4}, v_bits in {2,3,4}, query heads per KV head in {1,2,4,8}.
  *
  * Store format (one pool per layer; exported by tq_store_layout)
  *   pool = uint8[num_blocks][n_kv_heads][block_bytes], 16 tokens per block,
@@ -121,7 +121,7 @@ int tq_abi_version(void);
  *   mse         host out, nullable: expected squared error per coordinate
  * Iterates Lloyd's conditions from the quantile midpoints to max|delta c| < 1e-14,
  * at most 200,000 times; the 8-bit N(0,1) codebook does not reach that tolerance
- * within the cap and returns TQ_ERR_NOT_CONVERGED (the kernels use 2..4 bits). */
+ * within the cap and returns TQ_ERR_NOT_CONVERGED (the kernels use 1..4 bits). */
 tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids,
                             double* boundaries, double* mse);
 
@@ -174,7 +174,7 @@ typedef enum { TQ_VAL_GROUP = 0, TQ_VAL_MSE = 1 } tq_value_mode;
 typedef struct {
   int head_dim;             /* d; must be 128                                   */
   int n_kv_heads;           /* KV heads of the layer, >= 1                      */
-  int k_bits;               /* key codebook bits, 2..4 (QJL adds 1 bit/coord)   */
+  int k_bits;               /* key codebook bits, 1..4 (QJL adds 1 bit/coord)   */
   int v_bits;               /* value code bits, 2..4                            */
   int v_group;              /* value group width; must be 32                    */
   int block_size;           /* tokens per page; must be 16                      */

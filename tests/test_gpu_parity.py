@@ -221,7 +221,7 @@ def test_compress_tiny_fp32():
     _check_compress(gpu, res, st, layout, 1, slots, V, 2, 3)
 
 
-@pytest.mark.parametrize("kb,vb", [(2, 2), (3, 2), (3, 3), (4, 3), (4, 4), (2, 4)])
+@pytest.mark.parametrize("kb,vb", [(2, 2), (3, 2), (3, 3), (4, 3), (4, 4), (2, 4), (1, 3), (1, 2)])
 def test_compress_bits_ragged_slots(kb, vb):
     """8 heads, bf16 with outlier channels, shuffled slots with skipped (-1) tokens."""
     torch = _torch()
@@ -330,7 +330,7 @@ def test_decompress_mse_values(kb, vb, out_dtype):
     layer.close()
 
 
-@pytest.mark.parametrize("kb,vb,n,offset", [(4, 4, 2000, 37), (3, 2, 1000, 0), (2, 3, 777, 16)])
+@pytest.mark.parametrize("kb,vb,n,offset", [(4, 4, 2000, 37), (3, 2, 1000, 0), (2, 3, 777, 16), (1, 4, 500, 5)])
 def test_compress_page_runs(kb, vb, n, offset):
     """bf16 runs of consecutive slots: whole aligned pages (stored whole), a ragged
     last tile, and runs that start mid-page (every tile scattered token by token)."""
@@ -474,7 +474,7 @@ def test_decode_long_context_full():
     _decode_case(torch, 1, 32, 8, [131072], 3, 2, 204, out_dtypes=("f32",))
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 4), (4, 3), (3, 3), (3, 2), (2, 3), (2, 2)])
+@pytest.mark.parametrize("kb,vb", [(4, 4), (4, 3), (3, 3), (3, 2), (2, 3), (2, 2), (1, 3), (1, 4)])
 def test_decode_ragged_bits(kb, vb):
     """Ragged lengths with tails, a zero-length row, every supported bit pair."""
     torch = _torch()
@@ -643,12 +643,29 @@ def test_end_to_end_gpu_compress_then_decode():
     _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, 3, 3, 260, label="K3/V3")
 
 
+def test_end_to_end_one_bit_keys():
+    """1-bit key codebook (+-0.7979) with QJL signs, 2-bit values: GPU compress -> GPU
+    decode against the oracle (the matrix-core compressor and the 1-bit decode table)."""
+    torch = _torch()
+    say("end to end K1/V2")
+    B, Hq, Hkv, T = 3, 32, 8, 600
+    lens = np.array([T, 333, 1], np.int32)
+    maxb = (T + 15) // 16
+    table = synth.block_table(262, B, maxb, "random")
+    K, V = synth.kv_host(162, B * T, Hkv, outliers=4)
+    pos = np.tile(np.arange(T), B)
+    seq = np.repeat(np.arange(B), T)
+    slots = table[seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, 1, 2, 262, label="K1/V2")
+
+
 KEY_MODE_NAMES = {tq.KEY_QJL: "qjl", tq.KEY_MSE: "mse", tq.KEY_MSE_NC: "mse_nc"}
 
 
 @pytest.mark.parametrize("key_mode,kb,vb,n,dtype", [
     (tq.KEY_MSE, 4, 4, 700, "bf16"), (tq.KEY_MSE_NC, 3, 2, 700, "bf16"),
-    (tq.KEY_MSE_NC, 2, 3, 1024, "f32"), (tq.KEY_MSE, 3, 3, 40, "bf16")])
+    (tq.KEY_MSE_NC, 2, 3, 1024, "f32"), (tq.KEY_MSE, 3, 3, 40, "bf16"), (tq.KEY_MSE_NC, 1, 3, 500, "bf16"),
+    (tq.KEY_MSE, 1, 2, 100, "f32")])
 def test_compress_key_modes(key_mode, kb, vb, n, dtype):
     """Keys without the residual projection (plain and norm-corrected magnitude):
     the matrix-core compressor (bf16: whole pages and a ragged last tile) and the
@@ -723,7 +740,7 @@ def test_end_to_end_hadamard_rotation():
 
 @pytest.mark.parametrize("kb,vb,key_mode,rotation,out_dtype", [
     (4, 4, tq.KEY_QJL, tq.ROT_HAAR, "f32"), (3, 2, tq.KEY_MSE_NC, tq.ROT_HADAMARD, "f32"),
-    (2, 3, tq.KEY_QJL, tq.ROT_HAAR, "bf16")])
+    (2, 3, tq.KEY_QJL, tq.ROT_HAAR, "bf16"), (1, 3, tq.KEY_QJL, tq.ROT_HADAMARD, "f32")])
 def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype):
     """Keys and values reconstructed from a GPU-written store (shuffled slots, some
     negative: zero rows) against the oracle's reconstruction of the same bytes."""
@@ -936,7 +953,7 @@ def test_random_layer_configurations(case):
     Hkv = int(rng.choice([1, 2, 4, 8]))
     rep = int(rng.choice([1, 2, 4, 8]))
     Hq = Hkv * rep
-    kb, vb = int(rng.choice([2, 3, 4])), int(rng.choice([2, 3, 4]))
+    kb, vb = int(rng.choice([1, 2, 3, 4])), int(rng.choice([2, 3, 4]))
     key_mode = int(rng.choice([tq.KEY_QJL, tq.KEY_MSE, tq.KEY_MSE_NC]))
     rotation = int(rng.choice([tq.ROT_HAAR, tq.ROT_HADAMARD]))
     B = int(rng.integers(1, 5))

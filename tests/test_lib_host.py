@@ -50,7 +50,7 @@ def test_codebook_matches_oracle(bits, dist, name):
     assert np.array_equal(c.astype(np.float16), oc.astype(np.float16))
 
 
-@pytest.mark.parametrize("layer,heads,kb", [(0, 1, 2), (3, 8, 4), (17, 2, 3)])
+@pytest.mark.parametrize("layer,heads,kb", [(0, 1, 2), (3, 8, 4), (17, 2, 3), (5, 2, 1)])
 def test_layer_state_matches_oracle(layer, heads, kb):
     cfg = tq.config(heads, kb, 3, seed=205, layer=layer)
     R, S, c, b = tq.layer_state_host(cfg)
@@ -63,7 +63,7 @@ def test_layer_state_matches_oracle(layer, heads, kb):
     assert np.array_equal(b.astype(np.float64), st.boundaries)
 
 
-@pytest.mark.parametrize("kb,vb", [(2, 2), (2, 3), (3, 2), (3, 3), (4, 3), (4, 4)])
+@pytest.mark.parametrize("kb,vb", [(1, 2), (1, 3), (2, 2), (2, 3), (3, 2), (3, 3), (4, 3), (4, 4)])
 def test_store_layout_matches_oracle(kb, vb):
     bb, offs = tq.store_layout(tq.config(8, kb, vb))
     lay = layout.StoreLayout(128, kb, vb, 32)
@@ -84,7 +84,7 @@ def _status_of(fn):
 def test_config_errors():
     bad = [
         (dict(head_dim=64), tq.ERR_UNSUPPORTED), (dict(k_bits=5), tq.ERR_UNSUPPORTED),
-        (dict(k_bits=1), tq.ERR_UNSUPPORTED), (dict(v_bits=1), tq.ERR_UNSUPPORTED),
+        (dict(k_bits=0), tq.ERR_UNSUPPORTED), (dict(v_bits=1), tq.ERR_UNSUPPORTED),
         (dict(v_group=16), tq.ERR_UNSUPPORTED), (dict(block_size=32), tq.ERR_UNSUPPORTED),
         (dict(n_kv_heads=0), tq.ERR_INVALID_ARGUMENT), (dict(layer=-1), tq.ERR_INVALID_ARGUMENT),
         (dict(dist=7), tq.ERR_INVALID_ARGUMENT), (dict(key_mode=3), tq.ERR_INVALID_ARGUMENT),
