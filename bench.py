@@ -1,18 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the compressed-KV hot path on one MI355X.
 
-Headline workload: a Llama-3-8B-shaped decode layer -- batch 16, 32 query / 8
-KV heads, head_dim 128, context 4096, bf16 N(0,1) K/V with 4 outlier channels
-per head scaled x10, keys 4-bit codebook + 1-bit QJL, values 4-bit groups of
-32, 16-token pages.  One step = decode attention of every sequence's query over
-its whole compressed context (query rotation, split-K mainloop, combine and
-un-rotation: all kernels of the decode path).  Appending the newest token of
-each sequence to the store is timed on its own and reported beside it.  The store is rotated over several copies so the timed reads come
-from HBM and not from the 256 MB last-level cache.
+One step of the headline workload is the decode attention of a whole serving
+batch: 32 layers (4 protected bf16 layers, 28 compressed with seeded per-layer
+key/value bit widths from {(4,4), (4,3), (3,3), (3,2)}), batch 64 with context
+lengths drawn uniformly from 512..32768, 32 query / 8 KV heads, head_dim 128,
+16-token pages and random block tables, bf16 N(0,1) K/V with 4 outlier channels
+per head scaled x10 (keys: k_bits codebook + 1-bit QJL; values: v_bits groups of
+32).  It is the largest of the five workloads that fit one GPU.  The other four
+are measured in the same run and reported under "configs", each with its own
+roofline fraction: the tiny fp32 parity case (1 head, 1024 tokens), the
+Llama-3-8B-shaped decode layer (batch 16, context 4096, K4/V4), the fused
+compress of 1,048,576 tokens x 8 heads (K2 + QJL / V3) and the long-context
+decode (batch 1, context 131072, K3/V2).  Decode stores that fit the 256 MB
+last-level cache are rotated over several copies so that reads come from HBM.
 
-Also reported: fused compress throughput on 1,048,576 tokens x 8 heads (keys
-2-bit + QJL, values 3-bit), and the float64 CPU oracle timed on a bounded
-sample of the headline workload on this host.
+The float64 CPU oracle is timed on bounded samples of the same workloads on this
+host (cpu_baseline and configs.*.cpu_baseline).
 
 Prints one JSON line.
 """
@@ -29,19 +33,20 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20, help="timed steps of the headline (32-layer) workload")
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--pools", type=int, default=6, help="store copies rotated to defeat the cache")
     ap.add_argument("--compress-iters", type=int, default=5)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="size of one plain device copy run before the workloads (counter calibration)")
     ap.add_argument("--all-configs", action="store_true",
-                    help="also time the tiny, long-context and ragged mixed-bit serving workloads")
+                    help="also time the compress variants (key modes, Hadamard rotation), decompress and MSE values")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarise a rocprofv3 --kernel-trace file per kernel and grid and exit")
     return ap.parse_args()
 
 
@@ -50,11 +55,14 @@ def log(*a):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_llama3_8b_layer_and_compress_1m.txt")
-# kernels whose HBM traffic is taken from counters, with the sources that define them
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_by_workload.txt")
+# kernels whose HBM traffic is taken from counters: (kernel, workload tag) -> (grid in
+# workgroups x*y*z, or None for any grid; the sources that define the kernel)
 TRAFFIC_KERNELS = {
-    "splitk_mfma_kernel<4, 4, 4>": ["decode_mainloop.hip"],
-    "compress_mfma_kernel<2, 3, 3, false, true>": ["compress_mfma.hip"],
+    ("splitk_mfma_kernel<4,4,4>", "serving"): (8 * 8 * 64, ["decode_mainloop.hip"]),
+    ("splitk_mfma_kernel<4,4,4>", "layer"): (4 * 8 * 16, ["decode_mainloop.hip"]),
+    ("splitk_mfma_kernel<4,3,2>", "long"): (64 * 8 * 1, ["decode_mainloop.hip"]),
+    ("compress_mfma_kernel<2,3,3,false,true>", "compress"): (None, ["compress_mfma.hip"]),
 }
 
 
@@ -97,61 +105,199 @@ def copy_bandwidth(torch, mib=1024, reps=10):
     return 2.0 * mib * (1 << 20) / (ms / 1e3) / 1e9
 
 
+def _norm(name):
+    """Kernel name without spaces, namespaces, argument list or return type."""
+    n = name.replace(" ", "")
+    if n.startswith("void"):
+        n = n[4:]
+    n = n.replace("tq::(anonymousnamespace)::", "").replace("tq::", "")
+    if "(" in n:
+        n = n[:n.index("(")]
+    return n
+
+
 def traffic_summary(fetch_csv, write_csv, mib):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the traffic kernels, scaled by
-    what the same counters read for the copy probe (known bytes)."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the traffic kernels, grouped by
+    kernel and grid, scaled by what the same counters read for the copy probe."""
     import csv
     import statistics
 
     def per_kernel(path, counter):
-        vals = {}
+        vals, grid = {}, {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+            grid[key] = int(r.get("Grid_Size", 0) or 0) // max(int(r.get("Workgroup_Size", 1) or 1), 1)
         out = {}
-        for (name, _), v in vals.items():
-            out.setdefault(name, []).append(v * 1024.0)
+        for (name, d), v in vals.items():
+            out.setdefault((_norm(name), grid[(name, d)]), []).append(v * 1024.0)
         return out
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    probe = [n for n in fetch if "neg" in n and "elementwise" in n]
+    probe = [k for k in fetch if "neg" in k[0] and "elementwise" in k[0]]
     if not probe:
         raise SystemExit("copy probe kernel not found in " + fetch_csv)
     nbytes = mib * (1 << 20)
     f_scale = nbytes / statistics.median(fetch[probe[0]])
     w_scale = nbytes / statistics.median(write[probe[0]])
     lines = ["copy_probe bytes=%d fetch_factor=%.4f write_factor=%.4f" % (nbytes, f_scale, w_scale)]
-    for short, files in TRAFFIC_KERNELS.items():
-        names = [n for n in fetch if short.replace(" ", "") in n.replace(" ", "")]
-        if not names:
+    for (kern, tag), (wgs, files) in TRAFFIC_KERNELS.items():
+        keys = [k for k in fetch if k[0] == kern and (wgs is None or k[1] == wgs)]
+        if not keys:
             continue
-        fb = statistics.median(fetch[names[0]]) * f_scale
-        wb = statistics.median(write[names[0]]) * w_scale
-        lines.append("kernel=%s sources_sha=%s fetch_bytes=%d write_bytes=%d traffic_bytes=%d dispatches=%d"
-                     % (short.replace(" ", ""), sources_sha(files), fb, wb, fb + wb, len(fetch[names[0]])))
+        k = keys[0]
+        fb = statistics.median(fetch[k]) * f_scale
+        wb = statistics.median(write[k]) * w_scale
+        lines.append("kernel=%s workload=%s grid_wgs=%d sources_sha=%s fetch_bytes=%d write_bytes=%d "
+                     "traffic_bytes=%d dispatches=%d" % (kern, tag, k[1], sources_sha(files), fb, wb, fb + wb,
+                                                          len(fetch[k])))
     return lines
 
 
-def traffic_for(kernel):
+def trace_summary(trace_csv):
+    """Per kernel and grid: dispatches, mean, median and minimum duration (us) from a
+    rocprofv3 --kernel-trace CSV."""
+    import csv
+    import statistics
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        name = _norm(r["Kernel_Name"])
+        if not any(x in name for x in ("splitk", "prologue", "combine", "compress", "decompress", "store_bypass")):
+            continue
+        grid = tuple(int(r["Grid_Size_" + a]) // max(int(r["Workgroup_Size_" + a]), 1) for a in "XYZ")
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, grid, int(r["Workgroup_Size_X"])), []).append(dur)
+    lines = ["| kernel | grid (WGs) | WG size | dispatches | mean (us) | median (us) | min (us) |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("| `%s` | %dx%dx%d | %d | %d | %.2f | %.2f | %.2f |" % (
+            name, grid[0], grid[1], grid[2], wg, len(d), statistics.mean(d), statistics.median(d), min(d)))
+    return lines
+
+
+def traffic_for(kernel, tag):
     """HBM bytes per launch from the committed counter summary, or None when the
     kernel's sources changed since the counters were taken."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
     except OSError:
         return None
-    key = kernel.replace(" ", "")
     for ln in lines:
         f = dict(x.split("=", 1) for x in ln.split() if "=" in x)
-        if f.get("kernel") == key:
-            if f.get("sources_sha") != sources_sha(TRAFFIC_KERNELS[kernel]):
+        if f.get("kernel") == kernel and f.get("workload") == tag:
+            if f.get("sources_sha") != sources_sha(TRAFFIC_KERNELS[(kernel, tag)][1]):
                 return None
             return int(f["traffic_bytes"])
     return None
 
 
-def decode_workload(torch, tq, synth, args):
+def _events_avg_us(torch, tq, kernel_id, fn, n):
+    """Average duration (us) of the library's `kernel_id` launches over n calls of fn,
+    from HIP events the library records around each launch on its own stream."""
+    tq.profile_reset()
+    tq.profile_enable(1 << kernel_id)
+    _time_steps(torch, fn, n)
+    ms, launches = tq.profile_read(kernel_id)
+    tq.profile_enable(0)
+    return ms / max(launches, 1) * 1e3, launches
+
+
+def _splitk_bytes(lens, Hkv, Hq, rec):
+    """Algorithmic bytes of one split-K launch: the KV records of every live token,
+    the used block-table entries, the lengths and the rotated query / projection (f32)."""
+    import numpy as np
+    lens = np.asarray(lens, dtype=np.int64)
+    return int(lens.sum()) * Hkv * rec + int(((lens + 15) // 16).sum()) * 4 + len(lens) * 4 + \
+        len(lens) * Hq * 2 * 128 * 4
+
+
+def _roofline(nbytes, avg_us, kernel, launches, traffic=None):
+    gbs = nbytes / (avg_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "avg_us": round(avg_us, 3), "launches": launches, "bytes_per_launch": int(nbytes)}
+
+
+def serving_workload(torch, tq, synth, args):
+    """Ragged mixed-bit serving batch: 32 layers, B = 64, lengths U{512..32768}.  One
+    step = decode attention of all 64 sequences through all 32 layers."""
+    import numpy as np
+    W, sd = synth.WORKLOADS[5], synth.seeds(5)
+    B, Hq, Hkv = W["B"], W["Hq"], W["Hkv"]
+    lens = synth.ragged_lengths(sd["lens"], B, W["min_len"], W["max_len"])
+    alloc = synth.mixed_bit_allocation(sd["alloc"], W["layers"])
+    table, _ = _compact_table(sd["table"], lens)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(lens).cuda()
+    maxlen = int(lens.max())
+    q = torch.from_numpy(synth.queries_host(sd["data"], B, Hq)).to("cuda", torch.bfloat16)
+    layers, pools, outs, wss = [], [], [], []
+    for li, kv in enumerate(alloc):
+        kb, vb = kv if kv else (4, 4)
+        lay = tq.Layer(tq.config(Hkv, kb, vb, seed=sd["state"], layer=li, bypass=kv is None))
+        layers.append(lay)
+        pools.append(_fill(torch, tq, synth, lay, table, lens, Hkv, sd["data"] * 100 + li, W["outliers"]))
+        outs.append(torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda"))
+        wss.append(tq.new_workspace(lay, B, Hq, maxlen))
+
+    def run_layer(li):
+        tq.decode_attn(layers[li], q, pools[li], bt, sl, maxlen, out=outs[li], workspace=wss[li])
+
+    def step(i):
+        for li in range(len(layers)):
+            run_layer(li)
+
+    for i in range(args.warmup):
+        step(i)
+    ms = _time_steps(torch, step, args.steps)
+    # split-K launches of each layer kind, timed with events in a second pass
+    kinds = {}
+    for li, kv in enumerate(alloc):
+        kinds.setdefault(kv, []).append(li)
+    n_ev = max(2, min(args.steps, 10))
+    per_kind = {}
+    for kv, lis in kinds.items():
+        tot, cnt = 0.0, 0
+        for li in lis:
+            us, n = _events_avg_us(torch, tq, tq.K_SPLITK, lambda i, li=li: run_layer(li), n_ev)
+            tot += us * n
+            cnt += n
+        rec = _record_bytes(*(kv if kv else (4, 4)), bypass=kv is None)
+        nbytes = _splitk_bytes(lens, Hkv, Hq, rec) if kv else int(lens.sum()) * Hkv * rec + \
+            int(((lens + 15) // 16).sum()) * 4 + B * 4 + B * Hq * 128 * 2
+        name = "bypass" if kv is None else "K%d/V%d" % kv
+        kern = "splitk_bypass_kernel<4,true>" if kv is None else "splitk_mfma_kernel<4,%d,%d>" % kv
+        per_kind[name] = dict(_roofline(nbytes, tot / cnt, kern, cnt), layers=len(lis))
+    total_bytes = sum(int(lens.sum()) * Hkv * _record_bytes(*(kv if kv else (4, 4)), bypass=kv is None)
+                      for kv in alloc)
+    dominant = max(per_kind, key=lambda k: per_kind[k]["avg_us"] * per_kind[k]["layers"])
+    roof = dict(per_kind[dominant])
+    roof["traffic"] = traffic_for(roof["kernel"], "serving")
+    res = {
+        "ms_per_step": ms, "value": B / (ms / 1e3),
+        "kv_tok_s": float(lens.sum()) * len(layers) / (ms / 1e3),
+        "step_hbm_gbs": total_bytes / (ms / 1e3) / 1e9,
+        "record_bytes_per_step": total_bytes,
+        "roofline": roof, "splitk_by_layer_kind": per_kind,
+        "config": {"workload": W["name"], "layers": W["layers"], "bypass_layers": [i for i, kv in enumerate(alloc)
+                                                                                    if kv is None],
+                   "layer_bits": [list(kv) if kv else None for kv in alloc], "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": 128, "seq_len_min": int(lens.min()), "seq_len_max": maxlen,
+                   "tokens": int(lens.sum()), "qjl_bits": 1, "v_group": 32, "page": 16,
+                   "outlier_channels": W["outliers"], "table": "random"},
+    }
+    ctx = {"lens": lens, "table": table, "alloc": alloc, "q": q, "W": W, "sd": sd}
+    for lay in layers:
+        lay.close()
+    del pools, outs, wss
+    torch.cuda.empty_cache()
+    return res, ctx
+
+
+def layer_workload(torch, tq, synth, args):
+    """Llama-3-8B-shaped decode layer: B = 16, 32/8 heads, ctx 4096, K4/V4."""
     W = synth.WORKLOADS[2]
     sd = synth.seeds(2)
     B, Hq, Hkv, T = W["B"], W["Hq"], W["Hkv"], W["ctx"]
@@ -178,55 +324,82 @@ def decode_workload(torch, tq, synth, args):
     def step(i):
         tq.decode_attn(layer, q, pools[i % len(pools)], bt, sl, T, out=out, workspace=ws)
 
-    def timed(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    for i in range(args.warmup):
-        step(i)
-    # headline: decode attention steps back to back, nothing else on the stream
-    ms = timed(step, args.steps)
-    # the same steps again with HIP events around each split-K launch (on the
-    # library's stream) for the kernel's own average duration
-    tq.profile_reset()
-    tq.profile_enable(1 << tq.K_SPLITK)
-    timed(step, args.steps)
-    sk_ms, sk_n = tq.profile_read(tq.K_SPLITK)
-    tq.profile_enable(0)
-    # appending the newest token of every sequence (compress into the store), timed on its own
-    append_ms = timed(lambda i: tq.compress_kv(layer, k_new, v_new, slot_new, pools[i % len(pools)]), args.steps)
-    rec = W["k_bits"] * 16 + 16 + 4 + W["v_bits"] * 16 + 16
-    kv_bytes = B * T * Hkv * rec
-    # algorithmic bytes of one split-K launch: the KV records, the block-table
-    # entries, the sequence lengths and the rotated query/projection (f32) once
-    splitk_bytes = kv_bytes + B * maxb * 4 + B * 4 + B * Hq * 2 * 128 * 4
-    # whole decode step: + q in (bf16) + out (bf16)
-    step_bytes = splitk_bytes + B * Hq * 128 * 2 * 2
-    sk_avg_s = sk_ms / max(sk_n, 1) / 1e3
-    achieved = splitk_bytes / sk_avg_s / 1e9
-    res = {
-        "ms_per_step": ms,
-        "value": B / (ms / 1e3),
-        "kv_tok_s": B * T / (ms / 1e3),
-        "step_hbm_gbs": step_bytes / (ms / 1e3) / 1e9,
-        "append_us": round(append_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for("splitk_mfma_kernel<4, 4, 4>"),
-                     "kernel": "splitk_mfma_kernel<4,4,4>", "avg_us": round(sk_avg_s * 1e6, 3),
-                     "launches": sk_n, "bytes_per_launch": splitk_bytes},
-        "config": {"workload": W["name"], "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
-                   "context": T, "k_bits": kb, "qjl_bits": 1, "v_bits": vb, "v_group": 32, "page": 16,
-                   "outlier_channels": W["outliers"], "store_copies_rotated": len(pools)},
-    }
-    ctx = {"k": k, "v": v, "q": q, "table": table, "layer": layer, "W": W, "sd": sd}
+    _time_steps(torch, step, 50)
+    ms = _time_steps(torch, step, 200)
+    sk_us, sk_n = _events_avg_us(torch, tq, tq.K_SPLITK, step, 200)
+    append_ms = _time_steps(torch, lambda i: tq.compress_kv(layer, k_new, v_new, slot_new, pools[i % len(pools)]),
+                            200)
+    rec = _record_bytes(kb, vb)
+    splitk_bytes = _splitk_bytes([T] * B, Hkv, Hq, rec)
+    step_bytes = splitk_bytes + B * Hq * 128 * 2 * 2  # + q in, out (bf16)
+    roof = _roofline(splitk_bytes, sk_us, "splitk_mfma_kernel<4,4,4>", sk_n, traffic_for("splitk_mfma_kernel<4,4,4>",
+                                                                                           "layer"))
+    res = {"workload": W["name"], "decode_us": round(ms * 1e3, 3), "decode_tok_s": round(B / (ms / 1e3), 1),
+           "kv_tok_s": round(B * T / (ms / 1e3), 1), "step_hbm_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
+           "step_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "roofline": roof,
+           "append_us": round(append_ms * 1e3, 2), "steps": 200, "warmup": 50,
+           "config": {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "context": T, "k_bits": kb,
+                      "qjl_bits": 1, "v_bits": vb, "v_group": 32, "page": 16, "outlier_channels": W["outliers"],
+                      "store_copies_rotated": len(pools)}}
+    ctx = {"k": k, "v": v, "q": q, "table": table, "W": W, "sd": sd}
+    layer.close()
+    del pools, pool0
     return res, ctx
+
+
+def long_context_workload(torch, tq, synth, args):
+    """B = 1, ctx 131072, K3/V2, seeded random block table; three store copies rotated."""
+    W, sd = synth.WORKLOADS[4], synth.seeds(4)
+    T, Hkv, Hq = W["ctx"], W["Hkv"], W["Hq"]
+    layer = tq.Layer(tq.config(Hkv, W["k_bits"], W["v_bits"], seed=sd["state"]))
+    table = synth.block_table(sd["table"], 1, T // 16, "random")
+    pool0 = _fill(torch, tq, synth, layer, table, [T], Hkv, sd["data"], W["outliers"])
+    pools = [pool0] + [pool0.clone() for _ in range(2)]
+    q = torch.from_numpy(synth.queries_host(sd["data"], 1, Hq)).to("cuda", torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    ws = tq.new_workspace(layer, 1, Hq, T)
+    out = torch.empty((1, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    step = lambda i: tq.decode_attn(layer, q, pools[i % 3], bt, sl, T, out=out, workspace=ws)
+    _time_steps(torch, step, 10)
+    ms = _time_steps(torch, step, 60)
+    sk_us, sk_n = _events_avg_us(torch, tq, tq.K_SPLITK, step, 60)
+    nbytes = _splitk_bytes([T], Hkv, Hq, _record_bytes(W["k_bits"], W["v_bits"]))
+    layer.close()
+    del pools, pool0
+    return {"workload": W["name"], "decode_us": round(ms * 1e3, 2), "decode_tok_s": round(1 / (ms / 1e3), 1),
+            "kv_tok_s": round(T / (ms / 1e3), 1), "step_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": _roofline(nbytes, sk_us, "splitk_mfma_kernel<4,3,2>", sk_n,
+                                  traffic_for("splitk_mfma_kernel<4,3,2>", "long")),
+            "steps": 60, "warmup": 10,
+            "config": {"batch": 1, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "context": T,
+                       "k_bits": W["k_bits"], "qjl_bits": 1, "v_bits": W["v_bits"], "v_group": 32, "page": 16,
+                       "outlier_channels": W["outliers"], "table": "random", "store_copies_rotated": 3}}
+
+
+def tiny_workload(torch, tq, synth, args):
+    """1 KV head, 1024 fp32 tokens, K2 + QJL / V3: launch-latency bound (latency reported)."""
+    W, sd = synth.WORKLOADS[1], synth.seeds(1)
+    layer = tq.Layer(tq.config(W["Hkv"], W["k_bits"], W["v_bits"], seed=sd["state"]))
+    table = synth.block_table(sd["table"], 1, W["ctx"] // 16, "identity")
+    pool = _fill(torch, tq, synth, layer, table, [W["ctx"]], W["Hkv"], sd["data"], 0, dtype="f32")
+    q = torch.from_numpy(synth.queries_host(sd["data"], 1, W["Hq"], dtype="f32")).cuda()
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.full((1,), W["ctx"], dtype=torch.int32, device="cuda")
+    ws = tq.new_workspace(layer, 1, W["Hq"], W["ctx"])
+    out = torch.empty((1, W["Hq"], 128), dtype=torch.float32, device="cuda")
+    step = lambda i: tq.decode_attn(layer, q, pool, bt, sl, W["ctx"], out=out, workspace=ws)
+    _time_steps(torch, step, 20)
+    ms = _time_steps(torch, step, 200)
+    sk_us, sk_n = _events_avg_us(torch, tq, tq.K_SPLITK, step, 200)
+    nbytes = _splitk_bytes([W["ctx"]], W["Hkv"], W["Hq"], _record_bytes(W["k_bits"], W["v_bits"]))
+    layer.close()
+    return {"workload": W["name"], "decode_us": round(ms * 1e3, 2), "decode_tok_s": round(1 / (ms / 1e3), 1),
+            "roofline": _roofline(nbytes, sk_us, "splitk_mfma_kernel<1,2,3>", sk_n),
+            "note": "0.12 MB per launch: launch-latency bound, the HBM fraction is not meaningful",
+            "steps": 200, "warmup": 20,
+            "config": {"batch": 1, "q_heads": W["Hq"], "kv_heads": W["Hkv"], "head_dim": 128, "context": W["ctx"],
+                       "dtype": "f32", "k_bits": W["k_bits"], "qjl_bits": 1, "v_bits": W["v_bits"], "v_group": 32}}
 
 
 def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
@@ -265,7 +438,7 @@ def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
             "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": traffic_for("compress_mfma_kernel<2, 3, 3, false, true>"),
+                         "traffic": traffic_for("compress_mfma_kernel<2,3,3,false,true>", "compress"),
                          "kernel": "compress_mfma_kernel<2,3,3,false,true>",
                          "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
 
@@ -372,107 +545,42 @@ def mse_values_workload(torch, tq, synth, args):
             "decompress_frac": round(nbytes / (ms_d / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
 
 
-def extra_workloads(torch, tq, synth, args):
-    """The tiny, long-context and serving workloads, each as decode-step figures."""
-    import numpy as np
-    res = {}
-    # tiny: 1 head, 1024 tokens, fp32 -- launch-latency bound
-    W, sd = synth.WORKLOADS[1], synth.seeds(1)
-    layer = tq.Layer(tq.config(W["Hkv"], W["k_bits"], W["v_bits"], seed=sd["state"]))
-    table = synth.block_table(sd["table"], 1, W["ctx"] // 16, "identity")
-    pool = _fill(torch, tq, synth, layer, table, [W["ctx"]], W["Hkv"], sd["data"], 0, dtype="f32")
-    q = torch.from_numpy(synth.queries_host(sd["data"], 1, W["Hq"], dtype="f32")).cuda()
-    bt = torch.from_numpy(table).cuda()
-    sl = torch.full((1,), W["ctx"], dtype=torch.int32, device="cuda")
-    ws = tq.new_workspace(layer, 1, W["Hq"], W["ctx"])
-    out = torch.empty((1, W["Hq"], 128), dtype=torch.float32, device="cuda")
-    step = lambda i: tq.decode_attn(layer, q, pool, bt, sl, W["ctx"], out=out, workspace=ws)
-    _time_steps(torch, step, 20)
-    ms = _time_steps(torch, step, 200)
-    res[W["name"]] = {"decode_us": round(ms * 1e3, 2)}
-    layer.close()
-    # long context: B = 1, ctx 131072, K3/V2, random table; three store copies rotated
-    W, sd = synth.WORKLOADS[4], synth.seeds(4)
-    T, Hkv, Hq = W["ctx"], W["Hkv"], W["Hq"]
-    layer = tq.Layer(tq.config(Hkv, W["k_bits"], W["v_bits"], seed=sd["state"]))
-    table = synth.block_table(sd["table"], 1, T // 16, "random")
-    pool0 = _fill(torch, tq, synth, layer, table, [T], Hkv, sd["data"], W["outliers"])
-    pools = [pool0] + [pool0.clone() for _ in range(2)]
-    q = torch.from_numpy(synth.queries_host(sd["data"], 1, Hq)).to("cuda", torch.bfloat16)
-    bt = torch.from_numpy(table).cuda()
-    sl = torch.full((1,), T, dtype=torch.int32, device="cuda")
-    ws = tq.new_workspace(layer, 1, Hq, T)
-    out = torch.empty((1, Hq, 128), dtype=torch.bfloat16, device="cuda")
-    step = lambda i: tq.decode_attn(layer, q, pools[i % 3], bt, sl, T, out=out, workspace=ws)
-    _time_steps(torch, step, 10)
-    ms = _time_steps(torch, step, 60)
-    tq.profile_reset()
-    tq.profile_enable(1 << tq.K_SPLITK)
-    _time_steps(torch, step, 60)
-    sk_ms, sk_n = tq.profile_read(tq.K_SPLITK)
-    tq.profile_enable(0)
-    nbytes = T * Hkv * _record_bytes(W["k_bits"], W["v_bits"]) + (T // 16) * 4 + 4 + Hq * 2 * 128 * 4
-    sk_s = sk_ms / max(sk_n, 1) / 1e3
-    res[W["name"]] = {"decode_us": round(ms * 1e3, 2), "decode_tok_s": round(1 / (ms / 1e3), 1),
-                      "kv_tok_s": round(T / (ms / 1e3), 1), "splitk_us": round(sk_s * 1e6, 2),
-                      "splitk_gbs": round(nbytes / sk_s / 1e9, 1),
-                      "splitk_frac": round(nbytes / sk_s / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
-    layer.close()
-    del pools, pool0
-    torch.cuda.empty_cache()
-    # ragged mixed-bit serving: 32 layers, B = 64, seq_lens U{512..32768}
-    W, sd = synth.WORKLOADS[5], synth.seeds(5)
-    B, Hq, Hkv = W["B"], W["Hq"], W["Hkv"]
-    lens = synth.ragged_lengths(sd["lens"], B, W["min_len"], W["max_len"])
-    alloc = synth.mixed_bit_allocation(sd["alloc"], W["layers"])
-    table, _ = _compact_table(sd["table"], lens)
-    bt = torch.from_numpy(table).cuda()
-    sl = torch.from_numpy(lens).cuda()
-    maxlen = int(lens.max())
-    q = torch.from_numpy(synth.queries_host(sd["data"], B, Hq)).to("cuda", torch.bfloat16)
-    layers, pools, outs, wss = [], [], [], []
-    nbytes = 0
-    for li, kv in enumerate(alloc):
-        kb, vb = kv if kv else (4, 4)
-        lay = tq.Layer(tq.config(Hkv, kb, vb, seed=sd["state"], layer=li, bypass=kv is None))
-        layers.append(lay)
-        pools.append(_fill(torch, tq, synth, lay, table, lens, Hkv, sd["data"] * 100 + li, W["outliers"]))
-        outs.append(torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda"))
-        wss.append(tq.new_workspace(lay, B, Hq, maxlen))
-        nbytes += int(lens.sum()) * Hkv * _record_bytes(kb, vb, kv is None)
-    def step(i):
-        for li in range(len(layers)):
-            tq.decode_attn(layers[li], q, pools[li], bt, sl, maxlen, out=outs[li], workspace=wss[li])
-    _time_steps(torch, step, 2)
-    ms = _time_steps(torch, step, 5)
-    res[W["name"]] = {"step_ms": round(ms, 3), "decode_tok_s": round(B / (ms / 1e3), 1),
-                      "kv_tok_s": round(float(lens.sum()) * len(layers) / (ms / 1e3), 1),
-                      "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
-                      "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "record_bytes_per_step": nbytes, "tokens": int(lens.sum())}
-    for lay in layers:
-        lay.close()
-    return res
-
-
-def _oracle_sequence(args):
-    """One sequence of the headline workload through the float64 oracle in a
-    worker process: compress its context (untimed), wait for the other workers,
-    then time its decode step.  Returns (start, end) on the shared monotonic clock."""
+def _oracle_job(job):
+    """One oracle job in a worker process (one BLAS thread): set up untimed, wait
+    for the other workers at the barrier, then run the timed part.  Returns
+    (start, end) on the shared monotonic clock.
+      ("decode", K, V, q, table_row, T, Hkv, kb, vb, seed, layer, bypass):
+          compress the sequence's context into a store (untimed), then decode
+      ("compress", K, V, Hkv, kb, vb, seed): compress the tokens into a store"""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import compress as ocomp, decode as odec, layout as olay, state as ostate
 
-    (K, V, q, table_row, T, Hkv, kb, vb, seed) = args
+    from compressed_decode_attention_tq_amd import synth
+
     with threadpool_limits(1):
-        st = ostate.LayerState(seed, 0, Hkv, 128, kb, vb, 32)
-        lay = olay.StoreLayout(128, kb, vb, 32)
+        if job[0] == "compress":
+            _, K, V, Hkv, kb, vb, seed = job
+            st = ostate.LayerState(seed, 0, Hkv, 128, kb, vb, 32)
+            lay = olay.StoreLayout(128, kb, vb, 32)
+            pool = olay.new_pool((len(K) + 15) // 16, Hkv, lay)
+            _BARRIER.wait()
+            t0 = time.perf_counter()
+            ocomp.compress_into_pool(K, V, np.arange(len(K)), pool, lay, st, keep=False)
+            return t0, time.perf_counter()
+        _, K, V, q, table_row, T, Hkv, kb, vb, seed, layer, bypass = job
+        lay = olay.StoreLayout(128, kb, vb, 32, bypass=bypass)
         nb = int(table_row.max()) + 1
         pool = olay.new_pool(nb, Hkv, lay)
         pos = np.arange(T)
         slots = table_row[pos // 16].astype(np.int64) * 16 + pos % 16
-        ocomp.compress_into_pool(K, V, slots, pool, lay, st, keep=False)
+        if bypass:
+            st = None
+            ocomp.store_bypass(synth.bf16_bits(K), synth.bf16_bits(V), slots, pool, lay, Hkv)
+        else:
+            st = ostate.LayerState(seed, layer, Hkv, 128, kb, vb, 32)
+            ocomp.compress_into_pool(K, V, slots, pool, lay, st, keep=False)
         _BARRIER.wait()
         t0 = time.perf_counter()
         odec.decode(q, pool, lay, Hkv, table_row[None, :], np.array([T]), st)
@@ -487,60 +595,151 @@ def _worker_init(barrier):
     _BARRIER = barrier
 
 
-def cpu_baseline(torch, synth, ctx, budget_s):
-    """The float64 oracle on the headline workload: the 16 sequences' decode steps
-    run side by side in worker processes, one sequence and one thread each, on the
-    host cores (at most 16 workers).  Setup (compressing each sequence's context) is
-    not timed; the timed part is the wall-clock span of the decode steps.  If the
-    workers cannot be started, one sequence after another in this process."""
+def _run_oracle_jobs(jobs):
+    """Run jobs side by side in worker processes (at most 16 at a time: the host
+    cores the run may use); per job its (start, end).  Raises if workers cannot start."""
     import multiprocessing as mp
-
-    import numpy as np
-
-    W, sd = ctx["W"], ctx["sd"]
-    B, Hq, Hkv, T = W["B"], W["Hq"], W["Hkv"], W["ctx"]
     cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, 16, len(jobs)))
+    mctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state
+    spans = []
+    for r0 in range(0, len(jobs), workers):
+        batch = jobs[r0:r0 + workers]
+        barrier = mctx.Barrier(len(batch))
+        with mctx.Pool(len(batch), initializer=_worker_init, initargs=(barrier,)) as pool:
+            spans += pool.map(_oracle_job, batch)
+    return spans, workers, cores
+
+
+def _host_rows(t, rows):
+    return t[rows].float().cpu().numpy()
+
+
+def cpu_baseline_serving(torch, synth, ctx):
+    """Oracle decode of a bounded sample of the serving batch: sequences 0, 31, 63
+    through one layer of each kind (bf16, K4/V4, K3/V2, K4/V3, K3/V3); the cost per
+    token of each layer kind is extrapolated to all 64 sequences x 32 layers run on
+    the same number of worker processes."""
+    import numpy as np
+    lens, table, alloc, W, sd = ctx["lens"], ctx["table"], ctx["alloc"], ctx["W"], ctx["sd"]
+    B, Hkv = W["B"], W["Hkv"]
     q = ctx["q"].float().cpu().numpy().astype(np.float64)
-    table = ctx["table"]
-    jobs = [(ctx["k"][b * T:(b + 1) * T].float().cpu().numpy(), ctx["v"][b * T:(b + 1) * T].float().cpu().numpy(),
-             q[b:b + 1], table[b], T, Hkv, W["k_bits"], W["v_bits"], sd["state"]) for b in range(B)]
-    workers = max(1, min(cores, 16, B))
-    try:
-        mctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state
-        rounds = []
-        for r0 in range(0, B, workers):
-            batch = jobs[r0:r0 + workers]
-            barrier = mctx.Barrier(len(batch))
-            with mctx.Pool(len(batch), initializer=_worker_init, initargs=(barrier,)) as pool:
-                spans = pool.map(_oracle_sequence, batch)
-            rounds.append(max(e for _, e in spans) - min(s for s, _ in spans))
-        spent = sum(rounds)
-        return {"value": round(B / spent, 3), "unit": "decode tok/s", "cores": workers, "kind": "oracle",
-                "sample": "all %d sequences of the headline workload (float64 NumPy), %d worker processes of one "
-                          "thread each; timed: wall clock of the decode steps (32 query heads over 4096 "
-                          "compressed tokens per sequence)" % (B, workers),
-                "seconds": round(spent, 2), "host_cores_available": cores}
-    except Exception as e:  # a reported baseline: fall back to one process
-        log("cpu baseline workers failed (%s); one process" % (e,))
-    global _BARRIER
-    _BARRIER = type("NoBarrier", (), {"wait": lambda self: None})()
-    done, spent = 0, 0.0
-    for job in jobs:
-        t0, t1 = _oracle_sequence(job)
-        spent += t1 - t0
-        done += 1
-        if spent >= budget_s:
-            break
-    return {"value": round(done / spent, 3), "unit": "decode tok/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d sequences of the headline workload (float64 NumPy, one thread); "
-                      "timed: decode of 32 query heads over 4096 compressed tokens, per sequence" % (done, B),
-            "seconds": round(spent, 2), "host_cores_available": cores}
+    picks, seen = [], set()
+    for li, kv in enumerate(alloc):
+        if kv not in seen:
+            seen.add(kv)
+            picks.append(li)
+    sample = [0, 31, 63]
+    off = np.concatenate([[0], np.cumsum(lens)])
+    jobs, meta = [], []
+    for li in picks:
+        kv = alloc[li]
+        kb, vb = kv if kv else (4, 4)
+        k, v = synth.kv_device(sd["data"] * 100 + li, int(lens.sum()), Hkv, outliers=W["outliers"])
+        for b in sample:
+            rows = torch.arange(int(off[b]), int(off[b + 1]), device="cuda")
+            jobs.append(("decode", _host_rows(k, rows), _host_rows(v, rows), q[b:b + 1], table[b], int(lens[b]), Hkv,
+                         kb, vb, sd["state"], li, kv is None))
+            meta.append((kv, int(lens[b])))
+        del k, v
+    spans, workers, cores = _run_oracle_jobs(jobs)
+    per_tok = {}
+    for (kv, T), (t0, t1) in zip(meta, spans):
+        per_tok.setdefault(kv, []).append((t1 - t0) / T)
+    cost = {kv: float(np.mean(c)) for kv, c in per_tok.items()}
+    serial_s = sum(float(lens.sum()) * cost[kv] for kv in alloc)
+    step_s = serial_s / workers
+    return {"value": round(B / step_s, 4), "unit": "decode tok/s", "cores": workers, "kind": "oracle",
+            "sample": "float64 NumPy oracle, %d worker processes of one thread: decode of sequences %s (%s tokens) "
+                      "through layers %s (one of each kind: bf16, K4/V4, K3/V2, K4/V3, K3/V3), 32 query heads each; "
+                      "the measured seconds per token of each layer kind extrapolated to all %d sequences x 32 "
+                      "layers on the same workers (%.0f s of oracle work per step)"
+                      % (workers, sample, [int(lens[b]) for b in sample], picks, B, serial_s),
+            "measured_s": round(sum(t1 - t0 for t0, t1 in spans), 2), "host_cores_available": cores,
+            "extrapolated": True}
+
+
+def cpu_baseline_layer(torch, synth, ctx):
+    """Oracle decode of all 16 sequences of the Llama-3-8B-shaped layer, side by side."""
+    import numpy as np
+    W, sd = ctx["W"], ctx["sd"]
+    B, Hkv, T = W["B"], W["Hkv"], W["ctx"]
+    q = ctx["q"].float().cpu().numpy().astype(np.float64)
+    jobs = [("decode", ctx["k"][b * T:(b + 1) * T].float().cpu().numpy(),
+             ctx["v"][b * T:(b + 1) * T].float().cpu().numpy(), q[b:b + 1], ctx["table"][b], T, Hkv, W["k_bits"],
+             W["v_bits"], sd["state"], 0, False) for b in range(B)]
+    spans, workers, cores = _run_oracle_jobs(jobs)
+    wall = max(e for _, e in spans) - min(s for s, _ in spans)
+    return {"value": round(B / wall, 3), "unit": "decode tok/s", "cores": workers, "kind": "oracle",
+            "sample": "all %d sequences (float64 NumPy), %d worker processes of one thread; timed: wall clock of "
+                      "the decode steps (32 query heads over 4096 compressed tokens each)" % (B, workers),
+            "seconds": round(wall, 2), "host_cores_available": cores, "extrapolated": False}
+
+
+def cpu_baseline_compress(torch, synth):
+    """Oracle compress of the first 65,536 tokens of the 1,048,576-token workload,
+    split over the worker processes (4,096 tokens x 8 heads each)."""
+    W, sd = synth.WORKLOADS[3], synth.seeds(3)
+    n_sample, H = 65536, W["Hkv"]
+    k, v = synth.kv_device(sd["data"], W["N"], H)
+    chunk = 4096
+    jobs = [("compress", k[i:i + chunk].float().cpu().numpy(), v[i:i + chunk].float().cpu().numpy(), H,
+             W["k_bits"], W["v_bits"], sd["state"]) for i in range(0, n_sample, chunk)]
+    del k, v
+    spans, workers, cores = _run_oracle_jobs(jobs)
+    rounds = (len(jobs) + workers - 1) // workers
+    wall = max(e for _, e in spans) - min(s for s, _ in spans)
+    return {"value": round(n_sample / wall / 1e6, 6), "unit": "Mtok/s", "cores": workers, "kind": "oracle",
+            "sample": "the first %d of %d tokens x %d heads (float64 NumPy), %d jobs of %d tokens on %d worker "
+                      "processes of one thread (%d round%s); timed: wall clock of the compress calls"
+                      % (n_sample, W["N"], H, len(jobs), chunk, workers, rounds, "s" if rounds > 1 else ""),
+            "seconds": round(wall, 2), "host_cores_available": cores, "extrapolated": False}
+
+
+def cpu_baseline_long(torch, synth):
+    """Oracle decode of the first 8,192 tokens of the 131,072-token context (one
+    worker), extrapolated linearly to the whole context."""
+    import numpy as np
+    W, sd = synth.WORKLOADS[4], synth.seeds(4)
+    T, Hkv, Hq, n = W["ctx"], W["Hkv"], W["Hq"], 8192
+    table = synth.block_table(sd["table"], 1, T // 16, "random")
+    k, v = synth.kv_device(sd["data"], T, Hkv, outliers=W["outliers"])
+    q = synth.queries_host(sd["data"], 1, Hq).astype(np.float64)
+    rows = torch.arange(n, device="cuda")
+    jobs = [("decode", _host_rows(k, rows), _host_rows(v, rows), q, table[0], n, Hkv, W["k_bits"], W["v_bits"],
+             sd["state"], 0, False)]
+    del k, v
+    spans, workers, cores = _run_oracle_jobs(jobs)
+    t = spans[0][1] - spans[0][0]
+    step_s = t * T / n
+    return {"value": round(1.0 / step_s, 5), "unit": "decode tok/s", "cores": 1, "kind": "oracle",
+            "sample": "decode of the first %d of %d context tokens (float64 NumPy, one thread, 32 query heads), "
+                      "extrapolated linearly in the context length" % (n, T),
+            "measured_s": round(t, 2), "host_cores_available": cores, "extrapolated": True}
+
+
+def cpu_baseline_tiny(torch, synth):
+    """Oracle decode of the whole tiny case (1 head, 1024 fp32 tokens)."""
+    W, sd = synth.WORKLOADS[1], synth.seeds(1)
+    K, V = synth.kv_host(sd["data"], W["ctx"], W["Hkv"], dtype="f32")
+    import numpy as np
+    q = synth.queries_host(sd["data"], 1, W["Hq"], dtype="f32").astype(np.float64)
+    table = synth.block_table(sd["table"], 1, W["ctx"] // 16, "identity")
+    jobs = [("decode", K, V, q, table[0], W["ctx"], W["Hkv"], W["k_bits"], W["v_bits"], sd["state"], 0, False)]
+    spans, workers, cores = _run_oracle_jobs(jobs)
+    t = spans[0][1] - spans[0][0]
+    return {"value": round(t * 1e6, 1), "unit": "decode us", "cores": 1, "kind": "oracle",
+            "sample": "the whole case (float64 NumPy, one thread)", "host_cores_available": cores,
+            "extrapolated": False}
 
 
 def main():
     args = parse()
     if args.traffic_from:
         print("\n".join(traffic_summary(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib)))
+        return
+    if args.trace_summary:
+        print("\n".join(trace_summary(args.trace_summary)))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the compressed-KV path runs on one device per process and "
@@ -558,16 +757,29 @@ def main():
     if args.copy_probe_mib > 0:
         copy_probe(torch, args.copy_probe_mib)
     copy_gbs = copy_bandwidth(torch)
-    log("decode workload")
-    dec, ctx = decode_workload(torch, tq, synth, args)
+    log("serving batch (headline): 32 layers, B=64")
+    head, head_ctx = serving_workload(torch, tq, synth, args)
+    configs = {}
+    log("tiny fp32 case")
+    configs["1"] = tiny_workload(torch, tq, synth, args)
+    log("llama3-8b-shaped decode layer")
+    configs["2"], layer_ctx = layer_workload(torch, tq, synth, args)
     comp = None
     if not args.no_compress:
-        log("compress workload")
+        log("fused compress, 1M tokens x 8 heads")
         comp = compress_workload(torch, tq, synth, args)
+        configs["3"] = comp
+    log("long-context decode")
+    configs["4"] = long_context_workload(torch, tq, synth, args)
+    configs["5"] = {"workload": head["config"]["workload"], "decode_ms": round(head["ms_per_step"], 4),
+                    "decode_tok_s": round(head["value"], 2), "kv_tok_s": round(head["kv_tok_s"], 1),
+                    "step_hbm_gbs": round(head["step_hbm_gbs"], 1),
+                    "step_frac": round(head["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
+                    "roofline": head["roofline"], "splitk_by_layer_kind": head["splitk_by_layer_kind"],
+                    "steps": args.steps, "warmup": args.warmup}
     extra = None
     if args.all_configs:
-        log("tiny, long-context and serving workloads")
-        extra = extra_workloads(torch, tq, synth, args)
+        extra = {}
         if not args.no_compress:
             log("compress workload, key modes without QJL")
             extra["fused-compress-key-mse"] = compress_workload(torch, tq, synth, args, key_mode=tq.KEY_MSE)
@@ -582,32 +794,49 @@ def main():
         extra["mse_values"] = mse_values_workload(torch, tq, synth, args)
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline")
-        cpu = cpu_baseline(torch, synth, ctx, args.cpu_budget_s)
+        for key, name, fn in (("5", "serving", lambda: cpu_baseline_serving(torch, synth, head_ctx)),
+                              ("1", "tiny", lambda: cpu_baseline_tiny(torch, synth)),
+                              ("2", "layer", lambda: cpu_baseline_layer(torch, synth, layer_ctx)),
+                              ("3", "compress", lambda: cpu_baseline_compress(torch, synth)),
+                              ("4", "long context", lambda: cpu_baseline_long(torch, synth))):
+            if key not in configs:
+                continue
+            log("cpu baseline:", name)
+            try:
+                configs[key]["cpu_baseline"] = fn()
+            except Exception as e:  # a reported baseline; the GPU figures stand without it
+                log("cpu baseline %s failed: %r" % (name, e))
+                configs[key]["cpu_baseline"] = None
+        cpu = configs["5"].get("cpu_baseline")
+    layer_roof = configs["2"]["roofline"]
     line = {
         "metric": "compressed-KV decode attn tokens/s + HBM GB/s (% of peak); compress Mtok/s",
-        "value": round(dec["value"], 1),
+        "value": round(head["value"], 2),
         "unit": "decode tok/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dec["ms_per_step"], 5),
+        "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded N(0,1) bf16 K/V with outlier channels)",
-        "config": dec["config"],
-        "roofline": dec["roofline"],
+        "dtype_note": "scores, softmax and accumulation in float32; matrix-core operands are float16 hi + lo "
+                      "pieces (about 22 significant bits) of float32 values, bf16 K/V and queries in",
+        "data": "synthetic (seeded N(0,1) bf16 K/V with 4 outlier channels per head x10; ragged lengths; "
+                "random block tables)",
+        "config": head["config"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
-        "kv_tok_s": round(dec["kv_tok_s"], 1),
-        "step_hbm_gbs": round(dec["step_hbm_gbs"], 1),
-        "step_hbm_frac": round(dec["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
-        "append_us": dec["append_us"],
+        "kv_tok_s": round(head["kv_tok_s"], 1),
+        "step_hbm_gbs": round(head["step_hbm_gbs"], 1),
+        "step_hbm_frac": round(head["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
         "device_copy_gbs": round(copy_gbs, 1),
-        "splitk_frac_of_copy": round(dec["roofline"]["achieved"] / copy_gbs, 4),
-        "compress_frac_of_copy": round(comp["roofline"]["achieved"] / copy_gbs, 4) if comp else None,
-        "compress": comp,
+        "splitk_frac_of_copy": round(head["roofline"]["achieved"] / copy_gbs, 4),
+        "layer_splitk_frac": layer_roof["frac"],
+        "compress_mtok_s": comp["mtok_s"] if comp else None,
+        "compress_frac": comp["roofline"]["frac"] if comp else None,
+        "configs": configs,
     }
     if extra is not None:
         line["other_workloads"] = extra
