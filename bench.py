@@ -518,10 +518,11 @@ def decompress_workload(torch, tq, synth, args):
 
 
 def mse_values_workload(torch, tq, synth, args):
-    """The headline store's shape (16 x 4096 tokens x 8 KV heads) with 2-bit keys + QJL and
-    3-bit values coded like the keys (the 102-byte record): the per-token fused compress
-    into the store, then the decompress to bf16 K and V."""
-    B, Hkv, T = 16, 8, 4096
+    """The Llama-3-8B layer's shape (16 x 4096 tokens x 8 KV heads, 32 query heads) with
+    2-bit keys + QJL and 3-bit values coded like the keys (the 102-byte record): the
+    fused compress into the store, the decode step over it (three store copies
+    rotated) and the decompress to bf16 K and V."""
+    B, Hkv, Hq, T = 16, 8, 32, 4096
     N = B * T
     layer = tq.Layer(tq.config(Hkv, 2, 3, seed=361, value_mode=tq.VAL_MSE))
     k, v = synth.kv_device(362, N, Hkv, outliers=4)
@@ -530,6 +531,16 @@ def mse_values_workload(torch, tq, synth, args):
     comp = lambda i: tq.compress_kv(layer, k, v, slots, pool)
     _time_steps(torch, comp, 2)
     ms_c = _time_steps(torch, comp, 10)
+    pools = [pool] + [pool.clone() for _ in range(2)]
+    table = torch.arange(N // 16, dtype=torch.int32, device="cuda").view(B, T // 16)
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(synth.queries_host(363, B, Hq)).to("cuda", torch.bfloat16)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = tq.new_workspace(layer, B, Hq, T)
+    step = lambda i: tq.decode_attn(layer, q, pools[i % 3], table, sl, T, out=out, workspace=ws)
+    _time_steps(torch, step, 20)
+    ms_s = _time_steps(torch, step, 100)
+    sk_us, sk_n = _events_avg_us(torch, tq, tq.K_SPLITK, step, 100)
     kd = torch.empty((N, Hkv, 128), dtype=torch.bfloat16, device="cuda")
     vd = torch.empty_like(kd)
     dec = lambda i: tq.decompress_kv(layer, pool, slots, k_out=kd, v_out=vd)
@@ -538,9 +549,12 @@ def mse_values_workload(torch, tq, synth, args):
     rec = layer.block_bytes // 16
     layer.close()
     nbytes = N * Hkv * (512 + rec) + N * 8  # bf16 K+V and the record, either direction, + slots
-    return {"workload": "mse-values-k2qjl-v3-store", "token_heads": N * Hkv, "record_bytes": rec,
+    sk_bytes = _splitk_bytes([T] * B, Hkv, Hq, rec)
+    return {"workload": "mse-values-k2qjl-v3-layer", "token_heads": N * Hkv, "record_bytes": rec,
             "compress_ms": round(ms_c, 4), "compress_gbs": round(nbytes / (ms_c / 1e3) / 1e9, 1),
             "compress_frac": round(nbytes / (ms_c / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_us": round(ms_s * 1e3, 3), "decode_tok_s": round(B / (ms_s / 1e3), 1),
+            "splitk": _roofline(sk_bytes, sk_us, "splitk_mfma_kernel<4,2,3,true>", sk_n),
             "decompress_ms": round(ms_d, 4), "decompress_gbs": round(nbytes / (ms_d / 1e3) / 1e9, 1),
             "decompress_frac": round(nbytes / (ms_d / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
 

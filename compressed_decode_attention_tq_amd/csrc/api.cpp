@@ -203,8 +203,6 @@ tq_status prepare_decode(const tq_layer* L, const void* q, tq_dtype q_dtype, int
     return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head = %d not supported (1, 2, 4, 8)", rep);
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16)
     return fail(TQ_ERR_UNSUPPORTED, "query dtype %d not supported (F32, BF16)", static_cast<int>(q_dtype));
-  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_MSE)
-    return fail(TQ_ERR_UNSUPPORTED, "decode of layers with MSE-coded values is not built");
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16)
     return fail(TQ_ERR_UNSUPPORTED, "output dtype %d not supported (F32, BF16)", static_cast<int>(out_dtype));
   if (static_cast<long long>(max_blocks_per_seq) * kPage < max_seq_len)

@@ -56,6 +56,13 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
 }
+// Squared norms are summed in float64: a vector of tiny entries (say 2^-70) has a
+// squared norm below the float32 normal range, where float32 keeps too few bits
+// for the standardising factor sqrt(d) / n.
+__device__ __forceinline__ double wave_sum_d(double x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
 
 // Element index of the value code of (coordinate dim, in-page token t) in the
 // page's Vc stream: lane block 16 (t / 8) + dim % 16, group 2 (dim / 16) + (t % 8) / 4
@@ -94,7 +101,8 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
   const long long slot = a.slots[tok];
   if (slot < 0) return;
 
-  __shared__ float sk[128], sv[128], srho[128], red[4], redv[2];
+  __shared__ float sk[128], sv[128], srho[128], red[4];
+  __shared__ double rk2[2], rv2[2];
   __shared__ float pk[4][128], pv[4][128];
   __shared__ unsigned char ck[128];
   __shared__ unsigned sbits[4];
@@ -114,13 +122,13 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
   if (c == 0) {
     kx = load_elem<BF16>(a.k, tok * a.k_stride + h * 128 + i);
     sk[i] = kx;
-    const float w2 = wave_sum(kx * kx);
-    if ((i & 63) == 0) red[i >> 6] = w2;
+    const double w2 = wave_sum_d(static_cast<double>(kx) * kx);
+    if ((i & 63) == 0) rk2[i >> 6] = w2;
   } else if (c == 1) {
     const float vx = load_elem<BF16>(a.v, tok * a.v_stride + h * 128 + i);
     sv[i] = vx;
-    const float w2 = wave_sum(vx * vx);  // ||v||^2 (used with codebook-coded values)
-    if ((i & 63) == 0) redv[i >> 6] = w2;
+    const double w2 = wave_sum_d(static_cast<double>(vx) * vx);  // ||v||^2 (codebook-coded values)
+    if ((i & 63) == 0) rv2[i >> 6] = w2;
   }
   __syncthreads();
   {
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     const float rk = (pk[0][i] + pk[1][i]) + (pk[2][i] + pk[3][i]);
     rv = (pv[0][i] + pv[1][i]) + (pv[2][i] + pv[3][i]);
     // keys: standardise, quantise, residual
-    n = sqrtf(red[0] + red[1]);
+    n = static_cast<float>(sqrt(rk2[0] + rk2[1]));
     const float t = (n > 0.0f) ? rk * (sqrtf(128.0f) / n) : 0.0f;
     int idx = 0;
 #pragma unroll
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     if ((i & 63) == 0) red[2 + (i >> 6)] = g2;
     if (a.vm == 1) {
       // values: standardise by the vector norm, then the value codebook
-      const float nv = sqrtf(redv[0] + redv[1]);
+      const float nv = static_cast<float>(sqrt(rv2[0] + rv2[1]));
       const float tv = (nv > 0.0f) ? rv * (sqrtf(128.0f) / nv) : 0.0f;
 #pragma unroll
       for (int b = 0; b < (1 << VB) - 1; ++b) code += (a.vbnd[b] < tv) ? 1 : 0;
@@ -300,8 +308,7 @@ tq_status launch_compress(const tq_layer* L, const void* k, const void* v, tq_dt
                           const long long* slots, void* pool, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   ProfScope prof(kKCompress, stream);
-  if (!L->cfg.bypass && L->cfg.value_mode == TQ_VAL_GROUP &&  // MSE-coded values: the per-token kernel below
-      compress_mfma_applies(L, k, v, in_dtype, n_tokens, k_stride, v_stride)) {
+  if (!L->cfg.bypass && compress_mfma_applies(L, k, v, in_dtype, n_tokens, k_stride, v_stride)) {
     tq_status st = launch_compress_mfma(L, k, v, n_tokens, k_stride, v_stride, slots, pool, stream);
     if (st != TQ_OK) return st;
     hipError_t e = hipGetLastError();

@@ -6,7 +6,10 @@
 //   keys:   n = ||k||, t = sqrt(d) R k / n, idx = #{beta < t}, rho = t - c[idx],
 //           gamma = ||rho||, z = [S rho >= 0]
 //   values: v' = R v; per 32-group scale16 = fp16((max-min)/(2^b-1)), zero16 = fp16(min),
-//           code = clamp(rint((v' - zero16)/scale16), 0, 2^b-1)  (0 when scale16 == 0)
+//           code = clamp(rint((v' - zero16)/scale16), 0, 2^b-1)  (0 when scale16 == 0);
+//           or, coded like the keys' codebook part ("5x Faster LLM Inference? ...",
+//           "What is TurboQuant-GPU?": MSE-coded values), nv = ||v||,
+//           code = #{beta_v < sqrt(d) v' / nv} with the value codebook, Vn = fp16(nv)
 //
 // The three 128x128 contractions are 16x16x32 matrix-core tiles (16 output
 // coordinates x 16 tokens x 32 inputs).  The matrix core forms exact products,
@@ -61,6 +64,8 @@ struct CArgs {
   unsigned block_bytes;
   float cent[16];
   float bnd[16];
+  float vcent[16];  // value codebook (MSE-coded values)
+  float vbnd[16];
 };
 
 __device__ __forceinline__ floatx4 mfma_h(const half8& a, const half8& b, const floatx4& c) {
@@ -159,16 +164,44 @@ __device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
                : "memory", "m0");
 }
 
-// Page image offsets (same format as the store).
-template <int KB, int VB>
+// Page image offsets (same format as the store; MSEV: the last field is Vn
+// [16] fp16 instead of the groups' scale and zero).
+template <int KB, int VB, bool MSEV>
 struct Page {
   static constexpr int kc = 0;
   static constexpr int ks = 256 * KB;
   static constexpr int kn = ks + 256;
   static constexpr int vc = kn + 64;
   static constexpr int vsz = vc + 256 * VB;
-  static constexpr int bytes = vsz + 256;
+  static constexpr int bytes = vsz + (MSEV ? 32 : 256);
 };
+
+// Code of t in a symmetric codebook of 2 HALF levels: idx = #{beta < t}, ties to
+// the lower cell.  For t <= 0 the count of positive boundaries uses the next
+// float above |t|, so a boundary equal to |t| counts as "not below".  *cp = the
+// chosen centroid's magnitude.
+template <int HALF>
+__device__ __forceinline__ int sym_code(float t, const float* cent, const float* bnd, float* cp) {
+  const float m = fabsf(t);
+  const float mq = (t > 0.0f) ? m : __uint_as_float(__float_as_uint(m) + 1u);
+  int cnt = 0;
+  float c = cent[HALF];
+#pragma unroll
+  for (int j = 0; j < HALF - 1; ++j) {
+    const bool above = bnd[HALF + j] < mq;
+    cnt += above ? 1 : 0;
+    c = above ? cent[HALF + j + 1] : c;
+  }
+  *cp = c;
+  return (t > 0.0f) ? HALF + cnt : HALF - 1 - cnt;
+}
+
+// sqrt(d) / n from n^2 (0 for a zero vector): the reciprocal square root where
+// n^2 is a normal float, the quotient of roots for a subnormal n^2.
+__device__ __forceinline__ float std_factor(float n2) {
+  return (n2 >= 1.17549435e-38f) ? sqrtf(128.0f) * __builtin_amdgcn_rsqf(n2)
+                                 : (n2 > 0.0f ? sqrtf(128.0f) / sqrtf(n2) : 0.0f);
+}
 
 // Wait until at most n of this wave's vector-memory operations are outstanding,
 // for n rounded down to 2P - 1, P - 1 or 0 (wave-uniform n).  Loads and stores
@@ -200,9 +233,10 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // +-rscale: R k = rscale (sign pattern) k, one exact bf16 pass instead of three.
 // QJL: keys get the residual signs and gamma (key mode 0); otherwise the key
 // mode (1 or 2: plain or norm-corrected magnitude) comes from a.km.
-template <int KB, int VB, int P, bool HAD, bool QJL>
+// MSEV: values coded like the keys' codebook part (value norm + value codebook).
+template <int KB, int VB, int P, bool HAD, bool QJL, bool MSEV>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 : 8))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
-  using PG = Page<KB, VB>;
+  using PG = Page<KB, VB, MSEV>;
   constexpr int HALF = 1 << (KB - 1);  // codebook levels per sign
   constexpr float kTop = static_cast<float>((1 << VB) - 1);
   constexpr int kChunks = PG::bytes / 16;  // 16-byte chunks of a page (at most 164 = 8 waves x 21 lanes)
@@ -322,6 +356,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     // K-step at a time (8 registers live, not 32); the key chunk a lane holds
     // is both the A row (token col) and the B column (token col) of the step.
     floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f}, V = {0.0f, 0.0f, 0.0f, 0.0f}, NK = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4 NV = {0.0f, 0.0f, 0.0f, 0.0f};  // MSE-coded values: the values' Gram product
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int pos = (4 * s + kg + col) & 15;  // chunk 4s + kg of token col
@@ -330,6 +365,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       T = mfma_b(R0[s], kb, T);
       V = mfma_b(R0[s], vb, V);
       NK = mfma_b(kb, kb, NK);
+      if constexpr (MSEV) NV = mfma_b(vb, vb, NV);
       if constexpr (!HAD) {
         T = mfma_b(R1[s], kb, T);
         V = mfma_b(R1[s], vb, V);
@@ -345,15 +381,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     // The standardising factor sqrt(d)/n comes from the reciprocal square root
     // (within an ulp or so, like the quotient of rounded roots); the stored
     // norm n16 is taken from the correctly rounded root by the wave storing it.
-    float f, k2;
+    float f, k2, v2 = 0.0f;
     {
       const int e = col & 3;
       const float d01 = (e & 1) ? NK[1] : NK[0];
       const float d23 = (e & 1) ? NK[3] : NK[2];
       k2 = __shfl((e & 2) ? d23 : d01, col + 16 * (col >> 2), 64);
-      f = (k2 >= 1.17549435e-38f) ? sqrtf(128.0f) * __builtin_amdgcn_rsqf(k2)
-                                  : (k2 > 0.0f ? sqrtf(128.0f) / sqrtf(k2) : 0.0f);  // zero norm: t = 0
+      f = std_factor(k2);  // zero norm: t = 0
       if constexpr (HAD) f *= a.rscale;  // t = (sqrt(d) / n) rscale (sign pattern) k
+      if constexpr (MSEV) {
+        const float e01 = (e & 1) ? NV[1] : NV[0];
+        const float e23 = (e & 1) ? NV[3] : NV[2];
+        v2 = __shfl((e & 2) ? e23 : e01, col + 16 * (col >> 2), 64);
+      }
+    }
+    // A squared norm below 2^-100 (every entry below 2^-50) has too few float32
+    // bits for the standardising factor, or none (products below the smallest
+    // subnormal): rare, so recomputed here from the tile rows scaled by 2^100
+    // (exact), with sqrt(d)/n = sqrt(d) 2^100 / ||2^100 x||.  Such a vector's
+    // stored norm rounds to float16 0.
+    float fv = MSEV ? std_factor(v2) : 0.0f;
+    if (__builtin_amdgcn_ballot_w64(k2 < 0x1p-100f || (MSEV && v2 < 0x1p-100f)) != 0ull) {
+      float sk2 = 0.0f, sv2 = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int pos = (4 * s + kg + col) & 15;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xk = __uint_as_float(static_cast<unsigned>(kv_in[slot][0][col][8 * pos + e]) << 16) * 0x1p100f;
+          const float xv = __uint_as_float(static_cast<unsigned>(kv_in[slot][1][col][8 * pos + e]) << 16) * 0x1p100f;
+          sk2 = fmaf(xk, xk, sk2);
+          sv2 = fmaf(xv, xv, sv2);
+        }
+      }
+      sk2 = rows_sum(sk2);
+      sv2 = rows_sum(sv2);
+      if (k2 < 0x1p-100f) {
+        f = sk2 > 0.0f ? sqrtf(128.0f) * 0x1p100f * __builtin_amdgcn_rsqf(sk2) : 0.0f;
+        if constexpr (HAD) f *= a.rscale;
+        k2 = 0.0f;
+      }
+      if (MSEV && v2 < 0x1p-100f) {
+        fv = sv2 > 0.0f ? sqrtf(128.0f) * 0x1p100f * __builtin_amdgcn_rsqf(sv2) : 0.0f;
+        v2 = 0.0f;
+      }
     }
 
     // ---- B2: t, codes, residual (rho -> LDS), key codes -> image; value extremes
@@ -364,19 +435,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float t = T[r] * f;
-        // symmetric codebook: cnt = #{positive boundaries below |t|}, ties to the
-        // lower cell (so for t <= 0 compare against the next float above |t|)
-        const float m = fabsf(t);
-        const float mq = (t > 0.0f) ? m : __uint_as_float(__float_as_uint(m) + 1u);
-        int cnt = 0;
-        float cp = a.cent[HALF];
-#pragma unroll
-        for (int j = 0; j < HALF - 1; ++j) {
-          const bool above = a.bnd[HALF + j] < mq;
-          cnt += above ? 1 : 0;
-          cp = above ? a.cent[HALF + j + 1] : cp;
-        }
-        const int idx = (t > 0.0f) ? HALF + cnt : HALF - 1 - cnt;
+        float cp;
+        const int idx = sym_code<HALF>(t, a.cent, a.bnd, &cp);
         rho[r] = t - ((t > 0.0f) ? cp : -cp);
         // squared norm of the residual (QJL) or of the centroid vector (norm correction)
         const float gt = QJL ? rho[r] : (a.km == 2 ? cp : 0.0f);
@@ -411,18 +471,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
         if (sh + 4 * KB > 32) atomicOr(&rw[wi + 1], codes >> (32 - sh));
       }
 
-      float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vp[r] = V[r];
-        mn = fminf(mn, vp[r]);
-        mx = fmaxf(mx, vp[r]);
-      }
-      mn = rows_min(mn);
-      mx = rows_max(mx);
-      if (kg == 0) {
-        vmin[w][col] = mn;
-        vmax[w][col] = mx;
+      for (int r = 0; r < 4; ++r) vp[r] = V[r];
+      if constexpr (!MSEV) {
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mn = fminf(mn, vp[r]);
+          mx = fmaxf(mx, vp[r]);
+        }
+        mn = rows_min(mn);
+        mx = rows_max(mx);
+        if (kg == 0) {
+          vmin[w][col] = mn;
+          vmax[w][col] = mx;
+        }
       }
     }
     __syncthreads();  // rho, norms and extremes in LDS; every wave is past B1, so
@@ -455,20 +518,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       if ((kg & 1) == 0)
         img[PG::ks + ((w >> 1) * 16 + col) * 4 + 2 * (w & 1) + (kg >> 1)] = static_cast<unsigned char>(ea | (eb << 4));
 
+      unsigned x0, x1, x2, x3;
+      __half s16, z16;
+      if constexpr (MSEV) {
+        // t = sqrt(d) v' / ||v|| against the value codebook (ties to the lower cell)
+        const unsigned sh = VB * (col & 7);
+        float cpv;
+        x0 = static_cast<unsigned>(sym_code<(1 << (VB - 1))>(vp[0] * fv, a.vcent, a.vbnd, &cpv)) << sh;
+        x1 = static_cast<unsigned>(sym_code<(1 << (VB - 1))>(vp[1] * fv, a.vcent, a.vbnd, &cpv)) << sh;
+        x2 = static_cast<unsigned>(sym_code<(1 << (VB - 1))>(vp[2] * fv, a.vcent, a.vbnd, &cpv)) << sh;
+        x3 = static_cast<unsigned>(sym_code<(1 << (VB - 1))>(vp[3] * fv, a.vcent, a.vbnd, &cpv)) << sh;
+      } else {
       const float mn = fminf(vmin[2 * G][col], vmin[2 * G + 1][col]);
       const float mx = fmaxf(vmax[2 * G][col], vmax[2 * G + 1][col]);
       // (mx - mn) / kTop as the correctly rounded float32 quotient: product by
       // the rounded reciprocal, then one residual step (exact residual by fma)
       const float span = mx - mn;
       const float q0s = span * (1.0f / kTop);
-      const __half s16 = __float2half_rn(fmaf(fmaf(-q0s, kTop, span), 1.0f / kTop, q0s));
-      const __half z16 = __float2half_rn(mn);
+      s16 = __float2half_rn(fmaf(fmaf(-q0s, kTop, span), 1.0f / kTop, q0s));
+      z16 = __float2half_rn(mn);
       const float sc = __half2float(s16), zr = __half2float(z16);
       // reciprocal of the scale with one correction step
       const float inv0 = __builtin_amdgcn_rcpf(sc);
       const float inv = fmaf(fmaf(-sc, inv0, 1.0f), inv0, inv0);
       const float invz = (sc > 0.0f) ? inv : 0.0f;  // a zero scale gives code 0
-      unsigned x0, x1, x2, x3;
       {
         // quotient to a couple of float32 ulps: a code can move only within
         // ~1e-7 relative of a rounding midpoint
@@ -477,6 +550,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
         x1 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[1] - zr) * invz), 0.0f, kTop)) << sh;
         x2 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[2] - zr) * invz), 0.0f, kTop)) << sh;
         x3 = static_cast<unsigned>(__builtin_amdgcn_fmed3f(rintf((vp[3] - zr) * invz), 0.0f, kTop)) << sh;
+      }
       }
       // Value codes into the image's Vc field, in lane blocks: the run of
       // block (h, c, i) holds tokens 8h..8h+7 of coordinate 16i + c (token
@@ -518,9 +592,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
           }
         }
       }
-      if ((w & 1) == 0 && kg == 0)
+      if constexpr (MSEV) {
+        if (w == 6 && kg == 0)
+          *reinterpret_cast<unsigned short*>(&img[PG::vsz + col * 2]) = __half_as_ushort(__float2half_rn(sqrtf(v2)));
+      } else if ((w & 1) == 0 && kg == 0) {
         *reinterpret_cast<unsigned*>(&img[PG::vsz + col * 16 + G * 4]) =
             static_cast<unsigned>(__half_as_ushort(s16)) | (static_cast<unsigned>(__half_as_ushort(z16)) << 16);
+      }
       if (w == 7 && kg == 0) {
         float g2 = 0.0f;
 #pragma unroll
@@ -566,7 +644,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
               *reinterpret_cast<const unsigned*>(&img[PG::ks + (b * 16 + t) * 4]);
         } else if (f == 4 * KB + 4) {
           *reinterpret_cast<unsigned*>(page + PG::kn + o * 4) = *reinterpret_cast<const unsigned*>(&img[PG::kn + t * 4]);
-        } else if (f < 4 * KB + 9) {
+        } else if (MSEV && f == 4 * KB + 5) {
+          *reinterpret_cast<unsigned short*>(page + PG::vsz + o * 2) =
+              *reinterpret_cast<const unsigned short*>(&img[PG::vsz + t * 2]);
+        } else if (!MSEV && f < 4 * KB + 9) {
           const int G = f - (4 * KB + 5);
           reinterpret_cast<unsigned*>(page + PG::vsz + o * 16)[G] =
               reinterpret_cast<const unsigned*>(&img[PG::vsz + t * 16])[G];
@@ -606,24 +687,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
 }
 
 constexpr int kRing = 3;  // tiles in flight per workgroup
-template <int KB, bool HAD, bool QJL>
+template <int KB, bool HAD, bool QJL, bool MSEV>
 void* pick_v(int vb) {
   switch (vb) {
-    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing, HAD, QJL>);
-    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing, HAD, QJL>);
-    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing, HAD, QJL>);
+    case 2: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 2, kRing, HAD, QJL, MSEV>);
+    case 3: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 3, kRing, HAD, QJL, MSEV>);
+    case 4: return reinterpret_cast<void*>(&compress_mfma_kernel<KB, 4, kRing, HAD, QJL, MSEV>);
   }
   return nullptr;
 }
-template <bool HAD, bool QJL>
+template <bool HAD, bool QJL, bool MSEV>
 void* pick_kv(int kb, int vb) {
   switch (kb) {
-    case 1: return pick_v<1, HAD, QJL>(vb);
-    case 2: return pick_v<2, HAD, QJL>(vb);
-    case 3: return pick_v<3, HAD, QJL>(vb);
-    case 4: return pick_v<4, HAD, QJL>(vb);
+    case 1: return pick_v<1, HAD, QJL, MSEV>(vb);
+    case 2: return pick_v<2, HAD, QJL, MSEV>(vb);
+    case 3: return pick_v<3, HAD, QJL, MSEV>(vb);
+    case 4: return pick_v<4, HAD, QJL, MSEV>(vb);
   }
   return nullptr;
+}
+template <bool MSEV>
+void* pick_rot(bool had, bool qjl, int kb, int vb) {
+  return had ? (qjl ? pick_kv<true, true, MSEV>(kb, vb) : pick_kv<true, false, MSEV>(kb, vb))
+             : (qjl ? pick_kv<false, true, MSEV>(kb, vb) : pick_kv<false, false, MSEV>(kb, vb));
 }
 
 }  // namespace
@@ -659,12 +745,12 @@ tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, 
   for (int i = 0; i < 16; ++i) {
     a.cent[i] = L->centroids[i];
     a.bnd[i] = L->boundaries[i];
+    a.vcent[i] = L->v_centroids[i];
+    a.vbnd[i] = L->v_boundaries[i];
   }
   const bool had = L->cfg.rotation == TQ_ROT_HADAMARD, qjl = L->cfg.key_mode == TQ_KEY_QJL;
-  void* fn = had ? (qjl ? pick_kv<true, true>(L->cfg.k_bits, L->cfg.v_bits)
-                        : pick_kv<true, false>(L->cfg.k_bits, L->cfg.v_bits))
-                 : (qjl ? pick_kv<false, true>(L->cfg.k_bits, L->cfg.v_bits)
-                        : pick_kv<false, false>(L->cfg.k_bits, L->cfg.v_bits));
+  void* fn = L->cfg.value_mode == TQ_VAL_MSE ? pick_rot<true>(had, qjl, L->cfg.k_bits, L->cfg.v_bits)
+                                             : pick_rot<false>(had, qjl, L->cfg.k_bits, L->cfg.v_bits);
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits, L->cfg.v_bits);
   // Workgroups loop over their tiles: as many as fit on the chip at once over all
   // heads (resident workgroups per CU from the kernel's register and LDS use).

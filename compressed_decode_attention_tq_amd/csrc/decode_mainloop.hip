@@ -5,7 +5,10 @@
 // records are read directly, with no expanded copy of the cache):
 //   s_i = scale * (n_i / sqrt d) * (q'.c[idx_i] + sqrt(pi/2)/128 * gamma_i * u.(2 z_i - 1)).
 // Values ("How 0xsero/turboquant works", "Value Compression"):
-//   o' = sum_i p_i (zero_i + scale_i * code_i), per 32-wide group.
+//   o' = sum_i p_i (zero_i + scale_i * code_i), per 32-wide group;
+// or, for values coded like the keys' codebook part ("5x Faster LLM
+// Inference? ...", "What is TurboQuant-GPU?": MSE-coded values),
+//   o' = sum_i p_i (nv_i / sqrt d) cv[code_i].
 //
 // Both contractions run on v_mfma_f32_16x16x32_f16 with float32 accumulation.
 //
@@ -27,7 +30,10 @@
 // per-group offset sum_i p_i (zero_i + 2^(b-1) scale_i) is accumulated on the
 // vector ALU.  Centring keeps both sums free of a large cancelling offset (each
 // accumulate rounds at the accumulator's magnitude, so a 1024-biased code would
-// bury the signal).
+// bury the signal).  MSE-coded values: A = the float16 value-codebook entries of
+// the codes (exact; two codes per lookup in a replicated LDS table), B = the
+// weights p * nv16 / sqrt(d) in two float16 pieces, the same for every group;
+// no offset term.
 //
 // A wave takes a 32-token chunk (two 16-token pages) at a time; the four waves
 // of a workgroup take chunks in turn and merge at the end.  While a chunk is
@@ -65,6 +71,7 @@ struct MainArgs {
   float scale;
   unsigned block_bytes;
   float cent[16];
+  float vcent[16];  // value codebook (MSE-coded values)
 };
 
 __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
@@ -225,19 +232,25 @@ constexpr unsigned centre_bits(int p, int vb) {
 // kg/2, token 8(kg%2) + k at bit VB k of the run).  Element pair cc of the
 // operand is (token cc, token 4 + cc): the run's two 4-code groups go to the
 // two float16 halves, each code becomes a centred float16 integer exactly.
+// The lane's run of 8 codes for tile i with tokens 0..3 in the low 16 bits and
+// tokens 4..7 in the high 16 bits (field k of each half at bit VB k).
 template <int VB>
-__device__ __forceinline__ half8 value_operand(const unsigned* vc, int i) {
-  unsigned x;
+__device__ __forceinline__ unsigned value_run(const unsigned* vc, int i) {
   if constexpr (VB == 4) {
-    x = vc[i];
+    return vc[i];
   } else if constexpr (VB == 2) {
     // bytes 2(i%2), 2(i%2)+1 of the dword -> bytes 0 and 2 (zeros between)
-    x = __builtin_amdgcn_perm(vc[i >> 1], vc[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
+    return __builtin_amdgcn_perm(vc[i >> 1], vc[i >> 1], (i & 1) ? 0x0C030C02u : 0x0C010C00u);
   } else {  // VB == 3: 24 bits at bit 24 i of the lane's 192
     const int bit = 24 * i, w = bit >> 5, sh = bit & 31;
     const unsigned f = (sh <= 8) ? (vc[w] >> sh) : __builtin_amdgcn_alignbit(vc[w + 1], vc[w], sh);
-    x = hi16_or((f >> 12) & 0xfffu, f & 0xfffu);
+    return hi16_or((f >> 12) & 0xfffu, f & 0xfffu);
   }
+}
+
+template <int VB>
+__device__ __forceinline__ half8 value_operand(const unsigned* vc, int i) {
+  const unsigned x = value_run<VB>(vc, i);
   // Field cc sits at bit VB*cc of each half.  Fields that end inside the
   // float16 mantissa (bits 0..9) are used in place with a matching exponent;
   // the others are shifted down by 8 first.
@@ -256,6 +269,31 @@ __device__ __forceinline__ half8 value_operand(const unsigned* vc, int i) {
   return as_h8(r);
 }
 
+// Value-codebook table of MSE-coded values: entry code_a | code_b << VB holds the
+// float16 pair (cv[code_a], cv[code_b]), in `copies` adjacent copies so that the
+// code-indexed reads of a wave spread over the LDS banks (2, 4 or 8 KB).
+template <int VB>
+struct ValLut {
+  static constexpr int entries = 1 << (2 * VB);
+  static constexpr int copies = VB == 2 ? 32 : VB == 3 ? 16 : 8;
+  static constexpr int words = entries * copies;
+};
+
+// A operand of the P.V product for tile i with MSE-coded values: element pair cc
+// = (token cc, token cc + 4) of the run, both codebook values from one lookup.
+template <int VB>
+__device__ __forceinline__ half8 value_operand_mse(const unsigned* vc, int i, const unsigned* vlut, unsigned vcopy) {
+  const unsigned x = value_run<VB>(vc, i);
+  constexpr unsigned m = (1u << VB) - 1u;
+  u32x4 r;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const unsigned idx = ((x >> (VB * cc)) & m) | (((x >> (16 + VB * cc)) & m) << VB);
+    r[cc] = vlut[idx * ValLut<VB>::copies + vcopy];
+  }
+  return as_h8(r);
+}
+
 // P.V operand slot of (page pg, in-page token t): the inverse of value_operand's
 // element order (slot 8kg + j holds page kg/2, token 8(kg%2) + j/2 + 4(j%2)).
 __device__ __forceinline__ int pv_slot(int pg, int t) {
@@ -264,14 +302,16 @@ __device__ __forceinline__ int pv_slot(int pg, int t) {
 
 // Byte layout of one (block, head) page; the host checks that it matches the
 // store layout before launching.
-template <int KB, int VB>
+// MSEV: the last field is Vn [16] fp16 (the values' norms) instead of the
+// groups' scale and zero.
+template <int KB, int VB, bool MSEV>
 struct PageLayout {
   static constexpr int kc = 0;
   static constexpr int ks = 256 * KB;
   static constexpr int kn = ks + 256;
   static constexpr int vc = kn + 64;
   static constexpr int vsz = vc + 256 * VB;
-  static constexpr int bytes = vsz + 256;
+  static constexpr int bytes = vsz + (MSEV ? 32 : 256);
 };
 
 // Dword-aligned vector types for the global loads.
@@ -282,12 +322,13 @@ typedef unsigned u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 // One lane's share of one 32-token chunk (pages 0 and 1), loaded from the pool
 // straight into registers: every field is stored so that this share is one
 // contiguous read per field.
-template <int KB, int VB>
+template <int KB, int VB, bool MSEV>
 struct Chunk {
   unsigned kc[2][KB];   // key codes of 32-dim block kg of token col
   unsigned ks[2];       // their sign bits
   unsigned kn[2];       // float16 n, gamma of token col
-  u32x4 sz[2];          // float16 scale, zero of token col's 4 groups
+  u32x4 sz[2];          // float16 scale, zero of token col's 4 groups (group-coded values)
+  unsigned vn[2];       // float16 value norm of token col (MSE-coded values)
   unsigned vc[2 * VB];  // value-code runs of lane block 16(kg%2) + col of page kg/2
 };
 
@@ -295,17 +336,17 @@ struct Chunk {
 struct LaneOffsets {
   unsigned kc, ks, kn, sz, vc;
 };
-template <int KB, int VB>
+template <int KB, int VB, bool MSEV>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
-  using PL = PageLayout<KB, VB>;
+  using PL = PageLayout<KB, VB, MSEV>;
   const unsigned col = lane & 15, kg = lane >> 4;
   return LaneOffsets{PL::kc + static_cast<unsigned>(lane) * (4 * KB), PL::ks + 4u * lane, PL::kn + 4u * col,
-                     PL::vsz + 16u * col, PL::vc + (16u * (kg & 1u) + col) * (8 * VB)};
+                     PL::vsz + (MSEV ? 2u : 16u) * col, PL::vc + (16u * (kg & 1u) + col) * (8 * VB)};
 }
 
 // Loads of one lane: a page base common to the wave plus a 32-bit lane offset.
-template <int KB, int VB>
-__device__ __forceinline__ void load_chunk(Chunk<KB, VB>& c, const unsigned char* p0, const unsigned char* p1,
+template <int KB, int VB, bool MSEV>
+__device__ __forceinline__ void load_chunk(Chunk<KB, VB, MSEV>& c, const unsigned char* p0, const unsigned char* p1,
                                            const LaneOffsets& o, bool second_page_values) {
   const unsigned char* pg[2] = {p0, p1};
 #pragma unroll
@@ -325,7 +366,10 @@ __device__ __forceinline__ void load_chunk(Chunk<KB, VB>& c, const unsigned char
     }
     c.ks[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.ks);
     c.kn[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.kn);
-    c.sz[t] = *reinterpret_cast<const u32x4*>(pg[t] + o.sz);
+    if constexpr (MSEV)
+      c.vn[t] = *reinterpret_cast<const unsigned short*>(pg[t] + o.sz);
+    else
+      c.sz[t] = *reinterpret_cast<const u32x4*>(pg[t] + o.sz);
   }
   const unsigned char* vp = (second_page_values ? p1 : p0) + o.vc;
   if constexpr (VB == 4) {
@@ -416,10 +460,12 @@ __device__ __forceinline__ void fold_scores(const floatx4& acc1, const floatx4& 
 constexpr int kRing = 2;
 
 // The block table comes as its own read-only, non-aliased parameter.
-template <int NREP, int KB, int VB>
+// MSEV: values coded like the keys' codebook part (norm + value codebook).
+template <int NREP, int KB, int VB, bool MSEV>
 __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int* __restrict__ btab) {
   using SM = ScoreMap<NREP>;
   using KL = KeyLut<KB>;
+  using VL = ValLut<VB>;
   constexpr int HPL = SM::HPL;
   constexpr int NSET = NREP == 8 ? 2 : 1;
   constexpr int WC = 2 * NREP;  // used P.V columns (hi, lo per head)
@@ -428,7 +474,8 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   const int start = split * a.split_tokens;
 
   __shared__ __attribute__((aligned(16))) unsigned char lut[256 * kLutEntry];
-  __shared__ __attribute__((aligned(16))) unsigned short wl[4][4][WC][32];  // P.V weights (float16)
+  __shared__ __attribute__((aligned(16))) unsigned short wl[4][MSEV ? 1 : 4][WC][32];  // P.V weights (float16)
+  __shared__ unsigned vlut[MSEV ? VL::words : 1];  // value-codebook pairs (MSE-coded values)
   __shared__ __attribute__((aligned(16))) unsigned zero16[4];
   __shared__ float mg_m[4][NREP], mg_l[4][NREP];
   __shared__ float mg_z[4][NREP][4];
@@ -477,34 +524,45 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     return;
   }
   const int end = min(T, start + a.split_tokens);
-  const LaneOffsets lofs = lane_offsets<KB, VB>(lane);
+  const LaneOffsets lofs = lane_offsets<KB, VB, MSEV>(lane);
   const int span = end - start - 32 * wave;
   const int nch = span > 0 ? (span + 127) / 128 : 0;  // chunks of this wave
-  auto load = [&](Chunk<KB, VB>& c, int j) {
+  auto load = [&](Chunk<KB, VB, MSEV>& c, int j) {
     const int c0 = start + 32 * (wave + 4 * j);
     // A wave with no chunk in the context (its first chunk starts at or past
     // the end) still issues the ring's loads, from block 0 (the pool holds at
     // least one block), so that no table entry past the context is used.
     const int b0 = nch > 0 ? __builtin_amdgcn_readlane(ids, 2 * j) : 0;
     const int b1 = (nch > 0 && c0 + 16 < end) ? __builtin_amdgcn_readlane(ids, 2 * j + 1) : b0;
-    load_chunk<KB, VB>(c, page_ptr(b0), page_ptr(b1), lofs, kg >= 2);
+    load_chunk<KB, VB, MSEV>(c, page_ptr(b0), page_ptr(b1), lofs, kg >= 2);
   };
   // Every step loads one chunk (past the wave's last chunk, the last one again:
   // a few cached re-reads) so that the number of loads in flight is the same on
   // every path, and each wait leaves the younger chunks' loads outstanding.
   const int jmax = nch > 0 ? nch - 1 : 0;
-  Chunk<KB, VB> ring[kRing];
+  Chunk<KB, VB, MSEV> ring[kRing];
 #pragma unroll
   for (int r = 0; r < kRing; ++r) load(ring[r], r < jmax ? r : jmax);
 
   // ---- tables (lane copies); the codebook is staged in LDS from scalar
   //      registers so that no vector load joins the chunk loads in flight
-  __shared__ unsigned short cent_h[16];
+  __shared__ unsigned short cent_h[16], vcent_h[16];
   if (tid == 0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) cent_h[e] = static_cast<unsigned short>(h_bits(a.cent[e]));
+    if constexpr (MSEV) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vcent_h[e] = static_cast<unsigned short>(h_bits(a.vcent[e]));
+    }
   }
   __syncthreads();
+  if constexpr (MSEV) {
+    constexpr unsigned m = (1u << VB) - 1u;
+    for (int x = tid; x < VL::words; x += 256) {
+      const unsigned e = static_cast<unsigned>(x / VL::copies);
+      vlut[x] = vcent_h[e & m] | (static_cast<unsigned>(vcent_h[e >> VB]) << 16);
+    }
+  }
   {
     // lane tid fills entry tid of both tables, all copies (16-byte stores)
     const int e = tid;
@@ -559,7 +617,8 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   const float sc = a.scale * kInvSqrtD;
   const int slot0 = pv_slot(0, col);
 
-  auto process = [&](const Chunk<KB, VB>& c, int c0) {
+  const unsigned vcopy = static_cast<unsigned>(lane % VL::copies);
+  auto process = [&](const Chunk<KB, VB, MSEV>& c, int c0) {
     // ---- scores: one 16-token tile per page
     float s[2][HPL];
 #pragma unroll
@@ -625,6 +684,38 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     //      pv_slot(page, col)); offset term p (zero + mid scale) on the VALU.
     //      Past the context end (slots never written may hold any bits) the
     //      scale and zero are taken as 0, so that p = 0 gives exact zeros.
+    if constexpr (MSEV) {
+      // w = p * nv16 / sqrt(d), the same for every group (no offset term); a
+      // never-written slot past the context end gets the norm 0
+      float nv[2] = {h_lo(c.vn[0]) * kInvSqrtD, h_lo(c.vn[1]) * kInvSqrtD};
+      if (c0 + 32 > end) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (c0 + 16 * t + col >= end) nv[t] = 0.0f;
+      }
+      if (active) {
+#pragma unroll
+        for (int hs = 0; hs < HPL; ++hs) {
+          const int h = SM::head(kg, hs);
+          const float w0 = p[0][hs] * nv[0], w1 = p[1][hs] * nv[1];
+          const _Float16 hi0 = static_cast<_Float16>(w0), hi1 = static_cast<_Float16>(w1);
+          const _Float16 lo0 = static_cast<_Float16>(fmaf(p[0][hs], nv[0], -static_cast<float>(hi0)));
+          const _Float16 lo1 = static_cast<_Float16>(fmaf(p[1][hs], nv[1], -static_cast<float>(hi1)));
+          unsigned short* wh = &wl[wave][0][h][0];
+          unsigned short* wo = &wl[wave][0][NREP + h][0];
+          wh[slot0] = __builtin_bit_cast(unsigned short, hi0);
+          wh[slot0 + 16] = __builtin_bit_cast(unsigned short, hi1);
+          wo[slot0] = __builtin_bit_cast(unsigned short, lo0);
+          wo[slot0 + 16] = __builtin_bit_cast(unsigned short, lo1);
+        }
+      }
+      const u32x4* wsrc = (col < WC) ? reinterpret_cast<const u32x4*>(&wl[wave][0][col][8 * kg])
+                                     : reinterpret_cast<const u32x4*>(zero16);
+      const half8 w = as_h8(*wsrc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) accv[i] = mfma(value_operand_mse<VB>(c.vc, i, vlut, vcopy), w, accv[i]);
+      return;
+    }
     u32x4 sz[2] = {c.sz[0], c.sz[1]};
     if (c0 + 32 > end) {
 #pragma unroll
@@ -741,24 +832,28 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   }
 }
 
-template <int NREP, int KB>
+template <int NREP, int KB, bool MSEV>
 void* pick_vb(int vb) {
   switch (vb) {
-    case 2: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 2>);
-    case 3: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 3>);
-    case 4: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 4>);
+    case 2: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 2, MSEV>);
+    case 3: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 3, MSEV>);
+    case 4: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 4, MSEV>);
+  }
+  return nullptr;
+}
+template <int NREP, bool MSEV>
+void* pick_kb(int kb, int vb) {
+  switch (kb) {
+    case 1: return pick_vb<NREP, 1, MSEV>(vb);
+    case 2: return pick_vb<NREP, 2, MSEV>(vb);
+    case 3: return pick_vb<NREP, 3, MSEV>(vb);
+    case 4: return pick_vb<NREP, 4, MSEV>(vb);
   }
   return nullptr;
 }
 template <int NREP>
-void* pick_kb(int kb, int vb) {
-  switch (kb) {
-    case 1: return pick_vb<NREP, 1>(vb);
-    case 2: return pick_vb<NREP, 2>(vb);
-    case 3: return pick_vb<NREP, 3>(vb);
-    case 4: return pick_vb<NREP, 4>(vb);
-  }
-  return nullptr;
+void* pick_mode(bool msev, int kb, int vb) {
+  return msev ? pick_kb<NREP, true>(kb, vb) : pick_kb<NREP, false>(kb, vb);
 }
 
 }  // namespace
@@ -768,9 +863,10 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
                            float* part, void* stream) {
   {
     const unsigned kb = L->cfg.k_bits, vb = L->cfg.v_bits;
+    const unsigned last = L->cfg.value_mode == TQ_VAL_MSE ? 32 : 256;
     const tq::Layout& ly = L->lay;
     if (ly.off_kc != 0 || ly.off_ks != 256 * kb || ly.off_kn != 256 * kb + 256 || ly.off_vc != 256 * kb + 320 ||
-        ly.off_vsz != 256 * (kb + vb) + 320 || ly.block_bytes != 256 * (kb + vb) + 576)
+        ly.off_vsz != 256 * (kb + vb) + 320 || ly.block_bytes != 256 * (kb + vb) + 320 + last)
       return fail(TQ_ERR_UNSUPPORTED, "store layout does not match the decode kernels' page layout");
   }
   MainArgs a;
@@ -785,13 +881,17 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
   a.split_tokens = plan.split_tokens;
   a.scale = softmax_scale;
   a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
-  for (int i = 0; i < 16; ++i) a.cent[i] = L->centroids[i];
+  for (int i = 0; i < 16; ++i) {
+    a.cent[i] = L->centroids[i];
+    a.vcent[i] = L->v_centroids[i];
+  }
+  const bool msev = L->cfg.value_mode == TQ_VAL_MSE;
   void* fn = nullptr;
   switch (plan.rep) {
-    case 1: fn = pick_kb<1>(L->cfg.k_bits, L->cfg.v_bits); break;
-    case 2: fn = pick_kb<2>(L->cfg.k_bits, L->cfg.v_bits); break;
-    case 4: fn = pick_kb<4>(L->cfg.k_bits, L->cfg.v_bits); break;
-    case 8: fn = pick_kb<8>(L->cfg.k_bits, L->cfg.v_bits); break;
+    case 1: fn = pick_mode<1>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 2: fn = pick_mode<2>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 4: fn = pick_mode<4>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 8: fn = pick_mode<8>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
   }
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for rep=%d k_bits=%d v_bits=%d", plan.rep,
                        L->cfg.k_bits, L->cfg.v_bits);

@@ -79,9 +79,10 @@ def _edge_rows(st, n_heads, kind):
     return K, V
 
 
-@pytest.mark.parametrize("path,rotation", [("mfma-pages", 0), ("mfma-pages", 1), ("mfma-scattered", 1),
-                                           ("per-token-bf16", 0), ("per-token-bf16", 1), ("per-token-f32", 1)])
-def test_compress_edge_cases(path, rotation):
+@pytest.mark.parametrize("path,rotation,value_mode", [
+    ("mfma-pages", 0, 0), ("mfma-pages", 1, 0), ("mfma-scattered", 1, 0), ("per-token-bf16", 0, 0),
+    ("per-token-bf16", 1, 0), ("per-token-f32", 1, 0), ("mfma-pages", 1, 1), ("per-token-f32", 0, 1)])
+def test_compress_edge_cases(path, rotation, value_mode):
     """Zero keys and values, keys with a subnormal squared norm, values whose float16
     scale is 0, coordinates exactly on the middle decision boundary and constant
     value groups, mixed with ordinary rows, through each compressor (the
@@ -106,9 +107,17 @@ def test_compress_edge_cases(path, rotation):
         slots = np.arange(n, dtype=np.int64)
     else:
         slots = np.random.default_rng(292).permutation(nb * 16)[:n].astype(np.int64)
-    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, seed, layer=1, dtype=dtype, rotation=rotation)
-    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, H, kb, vb, seed, layer=1, rotation_kind=rot)
+    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, seed, layer=1, dtype=dtype, rotation=rotation,
+                        value_mode=value_mode)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, H, kb, vb, seed, layer=1, rotation_kind=rot,
+                                                value_mode="mse" if value_mode else "group")
     _check_compress(gpu, res, st, layout, H, slots, V, kb, vb, pool=False)
+    if value_mode:
+        for h in range(H):
+            f = parity.fields_at(gpu, layout, H, slots[:32], h)
+            assert not f["n16"].astype(np.float64).any() and not f["vn16"].astype(np.float64).any()
+            assert np.all(f["idx"][:16] == (1 << kb) // 2 - 1) and np.all(f["vcode"][:16] == (1 << vb) // 2 - 1)
+        return
     # the special rows as the method defines them (read from the GPU's store)
     for h in range(H):
         f = parity.fields_at(gpu, layout, H, slots[:16 * len(kinds)], h)
@@ -241,14 +250,16 @@ def test_compress_bits_ragged_slots(kb, vb):
         assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
 
-@pytest.mark.parametrize("kb,vb,n,dtype,key_mode,rotation", [
-    (2, 3, 301, "bf16", 0, 0), (4, 4, 500, "bf16", 0, 0), (3, 2, 200, "f32", 0, 0), (2, 3, 2003, "bf16", 0, 0),
-    (3, 3, 300, "bf16", 2, 1)])
-def test_compress_mse_values(kb, vb, n, dtype, key_mode, rotation):
+@pytest.mark.parametrize("kb,vb,n,dtype,key_mode,rotation,pages", [
+    (2, 3, 301, "bf16", 0, 0, False), (4, 4, 500, "bf16", 0, 0, False), (3, 2, 200, "f32", 0, 0, False),
+    (2, 3, 2003, "bf16", 0, 0, False), (3, 3, 300, "bf16", 2, 1, False), (2, 3, 1024, "bf16", 0, 0, True),
+    (1, 4, 777, "bf16", 1, 1, True), (2, 2, 40, "bf16", 0, 0, False)])
+def test_compress_mse_values(kb, vb, n, dtype, key_mode, rotation, pages):
     """Values coded like the keys' codebook part (the 102-byte record at K2/V3): 8
-    heads with outlier channels, shuffled slots with skipped tokens, bf16 (more
-    than 64 tokens, which the matrix-core compressor would otherwise take) and
-    fp32; and together with norm-corrected keys and the Hadamard rotation. Codes as
+    heads with outlier channels; bf16 runs of 64+ tokens through the matrix-core
+    compressor, on whole pages (identity slots) and on shuffled slots with skipped
+    tokens; fp32 inputs and a 40-token append through the per-token compressor;
+    together with norm-corrected or plain keys and the Hadamard rotation.  Codes as
     the keys' protocol, the value norm within an fp16 ulp, slots nobody wrote
     untouched."""
     torch = _torch()
@@ -256,8 +267,11 @@ def test_compress_mse_values(kb, vb, n, dtype, key_mode, rotation):
     K, V = synth.kv_host(340 + kb * 10 + vb, n, 8, outliers=4, dtype=dtype)
     rng = np.random.default_rng(340 + kb)
     nb = max(40, (n + 15) // 16 + 4)  # 2003 tokens: 16 per workgroup, a ragged last run
-    slots = rng.permutation(nb * 16)[:n].astype(np.int64)
-    slots[rng.choice(n, 15, replace=False)] = -1
+    if pages:
+        slots = np.arange(n, dtype=np.int64)
+    else:
+        slots = rng.permutation(nb * 16)[:n].astype(np.int64)
+        slots[rng.choice(n, min(15, n // 3), replace=False)] = -1
     gpu = _gpu_compress(torch, K, V, slots, nb, 8, kb, vb, 341, layer=kb, dtype=dtype, key_mode=key_mode,
                         rotation=rotation, value_mode=tq.VAL_MSE)
     st, layout, pool, res = parity.oracle_store(K, V, slots, nb, 8, kb, vb, 341, layer=kb, value_mode="mse",
@@ -271,25 +285,41 @@ def test_compress_mse_values(kb, vb, n, dtype, key_mode, rotation):
             assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
 
 
-def test_mse_value_layers_refuse_decode():
-    """Decode of MSE-value layers is not built: it returns TQ_ERR_UNSUPPORTED
-    before any launch (no silent fallback)."""
+@pytest.mark.parametrize("kb,vb,rep,splits", [(2, 3, 4, 0), (4, 4, 8, 0), (3, 2, 1, 3), (1, 3, 2, 64),
+                                               (4, 3, 4, 1)])
+def test_decode_mse_values(kb, vb, rep, splits):
+    """Decode over stores with MSE-coded values (norm + value codebook; the 102-byte
+    record at K2/V3): ragged lengths, random block tables, GQA 1/2/4/8, forced splits,
+    float32 and bf16 output, against the oracle on the same store."""
     torch = _torch()
-    say("mse values: decode refused")
-    layer = tq.Layer(tq.config(2, 2, 3, seed=5, value_mode=tq.VAL_MSE))
-    pool = layer.new_pool(4)
-    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
-    bt = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
-    sl = torch.full((1,), 16, dtype=torch.int32, device="cuda")
-    out = torch.zeros((1, 8, 128), device="cuda")
-    ws = tq.new_workspace(layer, 1, 8, 64)
-    st = tq.lib().tq_decode_attn(layer.handle, tq._ptr(q), tq._dtype_code(q), 1, 8, tq._ptr(pool), 4,
-                                 tq._ptr(bt), 4, tq._ptr(sl), 64, 0.0, 0, tq._ptr(out), tq._dtype_code(out),
-                                 tq._ptr(ws), ws.numel(), tq._stream(None))
-    assert st == tq.ERR_UNSUPPORTED and b"MSE" in tq.lib().tq_last_error()
-    torch.cuda.synchronize()
-    assert not out.any()
-    layer.close()
+    say("decode mse values", kb, vb, rep, splits)
+    Hkv = 4
+    _decode_case(torch, 4, Hkv * rep, Hkv, [700, 1, 129, 2050], kb, vb, 360 + kb, num_splits=splits,
+                 value_mode=tq.VAL_MSE)
+
+
+def test_decode_mse_values_unwritten_slots():
+    """MSE-value pools filled with 0xFF before the records are written: the slots
+    past each context end hold NaN norms, which must not reach the output."""
+    torch = _torch()
+    say("decode mse values, unwritten slots")
+    _decode_case(torch, 5, 8, 2, [1, 17, 40, 129, 1000], 2, 3, 371, fill=0xFF, value_mode=tq.VAL_MSE)
+
+
+def test_end_to_end_mse_values():
+    """The pages' 102-byte format (2-bit keys + QJL, 3-bit MSE values): GPU compress ->
+    GPU decode against oracle compress -> oracle decode."""
+    torch = _torch()
+    say("end to end mse values K2/V3")
+    B, Hq, Hkv, T = 3, 32, 8, 700
+    lens = np.array([T, 300, 64], np.int32)
+    maxb = (T + 15) // 16
+    table = synth.block_table(372, B, maxb, "random")
+    K, V = synth.kv_host(373, B * T, Hkv, outliers=4)
+    pos = np.tile(np.arange(T), B)
+    seq = np.repeat(np.arange(B), T)
+    slots = table[seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, 2, 3, 372, value_mode=tq.VAL_MSE, label="mse K2/V3")
 
 
 @pytest.mark.parametrize("kb,vb,out_dtype", [(2, 3, "f32"), (4, 4, "bf16"), (3, 2, "f32")])
@@ -418,7 +448,7 @@ def _gpu_decode(torch, layer_cfg, pool_np, q, table, lens, max_len, out_dtype="f
 
 def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_dtype="bf16",
                  outliers=4, out_dtypes=("f32", "bf16"), num_splits=0, scale=0.0, layer=0, bypass=False,
-                 fill=0):
+                 fill=0, value_mode=0):
     lens = np.asarray(lens, dtype=np.int32)
     maxb = max(1, (int(lens.max()) + 15) // 16)
     table = synth.block_table(seed, B, maxb, table_kind)
@@ -440,11 +470,11 @@ def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_d
                                                   fill=fill)
     else:
         st, layout, pool, _ = parity.oracle_store(K, V, slots, nblk, Hkv, kb, vb, seed, layer=layer, keep=False,
-                                                  fill=fill)
+                                                  fill=fill, value_mode="mse" if value_mode else "group")
     q = synth.queries_host(seed, B, Hq, dtype=q_dtype)
     ref = parity.oracle_decode(q.astype(np.float64), pool, layout, Hkv, table, lens, st,
                                scale=scale if scale else None)
-    cfg = tq.config(Hkv, kb, vb, seed=seed, layer=layer, bypass=bypass)
+    cfg = tq.config(Hkv, kb, vb, seed=seed, layer=layer, bypass=bypass, value_mode=value_mode)
     results = {}
     for od in out_dtypes:
         got = _gpu_decode(torch, cfg, pool, q, table, lens, int(lens.max()), od, num_splits, scale,
@@ -593,7 +623,8 @@ def test_decode_ragged_serving_sampled():
         parity.assert_decode_ok(got[sample], ref[sample], "f32", "ragged serving %d/%d" % (kb, vb))
 
 
-def _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, kb, vb, seed, key_mode=0, rotation=0, label=""):
+def _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, kb, vb, seed, key_mode=0, rotation=0, label="",
+                value_mode=0):
     """GPU compress, then: the GPU store against the oracle's (compress protocol);
     GPU decode of the GPU store against the oracle decode of the same store, and
     of the oracle store likewise (decode protocol, whole output and worst row);
@@ -604,10 +635,11 @@ def _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, kb, vb, seed, key_mode
     nblk = table.size
     rot = "haar" if rotation == tq.ROT_HAAR else "hadamard"
     st, layout, opool, res = parity.oracle_store(K, V, slots, nblk, Hkv, kb, vb, seed,
-                                                 key_mode=KEY_MODE_NAMES[key_mode], rotation_kind=rot)
+                                                 key_mode=KEY_MODE_NAMES[key_mode], rotation_kind=rot,
+                                                 value_mode="mse" if value_mode else "group")
     q = synth.queries_host(seed, B, Hq)
     ref = parity.oracle_decode(q.astype(np.float64), opool, layout, Hkv, table, lens, st)
-    layer = tq.Layer(tq.config(Hkv, kb, vb, seed=seed, key_mode=key_mode, rotation=rotation))
+    layer = tq.Layer(tq.config(Hkv, kb, vb, seed=seed, key_mode=key_mode, rotation=rotation, value_mode=value_mode))
     pool = layer.new_pool(nblk)
     tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
                    torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
