@@ -424,14 +424,14 @@ def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
     ms = e0.elapsed_time(e1) / args.compress_iters
     c_ms, c_n = tq.profile_read(tq.K_COMPRESS)
     tq.profile_enable(0)
-    rec = W["k_bits"] * 16 + 20 + W["v_bits"] * 16 + 16
+    rec = layer.block_bytes // 16  # per token-head; the key modes without QJL store no sign field
     nbytes = N * H * (512 + rec) + N * 8
     avg_s = c_ms / max(c_n, 1) / 1e3
     layer.close()
     del k, v, pool
     if key_mode or rotation:
         return {"workload": W["name"], "key_mode": ["qjl", "mse", "mse_nc"][key_mode],
-                "rotation": ["haar", "hadamard"][rotation], "ms": round(ms, 4),
+                "rotation": ["haar", "hadamard"][rotation], "record_bytes": rec, "ms": round(ms, 4),
                 "mtok_s": round(N / (ms / 1e3) / 1e6, 2), "gbs": round(nbytes / avg_s / 1e9, 1),
                 "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
     return {"workload": W["name"], "tokens": N, "kv_heads": H, "k_bits": W["k_bits"], "v_bits": W["v_bits"],

@@ -71,8 +71,10 @@ tq_status make_layout(const tq_layer_config* cfg, Layout* out) {
   l.k_bits = cfg->k_bits;
   l.v_bits = cfg->v_bits;
   l.kc_bytes = kDim * cfg->k_bits / 8;
-  l.ks_bytes = kDim / 8;
-  l.kn_bytes = 4;
+  // key modes without QJL: no sign field and no gamma, the magnitude alone
+  const bool qjl = cfg->key_mode == TQ_KEY_QJL;
+  l.ks_bytes = qjl ? kDim / 8 : 0;
+  l.kn_bytes = qjl ? 4 : 2;
   l.vc_bytes = kDim * cfg->v_bits / 8;
   // last field: per-group fp16 scale/zero, or one fp16 norm with MSE values
   l.vsz_bytes = cfg->value_mode == TQ_VAL_MSE ? 2 : 4 * (kDim / kGroup);

@@ -235,17 +235,22 @@ __global__ __launch_bounds__(512) void compress_kernel(CompressArgs a) {
     // word i of the 128-code key stream lies in 32-dim block i / KB
     const int blk = i / KB, wi = i % KB;
     reinterpret_cast<unsigned*>(base + a.off_kc + (blk * 16 + off) * (4 * KB))[wi] = pack_word<KB>(ck, i);
-  } else if (i >= 64 && i < 68) {
+  } else if (a.km == 0 && i >= 64 && i < 68) {
     const int blk = i - 64;
     *reinterpret_cast<unsigned*>(base + a.off_ks + (blk * 16 + off) * 4) = sbits[blk];
   } else if (i == 68) {
     const float g2 = red[2] + red[3];
-    // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction; gamma 0 without QJL
+    // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction; with
+    // QJL the pair (n, gamma), without QJL the magnitude alone (no sign field)
     const __half hn = __float2half_rn(a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n);
-    const __half hg = __float2half_rn(a.km == 0 ? sqrtf(g2) : 0.0f);
-    const unsigned w = static_cast<unsigned>(__half_as_ushort(hn)) |
-                       (static_cast<unsigned>(__half_as_ushort(hg)) << 16);
-    *reinterpret_cast<unsigned*>(base + a.off_kn + off * 4) = w;
+    if (a.km == 0) {
+      const __half hg = __float2half_rn(sqrtf(g2));
+      const unsigned w = static_cast<unsigned>(__half_as_ushort(hn)) |
+                         (static_cast<unsigned>(__half_as_ushort(hg)) << 16);
+      *reinterpret_cast<unsigned*>(base + a.off_kn + off * 4) = w;
+    } else {
+      *reinterpret_cast<unsigned short*>(base + a.off_kn + off * 2) = __half_as_ushort(hn);
+    }
   } else if (a.vm == 1 && i == 72) {
     // the token's fp16 value norm (two bytes of its own)
     *reinterpret_cast<unsigned short*>(base + a.off_vsz + off * 2) = __half_as_ushort(sgroup[0]);

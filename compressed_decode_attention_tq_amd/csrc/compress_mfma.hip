@@ -165,13 +165,14 @@ __device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
 }
 
 // Page image offsets (same format as the store; MSEV: the last field is Vn
-// [16] fp16 instead of the groups' scale and zero).
-template <int KB, int VB, bool MSEV>
+// [16] fp16 instead of the groups' scale and zero; without QJL there is no sign
+// field and Kn holds the magnitude alone, [16] fp16).
+template <int KB, int VB, bool MSEV, bool QJL>
 struct Page {
   static constexpr int kc = 0;
   static constexpr int ks = 256 * KB;
-  static constexpr int kn = ks + 256;
-  static constexpr int vc = kn + 64;
+  static constexpr int kn = ks + (QJL ? 256 : 0);
+  static constexpr int vc = kn + (QJL ? 64 : 32);
   static constexpr int vsz = vc + 256 * VB;
   static constexpr int bytes = vsz + (MSEV ? 32 : 256);
 };
@@ -236,7 +237,7 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // MSEV: values coded like the keys' codebook part (value norm + value codebook).
 template <int KB, int VB, int P, bool HAD, bool QJL, bool MSEV>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 : 8))) void compress_mfma_kernel(CArgs a, const long long* __restrict__ slots) {
-  using PG = Page<KB, VB, MSEV>;
+  using PG = Page<KB, VB, MSEV, QJL>;
   constexpr int HALF = 1 << (KB - 1);  // codebook levels per sign
   constexpr float kTop = static_cast<float>((1 << VB) - 1);
   constexpr int kChunks = PG::bytes / 16;  // 16-byte chunks of a page (at most 164 = 8 waves x 21 lanes)
@@ -513,10 +514,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
 #pragma unroll
         for (int r = 0; r < 4; ++r) nib |= (Y[r] >= 0.0f ? 1u : 0u) << r;
       }
-      unsigned ea = nib, eb = nib;
-      swap16u(ea, eb);  // even row groups: ea = own, eb = the next group's nibble
-      if ((kg & 1) == 0)
-        img[PG::ks + ((w >> 1) * 16 + col) * 4 + 2 * (w & 1) + (kg >> 1)] = static_cast<unsigned char>(ea | (eb << 4));
+      if constexpr (QJL) {
+        unsigned ea = nib, eb = nib;
+        swap16u(ea, eb);  // even row groups: ea = own, eb = the next group's nibble
+        if ((kg & 1) == 0)
+          img[PG::ks + ((w >> 1) * 16 + col) * 4 + 2 * (w & 1) + (kg >> 1)] = static_cast<unsigned char>(ea | (eb << 4));
+      }
 
       unsigned x0, x1, x2, x3;
       __half s16, z16;
@@ -603,13 +606,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
         float g2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) g2 += gpart[i][col];
-        // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction; gamma 0 without QJL
+        // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction;
+        // with QJL the pair (n, gamma), without QJL the magnitude alone
         const float n = sqrtf(k2);
-        const unsigned short g16 = __half_as_ushort(__float2half_rn(QJL ? sqrtf(g2) : 0.0f));
         const unsigned short n16 =
             __half_as_ushort(__float2half_rn(!QJL && a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n));
-        *reinterpret_cast<unsigned*>(&img[PG::kn + col * 4]) =
-            static_cast<unsigned>(n16) | (static_cast<unsigned>(g16) << 16);
+        if constexpr (QJL) {
+          const unsigned short g16 = __half_as_ushort(__float2half_rn(sqrtf(g2)));
+          *reinterpret_cast<unsigned*>(&img[PG::kn + col * 4]) =
+              static_cast<unsigned>(n16) | (static_cast<unsigned>(g16) << 16);
+        } else {
+          *reinterpret_cast<unsigned short*>(&img[PG::kn + col * 2]) = n16;
+        }
       }
     }
     __syncthreads();  // the page image is complete
@@ -638,19 +646,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
           const int b = f / KB, i = f % KB;
           reinterpret_cast<unsigned*>(page + PG::kc + (b * 16 + o) * 4 * KB)[i] =
               reinterpret_cast<const unsigned*>(&img[PG::kc + (b * 16 + t) * 4 * KB])[i];
-        } else if (f < 4 * KB + 4) {
-          const int b = f - 4 * KB;
-          *reinterpret_cast<unsigned*>(page + PG::ks + (b * 16 + o) * 4) =
-              *reinterpret_cast<const unsigned*>(&img[PG::ks + (b * 16 + t) * 4]);
+        } else if (f < 4 * KB + 4) {  // sign words (none without QJL)
+          if constexpr (QJL) {
+            const int b = f - 4 * KB;
+            *reinterpret_cast<unsigned*>(page + PG::ks + (b * 16 + o) * 4) =
+                *reinterpret_cast<const unsigned*>(&img[PG::ks + (b * 16 + t) * 4]);
+          }
         } else if (f == 4 * KB + 4) {
-          *reinterpret_cast<unsigned*>(page + PG::kn + o * 4) = *reinterpret_cast<const unsigned*>(&img[PG::kn + t * 4]);
-        } else if (MSEV && f == 4 * KB + 5) {
-          *reinterpret_cast<unsigned short*>(page + PG::vsz + o * 2) =
-              *reinterpret_cast<const unsigned short*>(&img[PG::vsz + t * 2]);
-        } else if (!MSEV && f < 4 * KB + 9) {
+          if constexpr (QJL)
+            *reinterpret_cast<unsigned*>(page + PG::kn + o * 4) = *reinterpret_cast<const unsigned*>(&img[PG::kn + t * 4]);
+          else
+            *reinterpret_cast<unsigned short*>(page + PG::kn + o * 2) =
+                *reinterpret_cast<const unsigned short*>(&img[PG::kn + t * 2]);
+        } else if (f < 4 * KB + 9) {  // value metadata: word G of the token's record
           const int G = f - (4 * KB + 5);
-          reinterpret_cast<unsigned*>(page + PG::vsz + o * 16)[G] =
-              reinterpret_cast<const unsigned*>(&img[PG::vsz + t * 16])[G];
+          if constexpr (MSEV) {
+            if (G == 0)
+              *reinterpret_cast<unsigned short*>(page + PG::vsz + o * 2) =
+                  *reinterpret_cast<const unsigned short*>(&img[PG::vsz + t * 2]);
+          } else {
+            reinterpret_cast<unsigned*>(page + PG::vsz + o * 16)[G] =
+                reinterpret_cast<const unsigned*>(&img[PG::vsz + t * 16])[G];
+          }
         } else if (f >= 128 && f < 256) {
           const int d = f - 128;
           unsigned* vw = reinterpret_cast<unsigned*>(page + PG::vc);

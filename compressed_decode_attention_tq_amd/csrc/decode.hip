@@ -386,7 +386,9 @@ tq_status launch_decode(const tq_layer* L, const DecodePlan& plan, const void* q
     const u32x4* opq = reinterpret_cast<const u32x4*>(L->dOpQ);
     unsigned short* qa = reinterpret_cast<unsigned short*>(ws + plan.ws_qa);
     int B = plan.batch, Hq = plan.n_q_heads, rep = plan.rep;
-    float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / kDim);  // sqrt(pi/2) / m, m = d
+    // sqrt(pi/2) / m, m = d; 0 for the key modes without QJL, whose split-K
+    // kernels then see zero projection rows in the query operand
+    float kappa = L->cfg.key_mode == TQ_KEY_QJL ? static_cast<float>(std::sqrt(M_PI / 2.0) / kDim) : 0.0f;
     void* args[] = {const_cast<void**>(&q), &opq, &qa, &B, &Hq, &rep, &kappa};
     const int spg = 16 / rep;
     ProfScope prof(kKPrologue, stream);

@@ -303,13 +303,14 @@ __device__ __forceinline__ int pv_slot(int pg, int t) {
 // Byte layout of one (block, head) page; the host checks that it matches the
 // store layout before launching.
 // MSEV: the last field is Vn [16] fp16 (the values' norms) instead of the
-// groups' scale and zero.
-template <int KB, int VB, bool MSEV>
+// groups' scale and zero.  !QJL (key modes without residual signs): no sign
+// field, Kn [16] fp16 holds the magnitude alone.
+template <int KB, int VB, bool MSEV, bool QJL>
 struct PageLayout {
   static constexpr int kc = 0;
   static constexpr int ks = 256 * KB;
-  static constexpr int kn = ks + 256;
-  static constexpr int vc = kn + 64;
+  static constexpr int kn = ks + (QJL ? 256 : 0);
+  static constexpr int vc = kn + (QJL ? 64 : 32);
   static constexpr int vsz = vc + 256 * VB;
   static constexpr int bytes = vsz + (MSEV ? 32 : 256);
 };
@@ -336,16 +337,17 @@ struct Chunk {
 struct LaneOffsets {
   unsigned kc, ks, kn, sz, vc;
 };
-template <int KB, int VB, bool MSEV>
+template <int KB, int VB, bool MSEV, bool QJL>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
-  using PL = PageLayout<KB, VB, MSEV>;
+  using PL = PageLayout<KB, VB, MSEV, QJL>;
   const unsigned col = lane & 15, kg = lane >> 4;
-  return LaneOffsets{PL::kc + static_cast<unsigned>(lane) * (4 * KB), PL::ks + 4u * lane, PL::kn + 4u * col,
+  return LaneOffsets{PL::kc + static_cast<unsigned>(lane) * (4 * KB), PL::ks + 4u * lane,
+                     PL::kn + (QJL ? 4u : 2u) * col,
                      PL::vsz + (MSEV ? 2u : 16u) * col, PL::vc + (16u * (kg & 1u) + col) * (8 * VB)};
 }
 
 // Loads of one lane: a page base common to the wave plus a 32-bit lane offset.
-template <int KB, int VB, bool MSEV>
+template <int KB, int VB, bool MSEV, bool QJL>
 __device__ __forceinline__ void load_chunk(Chunk<KB, VB, MSEV>& c, const unsigned char* p0, const unsigned char* p1,
                                            const LaneOffsets& o, bool second_page_values) {
   const unsigned char* pg[2] = {p0, p1};
@@ -364,8 +366,12 @@ __device__ __forceinline__ void load_chunk(Chunk<KB, VB, MSEV>& c, const unsigne
       const u32x2a v = *reinterpret_cast<const u32x2a*>(kp);
       c.kc[t][0] = v[0]; c.kc[t][1] = v[1];
     }
-    c.ks[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.ks);
-    c.kn[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.kn);
+    if constexpr (QJL) {
+      c.ks[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.ks);
+      c.kn[t] = *reinterpret_cast<const unsigned*>(pg[t] + o.kn);
+    } else {  // the magnitude alone, in the low half (gamma taken as 0)
+      c.kn[t] = *reinterpret_cast<const unsigned short*>(pg[t] + o.kn);
+    }
     if constexpr (MSEV)
       c.vn[t] = *reinterpret_cast<const unsigned short*>(pg[t] + o.sz);
     else
@@ -419,10 +425,33 @@ struct ScoreMap {
 
 // Fold the Q.K accumulators of one 16-token tile into scores (before the
 // per-token factor alpha): acc1 = code steps, acc2 = sign steps, g = gamma.
-template <int NREP>
+// Without QJL (acc2 unused) the prologue has written zero projection rows, so
+// the rows that would hold kappa u contribute nothing to acc1 and need no mask.
+template <int NREP, bool QJL>
 __device__ __forceinline__ void fold_scores(const floatx4& acc1, const floatx4& acc2, float g, int kg,
                                             float (&out)[ScoreMap<NREP>::HPL]) {
-  if constexpr (NREP == 8) {
+  if constexpr (!QJL) {
+    if constexpr (NREP == 8) {
+      float x0 = acc1[0], x1 = acc1[1], x2 = acc1[2], x3 = acc1[3];
+      swap32(x0, x2);
+      swap32(x1, x3);
+      out[0] = x0 + x2;
+      out[1] = x1 + x3;
+    } else if constexpr (NREP == 4) {
+      float x0 = acc1[0], x1 = acc1[1], x2 = acc1[2], x3 = acc1[3];
+      swap32(x0, x2);
+      swap32(x1, x3);
+      float y0 = x0 + x2, y1 = x1 + x3;
+      swap16(y0, y1);
+      out[0] = y0 + y1;
+    } else if constexpr (NREP == 2) {
+      float x0 = acc1[0] + acc1[2], x1 = acc1[1] + acc1[3];
+      swap16(x0, x1);
+      out[0] = x0 + x1;
+    } else {
+      out[0] = acc1[0] + acc1[1];
+    }
+  } else if constexpr (NREP == 8) {
     // tile 1 (q') rows 0-7 hi, 8-15 lo; tile 2 (kappa u) the same; row group kg
     // holds rows 4kg..4kg+3 -> hi/lo halves are lanes l and l+32
     float x0 = fmaf(g, acc2[0], acc1[0]), x1 = fmaf(g, acc2[1], acc1[1]);
@@ -461,7 +490,7 @@ constexpr int kRing = 2;
 
 // The block table comes as its own read-only, non-aliased parameter.
 // MSEV: values coded like the keys' codebook part (norm + value codebook).
-template <int NREP, int KB, int VB, bool MSEV>
+template <int NREP, int KB, int VB, bool MSEV, bool QJL>
 __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int* __restrict__ btab) {
   using SM = ScoreMap<NREP>;
   using KL = KeyLut<KB>;
@@ -524,7 +553,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     return;
   }
   const int end = min(T, start + a.split_tokens);
-  const LaneOffsets lofs = lane_offsets<KB, VB, MSEV>(lane);
+  const LaneOffsets lofs = lane_offsets<KB, VB, MSEV, QJL>(lane);
   const int span = end - start - 32 * wave;
   const int nch = span > 0 ? (span + 127) / 128 : 0;  // chunks of this wave
   auto load = [&](Chunk<KB, VB, MSEV>& c, int j) {
@@ -534,7 +563,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     // least one block), so that no table entry past the context is used.
     const int b0 = nch > 0 ? __builtin_amdgcn_readlane(ids, 2 * j) : 0;
     const int b1 = (nch > 0 && c0 + 16 < end) ? __builtin_amdgcn_readlane(ids, 2 * j + 1) : b0;
-    load_chunk<KB, VB, MSEV>(c, page_ptr(b0), page_ptr(b1), lofs, kg >= 2);
+    load_chunk<KB, VB, MSEV, QJL>(c, page_ptr(b0), page_ptr(b1), lofs, kg >= 2);
   };
   // Every step loads one chunk (past the wave's last chunk, the last one again:
   // a few cached re-reads) so that the number of loads in flight is the same on
@@ -627,14 +656,16 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         acc1 = mfma(qa[0][st], dequant_keys<KB>(c.kc[t], st, lut, koff), acc1);
-        const unsigned sa = (st == 0) ? lut_addr<0>(c.ks[t], soff)
-                          : (st == 1) ? lut_addr<1>(c.ks[t], soff)
-                          : (st == 2) ? lut_addr<2>(c.ks[t], soff) : lut_addr<3>(c.ks[t], soff);
-        acc2 = mfma(qa[NSET - 1][st], as_h8(*reinterpret_cast<const u32x4*>(lut + sa)), acc2);
+        if constexpr (QJL) {
+          const unsigned sa = (st == 0) ? lut_addr<0>(c.ks[t], soff)
+                            : (st == 1) ? lut_addr<1>(c.ks[t], soff)
+                            : (st == 2) ? lut_addr<2>(c.ks[t], soff) : lut_addr<3>(c.ks[t], soff);
+          acc2 = mfma(qa[NSET - 1][st], as_h8(*reinterpret_cast<const u32x4*>(lut + sa)), acc2);
+        }
       }
       const bool valid = active && (c0 + 16 * t + col) < end;
       float f[HPL];
-      fold_scores<NREP>(acc1, acc2, h_hi(c.kn[t]), kg, f);
+      fold_scores<NREP, QJL>(acc1, acc2, h_hi(c.kn[t]), kg, f);
       const float alpha = sc * h_lo(c.kn[t]);
 #pragma unroll
       for (int hs = 0; hs < HPL; ++hs) s[t][hs] = valid ? alpha * f[hs] : -INFINITY;
@@ -832,28 +863,29 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   }
 }
 
-template <int NREP, int KB, bool MSEV>
+template <int NREP, int KB, bool MSEV, bool QJL>
 void* pick_vb(int vb) {
   switch (vb) {
-    case 2: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 2, MSEV>);
-    case 3: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 3, MSEV>);
-    case 4: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 4, MSEV>);
+    case 2: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 2, MSEV, QJL>);
+    case 3: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 3, MSEV, QJL>);
+    case 4: return reinterpret_cast<void*>(&splitk_mfma_kernel<NREP, KB, 4, MSEV, QJL>);
   }
   return nullptr;
 }
-template <int NREP, bool MSEV>
+template <int NREP, bool MSEV, bool QJL>
 void* pick_kb(int kb, int vb) {
   switch (kb) {
-    case 1: return pick_vb<NREP, 1, MSEV>(vb);
-    case 2: return pick_vb<NREP, 2, MSEV>(vb);
-    case 3: return pick_vb<NREP, 3, MSEV>(vb);
-    case 4: return pick_vb<NREP, 4, MSEV>(vb);
+    case 1: return pick_vb<NREP, 1, MSEV, QJL>(vb);
+    case 2: return pick_vb<NREP, 2, MSEV, QJL>(vb);
+    case 3: return pick_vb<NREP, 3, MSEV, QJL>(vb);
+    case 4: return pick_vb<NREP, 4, MSEV, QJL>(vb);
   }
   return nullptr;
 }
 template <int NREP>
-void* pick_mode(bool msev, int kb, int vb) {
-  return msev ? pick_kb<NREP, true>(kb, vb) : pick_kb<NREP, false>(kb, vb);
+void* pick_mode(bool msev, bool qjl, int kb, int vb) {
+  return msev ? (qjl ? pick_kb<NREP, true, true>(kb, vb) : pick_kb<NREP, true, false>(kb, vb))
+              : (qjl ? pick_kb<NREP, false, true>(kb, vb) : pick_kb<NREP, false, false>(kb, vb));
 }
 
 }  // namespace
@@ -864,9 +896,11 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
   {
     const unsigned kb = L->cfg.k_bits, vb = L->cfg.v_bits;
     const unsigned last = L->cfg.value_mode == TQ_VAL_MSE ? 32 : 256;
+    const unsigned key_meta = L->cfg.key_mode == TQ_KEY_QJL ? 320 : 32;  // Ks + Kn, or Kn alone
+    const unsigned kn = L->cfg.key_mode == TQ_KEY_QJL ? 256 * kb + 256 : 256 * kb;
     const tq::Layout& ly = L->lay;
-    if (ly.off_kc != 0 || ly.off_ks != 256 * kb || ly.off_kn != 256 * kb + 256 || ly.off_vc != 256 * kb + 320 ||
-        ly.off_vsz != 256 * (kb + vb) + 320 || ly.block_bytes != 256 * (kb + vb) + 320 + last)
+    if (ly.off_kc != 0 || ly.off_ks != 256 * kb || ly.off_kn != kn || ly.off_vc != 256 * kb + key_meta ||
+        ly.off_vsz != 256 * (kb + vb) + key_meta || ly.block_bytes != 256 * (kb + vb) + key_meta + last)
       return fail(TQ_ERR_UNSUPPORTED, "store layout does not match the decode kernels' page layout");
   }
   MainArgs a;
@@ -885,13 +919,13 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
     a.cent[i] = L->centroids[i];
     a.vcent[i] = L->v_centroids[i];
   }
-  const bool msev = L->cfg.value_mode == TQ_VAL_MSE;
+  const bool msev = L->cfg.value_mode == TQ_VAL_MSE, qjl = L->cfg.key_mode == TQ_KEY_QJL;
   void* fn = nullptr;
   switch (plan.rep) {
-    case 1: fn = pick_mode<1>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
-    case 2: fn = pick_mode<2>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
-    case 4: fn = pick_mode<4>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
-    case 8: fn = pick_mode<8>(msev, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 1: fn = pick_mode<1>(msev, qjl, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 2: fn = pick_mode<2>(msev, qjl, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 4: fn = pick_mode<4>(msev, qjl, L->cfg.k_bits, L->cfg.v_bits); break;
+    case 8: fn = pick_mode<8>(msev, qjl, L->cfg.k_bits, L->cfg.v_bits); break;
   }
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for rep=%d k_bits=%d v_bits=%d", plan.rep,
                        L->cfg.k_bits, L->cfg.v_bits);

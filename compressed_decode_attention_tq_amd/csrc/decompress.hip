@@ -44,6 +44,7 @@ struct DArgs {
   float kappa;
   float cent[16];
   int vm;           // value mode: 0 group scale/zero, 1 codebook codes and one fp16 norm
+  int qjl;          // 1: sign field and (n, gamma) pairs; 0: no sign field, Kn = [16] fp16 n
   float vcent[16];  // value codebook (vm == 1)
 };
 
@@ -92,8 +93,10 @@ __device__ __forceinline__ void expand(const DArgs& a, const unsigned char* page
   unsigned x = 0;
 #pragma unroll
   for (int b = 0; b < KB; ++b) x |= static_cast<unsigned>(kc[b]) << (8 * b);
-  const unsigned zb = page[a.off_ks + (blk * 16 + o) * 4 + e0 / 8];  // sign bits of dims d0..d0+7
-  const unsigned kn = *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4);
+  // sign bits of dims d0..d0+7 and (n, gamma); without QJL no signs and gamma 0
+  const unsigned zb = a.qjl ? page[a.off_ks + (blk * 16 + o) * 4 + e0 / 8] : 0u;
+  const unsigned kn = a.qjl ? *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4)
+                            : *reinterpret_cast<const unsigned short*>(page + a.off_kn + o * 2);
   // value metadata: the group's scale and zero, or (codebook-coded values) the
   // token's norm / sqrt(d), read from a last field of 32 bytes per page
   float sc, zr;
@@ -295,6 +298,7 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
       a.vcent[i] = L->v_centroids[i];
     }
     a.vm = L->cfg.value_mode == TQ_VAL_MSE ? 1 : 0;
+    a.qjl = L->cfg.key_mode == TQ_KEY_QJL ? 1 : 0;
     fn = bf ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits) : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
                          L->cfg.v_bits);

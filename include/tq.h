@@ -59,7 +59,8 @@
  *     Kc  [4][16][4*k_bits]  key codebook indices: for 32-dim block j and token
  *                            t, the k_bits stream of dims 32j .. 32j+31
  *     Ks  [4][16][4]         QJL sign bits (1 <=> (S rho)_j >= 0), same blocking
- *     Kn  [16][2] fp16       ||k|| then gamma = ||rho||
+ *     Kn  [16][2] fp16       ||k|| then gamma = ||rho||   ([16] fp16 ||k||, and no
+ *                            Ks field, in the key modes without QJL)
  *     Vc  [32][64] v_bits    value codes in 32 lane blocks: for dim = 16i + c
  *                            and token t = 8h + k, block 16h + c, group
  *                            2i + k/4 of four codes, element k % 4 (one stream
@@ -138,8 +139,10 @@ tq_status tq_codebook_build(int bits, tq_dist dist, int dim, double* centroids,
  *                  n * sqrt(d) / ||c[idx]||, so that the reconstruction
  *                  (n16 / sqrt d) R^T c[idx] has the key's own norm ("turbo-attn
  *                  0.24.0", "Configuration", TKV_K_NC: norm-correction of K reads).
- * The page layout is the same for all three (the sign field is kept), so the
- * decode kernels serve every mode unchanged. */
+ * The two modes without QJL use a compact page: no sign field (Ks has 0 bytes,
+ * its offset is Kn's) and Kn [16] fp16 holds the magnitude alone (18 bytes less
+ * per token-head; 146 instead of 164 at K4/V4); the decode then runs no sign
+ * products. */
 typedef enum { TQ_KEY_QJL = 0, TQ_KEY_MSE = 1, TQ_KEY_MSE_NC = 2 } tq_key_mode;
 
 /* Rotation family of a compressed layer (per KV head g).

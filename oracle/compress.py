@@ -151,6 +151,8 @@ def compress_into_pool(K, V, slots, pool, layout, state, keep=True):
     value_mode = getattr(state, "value_mode", "group")
     if value_mode != layout.value_mode:
         raise ValueError("layer state (%s values) and layout (%s values) disagree" % (value_mode, layout.value_mode))
+    if (getattr(state, "key_mode", "qjl") == "qjl") != layout.qjl:
+        raise ValueError("layer state (%s keys) and layout (qjl=%s) disagree" % (state.key_mode, layout.qjl))
     out = {}
     for h in range(H):
         ck = compress_keys(K[:, h], state.R[h], state.S[h], state.centroids, state.boundaries,

@@ -28,6 +28,11 @@ With MSE values (value_mode "mse": values coded like the keys' codebook part,
 codebook indices in the same stream order and the last field is
   Vn  [P] fp16             ||v||
 so that K2 + QJL / V3 is 102 bytes per (token, head) and 1632 per page.
+Key modes without the QJL residual signs ("turbo-attn 0.24.0", "How it works":
+one magnitude and the shared-codebook codes per key) store neither the sign
+field nor gamma: Ks has 0 bytes (its offset is Kn's) and
+  Kn  [P] fp16             the stored magnitude only
+so that K4 / V4 is 146 bytes per (token, head) instead of 164.
 Bypass (uncompressed) layers: region = Kb [P][d] bf16 (token-major: one token's
 d keys together) followed by Vb [d][P] bf16 (dim-major: the P tokens' values of
 one dim together), so that a page's values load as the matrix-core operand of
@@ -41,11 +46,12 @@ VALUE_MODES = ("group", "mse")
 
 
 class StoreLayout:
-    def __init__(self, d=128, k_bits=4, v_bits=4, group=32, bypass=False, m=None, value_mode="group"):
+    def __init__(self, d=128, k_bits=4, v_bits=4, group=32, bypass=False, m=None, value_mode="group", qjl=True):
         if value_mode not in VALUE_MODES:
             raise ValueError("unknown value mode %r" % (value_mode,))
         self.d, self.k_bits, self.v_bits, self.group, self.bypass = d, k_bits, v_bits, group, bypass
         self.value_mode = value_mode
+        self.qjl = bool(qjl)  # False: key modes without residual signs (no Ks field, no gamma)
         self.m = d if m is None else m
         if bypass:
             self.kb_bytes = d * 2
@@ -54,8 +60,8 @@ class StoreLayout:
             self.block_bytes = 2 * P * self.kb_bytes
             return
         self.kc_bytes = d * k_bits // 8
-        self.ks_bytes = self.m // 8
-        self.kn_bytes = 4
+        self.ks_bytes = self.m // 8 if self.qjl else 0
+        self.kn_bytes = 4 if self.qjl else 2
         self.vc_bytes = d * v_bits // 8
         # the last field: group scale/zero, or one fp16 norm with MSE values
         self.vsz_bytes = 4 * (d // group) if value_mode == "group" else 2
@@ -123,6 +129,8 @@ def _field_bits(layout, base, offs, name):
         rec = (dim // 32) * P + offs
         return (base + layout.off_kc) * 8 + rec * (32 * layout.k_bits) + (dim % 32) * layout.k_bits
     if name == "z":        # [N, m]
+        if not layout.qjl:
+            raise KeyError("no sign field in a layout without QJL")
         j = np.arange(layout.m)[None, :]
         rec = (j // 32) * P + offs
         return (base + layout.off_ks) * 8 + rec * 32 + (j % 32)
@@ -142,17 +150,23 @@ def put_records(pool, layout, n_kv_heads, slots, head, rec):
 
     rec: idx [N, d] and z [N, m] (ints), n16, g16 [N] (float16),
     vcode [N, d] (ints), scale16, zero16 [N, d/G] (float16); with MSE values
-    vn16 [N] (float16) in place of scale16 and zero16.
+    vn16 [N] (float16) in place of scale16 and zero16.  A layout without QJL
+    stores n16 only (z and g16 must then be zero).
     """
     slots = np.asarray(slots, dtype=np.int64)
     blocks, offs = np.divmod(slots, P)
     base = (blocks * n_kv_heads + head) * layout.block_bytes
     _bit_write(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits, rec["idx"])
-    _bit_write(pool, _field_bits(layout, base, offs, "z"), 1, rec["z"])
+    if layout.qjl:
+        _bit_write(pool, _field_bits(layout, base, offs, "z"), 1, rec["z"])
+        kn = np.stack([np.asarray(rec["n16"], np.float16), np.asarray(rec["g16"], np.float16)], axis=-1)
+    else:
+        if np.any(np.asarray(rec["z"])) or np.any(np.asarray(rec["g16"], np.float64)):
+            raise ValueError("a layout without QJL holds no residual signs or gamma")
+        kn = np.asarray(rec["n16"], np.float16).reshape(len(slots), 1)
     _bit_write(pool, _field_bits(layout, base, offs, "vcode"), layout.v_bits, rec["vcode"])
-    kn = np.stack([np.asarray(rec["n16"], np.float16), np.asarray(rec["g16"], np.float16)], axis=-1)
-    at = (base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(4)
-    pool[at] = kn.view(np.uint8).reshape(len(slots), 4)
+    at = (base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(layout.kn_bytes)
+    pool[at] = np.ascontiguousarray(kn).view(np.uint8).reshape(len(slots), layout.kn_bytes)
     if layout.value_mode == "mse":
         sz = np.asarray(rec["vn16"], np.float16).reshape(len(slots), 1)
     else:
@@ -167,15 +181,20 @@ def get_records(pool, layout, n_kv_heads, slots, head):
     slots = np.asarray(slots, dtype=np.int64)
     blocks, offs = np.divmod(slots, P)
     base = (blocks * n_kv_heads + head) * layout.block_bytes
-    kn = pool[(base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(4)]
-    kn = np.ascontiguousarray(kn).view(np.float16)
+    kn = pool[(base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(layout.kn_bytes)]
+    kn = np.ascontiguousarray(kn).view(np.float16).reshape(len(slots), -1)
     sz = pool[(base + layout.off_vsz + offs * layout.vsz_bytes)[:, None] + np.arange(layout.vsz_bytes)]
     out = {
         "idx": _bit_read(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits),
-        "z": _bit_read(pool, _field_bits(layout, base, offs, "z"), 1),
-        "n16": kn[:, 0], "g16": kn[:, 1],
+        "n16": kn[:, 0],
         "vcode": _bit_read(pool, _field_bits(layout, base, offs, "vcode"), layout.v_bits),
     }
+    if layout.qjl:
+        out["z"] = _bit_read(pool, _field_bits(layout, base, offs, "z"), 1)
+        out["g16"] = kn[:, 1]
+    else:  # no residual signs: the decoder's QJL term is zero
+        out["z"] = np.zeros((len(slots), layout.m), dtype=np.int64)
+        out["g16"] = np.zeros(len(slots), dtype=np.float16)
     if layout.value_mode == "mse":
         out["vn16"] = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots))
     else:

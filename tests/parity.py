@@ -228,7 +228,7 @@ def oracle_store(K, V, slots, num_blocks, n_heads, k_bits, v_bits, seed, layer=0
                  value_mode="group"):
     """Oracle state + pool for the given inputs (float arrays [N, H, d]); every
     pool byte starts as `fill` (0xFF: all-ones fields, NaN norms and values)."""
-    layout = lay.StoreLayout(128, k_bits, v_bits, 32, bypass=bypass, value_mode=value_mode)
+    layout = lay.StoreLayout(128, k_bits, v_bits, 32, bypass=bypass, value_mode=value_mode, qjl=key_mode == "qjl")
     pool = lay.new_pool(num_blocks, n_heads, layout)
     pool[:] = fill
     if bypass:

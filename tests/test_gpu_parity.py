@@ -277,7 +277,8 @@ def test_compress_mse_values(kb, vb, n, dtype, key_mode, rotation, pages):
     st, layout, pool, res = parity.oracle_store(K, V, slots, nb, 8, kb, vb, 341, layer=kb, value_mode="mse",
                                                 key_mode=KEY_MODE_NAMES[key_mode],
                                                 rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard")
-    assert layout.record_bytes() == 16 * kb + 16 + 4 + 16 * vb + 2
+    # key metadata: 16 B of signs + (n, gamma) with QJL, the magnitude alone without
+    assert layout.record_bytes() == 16 * kb + (20 if key_mode == tq.KEY_QJL else 2) + 16 * vb + 2
     _check_compress(gpu, res, st, layout, 8, slots, V, kb, vb)
     written = set((slots[slots >= 0] // 16).tolist())
     for b in range(nb):
@@ -296,6 +297,19 @@ def test_decode_mse_values(kb, vb, rep, splits):
     Hkv = 4
     _decode_case(torch, 4, Hkv * rep, Hkv, [700, 1, 129, 2050], kb, vb, 360 + kb, num_splits=splits,
                  value_mode=tq.VAL_MSE)
+
+
+@pytest.mark.parametrize("key_mode,kb,vb,rep,value_mode", [
+    (1, 4, 4, 4, 0), (2, 3, 2, 8, 0), (1, 2, 3, 1, 1), (2, 1, 3, 2, 0), (1, 4, 3, 4, 1)])
+def test_decode_compact_layout_without_qjl(key_mode, kb, vb, rep, value_mode):
+    """Key modes without QJL store no sign field and no gamma (the compact page); the
+    decode variant without sign products, over oracle-written compact stores at every
+    GQA ratio, with group- and MSE-coded values, and 0xFF-filled pools."""
+    torch = _torch()
+    say("decode compact layout", key_mode, kb, vb, rep, value_mode)
+    Hkv = 2
+    _decode_case(torch, 4, Hkv * rep, Hkv, [1, 700, 129, 2050], kb, vb, 380 + kb, key_mode=key_mode,
+                 value_mode=value_mode, fill=0xFF)
 
 
 def test_decode_mse_values_unwritten_slots():
@@ -448,7 +462,7 @@ def _gpu_decode(torch, layer_cfg, pool_np, q, table, lens, max_len, out_dtype="f
 
 def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_dtype="bf16",
                  outliers=4, out_dtypes=("f32", "bf16"), num_splits=0, scale=0.0, layer=0, bypass=False,
-                 fill=0, value_mode=0):
+                 fill=0, value_mode=0, key_mode=0):
     lens = np.asarray(lens, dtype=np.int32)
     maxb = max(1, (int(lens.max()) + 15) // 16)
     table = synth.block_table(seed, B, maxb, table_kind)
@@ -470,11 +484,12 @@ def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_d
                                                   fill=fill)
     else:
         st, layout, pool, _ = parity.oracle_store(K, V, slots, nblk, Hkv, kb, vb, seed, layer=layer, keep=False,
-                                                  fill=fill, value_mode="mse" if value_mode else "group")
+                                                  fill=fill, value_mode="mse" if value_mode else "group",
+                                                  key_mode=("qjl", "mse", "mse_nc")[key_mode])
     q = synth.queries_host(seed, B, Hq, dtype=q_dtype)
     ref = parity.oracle_decode(q.astype(np.float64), pool, layout, Hkv, table, lens, st,
                                scale=scale if scale else None)
-    cfg = tq.config(Hkv, kb, vb, seed=seed, layer=layer, bypass=bypass, value_mode=value_mode)
+    cfg = tq.config(Hkv, kb, vb, seed=seed, layer=layer, bypass=bypass, value_mode=value_mode, key_mode=key_mode)
     results = {}
     for od in out_dtypes:
         got = _gpu_decode(torch, cfg, pool, q, table, lens, int(lens.max()), od, num_splits, scale,
@@ -694,23 +709,35 @@ def test_end_to_end_one_bit_keys():
 KEY_MODE_NAMES = {tq.KEY_QJL: "qjl", tq.KEY_MSE: "mse", tq.KEY_MSE_NC: "mse_nc"}
 
 
-@pytest.mark.parametrize("key_mode,kb,vb,n,dtype", [
-    (tq.KEY_MSE, 4, 4, 700, "bf16"), (tq.KEY_MSE_NC, 3, 2, 700, "bf16"),
-    (tq.KEY_MSE_NC, 2, 3, 1024, "f32"), (tq.KEY_MSE, 3, 3, 40, "bf16"), (tq.KEY_MSE_NC, 1, 3, 500, "bf16"),
-    (tq.KEY_MSE, 1, 2, 100, "f32")])
-def test_compress_key_modes(key_mode, kb, vb, n, dtype):
+@pytest.mark.parametrize("key_mode,kb,vb,n,dtype,value_mode,scattered", [
+    (tq.KEY_MSE, 4, 4, 700, "bf16", "group", False), (tq.KEY_MSE_NC, 3, 2, 700, "bf16", "group", False),
+    (tq.KEY_MSE_NC, 2, 3, 1024, "f32", "group", False), (tq.KEY_MSE, 3, 3, 40, "bf16", "group", False),
+    (tq.KEY_MSE_NC, 1, 3, 500, "bf16", "group", False), (tq.KEY_MSE, 1, 2, 100, "f32", "group", False),
+    (tq.KEY_MSE, 4, 3, 613, "bf16", "group", True), (tq.KEY_MSE_NC, 2, 4, 509, "bf16", "mse", True),
+    (tq.KEY_MSE, 3, 2, 300, "f32", "group", True)])
+def test_compress_key_modes(key_mode, kb, vb, n, dtype, value_mode, scattered):
     """Keys without the residual projection (plain and norm-corrected magnitude):
     the matrix-core compressor (bf16: whole pages and a ragged last tile) and the
-    per-token one (fp32 inputs; a 40-token append)."""
+    per-token one (fp32 inputs; a 40-token append).  Scattered: every page starts
+    at offset 5 of a shuffled block, so no 16-token tile fills one page and each
+    record goes through the token-by-token store."""
     torch = _torch()
-    say("compress key mode", key_mode, kb, vb, n, dtype)
+    say("compress key mode", key_mode, kb, vb, n, dtype, value_mode, scattered)
     H = 8 if dtype == "bf16" else 1
     K, V = synth.kv_host(170 + key_mode, n, H, dtype=dtype, outliers=4 if dtype == "bf16" else 0)
-    slots = np.arange(n, dtype=np.int64)
-    nb = (n + 15) // 16
-    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, 230, layer=key_mode, dtype=dtype, key_mode=key_mode)
+    if scattered:
+        pos = np.arange(n) + 5
+        perm = np.random.default_rng(171 + kb).permutation((n + 5 + 15) // 16)
+        slots = (perm[pos // 16] * 16 + pos % 16).astype(np.int64)
+        nb = len(perm)
+    else:
+        slots = np.arange(n, dtype=np.int64)
+        nb = (n + 15) // 16
+    vm = tq.VAL_MSE if value_mode == "mse" else tq.VAL_GROUP
+    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, 230, layer=key_mode, dtype=dtype, key_mode=key_mode,
+                        value_mode=vm)
     st, layout, pool, res = parity.oracle_store(K, V, slots, nb, H, kb, vb, 230, layer=key_mode,
-                                                key_mode=KEY_MODE_NAMES[key_mode])
+                                                key_mode=KEY_MODE_NAMES[key_mode], value_mode=value_mode)
     _check_compress(gpu, res, st, layout, H, slots, V, kb, vb)
     # no residual signs and gamma 0 in the store
     for h in range(H):
@@ -795,7 +822,7 @@ def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype):
     kd, vd = kd.float().cpu().numpy(), vd.float().cpu().numpy()
     st = parity.ostate.LayerState(290, kb, H, 128, kb, vb, 32, key_mode=KEY_MODE_NAMES[key_mode],
                                   rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard")
-    layout = parity.lay.StoreLayout(128, kb, vb, 32)
+    layout = parity.lay.StoreLayout(128, kb, vb, 32, qjl=key_mode == tq.KEY_QJL)
     kr, vr = odec.decompress(pool.cpu().numpy(), layout, H, q_slots, st)
     neg = q_slots < 0
     assert not kd[neg].any() and not vd[neg].any()

@@ -119,12 +119,19 @@ def test_null_and_bad_arguments_on_device_entry_points():
     assert lib.tq_layer_create(None, None, ctypes.byref(vp())) == tq.ERR_INVALID_ARGUMENT
 
 
-def test_key_modes_share_the_page_layout():
-    """The key modes change what is stored in the fields, not the fields."""
-    for kb, vb in ((2, 3), (4, 4)):
-        ref = tq.store_layout(tq.config(8, kb, vb))
-        for km in (tq.KEY_MSE, tq.KEY_MSE_NC):
-            assert tq.store_layout(tq.config(8, kb, vb, key_mode=km)) == ref
+@pytest.mark.parametrize("kb,vb,value_mode", [(2, 3, 0), (4, 4, 0), (1, 2, 0), (2, 3, 1)])
+def test_key_modes_without_qjl_use_the_compact_layout(kb, vb, value_mode):
+    """The two key modes without QJL store no sign field and no gamma: the library's
+    layout equals the oracle's compact layout (Ks 0 bytes at Kn's offset, Kn [16]
+    fp16), 18 bytes per token-head less than with QJL."""
+    vm = "mse" if value_mode else "group"
+    ref = tq.store_layout(tq.config(8, kb, vb, value_mode=value_mode))
+    for km in (tq.KEY_MSE, tq.KEY_MSE_NC):
+        bb, offs = tq.store_layout(tq.config(8, kb, vb, key_mode=km, value_mode=value_mode))
+        lay = layout.StoreLayout(128, kb, vb, 32, value_mode=vm, qjl=False)
+        assert bb == lay.block_bytes and offs == lay.field_offsets()
+        assert ref[0] - bb == 16 * 18
+        assert all(o % 16 == 0 for o in offs)
 
 
 @pytest.mark.parametrize("layer,heads", [(0, 1), (5, 3)])

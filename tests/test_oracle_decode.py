@@ -14,7 +14,7 @@ def _setup(k_bits=3, v_bits=2, B=2, Hq=4, Hkv=2, lens=(40, 17), seed=0, bypass=F
            rotation_kind="haar", value_mode="group"):
     st = state.LayerState(200 + seed, 0, Hkv, D, k_bits, v_bits, 32, key_mode=key_mode,
                           rotation_kind=rotation_kind, value_mode=value_mode)
-    lay = layout.StoreLayout(D, k_bits, v_bits, 32, bypass=bypass, value_mode=value_mode)
+    lay = layout.StoreLayout(D, k_bits, v_bits, 32, bypass=bypass, value_mode=value_mode, qjl=key_mode == "qjl")
     maxb = (max(lens) + 15) // 16
     table = np.random.default_rng(seed).permutation(B * maxb).reshape(B, maxb)
     pool = layout.new_pool(B * maxb, Hkv, lay)

@@ -221,3 +221,31 @@ def test_mse_value_norm_placement_by_hand():
     at = 3 * 1632 + 1600 + 10
     assert list(np.nonzero(pool)[0]) == [at + 1]  # 1.5 = 0x3E00: low byte 0, high byte 0x3E
     assert pool[at + 1] == 0x3E
+
+
+def test_layout_without_qjl_by_hand():
+    """Key modes without residual signs: no sign field, no gamma.  K4/V4 page =
+    16 x (64 Kc + 2 Kn + 64 Vc + 16 Vsz) = 2336 bytes (146 per token-head, against
+    164 with QJL); offsets Kc 0, Ks = Kn 1024 (0 bytes), Kn 1024, Vc 1056, Vsz 2080."""
+    lay = layout.StoreLayout(128, 4, 4, 32, qjl=False)
+    assert lay.block_bytes == 2336 and lay.record_bytes() == 146
+    assert lay.field_offsets() == [0, 1024, 1024, 1056, 2080]
+    mse = layout.StoreLayout(128, 2, 3, 32, value_mode="mse", qjl=False)
+    assert mse.record_bytes() == 32 + 2 + 48 + 2  # 84
+    # one token's magnitude at slot 37 (block 2, offset 5), head 1 of 2: bytes
+    # off_kn + 2*5 of region 5, nothing else written
+    zero = {k: np.zeros_like(v) for k, v in _records(lay, 1, 0).items()}
+    r = dict(zero, n16=np.float16([2.0]))
+    pool = layout.new_pool(3, 2, lay)
+    layout.put_records(pool, lay, 2, [37], 1, r)
+    base = 5 * lay.block_bytes
+    assert list(np.flatnonzero(pool)) == [base + 1024 + 11] and pool[base + 1024 + 11] == 0x40  # fp16 2.0 = 0x4000
+    got = layout.get_records(pool, lay, 2, [37], 1)
+    assert got["n16"][0] == 2.0 and not got["z"].any() and got["g16"][0] == 0
+    # signs or gamma handed to a layout without QJL are refused
+    bad = dict(zero, z=zero["z"].copy())
+    bad["z"][0, 3] = 1
+    with pytest.raises(ValueError):
+        layout.put_records(pool, lay, 2, [37], 1, bad)
+    with pytest.raises(ValueError):
+        layout.put_records(pool, lay, 2, [37], 1, dict(zero, g16=np.float16([0.5])))
