@@ -147,6 +147,13 @@ int env_splits() {
   return v > 0 ? v : 0;
 }
 
+// TQ_DECODE_WORK_LIST: "0" plain item order, "1" work list, unset or other: automatic.
+int env_work_list() {
+  const char* s = std::getenv("TQ_DECODE_WORK_LIST");
+  if (!s || (s[0] != '0' && s[0] != '1') || s[1] != 0) return -1;
+  return s[0] - '0';
+}
+
 }  // namespace
 
 tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_len, int num_splits,
@@ -178,6 +185,15 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
   }
   p.split_tokens = split_tokens;
   p.n_splits = (ctx + split_tokens - 1) / split_tokens;
+  const long long items = static_cast<long long>(batch) * L->cfg.n_kv_heads * p.n_splits;
+  if (items > 0x7fffffffLL)
+    return fail(TQ_ERR_UNSUPPORTED, "decode grid of %lld workgroups (batch x kv_heads x splits) exceeds 2^31 - 1",
+                items);
+  // The work list pays one dependent read of seq_lens per workgroup; it is used
+  // where the grid is more than one round of resident workgroups (two per CU),
+  // so that dispatch order and the last round matter.
+  const int wl = env_work_list();
+  p.work_list = wl >= 0 ? wl == 1 : items > 2LL * (L->cu_count > 0 ? L->cu_count : 256);
   const size_t bh = static_cast<size_t>(batch) * n_q_heads;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   p.ws_part = 0;

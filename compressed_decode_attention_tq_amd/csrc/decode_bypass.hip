@@ -29,6 +29,7 @@
 
 #include <cmath>
 
+#include "split_items.hpp"
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -54,6 +55,7 @@ struct BypassArgs {
   float* part;    // [B*Hq][n_splits][kPart]
   long long max_blocks;
   int Hq, Hkv, n_splits, split_tokens;
+  int batch, work_list;  // item order of the grid (split_items.hpp)
   float qscale;  // softmax scale * log2(e)
 };
 
@@ -107,7 +109,9 @@ struct Page {
 // read-only, non-aliased parameter.
 template <int NREP, bool QBF16>
 __global__ __launch_bounds__(256) void splitk_bypass_kernel(BypassArgs a, const int* __restrict__ btab) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const SplitItem item = split_item(a.seq_lens, a.batch, a.Hkv, a.split_tokens, a.n_splits, a.work_list != 0);
+  if (item.b < 0) return;  // past the work list (the whole workgroup)
+  const int split = item.split, g = item.g, b = item.b;
   const int start = split * a.split_tokens;
 
   __shared__ __attribute__((aligned(16))) float mbuf[4][NREP][kDim];
@@ -348,12 +352,14 @@ tq_status launch_splitk_bypass(const tq_layer* L, const DecodePlan& plan, const 
   a.Hkv = L->cfg.n_kv_heads;
   a.n_splits = plan.n_splits;
   a.split_tokens = plan.split_tokens;
+  a.batch = plan.batch;
+  a.work_list = plan.work_list ? 1 : 0;
   a.qscale = softmax_scale * 1.4426950408889634f;
   void* fn = (q_dtype == TQ_BF16) ? pick<true>(plan.rep) : pick<false>(plan.rep);
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no bypass decode kernel for rep=%d", plan.rep);
   const int* btab = block_table;
   void* args[] = {&a, &btab};
-  const dim3 grid(plan.n_splits, L->cfg.n_kv_heads, plan.batch);
+  const dim3 grid(static_cast<unsigned>(plan.n_splits * L->cfg.n_kv_heads * plan.batch));
   hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode split-K launch: %s", hipGetErrorString(e));
   return TQ_OK;

@@ -45,6 +45,7 @@
 
 #include <cmath>
 
+#include "split_items.hpp"
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -68,6 +69,7 @@ struct MainArgs {
   float* part;      // [B*Hq][n_splits][kPart]
   long long max_blocks;
   int Hq, Hkv, n_splits, split_tokens;
+  int batch, work_list;  // item order of the grid (split_items.hpp)
   float scale;
   unsigned block_bytes;
   float cent[16];
@@ -499,7 +501,9 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   constexpr int NSET = NREP == 8 ? 2 : 1;
   constexpr int WC = 2 * NREP;  // used P.V columns (hi, lo per head)
   constexpr float kMidCode = static_cast<float>(1 << (VB - 1));
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const SplitItem item = split_item(a.seq_lens, a.batch, a.Hkv, a.split_tokens, a.n_splits, a.work_list != 0);
+  if (item.b < 0) return;  // past the work list (the whole workgroup)
+  const int split = item.split, g = item.g, b = item.b;
   const int start = split * a.split_tokens;
 
   __shared__ __attribute__((aligned(16))) unsigned char lut[256 * kLutEntry];
@@ -913,6 +917,8 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
   a.Hkv = L->cfg.n_kv_heads;
   a.n_splits = plan.n_splits;
   a.split_tokens = plan.split_tokens;
+  a.batch = plan.batch;
+  a.work_list = plan.work_list ? 1 : 0;
   a.scale = softmax_scale;
   a.block_bytes = static_cast<unsigned>(L->lay.block_bytes);
   for (int i = 0; i < 16; ++i) {
@@ -931,7 +937,7 @@ tq_status launch_splitk_tq(const tq_layer* L, const DecodePlan& plan, const void
                        L->cfg.k_bits, L->cfg.v_bits);
   const int* btab = block_table;
   void* args[] = {&a, &btab};
-  const dim3 grid(plan.n_splits, L->cfg.n_kv_heads, plan.batch);
+  const dim3 grid(static_cast<unsigned>(plan.n_splits * L->cfg.n_kv_heads * plan.batch));
   hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TQ_ERR_HIP, "decode split-K launch: %s", hipGetErrorString(e));
   return TQ_OK;

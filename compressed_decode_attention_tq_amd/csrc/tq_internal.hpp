@@ -123,7 +123,8 @@ tq_status launch_compress_mfma(const tq_layer* L, const void* k, const void* v, 
 struct DecodePlan {
   int batch = 0, n_q_heads = 0, rep = 0;
   int split_tokens = 0;   // tokens per split (multiple of 64)
-  int n_splits = 0;       // splits per sequence (grid x)
+  int n_splits = 0;       // splits per sequence
+  bool work_list = false; // split-K item order: work list of live items (else plain order)
   size_t ws_part = 0;     // byte offset of split partials
   size_t ws_qa = 0;       // byte offset of the Q.K matrix-core operand (compressed layers)
   size_t ws_bytes = 0;    // total

@@ -321,6 +321,13 @@ tq_status tq_decode_workspace_size(const tq_layer* layer, int batch, int n_q_hea
  *                otherwise the number of context splits per sequence, raised
  *                where needed so that no split spans more than 4096 tokens.
  *                The environment variable TQ_DECODE_SPLITS overrides 0.
+ *                The split-K grid is batch x n_kv_heads x splits workgroups;
+ *                when it is more than one round of resident workgroups, they
+ *                take the live (sequence, split, head) items as a work list
+ *                built on the device from seq_lens (whole splits first, heads
+ *                spread over the XCDs), so that ragged batches keep every XCD
+ *                busy.  TQ_DECODE_WORK_LIST=0 or 1 forces the plain item order
+ *                or the work list (the output is the same bit for bit).
  *   out          device [batch][n_q_heads][128] of out_dtype (F32 or BF16, RNE)
  *   workspace    device scratch of at least tq_decode_workspace_size() bytes,
  *                256-byte aligned; contents need not be initialised

@@ -108,3 +108,92 @@ def test_every_page_of_the_context_is_loaded():
         assert seen == set(range(limit)), (T, st)
         seen_b = {i for (i,) in bypass_pages(T, st, ns, limit)}
         assert seen_b == set(range(limit)), (T, st)
+
+
+# ---------------------------------------------------------------- item order
+# Replay of split_items.hpp: a wave of 64 lanes, four sequences per lane and
+# pass, an inclusive prefix sum over lanes, a ballot for the first lane whose
+# running count passes the key.
+
+def split_item(seq_lens, batch, Hkv, split_tokens, n_splits, work_list, wid):
+    g, p = wid % Hkv, wid // Hkv
+    if not work_list:
+        return p // n_splits, p % n_splits, g
+    per, span = 4, 256
+    cap = n_splits * split_tokens
+
+    def counts(base):
+        whole, last = np.zeros((64, per), np.int64), np.zeros((64, per), np.int64)
+        for lane in range(64):
+            for k in range(per):
+                i = base + per * lane + k
+                t0 = int(seq_lens[i]) if i < batch else 0
+                t = 0 if t0 <= 0 else min(t0, cap)
+                whole[lane, k] = t // split_tokens
+                last[lane, k] = int(t % split_tokens != 0)
+        return whole, last
+
+    n_whole = 0
+    for base in range(0, batch, span):
+        whole, last = counts(base)
+        n_whole += int(np.cumsum(whole.sum(1))[63])
+    in_whole = p < n_whole
+    key = p if in_whole else p - n_whole
+    carry = 0
+    for base in range(0, batch, span):
+        whole, last = counts(base)
+        v = whole if in_whole else last
+        own = v.sum(1)
+        incl = np.cumsum(own)
+        tot = int(incl[63])
+        if key < carry + tot:
+            lane = int(np.flatnonzero(carry + incl > key)[0])
+            acc = carry + int(incl[lane]) - int(own[lane])
+            for k in range(per):
+                if key < acc + v[lane, k]:
+                    return base + per * lane + k, (key - acc) if in_whole else int(whole[lane, k]), g
+                acc += int(v[lane, k])
+        carry += tot
+    return -1, 0, g
+
+
+def _live(seq_lens, Hkv, split_tokens, n_splits):
+    cap = n_splits * split_tokens
+    out = set()
+    for b, t in enumerate(seq_lens):
+        t = 0 if t <= 0 else min(int(t), cap)
+        for s in range((t + split_tokens - 1) // split_tokens):
+            out |= {(b, s, g) for g in range(Hkv)}
+    return out
+
+
+def test_work_list_covers_every_live_item_once_whole_splits_first():
+    rng = np.random.default_rng(23)
+    cases = []
+    for batch in (1, 3, 64, 255, 256, 257, 600):
+        lens = rng.integers(0, 5000, batch)
+        lens[rng.random(batch) < 0.1] = 0
+        cases.append((lens, 8 if batch < 300 else 2, 1024))
+    special = np.array([0, 1, 1024, 1025, 2048, 4096 * 3, -5, 2 ** 31 - 1], np.int64)
+    cases.append((special, 4, 4096))  # negative and far past max_seq_len: clamped
+    for lens, Hkv, S in cases:
+        n_splits = max(1, (int(max(0, min(lens.max(), 5000))) + S - 1) // S)
+        grid = len(lens) * Hkv * n_splits
+        got = [split_item(lens, len(lens), Hkv, S, n_splits, True, w) for w in range(grid)]
+        live = [x for x in got if x[0] >= 0]
+        assert len(live) == len(set(live)) and set(live) == _live(lens, Hkv, S, n_splits)
+        # dense at the front, head fastest
+        assert all(x[0] >= 0 for x in got[:len(live)]) and all(x[0] < 0 for x in got[len(live):])
+        assert [x[2] for x in got[:len(live)]] == [w % Hkv for w in range(len(live))]
+        # the whole splits come before every shorter last split
+        cap = n_splits * S
+        short = [min(max(int(lens[b]), 0), cap) < (s + 1) * S for b, s, g in live]
+        assert short == sorted(short)
+        assert all(0 <= s < n_splits for b, s, g in live)
+
+
+def test_plain_order_is_a_bijection():
+    for batch, Hkv, n_splits in ((16, 8, 4), (1, 8, 64), (5, 3, 7)):
+        got = [split_item(None, batch, Hkv, 64, n_splits, False, w) for w in range(batch * Hkv * n_splits)]
+        assert sorted(got) == sorted((b, s, g) for b in range(batch) for s in range(n_splits) for g in range(Hkv))
+        assert [x[2] for x in got] == [w % Hkv for w in range(len(got))]

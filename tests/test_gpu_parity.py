@@ -1,5 +1,7 @@
 """GPU parity: libtq's HIP kernels (through the C ABI) against the oracle."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -462,7 +464,9 @@ def _gpu_decode(torch, layer_cfg, pool_np, q, table, lens, max_len, out_dtype="f
 
 def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_dtype="bf16",
                  outliers=4, out_dtypes=("f32", "bf16"), num_splits=0, scale=0.0, layer=0, bypass=False,
-                 fill=0, value_mode=0, key_mode=0):
+                 fill=0, value_mode=0, key_mode=0, orders=(None,)):
+    """orders: split-K item orders to run (TQ_DECODE_WORK_LIST values, None = automatic);
+    every order must give the same output bit for bit."""
     lens = np.asarray(lens, dtype=np.int32)
     maxb = max(1, (int(lens.max()) + 15) // 16)
     table = synth.block_table(seed, B, maxb, table_kind)
@@ -492,10 +496,42 @@ def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_d
     cfg = tq.config(Hkv, kb, vb, seed=seed, layer=layer, bypass=bypass, value_mode=value_mode, key_mode=key_mode)
     results = {}
     for od in out_dtypes:
-        got = _gpu_decode(torch, cfg, pool, q, table, lens, int(lens.max()), od, num_splits, scale,
-                          q_dtype=q_dtype)
-        results[od], _ = parity.assert_decode_ok(got, ref, od)
+        first = None
+        for order in orders:
+            saved = os.environ.pop("TQ_DECODE_WORK_LIST", None)
+            try:
+                if order is not None:
+                    os.environ["TQ_DECODE_WORK_LIST"] = order
+                got = _gpu_decode(torch, cfg, pool, q, table, lens, int(lens.max()), od, num_splits, scale,
+                                  q_dtype=q_dtype)
+            finally:
+                os.environ.pop("TQ_DECODE_WORK_LIST", None)
+                if saved is not None:
+                    os.environ["TQ_DECODE_WORK_LIST"] = saved
+            results[od], _ = parity.assert_decode_ok(got, ref, od, label="order %s" % order)
+            if first is None:
+                first = got
+            else:
+                assert np.array_equal(got.view(np.uint32), first.view(np.uint32)), ("orders differ", order)
     return results
+
+
+@pytest.mark.parametrize("bypass", [False, True])
+def test_decode_work_list_matches_plain_order(bypass):
+    """Ragged batches through the split-K work list and through the plain item order:
+    the same output bit for bit (each item's arithmetic does not depend on where
+    it sits in the grid) and parity with the oracle.  300 sequences (two passes of
+    the per-wave count), empty and one-token sequences, lengths on and around the
+    split boundary, 64-token splits (a grid of 9,600 workgroups), 2 KV heads."""
+    torch = _torch()
+    say("decode work list vs plain order", bypass)
+    rng = np.random.default_rng(63)
+    lens = rng.integers(1, 300, 300).astype(np.int32)
+    lens[::11] = 0
+    lens[[3, 4, 5, 6]] = [1, 64, 65, 128]
+    lens[200] = 1000
+    _decode_case(torch, 300, 8, 2, lens, 3, 3, 291, num_splits=16, out_dtypes=("f32",), bypass=bypass,
+                 orders=("1", "0"))
 
 
 def test_decode_tiny_fp32():
