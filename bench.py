@@ -59,10 +59,10 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_by_workload.txt")
 # kernels whose HBM traffic is taken from counters: (kernel, workload tag) -> (grid in
 # workgroups x*y*z, or None for any grid; the sources that define the kernel)
 TRAFFIC_KERNELS = {
-    ("splitk_mfma_kernel<4,4,4>", "serving"): (8 * 8 * 64, ["decode_mainloop.hip"]),
-    ("splitk_mfma_kernel<4,4,4>", "layer"): (4 * 8 * 16, ["decode_mainloop.hip"]),
-    ("splitk_mfma_kernel<4,3,2>", "long"): (64 * 8 * 1, ["decode_mainloop.hip"]),
-    ("compress_mfma_kernel<2,3,3,false,true>", "compress"): (None, ["compress_mfma.hip"]),
+    ("splitk_mfma_kernel<4,4,4,false,true>", "serving"): (8 * 8 * 64, ["decode_mainloop.hip", "split_items.hpp"]),
+    ("splitk_mfma_kernel<4,4,4,false,true>", "layer"): (4 * 8 * 16, ["decode_mainloop.hip", "split_items.hpp"]),
+    ("splitk_mfma_kernel<4,3,2,false,true>", "long"): (64 * 8 * 1, ["decode_mainloop.hip", "split_items.hpp"]),
+    ("compress_mfma_kernel<2,3,3,false,true,false>", "compress"): (None, ["compress_mfma.hip"]),
 }
 
 
@@ -268,7 +268,7 @@ def serving_workload(torch, tq, synth, args):
         nbytes = _splitk_bytes(lens, Hkv, Hq, rec) if kv else int(lens.sum()) * Hkv * rec + \
             int(((lens + 15) // 16).sum()) * 4 + B * 4 + B * Hq * 128 * 2
         name = "bypass" if kv is None else "K%d/V%d" % kv
-        kern = "splitk_bypass_kernel<4,true>" if kv is None else "splitk_mfma_kernel<4,%d,%d>" % kv
+        kern = "splitk_bypass_kernel<4,true>" if kv is None else "splitk_mfma_kernel<4,%d,%d,false,true>" % kv
         per_kind[name] = dict(_roofline(nbytes, tot / cnt, kern, cnt), layers=len(lis))
     total_bytes = sum(int(lens.sum()) * Hkv * _record_bytes(*(kv if kv else (4, 4)), bypass=kv is None)
                       for kv in alloc)
@@ -332,7 +332,7 @@ def layer_workload(torch, tq, synth, args):
     rec = _record_bytes(kb, vb)
     splitk_bytes = _splitk_bytes([T] * B, Hkv, Hq, rec)
     step_bytes = splitk_bytes + B * Hq * 128 * 2 * 2  # + q in, out (bf16)
-    roof = _roofline(splitk_bytes, sk_us, "splitk_mfma_kernel<4,4,4>", sk_n, traffic_for("splitk_mfma_kernel<4,4,4>",
+    roof = _roofline(splitk_bytes, sk_us, "splitk_mfma_kernel<4,4,4,false,true>", sk_n, traffic_for("splitk_mfma_kernel<4,4,4,false,true>",
                                                                                            "layer"))
     res = {"workload": W["name"], "decode_us": round(ms * 1e3, 3), "decode_tok_s": round(B / (ms / 1e3), 1),
            "kv_tok_s": round(B * T / (ms / 1e3), 1), "step_hbm_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
@@ -369,8 +369,8 @@ def long_context_workload(torch, tq, synth, args):
     del pools, pool0
     return {"workload": W["name"], "decode_us": round(ms * 1e3, 2), "decode_tok_s": round(1 / (ms / 1e3), 1),
             "kv_tok_s": round(T / (ms / 1e3), 1), "step_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "roofline": _roofline(nbytes, sk_us, "splitk_mfma_kernel<4,3,2>", sk_n,
-                                  traffic_for("splitk_mfma_kernel<4,3,2>", "long")),
+            "roofline": _roofline(nbytes, sk_us, "splitk_mfma_kernel<4,3,2,false,true>", sk_n,
+                                  traffic_for("splitk_mfma_kernel<4,3,2,false,true>", "long")),
             "steps": 60, "warmup": 10,
             "config": {"batch": 1, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "context": T,
                        "k_bits": W["k_bits"], "qjl_bits": 1, "v_bits": W["v_bits"], "v_group": 32, "page": 16,
@@ -395,7 +395,7 @@ def tiny_workload(torch, tq, synth, args):
     nbytes = _splitk_bytes([W["ctx"]], W["Hkv"], W["Hq"], _record_bytes(W["k_bits"], W["v_bits"]))
     layer.close()
     return {"workload": W["name"], "decode_us": round(ms * 1e3, 2), "decode_tok_s": round(1 / (ms / 1e3), 1),
-            "roofline": _roofline(nbytes, sk_us, "splitk_mfma_kernel<1,2,3>", sk_n),
+            "roofline": _roofline(nbytes, sk_us, "splitk_mfma_kernel<1,2,3,false,true>", sk_n),
             "note": "0.12 MB per launch: launch-latency bound, the HBM fraction is not meaningful",
             "steps": 200, "warmup": 20,
             "config": {"batch": 1, "q_heads": W["Hq"], "kv_heads": W["Hkv"], "head_dim": 128, "context": W["ctx"],
@@ -438,8 +438,8 @@ def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
             "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": traffic_for("compress_mfma_kernel<2,3,3,false,true>", "compress"),
-                         "kernel": "compress_mfma_kernel<2,3,3,false,true>",
+                         "traffic": traffic_for("compress_mfma_kernel<2,3,3,false,true,false>", "compress"),
+                         "kernel": "compress_mfma_kernel<2,3,3,false,true,false>",
                          "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
 
 
@@ -554,7 +554,7 @@ def mse_values_workload(torch, tq, synth, args):
             "compress_ms": round(ms_c, 4), "compress_gbs": round(nbytes / (ms_c / 1e3) / 1e9, 1),
             "compress_frac": round(nbytes / (ms_c / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "decode_us": round(ms_s * 1e3, 3), "decode_tok_s": round(B / (ms_s / 1e3), 1),
-            "splitk": _roofline(sk_bytes, sk_us, "splitk_mfma_kernel<4,2,3,true>", sk_n),
+            "splitk": _roofline(sk_bytes, sk_us, "splitk_mfma_kernel<4,2,3,true,true>", sk_n),
             "decompress_ms": round(ms_d, 4), "decompress_gbs": round(nbytes / (ms_d / 1e3) / 1e9, 1),
             "decompress_frac": round(nbytes / (ms_d / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
 
