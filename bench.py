@@ -427,6 +427,9 @@ def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
     rec = layer.block_bytes // 16  # per token-head; the key modes without QJL store no sign field
     nbytes = N * H * (512 + rec) + N * 8
     avg_s = c_ms / max(c_n, 1) / 1e3
+    prefill = None
+    if not (key_mode or rotation):
+        prefill = _prefill_batch_leg(torch, tq, synth, args, layer, k, v, N, H, rec)
     layer.close()
     del k, v, pool
     if key_mode or rotation:
@@ -435,12 +438,41 @@ def compress_workload(torch, tq, synth, args, key_mode=0, rotation=0):
                 "mtok_s": round(N / (ms / 1e3) / 1e6, 2), "gbs": round(nbytes / avg_s / 1e9, 1),
                 "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}
     return {"workload": W["name"], "tokens": N, "kv_heads": H, "k_bits": W["k_bits"], "v_bits": W["v_bits"],
-            "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2),
+            "ms": round(ms, 4), "mtok_s": round(N / (ms / 1e3) / 1e6, 2), "prefill_batch": prefill,
             "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": traffic_for("compress_mfma_kernel<2,3,3,false,true,false>", "compress"),
                          "kernel": "compress_mfma_kernel<2,3,3,false,true,false>",
                          "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": nbytes}}
+
+
+def _prefill_batch_leg(torch, tq, synth, args, layer, k, v, N, H, rec):
+    """The same tokens as a prefill batch: 64 sequences of seeded lengths U{512..32768},
+    scaled to N tokens in all, laid end to end in the input, each written from offset
+    0 of its own shuffled pages (so the compressor's 16-token tiles straddle pages)."""
+    import numpy as np
+    lens = synth.ragged_lengths(606, 64, 512, 32768).astype(np.int64)
+    lens = np.maximum(lens * N // int(lens.sum()), 1)
+    lens[-1] += N - int(lens.sum())
+    table, _ = _compact_table(607, lens)
+    b_of = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(x) for x in lens])
+    slots = torch.from_numpy(table[b_of, pos // 16].astype(np.int64) * 16 + pos % 16).cuda()
+    pool = layer.new_pool(int(table.max()) + 1)
+    tq.compress_kv(layer, k, v, slots, pool)
+    torch.cuda.synchronize()
+    tq.profile_reset()
+    tq.profile_enable(1 << tq.K_COMPRESS)
+    for _ in range(args.compress_iters):
+        tq.compress_kv(layer, k, v, slots, pool)
+    torch.cuda.synchronize()
+    c_ms, c_n = tq.profile_read(tq.K_COMPRESS)
+    tq.profile_enable(0)
+    avg_s = c_ms / max(c_n, 1) / 1e3
+    nbytes = N * H * (512 + rec) + N * 8
+    del pool
+    return {"sequences": len(lens), "tokens": N, "avg_us": round(avg_s * 1e6, 1),
+            "mtok_s": round(N / avg_s / 1e6, 2), "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def _time_steps(torch, fn, n):

@@ -204,16 +204,35 @@ __device__ __forceinline__ float std_factor(float n2) {
                                  : (n2 > 0.0f ? sqrtf(128.0f) / sqrtf(n2) : 0.0f);
 }
 
+// Bits of word p (0 .. 2 VB - 1) of a value-code run (the 64 codes of one
+// coordinate column and half page: code 8 i + k at bits VB (8 i + k), k the
+// offset within the half) that hold the codes of offsets k >= m.  The pattern
+// repeats every 8 VB bits and a run starts on a word boundary.
+template <int VB>
+__device__ __forceinline__ unsigned vc_upper_mask(int p, int m) {
+  constexpr int G = 8 * VB;
+  const unsigned long long per = ((1ull << G) - 1ull) & ~((1ull << (VB * m)) - 1ull);
+  unsigned long long q = 0;
+#pragma unroll
+  for (int i = 0; i < 64; i += G) q |= per << i;
+  return static_cast<unsigned>(q >> ((32 * p) % G));
+}
+
 // Wait until at most n of this wave's vector-memory operations are outstanding,
-// for n rounded down to 2P - 1, P - 1 or 0 (wave-uniform n).  Loads and stores
-// retire in issue order on this counter, so "at most n left" means every
-// operation issued before the last n has completed.
+// for n rounded down to one of the counts the tile loop can ask for with a
+// ring of P tiles and two operations per fetched tile (3P - 2 in steady state,
+// 2 (P - 1), ..., 2, 0 otherwise); wave-uniform n.  Loads and stores retire in
+// issue order on this counter, so "at most n left" means every operation issued
+// before the last n has completed.
 template <int P>
 __device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  if (n >= 2 * P - 1)
-    wait_vmcnt<2 * P - 1>();
-  else if (n >= P - 1)
-    wait_vmcnt<P - 1>();
+  static_assert(P == 3, "wait levels are spelled out for a ring of three tiles");
+  if (n >= 7)
+    wait_vmcnt<7>();
+  else if (n >= 4)
+    wait_vmcnt<4>();
+  else if (n >= 2)
+    wait_vmcnt<2>();
   else
     wait_vmcnt<0>();
 }
@@ -221,14 +240,23 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // Slot ids come as their own read-only, non-aliased parameter: the reads are
 // wave-uniform and become scalar loads, which do not wait on the tile copies.
 //
-// The K/V rows of P tiles are in flight at once (a ring of P LDS slots): HBM
-// latency is covered by P tiles of work instead of one.  Every wave issues
-// exactly one copy per tile it fetches and, for a whole-page tile, exactly one
-// 16-byte page store, so the wait for tile k counts the operations issued after
-// that tile's copy: 2P - 1 in steady state (the P - 1 later copies and the P
-// page stores in between).  When a store was scattered or a copy skipped within
-// that window, the wait counts only the copies known to follow, which is never
-// more than what is outstanding.
+// The K/V rows and slots of P tiles are in flight at once (a ring of P LDS
+// slots): HBM latency is covered by P tiles of work instead of one.  Every wave
+// issues exactly two copies per tile it fetches (its share of the rows, then
+// two of the tile's slots) and, for a whole-page tile, exactly one 16-byte page
+// store, so the wait for tile k counts the operations issued after that tile's
+// copies: 3P - 2 in steady state (the 2 (P - 1) copies of later tiles and the P
+// page stores in between).  When a store was split or scattered, or a copy
+// skipped, within that window, the wait counts only the copies known to follow,
+// which is never more than what is outstanding.
+//
+// Page offsets: MFMA column c of a tile is page offset c.  A tile whose first
+// token sits at offset r of its page is read rotated: column c takes the tile's
+// input token (c - r) mod 16 (the rows stay in input order in LDS).  So a tile
+// of 16 consecutive slots from offset 0 is one page image, and a tile whose
+// first 16 - r tokens end one page and whose last r tokens start another (a
+// sequence of a prefill batch that began at any token) is one image of two
+// page parts, offsets r..15 for the first page and 0..r-1 for the second.
 //
 // HAD: the layer's rotation is a randomised Hadamard matrix, all entries
 // +-rscale: R k = rscale (sign pattern) k, one exact bf16 pass instead of three.
@@ -253,6 +281,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
   __shared__ __attribute__((aligned(16))) unsigned char img[PG::bytes];
   __shared__ float gpart[8][16], vmin[8][16], vmax[8][16];
   __shared__ __attribute__((aligned(16))) u32x4 s_hi[8][4][64];  // S_hi operands per wave and K-step
+  __shared__ __attribute__((aligned(16))) long long sring[P][16];  // slots of the tiles in the ring
 
   // ---- this wave's R and S operands (row tile w), kept for the whole launch
   bf16x8 R0[4], R1[HAD ? 1 : 4], R2[HAD ? 1 : 4];
@@ -302,6 +331,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       if (n >= a.n_tokens) n = 0;
       copy_to_lds(base + n * stride + static_cast<long long>(h) * 128 + q * 8, dst);
     }
+    // slots 2w, 2w + 1 of the tile (one lane, 16 bytes); past the end, the last
+    // two slots of the input (at least 64 tokens) stand in and are not used
+    if (lane == 0) {
+      long long i = tile * 16 + 2 * w;
+      if (i + 2 > a.n_tokens) i = a.n_tokens - 2;
+      copy_to_lds(slots + i, &sring[slot][2 * w]);
+    }
   };
 
   const long long first = blockIdx.x, step = gridDim.x;
@@ -312,7 +348,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
   if constexpr (KB == 1 || KB == 3) {  // key-code words are OR-ed into; each tile's store clears them again
     for (int i = static_cast<int>(threadIdx.x); i < PG::ks / 4; i += 512) reinterpret_cast<unsigned*>(img)[i] = 0u;
   }
-  unsigned clean = 0;  // bit i: iteration k-1-i issued one copy and one page store
+  unsigned clean = 0;  // bit i: iteration k-1-i issued two copies and one page store
   int slot = 0;  // k mod P
   for (int k = 0; k < mine; ++k, slot = (slot == P - 1) ? 0 : slot + 1) {
     const long long tile = first + static_cast<long long>(k) * step;
@@ -323,32 +359,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     asm volatile("" : "+v"(lane));
     const int tid = 64 * w + lane;
     const int col = lane & 15, kg = lane >> 4;
-    int after;  // operations known to be issued after this tile's copy
+    int after;  // operations known to be issued after this tile's copies
     if (k < P) {
-      after = pro - 1 - k;
+      after = 2 * (pro - 1 - k);
     } else if ((clean & ((1u << P) - 1)) == (1u << P) - 1) {
-      after = 2 * P - 1;
+      after = 3 * P - 2;
     } else {
       const int last = (k - 1 < mine - 1 - P) ? k - 1 : mine - 1 - P;
-      after = last - (k - P + 1) + 1;
+      after = 2 * (last - (k - P + 1) + 1);
     }
     wait_vmcnt_upto<P>(after);
-    // ---- slots of the tile (scalar loads), whole-page test
-    long long sl[16];
+    __syncthreads();  // tile rows and slots in LDS (every wave waited on its copies)
+    // ---- the tile's slots (lane j < 16: input token j) and its store mode:
+    // whole page (r = 0, 16 consecutive slots), two page parts (16 - r
+    // consecutive slots from offset r, then r from offset 0 of a page), or
+    // token by token
+    const long long n0 = tile * 16;
+    const long long sj = (n0 + (lane & 15) < a.n_tokens) ? sring[slot][lane & 15] : -1;
+    const long long sA = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj)) |
+                         (static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj >> 32))) << 32);
+    const int r = sA >= 0 ? static_cast<int>(sA & 15) : 0;
+    const int na = 16 - r;  // tokens of the first part
+    const long long sB = r > 0 ? (static_cast<long long>(__builtin_amdgcn_readlane(static_cast<unsigned>(sj), na)) |
+                                  (static_cast<long long>(__builtin_amdgcn_readlane(static_cast<unsigned>(sj >> 32), na)) << 32))
+                               : sA;
+    int mode;  // 1 whole page, 2 two page parts, 0 token by token
     {
-      const long long n0 = tile * 16;
-      if (n0 + 16 <= a.n_tokens) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sl[j] = slots[n0 + j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sl[j] = (n0 + j < a.n_tokens) ? slots[n0 + j] : -1;
-      }
+      const int jj = lane & 15;
+      const long long want = jj < na ? sA + jj : sB + (jj - na);
+      const bool ok = sA >= 0 && sB >= 0 && (sB & 15) == (r > 0 ? 0 : sA & 15) && sj == want;
+      const bool all = (__builtin_amdgcn_ballot_w64(ok) & 0xffffull) == 0xffffull;
+      mode = all ? (r == 0 ? 1 : 2) : 0;
     }
-    bool full = sl[0] >= 0 && (sl[0] & 15) == 0;
-#pragma unroll
-    for (int j = 1; j < 16; ++j) full = full && sl[j] == sl[0] + j;
-    __syncthreads();  // tile rows in LDS (every wave waited on its copy)
+    const bool full = mode == 1;
 
     // ---- B1: T = R k, V = R v (row tile w, 16 tokens), and every wave's own
     // ||k||^2: the Gram product of the tile's key rows with themselves, whose
@@ -358,11 +401,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     // is both the A row (token col) and the B column (token col) of the step.
     floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f}, V = {0.0f, 0.0f, 0.0f, 0.0f}, NK = {0.0f, 0.0f, 0.0f, 0.0f};
     floatx4 NV = {0.0f, 0.0f, 0.0f, 0.0f};  // MSE-coded values: the values' Gram product
+    const int row = (col - r) & 15;  // input token of column (page offset) col
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int pos = (4 * s + kg + col) & 15;  // chunk 4s + kg of token col
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][0][col][8 * pos]);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][1][col][8 * pos]);
+      const int pos = (4 * s + kg + row) & 15;  // chunk 4s + kg of that token
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][0][row][8 * pos]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&kv_in[slot][1][row][8 * pos]);
       T = mfma_b(R0[s], kb, T);
       V = mfma_b(R0[s], vb, V);
       NK = mfma_b(kb, kb, NK);
@@ -406,11 +450,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       float sk2 = 0.0f, sv2 = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int pos = (4 * s + kg + col) & 15;
+        const int pos = (4 * s + kg + row) & 15;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float xk = __uint_as_float(static_cast<unsigned>(kv_in[slot][0][col][8 * pos + e]) << 16) * 0x1p100f;
-          const float xv = __uint_as_float(static_cast<unsigned>(kv_in[slot][1][col][8 * pos + e]) << 16) * 0x1p100f;
+          const float xk = __uint_as_float(static_cast<unsigned>(kv_in[slot][0][row][8 * pos + e]) << 16) * 0x1p100f;
+          const float xv = __uint_as_float(static_cast<unsigned>(kv_in[slot][1][row][8 * pos + e]) << 16) * 0x1p100f;
           sk2 = fmaf(xk, xk, sk2);
           sv2 = fmaf(xv, xv, sv2);
         }
@@ -625,7 +669,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     // ---- E: store
     if (full) {
       // one 16-byte store per wave: chunk w + 8 * lane (lane 0 is always in range)
-      unsigned char* page = a.pool + (static_cast<size_t>(sl[0] >> 4) * a.H + h) * a.block_bytes;
+      unsigned char* page = a.pool + (static_cast<size_t>(sA >> 4) * a.H + h) * a.block_bytes;
       const int c = w + 8 * lane;
       if (c < kChunks) {
         *reinterpret_cast<u32x4*>(page + 16 * c) = *reinterpret_cast<const u32x4*>(&img[16 * c]);
@@ -633,11 +677,75 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
           if (c < PG::ks / 16) *reinterpret_cast<u32x4*>(&img[16 * c]) = u32x4{0u, 0u, 0u, 0u};
         }
       }
+    } else if (mode == 2) {
+      // two page parts: offsets r..15 of the image to page A, 0..r-1 to page B.
+      // Per-token fields move in units of 4 bytes (2 for the 16-bit magnitude
+      // and norm fields), each unit one offset's; a value-code word holds the
+      // codes of eight offsets, so a word with offsets of both parts is merged
+      // into both pages with atomic clear / set of its bits (the neighbouring
+      // tiles write the other bits of those pages' words the same way).
+      unsigned char* pa = a.pool + (static_cast<size_t>(sA >> 4) * a.H + h) * a.block_bytes;
+      unsigned char* pb = a.pool + (static_cast<size_t>(sB >> 4) * a.H + h) * a.block_bytes;
+      constexpr int nKc = 64 * KB;        // word (16 b + o) KB + i
+      constexpr int nKs = QJL ? 64 : 0;   // word 16 b + o
+      constexpr int nKn = 16;             // unit o (4 bytes with QJL, else 2)
+      constexpr int nVz = MSEV ? 16 : 64; // unit o (2 bytes), or word 4 o + G
+      for (int u = tid; u < nKc + nKs + nKn + nVz; u += 512) {
+        if (u < nKc) {
+          const int o = (u / KB) & 15;
+          *reinterpret_cast<unsigned*>((o >= r ? pa : pb) + PG::kc + 4 * u) =
+              *reinterpret_cast<const unsigned*>(&img[PG::kc + 4 * u]);
+        } else if (u < nKc + nKs) {
+          const int v = u - nKc, o = v & 15;
+          *reinterpret_cast<unsigned*>((o >= r ? pa : pb) + PG::ks + 4 * v) =
+              *reinterpret_cast<const unsigned*>(&img[PG::ks + 4 * v]);
+        } else if (u < nKc + nKs + nKn) {
+          const int o = u - nKc - nKs;
+          if constexpr (QJL)
+            *reinterpret_cast<unsigned*>((o >= r ? pa : pb) + PG::kn + 4 * o) =
+                *reinterpret_cast<const unsigned*>(&img[PG::kn + 4 * o]);
+          else
+            *reinterpret_cast<unsigned short*>((o >= r ? pa : pb) + PG::kn + 2 * o) =
+                *reinterpret_cast<const unsigned short*>(&img[PG::kn + 2 * o]);
+        } else {
+          const int v = u - nKc - nKs - nKn;
+          if constexpr (MSEV)
+            *reinterpret_cast<unsigned short*>((v >= r ? pa : pb) + PG::vsz + 2 * v) =
+                *reinterpret_cast<const unsigned short*>(&img[PG::vsz + 2 * v]);
+          else
+            *reinterpret_cast<unsigned*>(((v >> 2) >= r ? pa : pb) + PG::vsz + 4 * v) =
+                *reinterpret_cast<const unsigned*>(&img[PG::vsz + 4 * v]);
+        }
+      }
+      // value-code words: word u holds offsets 8 hh .. 8 hh + 7, hh = u / (32 VB)
+      for (int u = tid; u < 64 * VB; u += 512) {
+        const unsigned x = *reinterpret_cast<const unsigned*>(&img[PG::vc + 4 * u]);
+        const int hh = u / (32 * VB), rs = r >> 3;
+        const unsigned ma = hh > rs ? ~0u : (hh < rs ? 0u : vc_upper_mask<VB>(u % (2 * VB), r & 7));
+        unsigned* wa = reinterpret_cast<unsigned*>(pa + PG::vc) + u;
+        unsigned* wb = reinterpret_cast<unsigned*>(pb + PG::vc) + u;
+        if (ma == ~0u) {
+          *wa = x;
+        } else if (ma == 0u) {
+          *wb = x;
+        } else {
+          atomicAnd(wa, ~ma);
+          atomicOr(wa, x & ma);
+          atomicAnd(wb, ma);
+          atomicOr(wb, x & ~ma);
+        }
+      }
+      if constexpr (KB == 1 || KB == 3) {  // clear the key-code words read above
+        for (int u = tid; u < nKc; u += 512) reinterpret_cast<unsigned*>(&img[PG::kc])[u] = 0u;
+      }
     } else {
-      // token by token: fixed-size fields copied, value-code bits set atomically
+      // token by token: fixed-size fields copied, value-code bits set atomically;
+      // image offset t holds the tile's input token (t - r) mod 16
 #pragma unroll 1
       for (int t = 0; t < 16; ++t) {
-        const long long s = sl[t];
+        const int j = (t - r) & 15;
+        // (the ring slot of this tile's slots is being refilled by now: read again)
+        const long long s = n0 + j < a.n_tokens ? slots[n0 + j] : -1;
         if (s < 0) continue;
         unsigned char* page = a.pool + (static_cast<size_t>(s >> 4) * a.H + h) * a.block_bytes;
         const int o = static_cast<int>(s & 15);

@@ -26,13 +26,15 @@ def say(*a):
 
 # ------------------------------------------------------------------ compress
 def _gpu_compress(torch, K, V, slots, num_blocks, n_heads, kb, vb, seed, layer=0, dtype="bf16", key_mode=0,
-                  rotation=0, value_mode=0):
+                  rotation=0, value_mode=0, fill=None):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     layer_obj = tq.Layer(tq.config(n_heads, kb, vb, seed=seed, layer=layer, key_mode=key_mode, rotation=rotation,
                                    value_mode=value_mode))
     k = torch.from_numpy(np.ascontiguousarray(K)).to("cuda", tdt)
     v = torch.from_numpy(np.ascontiguousarray(V)).to("cuda", tdt)
     pool = layer_obj.new_pool(num_blocks)
+    if fill is not None:
+        pool.fill_(fill)
     tq.compress_kv(layer_obj, k, v, torch.from_numpy(np.asarray(slots, np.int64)).cuda(), pool)
     torch.cuda.synchronize()
     out = pool.cpu().numpy()
@@ -250,6 +252,51 @@ def test_compress_bits_ragged_slots(kb, vb):
     untouched = [b for b in range(40) if b not in written]
     for b in untouched:
         assert not gpu[b * 8 * layout.block_bytes:(b + 1) * 8 * layout.block_bytes].any()
+
+
+@pytest.mark.parametrize("kb,vb,key_mode,value_mode", [
+    (2, 3, tq.KEY_QJL, "group"), (4, 4, tq.KEY_QJL, "group"), (3, 2, tq.KEY_MSE, "group"),
+    (1, 3, tq.KEY_QJL, "mse"), (2, 4, tq.KEY_MSE_NC, "mse"), (3, 3, tq.KEY_QJL, "group")])
+def test_compress_prefill_batch(kb, vb, key_mode, value_mode):
+    """A prefill batch through the matrix-core compressor: 14 sequences of ragged
+    lengths laid end to end in the input, each from offset 0 of its own shuffled
+    pages, so the 16-token tiles straddle two pages at many rotations (and a tile
+    holding a sequence's end and the next one's start goes token by token).
+    Written records against the oracle; every offset nobody wrote (the tail of
+    each sequence's last page, pages left free) keeps the pool's prior bytes, read
+    field by field against the oracle's pool filled the same way."""
+    torch = _torch()
+    say("compress prefill batch", kb, vb, key_mode, value_mode)
+    rng = np.random.default_rng(400 + 10 * kb + vb)
+    lens = rng.integers(17, 200, 14)
+    lens[3] = 16  # one sequence of exactly a page
+    npg = (lens + 15) // 16
+    nb = int(npg.sum()) + 3
+    perm = rng.permutation(nb)
+    slots, o = [], 0
+    for L, m in zip(lens, npg):
+        pages = perm[o:o + m]
+        o += m
+        pos = np.arange(L)
+        slots.append(pages[pos // 16].astype(np.int64) * 16 + pos % 16)
+    slots = np.concatenate(slots)
+    n = len(slots)
+    H = 8
+    K, V = synth.kv_host(410 + kb, n, H, outliers=4)
+    vm = tq.VAL_MSE if value_mode == "mse" else tq.VAL_GROUP
+    gpu = _gpu_compress(torch, K, V, slots, nb, H, kb, vb, 420, layer=kb, key_mode=key_mode, value_mode=vm,
+                        fill=0xA5)
+    st, layout, pool, res = parity.oracle_store(K, V, slots, nb, H, kb, vb, 420, layer=kb, fill=0xA5,
+                                                key_mode=KEY_MODE_NAMES[key_mode], value_mode=value_mode)
+    _check_compress(gpu, res, st, layout, H, slots, V, kb, vb)
+    unwritten = np.setdiff1d(np.arange(nb * 16), slots)
+    assert len(unwritten) > 16 * 3
+    for h in range(H):
+        g = parity.fields_at(gpu, layout, H, unwritten, h)
+        o_ = parity.fields_at(pool, layout, H, unwritten, h)
+        for key in o_:
+            a_, b_ = np.ascontiguousarray(g[key]), np.ascontiguousarray(o_[key])
+            assert a_.shape == b_.shape and a_.tobytes() == b_.tobytes(), (h, key)
 
 
 @pytest.mark.parametrize("kb,vb,n,dtype,key_mode,rotation,pages", [
