@@ -35,6 +35,8 @@
 
 #include <cmath>
 
+#include "f16_pieces.hpp"
+#include "lds_copy.hpp"
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -46,7 +48,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) unsigned char lbyte;
 
 constexpr int kRow = 136;      // float16 elements per LDS operand row (128 + pad)
 
@@ -130,39 +131,6 @@ __device__ __forceinline__ float rows_max(float x) {
   return max_raw(c, d);
 }
 
-// Two floats as float16 (RNE), packed lo | hi << 16.
-__device__ __forceinline__ unsigned pack_f16(float a, float b) {
-  unsigned r;
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-// float16(x - hi) for each half, hi = the packed float16 roundings of (a, b):
-// one mixed-precision fma per half reads its hi as float16 and writes the
-// result's half (a - hi is exact in float32, so each is the float16 rounding
-// of the exact residual).
-__device__ __forceinline__ unsigned residual_pair(float a, float b, unsigned hi) {
-  unsigned r;
-  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : "=&v"(r) : "v"(a), "v"(b), "v"(hi));
-  return r;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// One 64-lane x 16 B copy from global memory into LDS at dst + 16*lane (inline
-// asm so the compiler's waits do not drain on it; awaited with wait_vmcnt).
-// M0 is set inside the same asm statement that uses it; the compiler warns that
-// it treats M0 as reserved, and this kernel's own code uses M0 nowhere else
-// (checked in the generated code), so nothing else depends on its value.
-__device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<unsigned>(reinterpret_cast<unsigned long>((lbyte*)dst)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
-               : "memory", "m0");
-}
 
 // Page image offsets (same format as the store; MSEV: the last field is Vn
 // [16] fp16 instead of the groups' scale and zero; without QJL there is no sign

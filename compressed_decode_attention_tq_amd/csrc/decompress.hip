@@ -19,14 +19,18 @@
 
 #include <cmath>
 
+#include "f16_pieces.hpp"
+#include "lds_copy.hpp"
 #include "tq_internal.hpp"
 
 namespace tq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kARow = 136;  // float16 elements per LDS operand row (128 + pad)
 constexpr int kMaxPage = 256 * 8 + 576;  // bytes of a K4/V4 page, the largest
@@ -109,6 +113,7 @@ __device__ __forceinline__ void expand(const DArgs& a, const unsigned char* page
     sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
     zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
   }
+  float vx[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     ac[t][d0 + i] = static_cast<_Float16>(a.cent[(x >> (KB * i)) & ((1u << KB) - 1u)]);
@@ -120,10 +125,15 @@ __device__ __forceinline__ void expand(const DArgs& a, const unsigned char* page
     const unsigned char* vb = page + a.off_vc + (bit >> 3);
     const unsigned w = static_cast<unsigned>(vb[0]) | (static_cast<unsigned>(vb[1]) << 8);
     const unsigned code = (w >> (bit & 7)) & ((1u << VB) - 1u);
-    const float v = (a.vm == 1) ? sc * a.vcent[code] : fmaf(sc, static_cast<float>(code), zr);
-    const _Float16 h = static_cast<_Float16>(v);
-    avh[t][d0 + i] = h;
-    avl[t][d0 + i] = static_cast<_Float16>(v - static_cast<float>(h));
+    vx[i] = (a.vm == 1) ? sc * a.vcent[code] : fmaf(sc, static_cast<float>(code), zr);
+  }
+  // v' as float16 hi + lo of the float32 value (pieces against the same hi)
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const unsigned hh = pack_f16(vx[i], vx[i + 1]);
+    const unsigned ll = residual_pair(vx[i], vx[i + 1], hh);
+    *reinterpret_cast<unsigned*>(&avh[t][d0 + i]) = hh;
+    *reinterpret_cast<unsigned*>(&avl[t][d0 + i]) = ll;
   }
   if ((tid & 15) == 0) {
     sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
@@ -225,6 +235,266 @@ __global__ __launch_bounds__(256) void decompress_kernel(DArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- persistent
+// Inputs of 64+ tokens: one workgroup of eight waves per KV head and a share of
+// its 16-token tiles; wave w forms output dims 16w..16w+15 and keeps that
+// column tile's B operands (R hi, lo and, with QJL, P hi, lo: 64 VGPRs) in
+// registers for the whole launch, so no tile re-reads them.  Tiles stream
+// through two LDS rings: each tile's 16 slots are copied four tiles ahead and
+// its page two tiles ahead (the page address comes from the slots, which have
+// then been in LDS for two iterations), so two page reads and two slot reads
+// are in flight while a tile is expanded and contracted.  Every wave issues
+// exactly one slot copy, one page copy and kStores output stores per tile, so
+// the wait for tile k's page (and tile k+2's slots, issued before it) is a
+// counted one.
+// A tile that is not one whole aligned page reads its records from global
+// memory in the expansion (the page copied for it is not used).
+constexpr int kPageChunks = kMaxPage / 16 + 4;  // page ring slot, with room for the per-wave rounding
+
+template <int KB, int VB, bool OUT_BF16, bool QJL, bool MSEV>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decompress_ring_kernel(DArgs a) {
+  constexpr int kStores = OUT_BF16 ? 1 : 2;  // output stores per lane and tile
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kg = lane >> 4;
+
+  __shared__ __attribute__((aligned(16))) _Float16 ac[16][kARow];   // codebook values
+  __shared__ __attribute__((aligned(16))) _Float16 az[QJL ? 16 : 1][kARow];  // signs +-1
+  __shared__ __attribute__((aligned(16))) _Float16 avh[16][kARow];  // v' hi
+  __shared__ __attribute__((aligned(16))) _Float16 avl[16][kARow];  // v' lo
+  __shared__ float sn[16], sg[16];
+  // per-wave output staging; rows of 24 floats put the four row groups a lane
+  // quarter writes at once on distinct banks
+  __shared__ __attribute__((aligned(16))) float stage_k[8][16][24], stage_v[8][16][24];
+  __shared__ __attribute__((aligned(16))) u32x4 pring[3][kPageChunks];
+  __shared__ __attribute__((aligned(16))) long long sring[8][16];
+  __shared__ _Float16 cent_h[16];  // key codebook (float16 values: exact)
+  __shared__ float vcent_f[16];     // value codebook (float32)
+
+  // ---- this wave's B operands (column tile w)
+  half8 RH[4], RL[4], PH[QJL ? 4 : 1], PL[QJL ? 4 : 1];
+  {
+    const u32x4* op = a.opd + (static_cast<size_t>(g) * 8 + w) * 4 * 4 * 64 + lane;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      RH[s] = __builtin_bit_cast(half8, op[(4 * s + 0) * 64]);
+      RL[s] = __builtin_bit_cast(half8, op[(4 * s + 1) * 64]);
+      if constexpr (QJL) {
+        PH[s] = __builtin_bit_cast(half8, op[(4 * s + 2) * 64]);
+        PL[s] = __builtin_bit_cast(half8, op[(4 * s + 3) * 64]);
+      }
+    }
+  }
+  if (tid < 16) {
+    cent_h[tid] = static_cast<_Float16>(a.cent[tid]);
+    vcent_f[tid] = a.vcent[tid];
+  }
+  // Consume the operands here, so that the compiler's wait for their loads is
+  // not placed at their first use inside the tile loop, where it would also
+  // drain the copy rings every tile.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    asm volatile("" ::"v"(RH[s]), "v"(RL[s]));
+    if constexpr (QJL) asm volatile("" ::"v"(PH[s]), "v"(PL[s]));
+  }
+  wait_vmcnt<0>();
+
+  const long long n_tiles = (a.n_tokens + 15) / 16;
+  const long long first = blockIdx.x, step = gridDim.x;
+  const int mine = first < n_tiles ? static_cast<int>((n_tiles - 1 - first) / step + 1) : 0;
+  if (mine == 0) return;  // the whole workgroup (uniform)
+  auto tile_of = [&](int j) { return first + static_cast<long long>(j < mine ? j : mine - 1) * step; };
+  const int nch = static_cast<int>(a.block_bytes / 16);
+  const int per = (nch + 7) / 8;  // page chunks per wave
+
+  // slots 2w, 2w+1 of tile j (one lane; near the input's end the last two slots
+  // of the input are copied instead, so the ragged last tile's entry is not
+  // read by position)
+  auto copy_slots = [&](int j) {
+    if (lane == 0) {
+      long long i = tile_of(j) * 16 + 2 * w;
+      if (i + 2 > a.n_tokens) i = a.n_tokens - 2;
+      copy_to_lds(a.slots + i, &sring[j & 7][2 * w]);
+    }
+  };
+  // the tile's store mode from its slots in the ring: whole aligned page or not
+  auto whole_page = [&](int j, long long* s0) {
+    const long long n0 = tile_of(j) * 16;
+    const long long sj = n0 + (lane & 15) < a.n_tokens ? sring[j & 7][lane & 15] : -1;
+    const long long f = static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj))) |
+                        (static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj >> 32))) << 32);
+    *s0 = f;
+    const bool ok = f >= 0 && (f & 15) == 0 && sj == f + (lane & 15);
+    return (__builtin_amdgcn_ballot_w64(ok) & 0xffffull) == 0xffffull;
+  };
+  // page of tile j into ring slot j % 3 (every wave its share of chunks; a tile
+  // that is not a whole page copies the page of its first slot, or block 0)
+  auto copy_page = [&](int j) {
+    long long s0;
+    whole_page(j, &s0);
+    const long long blk = s0 >= 0 ? (s0 >> 4) : 0;
+    const unsigned char* src = a.pool + (static_cast<size_t>(blk) * a.H + g) * a.block_bytes;
+    if (lane < per) {
+      const int c = w * per + lane;
+      copy_to_lds(src + 16 * (c < nch ? c : 0), &pring[j % 3][w * per]);
+    }
+  };
+
+  // ---- prologue: slots of tiles 0..3, then pages of tiles 0, 1
+  for (int j = 0; j < 4; ++j) copy_slots(j);
+  wait_vmcnt<0>();
+  __syncthreads();
+  copy_page(0);
+  copy_page(1);
+
+  // expansion: thread tid takes token t = tid / 32, dims d0..d0+3 (each token's
+  // A-operand row is written by 32 consecutive lanes, 256 contiguous bytes)
+  const int t = tid >> 5, d0 = 4 * (tid & 31);
+#pragma unroll 1
+  for (int k = 0; k < mine; ++k) {
+    // operations issued after tile k's page copy: the page copy of tile 1
+    // (k = 0); the slot copy of tile 4, the page copy of tile 2 and the stores
+    // of tile 0 (k = 1); the stores of tile k-2, then the slot copy of k+3, the
+    // page copy of k+1 and the stores of k-1 (k >= 2)
+    if (k == 0)
+      wait_vmcnt<1>();
+    else if (k == 1)
+      wait_vmcnt<2 + kStores>();
+    else
+      wait_vmcnt<2 + 2 * kStores>();
+    __syncthreads();  // tile k's page and tile k+2's slots in LDS; tile k-1's products done
+    copy_slots(k + 4);
+    copy_page(k + 2);
+
+    // ---- expand tile k: thread (t, d0) -> A operands of token t, dims d0..d0+3
+    const long long n0 = tile_of(k) * 16;
+    long long s0;
+    const bool whole = whole_page(k, &s0);
+    {
+      long long slot;
+      const unsigned char* page;
+      if (whole) {
+        slot = s0 + t;
+        page = reinterpret_cast<const unsigned char*>(&pring[k % 3][0]);
+      } else {
+        // (the ragged last tile's ring entry holds shifted slots near the input's end)
+        slot = n0 + t < a.n_tokens ? (n0 + 16 <= a.n_tokens ? sring[k & 7][t] : a.slots[n0 + t]) : -1;
+        page = a.pool + (static_cast<size_t>(slot >= 0 ? slot >> 4 : 0) * a.H + g) * a.block_bytes;
+      }
+      const int o = static_cast<int>(slot & 15);
+      if (slot >= 0) {
+        const int blk = d0 >> 5, e0 = d0 & 31;
+        // key codes of dims d0..d0+3: 4 KB bits at bit e0 KB of the block record
+        const unsigned char* kc = page + a.off_kc + (blk * 16 + o) * 4 * KB;
+        const int bit0 = e0 * KB;
+        const unsigned kw = static_cast<unsigned>(kc[bit0 >> 3]) | (static_cast<unsigned>(kc[(bit0 >> 3) + (KB > 2 ? 1 : 0)]) << 8);
+        const unsigned kx = kw >> (bit0 & 7);
+        unsigned zb = 0u;
+        if constexpr (QJL) zb = page[a.off_ks + (blk * 16 + o) * 4 + (e0 >> 3)] >> (e0 & 7);
+        float sc, zr;
+        if constexpr (MSEV) {
+          const unsigned short vn = *reinterpret_cast<const unsigned short*>(page + a.off_vsz + o * 2);
+          sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
+          zr = 0.0f;
+        } else {
+          const unsigned sz = *reinterpret_cast<const unsigned*>(page + a.off_vsz + o * 16 + blk * 4);
+          sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
+          zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
+        }
+        _Float16 hc[4], hz[4];
+        float vx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
+          hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+          const int jd = d0 + i;
+          const unsigned e = ((16u * (o >> 3) + (jd & 15)) * 16u + 2u * (jd >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
+          const unsigned bit = e * VB;
+          const unsigned char* vb = page + a.off_vc + (bit >> 3);
+          const unsigned vw = static_cast<unsigned>(vb[0]) | (static_cast<unsigned>(vb[1]) << 8);
+          const unsigned code = (vw >> (bit & 7)) & ((1u << VB) - 1u);
+          vx[i] = MSEV ? sc * vcent_f[code] : fmaf(sc, static_cast<float>(code), zr);
+        }
+        *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
+        if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
+        // v' as float16 hi + lo of the float32 value (pieces against the same hi)
+        const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
+        *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(&avl[t][d0]) = u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
+        if ((tid & 31) == 0) {
+          if constexpr (QJL) {
+            const unsigned kn = *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4);
+            sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
+            sg[t] = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
+          } else {
+            const unsigned short kn = *reinterpret_cast<const unsigned short*>(page + a.off_kn + o * 2);
+            sn[t] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f;
+            sg[t] = 0.0f;
+          }
+        }
+      } else {
+        const half4 z4 = {static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f),
+                          static_cast<_Float16>(0.0f)};
+        *reinterpret_cast<half4*>(&ac[t][d0]) = z4;
+        if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = z4;
+        *reinterpret_cast<half4*>(&avh[t][d0]) = z4;
+        *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
+        if ((tid & 31) == 0) sn[t] = sg[t] = 0.0f;
+      }
+    }
+    __syncthreads();  // the tile's A operands
+
+    // ---- wave w: output dims 16w + col of tokens 4kg + r
+    floatx4 k1 = {0.0f, 0.0f, 0.0f, 0.0f}, k2 = k1, vv = k1;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c0 = 32 * s + 8 * kg;
+      const half8 xc = *reinterpret_cast<const half8*>(&ac[col][c0]);
+      const half8 xh = *reinterpret_cast<const half8*>(&avh[col][c0]);
+      const half8 xl = *reinterpret_cast<const half8*>(&avl[col][c0]);
+      k1 = mfma(xc, RH[s], k1);
+      k1 = mfma(xc, RL[s], k1);
+      if constexpr (QJL) {
+        const half8 xz = *reinterpret_cast<const half8*>(&az[col][c0]);
+        k2 = mfma(xz, PH[s], k2);
+        k2 = mfma(xz, PL[s], k2);
+      }
+      vv = mfma(xh, RH[s], vv);
+      vv = mfma(xh, RL[s], vv);
+      vv = mfma(xl, RH[s], vv);
+      // one K-step's A operands live at a time (next to the 64 registers of B
+      // operands): the scheduler may not hoist the next step's reads above here
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 4 * kg + r;
+      stage_k[w][tt][col] = QJL ? sn[tt] * fmaf(sg[tt], k2[r], k1[r]) : sn[tt] * k1[r];
+      stage_v[w][tt][col] = vv[r];
+    }
+    // lane l < 32: K of token l / 2, dims 8 (l % 2) .. +7; l >= 32: V likewise
+    // (bf16: one 16-byte store; fp32: two, the second covering the other half)
+    {
+      const int u = lane & 31, tt = u >> 1, half_ = u & 1;
+      const float* src = lane < 32 ? &stage_k[w][tt][0] : &stage_v[w][tt][0];
+      void* out = lane < 32 ? a.kout : a.vout;
+      const long long n = n0 + tt;
+      if (n < a.n_tokens) {
+        const size_t at = (static_cast<size_t>(n) * a.H + g) * 128 + 16 * w;
+        if constexpr (OUT_BF16) {
+          store8<true>(out, at + 8 * half_, src + 8 * half_);
+        } else {
+          float* o = static_cast<float*>(out) + at;
+          *reinterpret_cast<floatx4*>(o + 8 * half_) = *reinterpret_cast<const floatx4*>(src + 8 * half_);
+          *reinterpret_cast<floatx4*>(o + 8 * half_ + 4) = *reinterpret_cast<const floatx4*>(src + 8 * half_ + 4);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+}
+
 // Uncompressed (bypass) pages: K [16][128] token-major, V^T [128][16] dim-major (bf16).
 template <bool OUT_BF16>
 __global__ __launch_bounds__(128) void decompress_bypass_kernel(const unsigned char* pool, const long long* slots,
@@ -253,6 +523,33 @@ void* pick_v(int vb) {
     case 4: return reinterpret_cast<void*>(&decompress_kernel<KB, 4, BF>);
   }
   return nullptr;
+}
+template <int KB, bool BF, bool QJL, bool MSEV>
+void* pick_ring_v(int vb) {
+  switch (vb) {
+    case 2: return reinterpret_cast<void*>(&decompress_ring_kernel<KB, 2, BF, QJL, MSEV>);
+    case 3: return reinterpret_cast<void*>(&decompress_ring_kernel<KB, 3, BF, QJL, MSEV>);
+    case 4: return reinterpret_cast<void*>(&decompress_ring_kernel<KB, 4, BF, QJL, MSEV>);
+  }
+  return nullptr;
+}
+template <bool BF, bool QJL, bool MSEV>
+void* pick_ring_kv(int kb, int vb) {
+  switch (kb) {
+    case 1: return pick_ring_v<1, BF, QJL, MSEV>(vb);
+    case 2: return pick_ring_v<2, BF, QJL, MSEV>(vb);
+    case 3: return pick_ring_v<3, BF, QJL, MSEV>(vb);
+    case 4: return pick_ring_v<4, BF, QJL, MSEV>(vb);
+  }
+  return nullptr;
+}
+void* pick_ring(bool bf, bool qjl, bool msev, int kb, int vb) {
+  if (bf) {
+    if (qjl) return msev ? pick_ring_kv<true, true, true>(kb, vb) : pick_ring_kv<true, true, false>(kb, vb);
+    return msev ? pick_ring_kv<true, false, true>(kb, vb) : pick_ring_kv<true, false, false>(kb, vb);
+  }
+  if (qjl) return msev ? pick_ring_kv<false, true, true>(kb, vb) : pick_ring_kv<false, true, false>(kb, vb);
+  return msev ? pick_ring_kv<false, false, true>(kb, vb) : pick_ring_kv<false, false, false>(kb, vb);
 }
 template <bool BF>
 void* pick_kv(int kb, int vb) {
@@ -299,6 +596,28 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
     }
     a.vm = L->cfg.value_mode == TQ_VAL_MSE ? 1 : 0;
     a.qjl = L->cfg.key_mode == TQ_KEY_QJL ? 1 : 0;
+    if (n_tokens >= 64) {
+      // persistent ring kernel: as many workgroups over all heads as fit on the
+      // chip at once, each looping over its head's tiles
+      void* rf = pick_ring(bf, a.qjl != 0, a.vm == 1, L->cfg.k_bits, L->cfg.v_bits);
+      if (!rf) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
+                           L->cfg.v_bits);
+      int per_cu = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rf, 512, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+      const int cus = L->cu_count > 0 ? L->cu_count : 256;
+      const long long n_tiles = (n_tokens + 15) / 16;
+      long long gx = (static_cast<long long>(cus) * per_cu + H - 1) / H;
+      if (gx > n_tiles) gx = n_tiles;
+      if (gx < 1) gx = 1;
+      a.slots = slots;
+      a.kout = k_out;
+      a.vout = v_out;
+      a.n_tokens = n_tokens;
+      void* args[] = {&a};
+      hipError_t e = hipLaunchKernel(rf, dim3(static_cast<unsigned>(gx), H), dim3(512), args, 0, s);
+      if (e != hipSuccess) return fail(TQ_ERR_HIP, "decompress launch: %s", hipGetErrorString(e));
+      return TQ_OK;
+    }
     fn = bf ? pick_kv<true>(L->cfg.k_bits, L->cfg.v_bits) : pick_kv<false>(L->cfg.k_bits, L->cfg.v_bits);
     if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
                          L->cfg.v_bits);

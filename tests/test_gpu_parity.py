@@ -880,19 +880,27 @@ def test_end_to_end_hadamard_rotation():
     _end_to_end(torch, K, V, slots, table, lens, Hq, Hkv, 4, 4, 280, rotation=tq.ROT_HADAMARD, label="hadamard")
 
 
-@pytest.mark.parametrize("kb,vb,key_mode,rotation,out_dtype", [
-    (4, 4, tq.KEY_QJL, tq.ROT_HAAR, "f32"), (3, 2, tq.KEY_MSE_NC, tq.ROT_HADAMARD, "f32"),
-    (2, 3, tq.KEY_QJL, tq.ROT_HAAR, "bf16"), (1, 3, tq.KEY_QJL, tq.ROT_HADAMARD, "f32")])
-def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype):
-    """Keys and values reconstructed from a GPU-written store (shuffled slots, some
-    negative: zero rows) against the oracle's reconstruction of the same bytes."""
+@pytest.mark.parametrize("kb,vb,key_mode,rotation,out_dtype,slot_kind", [
+    (4, 4, tq.KEY_QJL, tq.ROT_HAAR, "f32", "shuffled"), (3, 2, tq.KEY_MSE_NC, tq.ROT_HADAMARD, "f32", "shuffled"),
+    (2, 3, tq.KEY_QJL, tq.ROT_HAAR, "bf16", "shuffled"), (1, 3, tq.KEY_QJL, tq.ROT_HADAMARD, "f32", "shuffled"),
+    (4, 4, tq.KEY_QJL, tq.ROT_HAAR, "f32", "pages"), (3, 2, tq.KEY_MSE_NC, tq.ROT_HADAMARD, "bf16", "pages"),
+    (2, 3, tq.KEY_QJL, tq.ROT_HAAR, "bf16", "pages"), (3, 4, tq.KEY_MSE, tq.ROT_HAAR, "f32", "pages")])
+def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype, slot_kind):
+    """Keys and values reconstructed from a GPU-written store against the oracle's
+    reconstruction of the same bytes.  Shuffled slots (every tile read record by
+    record), or consecutive slots (whole pages through the kernel's page ring, a
+    ragged last tile); some read slots negative (zero rows, and a tile that is no
+    longer one whole page)."""
     from oracle import decompress as odec
     torch = _torch()
-    say("decompress", kb, vb, key_mode, rotation, out_dtype)
+    say("decompress", kb, vb, key_mode, rotation, out_dtype, slot_kind)
     H, n = 8, 613
     K, V = synth.kv_host(300 + kb, n, H, outliers=4)
     rng = np.random.default_rng(kb)
-    slots = rng.permutation(48 * 16)[:n].astype(np.int64)
+    if slot_kind == "pages":
+        slots = np.arange(n, dtype=np.int64)
+    else:
+        slots = rng.permutation(48 * 16)[:n].astype(np.int64)
     layer = tq.Layer(tq.config(H, kb, vb, seed=290, layer=kb, key_mode=key_mode, rotation=rotation))
     pool = layer.new_pool(48)
     tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
