@@ -346,18 +346,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     const long long sj = (n0 + (lane & 15) < a.n_tokens) ? sring[slot][lane & 15] : -1;
     const long long sA = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj)) |
                          (static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj >> 32))) << 32);
-    const int r = sA >= 0 ? static_cast<int>(sA & 15) : 0;
-    const int na = 16 - r;  // tokens of the first part
-    const long long sB = r > 0 ? (static_cast<long long>(__builtin_amdgcn_readlane(static_cast<unsigned>(sj), na)) |
+    const int rot = sA >= 0 ? static_cast<int>(sA & 15) : 0;  // page offset of the tile's first token
+    const int na = 16 - rot;  // tokens of the first part
+    const long long sB = rot > 0 ? (static_cast<long long>(__builtin_amdgcn_readlane(static_cast<unsigned>(sj), na)) |
                                   (static_cast<long long>(__builtin_amdgcn_readlane(static_cast<unsigned>(sj >> 32), na)) << 32))
                                : sA;
     int mode;  // 1 whole page, 2 two page parts, 0 token by token
     {
       const int jj = lane & 15;
       const long long want = jj < na ? sA + jj : sB + (jj - na);
-      const bool ok = sA >= 0 && sB >= 0 && (sB & 15) == (r > 0 ? 0 : sA & 15) && sj == want;
+      const bool ok = sA >= 0 && sB >= 0 && (sB & 15) == (rot > 0 ? 0 : sA & 15) && sj == want;
       const bool all = (__builtin_amdgcn_ballot_w64(ok) & 0xffffull) == 0xffffull;
-      mode = all ? (r == 0 ? 1 : 2) : 0;
+      mode = all ? (rot == 0 ? 1 : 2) : 0;
     }
     const bool full = mode == 1;
 
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
     // is both the A row (token col) and the B column (token col) of the step.
     floatx4 T = {0.0f, 0.0f, 0.0f, 0.0f}, V = {0.0f, 0.0f, 0.0f, 0.0f}, NK = {0.0f, 0.0f, 0.0f, 0.0f};
     floatx4 NV = {0.0f, 0.0f, 0.0f, 0.0f};  // MSE-coded values: the values' Gram product
-    const int row = (col - r) & 15;  // input token of column (page offset) col
+    const int row = (col - rot) & 15;  // input token of column (page offset) col
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int pos = (4 * s + kg + row) & 15;  // chunk 4s + kg of that token
@@ -661,35 +661,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       for (int u = tid; u < nKc + nKs + nKn + nVz; u += 512) {
         if (u < nKc) {
           const int o = (u / KB) & 15;
-          *reinterpret_cast<unsigned*>((o >= r ? pa : pb) + PG::kc + 4 * u) =
+          *reinterpret_cast<unsigned*>((o >= rot ? pa : pb) + PG::kc + 4 * u) =
               *reinterpret_cast<const unsigned*>(&img[PG::kc + 4 * u]);
         } else if (u < nKc + nKs) {
           const int v = u - nKc, o = v & 15;
-          *reinterpret_cast<unsigned*>((o >= r ? pa : pb) + PG::ks + 4 * v) =
+          *reinterpret_cast<unsigned*>((o >= rot ? pa : pb) + PG::ks + 4 * v) =
               *reinterpret_cast<const unsigned*>(&img[PG::ks + 4 * v]);
         } else if (u < nKc + nKs + nKn) {
           const int o = u - nKc - nKs;
           if constexpr (QJL)
-            *reinterpret_cast<unsigned*>((o >= r ? pa : pb) + PG::kn + 4 * o) =
+            *reinterpret_cast<unsigned*>((o >= rot ? pa : pb) + PG::kn + 4 * o) =
                 *reinterpret_cast<const unsigned*>(&img[PG::kn + 4 * o]);
           else
-            *reinterpret_cast<unsigned short*>((o >= r ? pa : pb) + PG::kn + 2 * o) =
+            *reinterpret_cast<unsigned short*>((o >= rot ? pa : pb) + PG::kn + 2 * o) =
                 *reinterpret_cast<const unsigned short*>(&img[PG::kn + 2 * o]);
         } else {
           const int v = u - nKc - nKs - nKn;
           if constexpr (MSEV)
-            *reinterpret_cast<unsigned short*>((v >= r ? pa : pb) + PG::vsz + 2 * v) =
+            *reinterpret_cast<unsigned short*>((v >= rot ? pa : pb) + PG::vsz + 2 * v) =
                 *reinterpret_cast<const unsigned short*>(&img[PG::vsz + 2 * v]);
           else
-            *reinterpret_cast<unsigned*>(((v >> 2) >= r ? pa : pb) + PG::vsz + 4 * v) =
+            *reinterpret_cast<unsigned*>(((v >> 2) >= rot ? pa : pb) + PG::vsz + 4 * v) =
                 *reinterpret_cast<const unsigned*>(&img[PG::vsz + 4 * v]);
         }
       }
       // value-code words: word u holds offsets 8 hh .. 8 hh + 7, hh = u / (32 VB)
       for (int u = tid; u < 64 * VB; u += 512) {
         const unsigned x = *reinterpret_cast<const unsigned*>(&img[PG::vc + 4 * u]);
-        const int hh = u / (32 * VB), rs = r >> 3;
-        const unsigned ma = hh > rs ? ~0u : (hh < rs ? 0u : vc_upper_mask<VB>(u % (2 * VB), r & 7));
+        const int hh = u / (32 * VB), rs = rot >> 3;
+        const unsigned ma = hh > rs ? ~0u : (hh < rs ? 0u : vc_upper_mask<VB>(u % (2 * VB), rot & 7));
         unsigned* wa = reinterpret_cast<unsigned*>(pa + PG::vc) + u;
         unsigned* wb = reinterpret_cast<unsigned*>(pb + PG::vc) + u;
         if (ma == ~0u) {
@@ -708,10 +708,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       }
     } else {
       // token by token: fixed-size fields copied, value-code bits set atomically;
-      // image offset t holds the tile's input token (t - r) mod 16
+      // image offset t holds the tile's input token (t - rot) mod 16
 #pragma unroll 1
       for (int t = 0; t < 16; ++t) {
-        const int j = (t - r) & 15;
+        const int j = (t - rot) & 15;
         // (the ring slot of this tile's slots is being refilled by now: read again)
         const long long s = n0 + j < a.n_tokens ? slots[n0 + j] : -1;
         if (s < 0) continue;
