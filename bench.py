@@ -57,12 +57,16 @@ def log(*a):
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_by_workload.txt")
 # kernels whose HBM traffic is taken from counters: (kernel, workload tag) -> (grid in
-# workgroups x*y*z, or None for any grid; the sources that define the kernel)
+# workgroups x*y*z, or None for any grid; the sources that define the kernel; which
+# half of the matching dispatches in launch order: None all, 0 the first, 1 the second
+# -- the compress workload launches the contiguous store, then the prefill batch)
 TRAFFIC_KERNELS = {
-    ("splitk_mfma_kernel<4,4,4,false,true>", "serving"): (8 * 8 * 64, ["decode_mainloop.hip", "split_items.hpp"]),
-    ("splitk_mfma_kernel<4,4,4,false,true>", "layer"): (4 * 8 * 16, ["decode_mainloop.hip", "split_items.hpp"]),
-    ("splitk_mfma_kernel<4,3,2,false,true>", "long"): (64 * 8 * 1, ["decode_mainloop.hip", "split_items.hpp"]),
-    ("compress_mfma_kernel<2,3,3,false,true,false>", "compress"): (None, ["compress_mfma.hip"]),
+    ("splitk_mfma_kernel<4,4,4,false,true>", "serving"): (8 * 8 * 64, ["decode_mainloop.hip", "split_items.hpp"], None),
+    ("splitk_mfma_kernel<4,4,4,false,true>", "layer"): (4 * 8 * 16, ["decode_mainloop.hip", "split_items.hpp"], None),
+    ("splitk_mfma_kernel<4,3,2,false,true>", "long"): (64 * 8 * 1, ["decode_mainloop.hip", "split_items.hpp"], None),
+    ("compress_mfma_kernel<2,3,3,false,true,false>", "compress"): (None, ["compress_mfma.hip"], 0),
+    ("compress_mfma_kernel<2,3,3,false,true,false>", "compress-prefill"): (None, ["compress_mfma.hip"], 1),
+    ("decompress_ring_kernel<4,4,true,true,false>", "decompress"): (None, ["decompress.hip"], None),
 }
 
 
@@ -131,7 +135,7 @@ def traffic_summary(fetch_csv, write_csv, mib):
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
             grid[key] = int(r.get("Grid_Size", 0) or 0) // max(int(r.get("Workgroup_Size", 1) or 1), 1)
         out = {}
-        for (name, d), v in vals.items():
+        for (name, d), v in sorted(vals.items(), key=lambda kv: int(kv[0][1])):
             out.setdefault((_norm(name), grid[(name, d)]), []).append(v * 1024.0)
         return out
 
@@ -143,16 +147,22 @@ def traffic_summary(fetch_csv, write_csv, mib):
     f_scale = nbytes / statistics.median(fetch[probe[0]])
     w_scale = nbytes / statistics.median(write[probe[0]])
     lines = ["copy_probe bytes=%d fetch_factor=%.4f write_factor=%.4f" % (nbytes, f_scale, w_scale)]
-    for (kern, tag), (wgs, files) in TRAFFIC_KERNELS.items():
+    def part(vals, half):
+        if half is None:
+            return vals
+        m = len(vals) // 2
+        return vals[:m] if half == 0 else vals[m:]
+
+    for (kern, tag), (wgs, files, half) in TRAFFIC_KERNELS.items():
         keys = [k for k in fetch if k[0] == kern and (wgs is None or k[1] == wgs)]
-        if not keys:
+        if not keys or (half is not None and len(fetch[keys[0]]) < 2):
             continue
         k = keys[0]
-        fb = statistics.median(fetch[k]) * f_scale
-        wb = statistics.median(write[k]) * w_scale
+        fb = statistics.median(part(fetch[k], half)) * f_scale
+        wb = statistics.median(part(write[k], half)) * w_scale
         lines.append("kernel=%s workload=%s grid_wgs=%d sources_sha=%s fetch_bytes=%d write_bytes=%d "
                      "traffic_bytes=%d dispatches=%d" % (kern, tag, k[1], sources_sha(files), fb, wb, fb + wb,
-                                                          len(fetch[k])))
+                                                          len(part(fetch[k], half))))
     return lines
 
 
@@ -472,7 +482,9 @@ def _prefill_batch_leg(torch, tq, synth, args, layer, k, v, N, H, rec):
     nbytes = N * H * (512 + rec) + N * 8
     del pool
     return {"sequences": len(lens), "tokens": N, "avg_us": round(avg_s * 1e6, 1),
-            "mtok_s": round(N / avg_s / 1e6, 2), "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
+            "mtok_s": round(N / avg_s / 1e6, 2), "frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": nbytes,
+            "traffic": traffic_for("compress_mfma_kernel<2,3,3,false,true,false>", "compress-prefill")}
 
 
 def _time_steps(torch, fn, n):
@@ -543,10 +555,12 @@ def decompress_workload(torch, tq, synth, args):
     # matrix-core floor: 7 passes x 4 K-steps x 8 column tiles per 16 token-heads,
     # 16 cycles each at 1024 SIMDs x 2.4 GHz
     mfma_us = N * Hkv / 16 * 224 * 16 / (1024 * 2.4e9) * 1e6
+    kern = "decompress_ring_kernel<4,4,true,true,false>"
     return {"workload": "decompress-llama3-8b-layer-store", "token_heads": N * Hkv, "out_dtype": "bf16",
             "ms": round(ms, 4), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
             "frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
-            "mfma_floor_us": round(mfma_us, 1)}
+            "mfma_floor_us": round(mfma_us, 1),
+            "roofline": _roofline(nbytes, ms * 1e3, kern, 50, traffic_for(kern, "decompress"))}
 
 
 def mse_values_workload(torch, tq, synth, args):
