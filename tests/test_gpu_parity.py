@@ -563,22 +563,25 @@ def _decode_case(torch, B, Hq, Hkv, lens, kb, vb, seed, table_kind="random", q_d
     return results
 
 
-@pytest.mark.parametrize("bypass", [False, True])
-def test_decode_work_list_matches_plain_order(bypass):
+@pytest.mark.parametrize("bypass,kb,vb,value_mode,key_mode", [
+    (False, 3, 3, 0, 0), (True, 4, 4, 0, 0), (False, 2, 3, 1, 0), (False, 4, 2, 0, 2)])
+def test_decode_work_list_matches_plain_order(bypass, kb, vb, value_mode, key_mode):
     """Ragged batches through the split-K work list and through the plain item order:
     the same output bit for bit (each item's arithmetic does not depend on where
     it sits in the grid) and parity with the oracle.  300 sequences (two passes of
     the per-wave count), empty and one-token sequences, lengths on and around the
-    split boundary, 64-token splits (a grid of 9,600 workgroups), 2 KV heads."""
+    split boundary, 64-token splits (a grid of 9,600 workgroups), 2 KV heads; group
+    or codebook-coded values, keys with QJL or the compact page without it, and
+    uncompressed layers."""
     torch = _torch()
-    say("decode work list vs plain order", bypass)
+    say("decode work list vs plain order", bypass, kb, vb, value_mode, key_mode)
     rng = np.random.default_rng(63)
     lens = rng.integers(1, 300, 300).astype(np.int32)
     lens[::11] = 0
     lens[[3, 4, 5, 6]] = [1, 64, 65, 128]
     lens[200] = 1000
-    _decode_case(torch, 300, 8, 2, lens, 3, 3, 291, num_splits=16, out_dtypes=("f32",), bypass=bypass,
-                 orders=("1", "0"))
+    _decode_case(torch, 300, 8, 2, lens, kb, vb, 291, num_splits=16, out_dtypes=("f32",), bypass=bypass,
+                 value_mode=value_mode, key_mode=key_mode, orders=("1", "0"))
 
 
 def test_decode_tiny_fp32():
