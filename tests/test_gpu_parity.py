@@ -1235,3 +1235,19 @@ def test_debug_checks_refuse_bad_indices(monkeypatch):
         tq.decode_attn(layer, q, pool, bt, sl, 48)
     assert "seq_lens[1]" in str(e.value)
     layer.close()
+
+
+def test_decode_plan_grid_limit():
+    """The split-K grid (batch x KV heads x splits workgroups, one-dimensional) must
+    stay below 2^31: the plan refuses larger ones with TQ_ERR_UNSUPPORTED instead of
+    launching a truncated grid (host arithmetic only, no kernel)."""
+    _torch()
+    layer = tq.Layer(tq.config(8, 4, 4))
+    try:
+        ok = tq.decode_workspace_size(layer, 1 << 16, 32, 1 << 20)  # 65,536 x 8 x 256 splits = 2^27
+        assert ok > 0
+        with pytest.raises(tq.TQError) as e:
+            tq.decode_workspace_size(layer, 1 << 20, 32, 1 << 20)  # 2^20 x 8 x 256 = 2^31
+        assert e.value.status == tq.ERR_UNSUPPORTED and "exceeds" in str(e.value)
+    finally:
+        layer.close()
