@@ -235,6 +235,19 @@ __global__ __launch_bounds__(256) void decompress_kernel(DArgs a) {
   }
 }
 
+// Loads of T at byte address p, typed by address space: an LDS page image
+// (ds_read) or a page in global memory, so that the common path is never a
+// FLAT access (whose waits would also cover the in-flight copies).
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+template <typename T>
+__device__ __forceinline__ T ld(const lds_byte* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
+}
+template <typename T>
+__device__ __forceinline__ T ld(const unsigned char* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
 // ---------------------------------------------------------------- persistent
 // Inputs of 64+ tokens: one workgroup of eight waves per KV head and a share of
 // its 16-token tiles; wave w forms output dims 16w..16w+15 and keeps that
@@ -251,6 +264,26 @@ __global__ __launch_bounds__(256) void decompress_kernel(DArgs a) {
 // memory in the expansion (the page copied for it is not used).
 constexpr int kPageChunks = kMaxPage / 16 + 4;  // page ring slot, with room for the per-wave rounding
 
+// Field offsets of a compressed page as a function of the variant: Kc [16
+// tokens x 4 blocks] of 4 KB bytes, Ks (QJL) 4 bytes each, Kn (n, gamma) or
+// n, Vc lane-blocked VB-bit codes, then per-group scale/zero or one norm.
+// The ring kernel takes them as constants (every field read is then a fixed
+// offset from one per-lane address); its launcher checks them against the
+// layer's layout.
+struct PageFields {
+  unsigned kc, ks, kn, vc, vsz, bytes;
+};
+__host__ __device__ constexpr PageFields page_fields(int kb, int vb, bool qjl, bool msev) {
+  PageFields f{};
+  f.kc = 0;
+  f.ks = f.kc + 16u * (kDim * kb / 8);
+  f.kn = f.ks + (qjl ? 16u * (kDim / 8) : 0u);
+  f.vc = f.kn + 16u * (qjl ? 4u : 2u);
+  f.vsz = f.vc + 16u * (kDim * vb / 8);
+  f.bytes = f.vsz + 16u * (msev ? 2u : 4u * (kDim / kGroup));
+  return f;
+}
+
 template <int KB, int VB, bool OUT_BF16, bool QJL, bool MSEV>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decompress_ring_kernel(DArgs a) {
   constexpr int kStores = OUT_BF16 ? 1 : 2;  // output stores per lane and tile
@@ -259,14 +292,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, kg = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) _Float16 ac[16][kARow];   // codebook values
-  __shared__ __attribute__((aligned(16))) _Float16 az[QJL ? 16 : 1][kARow];  // signs +-1
-  __shared__ __attribute__((aligned(16))) _Float16 avh[16][kARow];  // v' hi
-  __shared__ __attribute__((aligned(16))) _Float16 avl[16][kARow];  // v' lo
-  __shared__ float sn[16], sg[16];
-  // per-wave output staging; rows of 24 floats put the four row groups a lane
-  // quarter writes at once on distinct banks
-  __shared__ __attribute__((aligned(16))) float stage_k[8][16][24], stage_v[8][16][24];
+  // The tile's A operands (codebook values, v' hi, v' lo and, with QJL, signs
+  // +-1), the per-token scales n and gamma, and the per-wave output staging
+  // (rows of 24 floats put the four row groups a lane quarter writes at once
+  // on distinct banks), each kind as one array: an access is then one per-lane
+  // address plus a constant offset, which keeps the loop's live registers few.
+  __shared__ __attribute__((aligned(16))) _Float16 aop[QJL ? 4 : 3][16][kARow];
+  __shared__ float sng[2][16];
+  __shared__ __attribute__((aligned(16))) float stage[2][8][16][24];
+  auto& ac = aop[0];
+  auto& avh = aop[1];
+  auto& avl = aop[2];
+  auto& az = aop[QJL ? 3 : 0];  // (read and written with QJL only)
+  auto& sn = sng[0];
+  auto& sg = sng[1];
+  auto& stage_k = stage[0];
+  auto& stage_v = stage[1];
   __shared__ __attribute__((aligned(16))) u32x4 pring[3][kPageChunks];
   __shared__ __attribute__((aligned(16))) long long sring[8][16];
   __shared__ _Float16 cent_h[16];  // key codebook (float16 values: exact)
@@ -305,7 +346,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
   const int mine = first < n_tiles ? static_cast<int>((n_tiles - 1 - first) / step + 1) : 0;
   if (mine == 0) return;  // the whole workgroup (uniform)
   auto tile_of = [&](int j) { return first + static_cast<long long>(j < mine ? j : mine - 1) * step; };
-  const int nch = static_cast<int>(a.block_bytes / 16);
+  constexpr PageFields F = page_fields(KB, VB, QJL, MSEV);
+  constexpr int nch = static_cast<int>(F.bytes / 16);
   const int per = (nch + 7) / 8;  // page chunks per wave
 
   // slots 2w, 2w+1 of tile j (one lane; near the input's end the last two slots
@@ -334,7 +376,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
     long long s0;
     whole_page(j, &s0);
     const long long blk = s0 >= 0 ? (s0 >> 4) : 0;
-    const unsigned char* src = a.pool + (static_cast<size_t>(blk) * a.H + g) * a.block_bytes;
+    const unsigned char* src = a.pool + (static_cast<size_t>(blk) * a.H + g) * F.bytes;
     if (lane < per) {
       const int c = w * per + lane;
       copy_to_lds(src + 16 * (c < nch ? c : 0), &pring[j % 3][w * per]);
@@ -371,68 +413,78 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
     const long long n0 = tile_of(k) * 16;
     long long s0;
     const bool whole = whole_page(k, &s0);
-    {
-      long long slot;
-      const unsigned char* page;
-      if (whole) {
-        slot = s0 + t;
-        page = reinterpret_cast<const unsigned char*>(&pring[k % 3][0]);
+    // expansion of token t's dims d0..d0+3 from its record at in-page offset o
+    auto expand = [&](auto page, int o) {
+      const int blk = d0 >> 5, e0 = d0 & 31;
+      // key codes of dims d0..d0+3: 4 KB bits at bit e0 KB of the block record
+      // (one byte for KB <= 2, an aligned halfword for KB = 4, two bytes for 3)
+      const auto kc = page + F.kc + (blk * 16 + o) * 4 * KB + ((e0 * KB) >> 3);
+      unsigned kx;
+      if constexpr (KB == 4)
+        kx = ld<unsigned short>(kc);
+      else if constexpr (KB == 3)
+        kx = (static_cast<unsigned>(ld<unsigned char>(kc)) | (static_cast<unsigned>(ld<unsigned char>(kc + 1)) << 8)) >>
+             ((e0 * KB) & 7);
+      else
+        kx = static_cast<unsigned>(ld<unsigned char>(kc)) >> ((e0 * KB) & 7);
+      unsigned zb = 0u;
+      if constexpr (QJL) zb = static_cast<unsigned>(ld<unsigned char>(page + F.ks + (blk * 16 + o) * 4 + (e0 >> 3))) >> (e0 & 7);
+      float sc, zr;
+      if constexpr (MSEV) {
+        const unsigned short vn = ld<unsigned short>(page + F.vsz + o * 2);
+        sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
+        zr = 0.0f;
       } else {
-        // (the ragged last tile's ring entry holds shifted slots near the input's end)
-        slot = n0 + t < a.n_tokens ? (n0 + 16 <= a.n_tokens ? sring[k & 7][t] : a.slots[n0 + t]) : -1;
-        page = a.pool + (static_cast<size_t>(slot >= 0 ? slot >> 4 : 0) * a.H + g) * a.block_bytes;
+        const unsigned sz = ld<unsigned>(page + F.vsz + o * 16 + blk * 4);
+        sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
+        zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
       }
-      const int o = static_cast<int>(slot & 15);
-      if (slot >= 0) {
-        const int blk = d0 >> 5, e0 = d0 & 31;
-        // key codes of dims d0..d0+3: 4 KB bits at bit e0 KB of the block record
-        const unsigned char* kc = page + a.off_kc + (blk * 16 + o) * 4 * KB;
-        const int bit0 = e0 * KB;
-        const unsigned kw = static_cast<unsigned>(kc[bit0 >> 3]) | (static_cast<unsigned>(kc[(bit0 >> 3) + (KB > 2 ? 1 : 0)]) << 8);
-        const unsigned kx = kw >> (bit0 & 7);
-        unsigned zb = 0u;
-        if constexpr (QJL) zb = page[a.off_ks + (blk * 16 + o) * 4 + (e0 >> 3)] >> (e0 & 7);
-        float sc, zr;
-        if constexpr (MSEV) {
-          const unsigned short vn = *reinterpret_cast<const unsigned short*>(page + a.off_vsz + o * 2);
-          sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
-          zr = 0.0f;
-        } else {
-          const unsigned sz = *reinterpret_cast<const unsigned*>(page + a.off_vsz + o * 16 + blk * 4);
-          sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
-          zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
-        }
-        _Float16 hc[4], hz[4];
-        float vx[4];
+      // value codes: element ((16 (o / 8) + jd % 16) 16 + 2 (jd / 16) + (o % 8) / 4) 4 + o % 4
+      // of the Vc field; dims d0 + i step the element by 64, so the byte by 8 VB
+      // and the bit position within it stays (one byte for VB = 2, 4; two for 3)
+      const unsigned e = ((16u * (o >> 3) + (d0 & 15)) * 16u + 2u * (d0 >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
+      const auto vb = page + F.vc + ((e * VB) >> 3);
+      const unsigned vsh = (e * VB) & 7;
+      _Float16 hc[4], hz[4];
+      float vx[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
-          hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-          const int jd = d0 + i;
-          const unsigned e = ((16u * (o >> 3) + (jd & 15)) * 16u + 2u * (jd >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
-          const unsigned bit = e * VB;
-          const unsigned char* vb = page + a.off_vc + (bit >> 3);
-          const unsigned vw = static_cast<unsigned>(vb[0]) | (static_cast<unsigned>(vb[1]) << 8);
-          const unsigned code = (vw >> (bit & 7)) & ((1u << VB) - 1u);
-          vx[i] = MSEV ? sc * vcent_f[code] : fmaf(sc, static_cast<float>(code), zr);
+      for (int i = 0; i < 4; ++i) {
+        hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
+        hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+        unsigned vw = ld<unsigned char>(vb + 8 * VB * i);
+        if constexpr (VB == 3) vw |= static_cast<unsigned>(ld<unsigned char>(vb + 8 * VB * i + 1)) << 8;
+        const unsigned code = (vw >> vsh) & ((1u << VB) - 1u);
+        vx[i] = MSEV ? sc * vcent_f[code] : fmaf(sc, static_cast<float>(code), zr);
+      }
+      *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
+      if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
+      // v' as float16 hi + lo of the float32 value (pieces against the same hi)
+      const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
+      *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
+      *reinterpret_cast<u32x2*>(&avl[t][d0]) = u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
+      if ((tid & 31) == 0) {
+        if constexpr (QJL) {
+          const unsigned kn = ld<unsigned>(page + F.kn + o * 4);
+          sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
+          sg[t] = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
+        } else {
+          const unsigned short kn = ld<unsigned short>(page + F.kn + o * 2);
+          sn[t] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f;
+          sg[t] = 0.0f;
         }
-        *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
-        if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
-        // v' as float16 hi + lo of the float32 value (pieces against the same hi)
-        const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
-        *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(&avl[t][d0]) = u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
-        if ((tid & 31) == 0) {
-          if constexpr (QJL) {
-            const unsigned kn = *reinterpret_cast<const unsigned*>(page + a.off_kn + o * 4);
-            sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
-            sg[t] = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
-          } else {
-            const unsigned short kn = *reinterpret_cast<const unsigned short*>(page + a.off_kn + o * 2);
-            sn[t] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f;
-            sg[t] = 0.0f;
-          }
-        }
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    if (whole) {
+      // the page image in the ring (LDS reads)
+      expand((const lds_byte*)(&pring[k % 3][0]), t);
+    } else {
+      // (the ragged last tile's ring entry holds shifted slots near the input's end)
+      const long long slot =
+          n0 + t < a.n_tokens ? (n0 + 16 <= a.n_tokens ? sring[k & 7][t] : a.slots[n0 + t]) : -1;
+      if (slot >= 0) {
+        expand(static_cast<const unsigned char*>(a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * F.bytes),
+               static_cast<int>(slot & 15));
       } else {
         const half4 z4 = {static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f),
                           static_cast<_Float16>(0.0f)};
@@ -443,6 +495,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
         if ((tid & 31) == 0) sn[t] = sg[t] = 0.0f;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // the tile's A operands
 
     // ---- wave w: output dims 16w + col of tokens 4kg + r
@@ -477,7 +530,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
     // (bf16: one 16-byte store; fp32: two, the second covering the other half)
     {
       const int u = lane & 31, tt = u >> 1, half_ = u & 1;
-      const float* src = lane < 32 ? &stage_k[w][tt][0] : &stage_v[w][tt][0];
+      const float* src = &stage[lane >> 5][w][tt][0];
       void* out = lane < 32 ? a.kout : a.vout;
       const long long n = n0 + tt;
       if (n < a.n_tokens) {
@@ -600,6 +653,10 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
       // persistent ring kernel: as many workgroups over all heads as fit on the
       // chip at once, each looping over its head's tiles
       void* rf = pick_ring(bf, a.qjl != 0, a.vm == 1, L->cfg.k_bits, L->cfg.v_bits);
+      const PageFields f = page_fields(L->cfg.k_bits, L->cfg.v_bits, a.qjl != 0, a.vm == 1);
+      if (f.kc != L->lay.off_kc || f.ks != L->lay.off_ks || f.kn != L->lay.off_kn || f.vc != L->lay.off_vc ||
+          f.vsz != L->lay.off_vsz || f.bytes != L->lay.block_bytes)
+        return fail(TQ_ERR_UNSUPPORTED, "decompress: page layout does not match the kernel's field offsets");
       if (!rf) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
                            L->cfg.v_bits);
       int per_cu = 0;
