@@ -31,6 +31,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kARow = 136;  // float16 elements per LDS operand row (128 + pad)
 constexpr int kMaxPage = 256 * 8 + 576;  // bytes of a K4/V4 page, the largest
@@ -64,8 +65,9 @@ __device__ __forceinline__ void store8(void* out, size_t at, const float* src) {
     u32x4 pk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const unsigned lo = __float_as_uint(src[2 * i]), hi = __float_as_uint(src[2 * i + 1]);
-      pk[i] = ((lo + 0x7fffu + ((lo >> 16) & 1u)) >> 16) | (((hi + 0x7fffu + ((hi >> 16) & 1u)) >> 16) << 16);
+      // (one packed conversion, nearest even)
+      const bf16x2 b = {static_cast<__bf16>(src[2 * i]), static_cast<__bf16>(src[2 * i + 1])};
+      pk[i] = __builtin_bit_cast(unsigned, b);
     }
     *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at) = pk;
   } else {
@@ -238,7 +240,6 @@ __global__ __launch_bounds__(256) void decompress_kernel(DArgs a) {
 // Loads of T at byte address p, typed by address space: an LDS page image
 // (ds_read) or a page in global memory, so that the common path is never a
 // FLAT access (whose waits would also cover the in-flight copies).
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
 template <typename T>
 __device__ __forceinline__ T ld(const lds_byte* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
@@ -249,17 +250,19 @@ __device__ __forceinline__ T ld(const unsigned char* p) {
 }
 
 // ---------------------------------------------------------------- persistent
-// Inputs of 64+ tokens: one workgroup of eight waves per KV head and a share of
-// its 16-token tiles; wave w forms output dims 16w..16w+15 and keeps that
-// column tile's B operands (R hi, lo and, with QJL, P hi, lo: 64 VGPRs) in
-// registers for the whole launch, so no tile re-reads them.  Tiles stream
-// through two LDS rings: each tile's 16 slots are copied four tiles ahead and
-// its page two tiles ahead (the page address comes from the slots, which have
-// then been in LDS for two iterations), so two page reads and two slot reads
-// are in flight while a tile is expanded and contracted.  Every wave issues
-// exactly one slot copy, one page copy and kStores output stores per tile, so
-// the wait for tile k's page (and tile k+2's slots, issued before it) is a
-// counted one.
+// Inputs of 64+ tokens: one workgroup of sixteen waves per KV head and a share
+// of its 16-token tiles, in two roles that work on consecutive tiles at once.
+// Waves 8..15 copy and expand: each tile's 16 slots are copied into an LDS ring
+// four tiles ahead and its page two tiles ahead (the page address comes from
+// the slots, by then in LDS for two iterations), and tile k is expanded into
+// one of two A-operand buffers.  Waves 0..7 contract: wave w forms output dims
+// 16w..16w+15 of tile k-1 from the other buffer, with that column tile's B
+// operands (R hi, lo and, with QJL, P hi, lo: 64 VGPRs) held in registers for
+// the whole launch, and stores them.  One workgroup barrier per tile hands the
+// buffers over.  Every copying wave issues exactly one slot copy and one page
+// copy per tile, so its wait for tile k's page (and tile k+2's slots, issued
+// before it) is a counted one; the contracting waves never wait on memory in
+// the loop.
 // A tile that is not one whole aligned page reads its records from global
 // memory in the expansion (the page copied for it is not used).
 constexpr int kPageChunks = kMaxPage / 16 + 4;  // page ring slot, with room for the per-wave rounding
@@ -285,37 +288,36 @@ __host__ __device__ constexpr PageFields page_fields(int kb, int vb, bool qjl, b
 }
 
 template <int KB, int VB, bool OUT_BF16, bool QJL, bool MSEV>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decompress_ring_kernel(DArgs a) {
-  constexpr int kStores = OUT_BF16 ? 1 : 2;  // output stores per lane and tile
+__global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool mma = wave < 8;  // contracting role (else copying and expanding)
+  const int w = wave & 7;
   const int col = lane & 15, kg = lane >> 4;
 
-  // The tile's A operands (codebook values, v' hi, v' lo and, with QJL, signs
-  // +-1), the per-token scales n and gamma, and the per-wave output staging
-  // (rows of 24 floats put the four row groups a lane quarter writes at once
-  // on distinct banks), each kind as one array: an access is then one per-lane
-  // address plus a constant offset, which keeps the loop's live registers few.
-  __shared__ __attribute__((aligned(16))) _Float16 aop[QJL ? 4 : 3][16][kARow];
-  __shared__ float sng[2][16];
-  __shared__ __attribute__((aligned(16))) float stage[2][8][16][24];
-  auto& ac = aop[0];
-  auto& avh = aop[1];
-  auto& avl = aop[2];
-  auto& az = aop[QJL ? 3 : 0];  // (read and written with QJL only)
-  auto& sn = sng[0];
-  auto& sg = sng[1];
-  auto& stage_k = stage[0];
-  auto& stage_v = stage[1];
+  // Two buffers of a tile's A operands (codebook values, v' hi, v' lo and,
+  // with QJL, signs +-1) and of its Kn words; each kind is one array, so an
+  // access is one per-lane address plus a constant offset, which keeps the
+  // loop's live registers few.
+  constexpr int NA = QJL ? 4 : 3;
+  __shared__ __attribute__((aligned(16))) _Float16 aop[2][NA][16][kARow];
+  __shared__ __attribute__((aligned(16))) unsigned char knb[2][64];
+  // Two buffers of a tile's outputs: the K and V rows of its 16 tokens (bf16
+  // pairs or fp32 values per word; the 4-word row padding puts the rows a
+  // half wave writes at once on distinct banks).  The contracting waves write
+  // one after a tile's products and store it, as whole rows, in the next
+  // iteration.
+  constexpr int kSRow = OUT_BF16 ? 68 : 132;
+  __shared__ __attribute__((aligned(16))) unsigned stage[2][2][16][kSRow];
   __shared__ __attribute__((aligned(16))) u32x4 pring[3][kPageChunks];
   __shared__ __attribute__((aligned(16))) long long sring[8][16];
   __shared__ _Float16 cent_h[16];  // key codebook (float16 values: exact)
   __shared__ float vcent_f[16];     // value codebook (float32)
 
-  // ---- this wave's B operands (column tile w)
+  // ---- contracting waves: B operands of column tile w
   half8 RH[4], RL[4], PH[QJL ? 4 : 1], PL[QJL ? 4 : 1];
-  {
+  if (mma) {
     const u32x4* op = a.opd + (static_cast<size_t>(g) * 8 + w) * 4 * 4 * 64 + lane;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -326,20 +328,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
         PL[s] = __builtin_bit_cast(half8, op[(4 * s + 3) * 64]);
       }
     }
+    // Consume the operands here, so that the compiler's wait for their loads
+    // is not placed at their first use inside the tile loop.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      asm volatile("" ::"v"(RH[s]), "v"(RL[s]));
+      if constexpr (QJL) asm volatile("" ::"v"(PH[s]), "v"(PL[s]));
+    }
+    wait_vmcnt<0>();
   }
   if (tid < 16) {
     cent_h[tid] = static_cast<_Float16>(a.cent[tid]);
     vcent_f[tid] = a.vcent[tid];
   }
-  // Consume the operands here, so that the compiler's wait for their loads is
-  // not placed at their first use inside the tile loop, where it would also
-  // drain the copy rings every tile.
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    asm volatile("" ::"v"(RH[s]), "v"(RL[s]));
-    if constexpr (QJL) asm volatile("" ::"v"(PH[s]), "v"(PL[s]));
-  }
-  wait_vmcnt<0>();
 
   const long long n_tiles = (a.n_tokens + 15) / 16;
   const long long first = blockIdx.x, step = gridDim.x;
@@ -348,11 +349,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
   auto tile_of = [&](int j) { return first + static_cast<long long>(j < mine ? j : mine - 1) * step; };
   constexpr PageFields F = page_fields(KB, VB, QJL, MSEV);
   constexpr int nch = static_cast<int>(F.bytes / 16);
-  const int per = (nch + 7) / 8;  // page chunks per wave
+  constexpr int per = (nch + 7) / 8;  // page chunks per copying wave
 
-  // slots 2w, 2w+1 of tile j (one lane; near the input's end the last two slots
-  // of the input are copied instead, so the ragged last tile's entry is not
-  // read by position)
+  // (copying waves) slots 2w, 2w+1 of tile j (one lane; near the input's end
+  // the last two slots of the input are copied instead, so the ragged last
+  // tile's entry is not read by position)
   auto copy_slots = [&](int j) {
     if (lane == 0) {
       long long i = tile_of(j) * 16 + 2 * w;
@@ -360,21 +361,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
       copy_to_lds(a.slots + i, &sring[j & 7][2 * w]);
     }
   };
-  // the tile's store mode from its slots in the ring: whole aligned page or not
-  auto whole_page = [&](int j, long long* s0) {
+  // slot of token lane % 16 of tile j from the ring (-1 past the input's end)
+  auto ring_slot = [&](int j) {
     const long long n0 = tile_of(j) * 16;
-    const long long sj = n0 + (lane & 15) < a.n_tokens ? sring[j & 7][lane & 15] : -1;
+    return n0 + (lane & 15) < a.n_tokens ? sring[j & 7][lane & 15] : -1LL;
+  };
+  // the tile's first slot and whether its slots are one whole aligned page,
+  // from ring_slot's value in every lane (wave-uniform results)
+  auto page_of = [&](long long sj, long long* s0) {
     const long long f = static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj))) |
                         (static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(sj >> 32))) << 32);
     *s0 = f;
     const bool ok = f >= 0 && (f & 15) == 0 && sj == f + (lane & 15);
     return (__builtin_amdgcn_ballot_w64(ok) & 0xffffull) == 0xffffull;
   };
-  // page of tile j into ring slot j % 3 (every wave its share of chunks; a tile
-  // that is not a whole page copies the page of its first slot, or block 0)
-  auto copy_page = [&](int j) {
-    long long s0;
-    whole_page(j, &s0);
+  // (copying waves) page of tile j, first slot s0, into ring slot j % 3, each
+  // wave its share of chunks; a tile that is not a whole page copies the page
+  // of its first slot, or block 0
+  auto copy_page = [&](int j, long long s0) {
     const long long blk = s0 >= 0 ? (s0 >> 4) : 0;
     const unsigned char* src = a.pool + (static_cast<size_t>(blk) * a.H + g) * F.bytes;
     if (lane < per) {
@@ -383,133 +387,189 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
     }
   };
 
-  // ---- prologue: slots of tiles 0..3, then pages of tiles 0, 1
-  for (int j = 0; j < 4; ++j) copy_slots(j);
-  wait_vmcnt<0>();
+  // ---- prologue: slots of tiles 0..3, then pages of tiles 0, 1.  The first
+  // slot and whole-page flag of a tile are found once, when its page copy is
+  // issued two iterations ahead, and carried to its expansion in scalar
+  // registers (s0c, wholec: tile k; s0n, wholen: tile k+1).
+  long long s0c = 0, s0n = 0;
+  bool wholec = false, wholen = false;
+  if (!mma) {
+    for (int j = 0; j < 4; ++j) copy_slots(j);
+    wait_vmcnt<0>();
+  }
   __syncthreads();
-  copy_page(0);
-  copy_page(1);
+  if (!mma) {
+    wholec = page_of(ring_slot(0), &s0c);
+    copy_page(0, s0c);
+    wholen = page_of(ring_slot(1), &s0n);
+    copy_page(1, s0n);
+  }
 
-  // expansion: thread tid takes token t = tid / 32, dims d0..d0+3 (each token's
-  // A-operand row is written by 32 consecutive lanes, 256 contiguous bytes)
-  const int t = tid >> 5, d0 = 4 * (tid & 31);
+  // expansion: copying-wave thread u takes token t = u / 32, dims d0..d0+3
+  // (each token's A-operand row is written by 32 consecutive lanes, 256
+  // contiguous bytes)
+  const int u = tid & 511;
+  const int t = u >> 5, d0 = 4 * (u & 31);
 #pragma unroll 1
-  for (int k = 0; k < mine; ++k) {
-    // operations issued after tile k's page copy: the page copy of tile 1
-    // (k = 0); the slot copy of tile 4, the page copy of tile 2 and the stores
-    // of tile 0 (k = 1); the stores of tile k-2, then the slot copy of k+3, the
-    // page copy of k+1 and the stores of k-1 (k >= 2)
-    if (k == 0)
-      wait_vmcnt<1>();
-    else if (k == 1)
-      wait_vmcnt<2 + kStores>();
-    else
-      wait_vmcnt<2 + 2 * kStores>();
-    __syncthreads();  // tile k's page and tile k+2's slots in LDS; tile k-1's products done
-    copy_slots(k + 4);
-    copy_page(k + 2);
-
-    // ---- expand tile k: thread (t, d0) -> A operands of token t, dims d0..d0+3
-    const long long n0 = tile_of(k) * 16;
-    long long s0;
-    const bool whole = whole_page(k, &s0);
-    // expansion of token t's dims d0..d0+3 from its record at in-page offset o
-    auto expand = [&](auto page, int o) {
-      const int blk = d0 >> 5, e0 = d0 & 31;
-      // key codes of dims d0..d0+3: 4 KB bits at bit e0 KB of the block record
-      // (one byte for KB <= 2, an aligned halfword for KB = 4, two bytes for 3)
-      const auto kc = page + F.kc + (blk * 16 + o) * 4 * KB + ((e0 * KB) >> 3);
-      unsigned kx;
-      if constexpr (KB == 4)
-        kx = ld<unsigned short>(kc);
-      else if constexpr (KB == 3)
-        kx = (static_cast<unsigned>(ld<unsigned char>(kc)) | (static_cast<unsigned>(ld<unsigned char>(kc + 1)) << 8)) >>
-             ((e0 * KB) & 7);
+  for (int k = 0; k <= mine + 1; ++k) {
+    // (copying waves) operations issued after tile k's page copy: the page copy
+    // of tile 1 (k = 0); the slot copy of tile k+3 and the page copy of k+1
+    if (!mma && k < mine) {
+      if (k == 0)
+        wait_vmcnt<1>();
       else
-        kx = static_cast<unsigned>(ld<unsigned char>(kc)) >> ((e0 * KB) & 7);
-      unsigned zb = 0u;
-      if constexpr (QJL) zb = static_cast<unsigned>(ld<unsigned char>(page + F.ks + (blk * 16 + o) * 4 + (e0 >> 3))) >> (e0 & 7);
-      float sc, zr;
-      if constexpr (MSEV) {
-        const unsigned short vn = ld<unsigned short>(page + F.vsz + o * 2);
-        sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
-        zr = 0.0f;
-      } else {
-        const unsigned sz = ld<unsigned>(page + F.vsz + o * 16 + blk * 4);
-        sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
-        zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
-      }
-      // value codes: element ((16 (o / 8) + jd % 16) 16 + 2 (jd / 16) + (o % 8) / 4) 4 + o % 4
-      // of the Vc field; dims d0 + i step the element by 64, so the byte by 8 VB
-      // and the bit position within it stays (one byte for VB = 2, 4; two for 3)
-      const unsigned e = ((16u * (o >> 3) + (d0 & 15)) * 16u + 2u * (d0 >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
-      const auto vb = page + F.vc + ((e * VB) >> 3);
-      const unsigned vsh = (e * VB) & 7;
-      _Float16 hc[4], hz[4];
-      float vx[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
-        hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-        unsigned vw = ld<unsigned char>(vb + 8 * VB * i);
-        if constexpr (VB == 3) vw |= static_cast<unsigned>(ld<unsigned char>(vb + 8 * VB * i + 1)) << 8;
-        const unsigned code = (vw >> vsh) & ((1u << VB) - 1u);
-        vx[i] = MSEV ? sc * vcent_f[code] : fmaf(sc, static_cast<float>(code), zr);
-      }
-      *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
-      if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
-      // v' as float16 hi + lo of the float32 value (pieces against the same hi)
-      const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
-      *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
-      *reinterpret_cast<u32x2*>(&avl[t][d0]) = u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
-      if ((tid & 31) == 0) {
-        if constexpr (QJL) {
-          const unsigned kn = ld<unsigned>(page + F.kn + o * 4);
-          sn[t] = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) * 0.08838834764831845f;
-          sg[t] = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
+        wait_vmcnt<2>();
+    }
+    // tile k's page and tile k+2's slots in LDS; tile k-1's A operands
+    // expanded; tile k-2's products formed (its buffer is free) and staged
+    __syncthreads();
+    if (!mma) {
+      if (k >= mine) continue;
+      // copies of tile k+4's slots and tile k+2's page
+      long long s02;
+      const bool whole2 = page_of(ring_slot(k + 2), &s02);
+      copy_slots(k + 4);
+      copy_page(k + 2, s02);
+
+      // ---- expand tile k: thread (t, d0) -> A operands of token t, dims d0..d0+3
+      auto& ac = aop[k & 1][0];
+      auto& avh = aop[k & 1][1];
+      auto& avl = aop[k & 1][2];
+      auto& az = aop[k & 1][NA - 1];  // (QJL only)
+      const long long n0 = tile_of(k) * 16;
+      const bool whole = wholec;
+      // expansion of token t's dims d0..d0+3 from its record at in-page offset o
+      auto expand = [&](auto page, int o) {
+        const int blk = d0 >> 5, e0 = d0 & 31;
+        // key codes of dims d0..d0+3: 4 KB bits at bit e0 KB of the block record
+        // (one byte for KB <= 2, an aligned halfword for KB = 4, two bytes for 3)
+        const auto kc = page + F.kc + (blk * 16 + o) * 4 * KB + ((e0 * KB) >> 3);
+        unsigned kx;
+        if constexpr (KB == 4)
+          kx = ld<unsigned short>(kc);
+        else if constexpr (KB == 3)
+          kx = (static_cast<unsigned>(ld<unsigned char>(kc)) | (static_cast<unsigned>(ld<unsigned char>(kc + 1)) << 8)) >>
+               ((e0 * KB) & 7);
+        else
+          kx = static_cast<unsigned>(ld<unsigned char>(kc)) >> ((e0 * KB) & 7);
+        unsigned zb = 0u;
+        if constexpr (QJL)
+          zb = static_cast<unsigned>(ld<unsigned char>(page + F.ks + (blk * 16 + o) * 4 + (e0 >> 3))) >> (e0 & 7);
+        float sc, zr;
+        if constexpr (MSEV) {
+          const unsigned short vn = ld<unsigned short>(page + F.vsz + o * 2);
+          sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
+          zr = 0.0f;
         } else {
-          const unsigned short kn = ld<unsigned short>(page + F.kn + o * 2);
-          sn[t] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f;
-          sg[t] = 0.0f;
+          const unsigned sz = ld<unsigned>(page + F.vsz + o * 16 + blk * 4);
+          sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
+          zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
+        }
+        // value codes: element ((16 (o / 8) + jd % 16) 16 + 2 (jd / 16) + (o % 8) / 4) 4 + o % 4
+        // of the Vc field; dims d0 + i step the element by 64, so the byte by 8 VB
+        // and the bit position within it stays (one byte for VB = 2, 4; two for 3)
+        const unsigned e = ((16u * (o >> 3) + (d0 & 15)) * 16u + 2u * (d0 >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
+        const auto vb = page + F.vc + ((e * VB) >> 3);
+        const unsigned vsh = (e * VB) & 7;
+        _Float16 hc[4], hz[4];
+        float vx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
+          hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+          unsigned vw = ld<unsigned char>(vb + 8 * VB * i);
+          if constexpr (VB == 3) vw |= static_cast<unsigned>(ld<unsigned char>(vb + 8 * VB * i + 1)) << 8;
+          const unsigned code = (vw >> vsh) & ((1u << VB) - 1u);
+          vx[i] = MSEV ? sc * vcent_f[code] : fmaf(sc, static_cast<float>(code), zr);
+        }
+        *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
+        if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
+        // v' as float16 hi + lo of the float32 value (pieces against the same hi)
+        const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
+        *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(&avl[t][d0]) =
+            u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
+      };
+      constexpr int kn_bytes = QJL ? 4 : 2;  // Kn bytes per token
+      __builtin_amdgcn_sched_barrier(0);
+      if (whole) {
+        // the page image in the ring (LDS reads); its Kn words as they are
+        const lds_byte* pg = (const lds_byte*)(&pring[k % 3][0]);
+        expand(pg, t);
+        if (u < 4 * kn_bytes) *reinterpret_cast<unsigned*>(&knb[k & 1][4 * u]) = ld<unsigned>(pg + F.kn + 4 * u);
+      } else {
+        // (the ragged last tile's ring entry holds shifted slots near the input's end)
+        const long long slot =
+            n0 + t < a.n_tokens ? (n0 + 16 <= a.n_tokens ? sring[k & 7][t] : a.slots[n0 + t]) : -1;
+        if (slot >= 0) {
+          const unsigned char* pg = a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * F.bytes;
+          const int o = static_cast<int>(slot & 15);
+          expand(pg, o);
+          if ((u & 31) == 0) {
+            if constexpr (QJL)
+              *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = ld<unsigned>(pg + F.kn + 4 * o);
+            else
+              *reinterpret_cast<unsigned short*>(&knb[k & 1][2 * t]) = ld<unsigned short>(pg + F.kn + 2 * o);
+          }
+        } else {
+          const half4 z4 = {static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f),
+                            static_cast<_Float16>(0.0f)};
+          *reinterpret_cast<half4*>(&ac[t][d0]) = z4;
+          if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = z4;
+          *reinterpret_cast<half4*>(&avh[t][d0]) = z4;
+          *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
+          if ((u & 31) == 0) {
+            if constexpr (QJL)
+              *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = 0u;
+            else
+              *reinterpret_cast<unsigned short*>(&knb[k & 1][2 * t]) = 0;
+          }
         }
       }
-    };
-    __builtin_amdgcn_sched_barrier(0);
-    if (whole) {
-      // the page image in the ring (LDS reads)
-      expand((const lds_byte*)(&pring[k % 3][0]), t);
-    } else {
-      // (the ragged last tile's ring entry holds shifted slots near the input's end)
-      const long long slot =
-          n0 + t < a.n_tokens ? (n0 + 16 <= a.n_tokens ? sring[k & 7][t] : a.slots[n0 + t]) : -1;
-      if (slot >= 0) {
-        expand(static_cast<const unsigned char*>(a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * F.bytes),
-               static_cast<int>(slot & 15));
-      } else {
-        const half4 z4 = {static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f),
-                          static_cast<_Float16>(0.0f)};
-        *reinterpret_cast<half4*>(&ac[t][d0]) = z4;
-        if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = z4;
-        *reinterpret_cast<half4*>(&avh[t][d0]) = z4;
-        *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
-        if ((tid & 31) == 0) sn[t] = sg[t] = 0.0f;
+      __builtin_amdgcn_sched_barrier(0);
+      wholec = wholen;
+      s0c = s0n;
+      wholen = whole2;
+      s0n = s02;
+      continue;
+    }
+    if (k == 0) continue;
+
+    // ---- store tile k-2 from its staging: wave w, rows 4w..4w+3 of the 32
+    // (K rows of tokens 0..15, then V rows), 16 lanes a row, 16 contiguous
+    // bytes each (two 16-byte pieces for fp32)
+    if (k >= 2) {
+      const int ridx = 4 * w + (lane >> 4), kv = ridx >> 4, tt = ridx & 15, c = lane & 15;
+      const unsigned* row = &stage[k & 1][kv][tt][0];
+      const long long n = tile_of(k - 2) * 16 + tt;
+      if (n < a.n_tokens) {
+        void* out = kv ? a.vout : a.kout;
+        const size_t at = (static_cast<size_t>(n) * a.H + g) * 128;
+        if constexpr (OUT_BF16) {
+          *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at + 8 * c) =
+              *reinterpret_cast<const u32x4*>(row + 4 * c);
+        } else {
+          float* o = static_cast<float*>(out) + at;
+          *reinterpret_cast<u32x4*>(o + 4 * c) = *reinterpret_cast<const u32x4*>(row + 4 * c);
+          *reinterpret_cast<u32x4*>(o + 64 + 4 * c) = *reinterpret_cast<const u32x4*>(row + 64 + 4 * c);
+        }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();  // the tile's A operands
+    if (k > mine) continue;
 
-    // ---- wave w: output dims 16w + col of tokens 4kg + r
+    // ---- contract tile k-1: wave w, output dims 16w + col of tokens 4kg + r
+    const int b = (k - 1) & 1;
     floatx4 k1 = {0.0f, 0.0f, 0.0f, 0.0f}, k2 = k1, vv = k1;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c0 = 32 * s + 8 * kg;
-      const half8 xc = *reinterpret_cast<const half8*>(&ac[col][c0]);
-      const half8 xh = *reinterpret_cast<const half8*>(&avh[col][c0]);
-      const half8 xl = *reinterpret_cast<const half8*>(&avl[col][c0]);
+      const half8 xc = *reinterpret_cast<const half8*>(&aop[b][0][col][c0]);
+      const half8 xh = *reinterpret_cast<const half8*>(&aop[b][1][col][c0]);
+      const half8 xl = *reinterpret_cast<const half8*>(&aop[b][2][col][c0]);
       k1 = mfma(xc, RH[s], k1);
       k1 = mfma(xc, RL[s], k1);
       if constexpr (QJL) {
-        const half8 xz = *reinterpret_cast<const half8*>(&az[col][c0]);
+        const half8 xz = *reinterpret_cast<const half8*>(&aop[b][NA - 1][col][c0]);
         k2 = mfma(xz, PH[s], k2);
         k2 = mfma(xz, PL[s], k2);
       }
@@ -520,28 +580,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
       // operands): the scheduler may not hoist the next step's reads above here
       __builtin_amdgcn_sched_barrier(0);
     }
+    // ---- stage tile k-1: lane (col, kg) holds rows 4kg..4kg+3 of output dim
+    // 16w + col; K = n (x1 + kappa gamma x2), n and gamma as float16
+    float kx[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = 4 * kg + r;
-      stage_k[w][tt][col] = QJL ? sn[tt] * fmaf(sg[tt], k2[r], k1[r]) : sn[tt] * k1[r];
-      stage_v[w][tt][col] = vv[r];
+      if constexpr (QJL) {
+        const unsigned kn = *reinterpret_cast<const unsigned*>(&knb[b][4 * tt]);
+        const float sn = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) *
+                         0.08838834764831845f;
+        const float sg = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
+        kx[r] = sn * fmaf(sg, k2[r], k1[r]);
+      } else {
+        const unsigned short kn = *reinterpret_cast<const unsigned short*>(&knb[b][2 * tt]);
+        kx[r] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f * k1[r];
+      }
     }
-    // lane l < 32: K of token l / 2, dims 8 (l % 2) .. +7; l >= 32: V likewise
-    // (bf16: one 16-byte store; fp32: two, the second covering the other half)
-    {
-      const int u = lane & 31, tt = u >> 1, half_ = u & 1;
-      const float* src = &stage[lane >> 5][w][tt][0];
-      void* out = lane < 32 ? a.kout : a.vout;
-      const long long n = n0 + tt;
-      if (n < a.n_tokens) {
-        const size_t at = (static_cast<size_t>(n) * a.H + g) * 128 + 16 * w;
-        if constexpr (OUT_BF16) {
-          store8<true>(out, at + 8 * half_, src + 8 * half_);
-        } else {
-          float* o = static_cast<float*>(out) + at;
-          *reinterpret_cast<floatx4*>(o + 8 * half_) = *reinterpret_cast<const floatx4*>(src + 8 * half_);
-          *reinterpret_cast<floatx4*>(o + 8 * half_ + 4) = *reinterpret_cast<const floatx4*>(src + 8 * half_ + 4);
-        }
+    const int dc = 16 * w + col;
+    auto& st = stage[b];
+    if constexpr (OUT_BF16) {
+      // two adjacent dims per word: of a lane pair (col, col ^ 1) the even lane
+      // writes rows 4kg, 4kg+1 and the odd lane rows 4kg+2, 4kg+3, each with
+      // the partner's values taken across the pair
+      const bool odd = col & 1;
+      const int r0 = 4 * kg + (odd ? 2 : 0);
+      auto put_pairs = [&](int kv, float x0, float x1, float x2, float x3) {
+        const bf16x2 p01 = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+        const bf16x2 p23 = {static_cast<__bf16>(x2), static_cast<__bf16>(x3)};
+        const unsigned b01 = __builtin_bit_cast(unsigned, p01), b23 = __builtin_bit_cast(unsigned, p23);
+        const unsigned send = odd ? b01 : b23;
+        // quad_perm [1, 0, 3, 2]: the word of lane col ^ 1
+        const unsigned recv =
+            static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(send), 0xB1, 0xF, 0xF, false));
+        const unsigned keep = odd ? b23 : b01;
+        // even lane: (own, partner) of rows r0, r0+1; odd lane: (partner, own)
+        const unsigned lo = odd ? recv : keep, hi = odd ? keep : recv;
+        st[kv][r0][dc >> 1] = (lo & 0xffffu) | (hi << 16);
+        st[kv][r0 + 1][dc >> 1] = (lo >> 16) | (hi & 0xffff0000u);
+      };
+      put_pairs(0, kx[0], kx[1], kx[2], kx[3]);
+      put_pairs(1, vv[0], vv[1], vv[2], vv[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[0][4 * kg + r][dc] = __float_as_uint(kx[r]);
+        st[1][4 * kg + r][dc] = __float_as_uint(vv[r]);
       }
     }
   }
@@ -660,7 +744,7 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
       if (!rf) return fail(TQ_ERR_UNSUPPORTED, "no decompress kernel for k_bits=%d v_bits=%d", L->cfg.k_bits,
                            L->cfg.v_bits);
       int per_cu = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rf, 512, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rf, 1024, 0) != hipSuccess || per_cu < 1) per_cu = 1;
       const int cus = L->cu_count > 0 ? L->cu_count : 256;
       const long long n_tiles = (n_tokens + 15) / 16;
       long long gx = (static_cast<long long>(cus) * per_cu + H - 1) / H;
@@ -671,7 +755,7 @@ tq_status launch_decompress(const tq_layer* L, const void* pool, const long long
       a.vout = v_out;
       a.n_tokens = n_tokens;
       void* args[] = {&a};
-      hipError_t e = hipLaunchKernel(rf, dim3(static_cast<unsigned>(gx), H), dim3(512), args, 0, s);
+      hipError_t e = hipLaunchKernel(rf, dim3(static_cast<unsigned>(gx), H), dim3(1024), args, 0, s);
       if (e != hipSuccess) return fail(TQ_ERR_HIP, "decompress launch: %s", hipGetErrorString(e));
       return TQ_OK;
     }
