@@ -933,6 +933,57 @@ def test_decompress_matches_oracle(kb, vb, key_mode, rotation, out_dtype, slot_k
     layer.close()
 
 
+@pytest.mark.parametrize("n", [1, 5, 16, 63, 64, 65, 80])
+@pytest.mark.parametrize("kb,vb,key_mode,out_dtype,slot_kind", [
+    (4, 4, tq.KEY_QJL, "bf16", "shuffled"), (3, 2, tq.KEY_MSE_NC, "f32", "shuffled"),
+    (4, 4, tq.KEY_QJL, "f32", "pages")])
+def test_decompress_short_and_boundary_lengths(n, kb, vb, key_mode, out_dtype, slot_kind):
+    """Decompress at the lengths around the switch between the per-tile kernel
+    (fewer than 64 tokens) and the persistent ring kernel (64 and more: exactly
+    four tiles, then a ragged last tile of one or sixteen tokens), against the
+    oracle's reconstruction.  Shuffled slots with one negative read slot, or
+    consecutive slots (whole pages through the page ring) whose last read slot
+    is negative."""
+    from oracle import decompress as odec
+    torch = _torch()
+    say("decompress length", n, kb, vb, key_mode, out_dtype, slot_kind)
+    H = 4
+    K, V = synth.kv_host(500 + n, 96, H, outliers=4)
+    rng = np.random.default_rng(n)
+    if slot_kind == "pages":
+        slots = np.arange(96, dtype=np.int64)
+    else:
+        slots = rng.permutation(12 * 16)[:96].astype(np.int64)
+    layer = tq.Layer(tq.config(H, kb, vb, seed=501, layer=kb, key_mode=key_mode))
+    pool = layer.new_pool(12)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(slots).cuda(), pool)
+    if slot_kind == "pages":
+        q_slots = slots[:n].copy()
+        q_slots[n - 1] = -1
+    else:
+        q_slots = slots[rng.permutation(96)[:n]].copy()
+        q_slots[rng.integers(n)] = -1
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    kd, vd = tq.decompress_kv(layer, pool, torch.from_numpy(q_slots).cuda(), out_dtype=tdt)
+    torch.cuda.synchronize()
+    kd, vd = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    assert kd.shape == (n, H, 128) and vd.shape == (n, H, 128)
+    st = parity.ostate.LayerState(501, kb, H, 128, kb, vb, 32, key_mode=KEY_MODE_NAMES[key_mode])
+    layout = parity.lay.StoreLayout(128, kb, vb, 32, qjl=key_mode == tq.KEY_QJL)
+    kr, vr = odec.decompress(pool.cpu().numpy(), layout, H, q_slots, st)
+    neg = q_slots < 0
+    assert not kd[neg].any() and not vd[neg].any()
+    for got, ref, name in ((kd, kr, "K"), (vd, vr, "V")):
+        err = np.abs(got - ref)
+        scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+        if out_dtype == "f32":
+            assert (err / scale).max() <= 2e-6, name
+        else:
+            assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-6 * scale), name
+    layer.close()
+
+
 def test_decompress_full_size_sampled():
     """The headline store (16 x 4096 tokens x 8 KV heads, K4/V4, outlier channels,
     random block table) written by the GPU compressor, all 65,536 tokens
