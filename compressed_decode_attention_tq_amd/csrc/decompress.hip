@@ -297,12 +297,15 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
   const int col = lane & 15, kg = lane >> 4;
 
   // Two buffers of a tile's A operands (codebook values, v' hi, v' lo and,
-  // with QJL, signs +-1) and of its Kn words; each kind is one array, so an
+  // with QJL, signs +-1; with MSE-coded values the value codebook entries in
+  // place of v' hi, exact in float16, and no lo piece), of its Kn words and
+  // (MSE-coded values) of its value norms; each kind is one array, so an
   // access is one per-lane address plus a constant offset, which keeps the
   // loop's live registers few.
   constexpr int NA = QJL ? 4 : 3;
   __shared__ __attribute__((aligned(16))) _Float16 aop[2][NA][16][kARow];
   __shared__ __attribute__((aligned(16))) unsigned char knb[2][64];
+  __shared__ __attribute__((aligned(16))) unsigned char vnb[2][MSEV ? 32 : 4];
   // Two buffers of a tile's outputs: the K and V rows of its 16 tokens (bf16
   // pairs or fp32 values per word; the 4-word row padding puts the rows a
   // half wave writes at once on distinct banks).  The contracting waves write
@@ -312,8 +315,8 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned stage[2][2][16][kSRow];
   __shared__ __attribute__((aligned(16))) u32x4 pring[3][kPageChunks];
   __shared__ __attribute__((aligned(16))) long long sring[8][16];
-  __shared__ _Float16 cent_h[16];  // key codebook (float16 values: exact)
-  __shared__ float vcent_f[16];     // value codebook (float32)
+  __shared__ _Float16 cent_h[16];   // key codebook (float16 values: exact)
+  __shared__ _Float16 vcent_h[16];  // value codebook (float16 values: exact)
 
   // ---- contracting waves: B operands of column tile w
   half8 RH[4], RL[4], PH[QJL ? 4 : 1], PL[QJL ? 4 : 1];
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
   }
   if (tid < 16) {
     cent_h[tid] = static_cast<_Float16>(a.cent[tid]);
-    vcent_f[tid] = a.vcent[tid];
+    vcent_h[tid] = static_cast<_Float16>(a.vcent[tid]);
   }
 
   const long long n_tiles = (a.n_tokens + 15) / 16;
@@ -455,12 +458,9 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
         unsigned zb = 0u;
         if constexpr (QJL)
           zb = static_cast<unsigned>(ld<unsigned char>(page + F.ks + (blk * 16 + o) * 4 + (e0 >> 3))) >> (e0 & 7);
-        float sc, zr;
-        if constexpr (MSEV) {
-          const unsigned short vn = ld<unsigned short>(page + F.vsz + o * 2);
-          sc = __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
-          zr = 0.0f;
-        } else {
+        // (MSE-coded values: the token's norm is applied after the products)
+        float sc = 0.0f, zr = 0.0f;
+        if constexpr (!MSEV) {
           const unsigned sz = ld<unsigned>(page + F.vsz + o * 16 + blk * 4);
           sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
           zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
         const unsigned e = ((16u * (o >> 3) + (d0 & 15)) * 16u + 2u * (d0 >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
         const auto vb = page + F.vc + ((e * VB) >> 3);
         const unsigned vsh = (e * VB) & 7;
-        _Float16 hc[4], hz[4];
+        _Float16 hc[4], hz[4], hv[4];
         float vx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -480,15 +480,22 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           unsigned vw = ld<unsigned char>(vb + 8 * VB * i);
           if constexpr (VB == 3) vw |= static_cast<unsigned>(ld<unsigned char>(vb + 8 * VB * i + 1)) << 8;
           const unsigned code = (vw >> vsh) & ((1u << VB) - 1u);
-          vx[i] = MSEV ? sc * vcent_f[code] : fmaf(sc, static_cast<float>(code), zr);
+          if constexpr (MSEV)
+            hv[i] = vcent_h[code];
+          else
+            vx[i] = fmaf(sc, static_cast<float>(code), zr);
         }
         *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
         if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
-        // v' as float16 hi + lo of the float32 value (pieces against the same hi)
-        const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
-        *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(&avl[t][d0]) =
-            u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
+        if constexpr (MSEV) {
+          *reinterpret_cast<half4*>(&avh[t][d0]) = half4{hv[0], hv[1], hv[2], hv[3]};
+        } else {
+          // v' as float16 hi + lo of the float32 value (pieces against the same hi)
+          const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
+          *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
+          *reinterpret_cast<u32x2*>(&avl[t][d0]) =
+              u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
+        }
       };
       constexpr int kn_bytes = QJL ? 4 : 2;  // Kn bytes per token
       __builtin_amdgcn_sched_barrier(0);
@@ -497,6 +504,9 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
         const lds_byte* pg = (const lds_byte*)(&pring[k % 3][0]);
         expand(pg, t);
         if (u < 4 * kn_bytes) *reinterpret_cast<unsigned*>(&knb[k & 1][4 * u]) = ld<unsigned>(pg + F.kn + 4 * u);
+        if constexpr (MSEV)
+          if (u >= 32 && u < 40)
+            *reinterpret_cast<unsigned*>(&vnb[k & 1][4 * (u - 32)]) = ld<unsigned>(pg + F.vsz + 4 * (u - 32));
       } else {
         // (the ragged last tile's ring entry holds shifted slots near the input's end)
         const long long slot =
@@ -510,6 +520,8 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
               *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = ld<unsigned>(pg + F.kn + 4 * o);
             else
               *reinterpret_cast<unsigned short*>(&knb[k & 1][2 * t]) = ld<unsigned short>(pg + F.kn + 2 * o);
+            if constexpr (MSEV)
+              *reinterpret_cast<unsigned short*>(&vnb[k & 1][2 * t]) = ld<unsigned short>(pg + F.vsz + 2 * o);
           }
         } else {
           const half4 z4 = {static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f), static_cast<_Float16>(0.0f),
@@ -517,12 +529,13 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           *reinterpret_cast<half4*>(&ac[t][d0]) = z4;
           if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = z4;
           *reinterpret_cast<half4*>(&avh[t][d0]) = z4;
-          *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
+          if constexpr (!MSEV) *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
           if ((u & 31) == 0) {
             if constexpr (QJL)
               *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = 0u;
             else
               *reinterpret_cast<unsigned short*>(&knb[k & 1][2 * t]) = 0;
+            if constexpr (MSEV) *reinterpret_cast<unsigned short*>(&vnb[k & 1][2 * t]) = 0;
           }
         }
       }
@@ -565,7 +578,6 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       const int c0 = 32 * s + 8 * kg;
       const half8 xc = *reinterpret_cast<const half8*>(&aop[b][0][col][c0]);
       const half8 xh = *reinterpret_cast<const half8*>(&aop[b][1][col][c0]);
-      const half8 xl = *reinterpret_cast<const half8*>(&aop[b][2][col][c0]);
       k1 = mfma(xc, RH[s], k1);
       k1 = mfma(xc, RL[s], k1);
       if constexpr (QJL) {
@@ -575,7 +587,10 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       }
       vv = mfma(xh, RH[s], vv);
       vv = mfma(xh, RL[s], vv);
-      vv = mfma(xl, RH[s], vv);
+      if constexpr (!MSEV) {  // (MSE-coded values: the codebook entries are exact, no lo piece)
+        const half8 xl = *reinterpret_cast<const half8*>(&aop[b][2][col][c0]);
+        vv = mfma(xl, RH[s], vv);
+      }
       // one K-step's A operands live at a time (next to the 64 registers of B
       // operands): the scheduler may not hoist the next step's reads above here
       __builtin_amdgcn_sched_barrier(0);
@@ -595,6 +610,11 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       } else {
         const unsigned short kn = *reinterpret_cast<const unsigned short*>(&knb[b][2 * tt]);
         kx[r] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f * k1[r];
+      }
+      // MSE-coded values: V = (nv / sqrt(d)) (codebook values . R), nv as float16
+      if constexpr (MSEV) {
+        const unsigned short vn = *reinterpret_cast<const unsigned short*>(&vnb[b][2 * tt]);
+        vv[r] *= __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
       }
     }
     const int dc = 16 * w + col;
