@@ -984,6 +984,74 @@ def test_decompress_short_and_boundary_lengths(n, kb, vb, key_mode, out_dtype, s
     layer.close()
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_decompress_random_configurations(case):
+    """Seeded random decompress cases: KV heads, bit widths, key mode, value mode,
+    rotation, output type, input length (both kernels), and read slots that mix
+    runs of whole pages, a run starting inside a page, shuffled slots, repeats
+    and negative slots; GPU-written store, GPU reconstruction against the
+    oracle's reconstruction of the same bytes."""
+    from oracle import decompress as odec
+    torch = _torch()
+    rng = np.random.default_rng(4000 + case)
+    H = int(rng.choice([1, 2, 4, 8]))
+    kb, vb = int(rng.choice([1, 2, 3, 4])), int(rng.choice([2, 3, 4]))
+    value_mode = int(rng.choice([tq.VAL_GROUP, tq.VAL_MSE]))
+    key_mode = int(rng.choice([tq.KEY_QJL, tq.KEY_MSE, tq.KEY_MSE_NC]))
+    rotation = int(rng.choice([tq.ROT_HAAR, tq.ROT_HADAMARD]))
+    out_dtype = str(rng.choice(["f32", "bf16"]))
+    n_blocks = 40
+    n = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 600))]))
+    say("random decompress", case, dict(H=H, kb=kb, vb=vb, key_mode=key_mode, value_mode=value_mode,
+                                         rotation=rotation, out=out_dtype, n=n))
+    # every slot of the pool written once, in a shuffled order
+    wslots = rng.permutation(n_blocks * 16).astype(np.int64)
+    K, V = synth.kv_host(4100 + case, n_blocks * 16, H, outliers=4)
+    layer = tq.Layer(tq.config(H, kb, vb, seed=4200 + case, layer=case, key_mode=key_mode, rotation=rotation,
+                               value_mode=value_mode))
+    pool = layer.new_pool(n_blocks)
+    tq.compress_kv(layer, torch.from_numpy(K).to("cuda", torch.bfloat16),
+                   torch.from_numpy(V).to("cuda", torch.bfloat16), torch.from_numpy(wslots).cuda(), pool)
+    # read slots: consecutive whole pages, a run from inside a page, shuffled, repeated, negative
+    parts, left = [], n
+    while left > 0:
+        kind = int(rng.integers(4))
+        m = min(left, int(rng.integers(1, 80)))
+        if kind == 0:
+            b0 = int(rng.integers(0, n_blocks - (m + 15) // 16 + 1)) if m <= n_blocks * 16 else 0
+            parts.append(np.arange(b0 * 16, b0 * 16 + m) % (n_blocks * 16))
+        elif kind == 1:
+            s0 = int(rng.integers(0, n_blocks * 16 - m + 1))
+            parts.append(np.arange(s0, s0 + m))
+        elif kind == 2:
+            parts.append(rng.integers(0, n_blocks * 16, m))
+        else:
+            parts.append(np.full(m, int(rng.integers(0, n_blocks * 16))))
+        left -= m
+    q_slots = np.concatenate(parts).astype(np.int64)[:n]
+    q_slots[rng.random(n) < 0.03] = -1
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    kd, vd = tq.decompress_kv(layer, pool, torch.from_numpy(q_slots).cuda(), out_dtype=tdt)
+    torch.cuda.synchronize()
+    kd, vd = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    st = parity.ostate.LayerState(4200 + case, case, H, 128, kb, vb, 32, key_mode=KEY_MODE_NAMES[key_mode],
+                                  rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard",
+                                  value_mode="mse" if value_mode == tq.VAL_MSE else "group")
+    layout = parity.lay.StoreLayout(128, kb, vb, 32, qjl=key_mode == tq.KEY_QJL,
+                                    value_mode="mse" if value_mode == tq.VAL_MSE else "group")
+    kr, vr = odec.decompress(pool.cpu().numpy(), layout, H, q_slots, st)
+    neg = q_slots < 0
+    assert not kd[neg].any() and not vd[neg].any()
+    for got, ref, name in ((kd, kr, "K"), (vd, vr, "V")):
+        err = np.abs(got - ref)
+        scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+        if out_dtype == "f32":
+            assert (err / scale).max() <= 2e-6, name
+        else:
+            assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-6 * scale), name
+    layer.close()
+
+
 def test_decompress_full_size_sampled():
     """The headline store (16 x 4096 tokens x 8 KV heads, K4/V4, outlier channels,
     random block table) written by the GPU compressor, all 65,536 tokens
