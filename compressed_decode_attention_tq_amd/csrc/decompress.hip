@@ -408,11 +408,16 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
     copy_page(1, s0n);
   }
 
-  // expansion: copying-wave thread u takes token t = u / 32, dims d0..d0+3
-  // (each token's A-operand row is written by 32 consecutive lanes, 256
-  // contiguous bytes)
+  // expansion: copying-wave thread u takes token t, dims d0..d0+3.  With 4-bit
+  // values, copying wave e = u / 64 takes tokens 8 (e % 2) + l % 8 and quads
+  // e / 2 + 4 (l / 8) of its lanes l, so all its dims have one residue modulo
+  // 16 and its reads of the value codes (lane-blocked runs) fall on distinct
+  // LDS banks or share a word; with 2- and 3-bit values (fewer such conflicts)
+  // 32 consecutive lanes take one token, so each token's A-operand row is
+  // written as 256 contiguous bytes.
   const int u = tid & 511;
-  const int t = u >> 5, d0 = 4 * (u & 31);
+  const int t = VB == 4 ? 8 * ((u >> 6) & 1) + (u & 7) : u >> 5;
+  const int d0 = VB == 4 ? 4 * ((u >> 7) + 4 * ((u >> 3) & 7)) : 4 * (u & 31);
 #pragma unroll 1
   for (int k = 0; k <= mine + 1; ++k) {
     // (copying waves) operations issued after tile k's page copy: the page copy
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           const unsigned char* pg = a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * F.bytes;
           const int o = static_cast<int>(slot & 15);
           expand(pg, o);
-          if ((u & 31) == 0) {
+          if (d0 == 0) {  // (one thread per token)
             if constexpr (QJL)
               *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = ld<unsigned>(pg + F.kn + 4 * o);
             else
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = z4;
           *reinterpret_cast<half4*>(&avh[t][d0]) = z4;
           if constexpr (!MSEV) *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
-          if ((u & 31) == 0) {
+          if (d0 == 0) {
             if constexpr (QJL)
               *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = 0u;
             else
