@@ -154,6 +154,8 @@ def put_records(pool, layout, n_kv_heads, slots, head, rec):
     stores n16 only (z and g16 must then be zero).
     """
     slots = np.asarray(slots, dtype=np.int64)
+    if slots.size == 0:  # no tokens: nothing to store
+        return
     blocks, offs = np.divmod(slots, P)
     base = (blocks * n_kv_heads + head) * layout.block_bytes
     _bit_write(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits, rec["idx"])
@@ -182,7 +184,7 @@ def get_records(pool, layout, n_kv_heads, slots, head):
     blocks, offs = np.divmod(slots, P)
     base = (blocks * n_kv_heads + head) * layout.block_bytes
     kn = pool[(base + layout.off_kn + offs * layout.kn_bytes)[:, None] + np.arange(layout.kn_bytes)]
-    kn = np.ascontiguousarray(kn).view(np.float16).reshape(len(slots), -1)
+    kn = np.ascontiguousarray(kn).view(np.float16).reshape(len(slots), layout.kn_bytes // 2)
     sz = pool[(base + layout.off_vsz + offs * layout.vsz_bytes)[:, None] + np.arange(layout.vsz_bytes)]
     out = {
         "idx": _bit_read(pool, _field_bits(layout, base, offs, "idx"), layout.k_bits),
@@ -198,7 +200,7 @@ def get_records(pool, layout, n_kv_heads, slots, head):
     if layout.value_mode == "mse":
         out["vn16"] = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots))
     else:
-        sz = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots), -1, 2)
+        sz = np.ascontiguousarray(sz).view(np.float16).reshape(len(slots), layout.vsz_bytes // 4, 2)
         out["scale16"], out["zero16"] = sz[:, :, 0], sz[:, :, 1]
     return out
 

@@ -249,3 +249,23 @@ def test_layout_without_qjl_by_hand():
         layout.put_records(pool, lay, 2, [37], 1, bad)
     with pytest.raises(ValueError):
         layout.put_records(pool, lay, 2, [37], 1, dict(zero, g16=np.float16([0.5])))
+
+
+@pytest.mark.parametrize("key_mode,value_mode", [("qjl", "group"), ("mse_nc", "group"), ("qjl", "mse")])
+def test_store_of_no_tokens_writes_nothing(key_mode, value_mode):
+    """A batch with no tokens (every sequence empty) stores nothing: the pool keeps
+    its bytes, and reading no slots gives empty fields of the right widths."""
+    from oracle import compress, state
+    lay = layout.StoreLayout(128, 3, 2, 32, qjl=key_mode == "qjl", value_mode=value_mode)
+    st = state.LayerState(7, 0, 2, 128, 3, 2, 32, key_mode=key_mode, value_mode=value_mode)
+    pool = np.full(2 * 2 * lay.block_bytes, 0xA5, dtype=np.uint8)
+    empty = np.zeros((0, 2, 128))
+    compress.compress_into_pool(empty, empty, np.zeros(0, np.int64), pool, lay, st)
+    assert np.all(pool == 0xA5)
+    got = layout.get_records(pool, lay, 2, np.zeros(0, np.int64), 1)
+    assert got["idx"].shape == (0, 128) and got["vcode"].shape == (0, 128)
+    assert got["n16"].shape == (0,) and got["g16"].shape == (0,) and got["z"].shape[0] == 0
+    if value_mode == "mse":
+        assert got["vn16"].shape == (0,)
+    else:
+        assert got["scale16"].shape == (0, 4) and got["zero16"].shape == (0, 4)
