@@ -1218,9 +1218,10 @@ def test_decode_step_graph_capture():
 @pytest.mark.parametrize("case", list(range(6)) + [17, 21])
 def test_random_layer_configurations(case):
     """Seeded random layers: KV heads, GQA ratio, bit widths, key mode, rotation,
-    ragged lengths (some zero), a random block table, K/V rows with a token stride
-    wider than the row, split count, query and output types: GPU compress against
-    the oracle's store, then GPU decode of the GPU store against the oracle decode."""
+    value coding (group scale/zero or codebook with a norm), ragged lengths (some
+    zero), a random block table, K/V rows with a token stride wider than the row,
+    split count, query and output types: GPU compress against the oracle's store,
+    then GPU decode of the GPU store against the oracle decode."""
     torch = _torch()
     rng = np.random.default_rng(1000 + case)
     Hkv = int(rng.choice([1, 2, 4, 8]))
@@ -1235,8 +1236,10 @@ def test_random_layer_configurations(case):
     splits = int(rng.choice([0, 0, 1, 3, 8]))
     q_dtype = str(rng.choice(["bf16", "f32"]))
     out_dtype = str(rng.choice(["f32", "bf16"]))
+    value_mode = str(rng.choice(["group", "group", "mse"]))
     say("random layer", case, dict(Hkv=Hkv, rep=rep, kb=kb, vb=vb, key_mode=key_mode, rotation=rotation,
-                                   lens=lens.tolist(), splits=splits, q=q_dtype, out=out_dtype))
+                                   value_mode=value_mode, lens=lens.tolist(), splits=splits, q=q_dtype,
+                                   out=out_dtype))
     maxb = max(1, int((lens.max() + 15) // 16) + 1)
     table = rng.permutation(B * maxb).reshape(B, maxb).astype(np.int32)
     N = int(lens.sum())
@@ -1245,7 +1248,8 @@ def test_random_layer_configurations(case):
     seq = np.repeat(np.arange(B), lens)
     pos = np.concatenate([np.arange(n) for n in lens]) if N else np.zeros(0, np.int64)
     slots = (table[seq, pos // 16].astype(np.int64) * 16 + pos % 16) if N else np.zeros(0, np.int64)
-    layer = tq.Layer(tq.config(Hkv, kb, vb, seed=3000 + case, layer=case, key_mode=key_mode, rotation=rotation))
+    layer = tq.Layer(tq.config(Hkv, kb, vb, seed=3000 + case, layer=case, key_mode=key_mode, rotation=rotation,
+                               value_mode=tq.VAL_MSE if value_mode == "mse" else tq.VAL_GROUP))
     pool = layer.new_pool(B * maxb)
     # K and V as views into wider rows: token stride (Hkv + 1) * 128
     kw = torch.zeros((N, Hkv + 1, 128), dtype=torch.bfloat16, device="cuda")
@@ -1259,7 +1263,8 @@ def test_random_layer_configurations(case):
         assert not gpu_pool.any()  # no tokens: the store is left as allocated
     st, layout, opool, res = parity.oracle_store(K, V, slots, B * maxb, Hkv, kb, vb, 3000 + case, layer=case,
                                                  key_mode=KEY_MODE_NAMES[key_mode],
-                                                 rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard")
+                                                 rotation_kind="haar" if rotation == tq.ROT_HAAR else "hadamard",
+                                                 value_mode=value_mode)
     if N:
         _check_compress(gpu_pool, res, st, layout, Hkv, slots, V, kb, vb)
     q = synth.queries_host(4000 + case, B, Hq, dtype=q_dtype)
