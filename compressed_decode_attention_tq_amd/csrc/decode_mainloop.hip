@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "split_items.hpp"
 #include "tq_internal.hpp"
@@ -178,6 +179,19 @@ struct KeyLut {
   static constexpr int copies = 128 / copy_bytes;
 };
 constexpr int kSignBase = 128, kSignCopies = 8;
+// Compact tables (3-bit keys with group-coded values): 3-bit keys use only
+// key entries 0..63, so the key copies take 64 entries at a 128-byte stride
+// (8 KB) and the sign copies follow at their own 128-byte stride (32 KB, none
+// without QJL): 40 KB instead of 64, which with the mainloop's registers lets
+// three workgroups share a CU.  The sign copy offset is given doubled, so that
+// halving the byte permute yields code byte x 128 + copy x 16.  (The other key
+// widths use all 256 key entries, and MSE-coded values add the value table.)
+template <int KB, bool MSEV, bool QJL>
+struct LutShape {
+  static constexpr bool compact = KB == 3 && !MSEV;
+  static constexpr int sign_base = compact ? 64 * 128 : 0;
+  static constexpr int bytes = compact ? 64 * 128 + (QJL ? 256 * 128 : 0) : 256 * kLutEntry;
+};
 
 // LDS address of entry `byte k of x` for a lane whose copy offset is `off`
 // (< 256): one v_perm_b32 puts off in byte 0 and the code byte in byte 1.
@@ -189,7 +203,7 @@ __device__ __forceinline__ unsigned lut_addr(unsigned x, unsigned off) {
 // B operand of the Q.K product for K-step s: the float16 codebook values of the
 // lane's 8 dims (32kg + 8s .. +7), from the packed codes of its 32-dim block.
 // lut: the table's LDS base; koff: the lane's key copy offset.
-template <int KB>
+template <int KB, bool COMPACT>
 __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const unsigned char* lut, unsigned koff) {
   u32x4 r;
   if constexpr (KB == 1) {
@@ -215,7 +229,7 @@ __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const u
     const unsigned x = (w + 1 < 3) ? __builtin_amdgcn_alignbit(kc[w + 1], kc[w], sh) : (kc[w] >> sh);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      r[q] = *reinterpret_cast<const unsigned*>(lut + ((((x >> (6 * q)) & 63u) << 8) | koff));
+      r[q] = *reinterpret_cast<const unsigned*>(lut + ((((x >> (6 * q)) & 63u) << (COMPACT ? 7 : 8)) | koff));
   }
   return as_h8(r);
 }
@@ -506,7 +520,8 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   const int split = item.split, g = item.g, b = item.b;
   const int start = split * a.split_tokens;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lut[256 * kLutEntry];
+  using LT = LutShape<KB, MSEV, QJL>;
+  __shared__ __attribute__((aligned(16))) unsigned char lut[LT::bytes > 2048 * NREP ? LT::bytes : 2048 * NREP];
   __shared__ __attribute__((aligned(16))) unsigned short wl[4][MSEV ? 1 : 4][WC][32];  // P.V weights (float16)
   __shared__ unsigned vlut[MSEV ? VL::words : 1];  // value-codebook pairs (MSE-coded values)
   __shared__ __attribute__((aligned(16))) unsigned zero16[4];
@@ -622,17 +637,31 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       const unsigned hi = ((e >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u;
       sv[q] = lo | (hi << 16);
     }
-    u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * kLutEntry]);
+    if constexpr (LT::compact) {
+      if (e < 64) {
+        u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * 128]);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ent[q] = kv;      // key copies
-      ent[8 + q] = sv;  // sign copies
+        for (int q = 0; q < 8; ++q) ent[q] = kv;  // key copies
+      }
+      if constexpr (QJL) {
+        u32x4* ent = reinterpret_cast<u32x4*>(&lut[LT::sign_base + e * 128]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ent[q] = sv;  // sign copies
+      }
+    } else {
+      u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * kLutEntry]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        ent[q] = kv;      // key copies
+        ent[8 + q] = sv;  // sign copies
+      }
     }
     if (tid < 4) zero16[tid] = 0u;
   }
   __syncthreads();
   const unsigned koff = static_cast<unsigned>((lane % KL::copies) * KL::copy_bytes);
-  const unsigned soff = static_cast<unsigned>(kSignBase + (lane % kSignCopies) * 16);
+  const unsigned soff = LT::compact ? static_cast<unsigned>((lane % kSignCopies) * 32)
+                                    : static_cast<unsigned>(kSignBase + (lane % kSignCopies) * 16);
 
   // ---- per-wave running state (score layout: slot hs = head SM::head(kg, hs))
   const bool active = SM::active(kg);
@@ -651,7 +680,11 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
   const int slot0 = pv_slot(0, col);
 
   const unsigned vcopy = static_cast<unsigned>(lane % VL::copies);
-  auto process = [&](const Chunk<KB, VB, MSEV>& c, int c0) {
+  // tail (std::true_type or std::false_type): whether the chunk may reach past
+  // the split's end.  Only a wave's last chunk can, so the others are compiled
+  // without the end-of-context selects (fewer instructions and registers).
+  auto process = [&](const Chunk<KB, VB, MSEV>& c, int c0, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     // ---- scores: one 16-token tile per page
     float s[2][HPL];
 #pragma unroll
@@ -659,15 +692,16 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f}, acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        acc1 = mfma(qa[0][st], dequant_keys<KB>(c.kc[t], st, lut, koff), acc1);
+        acc1 = mfma(qa[0][st], dequant_keys<KB, LT::compact>(c.kc[t], st, lut, koff), acc1);
         if constexpr (QJL) {
-          const unsigned sa = (st == 0) ? lut_addr<0>(c.ks[t], soff)
+          const unsigned sp = (st == 0) ? lut_addr<0>(c.ks[t], soff)
                             : (st == 1) ? lut_addr<1>(c.ks[t], soff)
                             : (st == 2) ? lut_addr<2>(c.ks[t], soff) : lut_addr<3>(c.ks[t], soff);
+          const unsigned sa = LT::compact ? LT::sign_base + (sp >> 1) : sp;
           acc2 = mfma(qa[NSET - 1][st], as_h8(*reinterpret_cast<const u32x4*>(lut + sa)), acc2);
         }
       }
-      const bool valid = active && (c0 + 16 * t + col) < end;
+      const bool valid = TAIL ? (active && (c0 + 16 * t + col) < end) : active;
       float f[HPL];
       fold_scores<NREP, QJL>(acc1, acc2, h_hi(c.kn[t]), kg, f);
       const float alpha = sc * h_lo(c.kn[t]);
@@ -723,7 +757,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       // w = p * nv16 / sqrt(d), the same for every group (no offset term); a
       // never-written slot past the context end gets the norm 0
       float nv[2] = {h_lo(c.vn[0]) * kInvSqrtD, h_lo(c.vn[1]) * kInvSqrtD};
-      if (c0 + 32 > end) {
+      if (TAIL && c0 + 32 > end) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           if (c0 + 16 * t + col >= end) nv[t] = 0.0f;
@@ -752,7 +786,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       return;
     }
     u32x4 sz[2] = {c.sz[0], c.sz[1]};
-    if (c0 + 32 > end) {
+    if (TAIL && c0 + 32 > end) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         if (c0 + 16 * t + col >= end) sz[t] = u32x4{0u, 0u, 0u, 0u};
@@ -795,20 +829,21 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     }
   };
 
-  // Whole rounds of kRing chunks (every step processes one and loads one),
-  // then the last nch % kRing chunks, already in flight.
+  // Whole rounds of kRing chunks that do not hold the wave's last chunk (every
+  // step processes one and loads one), then the last 1..kRing chunks, already
+  // in flight, with the end-of-context masking.
   int j0 = 0;
-  for (; j0 + kRing <= nch; j0 += kRing) {
+  for (; j0 + kRing < nch; j0 += kRing) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
       const int j = j0 + r;
-      process(ring[r], start + 32 * (wave + 4 * j));
+      process(ring[r], start + 32 * (wave + 4 * j), std::false_type{});
       load(ring[r], j + kRing < jmax ? j + kRing : jmax);
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRing - 1; ++r)
-    if (j0 + r < nch) process(ring[r], start + 32 * (wave + 4 * (j0 + r)));
+  for (int r = 0; r < kRing; ++r)
+    if (j0 + r < nch) process(ring[r], start + 32 * (wave + 4 * (j0 + r)), std::true_type{});
 
   // ---- per-wave results -> LDS, then merge the four waves
 #pragma unroll
