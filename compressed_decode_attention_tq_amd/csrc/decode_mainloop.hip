@@ -179,18 +179,33 @@ struct KeyLut {
   static constexpr int copies = 128 / copy_bytes;
 };
 constexpr int kSignBase = 128, kSignCopies = 8;
-// Compact tables (3-bit keys with group-coded values): 3-bit keys use only
-// key entries 0..63, so the key copies take 64 entries at a 128-byte stride
-// (8 KB) and the sign copies follow at their own 128-byte stride (32 KB, none
-// without QJL): 40 KB instead of 64, which with the mainloop's registers lets
-// three workgroups share a CU.  The sign copy offset is given doubled, so that
-// halving the byte permute yields code byte x 128 + copy x 16.  (The other key
-// widths use all 256 key entries, and MSE-coded values add the value table.)
+// Compact tables (group-coded values), so that three workgroups share a CU:
+//   3-bit keys use key entries 0..63 only: the key copies take 64 entries at a
+//   128-byte stride (8 KB) and the sign copies follow at a 128-byte stride
+//   (32 KB): 40 KB;
+//   4-bit keys: 16 key copies of 4 bytes and 4 sign copies of 16 bytes, each
+//   table at a 64-byte stride (16 KB each): 32 KB.
+// Where an address comes from the byte permute, the copy offset is given scaled
+// up (the sign copies x2 for 3-bit keys, key and sign copies x4 for 4-bit keys)
+// and the permute shifted right gives code byte x stride + copy offset.  Fewer
+// copies of the 4-bit tables cost some bank conflicts; the third workgroup per
+// CU more than makes up for them.
+// Without QJL there is no sign table.  (1- and 2-bit keys use all 256 key
+// entries at full width, and MSE-coded values add the value table: the
+// 256-byte layout above.)
 template <int KB, bool MSEV, bool QJL>
 struct LutShape {
-  static constexpr bool compact = KB == 3 && !MSEV;
-  static constexpr int sign_base = compact ? 64 * 128 : 0;
-  static constexpr int bytes = compact ? 64 * 128 + (QJL ? 256 * 128 : 0) : 256 * kLutEntry;
+  static constexpr int mode = MSEV ? 0 : KB == 3 ? 1 : KB == 4 ? 2 : 0;
+  static constexpr bool compact = mode != 0;
+  static constexpr int key_stride = mode == 0 ? kLutEntry : mode == 1 ? 128 : 64;
+  static constexpr int key_shift = mode == 2 ? 2 : 0;     // KB 4: permute >> key_shift
+  static constexpr int key_copies = mode == 2 ? 16 : KeyLut<KB>::copies;
+  static constexpr int sign_copies = mode == 2 ? 4 : kSignCopies;
+  static constexpr int sign_shift = mode == 0 ? 0 : mode == 1 ? 1 : 2;
+  static constexpr int sign_base = mode == 0 ? 0 : mode == 1 ? 64 * 128 : 256 * 64;
+  static constexpr int sign_stride = mode == 1 ? 128 : 64;
+  static constexpr int bytes = mode == 0 ? 256 * kLutEntry
+                             : sign_base + (QJL ? 256 * sign_stride : 0);
 };
 
 // LDS address of entry `byte k of x` for a lane whose copy offset is `off`
@@ -203,7 +218,7 @@ __device__ __forceinline__ unsigned lut_addr(unsigned x, unsigned off) {
 // B operand of the Q.K product for K-step s: the float16 codebook values of the
 // lane's 8 dims (32kg + 8s .. +7), from the packed codes of its 32-dim block.
 // lut: the table's LDS base; koff: the lane's key copy offset.
-template <int KB, bool COMPACT>
+template <int KB, int MODE>
 __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const unsigned char* lut, unsigned koff) {
   u32x4 r;
   if constexpr (KB == 1) {
@@ -214,10 +229,11 @@ __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const u
                                                                     : lut_addr<3>(kc[0], koff))));
   } else if constexpr (KB == 4) {
     const unsigned x = kc[s];  // 8 nibbles
-    r[0] = *reinterpret_cast<const unsigned*>(lut + lut_addr<0>(x, koff));
-    r[1] = *reinterpret_cast<const unsigned*>(lut + lut_addr<1>(x, koff));
-    r[2] = *reinterpret_cast<const unsigned*>(lut + lut_addr<2>(x, koff));
-    r[3] = *reinterpret_cast<const unsigned*>(lut + lut_addr<3>(x, koff));
+    constexpr int sh = MODE == 2 ? 2 : 0;
+    r[0] = *reinterpret_cast<const unsigned*>(lut + (lut_addr<0>(x, koff) >> sh));
+    r[1] = *reinterpret_cast<const unsigned*>(lut + (lut_addr<1>(x, koff) >> sh));
+    r[2] = *reinterpret_cast<const unsigned*>(lut + (lut_addr<2>(x, koff) >> sh));
+    r[3] = *reinterpret_cast<const unsigned*>(lut + (lut_addr<3>(x, koff) >> sh));
   } else if constexpr (KB == 2) {
     const unsigned x = kc[s >> 1];  // bytes 2(s%2), 2(s%2)+1 = 8 dims
     const u32x2 a = *reinterpret_cast<const u32x2*>(lut + ((s & 1) ? lut_addr<2>(x, koff) : lut_addr<0>(x, koff)));
@@ -229,7 +245,7 @@ __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const u
     const unsigned x = (w + 1 < 3) ? __builtin_amdgcn_alignbit(kc[w + 1], kc[w], sh) : (kc[w] >> sh);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      r[q] = *reinterpret_cast<const unsigned*>(lut + ((((x >> (6 * q)) & 63u) << (COMPACT ? 7 : 8)) | koff));
+      r[q] = *reinterpret_cast<const unsigned*>(lut + ((((x >> (6 * q)) & 63u) << (MODE == 1 ? 7 : 8)) | koff));
   }
   return as_h8(r);
 }
@@ -638,15 +654,17 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       sv[q] = lo | (hi << 16);
     }
     if constexpr (LT::compact) {
-      if (e < 64) {
-        u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * 128]);
+      constexpr int kq = LT::key_copies * KL::copy_bytes / 16;  // 16-byte stores per key entry
+      constexpr int sq = LT::sign_copies;                       // (16 bytes per sign copy)
+      if (e < (LT::mode == 1 ? 64 : 256)) {
+        u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * LT::key_stride]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ent[q] = kv;  // key copies
+        for (int q = 0; q < kq; ++q) ent[q] = kv;  // key copies
       }
       if constexpr (QJL) {
-        u32x4* ent = reinterpret_cast<u32x4*>(&lut[LT::sign_base + e * 128]);
+        u32x4* ent = reinterpret_cast<u32x4*>(&lut[LT::sign_base + e * LT::sign_stride]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ent[q] = sv;  // sign copies
+        for (int q = 0; q < sq; ++q) ent[q] = sv;  // sign copies
       }
     } else {
       u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * kLutEntry]);
@@ -659,8 +677,8 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
     if (tid < 4) zero16[tid] = 0u;
   }
   __syncthreads();
-  const unsigned koff = static_cast<unsigned>((lane % KL::copies) * KL::copy_bytes);
-  const unsigned soff = LT::compact ? static_cast<unsigned>((lane % kSignCopies) * 32)
+  const unsigned koff = static_cast<unsigned>((lane % LT::key_copies) * KL::copy_bytes) << LT::key_shift;
+  const unsigned soff = LT::compact ? static_cast<unsigned>((lane % LT::sign_copies) * 16) << LT::sign_shift
                                     : static_cast<unsigned>(kSignBase + (lane % kSignCopies) * 16);
 
   // ---- per-wave running state (score layout: slot hs = head SM::head(kg, hs))
@@ -692,12 +710,12 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f}, acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        acc1 = mfma(qa[0][st], dequant_keys<KB, LT::compact>(c.kc[t], st, lut, koff), acc1);
+        acc1 = mfma(qa[0][st], dequant_keys<KB, LT::mode>(c.kc[t], st, lut, koff), acc1);
         if constexpr (QJL) {
           const unsigned sp = (st == 0) ? lut_addr<0>(c.ks[t], soff)
                             : (st == 1) ? lut_addr<1>(c.ks[t], soff)
                             : (st == 2) ? lut_addr<2>(c.ks[t], soff) : lut_addr<3>(c.ks[t], soff);
-          const unsigned sa = LT::compact ? LT::sign_base + (sp >> 1) : sp;
+          const unsigned sa = LT::compact ? LT::sign_base + (sp >> LT::sign_shift) : sp;
           acc2 = mfma(qa[NSET - 1][st], as_h8(*reinterpret_cast<const u32x4*>(lut + sa)), acc2);
         }
       }
