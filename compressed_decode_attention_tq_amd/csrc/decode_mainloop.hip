@@ -161,51 +161,40 @@ __device__ __forceinline__ unsigned sub_h2(unsigned x, unsigned y) {
   return __builtin_bit_cast(unsigned, r);
 }
 
-// Lookup tables in LDS, one copy per lane of a bank-parallel group, so that
-// the random code-indexed reads of a wave do not collide.  Entry e of both
-// tables shares the 256 bytes at 256 e, so that a lookup address is the code
-// byte in bits 8..15 and the lane's copy offset in bits 0..7 (one byte permute):
-//   bytes   0..127: key entry (KB 4: byte of two codes -> two float16 values,
-//                   32 copies of 4 bytes; KB 2: byte of four codes -> four
-//                   float16 values, 16 copies of 8 bytes; KB 3: 6 bits of two
-//                   codes, entries 0..63 only, 32 copies of 4 bytes; KB 1: byte
-//                   of eight codes -> eight float16 values, 8 copies of 16 bytes);
-//   bytes 128..255: sign entry (byte of 8 sign bits -> eight float16 +-1,
-//                   8 copies of 16 bytes).
-constexpr int kLutEntry = 256;
+// Lookup tables in LDS, several copies of each so that the random
+// code-indexed reads of a wave spread over the banks.  A key entry maps one
+// byte of packed codes to float16 codebook values (KB 4: two codes -> two
+// values, 4 bytes; KB 2: four codes -> four values, 8 bytes; KB 1: eight codes
+// -> eight values, 16 bytes; KB 3: 6 bits of two codes -> two values, 4 bytes,
+// entries 0..63 only); a sign entry maps a byte of 8 sign bits to eight float16
+// +-1 (16 bytes).  The tables are sized so that three workgroups share a CU:
+//   KB 1, 2, 4: 64 bytes of key copies per entry (4 of 16 bytes, 8 of 8, 16
+//   of 4) and 4 sign copies of 16 bytes, each table 256 entries at a 64-byte
+//   stride (16 KB each);
+//   KB 3: 32 key copies of 4 bytes for entries 0..63 at a 128-byte stride
+//   (8 KB), then 8 sign copies at a 128-byte stride (32 KB).
+// A lookup address is one byte permute, which puts the code byte in bits
+// 8..15 and the lane's copy offset, given scaled up by the stride's shift, in
+// bits 0..7, then a shift right (by 2 for the 64-byte tables, by 1 for the
+// 3-bit sign table; the 3-bit key address is formed from its 6-bit field
+// directly).  Without QJL there is no sign table; MSE-coded values add the
+// value-codebook table beside these.  Every variant at up to four query heads
+// per KV head stays within a third of the CU's LDS.
 template <int KB>
 struct KeyLut {
   static constexpr int copy_bytes = KB == 1 ? 16 : KB == 2 ? 8 : 4;
-  static constexpr int copies = 128 / copy_bytes;
 };
-constexpr int kSignBase = 128, kSignCopies = 8;
-// Compact tables (group-coded values), so that three workgroups share a CU:
-//   3-bit keys use key entries 0..63 only: the key copies take 64 entries at a
-//   128-byte stride (8 KB) and the sign copies follow at a 128-byte stride
-//   (32 KB): 40 KB;
-//   4-bit keys: 16 key copies of 4 bytes and 4 sign copies of 16 bytes, each
-//   table at a 64-byte stride (16 KB each): 32 KB.
-// Where an address comes from the byte permute, the copy offset is given scaled
-// up (the sign copies x2 for 3-bit keys, key and sign copies x4 for 4-bit keys)
-// and the permute shifted right gives code byte x stride + copy offset.  Fewer
-// copies of the 4-bit tables cost some bank conflicts; the third workgroup per
-// CU more than makes up for them.
-// Without QJL there is no sign table.  (1- and 2-bit keys use all 256 key
-// entries at full width, and MSE-coded values add the value table: the
-// 256-byte layout above.)
 template <int KB, bool MSEV, bool QJL>
 struct LutShape {
-  static constexpr int mode = MSEV ? 0 : KB == 3 ? 1 : KB == 4 ? 2 : 0;
-  static constexpr bool compact = mode != 0;
-  static constexpr int key_stride = mode == 0 ? kLutEntry : mode == 1 ? 128 : 64;
-  static constexpr int key_shift = mode == 2 ? 2 : 0;     // KB 4: permute >> key_shift
-  static constexpr int key_copies = mode == 2 ? 16 : KeyLut<KB>::copies;
-  static constexpr int sign_copies = mode == 2 ? 4 : kSignCopies;
-  static constexpr int sign_shift = mode == 0 ? 0 : mode == 1 ? 1 : 2;
-  static constexpr int sign_base = mode == 0 ? 0 : mode == 1 ? 64 * 128 : 256 * 64;
+  static constexpr int mode = KB == 3 ? 1 : 2;
+  static constexpr int key_stride = mode == 1 ? 128 : 64;
+  static constexpr int key_shift = mode == 2 ? 2 : 0;  // permute >> key_shift (1, 2, 4 bits)
+  static constexpr int key_copies = mode == 2 ? 64 / KeyLut<KB>::copy_bytes : 32;
+  static constexpr int sign_copies = mode == 2 ? 4 : 8;
+  static constexpr int sign_shift = mode == 1 ? 1 : 2;
+  static constexpr int sign_base = mode == 1 ? 64 * 128 : 256 * 64;
   static constexpr int sign_stride = mode == 1 ? 128 : 64;
-  static constexpr int bytes = mode == 0 ? 256 * kLutEntry
-                             : sign_base + (QJL ? 256 * sign_stride : 0);
+  static constexpr int bytes = sign_base + (QJL ? 256 * sign_stride : 0);
 };
 
 // LDS address of entry `byte k of x` for a lane whose copy offset is `off`
@@ -223,10 +212,11 @@ __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const u
   u32x4 r;
   if constexpr (KB == 1) {
     // byte s of the block's 32 one-bit codes = dims 8s .. 8s+7: one 16-byte entry
-    return as_h8(*reinterpret_cast<const u32x4*>(lut + ((s == 0)   ? lut_addr<0>(kc[0], koff)
-                                                         : (s == 1) ? lut_addr<1>(kc[0], koff)
-                                                         : (s == 2) ? lut_addr<2>(kc[0], koff)
-                                                                    : lut_addr<3>(kc[0], koff))));
+    constexpr int sh = MODE == 2 ? 2 : 0;
+    return as_h8(*reinterpret_cast<const u32x4*>(lut + (((s == 0)   ? lut_addr<0>(kc[0], koff)
+                                                          : (s == 1) ? lut_addr<1>(kc[0], koff)
+                                                          : (s == 2) ? lut_addr<2>(kc[0], koff)
+                                                                     : lut_addr<3>(kc[0], koff)) >> sh)));
   } else if constexpr (KB == 4) {
     const unsigned x = kc[s];  // 8 nibbles
     constexpr int sh = MODE == 2 ? 2 : 0;
@@ -236,8 +226,9 @@ __device__ __forceinline__ half8 dequant_keys(const unsigned* kc, int s, const u
     r[3] = *reinterpret_cast<const unsigned*>(lut + (lut_addr<3>(x, koff) >> sh));
   } else if constexpr (KB == 2) {
     const unsigned x = kc[s >> 1];  // bytes 2(s%2), 2(s%2)+1 = 8 dims
-    const u32x2 a = *reinterpret_cast<const u32x2*>(lut + ((s & 1) ? lut_addr<2>(x, koff) : lut_addr<0>(x, koff)));
-    const u32x2 b = *reinterpret_cast<const u32x2*>(lut + ((s & 1) ? lut_addr<3>(x, koff) : lut_addr<1>(x, koff)));
+    constexpr int sh = MODE == 2 ? 2 : 0;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (((s & 1) ? lut_addr<2>(x, koff) : lut_addr<0>(x, koff)) >> sh));
+    const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (((s & 1) ? lut_addr<3>(x, koff) : lut_addr<1>(x, koff)) >> sh));
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   } else {  // KB == 3: 24 bits at bit 24 s of the block's 96
     const int bit = 24 * s;
@@ -653,33 +644,23 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
       const unsigned hi = ((e >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u;
       sv[q] = lo | (hi << 16);
     }
-    if constexpr (LT::compact) {
-      constexpr int kq = LT::key_copies * KL::copy_bytes / 16;  // 16-byte stores per key entry
-      constexpr int sq = LT::sign_copies;                       // (16 bytes per sign copy)
-      if (e < (LT::mode == 1 ? 64 : 256)) {
-        u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * LT::key_stride]);
+    constexpr int kq = LT::key_copies * KL::copy_bytes / 16;  // 16-byte stores per key entry
+    constexpr int sq = LT::sign_copies;                       // (16 bytes per sign copy)
+    if (e < (LT::mode == 1 ? 64 : 256)) {
+      u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * LT::key_stride]);
 #pragma unroll
-        for (int q = 0; q < kq; ++q) ent[q] = kv;  // key copies
-      }
-      if constexpr (QJL) {
-        u32x4* ent = reinterpret_cast<u32x4*>(&lut[LT::sign_base + e * LT::sign_stride]);
+      for (int q = 0; q < kq; ++q) ent[q] = kv;  // key copies
+    }
+    if constexpr (QJL) {
+      u32x4* ent = reinterpret_cast<u32x4*>(&lut[LT::sign_base + e * LT::sign_stride]);
 #pragma unroll
-        for (int q = 0; q < sq; ++q) ent[q] = sv;  // sign copies
-      }
-    } else {
-      u32x4* ent = reinterpret_cast<u32x4*>(&lut[e * kLutEntry]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        ent[q] = kv;      // key copies
-        ent[8 + q] = sv;  // sign copies
-      }
+      for (int q = 0; q < sq; ++q) ent[q] = sv;  // sign copies
     }
     if (tid < 4) zero16[tid] = 0u;
   }
   __syncthreads();
   const unsigned koff = static_cast<unsigned>((lane % LT::key_copies) * KL::copy_bytes) << LT::key_shift;
-  const unsigned soff = LT::compact ? static_cast<unsigned>((lane % LT::sign_copies) * 16) << LT::sign_shift
-                                    : static_cast<unsigned>(kSignBase + (lane % kSignCopies) * 16);
+  const unsigned soff = static_cast<unsigned>((lane % LT::sign_copies) * 16) << LT::sign_shift;
 
   // ---- per-wave running state (score layout: slot hs = head SM::head(kg, hs))
   const bool active = SM::active(kg);
@@ -715,7 +696,7 @@ __global__ __launch_bounds__(256) void splitk_mfma_kernel(MainArgs a, const int*
           const unsigned sp = (st == 0) ? lut_addr<0>(c.ks[t], soff)
                             : (st == 1) ? lut_addr<1>(c.ks[t], soff)
                             : (st == 2) ? lut_addr<2>(c.ks[t], soff) : lut_addr<3>(c.ks[t], soff);
-          const unsigned sa = LT::compact ? LT::sign_base + (sp >> LT::sign_shift) : sp;
+          const unsigned sa = LT::sign_base + (sp >> LT::sign_shift);
           acc2 = mfma(qa[NSET - 1][st], as_h8(*reinterpret_cast<const u32x4*>(lut + sa)), acc2);
         }
       }
