@@ -170,9 +170,10 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
     split_tokens = ((ctx + splits - 1) / splits + 63) / 64 * 64;
     if (split_tokens > kMaxSplitTokens) split_tokens = kMaxSplitTokens;  // the mainloop's per-wave chunk limit
   } else {
-    // Automatic: one wave of workgroups, ~2 per CU (the mainloop's LDS use
-    // allows two resident per CU) over (batch x kv_heads x splits), each split
-    // 256..4096 tokens (whole 64-token chunks).
+    // Automatic: about two workgroups per CU over (batch x kv_heads x splits),
+    // each split 256..4096 tokens (whole 64-token chunks).  Three fit per CU,
+    // but measured, splitting further costs more in partials and start-ups
+    // than the third workgroup gains.
     const long long pairs = static_cast<long long>(batch) * L->cfg.n_kv_heads;
     const long long target = 2LL * (L->cu_count > 0 ? L->cu_count : 256);
     const long long want = pairs > 0 ? (target + pairs - 1) / pairs : 1;
@@ -190,7 +191,7 @@ tq_status plan_decode(const tq_layer* L, int batch, int n_q_heads, int max_seq_l
     return fail(TQ_ERR_UNSUPPORTED, "decode grid of %lld workgroups (batch x kv_heads x splits) exceeds 2^31 - 1",
                 items);
   // The work list pays one dependent read of seq_lens per workgroup; it is used
-  // where the grid is more than one round of resident workgroups (two per CU),
+  // where the grid is more than about one round of workgroups (two per CU),
   // so that dispatch order and the last round matter.
   const int wl = env_work_list();
   p.work_list = wl >= 0 ? wl == 1 : items > 2LL * (L->cu_count > 0 ? L->cu_count : 256);

@@ -37,9 +37,11 @@
 //
 // A wave takes a 32-token chunk (two 16-token pages) at a time; the four waves
 // of a workgroup take chunks in turn and merge at the end.  While a chunk is
-// processed from one LDS stage, the next chunk's pages are copied into the
-// other straight from global memory.  Online softmax keeps a running max per
-// head, rescaling only when it grows by more than kRescale.
+// processed from registers, the next chunk's page fields are loaded straight
+// from global memory into a second register set (a two-chunk ring).  Online
+// softmax keeps a running max per head, rescaling only when it grows by more
+// than kRescale.  Registers and the lookup tables below are sized so that three
+// workgroups share a CU.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
