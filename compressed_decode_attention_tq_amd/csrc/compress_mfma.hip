@@ -458,6 +458,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
       }
       g2 = rows_sum(g2);
       if (kg == 0) gpart[w][col] = g2;
+      // the stored magnitude n (not the norm-corrected one, which needs the
+      // residual sums of every wave): wave 3, which reaches the next barrier
+      // early (its SIMD's matrix core served it first in B1)
+      if (w == 3 && kg == 0 && (QJL || a.km != 2))
+        *reinterpret_cast<unsigned short*>(&img[PG::kn + col * (QJL ? 4 : 2)]) =
+            __half_as_ushort(__float2half_rn(sqrtf(k2)));
       // rho as float16 hi (RNE) and lo = float16(rho - hi), two coordinates per word
       u32x2 rh, rl;
 #pragma unroll
@@ -614,21 +620,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, QJL ? 4 
         *reinterpret_cast<unsigned*>(&img[PG::vsz + col * 16 + G * 4]) =
             static_cast<unsigned>(__half_as_ushort(s16)) | (static_cast<unsigned>(__half_as_ushort(z16)) << 16);
       }
-      if (w == 7 && kg == 0) {
+      if (w == 1 && kg == 0 && (QJL || a.km == 2)) {
         float g2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) g2 += gpart[i][col];
-        // stored magnitude: n, or n sqrt(d) / ||c[idx]|| with norm correction;
-        // with QJL the pair (n, gamma), without QJL the magnitude alone
-        const float n = sqrtf(k2);
-        const unsigned short n16 =
-            __half_as_ushort(__float2half_rn(!QJL && a.km == 2 ? n * sqrtf(128.0f) / sqrtf(g2) : n));
+        // with QJL gamma beside n; without QJL and with norm correction the
+        // magnitude n sqrt(d) / ||c[idx]|| (the plain n was written in B2)
         if constexpr (QJL) {
-          const unsigned short g16 = __half_as_ushort(__float2half_rn(sqrtf(g2)));
-          *reinterpret_cast<unsigned*>(&img[PG::kn + col * 4]) =
-              static_cast<unsigned>(n16) | (static_cast<unsigned>(g16) << 16);
+          *reinterpret_cast<unsigned short*>(&img[PG::kn + col * 4 + 2]) = __half_as_ushort(__float2half_rn(sqrtf(g2)));
         } else {
-          *reinterpret_cast<unsigned short*>(&img[PG::kn + col * 2]) = n16;
+          *reinterpret_cast<unsigned short*>(&img[PG::kn + col * 2]) =
+              __half_as_ushort(__float2half_rn(sqrtf(k2) * sqrtf(128.0f) / sqrtf(g2)));
         }
       }
     }
