@@ -418,26 +418,25 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
   const int u = tid & 511;
   const int t = VB == 4 ? 8 * ((u >> 6) & 1) + (u & 7) : u >> 5;
   const int d0 = VB == 4 ? 4 * ((u >> 7) + 4 * ((u >> 3) & 7)) : 4 * (u & 31);
+  // The two roles run loops of their own with one workgroup barrier per
+  // iteration each (mine + 2 of them), so the copying loop does not hold the
+  // contracting waves' 64 registers of B operands.  At the barrier of
+  // iteration k: tile k's page and tile k+2's slots are in LDS, tile k-1's A
+  // operands expanded, and tile k-2's products formed (its buffer is free) and
+  // staged.
+  if (!mma) {
 #pragma unroll 1
-  for (int k = 0; k <= mine + 1; ++k) {
-    // (copying waves) operations issued after tile k's page copy: the page copy
-    // of tile 1 (k = 0); the slot copy of tile k+3 and the page copy of k+1
-    if (!mma && k < mine) {
-      if (k == 0)
-        wait_vmcnt<1>();
-      else
-        wait_vmcnt<2>();
-    }
-    // tile k's page and tile k+2's slots in LDS; tile k-1's A operands
-    // expanded; tile k-2's products formed (its buffer is free) and staged
-    __syncthreads();
-    if (!mma) {
+    for (int k = 0; k <= mine + 1; ++k) {
+      // operations issued after tile k's page copy: the page copy of tile 1
+      // (k = 0); the slot copy of tile k+3 and the page copy of k+1
+      if (k < mine) {
+        if (k == 0)
+          wait_vmcnt<1>();
+        else
+          wait_vmcnt<2>();
+      }
+      __syncthreads();
       if (k >= mine) continue;
-      // copies of tile k+4's slots and tile k+2's page
-      long long s02;
-      const bool whole2 = page_of(ring_slot(k + 2), &s02);
-      copy_slots(k + 4);
-      copy_page(k + 2, s02);
 
       // ---- expand tile k: thread (t, d0) -> A operands of token t, dims d0..d0+3
       auto& ac = aop[k & 1][0];
@@ -446,44 +445,65 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       auto& az = aop[k & 1][NA - 1];  // (QJL only)
       const long long n0 = tile_of(k) * 16;
       const bool whole = wholec;
-      // expansion of token t's dims d0..d0+3 from its record at in-page offset o
-      auto expand = [&](auto page, int o) {
+      // The expansion of token t's dims d0..d0+3 from its record at in-page
+      // offset o in two parts: fetch only issues the loads of the record's
+      // fields (so that other work can be placed while they are in flight),
+      // emit decodes them, looks the codes up and writes the A operands.
+      struct Raw {
+        unsigned k0, k1, z, sz, v0[4], v1[4];
+      };
+      // value codes: element ((16 (o / 8) + jd % 16) 16 + 2 (jd / 16) + (o % 8) / 4) 4 + o % 4
+      // of the Vc field; dims d0 + i step the element by 64, so the byte by 8 VB
+      // and the bit position within it stays (one byte for VB = 2, 4; two for 3)
+      auto vel = [&](int o) {
+        return ((16u * (o >> 3) + (d0 & 15)) * 16u + 2u * (d0 >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
+      };
+      auto fetch = [&](auto page, int o) {
+        Raw r{};
         const int blk = d0 >> 5, e0 = d0 & 31;
         // key codes of dims d0..d0+3: 4 KB bits at bit e0 KB of the block record
         // (one byte for KB <= 2, an aligned halfword for KB = 4, two bytes for 3)
         const auto kc = page + F.kc + (blk * 16 + o) * 4 * KB + ((e0 * KB) >> 3);
+        if constexpr (KB == 4) {
+          r.k0 = ld<unsigned short>(kc);
+        } else {
+          r.k0 = ld<unsigned char>(kc);
+          if constexpr (KB == 3) r.k1 = ld<unsigned char>(kc + 1);
+        }
+        if constexpr (QJL) r.z = ld<unsigned char>(page + F.ks + (blk * 16 + o) * 4 + (e0 >> 3));
+        // (MSE-coded values: the token's norm is applied after the products)
+        if constexpr (!MSEV) r.sz = ld<unsigned>(page + F.vsz + o * 16 + blk * 4);
+        const auto vb = page + F.vc + ((vel(o) * VB) >> 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r.v0[i] = ld<unsigned char>(vb + 8 * VB * i);
+          if constexpr (VB == 3) r.v1[i] = ld<unsigned char>(vb + 8 * VB * i + 1);
+        }
+        return r;
+      };
+      auto emit = [&](const Raw& r, int o) {
+        const int e0 = d0 & 31;
         unsigned kx;
         if constexpr (KB == 4)
-          kx = ld<unsigned short>(kc);
+          kx = r.k0;
         else if constexpr (KB == 3)
-          kx = (static_cast<unsigned>(ld<unsigned char>(kc)) | (static_cast<unsigned>(ld<unsigned char>(kc + 1)) << 8)) >>
-               ((e0 * KB) & 7);
+          kx = (r.k0 | (r.k1 << 8)) >> ((e0 * KB) & 7);
         else
-          kx = static_cast<unsigned>(ld<unsigned char>(kc)) >> ((e0 * KB) & 7);
-        unsigned zb = 0u;
-        if constexpr (QJL)
-          zb = static_cast<unsigned>(ld<unsigned char>(page + F.ks + (blk * 16 + o) * 4 + (e0 >> 3))) >> (e0 & 7);
-        // (MSE-coded values: the token's norm is applied after the products)
+          kx = r.k0 >> ((e0 * KB) & 7);
+        const unsigned zb = QJL ? r.z >> (e0 & 7) : 0u;
         float sc = 0.0f, zr = 0.0f;
         if constexpr (!MSEV) {
-          const unsigned sz = ld<unsigned>(page + F.vsz + o * 16 + blk * 4);
-          sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz & 0xffffu)));
-          zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz >> 16)));
+          sc = __half2float(__ushort_as_half(static_cast<unsigned short>(r.sz & 0xffffu)));
+          zr = __half2float(__ushort_as_half(static_cast<unsigned short>(r.sz >> 16)));
         }
-        // value codes: element ((16 (o / 8) + jd % 16) 16 + 2 (jd / 16) + (o % 8) / 4) 4 + o % 4
-        // of the Vc field; dims d0 + i step the element by 64, so the byte by 8 VB
-        // and the bit position within it stays (one byte for VB = 2, 4; two for 3)
-        const unsigned e = ((16u * (o >> 3) + (d0 & 15)) * 16u + 2u * (d0 >> 4) + ((o & 7) >> 2)) * 4u + (o & 3);
-        const auto vb = page + F.vc + ((e * VB) >> 3);
-        const unsigned vsh = (e * VB) & 7;
+        const unsigned vsh = (vel(o) * VB) & 7;
         _Float16 hc[4], hz[4], hv[4];
         float vx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
           hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-          unsigned vw = ld<unsigned char>(vb + 8 * VB * i);
-          if constexpr (VB == 3) vw |= static_cast<unsigned>(ld<unsigned char>(vb + 8 * VB * i + 1)) << 8;
+          const unsigned vw = VB == 3 ? (r.v0[i] | (r.v1[i] << 8)) : r.v0[i];
           const unsigned code = (vw >> vsh) & ((1u << VB) - 1u);
           if constexpr (MSEV)
             hv[i] = vcent_h[code];
@@ -503,23 +523,40 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
         }
       };
       constexpr int kn_bytes = QJL ? 4 : 2;  // Kn bytes per token
+      // copies of tile k+4's slots and tile k+2's page
+      long long s02;
+      bool whole2;
       __builtin_amdgcn_sched_barrier(0);
       if (whole) {
-        // the page image in the ring (LDS reads); its Kn words as they are
+        // The page image in the ring (LDS reads).  Tile k+2's slots are read
+        // with its fields, so that the two LDS round trips overlap, and that
+        // tile's copies are issued before the codebook lookups.
         const lds_byte* pg = (const lds_byte*)(&pring[k % 3][0]);
-        expand(pg, t);
+        const long long sj2 = ring_slot(k + 2);
+        const Raw r = fetch(pg, t);
+        __builtin_amdgcn_sched_barrier(0);
+        whole2 = page_of(sj2, &s02);
+        copy_slots(k + 4);
+        copy_page(k + 2, s02);
+        __builtin_amdgcn_sched_barrier(0);
+        emit(r, t);
+        // its Kn words as they are
         if (u < 4 * kn_bytes) *reinterpret_cast<unsigned*>(&knb[k & 1][4 * u]) = ld<unsigned>(pg + F.kn + 4 * u);
         if constexpr (MSEV)
           if (u >= 32 && u < 40)
             *reinterpret_cast<unsigned*>(&vnb[k & 1][4 * (u - 32)]) = ld<unsigned>(pg + F.vsz + 4 * (u - 32));
       } else {
+        whole2 = page_of(ring_slot(k + 2), &s02);
+        copy_slots(k + 4);
+        copy_page(k + 2, s02);
+        __builtin_amdgcn_sched_barrier(0);
         // (the ragged last tile's ring entry holds shifted slots near the input's end)
         const long long slot =
             n0 + t < a.n_tokens ? (n0 + 16 <= a.n_tokens ? sring[k & 7][t] : a.slots[n0 + t]) : -1;
         if (slot >= 0) {
           const unsigned char* pg = a.pool + (static_cast<size_t>(slot >> 4) * a.H + g) * F.bytes;
           const int o = static_cast<int>(slot & 15);
-          expand(pg, o);
+          emit(fetch(pg, o), o);
           if (d0 == 0) {  // (one thread per token)
             if constexpr (QJL)
               *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = ld<unsigned>(pg + F.kn + 4 * o);
@@ -549,108 +586,117 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       s0c = s0n;
       wholen = whole2;
       s0n = s02;
-      continue;
     }
-    if (k == 0) continue;
+  } else {
+#pragma unroll 1
+    for (int k = 0; k <= mine + 1; ++k) {
+      __syncthreads();
+      if (k == 0) continue;
 
-    // ---- store tile k-2 from its staging: wave w, rows 4w..4w+3 of the 32
-    // (K rows of tokens 0..15, then V rows), 16 lanes a row, 16 contiguous
-    // bytes each (two 16-byte pieces for fp32)
-    if (k >= 2) {
-      const int ridx = 4 * w + (lane >> 4), kv = ridx >> 4, tt = ridx & 15, c = lane & 15;
-      const unsigned* row = &stage[k & 1][kv][tt][0];
-      const long long n = tile_of(k - 2) * 16 + tt;
-      if (n < a.n_tokens) {
-        void* out = kv ? a.vout : a.kout;
-        const size_t at = (static_cast<size_t>(n) * a.H + g) * 128;
-        if constexpr (OUT_BF16) {
-          *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at + 8 * c) =
-              *reinterpret_cast<const u32x4*>(row + 4 * c);
-        } else {
-          float* o = static_cast<float*>(out) + at;
-          *reinterpret_cast<u32x4*>(o + 4 * c) = *reinterpret_cast<const u32x4*>(row + 4 * c);
-          *reinterpret_cast<u32x4*>(o + 64 + 4 * c) = *reinterpret_cast<const u32x4*>(row + 64 + 4 * c);
+      // ---- store tile k-2 from its staging: wave w, rows 4w..4w+3 of the 32
+      // (K rows of tokens 0..15, then V rows), 16 lanes a row, 16 contiguous
+      // bytes each (two 16-byte pieces for fp32)
+      if (k >= 2) {
+        const int ridx = 4 * w + (lane >> 4), kv = ridx >> 4, tt = ridx & 15, c = lane & 15;
+        const unsigned* row = &stage[k & 1][kv][tt][0];
+        const long long n = tile_of(k - 2) * 16 + tt;
+        if (n < a.n_tokens) {
+          void* out = kv ? a.vout : a.kout;
+          const size_t at = (static_cast<size_t>(n) * a.H + g) * 128;
+          if constexpr (OUT_BF16) {
+            *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at + 8 * c) =
+                *reinterpret_cast<const u32x4*>(row + 4 * c);
+          } else {
+            float* o = static_cast<float*>(out) + at;
+            *reinterpret_cast<u32x4*>(o + 4 * c) = *reinterpret_cast<const u32x4*>(row + 4 * c);
+            *reinterpret_cast<u32x4*>(o + 64 + 4 * c) = *reinterpret_cast<const u32x4*>(row + 64 + 4 * c);
+          }
         }
       }
-    }
-    if (k > mine) continue;
+      if (k > mine) continue;
 
-    // ---- contract tile k-1: wave w, output dims 16w + col of tokens 4kg + r
-    const int b = (k - 1) & 1;
-    floatx4 k1 = {0.0f, 0.0f, 0.0f, 0.0f}, k2 = k1, vv = k1;
+      // ---- contract tile k-1: wave w, output dims 16w + col of tokens 4kg + r
+      const int b = (k - 1) & 1;
+      floatx4 k1 = {0.0f, 0.0f, 0.0f, 0.0f}, k2 = k1, vv = k1;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c0 = 32 * s + 8 * kg;
-      const half8 xc = *reinterpret_cast<const half8*>(&aop[b][0][col][c0]);
-      const half8 xh = *reinterpret_cast<const half8*>(&aop[b][1][col][c0]);
-      k1 = mfma(xc, RH[s], k1);
-      k1 = mfma(xc, RL[s], k1);
-      if constexpr (QJL) {
-        const half8 xz = *reinterpret_cast<const half8*>(&aop[b][NA - 1][col][c0]);
-        k2 = mfma(xz, PH[s], k2);
-        k2 = mfma(xz, PL[s], k2);
+      for (int s = 0; s < 4; ++s) {
+        const int c0 = 32 * s + 8 * kg;
+        const half8 xc = *reinterpret_cast<const half8*>(&aop[b][0][col][c0]);
+        const half8 xh = *reinterpret_cast<const half8*>(&aop[b][1][col][c0]);
+        k1 = mfma(xc, RH[s], k1);
+        k1 = mfma(xc, RL[s], k1);
+        // (the fences keep each read next to its products: with all of a K-step's
+        // reads issued at once the copying waves' LDS round trips took longer,
+        // and the launch with them; layer store 189 against 207 us)
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (QJL) {
+          const half8 xz = *reinterpret_cast<const half8*>(&aop[b][NA - 1][col][c0]);
+          k2 = mfma(xz, PH[s], k2);
+          k2 = mfma(xz, PL[s], k2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        vv = mfma(xh, RH[s], vv);
+        vv = mfma(xh, RL[s], vv);
+        if constexpr (!MSEV) {  // (MSE-coded values: the codebook entries are exact, no lo piece)
+          const half8 xl = *reinterpret_cast<const half8*>(&aop[b][2][col][c0]);
+          vv = mfma(xl, RH[s], vv);
+        }
+        // one K-step's A operands live at a time (next to the 64 registers of B
+        // operands): the scheduler may not hoist the next step's reads above here
+        __builtin_amdgcn_sched_barrier(0);
       }
-      vv = mfma(xh, RH[s], vv);
-      vv = mfma(xh, RL[s], vv);
-      if constexpr (!MSEV) {  // (MSE-coded values: the codebook entries are exact, no lo piece)
-        const half8 xl = *reinterpret_cast<const half8*>(&aop[b][2][col][c0]);
-        vv = mfma(xl, RH[s], vv);
-      }
-      // one K-step's A operands live at a time (next to the 64 registers of B
-      // operands): the scheduler may not hoist the next step's reads above here
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // ---- stage tile k-1: lane (col, kg) holds rows 4kg..4kg+3 of output dim
-    // 16w + col; K = n (x1 + kappa gamma x2), n and gamma as float16
-    float kx[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tt = 4 * kg + r;
-      if constexpr (QJL) {
-        const unsigned kn = *reinterpret_cast<const unsigned*>(&knb[b][4 * tt]);
-        const float sn = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) *
-                         0.08838834764831845f;
-        const float sg = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
-        kx[r] = sn * fmaf(sg, k2[r], k1[r]);
-      } else {
-        const unsigned short kn = *reinterpret_cast<const unsigned short*>(&knb[b][2 * tt]);
-        kx[r] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f * k1[r];
-      }
-      // MSE-coded values: V = (nv / sqrt(d)) (codebook values . R), nv as float16
-      if constexpr (MSEV) {
-        const unsigned short vn = *reinterpret_cast<const unsigned short*>(&vnb[b][2 * tt]);
-        vv[r] *= __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
-      }
-    }
-    const int dc = 16 * w + col;
-    auto& st = stage[b];
-    if constexpr (OUT_BF16) {
-      // two adjacent dims per word: of a lane pair (col, col ^ 1) the even lane
-      // writes rows 4kg, 4kg+1 and the odd lane rows 4kg+2, 4kg+3, each with
-      // the partner's values taken across the pair
-      const bool odd = col & 1;
-      const int r0 = 4 * kg + (odd ? 2 : 0);
-      auto put_pairs = [&](int kv, float x0, float x1, float x2, float x3) {
-        const bf16x2 p01 = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
-        const bf16x2 p23 = {static_cast<__bf16>(x2), static_cast<__bf16>(x3)};
-        const unsigned b01 = __builtin_bit_cast(unsigned, p01), b23 = __builtin_bit_cast(unsigned, p23);
-        const unsigned send = odd ? b01 : b23;
-        // quad_perm [1, 0, 3, 2]: the word of lane col ^ 1
-        const unsigned recv =
-            static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(send), 0xB1, 0xF, 0xF, false));
-        const unsigned keep = odd ? b23 : b01;
-        // even lane: (own, partner) of rows r0, r0+1; odd lane: (partner, own)
-        const unsigned lo = odd ? recv : keep, hi = odd ? keep : recv;
-        st[kv][r0][dc >> 1] = (lo & 0xffffu) | (hi << 16);
-        st[kv][r0 + 1][dc >> 1] = (lo >> 16) | (hi & 0xffff0000u);
-      };
-      put_pairs(0, kx[0], kx[1], kx[2], kx[3]);
-      put_pairs(1, vv[0], vv[1], vv[2], vv[3]);
-    } else {
+      // ---- stage tile k-1: lane (col, kg) holds rows 4kg..4kg+3 of output dim
+      // 16w + col; K = n (x1 + kappa gamma x2), n and gamma as float16
+      float kx[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        st[0][4 * kg + r][dc] = __float_as_uint(kx[r]);
-        st[1][4 * kg + r][dc] = __float_as_uint(vv[r]);
+        const int tt = 4 * kg + r;
+        if constexpr (QJL) {
+          const unsigned kn = *reinterpret_cast<const unsigned*>(&knb[b][4 * tt]);
+          const float sn = __half2float(__ushort_as_half(static_cast<unsigned short>(kn & 0xffffu))) *
+                           0.08838834764831845f;
+          const float sg = a.kappa * __half2float(__ushort_as_half(static_cast<unsigned short>(kn >> 16)));
+          kx[r] = sn * fmaf(sg, k2[r], k1[r]);
+        } else {
+          const unsigned short kn = *reinterpret_cast<const unsigned short*>(&knb[b][2 * tt]);
+          kx[r] = __half2float(__ushort_as_half(kn)) * 0.08838834764831845f * k1[r];
+        }
+        // MSE-coded values: V = (nv / sqrt(d)) (codebook values . R), nv as float16
+        if constexpr (MSEV) {
+          const unsigned short vn = *reinterpret_cast<const unsigned short*>(&vnb[b][2 * tt]);
+          vv[r] *= __half2float(__ushort_as_half(vn)) * 0.08838834764831845f;
+        }
+      }
+      const int dc = 16 * w + col;
+      auto& st = stage[b];
+      if constexpr (OUT_BF16) {
+        // two adjacent dims per word: of a lane pair (col, col ^ 1) the even lane
+        // writes rows 4kg, 4kg+1 and the odd lane rows 4kg+2, 4kg+3, each with
+        // the partner's values taken across the pair
+        const bool odd = col & 1;
+        const int r0 = 4 * kg + (odd ? 2 : 0);
+        auto put_pairs = [&](int kv, float x0, float x1, float x2, float x3) {
+          const bf16x2 p01 = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+          const bf16x2 p23 = {static_cast<__bf16>(x2), static_cast<__bf16>(x3)};
+          const unsigned b01 = __builtin_bit_cast(unsigned, p01), b23 = __builtin_bit_cast(unsigned, p23);
+          const unsigned send = odd ? b01 : b23;
+          // quad_perm [1, 0, 3, 2]: the word of lane col ^ 1
+          const unsigned recv =
+              static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(send), 0xB1, 0xF, 0xF, false));
+          const unsigned keep = odd ? b23 : b01;
+          // even lane: (own, partner) of rows r0, r0+1; odd lane: (partner, own)
+          const unsigned lo = odd ? recv : keep, hi = odd ? keep : recv;
+          st[kv][r0][dc >> 1] = (lo & 0xffffu) | (hi << 16);
+          st[kv][r0 + 1][dc >> 1] = (lo >> 16) | (hi & 0xffff0000u);
+        };
+        put_pairs(0, kx[0], kx[1], kx[2], kx[3]);
+        put_pairs(1, vv[0], vv[1], vv[2], vv[3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          st[0][4 * kg + r][dc] = __float_as_uint(kx[r]);
+          st[1][4 * kg + r][dc] = __float_as_uint(vv[r]);
+        }
       }
     }
   }
