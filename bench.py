@@ -552,9 +552,9 @@ def decompress_workload(torch, tq, synth, args):
     layer.close()
     rec = _record_bytes(W["k_bits"], W["v_bits"])
     nbytes = N * Hkv * (rec + 512) + N * 8
-    # matrix-core floor: 7 passes x 4 K-steps x 8 column tiles per 16 token-heads,
+    # matrix-core floor: 6 passes x 4 K-steps x 8 column tiles per 16 token-heads,
     # 16 cycles each at 1024 SIMDs x 2.4 GHz
-    mfma_us = N * Hkv / 16 * 224 * 16 / (1024 * 2.4e9) * 1e6
+    mfma_us = N * Hkv / 16 * 192 * 16 / (1024 * 2.4e9) * 1e6
     kern = "decompress_ring_kernel<4,4,true,true,false>"
     return {"workload": "decompress-llama3-8b-layer-store", "token_heads": N * Hkv, "out_dtype": "bf16",
             "ms": round(ms, 4), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),

@@ -296,16 +296,18 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
   const int w = wave & 7;
   const int col = lane & 15, kg = lane >> 4;
 
-  // Two buffers of a tile's A operands (codebook values, v' hi, v' lo and,
-  // with QJL, signs +-1; with MSE-coded values the value codebook entries in
-  // place of v' hi, exact in float16, and no lo piece), of its Kn words and
-  // (MSE-coded values) of its value norms; each kind is one array, so an
-  // access is one per-lane address plus a constant offset, which keeps the
-  // loop's live registers few.
-  constexpr int NA = QJL ? 4 : 3;
+  // Two buffers of a tile's A operands (key codebook values, value operands
+  // and, with QJL, signs +-1; the value operands are the group codes as
+  // float16 integers, or with MSE-coded values the value codebook entries: all
+  // exact in float16), of its Kn words and of its value metadata (the
+  // per-group scale/zero words, or the value norms of MSE-coded values); each
+  // kind is one array, so an access is one per-lane address plus a constant
+  // offset, which keeps the loop's live registers few.
+  constexpr int NA = QJL ? 3 : 2;
   __shared__ __attribute__((aligned(16))) _Float16 aop[2][NA][16][kARow];
   __shared__ __attribute__((aligned(16))) unsigned char knb[2][64];
   __shared__ __attribute__((aligned(16))) unsigned char vnb[2][MSEV ? 32 : 4];
+  __shared__ __attribute__((aligned(16))) unsigned szb[2][MSEV ? 1 : 16][4];  // [token][group]
   // Two buffers of a tile's outputs: the K and V rows of its 16 tokens (bf16
   // pairs or fp32 values per word; the 4-word row padding puts the rows a
   // half wave writes at once on distinct banks).  The contracting waves write
@@ -441,7 +443,6 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       // ---- expand tile k: thread (t, d0) -> A operands of token t, dims d0..d0+3
       auto& ac = aop[k & 1][0];
       auto& avh = aop[k & 1][1];
-      auto& avl = aop[k & 1][2];
       auto& az = aop[k & 1][NA - 1];  // (QJL only)
       const long long n0 = tile_of(k) * 16;
       const bool whole = wholec;
@@ -491,36 +492,22 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
         else
           kx = r.k0 >> ((e0 * KB) & 7);
         const unsigned zb = QJL ? r.z >> (e0 & 7) : 0u;
-        float sc = 0.0f, zr = 0.0f;
-        if constexpr (!MSEV) {
-          sc = __half2float(__ushort_as_half(static_cast<unsigned short>(r.sz & 0xffffu)));
-          zr = __half2float(__ushort_as_half(static_cast<unsigned short>(r.sz >> 16)));
-        }
         const unsigned vsh = (vel(o) * VB) & 7;
         _Float16 hc[4], hz[4], hv[4];
-        float vx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           hc[i] = cent_h[(kx >> (KB * i)) & ((1u << KB) - 1u)];
           hz[i] = ((zb >> i) & 1u) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
           const unsigned vw = VB == 3 ? (r.v0[i] | (r.v1[i] << 8)) : r.v0[i];
           const unsigned code = (vw >> vsh) & ((1u << VB) - 1u);
-          if constexpr (MSEV)
-            hv[i] = vcent_h[code];
-          else
-            vx[i] = fmaf(sc, static_cast<float>(code), zr);
+          hv[i] = MSEV ? vcent_h[code] : static_cast<_Float16>(static_cast<float>(code));
         }
         *reinterpret_cast<half4*>(&ac[t][d0]) = half4{hc[0], hc[1], hc[2], hc[3]};
         if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = half4{hz[0], hz[1], hz[2], hz[3]};
-        if constexpr (MSEV) {
-          *reinterpret_cast<half4*>(&avh[t][d0]) = half4{hv[0], hv[1], hv[2], hv[3]};
-        } else {
-          // v' as float16 hi + lo of the float32 value (pieces against the same hi)
-          const unsigned h01 = pack_f16(vx[0], vx[1]), h23 = pack_f16(vx[2], vx[3]);
-          *reinterpret_cast<u32x2*>(&avh[t][d0]) = u32x2{h01, h23};
-          *reinterpret_cast<u32x2*>(&avl[t][d0]) =
-              u32x2{residual_pair(vx[0], vx[1], h01), residual_pair(vx[2], vx[3], h23)};
-        }
+        *reinterpret_cast<half4*>(&avh[t][d0]) = half4{hv[0], hv[1], hv[2], hv[3]};
+        // (group values: the group's scale/zero word, by the thread of its first dims)
+        if constexpr (!MSEV)
+          if (e0 == 0) szb[k & 1][t][d0 >> 5] = r.sz;
       };
       constexpr int kn_bytes = QJL ? 4 : 2;  // Kn bytes per token
       // copies of tile k+4's slots and tile k+2's page
@@ -571,7 +558,8 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           *reinterpret_cast<half4*>(&ac[t][d0]) = z4;
           if constexpr (QJL) *reinterpret_cast<half4*>(&az[t][d0]) = z4;
           *reinterpret_cast<half4*>(&avh[t][d0]) = z4;
-          if constexpr (!MSEV) *reinterpret_cast<half4*>(&avl[t][d0]) = z4;
+          if constexpr (!MSEV)
+            if ((d0 & 31) == 0) szb[k & 1][t][d0 >> 5] = 0u;
           if (d0 == 0) {
             if constexpr (QJL)
               *reinterpret_cast<unsigned*>(&knb[k & 1][4 * t]) = 0u;
@@ -588,6 +576,19 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
       s0n = s02;
     }
   } else {
+    // Group values: the column sums of R over each K-step's 32 rows (one value
+    // group), rows of ones times R hi + lo, for the groups' zero terms.
+    float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!MSEV) {
+      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = mfma(ones, RH[s], c);
+        c = mfma(ones, RL[s], c);
+        csum[s] = c[0];
+      }
+    }
 #pragma unroll 1
     for (int k = 0; k <= mine + 1; ++k) {
       __syncthreads();
@@ -623,6 +624,18 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
         const int c0 = 32 * s + 8 * kg;
         const half8 xc = *reinterpret_cast<const half8*>(&aop[b][0][col][c0]);
         const half8 xh = *reinterpret_cast<const half8*>(&aop[b][1][col][c0]);
+        // Group values: K-step s spans one group, v' = zero + scale code on it,
+        // so its share of V is scale (codes . R) + zero (column sum of R); the
+        // codes' products go first, so that they are done when the group's
+        // scale and zero are applied after the key products.
+        floatx4 vs = {0.0f, 0.0f, 0.0f, 0.0f};
+        unsigned sz[4];
+        if constexpr (!MSEV) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sz[r] = szb[b][4 * kg + r][s];
+          vs = mfma(xh, RH[s], vs);
+          vs = mfma(xh, RL[s], vs);
+        }
         k1 = mfma(xc, RH[s], k1);
         k1 = mfma(xc, RL[s], k1);
         // (the fences keep each read next to its products: with all of a K-step's
@@ -635,11 +648,16 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           k2 = mfma(xz, PL[s], k2);
         }
         __builtin_amdgcn_sched_barrier(0);
-        vv = mfma(xh, RH[s], vv);
-        vv = mfma(xh, RL[s], vv);
-        if constexpr (!MSEV) {  // (MSE-coded values: the codebook entries are exact, no lo piece)
-          const half8 xl = *reinterpret_cast<const half8*>(&aop[b][2][col][c0]);
-          vv = mfma(xl, RH[s], vv);
+        if constexpr (MSEV) {
+          vv = mfma(xh, RH[s], vv);
+          vv = mfma(xh, RL[s], vv);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sc = __half2float(__ushort_as_half(static_cast<unsigned short>(sz[r] & 0xffffu)));
+            const float zr = __half2float(__ushort_as_half(static_cast<unsigned short>(sz[r] >> 16)));
+            vv[r] = fmaf(sc, vs[r], fmaf(zr, csum[s], vv[r]));
+          }
         }
         // one K-step's A operands live at a time (next to the 64 registers of B
         // operands): the scheduler may not hoist the next step's reads above here
