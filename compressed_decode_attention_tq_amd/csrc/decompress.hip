@@ -596,7 +596,9 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
 
       // ---- store tile k-2 from its staging: wave w, rows 4w..4w+3 of the 32
       // (K rows of tokens 0..15, then V rows), 16 lanes a row, 16 contiguous
-      // bytes each (two 16-byte pieces for fp32)
+      // bytes each (two 16-byte pieces for fp32), as non-temporal stores: the
+      // output is written once and not read back by this launch (layer store
+      // 189 against 195 us with ordinary stores)
       if (k >= 2) {
         const int ridx = 4 * w + (lane >> 4), kv = ridx >> 4, tt = ridx & 15, c = lane & 15;
         const unsigned* row = &stage[k & 1][kv][tt][0];
@@ -605,12 +607,13 @@ __global__ __launch_bounds__(1024) void decompress_ring_kernel(DArgs a) {
           void* out = kv ? a.vout : a.kout;
           const size_t at = (static_cast<size_t>(n) * a.H + g) * 128;
           if constexpr (OUT_BF16) {
-            *reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at + 8 * c) =
-                *reinterpret_cast<const u32x4*>(row + 4 * c);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(row + 4 * c),
+                                        reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + at + 8 * c));
           } else {
             float* o = static_cast<float*>(out) + at;
-            *reinterpret_cast<u32x4*>(o + 4 * c) = *reinterpret_cast<const u32x4*>(row + 4 * c);
-            *reinterpret_cast<u32x4*>(o + 64 + 4 * c) = *reinterpret_cast<const u32x4*>(row + 64 + 4 * c);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(row + 4 * c), reinterpret_cast<u32x4*>(o + 4 * c));
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(row + 64 + 4 * c),
+                                        reinterpret_cast<u32x4*>(o + 64 + 4 * c));
           }
         }
       }
